@@ -1,0 +1,338 @@
+"""Benchmark of retrieval-based sparse-attention decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one decode step of every request of the workload through the whole
+hot path (centroid scoring, top-k lists, gather plan, gathered attention for
+the inverted-index workloads; indexer scan, top-k and attention for the token
+workload; RESOLVE and attention over the hot slots for the cache workload),
+with inputs resident in HBM (the cache workload's authoritative KV in pinned
+host memory). Prints one JSON line.
+
+value  = decode queries per second (one query = one request's decode step,
+         all of its heads) over the K timed steps;
+roofline = the gather-attention kernel: algorithmic bytes (512 B per unique
+         (request, KV head, token) K+V row it reads) / its mean launch time,
+         timed with HIP events recorded by the library around each launch.
+cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-decode queries/s + gathered-KV GB/s as % of MI355X HBM peak"
+HBM_PEAK_GBPS = 8000.0
+ROW_BYTES_BF16 = 2 * 128 * 2  # one K row + one V row, 128 bf16 each
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gather_attn_traffic.json")
+GATHER_SRC = os.path.join(ROOT, "top_sparse_attention_centroid_amd", "csrc", "attention.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gather_source_sha() -> str:
+    with open(GATHER_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gather launch from the committed counter summary, if it was
+    taken on the current kernel source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha") != gather_source_sha():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# inverted-index workloads
+# ----------------------------------------------------------------------------
+
+def bench_ivf(args, cfg, torch, tsa, W):
+    dev = "cuda"
+    B, Hq, Hkv, k = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.top_k
+    log(f"generating {cfg.name} on the GPU")
+    p = W.ivf_problem(cfg, device=dev)
+    nq = min(cfg.steps, 64)
+    q_all = W.ivf_queries(cfg, p["centroids"], steps=nq)
+    t0 = time.perf_counter()
+    offsets, ids = tsa.index_build(p["keys"], p["centroids"])
+    torch.cuda.synchronize()
+    index_ms = (time.perf_counter() - t0) * 1e3
+    out = torch.empty((B, Hq, cfg.head_dim), dtype=torch.float32, device=dev)
+    uniq = torch.empty((nq, B, Hkv), dtype=torch.int32, device=dev)
+    desc = tsa.binding.ivf_desc(p["keys"], p["centroids"], Hq)
+    ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        if ev is not None:
+            tsa.time_next_gather(*ev)
+        tsa.sparse_decode(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
+                          out=out, uniq_out=uniq[i % nq], ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_stop)
+    gather_ms = [a.elapsed_time(b) for a, b in evs]
+    rows_per_set = uniq.sum(dim=(1, 2)).cpu().double()
+    rows = sum(float(rows_per_set[i % nq]) for i in range(args.steps))
+    row_bytes = 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
+    res = {
+        "ms_total": ms_total, "wall_s": wall, "gather_ms": gather_ms, "gathered_bytes": rows * row_bytes,
+        "queries": B * args.steps, "index_build_ms": index_ms,
+        "unique_rows_per_step": rows / args.steps,
+    }
+    if args.cpu_seconds > 0:
+        res["cpu"] = cpu_baseline_ivf(args, cfg, p, q_all, torch, W)
+    return res
+
+
+def cpu_baseline_ivf(args, cfg, p, q_all, torch, W):
+    """The oracle on whole (request, step) decode queries of the same workload
+    until the time budget is used: queries/s on the host, single BLAS thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ivf
+
+    reqs = [0, 1] if cfg.batch > 1 else [0]
+    log(f"oracle baseline: building its index for requests {reqs}")
+    K = {b: p["keys"][b:b + 1].to("cpu", torch.float64).numpy() for b in reqs}
+    V = {b: p["values"][b:b + 1].to("cpu", torch.float64).numpy() for b in reqs}
+    cent = p["centroids"].to("cpu", torch.float64).numpy()
+    index = {}
+    for b in reqs:
+        cb = cent[0:1] if cent.shape[0] == 1 else cent[b:b + 1]
+        off, ids, _ = ivf.index_build(K[b], cb)
+        index[b] = (cb, off, ids)
+    q64 = q_all.to("cpu", torch.float64).numpy()
+    done = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            b = reqs[done % len(reqs)]
+            t = (done // len(reqs)) % q64.shape[0]
+            cb, off, ids = index[b]
+            ivf.sparse_decode(q64[t, b:b + 1], cb, off, ids, K[b], V[b], cfg.top_k)
+            done += 1
+        el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} whole decode queries (all {cfg.n_q_heads} heads) of requests {reqs} "
+                      f"over {el:.1f} s, fp64 numpy, one BLAS thread; index built untimed"}
+
+
+# ----------------------------------------------------------------------------
+# token-indexer workload
+# ----------------------------------------------------------------------------
+
+def bench_token(args, cfg, torch, tsa, W):
+    dev = "cuda"
+    B, Hq, k = cfg.batch, cfg.n_q_heads, cfg.top_k
+    log(f"generating {cfg.name} on the GPU")
+    prob = W.token_problem(cfg, device=dev)
+    nq = min(cfg.steps, 64)
+    q_idx, q = W.token_queries(cfg, prob, steps=nq)
+    out = torch.empty((B, Hq, cfg.head_dim), dtype=torch.float32, device=dev)
+    desc = tsa.binding.token_desc(prob["k_idx"], prob["keys"], Hq)
+    ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_TOKEN_DECODE, desc, k), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        if ev is not None:
+            tsa.time_next_gather(*ev)
+        tsa.token_decode(q_idx[i % nq], prob["k_idx"], q[i % nq], prob["keys"], prob["values"], k,
+                         out=out, ws=ws)
+
+    res = _timed(args, step, torch)
+    res["gathered_bytes"] = args.steps * B * cfg.n_kv_heads * k * ROW_BYTES_BF16
+    res["queries"] = B * args.steps
+    res["indexer_bytes_per_step"] = B * cfg.n_tokens * cfg.idx_dim * 2
+    return res
+
+
+# ----------------------------------------------------------------------------
+# hierarchical-cache workload
+# ----------------------------------------------------------------------------
+
+def bench_cache(args, cfg, torch, tsa, W):
+    dev = "cuda"
+    B, N, S, Hkv, Hq, d, k = (cfg.batch, cfg.n_tokens, cfg.n_slots, cfg.n_kv_heads, cfg.n_q_heads,
+                              cfg.head_dim, cfg.top_k)
+    steps = args.warmup + args.steps
+    log(f"generating {cfg.name}: full KV into pinned host memory")
+    cfg_t = cfg.replace(steps=steps)
+    prob = W.cache_problem(cfg_t, device=dev)
+    hk = tsa.HostArray((B, N, Hkv, d), cfg.torch_dtype)
+    hv = tsa.HostArray((B, N, Hkv, d), cfg.torch_dtype)
+    hk.tensor.copy_(prob["keys"])
+    hv.tensor.copy_(prob["values"])
+    del prob["keys"], prob["values"]
+    pt = torch.empty((B, N), dtype=torch.int32, device=dev)
+    st = torch.empty((B, S), dtype=torch.int32, device=dev)
+    lu = torch.empty((B, S), dtype=torch.int32, device=dev)
+    tsa.cache_reset(pt, st, lu)
+    pool_k = torch.zeros((B, S, Hkv, d), dtype=cfg.torch_dtype, device=dev)
+    pool_v = torch.zeros_like(pool_k)
+    trace = prob["trace"].to(dev)
+    q = prob["q"]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    slots = torch.empty((B, k), dtype=torch.int32, device=dev)
+    hits = torch.empty((steps, B), dtype=torch.int32, device=dev)
+    misses = torch.empty((steps, B), dtype=torch.int32, device=dev)
+    desc = tsa.binding.attn_desc(pool_k, Hq, k)
+    ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_ATTEND_ROWS, desc), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        tsa.resolve(pt, st, lu, trace[i], i, hk.tensor, hv.tensor, pool_k, pool_v, slots_out=slots,
+                    hits=hits[i], misses=misses[i])
+        if ev is not None:
+            tsa.time_next_gather(*ev)
+        tsa.attend_rows(q[i], pool_k, pool_v, slots, out=out, ws=ws)
+
+    res = _timed(args, step, torch, offset=args.warmup)
+    res["gathered_bytes"] = args.steps * B * Hkv * k * ROW_BYTES_BF16
+    res["queries"] = B * args.steps
+    m = misses.cpu()
+    res["misses_per_step"] = m.sum(dim=1).tolist()
+    res["miss_rate_steady"] = float(m[args.warmup:].double().mean() / k)
+    res["fetched_bytes"] = float(m[args.warmup:].double().sum()) * Hkv * d * 2 * 2
+    return res
+
+
+def _timed(args, step, torch, offset=0):
+    for i in range(args.warmup):
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i + offset if offset else i, evs[i])
+    t_stop.record()
+    torch.cuda.synchronize()
+    return {"ms_total": t_start.elapsed_time(t_stop), "wall_s": time.perf_counter() - wall0,
+            "gather_ms": [a.elapsed_time(b) for a, b in evs]}
+
+
+# ----------------------------------------------------------------------------
+
+def calibrate_copy(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                      "gbps_read_plus_write": 2 * n / ms / 1e6}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported by this build "
+              "(the decode path shards by request; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+    import top_sparse_attention_centroid_amd as tsa
+    from top_sparse_attention_centroid_amd import workloads as W
+
+    tsa.load()
+    cfg = W.config(args.config)
+    kind = {"ivf": bench_ivf, "token": bench_token, "cache": bench_cache}[cfg.kind]
+    res = kind(args, cfg, torch, tsa, W)
+
+    K = args.steps
+    ms_step = res["ms_total"] / K
+    value = res["queries"] / (res["ms_total"] / 1e3)
+    gb_s = res["gathered_bytes"] / (res["ms_total"] / 1e3) / 1e9
+    g_ms = res["gather_ms"]
+    g_mean_ms = sum(g_ms) / len(g_ms)
+    bytes_per_launch = res["gathered_bytes"] / K
+    achieved = bytes_per_launch / (g_mean_ms / 1e3) / 1e9
+    traffic = measured_traffic(cfg.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "storage_dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "context": cfg.n_tokens,
+                   "kv_heads": cfg.n_kv_heads, "q_heads": cfg.n_q_heads, "head_dim": cfg.head_dim,
+                   "top_k": cfg.top_k, "centroids": cfg.n_centroids or None,
+                   "slots": cfg.n_slots or None, "parallelism": "none (1 GPU)"},
+        "gathered_kv_gbps": round(gb_s, 1),
+        "gathered_kv_frac_of_peak": round(gb_s / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "gather_attn", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": round(bytes_per_launch),
+                     "mean_launch_us": round(g_mean_ms * 1e3, 2)},
+        "cpu_baseline": res.get("cpu"),
+    }
+    for key in ("index_build_ms", "unique_rows_per_step", "misses_per_step", "miss_rate_steady",
+                "fetched_bytes", "indexer_bytes_per_step"):
+        if key in res:
+            line[key] = res[key]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

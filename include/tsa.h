@@ -1,0 +1,271 @@
+/*
+ * tsa.h - retrieval-based sparse-attention decode for AMD Instinct MI355X
+ * (gfx950). C ABI: plain integers and pointers only.
+ *
+ * Pages the operations come from (cited by title and section):
+ *   [KARAT]  paper-daily digest "Heterogeneous LLM Serving with
+ *            General-Purpose Processing-Near-Memory for Retrieval-Based
+ *            Sparse Attention": How (index structure), core formulas (Eq. 2),
+ *            worked example (steps 3-4).
+ *   [HISPARSE-NEWS]  "KV卸载上主机:HiSparse、PDD与DDR4回收", paper analysis 1
+ *            (HiSparse): hot cache of B slots per request per layer, page
+ *            table + LRU, one fused RESOLVE kernel, authoritative KV in pinned
+ *            host memory, exactness.
+ *   [HISPARSE-NOTES] "10月14日学习笔记", HiSparse (indexer top-k selection,
+ *            LRU for the locality of consecutive selections).
+ *
+ * Conventions shared by every entry point
+ *   - Memory: every array argument is caller-owned. Pointers marked (device)
+ *     are device memory of the current HIP device; (host-mapped) is pinned
+ *     host memory the device can read (tsa_host_alloc). The library keeps no
+ *     pointer after a call returns and allocates nothing inside a call.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream). Every kernel of a call is enqueued on it; the call returns
+ *     without synchronising and results are valid once the stream reaches
+ *     them. No call records a memset or a host synchronisation, so calls can
+ *     be captured into a HIP graph.
+ *   - Layouts are dense and row-major, innermost index last. A "row" is one
+ *     token's head_dim elements for one KV head. K and V caches are
+ *     [batch][n_rows][n_kv_heads][head_dim]: the rows of one token for all KV
+ *     heads are contiguous. Query head h reads KV head h / (n_q_heads /
+ *     n_kv_heads).
+ *   - Element types: tsa_dtype selects fp32 or bf16 (bfloat16 bit patterns in
+ *     uint16). Arithmetic is fp32 (products of bf16 inputs, fp32 sums);
+ *     attention outputs are fp32.
+ *   - Workspace: ops that need scratch take (ws, ws_bytes); the size comes
+ *     from tsa_workspace_bytes for the same descriptor and k. It must be
+ *     16-byte aligned. Its contents need no initialisation and are
+ *     meaningless between calls.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; a failing call enqueues nothing and writes no output.
+ *     TSA_ERR_INVALID_ARG: null pointer, non-positive size, k out of range,
+ *     misaligned pointer. TSA_ERR_UNSUPPORTED: a shape this build does not
+ *     implement (head_dim != 128, idx_dim != 64, n_q_heads / n_kv_heads not
+ *     in {1,2,4,8}, sizes beyond the limits stated per call).
+ *     TSA_ERR_WORKSPACE: ws_bytes too small. TSA_ERR_HIP: a HIP launch
+ *     failed. tsa_last_error() returns this thread's last message.
+ *   - Tie rule for every top-k: the larger score wins, equal scores go to the
+ *     lower index, and selections are written in ascending index order.
+ */
+#ifndef TSA_H
+#define TSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TSA_ABI_VERSION 1
+
+typedef enum tsa_status {
+  TSA_OK = 0,
+  TSA_ERR_INVALID_ARG = 1,
+  TSA_ERR_UNSUPPORTED = 2,
+  TSA_ERR_WORKSPACE = 3,
+  TSA_ERR_HIP = 4
+} tsa_status;
+
+typedef enum tsa_dtype { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
+
+/* Workspace-sized operations, for tsa_workspace_bytes. */
+typedef enum tsa_op {
+  TSA_OP_INDEX_BUILD = 0,
+  TSA_OP_SPARSE_DECODE = 1,
+  TSA_OP_TOKEN_DECODE = 2,
+  TSA_OP_ATTEND_ROWS = 3
+} tsa_op;
+
+/* Inverted-index (centroid) problem. */
+typedef struct tsa_ivf_desc {
+  int32_t batch;           /* B requests                                   */
+  int32_t n_tokens;        /* N cached tokens per request                  */
+  int32_t n_kv_heads;      /* Hkv                                          */
+  int32_t n_q_heads;       /* Hq; Hq / Hkv in {1, 2, 4, 8}                 */
+  int32_t head_dim;        /* d; must be 128                               */
+  int32_t n_centroids;     /* C lists per (request, KV head); C <= 4096 and
+                              C * (Hq / Hkv + 1) <= 16384                  */
+  int32_t shared_codebook; /* 1: centroids [Hkv][C][d] for all requests;
+                              0: centroids [B][Hkv][C][d]                 */
+  int32_t dtype;           /* tsa_dtype of q, keys, values, centroids     */
+} tsa_ivf_desc;
+
+/* Token-indexer (DSA-style) problem. */
+typedef struct tsa_token_desc {
+  int32_t batch;       /* B                                    */
+  int32_t n_tokens;    /* N                                    */
+  int32_t n_kv_heads;  /* Hkv                                  */
+  int32_t n_q_heads;   /* Hq                                   */
+  int32_t head_dim;    /* d = 128                              */
+  int32_t idx_dim;     /* indexer key width; must be 64        */
+  int32_t dtype;       /* tsa_dtype of all inputs              */
+} tsa_token_desc;
+
+/* Hot-cache (HiSparse-style) problem: one layer. */
+typedef struct tsa_cache_desc {
+  int32_t batch;       /* B requests                                       */
+  int32_t n_tokens;    /* N tokens in each request's host copy             */
+  int32_t n_slots;     /* S hot slots per request; <= 4096                 */
+  int32_t n_kv_heads;  /* Hkv                                              */
+  int32_t head_dim;    /* d = 128                                          */
+  int32_t dtype;       /* tsa_dtype of the K/V rows                        */
+} tsa_cache_desc;
+
+/* Attention over explicit per-request row lists shared by all heads. */
+typedef struct tsa_attn_desc {
+  int32_t batch;       /* B                                                */
+  int32_t n_rows;      /* rows addressable per request in k/v (N, or S)    */
+  int32_t n_kv_heads;  /* Hkv                                              */
+  int32_t n_q_heads;   /* Hq                                               */
+  int32_t head_dim;    /* d = 128                                          */
+  int32_t max_rows;    /* capacity of each request's row list              */
+  int32_t dtype;       /* tsa_dtype of q, k, v                             */
+} tsa_attn_desc;
+
+/* ------------------------------------------------------------------------
+ * tsa_index_build - posting lists of an inverted index.
+ *   [KARAT] How, index structure: each KV entry goes to a posting list by
+ *   its key. Reading: every key joins exactly one list, that of its nearest
+ *   centroid by squared Euclidean distance (ties -> lower centroid id).
+ *   keys       (device) [B][N][Hkv][d], the K cache itself.
+ *   centroids  (device) [Hkv][C][d] shared, or [B][Hkv][C][d].
+ *   offsets    (device, out) int32 [B][Hkv][C+1]: list c of (b, g) holds
+ *              ids[b][g][offsets[b][g][c] .. offsets[b][g][c+1]).
+ *   ids        (device, out) int32 [B][Hkv][N]: token ids, ascending within
+ *              each list.
+ *   Workspace: tsa_workspace_bytes(TSA_OP_INDEX_BUILD, desc, 0, ...).
+ *   Distances are computed in fp32; they decide the same list as exact
+ *   arithmetic whenever the nearest and second-nearest squared distances
+ *   differ by more than fp32 rounding.
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_index_build(const tsa_ivf_desc* desc, const void* keys, const void* centroids,
+                           int32_t* offsets, int32_t* ids, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * tsa_sparse_decode - one decode step of retrieval-based sparse attention.
+ *   [KARAT] worked example steps 3-4 and Eq. 2: score q against every
+ *   centroid of its KV head (raw dot product), keep the k best lists, gather
+ *   the K/V rows of those lists and attend over them only:
+ *     out[b][h] = sum_{i in R} softmax_i(q.K_i / sqrt(d)) V_i,
+ *     R = union of the k chosen lists of (b, h).
+ *   q          (device) [B][Hq][d]
+ *   centroids  (device) as for tsa_index_build
+ *   offsets, ids (device) posting lists from tsa_index_build
+ *   k_cache, v_cache (device) [B][N][Hkv][d]
+ *   k          lists per query head, 1 <= k <= C
+ *   out        (device, out) fp32 [B][Hq][d]; zero where R is empty
+ *   sel_out    (device, out, nullable) int32 [B][Hq][k]: chosen lists,
+ *              ascending
+ *   rows_out   (device, out, nullable) int32 [B][Hq]: |R| per head (0 flags
+ *              an empty set)
+ *   uniq_out   (device, out, nullable) int32 [B][Hkv]: rows read once for the
+ *              whole KV group (the union over its query heads' lists)
+ *   Workspace: tsa_workspace_bytes(TSA_OP_SPARSE_DECODE, desc, k, ...).
+ *   Scores are fp32; the chosen lists equal the exact top-k whenever the
+ *   k-th and (k+1)-th scores differ by more than fp32 rounding.
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void* centroids,
+                             const int32_t* offsets, const int32_t* ids, const void* k_cache,
+                             const void* v_cache, int32_t k, float* out, int32_t* sel_out,
+                             int32_t* rows_out, int32_t* uniq_out, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
+ * tsa_token_decode - token-level indexer top-k and attention (DSA style).
+ *   [HISPARSE-NOTES] motivation (an indexer picks the top-k tokens, O(k)
+ *   work per step); [HISPARSE-NEWS] the selector states the positions each
+ *   step needs; [KARAT] Eq. 2 over that set.
+ *   score_i = q_idx[b] . k_idx[b][i]; the k best tokens of request b are
+ *   attended by all its query heads.
+ *   q_idx  (device) [B][idx_dim];  k_idx (device) [B][N][idx_dim]
+ *   q      (device) [B][Hq][d];    k_cache, v_cache (device) [B][N][Hkv][d]
+ *   k      1 <= k <= N, k <= 4096; N * k <= 2^30
+ *   out    (device, out) fp32 [B][Hq][d]
+ *   sel_out (device, out, nullable) int32 [B][k], ascending token ids
+ *   Workspace: tsa_workspace_bytes(TSA_OP_TOKEN_DECODE, desc, k, ...).
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const void* k_idx,
+                            const void* q, const void* k_cache, const void* v_cache, int32_t k,
+                            float* out, int32_t* sel_out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * tsa_resolve - one fused RESOLVE step of the hot cache, all requests.
+ *   [HISPARSE-NEWS] paper analysis 1: hit detection, LRU replacement,
+ *   metadata update and host fetch in one kernel.
+ *   Batch-step LRU (the page leaves the order inside a step open):
+ *     hits   = selected tokens with page_table >= 0; their slots' last_use
+ *              becomes `step` (protected from eviction in this step);
+ *     misses = the other selected tokens, in the order given (ascending);
+ *     victims = slots with last_use < step ordered by (last_use, slot),
+ *              free slots (-1) first; the r-th miss takes the r-th victim:
+ *              its old token leaves the page table, page_table[miss] = slot,
+ *              slot_token[slot] = miss, last_use[slot] = step, and the
+ *              token's K and V rows for every KV head are copied from the
+ *              host copy into the slot.
+ *   page_table (device, in/out) int32 [B][N]   slot or -1
+ *   slot_token (device, in/out) int32 [B][S]   token or -1
+ *   last_use   (device, in/out) int32 [B][S]   step or -1
+ *   sel        (device) int32 [B][k]: strictly ascending token ids in [0, N)
+ *   k          1 <= k <= min(S, 4096)
+ *   step       stamp of this step; larger than every stamp already stored
+ *   host_k, host_v (host-mapped) [B][N][Hkv][d]: the authoritative copy
+ *   pool_k, pool_v (device, in/out) [B][S][Hkv][d]: the hot slots
+ *   slots_out  (device, out) int32 [B][k]: slot holding sel[b][i]
+ *   hits, misses (device, out, nullable) int32 [B]
+ *   No workspace. Contract violations (unsorted or repeated sel, stale
+ *   step) give an undefined but in-bounds cache state.
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_resolve(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,
+                       int32_t* last_use, const int32_t* sel, int32_t k, int32_t step,
+                       const void* host_k, const void* host_v, void* pool_k, void* pool_v,
+                       int32_t* slots_out, int32_t* hits, int32_t* misses, void* stream);
+
+/* tsa_cache_reset - mark every page-table entry and slot empty (-1), so the
+ * next step misses every selected token ([HISPARSE-NEWS]: the hot cache is
+ * disposable, the host copy is authoritative). Uses a fill kernel. */
+tsa_status tsa_cache_reset(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,
+                           int32_t* last_use, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tsa_attend_rows - attention of every query head over a per-request row
+ *   list shared by all heads ([KARAT] Eq. 2; with slot ids it is the
+ *   attention over the hot cache, [HISPARSE-NEWS]).
+ *   q        (device) [B][Hq][d]
+ *   k_rows, v_rows (device) [B][n_rows][Hkv][d]
+ *   row_ids  (device) int32 [B][max_rows], entries in [0, n_rows)
+ *   row_counts (device, nullable) int32 [B] rows used per request, each in
+ *            [0, max_rows]; NULL means max_rows for every request
+ *   out      (device, out) fp32 [B][Hq][d]; zero for an empty list
+ *   Workspace: tsa_workspace_bytes(TSA_OP_ATTEND_ROWS, desc, 0, ...).
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_attend_rows(const tsa_attn_desc* desc, const void* q, const void* k_rows,
+                           const void* v_rows, const int32_t* row_ids, const int32_t* row_counts,
+                           float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for `op` with `desc` (the struct matching the op) and k. */
+tsa_status tsa_workspace_bytes(int32_t op, const void* desc, int32_t k, size_t* bytes);
+
+/* Pinned, device-mapped host memory for the authoritative KV copy
+ * ([HISPARSE-NEWS]: full KV in pinned host memory). tsa_host_alloc returns
+ * the host pointer, which the device may read directly. Set-up calls: they
+ * allocate and are not for use inside a decode step. */
+tsa_status tsa_host_alloc(size_t bytes, void** host_ptr);
+tsa_status tsa_host_free(void* host_ptr);
+
+/* Timing hook: arm (ev_start, ev_stop), two hipEvent_t as void*, to be
+ * recorded on the call's stream immediately before and after the next
+ * gather-attention kernel launched by this thread. One-shot. */
+tsa_status tsa_time_next_gather(void* ev_start, void* ev_stop);
+
+const char* tsa_status_str(tsa_status s);
+const char* tsa_last_error(void);
+int32_t tsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSA_H */

@@ -68,11 +68,16 @@ def _f64(x) -> np.ndarray:
 # Index build
 # ----------------------------------------------------------------------------
 
-def nearest_centroid(keys, centroids, chunk: int = 64):
+def nearest_centroid(keys, centroids, chunk: int = 4096):
     """Nearest centroid of every key by squared Euclidean distance.
 
     [KARAT] How, index structure (entries go to lists by their key); reading:
     single assignment to the nearest centroid, ties -> lower centroid index.
+
+    The squared distance |k - c|^2 is evaluated as |k|^2 - 2 k.c + |c|^2 with
+    the k.c block as one fp64 matrix product (the same quantity; fp64 keeps
+    the expansion's rounding near 1e-14 of |k|^2, far inside any margin the
+    workloads use).
 
     keys [n][d], centroids [C][d]. Returns (assign [n] int64, margin [n]) where
     margin = (d2_second - d2_best) / d2_best, the relative distance gap that
@@ -83,9 +88,11 @@ def nearest_centroid(keys, centroids, chunk: int = 64):
     n = K.shape[0]
     assign = np.empty(n, dtype=np.int64)
     margin = np.empty(n, dtype=np.float64)
+    c2 = np.sum(Cn * Cn, axis=1)
     for s in range(0, n, chunk):
-        diff = K[s:s + chunk, None, :] - Cn[None, :, :]          # [m][C][d]
-        d2 = np.sum(diff * diff, axis=2)                          # [m][C]
+        Kc = K[s:s + chunk]
+        d2 = np.sum(Kc * Kc, axis=1)[:, None] - 2.0 * (Kc @ Cn.T) + c2[None, :]   # [m][C]
+        d2 = np.maximum(d2, 0.0)
         best = np.argmin(d2, axis=1)                              # first minimum
         assign[s:s + chunk] = best
         if Cn.shape[0] > 1:

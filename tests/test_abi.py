@@ -1,0 +1,126 @@
+"""The C-ABI library: it loads, exports every symbol include/tsa.h declares, and
+rejects bad arguments on the host before touching a device (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from top_sparse_attention_centroid_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.lib_path()):
+        from top_sparse_attention_centroid_amd import build
+        build.build()
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("tsa_index_build", "tsa_sparse_decode", "tsa_token_decode", "tsa_resolve",
+              "tsa_attend_rows", "tsa_cache_reset", "tsa_workspace_bytes", "tsa_status_str",
+              "tsa_last_error", "tsa_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tsa_abi_version() == 1
+    assert lib.tsa_status_str(B.TSA_ERR_WORKSPACE) == b"TSA_ERR_WORKSPACE"
+    assert lib.tsa_status_str(99) == b"TSA_ERR_UNKNOWN"
+
+
+def _status(lib, fn, *args):
+    return getattr(lib, fn)(*args)
+
+
+def test_workspace_sizes_and_validation(lib):
+    d = B.IvfDesc(64, 32768, 8, 32, 128, 256, 1, B.TSA_BF16)
+    n = B.workspace_bytes(B.OP_SPARSE_DECODE, d, 16)
+    G, smax = 4, 4 * 16 + 32768 // 256
+    assert n >= 64 * 8 * smax * G * 132 * 4
+    assert B.workspace_bytes(B.OP_INDEX_BUILD, d) >= 64 * 8 * 32768 * 4
+    with pytest.raises(B.TsaError, match="INVALID_ARG"):
+        B.workspace_bytes(B.OP_SPARSE_DECODE, d, 0)
+    with pytest.raises(B.TsaError, match="INVALID_ARG"):
+        B.workspace_bytes(B.OP_SPARSE_DECODE, d, 257)
+    for bad, code in ((B.IvfDesc(1, 10, 8, 32, 64, 16, 1, 1), "UNSUPPORTED"),    # d != 128
+                      (B.IvfDesc(1, 10, 8, 24, 128, 16, 1, 1), "UNSUPPORTED"),   # G = 3
+                      (B.IvfDesc(1, 10, 8, 32, 128, 5000, 1, 1), "UNSUPPORTED"), # C too big
+                      (B.IvfDesc(1, 10, 8, 32, 128, 16, 1, 7), "UNSUPPORTED"),   # dtype
+                      (B.IvfDesc(0, 10, 8, 32, 128, 16, 1, 1), "INVALID_ARG")):
+        with pytest.raises(B.TsaError, match=code):
+            B.workspace_bytes(B.OP_SPARSE_DECODE, bad, 4)
+    t = B.TokenDesc(16, 200_000, 8, 32, 128, 64, B.TSA_BF16)
+    assert B.workspace_bytes(B.OP_TOKEN_DECODE, t, 2048) > 0
+    with pytest.raises(B.TsaError, match="UNSUPPORTED"):
+        B.workspace_bytes(B.OP_TOKEN_DECODE, B.TokenDesc(1, 1000, 8, 32, 128, 32, 1), 10)
+    with pytest.raises(B.TsaError, match="UNSUPPORTED"):   # too many merge candidates
+        B.workspace_bytes(B.OP_TOKEN_DECODE, B.TokenDesc(1, 2_000_000, 8, 32, 128, 64, 1), 4096)
+    a = B.AttnDesc(32, 4096, 8, 32, 128, 2048, B.TSA_BF16)
+    assert B.workspace_bytes(B.OP_ATTEND_ROWS, a) == 32 * 8 * 8 * 4 * 132 * 4
+
+
+def test_calls_reject_bad_arguments_before_any_launch(lib):
+    d = B.IvfDesc(2, 100, 2, 8, 128, 8, 1, B.TSA_BF16)
+    fake = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x10001)
+    args = [ctypes.byref(d), fake, fake, fake, fake, fake, fake]
+    ws_need = B.workspace_bytes(B.OP_SPARSE_DECODE, d, 4)
+    # null q
+    st = lib.tsa_sparse_decode(ctypes.byref(d), None, fake, fake, fake, fake, fake, 4, fake, None, None,
+                               None, fake, ws_need, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"q is NULL" in lib.tsa_last_error()
+    # misaligned k_cache
+    st = lib.tsa_sparse_decode(ctypes.byref(d), fake, fake, fake, fake, odd, fake, 4, fake, None, None,
+                               None, fake, ws_need, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"aligned" in lib.tsa_last_error()
+    # k out of range
+    st = lib.tsa_sparse_decode(*args, 9, fake, None, None, None, fake, ws_need, None)
+    assert st == B.TSA_ERR_INVALID_ARG
+    # workspace too small
+    st = lib.tsa_sparse_decode(*args, 4, fake, None, None, None, fake, ws_need - 1, None)
+    assert st == B.TSA_ERR_WORKSPACE
+    # resolve: k larger than the slot pool, too many slots
+    c = B.CacheDesc(2, 1000, 64, 8, 128, B.TSA_BF16)
+    st = lib.tsa_resolve(ctypes.byref(c), fake, fake, fake, fake, 65, 0, fake, fake, fake, fake, fake,
+                         None, None, None)
+    assert st == B.TSA_ERR_INVALID_ARG
+    c2 = B.CacheDesc(2, 10000, 8192, 8, 128, B.TSA_BF16)
+    st = lib.tsa_resolve(ctypes.byref(c2), fake, fake, fake, fake, 16, 0, fake, fake, fake, fake, fake,
+                         None, None, None)
+    assert st == B.TSA_ERR_UNSUPPORTED
+    st = lib.tsa_resolve(ctypes.byref(c), fake, fake, fake, fake, 16, -1, fake, fake, fake, fake, fake,
+                         None, None, None)
+    assert st == B.TSA_ERR_INVALID_ARG
+    # token decode: k > N
+    t = B.TokenDesc(1, 100, 8, 32, 128, 64, B.TSA_BF16)
+    st = lib.tsa_token_decode(ctypes.byref(t), fake, fake, fake, fake, fake, 101, fake, None, fake, 1 << 30, None)
+    assert st == B.TSA_ERR_INVALID_ARG
+    # timing hook needs both events
+    assert lib.tsa_time_next_gather(fake, None) == B.TSA_ERR_INVALID_ARG
+    assert lib.tsa_time_next_gather(None, None) == B.TSA_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros((1, 4, 1, 128), dtype=torch.bfloat16)
+    c = torch.zeros((1, 1, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        B.index_build(x, c)

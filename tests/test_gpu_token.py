@@ -1,0 +1,70 @@
+"""GPU parity of the token-indexer path (indexer scan, exact top-k over all
+tokens, attention over the selection) against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import top_sparse_attention_centroid_amd as tsa
+from oracle import token
+from top_sparse_attention_centroid_amd import workloads as W
+
+from helpers import GAP_MIN, OUT_TOL, announce, condition_token_keys, f64, out_error
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(cfg, steps, check_requests, attn_requests):
+    prob = W.token_problem(cfg, device=DEV)
+    q_idx, q = W.token_queries(cfg, prob, steps=steps)
+    k_idx = condition_token_keys(q_idx, prob["k_idx"], cfg.top_k, steps, requests=check_requests)
+    torch.cuda.synchronize()
+    B, k = cfg.batch, cfg.top_k
+    sel = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    kidx64 = {b: f64(k_idx[b]) for b in check_requests}
+    K64 = {b: f64(prob["keys"][b]) for b in attn_requests}
+    V64 = {b: f64(prob["values"][b]) for b in attn_requests}
+    for t in range(steps):
+        out = tsa.token_decode(q_idx[t], k_idx, q[t], prob["keys"], prob["values"], k, sel_out=sel)
+        torch.cuda.synchronize()
+        sel_g, out_g = sel.cpu().numpy(), out.cpu().numpy()
+        qi64, q64 = f64(q_idx[t]), f64(q[t])
+        for b in check_requests:
+            ref_sel, gap = token.token_topk(qi64[b], kidx64[b], k)
+            assert gap >= GAP_MIN
+            assert np.array_equal(sel_g[b], ref_sel), f"selection differs (step {t}, request {b})"
+            assert set(prob["planted"][b].tolist()) <= set(sel_g[b].tolist())
+            if b in attn_requests:
+                r = token.token_decode(qi64[b:b + 1], kidx64[b][None], q64[b:b + 1], K64[b][None],
+                                       V64[b][None], k)
+                err = out_error(out_g[b], r["out"][0])
+                assert err <= OUT_TOL, f"output error {err} (step {t}, request {b})"
+
+
+def test_token_topk_small():
+    cfg = W.config(3, batch=3, n_tokens=20_001, top_k=1000, n_planted=64, steps=2)
+    announce("token small N=20001 k=1000")
+    _run(cfg, 2, range(3), range(3))
+
+
+def test_token_topk_single_chunk_and_k_equals_n():
+    # one chunk shorter than k, and a selection of every token (dense attention)
+    cfg = W.config(3, batch=2, n_tokens=1500, top_k=1500, n_planted=8, steps=1)
+    announce("token k == N")
+    _run(cfg, 1, range(2), range(2))
+
+
+def test_token_topk_ragged_gqa():
+    cfg = W.config(3, batch=2, n_tokens=8193 * 2 + 7, top_k=333, n_planted=16, steps=2,
+                   n_kv_heads=2, n_q_heads=16)
+    announce("token ragged G=8")
+    _run(cfg, 2, range(2), range(2))
+
+
+def test_token_workload_full_size_sampled():
+    """16 requests x 200,000 tokens, top-2048: selections of every request are
+    checked; attention outputs of two requests."""
+    cfg = W.config(3)
+    announce(f"token {cfg.name} full size")
+    _run(cfg, 2, range(cfg.batch), [0, 9])

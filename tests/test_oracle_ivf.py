@@ -30,7 +30,7 @@ def test_keys_on_centroids_land_in_their_own_list():
     perm = rng.integers(0, C, size=200)
     a, margin = ivf.nearest_centroid(cent[perm], cent)
     assert np.array_equal(a, perm)
-    assert np.all(np.isinf(margin))
+    assert np.all(margin > 1e10)  # the key sits on its centroid: relative gap unbounded
 
 
 def test_perturbed_keys_keep_their_centroid():

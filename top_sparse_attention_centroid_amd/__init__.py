@@ -1,0 +1,30 @@
+"""Retrieval-based sparse-attention decode for AMD Instinct MI355X (gfx950).
+
+The compute path is libtsa.so (hand-written HIP kernels behind the C ABI in
+include/tsa.h); this package is its thin Python binding plus the seeded
+synthetic workload generators. The library is loaded on first use and any
+entry point raises ImportError when it has not been built.
+"""
+
+from . import workloads  # noqa: F401
+from .binding import (  # noqa: F401
+    HostArray,
+    TsaError,
+    abi_version,
+    attend_rows,
+    cache_reset,
+    index_build,
+    lib_path,
+    load,
+    resolve,
+    sparse_decode,
+    time_next_gather,
+    token_decode,
+    workspace_bytes,
+)
+
+__all__ = [
+    "workloads", "load", "lib_path", "abi_version", "index_build", "sparse_decode", "token_decode",
+    "attend_rows", "resolve", "cache_reset", "HostArray", "time_next_gather", "workspace_bytes",
+    "TsaError",
+]

@@ -1,0 +1,342 @@
+"""ctypes binding over libtsa.so (include/tsa.h). Argument marshalling only:
+torch supplies device memory and the current stream; every step of the decode
+path runs in the library's HIP kernels. Loading fails loudly when the library
+has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsa.so")
+
+TSA_OK, TSA_ERR_INVALID_ARG, TSA_ERR_UNSUPPORTED, TSA_ERR_WORKSPACE, TSA_ERR_HIP = range(5)
+TSA_F32, TSA_BF16 = 0, 1
+OP_INDEX_BUILD, OP_SPARSE_DECODE, OP_TOKEN_DECODE, OP_ATTEND_ROWS = range(4)
+
+_I32 = ctypes.c_int32
+_P = ctypes.c_void_p
+
+
+class IvfDesc(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("n_tokens", _I32), ("n_kv_heads", _I32), ("n_q_heads", _I32),
+                ("head_dim", _I32), ("n_centroids", _I32), ("shared_codebook", _I32), ("dtype", _I32)]
+
+
+class TokenDesc(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("n_tokens", _I32), ("n_kv_heads", _I32), ("n_q_heads", _I32),
+                ("head_dim", _I32), ("idx_dim", _I32), ("dtype", _I32)]
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("n_tokens", _I32), ("n_slots", _I32), ("n_kv_heads", _I32),
+                ("head_dim", _I32), ("dtype", _I32)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("n_rows", _I32), ("n_kv_heads", _I32), ("n_q_heads", _I32),
+                ("head_dim", _I32), ("max_rows", _I32), ("dtype", _I32)]
+
+
+# name -> argument types (all return tsa_status except where noted)
+_SIGNATURES = {
+    "tsa_index_build": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_sparse_decode": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
+                          ctypes.c_size_t, _P],
+    "tsa_token_decode": [ctypes.POINTER(TokenDesc), _P, _P, _P, _P, _P, _I32, _P, _P, _P,
+                         ctypes.c_size_t, _P],
+    "tsa_resolve": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P],
+    "tsa_cache_reset": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P],
+    "tsa_attend_rows": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_workspace_bytes": [_I32, _P, _I32, ctypes.POINTER(ctypes.c_size_t)],
+    "tsa_host_alloc": [ctypes.c_size_t, ctypes.POINTER(_P)],
+    "tsa_host_free": [_P],
+    "tsa_time_next_gather": [_P, _P],
+}
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libtsa.so (once). Raises ImportError when it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python -m top_sparse_attention_centroid_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, args in _SIGNATURES.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = _I32
+    lib.tsa_status_str.argtypes = [_I32]
+    lib.tsa_status_str.restype = ctypes.c_char_p
+    lib.tsa_last_error.argtypes = []
+    lib.tsa_last_error.restype = ctypes.c_char_p
+    lib.tsa_abi_version.argtypes = []
+    lib.tsa_abi_version.restype = _I32
+    _lib = lib
+    return lib
+
+
+class TsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{load().tsa_status_str(status).decode()}: {msg}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != TSA_OK:
+        raise TsaError(status, load().tsa_last_error().decode())
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return TSA_F32
+    if t == torch.bfloat16:
+        return TSA_BF16
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libtsa must be contiguous")
+    return t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _i32(t: Optional[torch.Tensor], name: str, shape):
+    if t is None:
+        return
+    if t.dtype != torch.int32 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be int32 {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def workspace_bytes(op: int, desc, k: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(load().tsa_workspace_bytes(op, ctypes.cast(ctypes.pointer(desc), _P), k, ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(op, desc, k, ws, device) -> torch.Tensor:
+    need = workspace_bytes(op, desc, k)
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace has {ws.numel() * ws.element_size()} bytes, needs {need}")
+    return ws
+
+
+# ----------------------------------------------------------------------------
+# descriptors
+# ----------------------------------------------------------------------------
+
+def ivf_desc(keys: torch.Tensor, centroids: torch.Tensor, n_q_heads: int) -> IvfDesc:
+    B, N, Hkv, d = keys.shape
+    Bc, Hkv2, C, d2 = centroids.shape
+    if Hkv2 != Hkv or d2 != d or Bc not in (1, B):
+        raise ValueError(f"centroids {tuple(centroids.shape)} do not match keys {tuple(keys.shape)}")
+    return IvfDesc(B, N, Hkv, n_q_heads, d, C, 1 if Bc == 1 else 0, _dtype_code(keys.dtype))
+
+
+def token_desc(k_idx: torch.Tensor, k_cache: torch.Tensor, n_q_heads: int) -> TokenDesc:
+    B, N, Hkv, d = k_cache.shape
+    if tuple(k_idx.shape[:2]) != (B, N):
+        raise ValueError("k_idx and k_cache disagree on batch / tokens")
+    return TokenDesc(B, N, Hkv, n_q_heads, d, k_idx.shape[2], _dtype_code(k_cache.dtype))
+
+
+def cache_desc(host_k: torch.Tensor, n_slots: int) -> CacheDesc:
+    B, N, Hkv, d = host_k.shape
+    return CacheDesc(B, N, n_slots, Hkv, d, _dtype_code(host_k.dtype))
+
+
+def attn_desc(k_rows: torch.Tensor, n_q_heads: int, max_rows: int) -> AttnDesc:
+    B, R, Hkv, d = k_rows.shape
+    return AttnDesc(B, R, Hkv, n_q_heads, d, max_rows, _dtype_code(k_rows.dtype))
+
+
+# ----------------------------------------------------------------------------
+# entry points (same names as the C ABI, without the tsa_ prefix)
+# ----------------------------------------------------------------------------
+
+def index_build(keys, centroids, *, offsets=None, ids=None, ws=None, stream=None):
+    """Posting lists of the K cache: returns (offsets [B][Hkv][C+1], ids [B][Hkv][N])."""
+    _dev(keys, "keys"), _dev(centroids, "centroids")
+    if centroids.dtype != keys.dtype:
+        raise ValueError("keys and centroids must share a dtype")
+    desc = ivf_desc(keys, centroids, keys.shape[2])
+    B, N, Hkv, _ = keys.shape
+    C = centroids.shape[2]
+    if offsets is None:
+        offsets = torch.empty((B, Hkv, C + 1), dtype=torch.int32, device=keys.device)
+    if ids is None:
+        ids = torch.empty((B, Hkv, N), dtype=torch.int32, device=keys.device)
+    _i32(offsets, "offsets", (B, Hkv, C + 1))
+    _i32(ids, "ids", (B, Hkv, N))
+    ws = _workspace(OP_INDEX_BUILD, desc, 0, ws, keys.device)
+    _check(load().tsa_index_build(ctypes.byref(desc), _ptr(keys), _ptr(centroids), _ptr(offsets),
+                                  _ptr(ids), _ptr(ws), ws.numel(), _stream(stream)))
+    return offsets, ids
+
+
+def sparse_decode(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, out=None, sel_out=None,
+                  rows_out=None, uniq_out=None, ws=None, stream=None):
+    """One retrieval-based sparse-attention decode step. Returns out [B][Hq][d] fp32."""
+    for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    if not (q.dtype == centroids.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, centroids, k_cache and v_cache must share a dtype")
+    B, Hq, d = q.shape
+    desc = ivf_desc(k_cache, centroids, Hq)
+    if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("q / k_cache / v_cache shapes disagree")
+    Hkv, C, N = desc.n_kv_heads, desc.n_centroids, desc.n_tokens
+    _i32(offsets, "offsets", (B, Hkv, C + 1))
+    _i32(ids, "ids", (B, Hkv, N))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, d):
+        raise ValueError("out must be fp32 [B][Hq][d]")
+    _i32(sel_out, "sel_out", (B, Hq, k))
+    _i32(rows_out, "rows_out", (B, Hq))
+    _i32(uniq_out, "uniq_out", (B, Hkv))
+    ws = _workspace(OP_SPARSE_DECODE, desc, k, ws, q.device)
+    _check(load().tsa_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(centroids), _ptr(offsets), _ptr(ids),
+                                    _ptr(k_cache), _ptr(v_cache), k, _ptr(out), _ptr(sel_out),
+                                    _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def token_decode(q_idx, k_idx, q, k_cache, v_cache, k: int, *, out=None, sel_out=None, ws=None,
+                 stream=None):
+    """Token-indexer top-k + attention. Returns out [B][Hq][d] fp32."""
+    for t, n in ((q_idx, "q_idx"), (k_idx, "k_idx"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    if not (q_idx.dtype == k_idx.dtype == q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("all inputs must share a dtype")
+    B, Hq, d = q.shape
+    desc = token_desc(k_idx, k_cache, Hq)
+    if tuple(q_idx.shape) != (B, desc.idx_dim) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q_idx / v_cache shapes disagree")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _i32(sel_out, "sel_out", (B, k))
+    ws = _workspace(OP_TOKEN_DECODE, desc, k, ws, q.device)
+    _check(load().tsa_token_decode(ctypes.byref(desc), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k_cache),
+                                   _ptr(v_cache), k, _ptr(out), _ptr(sel_out), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
+    return out
+
+
+def attend_rows(q, k_rows, v_rows, row_ids, row_counts=None, *, out=None, ws=None, stream=None):
+    """Attention of every query head over per-request row lists. row_ids [B][max_rows]."""
+    for t, n in ((q, "q"), (k_rows, "k_rows"), (v_rows, "v_rows"), (row_ids, "row_ids")):
+        _dev(t, n)
+    B, Hq, d = q.shape
+    max_rows = row_ids.shape[1]
+    desc = attn_desc(k_rows, Hq, max_rows)
+    _i32(row_ids, "row_ids", (B, max_rows))
+    _i32(row_counts, "row_counts", (B,))
+    if tuple(v_rows.shape) != tuple(k_rows.shape) or k_rows.shape[0] != B:
+        raise ValueError("k_rows / v_rows / q shapes disagree")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    ws = _workspace(OP_ATTEND_ROWS, desc, 0, ws, q.device)
+    _check(load().tsa_attend_rows(ctypes.byref(desc), _ptr(q), _ptr(k_rows), _ptr(v_rows), _ptr(row_ids),
+                                  _ptr(row_counts), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def resolve(page_table, slot_token, last_use, sel, step: int, host_k, host_v, pool_k, pool_v, *,
+            slots_out=None, hits=None, misses=None, stream=None):
+    """One RESOLVE step for all requests. Returns (slots_out, hits, misses)."""
+    B, N, Hkv, d = host_k.shape
+    S = pool_k.shape[1]
+    k = sel.shape[1]
+    desc = cache_desc(host_k, S)
+    _i32(page_table, "page_table", (B, N))
+    _i32(slot_token, "slot_token", (B, S))
+    _i32(last_use, "last_use", (B, S))
+    _i32(sel, "sel", (B, k))
+    if tuple(pool_k.shape) != (B, S, Hkv, d) or tuple(pool_v.shape) != (B, S, Hkv, d):
+        raise ValueError("pool shapes must be [B][S][Hkv][d]")
+    if host_k.is_cuda or host_v.is_cuda:
+        raise ValueError("host_k / host_v must be host-mapped memory (host_alloc)")
+    dev = pool_k.device
+    if slots_out is None:
+        slots_out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if hits is None:
+        hits = torch.empty((B,), dtype=torch.int32, device=dev)
+    if misses is None:
+        misses = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(load().tsa_resolve(ctypes.byref(desc), _ptr(page_table), _ptr(slot_token), _ptr(last_use),
+                              _ptr(sel), k, step, _ptr(host_k), _ptr(host_v), _ptr(pool_k), _ptr(pool_v),
+                              _ptr(slots_out), _ptr(hits), _ptr(misses), _stream(stream)))
+    return slots_out, hits, misses
+
+
+def cache_reset(page_table, slot_token, last_use, stream=None):
+    B, N = page_table.shape
+    S = slot_token.shape[1]
+    desc = CacheDesc(B, N, S, 1, 128, TSA_BF16)
+    _check(load().tsa_cache_reset(ctypes.byref(desc), _ptr(page_table), _ptr(slot_token), _ptr(last_use),
+                                  _stream(stream)))
+
+
+class HostArray:
+    """Pinned, device-readable host memory from tsa_host_alloc, viewed as a
+    torch CPU tensor (``.tensor``). Freed when this object is collected."""
+
+    def __init__(self, shape, dtype: torch.dtype):
+        nbytes = int(torch.Size(shape).numel()) * torch.empty((), dtype=dtype).element_size()
+        p = _P()
+        _check(load().tsa_host_alloc(max(nbytes, 1), ctypes.byref(p)))
+        self._ptr = p.value
+        buf = (ctypes.c_uint8 * max(nbytes, 1)).from_address(self._ptr)
+        self.tensor = torch.frombuffer(buf, dtype=torch.uint8)[:nbytes].view(dtype).view(shape)
+
+    def __del__(self):
+        if getattr(self, "_ptr", None):
+            self.tensor = None
+            load().tsa_host_free(self._ptr)
+            self._ptr = None
+
+
+def time_next_gather(ev_start: torch.cuda.Event, ev_stop: torch.cuda.Event):
+    """Have the next gather-attention launch of this thread record the two
+    events around itself (on the stream of that call)."""
+    for ev in (ev_start, ev_stop):
+        if not ev.cuda_event:  # torch creates the HIP event on its first record
+            ev.record()
+    _check(load().tsa_time_next_gather(_P(ev_start.cuda_event), _P(ev_stop.cuda_event)))
+
+
+def abi_version() -> int:
+    return load().tsa_abi_version()

@@ -1,0 +1,431 @@
+// C-ABI layer of libtsa: argument validation, workspace layout, launch
+// sequencing and error reporting. Every check runs on the host before the
+// first launch, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kernels.hpp"
+#include "tsa.h"
+
+using namespace tsa;
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_gather_ev0 = nullptr;
+thread_local hipEvent_t g_gather_ev1 = nullptr;
+
+tsa_status fail(tsa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+tsa_status ok() {
+  g_last_error.clear();
+  return TSA_OK;
+}
+
+tsa_status hip_fail(hipError_t e, const char* where) {
+  return fail(TSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
+
+bool valid_group(int Hq, int Hkv) {
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv) return false;
+  const int G = Hq / Hkv;
+  return G == 1 || G == 2 || G == 4 || G == 8;
+}
+
+float qscale(int d) { return static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d))); }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// ----------------------------------------------------------------- layouts
+struct IvfLayout {
+  int G = 0, smax = 0;
+  size_t scores = 0, seg = 0, nseg = 0, partial = 0, total = 0;
+};
+
+IvfLayout ivf_layout(const tsa_ivf_desc& d, int k) {
+  IvfLayout L;
+  L.G = d.n_q_heads / d.n_kv_heads;
+  L.smax = L.G * k + ceil_div(d.n_tokens, kSegRows);
+  const size_t bh = static_cast<size_t>(d.batch) * d.n_kv_heads;
+  size_t off = 0;
+  L.scores = off; off += align_up(static_cast<size_t>(d.batch) * d.n_q_heads * d.n_centroids * sizeof(float));
+  L.seg = off;    off += align_up(bh * L.smax * sizeof(int4));
+  L.nseg = off;   off += align_up(bh * sizeof(int32_t));
+  L.partial = off; off += align_up(bh * L.smax * L.G * kPartStride * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+struct TokLayout {
+  int G = 0, smax = 0, nchunk = 0;
+  size_t cand_key = 0, cand_id = 0, sel = 0, partial = 0, total = 0;
+};
+
+TokLayout tok_layout(const tsa_token_desc& d, int k) {
+  TokLayout L;
+  L.G = d.n_q_heads / d.n_kv_heads;
+  L.smax = ceil_div(k, kSegRows);
+  L.nchunk = ceil_div(d.n_tokens, kTokChunk);
+  const size_t ncand = static_cast<size_t>(d.batch) * L.nchunk * k;
+  size_t off = 0;
+  L.cand_key = off; off += align_up(ncand * sizeof(uint32_t));
+  L.cand_id = off;  off += align_up(ncand * sizeof(int32_t));
+  L.sel = off;      off += align_up(static_cast<size_t>(d.batch) * k * sizeof(int32_t));
+  L.partial = off;
+  off += align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * L.smax * L.G * kPartStride * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+struct RowsLayout {
+  int G = 0, smax = 0;
+  size_t partial = 0, total = 0;
+};
+
+RowsLayout rows_layout(const tsa_attn_desc& d) {
+  RowsLayout L;
+  L.G = d.n_q_heads / d.n_kv_heads;
+  L.smax = std::max(1, ceil_div(d.max_rows, kSegRows));
+  L.total = align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * L.smax * L.G * kPartStride * sizeof(float));
+  return L;
+}
+
+size_t index_ws(const tsa_ivf_desc& d) {
+  return align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * d.n_tokens * sizeof(int32_t));
+}
+
+// ------------------------------------------------------------- validation
+tsa_status check_dtype(int dtype) {
+  if (dtype != TSA_F32 && dtype != TSA_BF16) return fail(TSA_ERR_UNSUPPORTED, "dtype %d is not TSA_F32 or TSA_BF16", dtype);
+  return TSA_OK;
+}
+
+tsa_status check_ivf(const tsa_ivf_desc* d) {
+  if (!d) return fail(TSA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch <= 0 || d->n_tokens <= 0 || d->n_kv_heads <= 0 || d->n_q_heads <= 0 ||
+      d->head_dim <= 0 || d->n_centroids <= 0)
+    return fail(TSA_ERR_INVALID_ARG, "non-positive size in tsa_ivf_desc");
+  if (d->head_dim != kHeadDimRows) return fail(TSA_ERR_UNSUPPORTED, "head_dim %d != 128", d->head_dim);
+  if (!valid_group(d->n_q_heads, d->n_kv_heads))
+    return fail(TSA_ERR_UNSUPPORTED, "n_q_heads/n_kv_heads = %d/%d is not 1, 2, 4 or 8", d->n_q_heads, d->n_kv_heads);
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (d->n_centroids > kMaxCentroids || static_cast<long long>(d->n_centroids) * (G + 1) > 16384)
+    return fail(TSA_ERR_UNSUPPORTED, "n_centroids %d too large for group %d", d->n_centroids, G);
+  if (d->shared_codebook != 0 && d->shared_codebook != 1)
+    return fail(TSA_ERR_INVALID_ARG, "shared_codebook must be 0 or 1");
+  return check_dtype(d->dtype);
+}
+
+tsa_status check_token(const tsa_token_desc* d, int k) {
+  if (!d) return fail(TSA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch <= 0 || d->n_tokens <= 0 || d->n_kv_heads <= 0 || d->n_q_heads <= 0 ||
+      d->head_dim <= 0 || d->idx_dim <= 0)
+    return fail(TSA_ERR_INVALID_ARG, "non-positive size in tsa_token_desc");
+  if (d->head_dim != kHeadDimRows) return fail(TSA_ERR_UNSUPPORTED, "head_dim %d != 128", d->head_dim);
+  if (d->idx_dim != 64) return fail(TSA_ERR_UNSUPPORTED, "idx_dim %d != 64", d->idx_dim);
+  if (!valid_group(d->n_q_heads, d->n_kv_heads))
+    return fail(TSA_ERR_UNSUPPORTED, "n_q_heads/n_kv_heads = %d/%d is not 1, 2, 4 or 8", d->n_q_heads, d->n_kv_heads);
+  if (k < 1 || k > d->n_tokens) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, N=%d]", k, d->n_tokens);
+  if (k > kMaxTokenK) return fail(TSA_ERR_UNSUPPORTED, "k=%d > %d", k, kMaxTokenK);
+  const long long cand = static_cast<long long>(ceil_div(d->n_tokens, kTokChunk)) * k;
+  if (cand > static_cast<long long>(kMergeThreads) * kMaxMergePer)
+    return fail(TSA_ERR_UNSUPPORTED, "N*k too large: %lld merge candidates", cand);
+  return check_dtype(d->dtype);
+}
+
+tsa_status check_attn(const tsa_attn_desc* d) {
+  if (!d) return fail(TSA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch <= 0 || d->n_rows <= 0 || d->n_kv_heads <= 0 || d->n_q_heads <= 0 ||
+      d->head_dim <= 0 || d->max_rows < 0)
+    return fail(TSA_ERR_INVALID_ARG, "bad size in tsa_attn_desc");
+  if (d->head_dim != kHeadDimRows) return fail(TSA_ERR_UNSUPPORTED, "head_dim %d != 128", d->head_dim);
+  if (!valid_group(d->n_q_heads, d->n_kv_heads))
+    return fail(TSA_ERR_UNSUPPORTED, "n_q_heads/n_kv_heads = %d/%d is not 1, 2, 4 or 8", d->n_q_heads, d->n_kv_heads);
+  return check_dtype(d->dtype);
+}
+
+tsa_status check_cache(const tsa_cache_desc* d) {
+  if (!d) return fail(TSA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch <= 0 || d->n_tokens <= 0 || d->n_slots <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0)
+    return fail(TSA_ERR_INVALID_ARG, "non-positive size in tsa_cache_desc");
+  if (d->head_dim != kHeadDimRows) return fail(TSA_ERR_UNSUPPORTED, "head_dim %d != 128", d->head_dim);
+  if (d->n_slots > kMaxSlots) return fail(TSA_ERR_UNSUPPORTED, "n_slots %d > %d", d->n_slots, kMaxSlots);
+  return check_dtype(d->dtype);
+}
+
+#define REQUIRE_PTR(p)                                                     \
+  do {                                                                     \
+    if (!(p)) return fail(TSA_ERR_INVALID_ARG, "%s is NULL", #p);           \
+  } while (0)
+
+#define REQUIRE_ALIGN(p, a)                                                \
+  do {                                                                     \
+    if ((p) && !aligned((p), (a)))                                         \
+      return fail(TSA_ERR_INVALID_ARG, "%s is not %d-byte aligned", #p, (int)(a)); \
+  } while (0)
+
+tsa_status launch_gather_timed(const GatherParams& gp, int dtype, int G, bool explicit_plan,
+                               hipStream_t s) {
+  hipEvent_t e0 = g_gather_ev0, e1 = g_gather_ev1;
+  g_gather_ev0 = g_gather_ev1 = nullptr;
+  if (e0) {
+    hipError_t e = hipEventRecord(e0, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  hipError_t e = launch_gather(gp, dtype, G, explicit_plan, s);
+  if (e != hipSuccess) return hip_fail(e, "gather_attn launch");
+  if (e1) {
+    e = hipEventRecord(e1, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  e = launch_combine(gp, G, explicit_plan, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return TSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tsa_abi_version(void) { return TSA_ABI_VERSION; }
+
+const char* tsa_status_str(tsa_status s) {
+  switch (s) {
+    case TSA_OK: return "TSA_OK";
+    case TSA_ERR_INVALID_ARG: return "TSA_ERR_INVALID_ARG";
+    case TSA_ERR_UNSUPPORTED: return "TSA_ERR_UNSUPPORTED";
+    case TSA_ERR_WORKSPACE: return "TSA_ERR_WORKSPACE";
+    case TSA_ERR_HIP: return "TSA_ERR_HIP";
+  }
+  return "TSA_ERR_UNKNOWN";
+}
+
+const char* tsa_last_error(void) { return g_last_error.c_str(); }
+
+tsa_status tsa_workspace_bytes(int32_t op, const void* desc, int32_t k, size_t* bytes) {
+  REQUIRE_PTR(bytes);
+  REQUIRE_PTR(desc);
+  switch (op) {
+    case TSA_OP_INDEX_BUILD: {
+      const auto* d = static_cast<const tsa_ivf_desc*>(desc);
+      if (tsa_status s = check_ivf(d)) return s;
+      *bytes = index_ws(*d);
+      return ok();
+    }
+    case TSA_OP_SPARSE_DECODE: {
+      const auto* d = static_cast<const tsa_ivf_desc*>(desc);
+      if (tsa_status s = check_ivf(d)) return s;
+      if (k < 1 || k > d->n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d->n_centroids);
+      *bytes = ivf_layout(*d, k).total;
+      return ok();
+    }
+    case TSA_OP_TOKEN_DECODE: {
+      const auto* d = static_cast<const tsa_token_desc*>(desc);
+      if (tsa_status s = check_token(d, k)) return s;
+      *bytes = tok_layout(*d, k).total;
+      return ok();
+    }
+    case TSA_OP_ATTEND_ROWS: {
+      const auto* d = static_cast<const tsa_attn_desc*>(desc);
+      if (tsa_status s = check_attn(d)) return s;
+      *bytes = rows_layout(*d).total;
+      return ok();
+    }
+    default:
+      return fail(TSA_ERR_INVALID_ARG, "unknown op %d", op);
+  }
+}
+
+tsa_status tsa_index_build(const tsa_ivf_desc* desc, const void* keys, const void* centroids,
+                           int32_t* offsets, int32_t* ids, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  REQUIRE_PTR(keys); REQUIRE_PTR(centroids); REQUIRE_PTR(offsets); REQUIRE_PTR(ids); REQUIRE_PTR(ws);
+  REQUIRE_ALIGN(keys, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(ws, 16);
+  const size_t need = index_ws(*desc);
+  if (ws_bytes < need) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const tsa_ivf_desc& d = *desc;
+  hipStream_t s = as_stream(stream);
+  AssignParams ap{keys, centroids,
+                  d.shared_codebook ? 0LL : static_cast<long long>(d.n_kv_heads) * d.n_centroids * kHeadDimRows,
+                  static_cast<int32_t*>(ws), d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids};
+  hipError_t e = launch_assign(ap, d.dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "assign launch");
+  CsrParams cp{static_cast<const int32_t*>(ws), offsets, ids, d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids};
+  e = launch_csr(cp, s);
+  if (e != hipSuccess) return hip_fail(e, "csr launch");
+  return ok();
+}
+
+tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void* centroids,
+                             const int32_t* offsets, const int32_t* ids, const void* k_cache,
+                             const void* v_cache, int32_t k, float* out, int32_t* sel_out,
+                             int32_t* rows_out, int32_t* uniq_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(centroids); REQUIRE_PTR(offsets); REQUIRE_PTR(ids);
+  REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(out); REQUIRE_PTR(ws);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(k_cache, 16);
+  REQUIRE_ALIGN(v_cache, 16); REQUIRE_ALIGN(out, 8); REQUIRE_ALIGN(ws, 16);
+  const tsa_ivf_desc& d = *desc;
+  if (k < 1 || k > d.n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d.n_centroids);
+  const IvfLayout L = ivf_layout(d, k);
+  if (ws_bytes < L.total) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = as_stream(stream);
+  const long long cbs = d.shared_codebook ? 0LL : static_cast<long long>(d.n_kv_heads) * d.n_centroids * kHeadDimRows;
+
+  ScoreParams sp{q, centroids, cbs, reinterpret_cast<float*>(w + L.scores), d.batch, d.n_kv_heads, d.n_centroids};
+  hipError_t e = launch_centroid_scores(sp, d.dtype, L.G, s);
+  if (e != hipSuccess) return hip_fail(e, "centroid_scores launch");
+
+  SelectParams selp{reinterpret_cast<const float*>(w + L.scores), offsets, sel_out, rows_out, uniq_out,
+                    reinterpret_cast<int4*>(w + L.seg), reinterpret_cast<int32_t*>(w + L.nseg),
+                    d.batch, d.n_kv_heads, d.n_centroids, k, L.smax, d.n_tokens};
+  e = launch_ivf_select(selp, L.G, s);
+  if (e != hipSuccess) return hip_fail(e, "ivf_select launch");
+
+  GatherParams gp{};
+  gp.q = q; gp.k = k_cache; gp.v = v_cache; gp.n_rows = d.n_tokens;
+  gp.rowids = ids; gp.rid_bstride = static_cast<long long>(d.n_kv_heads) * d.n_tokens; gp.rid_gstride = d.n_tokens;
+  gp.seg = reinterpret_cast<const int4*>(w + L.seg); gp.nseg = reinterpret_cast<const int32_t*>(w + L.nseg);
+  gp.counts = nullptr; gp.count_const = 0;
+  gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
+  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax; gp.W = std::min(L.smax, L.G * k);
+  gp.qscale = qscale(d.head_dim);
+  if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, true, s)) return st;
+  return ok();
+}
+
+tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const void* k_idx,
+                            const void* q, const void* k_cache, const void* v_cache, int32_t k,
+                            float* out, int32_t* sel_out, void* ws, size_t ws_bytes, void* stream) {
+  if (tsa_status s = check_token(desc, k)) return s;
+  REQUIRE_PTR(q_idx); REQUIRE_PTR(k_idx); REQUIRE_PTR(q); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(out); REQUIRE_PTR(ws);
+  REQUIRE_ALIGN(q_idx, 16); REQUIRE_ALIGN(k_idx, 16); REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k_cache, 16);
+  REQUIRE_ALIGN(v_cache, 16); REQUIRE_ALIGN(out, 8); REQUIRE_ALIGN(ws, 16);
+  const tsa_token_desc& d = *desc;
+  const TokLayout L = tok_layout(d, k);
+  if (ws_bytes < L.total) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = as_stream(stream);
+  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + L.sel);
+  TokenSelectParams tp{q_idx, k_idx, reinterpret_cast<uint32_t*>(w + L.cand_key),
+                       reinterpret_cast<int32_t*>(w + L.cand_id), sel, d.batch, d.n_tokens, k, L.nchunk};
+  hipError_t e = launch_token_select(tp, d.dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "token_select launch");
+
+  GatherParams gp{};
+  gp.q = q; gp.k = k_cache; gp.v = v_cache; gp.n_rows = d.n_tokens;
+  gp.rowids = sel; gp.rid_bstride = k; gp.rid_gstride = 0;
+  gp.seg = nullptr; gp.nseg = nullptr; gp.counts = nullptr; gp.count_const = k; gp.count_max = k;
+  gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
+  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax; gp.W = L.smax;
+  gp.qscale = qscale(d.head_dim);
+  if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
+  return ok();
+}
+
+tsa_status tsa_attend_rows(const tsa_attn_desc* desc, const void* q, const void* k_rows,
+                           const void* v_rows, const int32_t* row_ids, const int32_t* row_counts,
+                           float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (tsa_status s = check_attn(desc)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(k_rows); REQUIRE_PTR(v_rows); REQUIRE_PTR(out); REQUIRE_PTR(ws);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k_rows, 16); REQUIRE_ALIGN(v_rows, 16); REQUIRE_ALIGN(out, 8);
+  REQUIRE_ALIGN(ws, 16);
+  const tsa_attn_desc& d = *desc;
+  if (d.max_rows > 0) REQUIRE_PTR(row_ids);
+  const RowsLayout L = rows_layout(d);
+  if (ws_bytes < L.total) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  hipStream_t s = as_stream(stream);
+  GatherParams gp{};
+  gp.q = q; gp.k = k_rows; gp.v = v_rows; gp.n_rows = d.n_rows;
+  gp.rowids = row_ids; gp.rid_bstride = d.max_rows; gp.rid_gstride = 0;
+  gp.seg = nullptr; gp.nseg = nullptr; gp.counts = row_counts; gp.count_const = d.max_rows;
+  gp.count_max = d.max_rows;
+  gp.partial = static_cast<float*>(ws); gp.out = out;
+  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax; gp.W = L.smax;
+  gp.qscale = qscale(d.head_dim);
+  if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
+  return ok();
+}
+
+tsa_status tsa_resolve(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,
+                       int32_t* last_use, const int32_t* sel, int32_t k, int32_t step,
+                       const void* host_k, const void* host_v, void* pool_k, void* pool_v,
+                       int32_t* slots_out, int32_t* hits, int32_t* misses, void* stream) {
+  if (tsa_status s = check_cache(desc)) return s;
+  REQUIRE_PTR(page_table); REQUIRE_PTR(slot_token); REQUIRE_PTR(last_use); REQUIRE_PTR(sel);
+  REQUIRE_PTR(host_k); REQUIRE_PTR(host_v); REQUIRE_PTR(pool_k); REQUIRE_PTR(pool_v); REQUIRE_PTR(slots_out);
+  REQUIRE_ALIGN(host_k, 16); REQUIRE_ALIGN(host_v, 16); REQUIRE_ALIGN(pool_k, 16); REQUIRE_ALIGN(pool_v, 16);
+  const tsa_cache_desc& d = *desc;
+  if (k < 1 || k > d.n_slots || k > kMaxTokenK)
+    return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, min(S=%d, %d)]", k, d.n_slots, kMaxTokenK);
+  if (step < 0 || step == INT32_MAX) return fail(TSA_ERR_INVALID_ARG, "step %d out of range", step);
+  ResolveParams rp{page_table, slot_token, last_use, sel, host_k, host_v, pool_k, pool_v, slots_out, hits,
+                   misses, static_cast<long long>(d.n_kv_heads) * d.head_dim * esize(d.dtype),
+                   d.batch, d.n_tokens, d.n_slots, k, step};
+  hipError_t e = launch_resolve(rp, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "resolve launch");
+  return ok();
+}
+
+tsa_status tsa_cache_reset(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,
+                           int32_t* last_use, void* stream) {
+  if (tsa_status s = check_cache(desc)) return s;
+  REQUIRE_PTR(page_table); REQUIRE_PTR(slot_token); REQUIRE_PTR(last_use);
+  const tsa_cache_desc& d = *desc;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = launch_fill_i32(page_table, static_cast<long long>(d.batch) * d.n_tokens, -1, s);
+  if (e == hipSuccess) e = launch_fill_i32(slot_token, static_cast<long long>(d.batch) * d.n_slots, -1, s);
+  if (e == hipSuccess) e = launch_fill_i32(last_use, static_cast<long long>(d.batch) * d.n_slots, -1, s);
+  if (e != hipSuccess) return hip_fail(e, "fill launch");
+  return ok();
+}
+
+tsa_status tsa_host_alloc(size_t bytes, void** host_ptr) {
+  REQUIRE_PTR(host_ptr);
+  if (bytes == 0) return fail(TSA_ERR_INVALID_ARG, "bytes == 0");
+  void* p = nullptr;
+  hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocPortable);
+  if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+  *host_ptr = p;
+  return ok();
+}
+
+tsa_status tsa_host_free(void* host_ptr) {
+  REQUIRE_PTR(host_ptr);
+  hipError_t e = hipHostFree(host_ptr);
+  if (e != hipSuccess) return hip_fail(e, "hipHostFree");
+  return ok();
+}
+
+tsa_status tsa_time_next_gather(void* ev_start, void* ev_stop) {
+  if ((ev_start == nullptr) != (ev_stop == nullptr))
+    return fail(TSA_ERR_INVALID_ARG, "give both events or neither");
+  g_gather_ev0 = static_cast<hipEvent_t>(ev_start);
+  g_gather_ev1 = static_cast<hipEvent_t>(ev_stop);
+  return ok();
+}
+
+}  // extern "C"

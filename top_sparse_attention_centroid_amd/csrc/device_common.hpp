@@ -1,0 +1,144 @@
+// Device helpers for the gfx950 kernels: element loads, wave64 cross-lane
+// reductions through DPP, ballot prefix counts, order-preserving float keys.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsa {
+
+constexpr int kHeadDim = 128;  // d: one row is 128 elements (256 B in bf16)
+constexpr int kWave = 64;
+
+// bf16 bit patterns are stored as uint16_t; widening to fp32 is exact.
+using bf16_t = uint16_t;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight consecutive elements in flight as raw bits: 16 B for bf16, 32 B for fp32.
+template <typename T>
+struct Raw8;
+
+template <>
+struct Raw8<bf16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void widen(float (&x)[8]) const {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  }
+};
+
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void widen(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
+  Raw8<T> r;
+  r.load(p);
+  r.widen(x);
+}
+
+__device__ __forceinline__ float dot8(const float (&a)[8], const float (&b)[8]) {
+  float s = a[0] * b[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) s = fmaf(a[i], b[i], s);
+  return s;
+}
+
+// DPP lane permutations inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8-lane half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each 16-lane row
+
+// Sum over aligned groups of 8 / 16 lanes. Every lane of a group ends with the
+// bitwise-same value (each step adds commutative pairs).
+__device__ __forceinline__ float group8_sum(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float group16_sum(float x) {
+  x = group8_sum(x);
+  x += dpp_f<kDppMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Number of set bits of `mask` in lanes below the calling lane.
+__device__ __forceinline__ int prefix_count(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Unsigned key whose order matches the float order (+0 and -0 collapse).
+// Finite floats map to keys >= 0x00800000, so key 0 can mark "no entry".
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exclusive prefix sum over a block of NW waves. `scratch` holds NW ints.
+// Returns the caller's exclusive prefix; *total receives the block total.
+template <int NW>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) scratch[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    int t = scratch[w];
+    before += (w < wave) ? t : 0;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+template <int NW>
+__device__ __forceinline__ int block_sum(int v, int* scratch) {
+  int total;
+  block_exclusive_scan<NW>(v, scratch, &total);
+  return total;
+}
+
+}  // namespace tsa

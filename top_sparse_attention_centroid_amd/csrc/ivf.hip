@@ -1,0 +1,340 @@
+// Inverted-index kernels for gfx950: index build (nearest-centroid assignment
+// and stable CSR posting lists), centroid scoring, and per-query-head top-k
+// list selection fused with the gather plan of the KV group.
+//
+// [KARAT] = paper-daily digest "Heterogeneous LLM Serving with General-Purpose
+// Processing-Near-Memory for Retrieval-Based Sparse Attention".
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace tsa {
+
+// ============================================================================
+// Index build, step 1: nearest centroid of every key ([KARAT] How, index
+// structure). One thread per key holds the key in registers; centroids stream
+// through LDS in tiles of 32 rows. argmin_c |k - c|^2 = argmin_c (|c|^2 -
+// 2 k.c); ties keep the lower centroid (strict <).
+// ============================================================================
+constexpr int kAssignTile = 32;
+
+template <typename T>
+__global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
+  __shared__ float4 tile[kAssignTile][kHeadDim / 4];
+  __shared__ float norm2[kAssignTile];
+  const int bg = blockIdx.y;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x * 256 + tid;
+  const bool valid = i < p.N;
+
+  float kf[kHeadDim];
+  {
+    const T* kr = static_cast<const T*>(p.keys) +
+                  ((static_cast<long long>(b) * p.N + (valid ? i : 0)) * p.Hkv + g) * kHeadDim;
+#pragma unroll
+    for (int j = 0; j < kHeadDim / 8; ++j) {
+      float x[8];
+      load8(kr + j * 8, x);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) kf[j * 8 + t] = x[t];
+    }
+  }
+  const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
+                static_cast<long long>(g) * p.C * kHeadDim;
+  float best = INFINITY;
+  int bestc = 0;
+  for (int c0 = 0; c0 < p.C; c0 += kAssignTile) {
+    __syncthreads();
+    for (int idx = tid; idx < kAssignTile * (kHeadDim / 8); idx += 256) {
+      const int row = idx / (kHeadDim / 8), part = idx % (kHeadDim / 8);
+      const int c = c0 + row;
+      float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (c < p.C) load8(cb + static_cast<long long>(c) * kHeadDim + part * 8, x);
+      tile[row][part * 2] = make_float4(x[0], x[1], x[2], x[3]);
+      tile[row][part * 2 + 1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+    __syncthreads();
+    if (tid < kAssignTile) {
+      float s = 0.f;
+      for (int t = 0; t < kHeadDim / 4; ++t) {
+        float4 v = tile[tid][t];
+        s = fmaf(v.x, v.x, s); s = fmaf(v.y, v.y, s); s = fmaf(v.z, v.z, s); s = fmaf(v.w, v.w, s);
+      }
+      norm2[tid] = s;
+    }
+    __syncthreads();
+    const int nc = min(kAssignTile, p.C - c0);
+    for (int j = 0; j < nc; ++j) {
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+      for (int t = 0; t < kHeadDim / 4; ++t) {
+        const float4 v = tile[j][t];
+        a0 = fmaf(kf[4 * t + 0], v.x, a0);
+        a1 = fmaf(kf[4 * t + 1], v.y, a1);
+        a2 = fmaf(kf[4 * t + 2], v.z, a2);
+        a3 = fmaf(kf[4 * t + 3], v.w, a3);
+      }
+      const float dist = norm2[j] - 2.f * ((a0 + a1) + (a2 + a3));
+      if (dist < best) { best = dist; bestc = c0 + j; }
+    }
+  }
+  if (valid) p.assign[static_cast<long long>(bg) * p.N + i] = bestc;
+}
+
+// ============================================================================
+// Index build, step 2: CSR posting lists, token ids ascending inside a list.
+// One workgroup per (request, KV head): LDS histogram, exclusive scan, then a
+// single wave walks the tokens in order; lanes sharing a list find each other
+// with one ballot per bit of the list id, which keeps the scatter stable.
+// ============================================================================
+__global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
+  extern __shared__ int cursor[];  // [C]
+  __shared__ int scan_scratch[4];
+  const int bg = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t* a = p.assign + static_cast<long long>(bg) * p.N;
+  int32_t* off = p.offsets + static_cast<long long>(bg) * (p.C + 1);
+  int32_t* ids = p.ids + static_cast<long long>(bg) * p.N;
+
+  for (int c = tid; c < p.C; c += 256) cursor[c] = 0;
+  __syncthreads();
+  for (int i = tid; i < p.N; i += 256) atomicAdd(&cursor[a[i]], 1);
+  __syncthreads();
+  int carry = 0;
+  for (int c0 = 0; c0 < p.C; c0 += 256) {
+    const int c = c0 + tid;
+    const int v = c < p.C ? cursor[c] : 0;
+    int tot;
+    const int ex = block_exclusive_scan<4>(v, scan_scratch, &tot);
+    if (c < p.C) {
+      off[c] = carry + ex;
+      cursor[c] = carry + ex;
+    }
+    carry += tot;
+  }
+  if (tid == 0) off[p.C] = p.N;
+  __syncthreads();
+  if (tid < kWave) {
+    const int lane = tid;
+    const int nbits = p.C > 1 ? 32 - __clz(p.C - 1) : 0;
+    for (int i0 = 0; i0 < p.N; i0 += kWave) {
+      const int i = i0 + lane;
+      const bool valid = i < p.N;
+      const int c = valid ? a[i] : 0;
+      uint64_t same = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (c >> bit) & 1;
+        const uint64_t bal = __ballot(set);
+        same &= set ? bal : ~bal;
+      }
+      if (valid) {
+        const int rank = prefix_count(same);
+        const int pos = cursor[c] + rank;
+        ids[pos] = i;
+        if (rank == __popcll(same) - 1) cursor[c] = pos + 1;
+      }
+    }
+  }
+}
+
+// ============================================================================
+// Centroid scoring ([KARAT] worked example, step 3): s[b][h][c] = q[b][h] .
+// centroid[g][c], raw dot product in fp32. A workgroup scores 64 centroids
+// for the G query heads of one KV group; 16 lanes cover one 128-element row
+// (8 elements each) and reduce through DPP.
+// ============================================================================
+template <typename T, int G>
+__global__ __launch_bounds__(256) void centroid_scores_kernel(ScoreParams p) {
+  const int bg = blockIdx.y;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int r = lane >> 4, e = lane & 15;
+  const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
+  float qf[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) load8(qb + h * kHeadDim + e * 8, qf[h]);
+  const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
+                static_cast<long long>(g) * p.C * kHeadDim;
+  const int cbase = blockIdx.x * 64 + wave * 16;
+  Raw8<T> raw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = cbase + u * 4 + r;
+    if (c < p.C) raw[u].load(cb + static_cast<long long>(c) * kHeadDim + e * 8);
+    else raw[u].zero();
+  }
+  float* out = p.scores + (static_cast<long long>(b) * p.Hkv + g) * G * p.C;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = cbase + u * 4 + r;
+    float x[8];
+    raw[u].widen(x);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float s = group16_sum(dot8(qf[h], x));
+      if (e == 0 && c < p.C) out[h * p.C + c] = s;
+    }
+  }
+}
+
+// ============================================================================
+// Top-k lists per query head + gather plan per KV group.
+// One workgroup of 4 waves per (request, KV head); wave w owns query heads
+// w, w + 4 of the group. Top-k: the k-th largest order-preserving key T is found bit by bit
+// (MSB first) with ballot counts; keys above T are taken, and keys equal to T
+// in ascending list order until k are taken (ties -> lower list id). Lists
+// are emitted in ascending order through ballot prefix counts.
+// Plan: the union of the G heads' lists (head bitmask per list), each list cut
+// into segments of at most kSegRows rows, in ascending list order.
+// ============================================================================
+// List c of a CSR index, clamped to [0, N] so malformed offsets cannot send
+// the gather outside the id array.
+__device__ __forceinline__ int list_start(const int32_t* off, int c, int N) {
+  return min(max(off[c], 0), N);
+}
+__device__ __forceinline__ int list_len(const int32_t* off, int c, int N) {
+  const int s = list_start(off, c, N);
+  return min(max(off[c + 1], s), N) - s;
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
+  extern __shared__ float smem[];
+  float* s = smem;                                              // [G][C]
+  uint32_t* lmask = reinterpret_cast<uint32_t*>(smem + G * p.C);  // [C]
+  __shared__ int scan_scratch[4];
+  const int bg = blockIdx.x;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int C = p.C, k = p.k;
+  const int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
+
+  const float* src = p.scores + static_cast<long long>(bg) * G * C;
+  for (int i = tid; i < G * C; i += 256) s[i] = src[i];
+  for (int c = tid; c < C; c += 256) lmask[c] = 0u;
+  __syncthreads();
+
+  for (int h = wave; h < G; h += 4) {
+    const float* sh = s + h * C;
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
+      for (int c0 = 0; c0 < C; c0 += kWave) {
+        const int c = c0 + lane;
+        cnt += __popcll(__ballot(c < C && order_key(sh[c]) >= cand));
+      }
+      if (cnt >= k) T = cand;
+    }
+    int n_gt = 0;
+    for (int c0 = 0; c0 < C; c0 += kWave) {
+      const int c = c0 + lane;
+      n_gt += __popcll(__ballot(c < C && order_key(sh[c]) > T));
+    }
+    const int need_eq = k - n_gt;
+    const int qh = g * G + h;
+    int32_t* sel = p.sel_out ? p.sel_out + (static_cast<long long>(b) * p.Hkv * G + qh) * k : nullptr;
+    int base = 0, eq_seen = 0, rows = 0;
+    for (int c0 = 0; c0 < C; c0 += kWave) {
+      const int c = c0 + lane;
+      const uint32_t key = c < C ? order_key(sh[c]) : 0u;
+      const bool gt = c < C && key > T;
+      const bool eq = c < C && key == T;
+      const uint64_t eqm = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + prefix_count(eqm) < need_eq);
+      const uint64_t tm = __ballot(take);
+      if (take) {
+        if (sel) sel[base + prefix_count(tm)] = c;
+        atomicOr(&lmask[c], 1u << h);
+        rows += list_len(off, c, p.N);
+      }
+      base += __popcll(tm);
+      eq_seen += __popcll(eqm);
+    }
+    rows = wave_sum_i(rows);
+    if (p.rows_out && lane == 0) p.rows_out[static_cast<long long>(b) * p.Hkv * G + qh] = rows;
+  }
+  __syncthreads();
+
+  int4* seg = p.seg + static_cast<long long>(bg) * p.smax;
+  int carry = 0, uniq = 0;
+  for (int c0 = 0; c0 < C; c0 += 256) {
+    const int c = c0 + tid;
+    const uint32_t m = c < C ? lmask[c] : 0u;
+    const int start = c < C ? list_start(off, c, p.N) : 0;
+    const int len = c < C ? list_len(off, c, p.N) : 0;
+    const int nsg = (m != 0u && len > 0) ? (len + kSegRows - 1) / kSegRows : 0;
+    uniq += m != 0u ? len : 0;
+    int tot;
+    const int pos = carry + block_exclusive_scan<4>(nsg, scan_scratch, &tot);
+    for (int j = 0; j < nsg; ++j) {
+      if (pos + j < p.smax)
+        seg[pos + j] = make_int4(start + j * kSegRows, min(kSegRows, len - j * kSegRows),
+                                 static_cast<int>(m), c);
+    }
+    carry += tot;
+  }
+  uniq = block_sum<4>(uniq, scan_scratch);
+  if (tid == 0) {
+    p.nseg[bg] = min(carry, p.smax);
+    if (p.uniq_out) p.uniq_out[bg] = uniq;
+  }
+}
+
+// ============================================================================
+// Launchers
+// ============================================================================
+hipError_t launch_assign(const AssignParams& p, int dtype, hipStream_t s) {
+  dim3 grid((p.N + 255) / 256, p.B * p.Hkv);
+  if (dtype == kBF16) hipLaunchKernelGGL(assign_kernel<bf16_t>, grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(assign_kernel<float>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_csr(const CsrParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(csr_kernel, dim3(p.B * p.Hkv), dim3(256), p.C * sizeof(int), s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+static void scores_dispatch(const ScoreParams& p, int G, hipStream_t s) {
+  dim3 grid((p.C + 63) / 64, p.B * p.Hkv);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((centroid_scores_kernel<T, 1>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((centroid_scores_kernel<T, 2>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((centroid_scores_kernel<T, 4>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((centroid_scores_kernel<T, 8>), grid, dim3(256), 0, s, p); break;
+  }
+}
+
+hipError_t launch_centroid_scores(const ScoreParams& p, int dtype, int G, hipStream_t s) {
+  if (dtype == kBF16) scores_dispatch<bf16_t>(p, G, s);
+  else scores_dispatch<float>(p, G, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_ivf_select(const SelectParams& p, int G, hipStream_t s) {
+  const size_t lds = (static_cast<size_t>(G) * p.C + p.C) * sizeof(float);
+  dim3 grid(p.B * p.Hkv);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(ivf_select_kernel<1>, grid, dim3(256), lds, s, p); break;
+    case 2: hipLaunchKernelGGL(ivf_select_kernel<2>, grid, dim3(256), lds, s, p); break;
+    case 4: hipLaunchKernelGGL(ivf_select_kernel<4>, grid, dim3(256), lds, s, p); break;
+    default: hipLaunchKernelGGL(ivf_select_kernel<8>, grid, dim3(256), lds, s, p); break;
+  }
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* p, long long n, int32_t value) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += 256LL * gridDim.x) p[i] = value;
+}
+
+hipError_t launch_fill_i32(int32_t* p, long long n, int32_t value, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
+                     dim3(256), 0, s, p, n, value);
+  return hipGetLastError();
+}
+
+}  // namespace tsa

@@ -1,0 +1,120 @@
+// Internal interface between the C-ABI layer and the gfx950 kernels.
+// Launchers validate nothing: the C-ABI layer checks every shape, pointer and
+// size before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tsa {
+
+constexpr int kHeadDimRows = 128;   // d: elements per row (head_dim)
+constexpr int kSegRows = 256;       // rows per attention segment (one workgroup pass)
+constexpr int kPartStride = 132;    // floats per partial state: m, l, 2 pad, o[128]
+constexpr int kTokChunk = 8192;     // indexer tokens per workgroup (keys kept in LDS)
+constexpr int kMergeThreads = 1024; // threads of the per-request top-k merge
+constexpr int kMaxMergePer = 64;    // candidates per merge thread
+constexpr int kMaxCentroids = 4096;
+constexpr int kMaxSlots = 4096;
+constexpr int kMaxTokenK = 4096;
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+inline int esize(int dtype) { return dtype == kF32 ? 4 : 2; }
+
+// ---------------------------------------------------------------- index build
+struct AssignParams {
+  const void* keys;        // [B][N][Hkv][d]
+  const void* centroids;   // [Bc][Hkv][C][d]
+  long long cent_bstride;  // elements between request codebooks (0 = shared)
+  int32_t* assign;         // [B][Hkv][N]
+  int B, N, Hkv, C;
+};
+hipError_t launch_assign(const AssignParams& p, int dtype, hipStream_t s);
+
+struct CsrParams {
+  const int32_t* assign;   // [B][Hkv][N]
+  int32_t* offsets;        // [B][Hkv][C+1]
+  int32_t* ids;            // [B][Hkv][N]
+  int B, N, Hkv, C;
+};
+hipError_t launch_csr(const CsrParams& p, hipStream_t s);
+
+// ---------------------------------------------------------- IVF select + plan
+struct ScoreParams {
+  const void* q;           // [B][Hq][d]
+  const void* centroids;   // [Bc][Hkv][C][d]
+  long long cent_bstride;
+  float* scores;           // [B][Hq][C]
+  int B, Hkv, C;
+};
+hipError_t launch_centroid_scores(const ScoreParams& p, int dtype, int G, hipStream_t s);
+
+struct SelectParams {
+  const float* scores;     // [B][Hq][C]
+  const int32_t* offsets;  // [B][Hkv][C+1]
+  int32_t* sel_out;        // [B][Hq][k] or null
+  int32_t* rows_out;       // [B][Hq] or null
+  int32_t* uniq_out;       // [B][Hkv] or null
+  int4* seg;               // [B*Hkv][smax]: {start, count, head mask, list}
+  int32_t* nseg;           // [B*Hkv]
+  int B, Hkv, C, k, smax, N;
+};
+hipError_t launch_ivf_select(const SelectParams& p, int G, hipStream_t s);
+
+// --------------------------------------------------------- gather attention
+struct GatherParams {
+  const void* q;           // [B][Hq][d]
+  const void* k;           // [B][n_rows][Hkv][d]
+  const void* v;
+  long long n_rows;
+  const int32_t* rowids;   // row-id arrays
+  long long rid_bstride;   // int32 elements between requests' row-id arrays
+  long long rid_gstride;   // ... between KV heads' (0: shared by all heads)
+  const int4* seg;         // explicit segments (IVF) or null
+  const int32_t* nseg;     // explicit segment counts or null
+  const int32_t* counts;   // implicit: rows per request, or null
+  int count_const;         // implicit: rows per request when counts is null
+  int count_max;           // implicit: capacity of each request's row-id array
+  float* partial;          // [B*Hkv][smax][G][kPartStride]
+  float* out;              // [B][Hq][d]
+  int B, Hkv, smax, W;
+  float qscale;            // log2(e) / sqrt(d)
+};
+hipError_t launch_gather(const GatherParams& p, int dtype, int G, bool explicit_plan,
+                         hipStream_t s);
+hipError_t launch_combine(const GatherParams& p, int G, bool explicit_plan, hipStream_t s);
+
+// ------------------------------------------------------------ token select
+struct TokenSelectParams {
+  const void* q_idx;       // [B][64]
+  const void* k_idx;       // [B][N][64]
+  uint32_t* cand_key;      // [B][nchunk][k]
+  int32_t* cand_id;        // [B][nchunk][k]
+  int32_t* sel;            // [B][k]
+  int B, N, k, nchunk;
+};
+hipError_t launch_token_select(const TokenSelectParams& p, int dtype, hipStream_t s);
+
+// ---------------------------------------------------------------- resolve
+struct ResolveParams {
+  int32_t* page_table;     // [B][N]
+  int32_t* slot_token;     // [B][S]
+  int32_t* last_use;       // [B][S]
+  const int32_t* sel;      // [B][k]
+  const void* host_k;      // [B][N][Hkv][d] host-mapped
+  const void* host_v;
+  void* pool_k;            // [B][S][Hkv][d]
+  void* pool_v;
+  int32_t* slots_out;      // [B][k]
+  int32_t* hits;           // [B] or null
+  int32_t* misses;         // [B] or null
+  long long row_bytes;     // Hkv * d * element size (multiple of 16)
+  int B, N, S, k, step;
+};
+hipError_t launch_resolve(const ResolveParams& p, hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, long long n, int32_t value, hipStream_t s);
+
+}  // namespace tsa

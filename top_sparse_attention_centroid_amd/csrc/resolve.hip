@@ -1,0 +1,163 @@
+// Fused RESOLVE step of the HiSparse-style hot cache for gfx950
+// ("KV卸载上主机:HiSparse、PDD与DDR4回收", paper analysis 1: hit detection, LRU
+// replacement, metadata update and host fetch in one kernel; the authoritative
+// KV stays in pinned host memory, HBM holds S slots per request per layer).
+//
+// One workgroup of 1024 threads per request:
+//   1. every slot gets the 64-bit key (last_use + 1) << 32 | slot in LDS
+//      (free slots, last_use = -1, get the smallest keys);
+//   2. selected tokens look up the page table; hit slots get the key of the
+//      current step, which sorts them after every evictable slot;
+//   3. misses are ranked in selection order (block prefix sums);
+//   4. a bitonic sort of the keys in LDS orders the slots by
+//      (last_use, slot); the r-th miss takes the r-th slot;
+//   5. page table, slot owners and stamps are updated in place;
+//   6. the missed tokens' K and V rows (all KV heads, contiguous in the host
+//      copy) are read straight from host-mapped memory and stored into the
+//      slots, one wave per missed token, 16 B per lane.
+// Token ids outside [0, N) are ignored (slot -1) so a bad selection cannot
+// address memory outside the tables.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace tsa {
+
+constexpr int kResolveThreads = 1024;
+constexpr int kResolvePer = kMaxTokenK / kResolveThreads;  // selected tokens per thread
+
+__global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams p, int spow2) {
+  constexpr int NW = kResolveThreads / kWave;
+  extern __shared__ unsigned long long lds[];
+  unsigned long long* sk = lds;                                   // [spow2]
+  int32_t* miss_tok = reinterpret_cast<int32_t*>(lds + spow2);     // [k]
+  int32_t* miss_slot = miss_tok + p.k;                            // [k]
+  __shared__ int scratch[NW];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int32_t* pt = p.page_table + static_cast<long long>(b) * p.N;
+  int32_t* st = p.slot_token + static_cast<long long>(b) * p.S;
+  int32_t* lu = p.last_use + static_cast<long long>(b) * p.S;
+  const int32_t* sel = p.sel + static_cast<long long>(b) * p.k;
+  const unsigned long long now = static_cast<unsigned long long>(static_cast<uint32_t>(p.step + 1)) << 32;
+
+  for (int s = tid; s < spow2; s += kResolveThreads) {
+    sk[s] = s < p.S ? (static_cast<unsigned long long>(static_cast<uint32_t>(lu[s] + 1)) << 32) |
+                          static_cast<uint32_t>(s)
+                    : ~0ull;
+  }
+  __syncthreads();
+
+  int tok[kResolvePer], slot[kResolvePer];
+#pragma unroll
+  for (int j = 0; j < kResolvePer; ++j) {
+    const int i = tid + j * kResolveThreads;
+    tok[j] = -1;
+    slot[j] = -1;
+    if (i < p.k) {
+      const int t = sel[i];
+      if (t >= 0 && t < p.N) {
+        tok[j] = t;
+        const int sl = pt[t];
+        slot[j] = (sl >= 0 && sl < p.S) ? sl : -1;  // a corrupt entry counts as absent
+        if (slot[j] >= 0) sk[slot[j]] = now | static_cast<uint32_t>(slot[j]);
+      }
+    }
+  }
+  int rank[kResolvePer];
+  int n_miss = 0, n_hit = 0;
+#pragma unroll
+  for (int j = 0; j < kResolvePer; ++j) {
+    const bool miss = tok[j] >= 0 && slot[j] < 0;
+    int tot;
+    rank[j] = n_miss + block_exclusive_scan<NW>(miss ? 1 : 0, scratch, &tot);
+    n_miss += tot;
+    n_hit += block_sum<NW>(tok[j] >= 0 && slot[j] >= 0 ? 1 : 0, scratch);
+  }
+  __syncthreads();
+
+  for (int size = 2; size <= spow2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (spow2 >> 1); i += kResolveThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool ascending = (lo & size) == 0;
+        const unsigned long long a = sk[lo], c = sk[hi];
+        if ((a > c) == ascending) {
+          sk[lo] = c;
+          sk[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < kResolvePer; ++j) {
+    const int i = tid + j * kResolveThreads;
+    if (tok[j] < 0) {
+      if (i < p.k) p.slots_out[static_cast<long long>(b) * p.k + i] = -1;
+      continue;
+    }
+    if (slot[j] >= 0) {
+      lu[slot[j]] = p.step;
+    } else {
+      const int v = static_cast<int>(sk[rank[j]] & 0xffffffffu);
+      const int old = st[v];
+      if (old >= 0 && old < p.N) pt[old] = -1;
+      pt[tok[j]] = v;
+      st[v] = tok[j];
+      lu[v] = p.step;
+      slot[j] = v;
+      miss_tok[rank[j]] = tok[j];
+      miss_slot[rank[j]] = v;
+    }
+    p.slots_out[static_cast<long long>(b) * p.k + i] = slot[j];
+  }
+  if (tid == 0) {
+    if (p.hits) p.hits[b] = n_hit;
+    if (p.misses) p.misses[b] = n_miss;
+  }
+  __syncthreads();
+
+  // Fetch: one wave per missed token; lanes stride over its 16-B chunks, K and
+  // V rows loaded together so each lane keeps four 16-B host reads in flight.
+  const int chunks = static_cast<int>(p.row_bytes / 16);
+  const int lane = lane_id(), wave = tid / kWave;
+  const char* hk = static_cast<const char*>(p.host_k);
+  const char* hv = static_cast<const char*>(p.host_v);
+  char* pk = static_cast<char*>(p.pool_k);
+  char* pv = static_cast<char*>(p.pool_v);
+  for (int r = wave; r < n_miss; r += NW) {
+    const long long src = (static_cast<long long>(b) * p.N + miss_tok[r]) * p.row_bytes;
+    const long long dst = (static_cast<long long>(b) * p.S + miss_slot[r]) * p.row_bytes;
+    const uint4* sk4 = reinterpret_cast<const uint4*>(hk + src);
+    const uint4* sv4 = reinterpret_cast<const uint4*>(hv + src);
+    uint4* dk4 = reinterpret_cast<uint4*>(pk + dst);
+    uint4* dv4 = reinterpret_cast<uint4*>(pv + dst);
+    for (int c = lane; c < chunks; c += 2 * kWave) {
+      const bool two = c + kWave < chunks;
+      const uint4 k0 = sk4[c], v0 = sv4[c];
+      uint4 k1 = k0, v1 = v0;
+      if (two) {
+        k1 = sk4[c + kWave];
+        v1 = sv4[c + kWave];
+      }
+      dk4[c] = k0;
+      dv4[c] = v0;
+      if (two) {
+        dk4[c + kWave] = k1;
+        dv4[c + kWave] = v1;
+      }
+    }
+  }
+}
+
+hipError_t launch_resolve(const ResolveParams& p, hipStream_t s) {
+  int spow2 = 1;
+  while (spow2 < p.S) spow2 <<= 1;
+  const size_t lds = static_cast<size_t>(spow2) * sizeof(unsigned long long) +
+                     2 * static_cast<size_t>(p.k) * sizeof(int32_t);
+  hipLaunchKernelGGL(resolve_kernel, dim3(p.B), dim3(kResolveThreads), lds, s, p, spow2);
+  return hipGetLastError();
+}
+
+}  // namespace tsa
