@@ -74,7 +74,7 @@ def test_workspace_sizes_and_validation(lib):
     with pytest.raises(B.TsaError, match="UNSUPPORTED"):   # too many merge candidates
         B.workspace_bytes(B.OP_TOKEN_DECODE, B.TokenDesc(1, 2_000_000, 8, 32, 128, 64, 1), 4096)
     a = B.AttnDesc(32, 4096, 8, 32, 128, 2048, B.TSA_BF16)
-    assert B.workspace_bytes(B.OP_ATTEND_ROWS, a) == 32 * 8 * 8 * 4 * 132 * 4
+    assert B.workspace_bytes(B.OP_ATTEND_ROWS, a) == 32 * 8 * (2048 // 64) * 4 * 132 * 4
 
 
 def test_calls_reject_bad_arguments_before_any_launch(lib):

@@ -83,7 +83,7 @@ struct TokLayout {
 TokLayout tok_layout(const tsa_token_desc& d, int k) {
   TokLayout L;
   L.G = d.n_q_heads / d.n_kv_heads;
-  L.smax = ceil_div(k, kSegRows);
+  L.smax = ceil_div(k, kRowSegRows);
   L.nchunk = ceil_div(d.n_tokens, kTokChunk);
   const size_t ncand = static_cast<size_t>(d.batch) * L.nchunk * k;
   size_t off = 0;
@@ -104,7 +104,7 @@ struct RowsLayout {
 RowsLayout rows_layout(const tsa_attn_desc& d) {
   RowsLayout L;
   L.G = d.n_q_heads / d.n_kv_heads;
-  L.smax = std::max(1, ceil_div(d.max_rows, kSegRows));
+  L.smax = std::max(1, ceil_div(d.max_rows, kRowSegRows));
   L.total = align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * L.smax * L.G * kPartStride * sizeof(float));
   return L;
 }
@@ -310,7 +310,8 @@ tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void
   gp.seg = reinterpret_cast<const int4*>(w + L.seg); gp.nseg = reinterpret_cast<const int32_t*>(w + L.nseg);
   gp.counts = nullptr; gp.count_const = 0;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
-  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax; gp.W = std::min(L.smax, L.G * k);
+  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
+  gp.W = ceil_div(std::min(L.smax, L.G * k), kGatherWavesPerBlock); gp.seg_rows = kSegRows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, true, s)) return st;
   return ok();
@@ -340,7 +341,8 @@ tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const
   gp.rowids = sel; gp.rid_bstride = k; gp.rid_gstride = 0;
   gp.seg = nullptr; gp.nseg = nullptr; gp.counts = nullptr; gp.count_const = k; gp.count_max = k;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
-  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax; gp.W = L.smax;
+  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
+  gp.W = ceil_div(L.smax, kGatherWavesPerBlock); gp.seg_rows = kRowSegRows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
   return ok();
@@ -364,7 +366,8 @@ tsa_status tsa_attend_rows(const tsa_attn_desc* desc, const void* q, const void*
   gp.seg = nullptr; gp.nseg = nullptr; gp.counts = row_counts; gp.count_const = d.max_rows;
   gp.count_max = d.max_rows;
   gp.partial = static_cast<float*>(ws); gp.out = out;
-  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax; gp.W = L.smax;
+  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
+  gp.W = ceil_div(L.smax, kGatherWavesPerBlock); gp.seg_rows = kRowSegRows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
   return ok();

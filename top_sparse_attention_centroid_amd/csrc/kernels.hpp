@@ -10,7 +10,9 @@
 namespace tsa {
 
 constexpr int kHeadDimRows = 128;   // d: elements per row (head_dim)
-constexpr int kSegRows = 256;       // rows per attention segment (one workgroup pass)
+constexpr int kSegRows = 256;       // max rows per attention segment (one wave's work unit)
+constexpr int kRowSegRows = 64;     // segment rows for per-request row lists (token / slot paths)
+constexpr int kGatherWavesPerBlock = 4;
 constexpr int kPartStride = 132;    // floats per partial state: m, l, 2 pad, o[128]
 constexpr int kTokChunk = 8192;     // indexer tokens per workgroup (keys kept in LDS)
 constexpr int kMergeThreads = 1024; // threads of the per-request top-k merge
@@ -77,9 +79,10 @@ struct GatherParams {
   const int32_t* counts;   // implicit: rows per request, or null
   int count_const;         // implicit: rows per request when counts is null
   int count_max;           // implicit: capacity of each request's row-id array
+  int seg_rows;            // implicit: rows per segment (<= kSegRows)
   float* partial;          // [B*Hkv][smax][G][kPartStride]
   float* out;              // [B][Hq][d]
-  int B, Hkv, smax, W;
+  int B, Hkv, smax, W;     // W: workgroups per (request, KV head), 4 segments each in flight
   float qscale;            // log2(e) / sqrt(d)
 };
 hipError_t launch_gather(const GatherParams& p, int dtype, int G, bool explicit_plan,
