@@ -85,7 +85,7 @@ typedef struct tsa_ivf_desc {
   int32_t n_q_heads;       /* Hq; Hq / Hkv in {1, 2, 4, 8}                 */
   int32_t head_dim;        /* d; must be 128                               */
   int32_t n_centroids;     /* C lists per (request, KV head); C <= 4096 and
-                              C * (Hq / Hkv + 1) <= 16384                  */
+                              C * (Hq / Hkv + 2) < 16384                   */
   int32_t shared_codebook; /* 1: centroids [Hkv][C][d] for all requests;
                               0: centroids [B][Hkv][C][d]                 */
   int32_t dtype;           /* tsa_dtype of q, keys, values, centroids     */

@@ -7,7 +7,7 @@
 // with the head mask of the GQA group's query heads that chose them, so a row
 // chosen by several heads of the group is read from HBM once. Each wave owns
 // whole segments: 16 lanes cover one 256-B bf16 row (16 B each), a wave load
-// instruction fetches 4 rows, and a batch of 16 rows is in flight while the
+// instruction fetches 4 rows, and a batch of rows is in flight while the
 // previous batch is scored (double buffering in registers). Each lane group
 // keeps an online-softmax state (running max m, sum l, output o) in the log2
 // domain; the four lane groups merge by lane shuffles and the segment writes
@@ -20,96 +20,113 @@
 namespace tsa {
 
 constexpr int kGatherWaves = kGatherWavesPerBlock;  // each wave owns whole segments
-constexpr int kGatherUnroll = 4;  // rows per 16-lane group per batch (a batch is 16 rows per wave)
-constexpr int kBatchRows = 4 * kGatherUnroll;
+#ifndef TSA_GATHER_UNROLL
+#define TSA_GATHER_UNROLL 4
+#endif
+#ifndef TSA_GATHER_NT
+#define TSA_GATHER_NT 1  // K/V rows are read once per call: non-temporal loads
+#endif
+#ifndef TSA_GATHER_WAVES_PER_EU
+#define TSA_GATHER_WAVES_PER_EU 0
+#endif
+#if TSA_GATHER_WAVES_PER_EU
+#define TSA_GATHER_OCC __attribute__((amdgpu_waves_per_eu(TSA_GATHER_WAVES_PER_EU, TSA_GATHER_WAVES_PER_EU)))
+#else
+#define TSA_GATHER_OCC
+#endif
+constexpr int kGatherUnroll = TSA_GATHER_UNROLL;  // rows per 16-lane group per batch
+constexpr int kBatchRows = 4 * kGatherUnroll;      // rows per wave per batch
 
-template <int G>
-struct SoftmaxState {
-  float m[G], l[G], o[G][8];
+// Online-softmax state of one query head in one 16-lane group (log2 domain).
+// The running max starts at a finite sentinel instead of -inf so masked rows
+// can be folded in with selects (no -inf - -inf); a state that saw no valid
+// row keeps l = 0 and contributes nothing when merged.
+constexpr float kEmptyMax = -1e30f;   // running max before any valid row
+constexpr float kMaskedScore = -3e30f; // score of a masked row: exp2(kMasked - m) == 0
+
+struct HeadState {
+  float m, l, o[8];
   __device__ __forceinline__ void init() {
+    m = kEmptyMax;
+    l = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      m[h] = -INFINITY;
-      l[h] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
-    }
+    for (int i = 0; i < 8; ++i) o[i] = 0.f;
   }
 };
 
-__device__ __forceinline__ void merge_into(float& m, float& l, float (&o)[8], float m2, float l2,
-                                           const float (&o2)[8]) {
-  const float M = fmaxf(m, m2);
-  if (M == -INFINITY) return;
-  const float a = fast_exp2(m - M), c = fast_exp2(m2 - M);
-  l = l * a + l2 * c;
+__device__ __forceinline__ void merge_into(HeadState& a, float m2, float l2, const float (&o2)[8]) {
+  const float M = fmaxf(a.m, m2);
+  const float x = fast_exp2(a.m - M), y = fast_exp2(m2 - M);
+  a.l = a.l * x + l2 * y;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = o[i] * a + o2[i] * c;
-  m = M;
+  for (int i = 0; i < 8; ++i) a.o[i] = a.o[i] * x + o2[i] * y;
+  a.m = M;
 }
 
-// K and V rows of one batch (16 rows per wave: lane group r = lane / 16 takes
-// rows r, r + 4, r + 8, r + 12 of the batch), raw bits in registers.
+// K and V rows of one batch: lane group r = lane / 16 takes rows r, r+4, ...
+// of the batch; raw bits stay in registers until scored.
 template <typename T>
 struct Batch {
   Raw8<T> k[kGatherUnroll], v[kGatherUnroll];
-  int row[kGatherUnroll];
+  bool valid[kGatherUnroll];
 };
 
+// Straight-line issue: every lane loads, rows past the segment end or with a
+// rejected id load row 0 of the request (always in bounds) and are masked at
+// scoring. Without control flow around the loads the compiler keeps all of
+// them in flight (a predicated load would force a wait for every earlier one).
 template <typename T>
 __device__ __forceinline__ void issue_batch(Batch<T>& bt, const int* ids, int base, int cnt, int r,
                                             const T* kb, const T* vb, long long row_stride) {
+  int row[kGatherUnroll];
 #pragma unroll
   for (int u = 0; u < kGatherUnroll; ++u) {
     const int j = base + u * 4 + r;
-    bt.row[u] = j < cnt ? ids[j] : -1;
+    const int id = ids[min(j, kSegRows - 1)];
+    bt.valid[u] = (j < cnt) & (id >= 0);
+    row[u] = bt.valid[u] ? id : 0;
   }
+#if TSA_GATHER_NT
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u)
-    if (bt.row[u] >= 0) bt.k[u].load(kb + bt.row[u] * row_stride);
+  for (int u = 0; u < kGatherUnroll; ++u) bt.k[u].load_stream(kb + row[u] * row_stride);
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u)
-    if (bt.row[u] >= 0) bt.v[u].load(vb + bt.row[u] * row_stride);
+  for (int u = 0; u < kGatherUnroll; ++u) bt.v[u].load_stream(vb + row[u] * row_stride);
+#else
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u) bt.k[u].load(kb + row[u] * row_stride);
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u) bt.v[u].load(vb + row[u] * row_stride);
+#endif
 }
 
-template <typename T, int G>
-__device__ __forceinline__ void consume_batch(const Batch<T>& bt, SoftmaxState<G>& st, uint32_t mask,
-                                              const float* qs, int e) {
+template <typename T>
+__device__ __forceinline__ void consume_batch(const Batch<T>& bt, HeadState& st, const float (&qf)[8]) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (!(mask & (1u << h))) continue;
-    float qf[8];
-    {
-      const float4 a = *reinterpret_cast<const float4*>(qs + h * kHeadDim + e * 8);
-      const float4 b = *reinterpret_cast<const float4*>(qs + h * kHeadDim + e * 8 + 4);
-      qf[0] = a.x; qf[1] = a.y; qf[2] = a.z; qf[3] = a.w;
-      qf[4] = b.x; qf[5] = b.y; qf[6] = b.z; qf[7] = b.w;
-    }
+  for (int u = 0; u < kGatherUnroll; ++u) {
+    float kx[8], vx[8];
+    bt.k[u].widen(kx);
+    bt.v[u].widen(vx);
+    const float sc = bt.valid[u] ? group16_sum(dot8(qf, kx)) : kMaskedScore;
+    const float mn = fmaxf(st.m, sc);
+    const float a = fast_exp2(st.m - mn);
+    const float pw = fast_exp2(sc - mn);
+    st.l = fmaf(st.l, a, pw);
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
-      if (bt.row[u] < 0) continue;
-      float kx[8], vx[8];
-      bt.k[u].widen(kx);
-      bt.v[u].widen(vx);
-      const float sc = group16_sum(dot8(qf, kx));
-      const float mn = fmaxf(st.m[h], sc);
-      const float a = fast_exp2(st.m[h] - mn);
-      const float pw = fast_exp2(sc - mn);
-      st.l[h] = fmaf(st.l[h], a, pw);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) st.o[h][i] = fmaf(pw, vx[i], st.o[h][i] * a);
-      st.m[h] = mn;
-    }
+    for (int i = 0; i < 8; ++i) st.o[i] = fmaf(pw, vx[i], st.o[i] * a);
+    st.m = mn;
   }
 }
 
 // gather_attn: every wave processes whole segments on its own (no block
 // barrier after the q staging). Per segment: row ids -> wave-private LDS in
-// one round trip, then K/V batches double-buffered in registers (batch i+1 in
-// flight while batch i is scored), then the four lane groups merge and lanes
-// 0..15 write the segment's partial state per masked head.
+// one round trip; then, for each query head in the segment's mask, one pass
+// over the rows with K/V batches double-buffered in registers (batch i+1 in
+// flight while batch i is scored). A second head's pass re-reads rows the
+// first pass just brought into L2, so HBM sees each row once while a wave
+// carries the state of a single head (which keeps occupancy high). The four
+// lane groups then merge and lanes 0..15 write the head's partial state.
 template <typename T, int G, bool EXPLICIT>
-__global__ __launch_bounds__(kGatherWaves * kWave) void gather_attn_kernel(GatherParams p) {
+__global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_attn_kernel(GatherParams p) {
   constexpr int NW = kGatherWaves;
   __shared__ float qs[G * kHeadDim];
   __shared__ int ids_lds[NW][kSegRows];
@@ -169,42 +186,46 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_attn_kernel(Gathe
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    SoftmaxState<G> st;
-    st.init();
-    Batch<T> A, Bb;
-    issue_batch(A, ids, 0, cnt, r, kb, vb, row_stride);
-    for (int base = 0; base < cnt; base += 2 * kBatchRows) {
-      const bool has_b = base + kBatchRows < cnt;
-      if (has_b) issue_batch(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride);
-      consume_batch(A, st, mask, qs, e);
-      if (has_b) {
-        if (base + 2 * kBatchRows < cnt) issue_batch(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride);
-        consume_batch(Bb, st, mask, qs, e);
-      }
-    }
-
-    // Merge the four 16-lane row groups (lanes e, e+16, e+32, e+48) and write
-    // the segment's partial for every masked head.
     float* part = p.partial + (static_cast<long long>(bg) * p.smax + s) * G * kPartStride;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (!(mask & (1u << h))) continue;
+    for (uint32_t hm = mask; hm != 0u; hm &= hm - 1u) {
+      const int h = __builtin_ctz(hm);
+      float qf[8];
+      {
+        const float4 a = *reinterpret_cast<const float4*>(qs + h * kHeadDim + e * 8);
+        const float4 c = *reinterpret_cast<const float4*>(qs + h * kHeadDim + e * 8 + 4);
+        qf[0] = a.x; qf[1] = a.y; qf[2] = a.z; qf[3] = a.w;
+        qf[4] = c.x; qf[5] = c.y; qf[6] = c.z; qf[7] = c.w;
+      }
+      HeadState st;
+      st.init();
+      // batches are taken in pairs; the pair loop always issues one batch
+      // ahead (past the end it reloads row 0, masked), so no load sits under
+      // a branch
+      Batch<T> A, Bb;
+      issue_batch(A, ids, 0, cnt, r, kb, vb, row_stride);
+      for (int base = 0; base < cnt; base += 2 * kBatchRows) {
+        issue_batch(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride);
+        consume_batch(A, st, qf);
+        issue_batch(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride);
+        consume_batch(Bb, st, qf);
+      }
+      // merge the four 16-lane row groups (lanes e, e+16, e+32, e+48)
 #pragma unroll
       for (int x = 16; x <= 32; x <<= 1) {
         float o2[8];
-        const float m2 = __shfl_xor(st.m[h], x);
-        const float l2 = __shfl_xor(st.l[h], x);
+        const float m2 = __shfl_xor(st.m, x);
+        const float l2 = __shfl_xor(st.l, x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o2[i] = __shfl_xor(st.o[h][i], x);
-        merge_into(st.m[h], st.l[h], st.o[h], m2, l2, o2);
+        for (int i = 0; i < 8; ++i) o2[i] = __shfl_xor(st.o[i], x);
+        merge_into(st, m2, l2, o2);
       }
       if (r == 0) {
         float* ph = part + h * kPartStride;
-        *reinterpret_cast<float4*>(ph + 4 + e * 8) = make_float4(st.o[h][0], st.o[h][1], st.o[h][2], st.o[h][3]);
-        *reinterpret_cast<float4*>(ph + 8 + e * 8) = make_float4(st.o[h][4], st.o[h][5], st.o[h][6], st.o[h][7]);
+        *reinterpret_cast<float4*>(ph + 4 + e * 8) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
+        *reinterpret_cast<float4*>(ph + 8 + e * 8) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
         if (e == 0) {
-          ph[0] = st.m[h];
-          ph[1] = st.l[h];
+          ph[0] = st.m;
+          ph[1] = st.l;
         }
       }
     }
@@ -240,7 +261,7 @@ __global__ __launch_bounds__(512) void combine_kernel(GatherParams p) {
     const int rows = min(max(p.counts ? p.counts[b] : p.count_const, 0), p.count_max);
     nseg = (rows + p.seg_rows - 1) / p.seg_rows;
   }
-  float M = -INFINITY, L = 0.f, O0 = 0.f, O1 = 0.f;
+  float M = kEmptyMax, L = 0.f, O0 = 0.f, O1 = 0.f;
   const float* base = p.partial + static_cast<long long>(bg) * p.smax * G * kPartStride + h * kPartStride;
   for (int s0 = 0; s0 < nseg; s0 += kWave) {
     const int s = s0 + lane;
@@ -249,17 +270,16 @@ __global__ __launch_bounds__(512) void combine_kernel(GatherParams p) {
       if (mine) mine = (static_cast<uint32_t>(p.seg[static_cast<long long>(bg) * p.smax + s].z) >> h) & 1u;
     }
     const float* ph = base + static_cast<long long>(s) * G * kPartStride;
-    const float pm = mine ? ph[0] : -INFINITY;
+    const float pm = mine ? ph[0] : kMaskedScore;
     const float pl = mine ? ph[1] : 0.f;
     const float Mn = fmaxf(M, wave_max_f(pm));
-    if (Mn == -INFINITY) continue;
     const float w = mine ? fast_exp2(pm - Mn) : 0.f;
     const float a = fast_exp2(M - Mn);
     L = L * a + wave_sum_f(pl * w);
     O0 *= a;
     O1 *= a;
     M = Mn;
-    uint64_t bal = __ballot(mine && pm != -INFINITY);
+    uint64_t bal = __ballot(mine);
     while (bal) {
       int j[4];
       float wj[4];
@@ -271,14 +291,13 @@ __global__ __launch_bounds__(512) void combine_kernel(GatherParams p) {
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        wj[u] = __shfl(w, j[u] < 0 ? 0 : j[u]);
-        po[u] = j[u] < 0 ? make_float2(0.f, 0.f)
-                         : *reinterpret_cast<const float2*>(base + static_cast<long long>(s0 + j[u]) * G * kPartStride +
-                                                            4 + lane * 2);
+        const int jj = j[u] < 0 ? 0 : j[u];  // j < 0: reload segment s0 (in range), weight 0
+        wj[u] = j[u] < 0 ? 0.f : __shfl(w, jj);
+        po[u] = *reinterpret_cast<const float2*>(base + static_cast<long long>(s0 + jj) * G * kPartStride +
+                                                 4 + lane * 2);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (j[u] < 0) continue;
         O0 = fmaf(wj[u], po[u].x, O0);
         O1 = fmaf(wj[u], po[u].y, O1);
       }

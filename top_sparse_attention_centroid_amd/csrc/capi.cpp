@@ -58,7 +58,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 // ----------------------------------------------------------------- layouts
 struct IvfLayout {
   int G = 0, smax = 0;
-  size_t scores = 0, seg = 0, nseg = 0, partial = 0, total = 0;
+  size_t seg = 0, nseg = 0, partial = 0, total = 0;
 };
 
 IvfLayout ivf_layout(const tsa_ivf_desc& d, int k) {
@@ -67,7 +67,6 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k) {
   L.smax = L.G * k + ceil_div(d.n_tokens, kSegRows);
   const size_t bh = static_cast<size_t>(d.batch) * d.n_kv_heads;
   size_t off = 0;
-  L.scores = off; off += align_up(static_cast<size_t>(d.batch) * d.n_q_heads * d.n_centroids * sizeof(float));
   L.seg = off;    off += align_up(bh * L.smax * sizeof(int4));
   L.nseg = off;   off += align_up(bh * sizeof(int32_t));
   L.partial = off; off += align_up(bh * L.smax * L.G * kPartStride * sizeof(float));
@@ -128,7 +127,7 @@ tsa_status check_ivf(const tsa_ivf_desc* d) {
   if (!valid_group(d->n_q_heads, d->n_kv_heads))
     return fail(TSA_ERR_UNSUPPORTED, "n_q_heads/n_kv_heads = %d/%d is not 1, 2, 4 or 8", d->n_q_heads, d->n_kv_heads);
   const int G = d->n_q_heads / d->n_kv_heads;
-  if (d->n_centroids > kMaxCentroids || static_cast<long long>(d->n_centroids) * (G + 1) > 16384)
+  if (d->n_centroids > kMaxCentroids || static_cast<long long>(d->n_centroids) * (G + 2) + 1 > 16384)
     return fail(TSA_ERR_UNSUPPORTED, "n_centroids %d too large for group %d", d->n_centroids, G);
   if (d->shared_codebook != 0 && d->shared_codebook != 1)
     return fail(TSA_ERR_INVALID_ARG, "shared_codebook must be 0 or 1");
@@ -294,14 +293,10 @@ tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void
   hipStream_t s = as_stream(stream);
   const long long cbs = d.shared_codebook ? 0LL : static_cast<long long>(d.n_kv_heads) * d.n_centroids * kHeadDimRows;
 
-  ScoreParams sp{q, centroids, cbs, reinterpret_cast<float*>(w + L.scores), d.batch, d.n_kv_heads, d.n_centroids};
-  hipError_t e = launch_centroid_scores(sp, d.dtype, L.G, s);
-  if (e != hipSuccess) return hip_fail(e, "centroid_scores launch");
-
-  SelectParams selp{reinterpret_cast<const float*>(w + L.scores), offsets, sel_out, rows_out, uniq_out,
+  SelectParams selp{q, centroids, cbs, offsets, sel_out, rows_out, uniq_out,
                     reinterpret_cast<int4*>(w + L.seg), reinterpret_cast<int32_t*>(w + L.nseg),
                     d.batch, d.n_kv_heads, d.n_centroids, k, L.smax, d.n_tokens};
-  e = launch_ivf_select(selp, L.G, s);
+  hipError_t e = launch_ivf_select(selp, d.dtype, L.G, s);
   if (e != hipSuccess) return hip_fail(e, "ivf_select launch");
 
   GatherParams gp{};

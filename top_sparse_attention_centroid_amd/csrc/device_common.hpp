@@ -20,10 +20,20 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 template <typename T>
 struct Raw8;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load; the streaming variant is for data touched once per call.
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <>
 struct Raw8<bf16_t> {
   uint4 v;
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_stream(const bf16_t* p) { v = load16_stream(p); }
   __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void widen(float (&x)[8]) const {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
@@ -39,6 +49,11 @@ struct Raw8<float> {
   __device__ __forceinline__ void load(const float* p) {
     a = reinterpret_cast<const float4*>(p)[0];
     b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void load_stream(const float* p) {
+    const uint4 x = load16_stream(p), y = load16_stream(p + 4);
+    a = make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+    b = make_float4(__uint_as_float(y.x), __uint_as_float(y.y), __uint_as_float(y.z), __uint_as_float(y.w));
   }
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ void widen(float (&x)[8]) const {

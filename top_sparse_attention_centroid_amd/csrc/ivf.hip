@@ -138,98 +138,86 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 }
 
 // ============================================================================
-// Centroid scoring ([KARAT] worked example, step 3): s[b][h][c] = q[b][h] .
-// centroid[g][c], raw dot product in fp32. A workgroup scores 64 centroids
-// for the G query heads of one KV group; 16 lanes cover one 128-element row
-// (8 elements each) and reduce through DPP.
+// Centroid scoring, top-k lists per query head, and the gather plan of the
+// KV group, fused in one workgroup (4 waves) per (request, KV head).
+//
+// Scoring ([KARAT] worked example, step 3): s[h][c] = q[h] . centroid[g][c],
+// raw dot product in fp32; 16 lanes cover one 128-element centroid row (8
+// elements each) and reduce through DPP, four rows per wave load. Scores go to
+// LDS as order-preserving keys, next to the list offsets.
+//
+// Top-k ([KARAT] How: the top-k most similar lists): wave w owns query heads
+// w, w + 4 of the group. The k-th largest key T is found bit by bit (MSB
+// first) with ballot counts; keys above it are taken, then keys equal to it in
+// ascending list order until k are taken (ties -> lower list id). Lists are
+// emitted in ascending order through ballot prefix counts.
+//
+// Plan: the union of the group's chosen lists with a head bitmask per list,
+// each list cut into segments of at most kSegRows rows, ascending list order.
 // ============================================================================
 template <typename T, int G>
-__global__ __launch_bounds__(256) void centroid_scores_kernel(ScoreParams p) {
-  const int bg = blockIdx.y;
-  const int b = bg / p.Hkv, g = bg % p.Hkv;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int r = lane >> 4, e = lane & 15;
-  const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
-  float qf[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) load8(qb + h * kHeadDim + e * 8, qf[h]);
-  const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
-                static_cast<long long>(g) * p.C * kHeadDim;
-  const int cbase = blockIdx.x * 64 + wave * 16;
-  Raw8<T> raw[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = cbase + u * 4 + r;
-    if (c < p.C) raw[u].load(cb + static_cast<long long>(c) * kHeadDim + e * 8);
-    else raw[u].zero();
-  }
-  float* out = p.scores + (static_cast<long long>(b) * p.Hkv + g) * G * p.C;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = cbase + u * 4 + r;
-    float x[8];
-    raw[u].widen(x);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float s = group16_sum(dot8(qf[h], x));
-      if (e == 0 && c < p.C) out[h * p.C + c] = s;
-    }
-  }
-}
-
-// ============================================================================
-// Top-k lists per query head + gather plan per KV group.
-// One workgroup of 4 waves per (request, KV head); wave w owns query heads
-// w, w + 4 of the group. Top-k: the k-th largest order-preserving key T is found bit by bit
-// (MSB first) with ballot counts; keys above T are taken, and keys equal to T
-// in ascending list order until k are taken (ties -> lower list id). Lists
-// are emitted in ascending order through ballot prefix counts.
-// Plan: the union of the G heads' lists (head bitmask per list), each list cut
-// into segments of at most kSegRows rows, in ascending list order.
-// ============================================================================
-// List c of a CSR index, clamped to [0, N] so malformed offsets cannot send
-// the gather outside the id array.
-__device__ __forceinline__ int list_start(const int32_t* off, int c, int N) {
-  return min(max(off[c], 0), N);
-}
-__device__ __forceinline__ int list_len(const int32_t* off, int c, int N) {
-  const int s = list_start(off, c, N);
-  return min(max(off[c + 1], s), N) - s;
-}
-
-template <int G>
 __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
-  extern __shared__ float smem[];
-  float* s = smem;                                              // [G][C]
-  uint32_t* lmask = reinterpret_cast<uint32_t*>(smem + G * p.C);  // [C]
+  extern __shared__ uint32_t smem[];
+  const int C = p.C, k = p.k;
+  uint32_t* keys = smem;                              // [G][C]
+  uint32_t* lmask = smem + G * C;                     // [C]
+  int* loff = reinterpret_cast<int*>(smem + (G + 1) * C);  // [C+1], clamped to [0, N]
   __shared__ int scan_scratch[4];
   const int bg = blockIdx.x;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int C = p.C, k = p.k;
-  const int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
+  const int r = lane >> 4, e = lane & 15;
 
-  const float* src = p.scores + static_cast<long long>(bg) * G * C;
-  for (int i = tid; i < G * C; i += 256) s[i] = src[i];
+  const int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
+  for (int c = tid; c <= C; c += 256) loff[c] = min(max(off[c], 0), p.N);
   for (int c = tid; c < C; c += 256) lmask[c] = 0u;
+
+  {
+    const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
+    float qf[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) load8(qb + h * kHeadDim + e * 8, qf[h]);
+    const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
+                  static_cast<long long>(g) * C * kHeadDim + e * 8;
+    constexpr int U = 4;  // centroid rows in flight per lane group
+    for (int c0 = wave * 4; c0 < C; c0 += 16 * U) {
+      Raw8<T> raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = min(c0 + u * 16 + r, C - 1);  // clamped: straight-line loads
+        raw[u].load(cb + static_cast<long long>(c) * kHeadDim);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 16 + r;
+        float x[8];
+        raw[u].widen(x);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float sc = group16_sum(dot8(qf[h], x));
+          if (e == 0 && c < C) keys[h * C + c] = order_key(sc);
+        }
+      }
+    }
+  }
   __syncthreads();
 
   for (int h = wave; h < G; h += 4) {
-    const float* sh = s + h * C;
-    uint32_t T = 0;
+    const uint32_t* kh = keys + h * C;
+    uint32_t thr = 0;
     for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
+      const uint32_t cand = thr | (1u << bit);
       int cnt = 0;
       for (int c0 = 0; c0 < C; c0 += kWave) {
         const int c = c0 + lane;
-        cnt += __popcll(__ballot(c < C && order_key(sh[c]) >= cand));
+        cnt += __popcll(__ballot(c < C && kh[c] >= cand));
       }
-      if (cnt >= k) T = cand;
+      if (cnt >= k) thr = cand;
     }
     int n_gt = 0;
     for (int c0 = 0; c0 < C; c0 += kWave) {
       const int c = c0 + lane;
-      n_gt += __popcll(__ballot(c < C && order_key(sh[c]) > T));
+      n_gt += __popcll(__ballot(c < C && kh[c] > thr));
     }
     const int need_eq = k - n_gt;
     const int qh = g * G + h;
@@ -237,16 +225,16 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     int base = 0, eq_seen = 0, rows = 0;
     for (int c0 = 0; c0 < C; c0 += kWave) {
       const int c = c0 + lane;
-      const uint32_t key = c < C ? order_key(sh[c]) : 0u;
-      const bool gt = c < C && key > T;
-      const bool eq = c < C && key == T;
+      const uint32_t key = c < C ? kh[c] : 0u;
+      const bool gt = c < C && key > thr;
+      const bool eq = c < C && key == thr;
       const uint64_t eqm = __ballot(eq);
       const bool take = gt || (eq && eq_seen + prefix_count(eqm) < need_eq);
       const uint64_t tm = __ballot(take);
       if (take) {
         if (sel) sel[base + prefix_count(tm)] = c;
         atomicOr(&lmask[c], 1u << h);
-        rows += list_len(off, c, p.N);
+        rows += max(loff[c + 1] - loff[c], 0);
       }
       base += __popcll(tm);
       eq_seen += __popcll(eqm);
@@ -261,8 +249,8 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   for (int c0 = 0; c0 < C; c0 += 256) {
     const int c = c0 + tid;
     const uint32_t m = c < C ? lmask[c] : 0u;
-    const int start = c < C ? list_start(off, c, p.N) : 0;
-    const int len = c < C ? list_len(off, c, p.N) : 0;
+    const int start = c < C ? loff[c] : 0;
+    const int len = c < C ? max(loff[c + 1] - start, 0) : 0;
     const int nsg = (m != 0u && len > 0) ? (len + kSegRows - 1) / kSegRows : 0;
     uniq += m != 0u ? len : 0;
     int tot;
@@ -297,31 +285,20 @@ hipError_t launch_csr(const CsrParams& p, hipStream_t s) {
 }
 
 template <typename T>
-static void scores_dispatch(const ScoreParams& p, int G, hipStream_t s) {
-  dim3 grid((p.C + 63) / 64, p.B * p.Hkv);
+static void select_dispatch(const SelectParams& p, int G, size_t lds, hipStream_t s) {
+  const dim3 grid(p.B * p.Hkv);
   switch (G) {
-    case 1: hipLaunchKernelGGL((centroid_scores_kernel<T, 1>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((centroid_scores_kernel<T, 2>), grid, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((centroid_scores_kernel<T, 4>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((centroid_scores_kernel<T, 8>), grid, dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((ivf_select_kernel<T, 1>), grid, dim3(256), lds, s, p); break;
+    case 2: hipLaunchKernelGGL((ivf_select_kernel<T, 2>), grid, dim3(256), lds, s, p); break;
+    case 4: hipLaunchKernelGGL((ivf_select_kernel<T, 4>), grid, dim3(256), lds, s, p); break;
+    default: hipLaunchKernelGGL((ivf_select_kernel<T, 8>), grid, dim3(256), lds, s, p); break;
   }
 }
 
-hipError_t launch_centroid_scores(const ScoreParams& p, int dtype, int G, hipStream_t s) {
-  if (dtype == kBF16) scores_dispatch<bf16_t>(p, G, s);
-  else scores_dispatch<float>(p, G, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_ivf_select(const SelectParams& p, int G, hipStream_t s) {
-  const size_t lds = (static_cast<size_t>(G) * p.C + p.C) * sizeof(float);
-  dim3 grid(p.B * p.Hkv);
-  switch (G) {
-    case 1: hipLaunchKernelGGL(ivf_select_kernel<1>, grid, dim3(256), lds, s, p); break;
-    case 2: hipLaunchKernelGGL(ivf_select_kernel<2>, grid, dim3(256), lds, s, p); break;
-    case 4: hipLaunchKernelGGL(ivf_select_kernel<4>, grid, dim3(256), lds, s, p); break;
-    default: hipLaunchKernelGGL(ivf_select_kernel<8>, grid, dim3(256), lds, s, p); break;
-  }
+hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s) {
+  const size_t lds = (static_cast<size_t>(G + 1) * p.C + p.C + 1) * sizeof(uint32_t);
+  if (dtype == kBF16) select_dispatch<bf16_t>(p, G, lds, s);
+  else select_dispatch<float>(p, G, lds, s);
   return hipGetLastError();
 }
 

@@ -44,17 +44,10 @@ struct CsrParams {
 hipError_t launch_csr(const CsrParams& p, hipStream_t s);
 
 // ---------------------------------------------------------- IVF select + plan
-struct ScoreParams {
+struct SelectParams {
   const void* q;           // [B][Hq][d]
   const void* centroids;   // [Bc][Hkv][C][d]
-  long long cent_bstride;
-  float* scores;           // [B][Hq][C]
-  int B, Hkv, C;
-};
-hipError_t launch_centroid_scores(const ScoreParams& p, int dtype, int G, hipStream_t s);
-
-struct SelectParams {
-  const float* scores;     // [B][Hq][C]
+  long long cent_bstride;  // elements between request codebooks (0 = shared)
   const int32_t* offsets;  // [B][Hkv][C+1]
   int32_t* sel_out;        // [B][Hq][k] or null
   int32_t* rows_out;       // [B][Hq] or null
@@ -63,7 +56,7 @@ struct SelectParams {
   int32_t* nseg;           // [B*Hkv]
   int B, Hkv, C, k, smax, N;
 };
-hipError_t launch_ivf_select(const SelectParams& p, int G, hipStream_t s);
+hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s);
 
 // --------------------------------------------------------- gather attention
 struct GatherParams {

@@ -80,9 +80,8 @@ __global__ __launch_bounds__(kLocalThreads) void token_local_kernel(TokenSelectP
     Raw8<T> raw[kLocalUnroll];
 #pragma unroll
     for (int u = 0; u < kLocalUnroll; ++u) {
-      const int i = iw + u * NW * 8 + tq;
-      if (i < n) raw[u].load(kb + static_cast<long long>(i) * kIdxDim);
-      else raw[u].zero();
+      const int i = min(iw + u * NW * 8 + tq, n - 1);  // clamped: straight-line loads
+      raw[u].load_stream(kb + static_cast<long long>(i) * kIdxDim);
     }
 #pragma unroll
     for (int u = 0; u < kLocalUnroll; ++u) {
