@@ -21,10 +21,13 @@ namespace tsa {
 
 constexpr int kGatherWaves = kGatherWavesPerBlock;  // each wave owns whole segments
 #ifndef TSA_GATHER_UNROLL
-#define TSA_GATHER_UNROLL 4
+#define TSA_GATHER_UNROLL 8
 #endif
 #ifndef TSA_GATHER_NT
 #define TSA_GATHER_NT 1  // K/V rows are read once per call: non-temporal loads
+#endif
+#ifndef TSA_GATHER_PIPE
+#define TSA_GATHER_PIPE 0  // 1: double-buffer batches in registers
 #endif
 #ifndef TSA_GATHER_WAVES_PER_EU
 #define TSA_GATHER_WAVES_PER_EU 0
@@ -99,36 +102,50 @@ __device__ __forceinline__ void issue_batch(Batch<T>& bt, const int* ids, int ba
 #endif
 }
 
+// Scores the batch's rows for one head, then folds them into the state with
+// one max update per batch (one rescale of o instead of one per row).
 template <typename T>
-__device__ __forceinline__ void consume_batch(const Batch<T>& bt, HeadState& st, const float (&qf)[8]) {
+__device__ __forceinline__ void consume_batch(const Batch<T>& bt, HeadState& st, const QFrag<T>& qf,
+                                              float qscale) {
+  float sc[kGatherUnroll];
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u)
+    sc[u] = bt.valid[u] ? group16_sum(qf.dot(bt.k[u])) * qscale : kMaskedScore;
+  float mb = sc[0];
+#pragma unroll
+  for (int u = 1; u < kGatherUnroll; ++u) mb = fmaxf(mb, sc[u]);
+  const float mn = fmaxf(st.m, mb);
+  const float a = fast_exp2(st.m - mn);
+  st.l *= a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.o[i] *= a;
 #pragma unroll
   for (int u = 0; u < kGatherUnroll; ++u) {
-    float kx[8], vx[8];
-    bt.k[u].widen(kx);
+    float vx[8];
     bt.v[u].widen(vx);
-    const float sc = bt.valid[u] ? group16_sum(dot8(qf, kx)) : kMaskedScore;
-    const float mn = fmaxf(st.m, sc);
-    const float a = fast_exp2(st.m - mn);
-    const float pw = fast_exp2(sc - mn);
-    st.l = fmaf(st.l, a, pw);
+    const float pw = fast_exp2(sc[u] - mn);
+    st.l += pw;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.o[i] = fmaf(pw, vx[i], st.o[i] * a);
-    st.m = mn;
+    for (int i = 0; i < 8; ++i) st.o[i] = fmaf(pw, vx[i], st.o[i]);
   }
+  st.m = mn;
 }
 
 // gather_attn: every wave processes whole segments on its own (no block
-// barrier after the q staging). Per segment: row ids -> wave-private LDS in
-// one round trip; then, for each query head in the segment's mask, one pass
-// over the rows with K/V batches double-buffered in registers (batch i+1 in
-// flight while batch i is scored). A second head's pass re-reads rows the
-// first pass just brought into L2, so HBM sees each row once while a wave
-// carries the state of a single head (which keeps occupancy high). The four
-// lane groups then merge and lanes 0..15 write the head's partial state.
+// barrier after the q staging); a workgroup covers up to 4 segments of one
+// (request, KV head) and exits, so the hardware dispatcher balances the
+// uneven segments across CUs. Per segment: row ids -> wave-private LDS in one
+// round trip; then, for each query head in the segment's mask, one pass over
+// the rows in batches of kBatchRows (16 lanes per row, all loads of a batch in
+// flight together). A second head's pass re-reads rows the first pass just
+// brought into L2, so HBM sees each row once while a wave carries the state of
+// a single head, which keeps register use low and occupancy high: latency is
+// hidden by many resident waves rather than by deep per-wave buffering. The
+// four lane groups then merge and lanes 0..15 write the head's partial state.
 template <typename T, int G, bool EXPLICIT>
 __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_attn_kernel(GatherParams p) {
   constexpr int NW = kGatherWaves;
-  __shared__ float qs[G * kHeadDim];
+  __shared__ __align__(16) T qs[G * kHeadDim];
   __shared__ int ids_lds[NW][kSegRows];
   const int bg = blockIdx.x / p.W, w0 = blockIdx.x % p.W;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
@@ -148,10 +165,9 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
   {
     const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
     for (int i = tid; i < G * kHeadDim / 8; i += NW * kWave) {
-      float x[8];
-      load8(qb + i * 8, x);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) qs[i * 8 + t] = x[t] * p.qscale;
+      Raw8<T> x;
+      x.load(qb + i * 8);
+      *reinterpret_cast<Raw8<T>*>(qs + i * 8) = x;
     }
   }
   __syncthreads();
@@ -189,26 +205,26 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
     float* part = p.partial + (static_cast<long long>(bg) * p.smax + s) * G * kPartStride;
     for (uint32_t hm = mask; hm != 0u; hm &= hm - 1u) {
       const int h = __builtin_ctz(hm);
-      float qf[8];
-      {
-        const float4 a = *reinterpret_cast<const float4*>(qs + h * kHeadDim + e * 8);
-        const float4 c = *reinterpret_cast<const float4*>(qs + h * kHeadDim + e * 8 + 4);
-        qf[0] = a.x; qf[1] = a.y; qf[2] = a.z; qf[3] = a.w;
-        qf[4] = c.x; qf[5] = c.y; qf[6] = c.z; qf[7] = c.w;
-      }
+      QFrag<T> qf;
+      qf.load(qs + h * kHeadDim + e * 8);
       HeadState st;
       st.init();
-      // batches are taken in pairs; the pair loop always issues one batch
-      // ahead (past the end it reloads row 0, masked), so no load sits under
-      // a branch
+#if TSA_GATHER_PIPE
       Batch<T> A, Bb;
       issue_batch(A, ids, 0, cnt, r, kb, vb, row_stride);
       for (int base = 0; base < cnt; base += 2 * kBatchRows) {
         issue_batch(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride);
-        consume_batch(A, st, qf);
+        consume_batch(A, st, qf, p.qscale);
         issue_batch(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride);
-        consume_batch(Bb, st, qf);
+        consume_batch(Bb, st, qf, p.qscale);
       }
+#else
+      for (int base = 0; base < cnt; base += kBatchRows) {
+        Batch<T> A;
+        issue_batch(A, ids, base, cnt, r, kb, vb, row_stride);
+        consume_batch(A, st, qf, p.qscale);
+      }
+#endif
       // merge the four 16-lane row groups (lanes e, e+16, e+32, e+48)
 #pragma unroll
       for (int x = 16; x <= 32; x <<= 1) {
@@ -216,7 +232,7 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
         const float m2 = __shfl_xor(st.m, x);
         const float l2 = __shfl_xor(st.l, x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o2[i] = __shfl_xor(st.o[i], x);
+        for (int t = 0; t < 8; ++t) o2[t] = __shfl_xor(st.o[t], x);
         merge_into(st, m2, l2, o2);
       }
       if (r == 0) {

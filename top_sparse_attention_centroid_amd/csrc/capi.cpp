@@ -55,6 +55,12 @@ float qscale(int d) { return static_cast<float>(1.4426950408889634 / std::sqrt(s
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Workgroups per (request, KV head) for gather_attn: one wave per expected
+// segment; short-lived workgroups let the dispatcher balance uneven segments.
+int gather_blocks_per_head(int expected_segments) {
+  return std::max(1, ceil_div(expected_segments, kGatherWavesPerBlock));
+}
+
 // ----------------------------------------------------------------- layouts
 struct IvfLayout {
   int G = 0, smax = 0;
@@ -306,7 +312,7 @@ tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void
   gp.counts = nullptr; gp.count_const = 0;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  gp.W = ceil_div(std::min(L.smax, L.G * k), kGatherWavesPerBlock); gp.seg_rows = kSegRows;
+  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k)); gp.seg_rows = kSegRows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, true, s)) return st;
   return ok();
@@ -337,7 +343,7 @@ tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const
   gp.seg = nullptr; gp.nseg = nullptr; gp.counts = nullptr; gp.count_const = k; gp.count_max = k;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  gp.W = ceil_div(L.smax, kGatherWavesPerBlock); gp.seg_rows = kRowSegRows;
+  gp.W = gather_blocks_per_head(L.smax); gp.seg_rows = kRowSegRows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
   return ok();
@@ -362,7 +368,7 @@ tsa_status tsa_attend_rows(const tsa_attn_desc* desc, const void* q, const void*
   gp.count_max = d.max_rows;
   gp.partial = static_cast<float*>(ws); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  gp.W = ceil_div(L.smax, kGatherWavesPerBlock); gp.seg_rows = kRowSegRows;
+  gp.W = gather_blocks_per_head(L.smax); gp.seg_rows = kRowSegRows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
   return ok();

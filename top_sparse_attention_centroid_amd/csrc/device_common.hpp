@@ -62,6 +62,46 @@ struct Raw8<float> {
   }
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// One lane's 8 query elements, kept in the storage type. dot() returns the
+// partial dot product with 8 key elements: bf16 pairs go through v_dot2 (the
+// bf16 x bf16 products are exact in fp32), fp32 through FMAs.
+template <typename T>
+struct QFrag;
+
+template <>
+struct QFrag<bf16_t> {
+  uint4 q;
+  __device__ __forceinline__ void load(const bf16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float dot(const Raw8<bf16_t>& k) const {
+    float acc = dot2_bf16(q.x, k.v.x, 0.f);
+    acc = dot2_bf16(q.y, k.v.y, acc);
+    acc = dot2_bf16(q.z, k.v.z, acc);
+    return dot2_bf16(q.w, k.v.w, acc);
+  }
+};
+
+template <>
+struct QFrag<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ float dot(const Raw8<float>& k) const {
+    float s = a.x * k.a.x;
+    s = fmaf(a.y, k.a.y, s); s = fmaf(a.z, k.a.z, s); s = fmaf(a.w, k.a.w, s);
+    s = fmaf(b.x, k.b.x, s); s = fmaf(b.y, k.b.y, s); s = fmaf(b.z, k.b.z, s);
+    return fmaf(b.w, k.b.w, s);
+  }
+};
+
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
   Raw8<T> r;

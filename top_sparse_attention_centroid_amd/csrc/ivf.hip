@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     for (int h = 0; h < G; ++h) load8(qb + h * kHeadDim + e * 8, qf[h]);
     const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
                   static_cast<long long>(g) * C * kHeadDim + e * 8;
-    constexpr int U = 4;  // centroid rows in flight per lane group
+    constexpr int U = 16;  // centroid rows in flight per lane group (64 per wave)
     for (int c0 = wave * 4; c0 < C; c0 += 16 * U) {
       Raw8<T> raw[U];
 #pragma unroll
