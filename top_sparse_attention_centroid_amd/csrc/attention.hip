@@ -78,7 +78,7 @@ struct Batch {
 // rejected id load row 0 of the request (always in bounds) and are masked at
 // scoring. Without control flow around the loads the compiler keeps all of
 // them in flight (a predicated load would force a wait for every earlier one).
-template <typename T>
+template <bool STREAM, typename T>
 __device__ __forceinline__ void issue_batch(Batch<T>& bt, const int* ids, int base, int cnt, int r,
                                             const T* kb, const T* vb, long long row_stride) {
   int row[kGatherUnroll];
@@ -89,17 +89,17 @@ __device__ __forceinline__ void issue_batch(Batch<T>& bt, const int* ids, int ba
     bt.valid[u] = (j < cnt) & (id >= 0);
     row[u] = bt.valid[u] ? id : 0;
   }
-#if TSA_GATHER_NT
+  if constexpr (STREAM) {
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) bt.k[u].load_stream(kb + row[u] * row_stride);
+    for (int u = 0; u < kGatherUnroll; ++u) bt.k[u].load_stream(kb + row[u] * row_stride);
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) bt.v[u].load_stream(vb + row[u] * row_stride);
-#else
+    for (int u = 0; u < kGatherUnroll; ++u) bt.v[u].load_stream(vb + row[u] * row_stride);
+  } else {
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) bt.k[u].load(kb + row[u] * row_stride);
+    for (int u = 0; u < kGatherUnroll; ++u) bt.k[u].load(kb + row[u] * row_stride);
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) bt.v[u].load(vb + row[u] * row_stride);
-#endif
+    for (int u = 0; u < kGatherUnroll; ++u) bt.v[u].load(vb + row[u] * row_stride);
+  }
 }
 
 // Scores the batch's rows for one head, then folds them into the state with
@@ -142,6 +142,55 @@ __device__ __forceinline__ void consume_batch(const Batch<T>& bt, HeadState& st,
 // a single head, which keeps register use low and occupancy high: latency is
 // hidden by many resident waves rather than by deep per-wave buffering. The
 // four lane groups then merge and lanes 0..15 write the head's partial state.
+// For each query head in `mask`: one pass over the segment's rows, then the
+// four 16-lane row groups merge and lanes 0..15 write the head's partial.
+template <bool STREAM, typename T>
+__device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int cnt, int r, int e, const T* kb,
+                                            const T* vb, long long row_stride, const T* qs, float qscale,
+                                            float* part) {
+  for (uint32_t hm = mask; hm != 0u; hm &= hm - 1u) {
+    const int h = __builtin_ctz(hm);
+    QFrag<T> qf;
+    qf.load(qs + h * kHeadDim + e * 8);
+    HeadState st;
+    st.init();
+#if TSA_GATHER_PIPE
+    Batch<T> A, Bb;
+    issue_batch<STREAM>(A, ids, 0, cnt, r, kb, vb, row_stride);
+    for (int base = 0; base < cnt; base += 2 * kBatchRows) {
+      issue_batch<STREAM>(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride);
+      consume_batch(A, st, qf, qscale);
+      issue_batch<STREAM>(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride);
+      consume_batch(Bb, st, qf, qscale);
+    }
+#else
+    for (int base = 0; base < cnt; base += kBatchRows) {
+      Batch<T> A;
+      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride);
+      consume_batch(A, st, qf, qscale);
+    }
+#endif
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+      float o2[8];
+      const float m2 = __shfl_xor(st.m, x);
+      const float l2 = __shfl_xor(st.l, x);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o2[t] = __shfl_xor(st.o[t], x);
+      merge_into(st, m2, l2, o2);
+    }
+    if (r == 0) {
+      float* ph = part + h * kPartStride;
+      *reinterpret_cast<float4*>(ph + 4 + e * 8) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
+      *reinterpret_cast<float4*>(ph + 8 + e * 8) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
+      if (e == 0) {
+        ph[0] = st.m;
+        ph[1] = st.l;
+      }
+    }
+  }
+}
+
 template <typename T, int G, bool EXPLICIT>
 __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_attn_kernel(GatherParams p) {
   constexpr int NW = kGatherWaves;
@@ -203,48 +252,12 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     float* part = p.partial + (static_cast<long long>(bg) * p.smax + s) * G * kPartStride;
-    for (uint32_t hm = mask; hm != 0u; hm &= hm - 1u) {
-      const int h = __builtin_ctz(hm);
-      QFrag<T> qf;
-      qf.load(qs + h * kHeadDim + e * 8);
-      HeadState st;
-      st.init();
-#if TSA_GATHER_PIPE
-      Batch<T> A, Bb;
-      issue_batch(A, ids, 0, cnt, r, kb, vb, row_stride);
-      for (int base = 0; base < cnt; base += 2 * kBatchRows) {
-        issue_batch(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride);
-        consume_batch(A, st, qf, p.qscale);
-        issue_batch(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride);
-        consume_batch(Bb, st, qf, p.qscale);
-      }
-#else
-      for (int base = 0; base < cnt; base += kBatchRows) {
-        Batch<T> A;
-        issue_batch(A, ids, base, cnt, r, kb, vb, row_stride);
-        consume_batch(A, st, qf, p.qscale);
-      }
-#endif
-      // merge the four 16-lane row groups (lanes e, e+16, e+32, e+48)
-#pragma unroll
-      for (int x = 16; x <= 32; x <<= 1) {
-        float o2[8];
-        const float m2 = __shfl_xor(st.m, x);
-        const float l2 = __shfl_xor(st.l, x);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) o2[t] = __shfl_xor(st.o[t], x);
-        merge_into(st, m2, l2, o2);
-      }
-      if (r == 0) {
-        float* ph = part + h * kPartStride;
-        *reinterpret_cast<float4*>(ph + 4 + e * 8) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
-        *reinterpret_cast<float4*>(ph + 8 + e * 8) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
-        if (e == 0) {
-          ph[0] = st.m;
-          ph[1] = st.l;
-        }
-      }
-    }
+    // A row read by a single head's pass streams past the caches; rows that a
+    // second head will re-read stay cacheable so that pass hits L2.
+    if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u)
+      head_passes<true>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
+    else
+      head_passes<false>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
     // the next segment overwrites this wave's id staging area
     __builtin_amdgcn_wave_barrier();
   }

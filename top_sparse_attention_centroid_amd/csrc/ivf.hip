@@ -147,15 +147,16 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 // LDS as order-preserving keys, next to the list offsets.
 //
 // Top-k ([KARAT] How: the top-k most similar lists): wave w owns query heads
-// w, w + 4 of the group. The k-th largest key T is found bit by bit (MSB
-// first) with ballot counts; keys above it are taken, then keys equal to it in
+// w, w + 4 of the group and holds that head's keys in registers, KPL per lane
+// (C <= 64 * KPL). The k-th largest key T is found bit by bit (MSB first)
+// with ballot counts; keys above it are taken, then keys equal to it in
 // ascending list order until k are taken (ties -> lower list id). Lists are
 // emitted in ascending order through ballot prefix counts.
 //
 // Plan: the union of the group's chosen lists with a head bitmask per list,
 // each list cut into segments of at most kSegRows rows, ascending list order.
 // ============================================================================
-template <typename T, int G>
+template <typename T, int G, int KPL>
 __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   extern __shared__ uint32_t smem[];
   const int C = p.C, k = p.k;
@@ -174,9 +175,9 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
 
   {
     const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
-    float qf[G][8];
+    QFrag<T> qf[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) load8(qb + h * kHeadDim + e * 8, qf[h]);
+    for (int h = 0; h < G; ++h) qf[h].load(qb + h * kHeadDim + e * 8);
     const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
                   static_cast<long long>(g) * C * kHeadDim + e * 8;
     constexpr int U = 16;  // centroid rows in flight per lane group (64 per wave)
@@ -190,11 +191,9 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * 16 + r;
-        float x[8];
-        raw[u].widen(x);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float sc = group16_sum(dot8(qf[h], x));
+          const float sc = group16_sum(qf[h].dot(raw[u]));
           if (e == 0 && c < C) keys[h * C + c] = order_key(sc);
         }
       }
@@ -204,30 +203,34 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
 
   for (int h = wave; h < G; h += 4) {
     const uint32_t* kh = keys + h * C;
+    // lane holds keys c = j * 64 + lane (ascending c by j); 0 marks "no list"
+    // and sits below every real key
+    uint32_t kk[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int c = j * kWave + lane;
+      kk[j] = c < C ? kh[c] : 0u;
+    }
     uint32_t thr = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = thr | (1u << bit);
       int cnt = 0;
-      for (int c0 = 0; c0 < C; c0 += kWave) {
-        const int c = c0 + lane;
-        cnt += __popcll(__ballot(c < C && kh[c] >= cand));
-      }
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(kk[j] >= cand));
       if (cnt >= k) thr = cand;
     }
     int n_gt = 0;
-    for (int c0 = 0; c0 < C; c0 += kWave) {
-      const int c = c0 + lane;
-      n_gt += __popcll(__ballot(c < C && kh[c] > thr));
-    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) n_gt += __popcll(__ballot(kk[j] > thr));
     const int need_eq = k - n_gt;
     const int qh = g * G + h;
     int32_t* sel = p.sel_out ? p.sel_out + (static_cast<long long>(b) * p.Hkv * G + qh) * k : nullptr;
     int base = 0, eq_seen = 0, rows = 0;
-    for (int c0 = 0; c0 < C; c0 += kWave) {
-      const int c = c0 + lane;
-      const uint32_t key = c < C ? kh[c] : 0u;
-      const bool gt = c < C && key > thr;
-      const bool eq = c < C && key == thr;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int c = j * kWave + lane;
+      const bool gt = kk[j] > thr;
+      const bool eq = kk[j] == thr;
       const uint64_t eqm = __ballot(eq);
       const bool take = gt || (eq && eq_seen + prefix_count(eqm) < need_eq);
       const uint64_t tm = __ballot(take);
@@ -284,15 +287,23 @@ hipError_t launch_csr(const CsrParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T>
-static void select_dispatch(const SelectParams& p, int G, size_t lds, hipStream_t s) {
+template <typename T, int KPL>
+static void select_dispatch_g(const SelectParams& p, int G, size_t lds, hipStream_t s) {
   const dim3 grid(p.B * p.Hkv);
   switch (G) {
-    case 1: hipLaunchKernelGGL((ivf_select_kernel<T, 1>), grid, dim3(256), lds, s, p); break;
-    case 2: hipLaunchKernelGGL((ivf_select_kernel<T, 2>), grid, dim3(256), lds, s, p); break;
-    case 4: hipLaunchKernelGGL((ivf_select_kernel<T, 4>), grid, dim3(256), lds, s, p); break;
-    default: hipLaunchKernelGGL((ivf_select_kernel<T, 8>), grid, dim3(256), lds, s, p); break;
+    case 1: hipLaunchKernelGGL((ivf_select_kernel<T, 1, KPL>), grid, dim3(256), lds, s, p); break;
+    case 2: hipLaunchKernelGGL((ivf_select_kernel<T, 2, KPL>), grid, dim3(256), lds, s, p); break;
+    case 4: hipLaunchKernelGGL((ivf_select_kernel<T, 4, KPL>), grid, dim3(256), lds, s, p); break;
+    default: hipLaunchKernelGGL((ivf_select_kernel<T, 8, KPL>), grid, dim3(256), lds, s, p); break;
   }
+}
+
+template <typename T>
+static void select_dispatch(const SelectParams& p, int G, size_t lds, hipStream_t s) {
+  if (p.C <= 64) select_dispatch_g<T, 1>(p, G, lds, s);
+  else if (p.C <= 256) select_dispatch_g<T, 4>(p, G, lds, s);
+  else if (p.C <= 1024) select_dispatch_g<T, 16>(p, G, lds, s);
+  else select_dispatch_g<T, kMaxCentroids / 64>(p, G, lds, s);
 }
 
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s) {
