@@ -55,6 +55,13 @@ def test_token_topk_single_chunk_and_k_equals_n():
     _run(cfg, 1, range(2), range(2))
 
 
+def test_token_topk_short_last_chunk():
+    # the last chunk holds fewer tokens than k, so all of it goes to the merge
+    cfg = W.config(3, batch=2, n_tokens=3 * 12288 + 100, top_k=1000, n_planted=32, steps=2)
+    announce("token short last chunk")
+    _run(cfg, 2, range(2), [1])
+
+
 def test_token_topk_ragged_gqa():
     cfg = W.config(3, batch=2, n_tokens=8193 * 2 + 7, top_k=333, n_planted=16, steps=2,
                    n_kv_heads=2, n_q_heads=16)

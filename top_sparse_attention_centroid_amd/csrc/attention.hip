@@ -39,6 +39,8 @@ constexpr int kGatherWaves = kGatherWavesPerBlock;  // each wave owns whole segm
 #endif
 constexpr int kGatherUnroll = TSA_GATHER_UNROLL;  // rows per 16-lane group per batch
 constexpr int kBatchRows = 4 * kGatherUnroll;      // rows per wave per batch
+constexpr int kUnrollAll = 4;                      // all-heads pass: rows per lane group per batch
+constexpr int kBatchRowsAll = 4 * kUnrollAll;
 
 // Online-softmax state of one query head in one 16-lane group (log2 domain).
 // The running max starts at a finite sentinel instead of -inf so masked rows
@@ -191,6 +193,83 @@ __device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int c
   }
 }
 
+// Row lists shared by every head of the group (token selections, hot-cache
+// slots): one pass scores each batch of rows for all G heads, so a row is
+// loaded into registers once; G online-softmax states per lane group.
+template <int G, typename T>
+__device__ __forceinline__ void all_heads_pass(const int* ids, int cnt, int r, int e, const T* kb, const T* vb,
+                                               long long row_stride, const T* qs, float qscale, float* part) {
+  QFrag<T> qf[G];
+  HeadState st[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    qf[h].load(qs + h * kHeadDim + e * 8);
+    st[h].init();
+  }
+  for (int base = 0; base < cnt; base += kBatchRowsAll) {
+    Raw8<T> k[kUnrollAll], v[kUnrollAll];
+    bool valid[kUnrollAll];
+    int row[kUnrollAll];
+#pragma unroll
+    for (int u = 0; u < kUnrollAll; ++u) {
+      const int j = base + u * 4 + r;
+      const int id = ids[min(j, kSegRows - 1)];
+      valid[u] = (j < cnt) & (id >= 0);
+      row[u] = valid[u] ? id : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnrollAll; ++u) k[u].load_stream(kb + row[u] * row_stride);
+#pragma unroll
+    for (int u = 0; u < kUnrollAll; ++u) v[u].load_stream(vb + row[u] * row_stride);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float sc[kUnrollAll];
+#pragma unroll
+      for (int u = 0; u < kUnrollAll; ++u)
+        sc[u] = valid[u] ? group16_sum(qf[h].dot(k[u])) * qscale : kMaskedScore;
+      float mb = sc[0];
+#pragma unroll
+      for (int u = 1; u < kUnrollAll; ++u) mb = fmaxf(mb, sc[u]);
+      const float mn = fmaxf(st[h].m, mb);
+      const float a = fast_exp2(st[h].m - mn);
+      st[h].l *= a;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st[h].o[i] *= a;
+#pragma unroll
+      for (int u = 0; u < kUnrollAll; ++u) {
+        float vx[8];
+        v[u].widen(vx);
+        const float pw = fast_exp2(sc[u] - mn);
+        st[h].l += pw;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st[h].o[i] = fmaf(pw, vx[i], st[h].o[i]);
+      }
+      st[h].m = mn;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+      float o2[8];
+      const float m2 = __shfl_xor(st[h].m, x);
+      const float l2 = __shfl_xor(st[h].l, x);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o2[t] = __shfl_xor(st[h].o[t], x);
+      merge_into(st[h], m2, l2, o2);
+    }
+    if (r == 0) {
+      float* ph = part + h * kPartStride;
+      *reinterpret_cast<float4*>(ph + 4 + e * 8) = make_float4(st[h].o[0], st[h].o[1], st[h].o[2], st[h].o[3]);
+      *reinterpret_cast<float4*>(ph + 8 + e * 8) = make_float4(st[h].o[4], st[h].o[5], st[h].o[6], st[h].o[7]);
+      if (e == 0) {
+        ph[0] = st[h].m;
+        ph[1] = st[h].l;
+      }
+    }
+  }
+}
+
 template <typename T, int G, bool EXPLICIT>
 __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_attn_kernel(GatherParams p) {
   constexpr int NW = kGatherWaves;
@@ -254,10 +333,13 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
     float* part = p.partial + (static_cast<long long>(bg) * p.smax + s) * G * kPartStride;
     // A row read by a single head's pass streams past the caches; rows that a
     // second head will re-read stay cacheable so that pass hits L2.
-    if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u)
+    if constexpr (!EXPLICIT) {
+      all_heads_pass<G>(ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
+    } else if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u) {
       head_passes<true>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
-    else
+    } else {
       head_passes<false>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
+    }
     // the next segment overwrites this wave's id staging area
     __builtin_amdgcn_wave_barrier();
   }

@@ -14,7 +14,7 @@ constexpr int kSegRows = 256;       // max rows per attention segment (one wave'
 constexpr int kRowSegRows = 64;     // segment rows for per-request row lists (token / slot paths)
 constexpr int kGatherWavesPerBlock = 4;
 constexpr int kPartStride = 132;    // floats per partial state: m, l, 2 pad, o[128]
-constexpr int kTokChunk = 8192;     // indexer tokens per workgroup (keys kept in LDS)
+constexpr int kTokChunk = 12288;    // indexer tokens per workgroup (keys kept in LDS)
 constexpr int kMergeThreads = 1024; // threads of the per-request top-k merge
 constexpr int kMaxMergePer = 64;    // candidates per merge thread
 constexpr int kMaxCentroids = 4096;
