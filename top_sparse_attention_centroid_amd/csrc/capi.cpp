@@ -114,8 +114,12 @@ RowsLayout rows_layout(const tsa_attn_desc& d) {
   return L;
 }
 
-size_t index_ws(const tsa_ivf_desc& d) {
+size_t index_assign_bytes(const tsa_ivf_desc& d) {
   return align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * d.n_tokens * sizeof(int32_t));
+}
+size_t index_ws(const tsa_ivf_desc& d) {
+  const size_t bc = d.shared_codebook ? 1 : static_cast<size_t>(d.batch);
+  return index_assign_bytes(d) + align_up(bc * d.n_kv_heads * d.n_centroids * sizeof(float));
 }
 
 // ------------------------------------------------------------- validation
@@ -273,7 +277,7 @@ tsa_status tsa_index_build(const tsa_ivf_desc* desc, const void* keys, const voi
   AssignParams ap{keys, centroids,
                   d.shared_codebook ? 0LL : static_cast<long long>(d.n_kv_heads) * d.n_centroids * kHeadDimRows,
                   static_cast<int32_t*>(ws), d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids};
-  hipError_t e = launch_assign(ap, d.dtype, s);
+  hipError_t e = launch_assign(ap, d.dtype, reinterpret_cast<float*>(static_cast<char*>(ws) + index_assign_bytes(d)), s);
   if (e != hipSuccess) return hip_fail(e, "assign launch");
   CsrParams cp{static_cast<const int32_t*>(ws), offsets, ids, d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids};
   e = launch_csr(cp, s);

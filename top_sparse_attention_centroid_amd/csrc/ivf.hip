@@ -10,9 +10,9 @@
 namespace tsa {
 
 // ============================================================================
-// Index build, step 1: nearest centroid of every key ([KARAT] How, index
-// structure). One thread per key holds the key in registers; centroids stream
-// through LDS in tiles of 32 rows. argmin_c |k - c|^2 = argmin_c (|c|^2 -
+// Index build, step 1 for fp32 data: nearest centroid of every key ([KARAT]
+// How, index structure). One thread per key holds the key in registers;
+// centroids stream through LDS in tiles of 32 rows. argmin_c |k - c|^2 = argmin_c (|c|^2 -
 // 2 k.c); ties keep the lower centroid (strict <).
 // ============================================================================
 constexpr int kAssignTile = 32;
@@ -79,6 +79,129 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     }
   }
   if (valid) p.assign[static_cast<long long>(bg) * p.N + i] = bestc;
+}
+
+// ============================================================================
+// Index build, step 1 on matrix cores (bf16): the same nearest-centroid search
+// as a dense contraction keys x centroids^T (16x16x32 bf16 MFMA, fp32
+// accumulate). Each wave keeps a 16-key A tile (4 fragments cover d = 128) in
+// registers and runs it against 16-centroid B tiles read from LDS (rows padded
+// so the 16 lanes of a fragment read distinct banks). Lane l of a 16x16 result holds centroid column l % 16
+// for keys (l / 16) * 4 .. +4; it keeps the best |c|^2 - 2 k.c per key over
+// ascending centroids (strict <), then the 16 lanes of each row group reduce
+// with the lexicographic order (distance, centroid id).
+// ============================================================================
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaCs = 256;      // centroids per LDS stage
+constexpr int kMfmaKb = 1024;     // keys per workgroup
+constexpr int kMfmaWaves = 8;
+constexpr int kCentPad = 136;     // LDS row stride in elements (128 + 8)
+
+__global__ __launch_bounds__(256) void centroid_norms_kernel(const bf16_t* cent, float* norms, long long rows) {
+  const long long row = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) / 16;
+  const int e = threadIdx.x & 15;
+  float x[8];
+  load8(cent + min(row, rows - 1) * kHeadDim + e * 8, x);
+  float s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s2 = fmaf(x[i], x[i], s2);
+  s2 = group16_sum(s2);
+  if (e == 0 && row < rows) norms[row] = s2;
+}
+
+// A workgroup owns kMfmaKb keys of one (request, KV head). Centroids are
+// staged kMfmaCs at a time; for each stage every wave runs its 16-key tiles
+// against all staged 16-centroid tiles, reduces each key's best over the 16
+// lanes of its row group, and folds it into the per-key best kept in LDS
+// (strict <, so a tie keeps the earlier stage's lower centroid id).
+__global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignParams p, const float* norms) {
+  __shared__ __align__(16) bf16_t cs[kMfmaCs * kCentPad];
+  __shared__ float cn[kMfmaCs];
+  __shared__ float best_d[kMfmaKb];
+  __shared__ int best_c[kMfmaKb];
+  const int bg = blockIdx.y;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int kbase = blockIdx.x * kMfmaKb;
+  const bf16_t* keys = static_cast<const bf16_t*>(p.keys);
+  const bf16_t* cb = static_cast<const bf16_t*>(p.centroids) + b * p.cent_bstride +
+                     static_cast<long long>(g) * p.C * kHeadDim;
+  const float* nb = norms + (p.cent_bstride ? (static_cast<long long>(b) * p.Hkv + g) : g) * p.C;
+  for (int i = tid; i < kMfmaKb; i += kMfmaWaves * kWave) {
+    best_d[i] = INFINITY;
+    best_c[i] = 0;
+  }
+  for (int c0 = 0; c0 < p.C; c0 += kMfmaCs) {
+    __syncthreads();
+    for (int idx = tid; idx < kMfmaCs * 16; idx += kMfmaWaves * kWave) {
+      const int row = idx / 16, part = idx % 16;
+      const int c = min(c0 + row, p.C - 1);
+      *reinterpret_cast<uint4*>(cs + row * kCentPad + part * 8) =
+          *reinterpret_cast<const uint4*>(cb + static_cast<long long>(c) * kHeadDim + part * 8);
+    }
+    for (int i = tid; i < kMfmaCs; i += kMfmaWaves * kWave) cn[i] = nb[min(c0 + i, p.C - 1)];
+    __syncthreads();
+    const int ntile = (min(kMfmaCs, p.C - c0) + 15) / 16;
+    for (int kt = wave; kt < kMfmaKb / 16; kt += kMfmaWaves) {
+      const int key0 = kbase + kt * 16;
+      if (key0 >= p.N) break;
+      const bf16_t* kr = keys + ((static_cast<long long>(b) * p.N + min(key0 + col, p.N - 1)) * p.Hkv + g) * kHeadDim +
+                         grp * 8;
+      bf16x8_t a[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
+      float best[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
+      int bid[4] = {0, 0, 0, 0};
+      for (int t = 0; t < ntile; ++t) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        const bf16_t* brow = cs + (t * 16 + col) * kCentPad + grp * 8;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], *reinterpret_cast<const bf16x8_t*>(brow + ks * 32),
+                                                        acc, 0, 0, 0);
+        const int c = c0 + t * 16 + col;
+        const float cnv = cn[t * 16 + col];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float d = cnv - 2.f * acc[i];
+          if (c < p.C && d < best[i]) {
+            best[i] = d;
+            bid[i] = c;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+          const float d2 = __shfl_xor(best[i], off);
+          const int c2 = __shfl_xor(bid[i], off);
+          if (d2 < best[i] || (d2 == best[i] && c2 < bid[i])) {
+            best[i] = d2;
+            bid[i] = c2;
+          }
+        }
+      }
+      if (col == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kl = kt * 16 + grp * 4 + i;
+          if (best[i] < best_d[kl]) {
+            best_d[kl] = best[i];
+            best_c[kl] = bid[i];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kMfmaKb; i += kMfmaWaves * kWave) {
+    const int key = kbase + i;
+    if (key < p.N) p.assign[static_cast<long long>(bg) * p.N + key] = best_c[i];
+  }
 }
 
 // ============================================================================
@@ -275,10 +398,19 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
 // ============================================================================
 // Launchers
 // ============================================================================
-hipError_t launch_assign(const AssignParams& p, int dtype, hipStream_t s) {
-  dim3 grid((p.N + 255) / 256, p.B * p.Hkv);
-  if (dtype == kBF16) hipLaunchKernelGGL(assign_kernel<bf16_t>, grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(assign_kernel<float>, grid, dim3(256), 0, s, p);
+hipError_t launch_assign(const AssignParams& p, int dtype, float* norms, hipStream_t s) {
+  if (dtype == kBF16) {
+    const long long rows = (p.cent_bstride ? static_cast<long long>(p.B) : 1LL) * p.Hkv * p.C;
+    hipLaunchKernelGGL(centroid_norms_kernel, dim3(static_cast<unsigned>((rows * 16 + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(p.centroids), norms, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid((p.N + kMfmaKb - 1) / kMfmaKb, p.B * p.Hkv);
+    hipLaunchKernelGGL(assign_mfma_kernel, grid, dim3(kMfmaWaves * kWave), 0, s, p, static_cast<const float*>(norms));
+  } else {
+    dim3 grid((p.N + 255) / 256, p.B * p.Hkv);
+    hipLaunchKernelGGL(assign_kernel<float>, grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ struct AssignParams {
   int32_t* assign;         // [B][Hkv][N]
   int B, N, Hkv, C;
 };
-hipError_t launch_assign(const AssignParams& p, int dtype, hipStream_t s);
+// norms: workspace for |c|^2 of every centroid row (bf16 path)
+hipError_t launch_assign(const AssignParams& p, int dtype, float* norms, hipStream_t s);
 
 struct CsrParams {
   const int32_t* assign;   // [B][Hkv][N]
