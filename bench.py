@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph (the gather kernel is then timed "
+                         "in an eager pass over the same steps after the timed region)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -92,35 +95,16 @@ def bench_ivf(args, cfg, torch, tsa, W):
     desc = tsa.binding.ivf_desc(p["keys"], p["centroids"], Hq)
     ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
 
-    def step(i, ev=None):
-        if ev is not None:
-            tsa.time_next_gather(*ev)
+    def call(i):
         tsa.sparse_decode(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
                           out=out, uniq_out=uniq[i % nq], ws=ws)
 
-    for i in range(args.warmup):
-        step(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step(i, evs[i])
-    t_stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_stop)
-    gather_ms = [a.elapsed_time(b) for a, b in evs]
+    res = _timed(args, call, torch, tsa, n_distinct=nq)
     rows_per_set = uniq.sum(dim=(1, 2)).cpu().double()
     rows = sum(float(rows_per_set[i % nq]) for i in range(args.steps))
     row_bytes = 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
-    res = {
-        "ms_total": ms_total, "wall_s": wall, "gather_ms": gather_ms, "gathered_bytes": rows * row_bytes,
-        "queries": B * args.steps, "index_build_ms": index_ms,
-        "unique_rows_per_step": rows / args.steps,
-    }
+    res.update({"gathered_bytes": rows * row_bytes, "queries": B * args.steps, "index_build_ms": index_ms,
+                "unique_rows_per_step": rows / args.steps})
     if args.cpu_seconds > 0:
         res["cpu"] = cpu_baseline_ivf(args, cfg, p, q_all, torch, W)
     return res
@@ -175,13 +159,11 @@ def bench_token(args, cfg, torch, tsa, W):
     desc = tsa.binding.token_desc(prob["k_idx"], prob["keys"], Hq)
     ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_TOKEN_DECODE, desc, k), dtype=torch.uint8, device=dev)
 
-    def step(i, ev=None):
-        if ev is not None:
-            tsa.time_next_gather(*ev)
+    def call(i):
         tsa.token_decode(q_idx[i % nq], prob["k_idx"], q[i % nq], prob["keys"], prob["values"], k,
                          out=out, ws=ws)
 
-    res = _timed(args, step, torch)
+    res = _timed(args, call, torch, tsa, n_distinct=nq)
     res["gathered_bytes"] = args.steps * B * cfg.n_kv_heads * k * ROW_BYTES_BF16
     res["queries"] = B * args.steps
     res["indexer_bytes_per_step"] = B * cfg.n_tokens * cfg.idx_dim * 2
@@ -196,6 +178,9 @@ def bench_cache(args, cfg, torch, tsa, W):
     dev = "cuda"
     B, N, S, Hkv, Hq, d, k = (cfg.batch, cfg.n_tokens, cfg.n_slots, cfg.n_kv_heads, cfg.n_q_heads,
                               cfg.head_dim, cfg.top_k)
+    if args.graph:
+        sys.exit("bench: --graph is for the stateless decode workloads; the cache walks its state "
+                 "once per step, so its steps cannot be re-run for the kernel timing pass")
     steps = args.warmup + args.steps
     log(f"generating {cfg.name}: full KV into pinned host memory")
     cfg_t = cfg.replace(steps=steps)
@@ -220,14 +205,12 @@ def bench_cache(args, cfg, torch, tsa, W):
     desc = tsa.binding.attn_desc(pool_k, Hq, k)
     ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_ATTEND_ROWS, desc), dtype=torch.uint8, device=dev)
 
-    def step(i, ev=None):
+    def call(i):
         tsa.resolve(pt, st, lu, trace[i], i, hk.tensor, hv.tensor, pool_k, pool_v, slots_out=slots,
                     hits=hits[i], misses=misses[i])
-        if ev is not None:
-            tsa.time_next_gather(*ev)
         tsa.attend_rows(q[i], pool_k, pool_v, slots, out=out, ws=ws)
 
-    res = _timed(args, step, torch, offset=args.warmup)
+    res = _timed(args, call, torch, tsa, n_distinct=steps, offset=args.warmup)
     res["gathered_bytes"] = args.steps * B * Hkv * k * ROW_BYTES_BF16
     res["queries"] = B * args.steps
     m = misses.cpu()
@@ -237,21 +220,59 @@ def bench_cache(args, cfg, torch, tsa, W):
     return res
 
 
-def _timed(args, step, torch, offset=0):
+def _timed(args, call, torch, tsa, n_distinct, offset=0):
+    """Warm up, then time args.steps steps (step i runs call(i + offset)).
+
+    Eager (default): every step launches directly, with the library's
+    gather-timing events armed around its gather kernel, so the kernel is
+    timed inside the timed region. With --graph each distinct step
+    (i mod n_distinct) is captured once into a HIP graph and the timed loop
+    replays the graphs; event records captured in a graph do not bracket the
+    kernel, so the gather kernel is then timed by an eager pass over the same
+    steps after the timed region.
+    """
     for i in range(args.warmup):
-        step(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+        call(i)
+    torch.cuda.synchronize()
+
+    def new_events(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def eager(i, ev):
+        tsa.time_next_gather(*ev)
+        call(i + offset)
+
+    graphs = []
+    if args.graph:
+        n = min(n_distinct, args.steps)
+        for j in range(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call(j + offset)
+            graphs.append(g)
+        torch.cuda.synchronize()
+    evs = new_events(args.steps)
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
-        step(i + offset if offset else i, evs[i])
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            eager(i, evs[i])
     t_stop.record()
     torch.cuda.synchronize()
-    return {"ms_total": t_start.elapsed_time(t_stop), "wall_s": time.perf_counter() - wall0,
-            "gather_ms": [a.elapsed_time(b) for a, b in evs]}
+    res = {"ms_total": t_start.elapsed_time(t_stop), "wall_s": time.perf_counter() - wall0,
+           "kernel_timing": "events around each gather launch inside the timed region"}
+    if graphs:
+        for i in range(min(args.steps, n_distinct)):
+            eager(i, evs[i])
+        evs = evs[:min(args.steps, n_distinct)]
+        torch.cuda.synchronize()
+        res["kernel_timing"] = "events around each gather launch in an eager pass after the timed graph region"
+    res["gather_ms"] = [a.elapsed_time(b) for a, b in evs]
+    return res
 
 
 # ----------------------------------------------------------------------------
@@ -277,7 +298,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported by this build "
-              "(the decode path shards by request; see the design notes)", file=sys.stderr)
+              "(across GPUs the decode path would shard by request, one batch slice per GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -321,10 +342,11 @@ def main():
                    "slots": cfg.n_slots or None, "parallelism": "none (1 GPU)"},
         "gathered_kv_gbps": round(gb_s, 1),
         "gathered_kv_frac_of_peak": round(gb_s / HBM_PEAK_GBPS, 4),
+        "graph": bool(args.graph),
         "roofline": {"bound": "hbm", "kernel": "gather_attn", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": round(bytes_per_launch),
-                     "mean_launch_us": round(g_mean_ms * 1e3, 2)},
+                     "mean_launch_us": round(g_mean_ms * 1e3, 2), "timing": res["kernel_timing"]},
         "cpu_baseline": res.get("cpu"),
     }
     for key in ("index_build_ms", "unique_rows_per_step", "misses_per_step", "miss_rate_steady",
