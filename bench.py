@@ -205,9 +205,14 @@ def bench_cache(args, cfg, torch, tsa, W):
     desc = tsa.binding.attn_desc(pool_k, Hq, k)
     ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_ATTEND_ROWS, desc), dtype=torch.uint8, device=dev)
 
+    # events around each RESOLVE launch (same stream as the library call)
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
     def call(i):
+        rev[i][0].record()
         tsa.resolve(pt, st, lu, trace[i], i, hk.tensor, hv.tensor, pool_k, pool_v, slots_out=slots,
                     hits=hits[i], misses=misses[i])
+        rev[i][1].record()
         tsa.attend_rows(q[i], pool_k, pool_v, slots, out=out, ws=ws)
 
     res = _timed(args, call, torch, tsa, n_distinct=steps, offset=args.warmup)
@@ -216,7 +221,24 @@ def bench_cache(args, cfg, torch, tsa, W):
     m = misses.cpu()
     res["misses_per_step"] = m.sum(dim=1).tolist()
     res["miss_rate_steady"] = float(m[args.warmup:].double().mean() / k)
-    res["fetched_bytes"] = float(m[args.warmup:].double().sum()) * Hkv * d * 2 * 2
+    fetched = m[args.warmup:].double().sum(dim=1) * Hkv * d * 2 * 2  # K and V rows per miss
+    res["fetched_bytes"] = float(fetched.sum())
+    r_ms = [rev[i][0].elapsed_time(rev[i][1]) for i in range(args.warmup, steps)]
+    # steady state: steps after the first (step 0 misses every slot)
+    first = 1 if args.warmup == 0 else 0
+    steady_bytes = float(fetched[first:].sum())
+    steady_ms = sum(r_ms[first:])
+    h2d = measure_h2d_gbps(torch)
+    fetch_gbps = steady_bytes / (steady_ms / 1e3) / 1e9 if steady_ms > 0 else None
+    res["resolve"] = {
+        "mean_us": round(sum(r_ms) / len(r_ms) * 1e3, 2),
+        "steady_mean_us": round(steady_ms / max(len(r_ms) - first, 1) * 1e3, 2),
+        "fetch_gbps": round(fetch_gbps, 2) if fetch_gbps else None,
+        "bound": "host link",
+        "h2d_copy_gbps_measured": round(h2d, 2),
+        "frac_of_h2d": round(fetch_gbps / h2d, 4) if fetch_gbps else None,
+        "timing": "torch events around each resolve launch on the call's stream",
+    }
     return res
 
 
@@ -277,6 +299,41 @@ def _timed(args, call, torch, tsa, n_distinct, offset=0):
 
 # ----------------------------------------------------------------------------
 
+def measure_h2d_gbps(torch, nbytes=512 << 20):
+    """Pinned host -> HBM copy rate (DMA), the host-link reference for RESOLVE."""
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dv = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        dv.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(4):
+        dv.copy_(h, non_blocking=True)
+    e.record()
+    torch.cuda.synchronize()
+    return 4 * nbytes / (s.elapsed_time(e) / 1e3) / 1e9
+
+
+def measure_copy_gbps(torch, nbytes=1 << 30):
+    """Device-to-device copy rate (bytes read + written per second): a
+    measured streaming ceiling to set beside the nominal HBM peak."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(4):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    rate = 4 * 2 * nbytes / (s.elapsed_time(e) / 1e3) / 1e9
+    del a, b
+    return rate
+
+
 def calibrate_copy(torch):
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -322,6 +379,7 @@ def main():
     bytes_per_launch = res["gathered_bytes"] / K
     achieved = bytes_per_launch / (g_mean_ms / 1e3) / 1e9
     traffic = measured_traffic(cfg.name)
+    copy_gbps = measure_copy_gbps(torch)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -346,11 +404,13 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gather_attn", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": round(bytes_per_launch),
-                     "mean_launch_us": round(g_mean_ms * 1e3, 2), "timing": res["kernel_timing"]},
+                     "mean_launch_us": round(g_mean_ms * 1e3, 2), "timing": res["kernel_timing"],
+                     "torch_d2d_copy_gbps": round(copy_gbps, 1),
+                     "ratio_to_torch_copy": round(achieved / copy_gbps, 4)},
         "cpu_baseline": res.get("cpu"),
     }
     for key in ("index_build_ms", "unique_rows_per_step", "misses_per_step", "miss_rate_steady",
-                "fetched_bytes", "indexer_bytes_per_step"):
+                "fetched_bytes", "resolve", "indexer_bytes_per_step"):
         if key in res:
             line[key] = res[key]
     print(json.dumps(line), flush=True)
