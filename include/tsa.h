@@ -181,7 +181,7 @@ tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void
  *   attended by all its query heads.
  *   q_idx  (device) [B][idx_dim];  k_idx (device) [B][N][idx_dim]
  *   q      (device) [B][Hq][d];    k_cache, v_cache (device) [B][N][Hkv][d]
- *   k      1 <= k <= N, k <= 4096; N * k <= 2^30
+ *   k      1 <= k <= N, k <= 4096; N <= 4096 * 4096
  *   out    (device, out) fp32 [B][Hq][d]
  *   sel_out (device, out, nullable) int32 [B][k], ascending token ids
  *   Workspace: tsa_workspace_bytes(TSA_OP_TOKEN_DECODE, desc, k, ...).

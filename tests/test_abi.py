@@ -71,8 +71,10 @@ def test_workspace_sizes_and_validation(lib):
     assert B.workspace_bytes(B.OP_TOKEN_DECODE, t, 2048) > 0
     with pytest.raises(B.TsaError, match="UNSUPPORTED"):
         B.workspace_bytes(B.OP_TOKEN_DECODE, B.TokenDesc(1, 1000, 8, 32, 128, 32, 1), 10)
-    with pytest.raises(B.TsaError, match="UNSUPPORTED"):   # too many merge candidates
-        B.workspace_bytes(B.OP_TOKEN_DECODE, B.TokenDesc(1, 2_000_000, 8, 32, 128, 64, 1), 4096)
+    # 2M tokens are fine now; the limit is 4096 filter chunks of 4096 keys
+    assert B.workspace_bytes(B.OP_TOKEN_DECODE, B.TokenDesc(1, 2_000_000, 8, 32, 128, 64, 1), 4096) > 0
+    with pytest.raises(B.TsaError, match="UNSUPPORTED"):
+        B.workspace_bytes(B.OP_TOKEN_DECODE, B.TokenDesc(1, 4096 * 4096 + 1, 8, 32, 128, 64, 1), 4096)
     a = B.AttnDesc(32, 4096, 8, 32, 128, 2048, B.TSA_BF16)
     assert B.workspace_bytes(B.OP_ATTEND_ROWS, a) == 32 * 8 * (2048 // 64) * 4 * 132 * 4
 

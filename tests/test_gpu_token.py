@@ -55,11 +55,50 @@ def test_token_topk_single_chunk_and_k_equals_n():
     _run(cfg, 1, range(2), range(2))
 
 
-def test_token_topk_short_last_chunk():
-    # the last chunk holds fewer tokens than k, so all of it goes to the merge
-    cfg = W.config(3, batch=2, n_tokens=3 * 12288 + 100, top_k=1000, n_planted=32, steps=2)
-    announce("token short last chunk")
+def test_token_topk_ragged_tiles():
+    # ragged last score tile (2048 tokens) and filter tile (4096 keys)
+    cfg = W.config(3, batch=2, n_tokens=5 * 4096 + 100, top_k=1000, n_planted=32, steps=2)
+    announce("token ragged tiles")
     _run(cfg, 2, range(2), [1])
+
+
+def _run_exact(cfg, q_idx, k_idx, attn=True):
+    """Integer-lattice indexer inputs: every score is an exact small integer in
+    fp32 and fp64 alike, so ties are real and the lower token id must win."""
+    prob = W.token_problem(cfg, device=DEV)
+    _, q = W.token_queries(cfg, prob, steps=1)
+    B, k = cfg.batch, cfg.top_k
+    sel = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    out = tsa.token_decode(q_idx, k_idx, q[0], prob["keys"], prob["values"], k, sel_out=sel)
+    torch.cuda.synchronize()
+    sel_g, out_g = sel.cpu().numpy(), out.cpu().numpy()
+    qi64, ki64 = f64(q_idx), f64(k_idx)
+    for b in range(B):
+        ref_sel, _ = token.token_topk(qi64[b], ki64[b], k)
+        assert np.array_equal(sel_g[b], ref_sel), f"selection differs (request {b})"
+        if attn:
+            r = token.token_decode(qi64[b:b + 1], ki64[b][None], f64(q[0][b:b + 1]), f64(prob["keys"][b])[None],
+                                   f64(prob["values"][b])[None], k)
+            err = out_error(out_g[b], r["out"][0])
+            assert err <= OUT_TOL, f"output error {err} (request {b})"
+
+
+def test_token_topk_integer_ties():
+    cfg = W.config(3, batch=2, n_tokens=9000, top_k=1500, n_planted=8, steps=1)
+    announce("token integer ties")
+    g = torch.Generator().manual_seed(11)
+    q_idx = torch.randint(-2, 3, (2, 64), generator=g).to(torch.bfloat16).to(DEV)
+    k_idx = torch.randint(-1, 2, (2, 9000, 64), generator=g).to(torch.bfloat16).to(DEV)
+    _run_exact(cfg, q_idx, k_idx)
+
+
+def test_token_topk_all_scores_equal():
+    # q_idx = 0: every score is 0, so the selection is the k lowest token ids
+    cfg = W.config(3, batch=2, n_tokens=10_000, top_k=777, n_planted=8, steps=1)
+    announce("token all-equal scores")
+    q_idx = torch.zeros((2, 64), dtype=torch.bfloat16, device=DEV)
+    k_idx = torch.randn((2, 10_000, 64), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    _run_exact(cfg, q_idx, k_idx, attn=False)
 
 
 def test_token_topk_ragged_gqa():

@@ -81,19 +81,22 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k) {
 }
 
 struct TokLayout {
-  int G = 0, smax = 0, nchunk = 0;
-  size_t cand_key = 0, cand_id = 0, sel = 0, partial = 0, total = 0;
+  int G = 0, smax = 0, nfchunk = 0;
+  size_t keys = 0, hist = 0, cand_key = 0, cand_id = 0, cand_cnt = 0, sel = 0, partial = 0, total = 0;
 };
 
 TokLayout tok_layout(const tsa_token_desc& d, int k) {
   TokLayout L;
   L.G = d.n_q_heads / d.n_kv_heads;
   L.smax = ceil_div(k, kRowSegRows);
-  L.nchunk = ceil_div(d.n_tokens, kTokChunk);
-  const size_t ncand = static_cast<size_t>(d.batch) * L.nchunk * k;
+  L.nfchunk = ceil_div(d.n_tokens, kTokFilterTile);
+  const size_t bn = static_cast<size_t>(d.batch) * d.n_tokens;
   size_t off = 0;
-  L.cand_key = off; off += align_up(ncand * sizeof(uint32_t));
-  L.cand_id = off;  off += align_up(ncand * sizeof(int32_t));
+  L.keys = off;     off += align_up(bn * sizeof(uint32_t));
+  L.hist = off;     off += align_up(static_cast<size_t>(d.batch) * kTokHistBins * sizeof(int32_t));
+  L.cand_key = off; off += align_up(bn * sizeof(uint32_t));
+  L.cand_id = off;  off += align_up(bn * sizeof(int32_t));
+  L.cand_cnt = off; off += align_up(static_cast<size_t>(d.batch) * L.nfchunk * sizeof(int32_t));
   L.sel = off;      off += align_up(static_cast<size_t>(d.batch) * k * sizeof(int32_t));
   L.partial = off;
   off += align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * L.smax * L.G * kPartStride * sizeof(float));
@@ -155,9 +158,8 @@ tsa_status check_token(const tsa_token_desc* d, int k) {
     return fail(TSA_ERR_UNSUPPORTED, "n_q_heads/n_kv_heads = %d/%d is not 1, 2, 4 or 8", d->n_q_heads, d->n_kv_heads);
   if (k < 1 || k > d->n_tokens) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, N=%d]", k, d->n_tokens);
   if (k > kMaxTokenK) return fail(TSA_ERR_UNSUPPORTED, "k=%d > %d", k, kMaxTokenK);
-  const long long cand = static_cast<long long>(ceil_div(d->n_tokens, kTokChunk)) * k;
-  if (cand > static_cast<long long>(kMergeThreads) * kMaxMergePer)
-    return fail(TSA_ERR_UNSUPPORTED, "N*k too large: %lld merge candidates", cand);
+  if (ceil_div(d->n_tokens, kTokFilterTile) > kMaxTokFilterChunks)
+    return fail(TSA_ERR_UNSUPPORTED, "N=%d > %d tokens", d->n_tokens, kTokFilterTile * kMaxTokFilterChunks);
   return check_dtype(d->dtype);
 }
 
@@ -336,8 +338,10 @@ tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const
   char* w = static_cast<char*>(ws);
   hipStream_t s = as_stream(stream);
   int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + L.sel);
-  TokenSelectParams tp{q_idx, k_idx, reinterpret_cast<uint32_t*>(w + L.cand_key),
-                       reinterpret_cast<int32_t*>(w + L.cand_id), sel, d.batch, d.n_tokens, k, L.nchunk};
+  TokenSelectParams tp{q_idx, k_idx, reinterpret_cast<uint32_t*>(w + L.keys),
+                       reinterpret_cast<int32_t*>(w + L.hist), reinterpret_cast<uint32_t*>(w + L.cand_key),
+                       reinterpret_cast<int32_t*>(w + L.cand_id), reinterpret_cast<int32_t*>(w + L.cand_cnt),
+                       sel, d.batch, d.n_tokens, k, L.nfchunk};
   hipError_t e = launch_token_select(tp, d.dtype, s);
   if (e != hipSuccess) return hip_fail(e, "token_select launch");
 

@@ -14,9 +14,14 @@ constexpr int kSegRows = 256;       // max rows per attention segment (one wave'
 constexpr int kRowSegRows = 64;     // segment rows for per-request row lists (token / slot paths)
 constexpr int kGatherWavesPerBlock = 4;
 constexpr int kPartStride = 132;    // floats per partial state: m, l, 2 pad, o[128]
-constexpr int kTokChunk = 12288;    // indexer tokens per workgroup (keys kept in LDS)
-constexpr int kMergeThreads = 1024; // threads of the per-request top-k merge
-constexpr int kMaxMergePer = 64;    // candidates per merge thread
+#ifndef TSA_SCORE_TILE
+#define TSA_SCORE_TILE 2048
+#endif
+constexpr int kTokScoreTile = TSA_SCORE_TILE;  // indexer tokens scored per workgroup
+constexpr int kTokFilterTile = 4096;      // score keys filtered per workgroup
+constexpr int kTokHistBits = 12;          // top bits of the score key in the threshold histogram
+constexpr int kTokHistBins = 1 << kTokHistBits;
+constexpr int kMaxTokFilterChunks = 4096; // N <= kTokFilterTile * kMaxTokFilterChunks
 constexpr int kMaxCentroids = 4096;
 constexpr int kMaxSlots = 4096;
 constexpr int kMaxTokenK = 4096;
@@ -87,10 +92,13 @@ hipError_t launch_combine(const GatherParams& p, int G, bool explicit_plan, hipS
 struct TokenSelectParams {
   const void* q_idx;       // [B][64]
   const void* k_idx;       // [B][N][64]
-  uint32_t* cand_key;      // [B][nchunk][k]
-  int32_t* cand_id;        // [B][nchunk][k]
+  uint32_t* keys;          // [B][N] order-preserving score keys
+  int32_t* hist;           // [B][kTokHistBins]
+  uint32_t* cand_key;      // [B][N]: filter chunk c's candidates from c * kTokFilterTile
+  int32_t* cand_id;        // [B][N]
+  int32_t* cand_cnt;       // [B][nfchunk]
   int32_t* sel;            // [B][k]
-  int B, N, k, nchunk;
+  int B, N, k, nfchunk;
 };
 hipError_t launch_token_select(const TokenSelectParams& p, int dtype, hipStream_t s);
 

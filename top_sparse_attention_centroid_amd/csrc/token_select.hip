@@ -3,94 +3,275 @@
 // is O(k); "KV卸载上主机:HiSparse、PDD与DDR4回收", HiSparse analysis -- the
 // selector names the positions each step needs).
 //
-// Stage 1 (token_local_kernel): a workgroup streams kTokChunk indexer keys of
-// one request (d_idx = 64 bf16 = 128 B per token, 8 lanes x 16 B), keeps their
-// order-preserving score keys in LDS and selects the chunk's own top-k under
-// the total order (score desc, token id asc). The global top-k lies inside the
-// union of the chunks' top-k under that order, so stage 2 is exact.
-// Stage 2 (token_merge_kernel): one workgroup per request holds every
-// candidate in registers and selects the top-k among them.
-// Both stages find the k-th largest key with an exact 8-bit radix select
-// (four passes over per-wave LDS histograms) and emit in ascending index
-// order from per-(tile, wave) ballot counts.
+// The selection is the k largest scores under the total order (score desc,
+// token id asc), emitted in ascending id order. Three kernels:
+//   score  -- streams the indexer keys (d_idx = 64 bf16 = 128 B per token,
+//             8 lanes x 16 B), writes one order-preserving 32-bit key per
+//             token and adds every key's top 12 bits to a per-request
+//             histogram (one LDS histogram per workgroup, flushed with
+//             global atomics).
+//   filter -- every workgroup reads the histogram, finds the threshold bin
+//             (the highest bin at which the count from the top reaches k)
+//             and compacts the keys at or above it, in id order, into its
+//             own region of the candidate buffer.
+//   final  -- one workgroup per request: an exact radix select over the
+//             low 20 bits of the threshold-bin candidates gives the k-th key
+//             T and how many keys equal to T are taken; the candidates are
+//             then emitted in id order from running block scans.
+// Every key above T lies above or in the threshold bin, so the candidates
+// hold the whole selection and the result is exact for any score
+// distribution (ties included); only the work of the final kernel grows
+// with the number of keys that share the threshold bin.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace tsa {
 
 constexpr int kIdxDim = 64;
-constexpr int kLocalThreads = 256;
-constexpr int kLocalUnroll = 8;
+constexpr int kScoreThreads = 256;
+#ifndef TSA_SCORE_UNROLL
+#define TSA_SCORE_UNROLL 8
+#endif
+constexpr int kScoreUnroll = TSA_SCORE_UNROLL;  // 16-B loads in flight per lane
+constexpr int kFilterThreads = 256;
+constexpr int kFinalThreads = 1024;
+constexpr int kHistShift = 32 - kTokHistBits;
+constexpr int kFinalLdsCands = 8192;  // candidates the final kernel stages in LDS
 
-// In-place exclusive prefix sum of n ints in LDS by the calling wave
-// (each lane scans a contiguous run, then the lane totals are scanned).
-__device__ __forceinline__ void wave_exclusive_scan_lds(int* a, int n) {
-  const int lane = lane_id();
-  const int per = (n + kWave - 1) / kWave;
-  const int lo = min(lane * per, n), hi = min(lo + per, n);
-  int run = 0;
-  for (int i = lo; i < hi; ++i) run += a[i];
-  int x = run;
+// The threshold bin of a request: the highest bin t with
+// count(bins >= t) >= k, and the count of keys in bins above t. NT threads,
+// each owning kTokHistBins / NT consecutive bins. scratch: NT / 64 ints;
+// misc: 2 ints.
+template <int NT>
+__device__ __forceinline__ void threshold_bin(const int32_t* hist, int k, int* scratch, int* misc, int* tbin,
+                                              int* above) {
+  constexpr int PB = kTokHistBins / NT;
+  const int tid = threadIdx.x;
+  int c[PB], v = 0;
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
+  for (int q = 0; q < PB; ++q) {
+    c[q] = hist[tid * PB + q];
+    v += c[q];
   }
-  int acc = x - run;
-  for (int i = lo; i < hi; ++i) {
-    const int v = a[i];
-    a[i] = acc;
-    acc += v;
+  if (tid == 0) {
+    misc[0] = 0;  // unreachable when the histogram holds all N >= k keys
+    misc[1] = 0;
+  }
+  int total;
+  const int excl = block_exclusive_scan<NT / kWave>(v, scratch, &total);
+  int a = total - excl - v;  // keys in the bins of higher threads
+  if (a < k && a + v >= k) {
+    int t = -1, at = 0;
+#pragma unroll
+    for (int q = PB - 1; q >= 0; --q) {
+      if (t < 0 && a + c[q] >= k) {
+        t = tid * PB + q;
+        at = a;
+      }
+      a += c[q];
+    }
+    misc[0] = t;
+    misc[1] = at;
+  }
+  __syncthreads();
+  *tbin = misc[0];
+  *above = misc[1];
+  __syncthreads();
+}
+
+template <typename T>
+__global__ __launch_bounds__(kScoreThreads) void token_score_kernel(TokenSelectParams p) {
+  constexpr int NW = kScoreThreads / kWave;
+  __shared__ uint32_t sk[kTokScoreTile];
+  __shared__ int h[kTokHistBins];
+  const int b = blockIdx.y;
+  const int start = blockIdx.x * kTokScoreTile;
+  const int n = min(kTokScoreTile, p.N - start);
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int e = lane & 7, tq = lane >> 3;
+  for (int i = tid; i < kTokHistBins; i += kScoreThreads) h[i] = 0;
+
+  float qf[8];
+  load8(static_cast<const T*>(p.q_idx) + static_cast<long long>(b) * kIdxDim + e * 8, qf);
+  const T* kb = static_cast<const T*>(p.k_idx) + (static_cast<long long>(b) * p.N + start) * kIdxDim + e * 8;
+  for (int iw = wave * 8; iw < n; iw += NW * 8 * kScoreUnroll) {
+    Raw8<T> raw[kScoreUnroll];
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int i = min(iw + u * NW * 8 + tq, n - 1);  // clamped: straight-line loads
+      raw[u].load_stream(kb + static_cast<long long>(i) * kIdxDim);
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int i = iw + u * NW * 8 + tq;
+      float x[8];
+      raw[u].widen(x);
+      const float sc = group8_sum(dot8(qf, x));
+      if (e == 0 && i < n) sk[i] = order_key(sc);
+    }
+  }
+  __syncthreads();
+  uint32_t* kout = p.keys + static_cast<long long>(b) * p.N + start;
+  for (int i = tid; i < n; i += kScoreThreads) {
+    const uint32_t kv = sk[i];
+    kout[i] = kv;
+    atomicAdd(&h[kv >> kHistShift], 1);
+  }
+  __syncthreads();
+  int32_t* gh = p.hist + static_cast<long long>(b) * kTokHistBins;
+  for (int i = tid; i < kTokHistBins; i += kScoreThreads) {
+    const int c = h[i];
+    if (c) atomicAdd(&gh[i], c);
   }
 }
 
-// The k-th largest of the valid keys held by a block (thread t holds the
-// keys of indices j * (NW * 64) + t; bit j of vmask marks key j valid): an exact
-// MSB-first radix select, 8 bits per pass, over per-wave LDS histograms
-// (hist: NW * 256 ints; misc: 2 ints). Returns the key T and sets *need_eq
-// to how many keys equal to T belong to the top k.
-template <int NW, int PER>
-__device__ __forceinline__ uint32_t block_radix_kth(const uint32_t (&kk)[PER], uint64_t vmask, int k, int* hist,
-                                                    int* misc, int* need_eq) {
+__global__ __launch_bounds__(kFilterThreads) void token_filter_kernel(TokenSelectParams p) {
+  constexpr int NW = kFilterThreads / kWave;
+  constexpr int PER = kTokFilterTile / kFilterThreads;
+  static_assert(PER * NW == kWave, "one count per lane of the scanning wave");
+  __shared__ int scratch[NW];
+  __shared__ int misc[2];
+  __shared__ int cnt[PER * NW];
+  const int b = blockIdx.y, c = blockIdx.x;
+  const int start = c * kTokFilterTile;
+  const int n = min(kTokFilterTile, p.N - start);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  uint32_t prefix = 0, pmask = 0;
-  int krem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < NW * 256; i += NW * kWave) hist[i] = 0;
+  int tbin, above;
+  threshold_bin<kFilterThreads>(p.hist + static_cast<long long>(b) * kTokHistBins, p.k, scratch, misc, &tbin,
+                                &above);
+  const long long base = static_cast<long long>(b) * p.N + start;
+  uint32_t kk[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = j * kFilterThreads + tid;
+    kk[j] = p.keys[base + min(i, n - 1)];
+  }
+  uint64_t bal[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = j * kFilterThreads + tid;
+    bal[j] = __ballot(i < n && static_cast<int>(kk[j] >> kHistShift) >= tbin);
+    if (lane == 0) cnt[j * NW + wave] = __popcll(bal[j]);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int v = cnt[lane];
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    cnt[lane] = x - v;
+    if (lane == kWave - 1) p.cand_cnt[static_cast<long long>(b) * p.nfchunk + c] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if ((bal[j] >> lane) & 1u) {
+      const int pos = cnt[j * NW + wave] + prefix_count(bal[j]);
+      p.cand_key[base + pos] = kk[j];
+      p.cand_id[base + pos] = start + j * kFilterThreads + tid;
+    }
+  }
+}
+
+// Candidate m of a request (m in [0, M)) sits in filter chunk c with
+// coff[c] <= m < coff[c + 1], at position m - coff[c] of that chunk's region.
+__device__ __forceinline__ long long cand_index(const int* coff, int nf, int m) {
+  int lo = 0, hi = nf;  // invariant: coff[lo] <= m < coff[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (coff[mid] <= m) lo = mid;
+    else hi = mid;
+  }
+  return static_cast<long long>(lo) * kTokFilterTile + (m - coff[lo]);
+}
+
+__global__ __launch_bounds__(kFinalThreads) void token_final_kernel(TokenSelectParams p) {
+  constexpr int NW = kFinalThreads / kWave;
+  __shared__ int coff[kMaxTokFilterChunks + 1];
+  __shared__ uint32_t lkey[kFinalLdsCands];
+  __shared__ int32_t lid[kFinalLdsCands];
+  __shared__ int hist[NW * 256];
+  __shared__ int scratch[NW];
+  __shared__ int misc[2];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int nf = p.nfchunk;
+  int tbin, above;
+  threshold_bin<kFinalThreads>(p.hist + static_cast<long long>(b) * kTokHistBins, p.k, scratch, misc, &tbin,
+                               &above);
+  // chunk offsets of the compacted candidates
+  int run = 0;
+  for (int c0 = 0; c0 < nf; c0 += kFinalThreads) {
+    const int c = c0 + tid;
+    const int v = c < nf ? p.cand_cnt[static_cast<long long>(b) * nf + c] : 0;
+    int total;
+    const int excl = block_exclusive_scan<NW>(v, scratch, &total);
+    if (c < nf) coff[c] = run + excl;
+    run += total;
+  }
+  if (tid == 0) coff[nf] = run;
+  __syncthreads();
+  const int M = run;
+  const long long base = static_cast<long long>(b) * p.N;
+  const uint32_t* ck = p.cand_key + base;
+  const int32_t* cid = p.cand_id + base;
+  // Candidates are read many times below: stage them in LDS when they fit
+  // (the usual case: the selection plus one histogram bin), else read them
+  // through the chunk offsets each time.
+  const bool staged = M <= kFinalLdsCands;
+  if (staged) {
+    for (int m = tid; m < M; m += kFinalThreads) {
+      const long long ci = cand_index(coff, nf, m);
+      lkey[m] = ck[ci];
+      lid[m] = cid[ci];
+    }
+    __syncthreads();
+  }
+  auto key_at = [&](int m) { return staged ? lkey[m] : ck[cand_index(coff, nf, m)]; };
+  auto id_at = [&](int m) { return staged ? lid[m] : cid[cand_index(coff, nf, m)]; };
+
+  // radix select of the (k - above)-th largest key inside the threshold bin
+  uint32_t prefix = static_cast<uint32_t>(tbin) << kHistShift;
+  uint32_t pmask = ~0u << kHistShift;
+  int krem = p.k - above;
+  for (int shift = kHistShift - 8; shift > -8; shift -= 8) {
+    const int sh = shift < 0 ? 0 : shift;
+    const uint32_t dmask = (shift < 0 ? (1u << (shift + 8)) : 256u) - 1u;
+    for (int i = tid; i < NW * 256; i += kFinalThreads) hist[i] = 0;
     __syncthreads();
     int* wh = hist + wave * 256;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (((vmask >> j) & 1u) && (kk[j] & pmask) == prefix) atomicAdd(&wh[(kk[j] >> shift) & 255u], 1);
+    for (int m = tid; m < M; m += kFinalThreads) {
+      const uint32_t key = key_at(m);
+      if ((key & pmask) == prefix) atomicAdd(&wh[(key >> sh) & dmask], 1);
     }
     __syncthreads();
     if (wave == 0) {
-      int c[4], t = 0;
+      int cq[4], t = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        c[q] = 0;
-        for (int w = 0; w < NW; ++w) c[q] += hist[w * 256 + lane * 4 + q];
-        t += c[q];
+        cq[q] = 0;
+        for (int w = 0; w < NW; ++w) cq[q] += hist[w * 256 + lane * 4 + q];
+        t += cq[q];
       }
-      // suffix sum over lanes above this one
       int x = t;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
         const int y = __shfl_down(x, o);
         if (lane + o < kWave) x += y;
       }
-      int above = x - t;  // keys in bins of higher lanes
-      int best = -1, best_above = 0;
+      int a = x - t;  // keys in the digits of higher lanes
+      int best = -1, best_a = 0;
 #pragma unroll
-      for (int q = 3; q >= 0; --q) {  // bins lane*4+q, descending
-        if (best < 0 && above + c[q] >= krem) {
+      for (int q = 3; q >= 0; --q) {
+        if (best < 0 && a + cq[q] >= krem) {
           best = lane * 4 + q;
-          best_above = above;
+          best_a = a;
         }
-        above += c[q];
+        a += cq[q];
       }
-      // the digit is the largest bin whose suffix count reaches krem
-      int d = best, da = best_above;
+      int d = best, da = best_a;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
         const int od = __shfl_xor(d, o), oa = __shfl_xor(da, o);
@@ -105,156 +286,47 @@ __device__ __forceinline__ uint32_t block_radix_kth(const uint32_t (&kk)[PER], u
       }
     }
     __syncthreads();
-    const int d = misc[0];
+    prefix |= static_cast<uint32_t>(misc[0]) << sh;
+    pmask |= dmask << sh;
     krem = misc[1];
-    prefix |= static_cast<uint32_t>(d) << shift;
-    pmask |= 255u << shift;
+    __syncthreads();
   }
-  *need_eq = krem;
-  return prefix;
-}
+  const uint32_t Tk = prefix;
+  const int need_eq = krem;
 
-// Emits, in ascending index order, every valid key above T and the first
-// need_eq keys equal to T: put(position, j) for each. Positions come from
-// per-(tile, wave) ballot counts and one wave-level scan. cnt: 2 * PER * NW ints.
-template <int NW, int PER, typename Put>
-__device__ __forceinline__ void block_emit_ordered(const uint32_t (&kk)[PER], uint64_t vmask, uint32_t T, int need_eq,
-                                                   int* cnt, Put put) {
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  int* cgt = cnt;
-  int* ceq = cnt + PER * NW;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool v = (vmask >> j) & 1u;
-    const uint64_t bgt = __ballot(v && kk[j] > T), beq = __ballot(v && kk[j] == T);
-    if (lane == 0) {
-      cgt[j * NW + wave] = __popcll(bgt);
-      ceq[j * NW + wave] = __popcll(beq);
-    }
-  }
-  __syncthreads();
-  if (wave == 0) wave_exclusive_scan_lds(cgt, PER * NW);
-  if (wave == (NW > 1 ? 1 : 0)) {
-    if (NW == 1) __builtin_amdgcn_wave_barrier();
-    wave_exclusive_scan_lds(ceq, PER * NW);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool v = (vmask >> j) & 1u;
-    const bool gt = v && kk[j] > T, eq = v && kk[j] == T;
-    const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
-    const int gt_before = cgt[j * NW + wave] + prefix_count(bgt);
-    const int eq_before = ceq[j * NW + wave] + prefix_count(beq);
-    if (gt || (eq && eq_before < need_eq)) put(gt_before + min(eq_before, need_eq), j);
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(kLocalThreads) void token_local_kernel(TokenSelectParams p) {
-  constexpr int NW = kLocalThreads / kWave;
-  constexpr int PER = kTokChunk / kLocalThreads;
-  __shared__ uint32_t keys[kTokChunk];
-  __shared__ int hist[NW * 256];
-  __shared__ int cnt[2 * PER * NW];
-  __shared__ int misc[2];
-  const int b = blockIdx.y, ch = blockIdx.x;
-  const int start = ch * kTokChunk;
-  const int n = min(kTokChunk, p.N - start);
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int e = lane & 7, tq = lane >> 3;
-
-  float qf[8];
-  load8(static_cast<const T*>(p.q_idx) + static_cast<long long>(b) * kIdxDim + e * 8, qf);
-  const T* kb = static_cast<const T*>(p.k_idx) + (static_cast<long long>(b) * p.N + start) * kIdxDim + e * 8;
-  for (int iw = wave * 8; iw < n; iw += NW * 8 * kLocalUnroll) {
-    Raw8<T> raw[kLocalUnroll];
-#pragma unroll
-    for (int u = 0; u < kLocalUnroll; ++u) {
-      const int i = min(iw + u * NW * 8 + tq, n - 1);  // clamped: straight-line loads
-      raw[u].load_stream(kb + static_cast<long long>(i) * kIdxDim);
-    }
-#pragma unroll
-    for (int u = 0; u < kLocalUnroll; ++u) {
-      const int i = iw + u * NW * 8 + tq;
-      float x[8];
-      raw[u].widen(x);
-      const float sc = group8_sum(dot8(qf, x));
-      if (e == 0 && i < n) keys[i] = order_key(sc);
-    }
-  }
-  __syncthreads();
-
-  const long long cbase = (static_cast<long long>(b) * p.nchunk + ch) * p.k;
-  if (n <= p.k) {
-    for (int i = tid; i < n; i += kLocalThreads) {
-      p.cand_key[cbase + i] = keys[i];
-      p.cand_id[cbase + i] = start + i;
-    }
-    return;
-  }
-  uint32_t kk[PER];
-  uint64_t vmask = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = j * kLocalThreads + tid;
-    kk[j] = i < n ? keys[i] : 0u;
-    vmask |= static_cast<uint64_t>(i < n) << j;
-  }
-  int need_eq;
-  const uint32_t Tk = block_radix_kth<NW, PER>(kk, vmask, p.k, hist, misc, &need_eq);
-  block_emit_ordered<NW, PER>(kk, vmask, Tk, need_eq, cnt, [&](int pos, int j) {
-    p.cand_key[cbase + pos] = kk[j];
-    p.cand_id[cbase + pos] = start + j * kLocalThreads + tid;
-  });
-}
-
-template <int PER>
-__global__ __launch_bounds__(kMergeThreads) void token_merge_kernel(TokenSelectParams p) {
-  constexpr int NW = kMergeThreads / kWave;
-  __shared__ int hist[NW * 256];
-  __shared__ int cnt[2 * PER * NW];
-  __shared__ int misc[2];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const long long P = static_cast<long long>(p.nchunk) * p.k;
-  const uint32_t* ck = p.cand_key + b * P;
-  const int32_t* ci = p.cand_id + b * P;
-  // candidate L = chunk * k + i is real when i < min(k, tokens in the chunk)
-  uint32_t kk[PER];
-  uint64_t vmask = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const long long L = static_cast<long long>(j) * kMergeThreads + tid;
-    bool valid = L < P;
-    if (valid) {
-      const int chunk = static_cast<int>(L / p.k), i = static_cast<int>(L % p.k);
-      valid = i < min(p.k, p.N - chunk * kTokChunk);
-    }
-    kk[j] = valid ? ck[L] : 0u;
-    vmask |= static_cast<uint64_t>(valid) << j;
-  }
-  int need_eq;
-  const uint32_t Tk = block_radix_kth<NW, PER>(kk, vmask, p.k, hist, misc, &need_eq);
+  // ordered emission: keys above Tk, then the first need_eq keys equal to Tk
   int32_t* sel = p.sel + static_cast<long long>(b) * p.k;
-  block_emit_ordered<NW, PER>(kk, vmask, Tk, need_eq, cnt, [&](int pos, int j) {
-    sel[pos] = ci[static_cast<long long>(j) * kMergeThreads + tid];
-  });
+  int run_gt = 0, run_eq = 0;
+  for (int m0 = 0; m0 < M; m0 += kFinalThreads) {
+    const int m = m0 + tid;
+    bool gt = false, eq = false;
+    if (m < M) {
+      const uint32_t key = key_at(m);
+      gt = key > Tk;
+      eq = key == Tk;
+    }
+    const int v = (gt ? 1 : 0) | (eq ? 1 << 16 : 0);
+    int total;
+    const int excl = block_exclusive_scan<NW>(v, scratch, &total);
+    const int gt_before = run_gt + (excl & 0xffff), eq_before = run_eq + (excl >> 16);
+    if (gt || (eq && eq_before < need_eq)) sel[gt_before + min(eq_before, need_eq)] = id_at(m);
+    run_gt += total & 0xffff;
+    run_eq += total >> 16;
+  }
 }
 
 template <typename T>
 static hipError_t token_select_typed(const TokenSelectParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(token_local_kernel<T>, dim3(p.nchunk, p.B), dim3(kLocalThreads), 0, s, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_fill_i32(p.hist, static_cast<long long>(p.B) * kTokHistBins, 0, s);
   if (e != hipSuccess) return e;
-  const long long P = static_cast<long long>(p.nchunk) * p.k;
-  const int per = static_cast<int>((P + kMergeThreads - 1) / kMergeThreads);
-  const dim3 grid(p.B), block(kMergeThreads);
-  if (per <= 8) hipLaunchKernelGGL(token_merge_kernel<8>, grid, block, 0, s, p);
-  else if (per <= 16) hipLaunchKernelGGL(token_merge_kernel<16>, grid, block, 0, s, p);
-  else if (per <= 32) hipLaunchKernelGGL(token_merge_kernel<32>, grid, block, 0, s, p);
-  else if (per <= 36) hipLaunchKernelGGL(token_merge_kernel<36>, grid, block, 0, s, p);
-  else if (per <= 52) hipLaunchKernelGGL(token_merge_kernel<52>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(token_merge_kernel<64>, grid, block, 0, s, p);
+  const int nscore = (p.N + kTokScoreTile - 1) / kTokScoreTile;
+  hipLaunchKernelGGL(token_score_kernel<T>, dim3(nscore, p.B), dim3(kScoreThreads), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(token_filter_kernel, dim3(p.nfchunk, p.B), dim3(kFilterThreads), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(token_final_kernel, dim3(p.B), dim3(kFinalThreads), 0, s, p);
   return hipGetLastError();
 }
 
