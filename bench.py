@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--event-stride", type=int, default=7,
+                    help="time the gather kernel with HIP events on every n-th timed step "
+                         "(event records between kernels slow the stream a little)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (the gather kernel is then timed "
                          "in an eager pass over the same steps after the timed region)")
@@ -102,6 +105,8 @@ def bench_ivf(args, cfg, torch, tsa, W):
     res = _timed(args, call, torch, tsa, n_distinct=nq)
     rows_per_set = uniq.sum(dim=(1, 2)).cpu().double()
     rows = sum(float(rows_per_set[i % nq]) for i in range(args.steps))
+    res["step_bytes"] = [float(rows_per_set[i % nq]) * (2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4))
+                         for i in range(args.steps)]
     row_bytes = 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
     res.update({"gathered_bytes": rows * row_bytes, "queries": B * args.steps, "index_build_ms": index_ms,
                 "unique_rows_per_step": rows / args.steps})
@@ -165,6 +170,7 @@ def bench_token(args, cfg, torch, tsa, W):
 
     res = _timed(args, call, torch, tsa, n_distinct=nq)
     res["gathered_bytes"] = args.steps * B * cfg.n_kv_heads * k * ROW_BYTES_BF16
+    res["step_bytes"] = [B * cfg.n_kv_heads * k * ROW_BYTES_BF16] * args.steps
     res["queries"] = B * args.steps
     res["indexer_bytes_per_step"] = B * cfg.n_tokens * cfg.idx_dim * 2
     return res
@@ -217,6 +223,7 @@ def bench_cache(args, cfg, torch, tsa, W):
 
     res = _timed(args, call, torch, tsa, n_distinct=steps, offset=args.warmup)
     res["gathered_bytes"] = args.steps * B * Hkv * k * ROW_BYTES_BF16
+    res["step_bytes"] = [B * Hkv * k * ROW_BYTES_BF16] * args.steps
     res["queries"] = B * args.steps
     m = misses.cpu()
     res["misses_per_step"] = m.sum(dim=1).tolist()
@@ -278,22 +285,32 @@ def _timed(args, call, torch, tsa, n_distinct, offset=0):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
+    stride = max(1, args.event_stride)
+    timed = []
     for i in range(args.steps):
         if graphs:
             graphs[i % len(graphs)].replay()
-        else:
+        elif i % stride == 0:
             eager(i, evs[i])
+            timed.append(i)
+        else:
+            call(i + offset)
     t_stop.record()
     torch.cuda.synchronize()
     res = {"ms_total": t_start.elapsed_time(t_stop), "wall_s": time.perf_counter() - wall0,
-           "kernel_timing": "events around each gather launch inside the timed region"}
+           "kernel_timing": f"events around the gather launch of every {stride}-th step inside the timed region"}
+    if not graphs:
+        evs = [evs[i] for i in timed]
+    else:
+        timed = list(range(min(args.steps, n_distinct)))
     if graphs:
         for i in range(min(args.steps, n_distinct)):
             eager(i, evs[i])
-        evs = evs[:min(args.steps, n_distinct)]
+        evs = evs[:len(timed)]
         torch.cuda.synchronize()
         res["kernel_timing"] = "events around each gather launch in an eager pass after the timed graph region"
     res["gather_ms"] = [a.elapsed_time(b) for a, b in evs]
+    res["timed_steps"] = timed
     return res
 
 
@@ -376,7 +393,8 @@ def main():
     gb_s = res["gathered_bytes"] / (res["ms_total"] / 1e3) / 1e9
     g_ms = res["gather_ms"]
     g_mean_ms = sum(g_ms) / len(g_ms)
-    bytes_per_launch = res["gathered_bytes"] / K
+    # algorithmic bytes of exactly the launches that were timed
+    bytes_per_launch = sum(res["step_bytes"][i] for i in res["timed_steps"]) / len(res["timed_steps"])
     achieved = bytes_per_launch / (g_mean_ms / 1e3) / 1e9
     traffic = measured_traffic(cfg.name)
     copy_gbps = measure_copy_gbps(torch)

@@ -61,6 +61,17 @@ int gather_blocks_per_head(int expected_segments) {
   return std::max(1, ceil_div(expected_segments, kGatherWavesPerBlock));
 }
 
+// Rows per attention segment for per-request row lists: the longest of
+// 256 / 128 / 64 rows that still gives at least 2048 segments (8 waves per
+// CU). Longer segments write fewer partial softmax states; shorter ones keep
+// every CU busy when the batch is small.
+constexpr long long kMinRowSegments = 2048;
+int row_seg_rows(long long pairs, int max_rows) {
+  for (int r = kSegRows; r > kRowSegRows; r >>= 1)
+    if (pairs * ceil_div(max_rows, r) >= kMinRowSegments) return r;
+  return kRowSegRows;
+}
+
 // ----------------------------------------------------------------- layouts
 struct IvfLayout {
   int G = 0, smax = 0;
@@ -81,14 +92,15 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k) {
 }
 
 struct TokLayout {
-  int G = 0, smax = 0, nfchunk = 0;
+  int G = 0, smax = 0, seg_rows = 0, nfchunk = 0;
   size_t keys = 0, hist = 0, cand_key = 0, cand_id = 0, cand_cnt = 0, sel = 0, partial = 0, total = 0;
 };
 
 TokLayout tok_layout(const tsa_token_desc& d, int k) {
   TokLayout L;
   L.G = d.n_q_heads / d.n_kv_heads;
-  L.smax = ceil_div(k, kRowSegRows);
+  L.seg_rows = row_seg_rows(static_cast<long long>(d.batch) * d.n_kv_heads, k);
+  L.smax = ceil_div(k, L.seg_rows);
   L.nfchunk = ceil_div(d.n_tokens, kTokFilterTile);
   const size_t bn = static_cast<size_t>(d.batch) * d.n_tokens;
   size_t off = 0;
@@ -105,14 +117,15 @@ TokLayout tok_layout(const tsa_token_desc& d, int k) {
 }
 
 struct RowsLayout {
-  int G = 0, smax = 0;
+  int G = 0, smax = 0, seg_rows = 0;
   size_t partial = 0, total = 0;
 };
 
 RowsLayout rows_layout(const tsa_attn_desc& d) {
   RowsLayout L;
   L.G = d.n_q_heads / d.n_kv_heads;
-  L.smax = std::max(1, ceil_div(d.max_rows, kRowSegRows));
+  L.seg_rows = row_seg_rows(static_cast<long long>(d.batch) * d.n_kv_heads, std::max(1, d.max_rows));
+  L.smax = std::max(1, ceil_div(d.max_rows, L.seg_rows));
   L.total = align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * L.smax * L.G * kPartStride * sizeof(float));
   return L;
 }
@@ -351,7 +364,7 @@ tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const
   gp.seg = nullptr; gp.nseg = nullptr; gp.counts = nullptr; gp.count_const = k; gp.count_max = k;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  gp.W = gather_blocks_per_head(L.smax); gp.seg_rows = kRowSegRows;
+  gp.W = gather_blocks_per_head(L.smax); gp.seg_rows = L.seg_rows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
   return ok();
@@ -376,7 +389,7 @@ tsa_status tsa_attend_rows(const tsa_attn_desc* desc, const void* q, const void*
   gp.count_max = d.max_rows;
   gp.partial = static_cast<float*>(ws); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  gp.W = gather_blocks_per_head(L.smax); gp.seg_rows = kRowSegRows;
+  gp.W = gather_blocks_per_head(L.smax); gp.seg_rows = L.seg_rows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
   return ok();

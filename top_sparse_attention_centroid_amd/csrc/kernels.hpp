@@ -11,7 +11,7 @@ namespace tsa {
 
 constexpr int kHeadDimRows = 128;   // d: elements per row (head_dim)
 constexpr int kSegRows = 256;       // max rows per attention segment (one wave's work unit)
-constexpr int kRowSegRows = 64;     // segment rows for per-request row lists (token / slot paths)
+constexpr int kRowSegRows = 64;       // shortest segment for per-request row lists (token / slot paths)
 constexpr int kGatherWavesPerBlock = 4;
 constexpr int kPartStride = 132;    // floats per partial state: m, l, 2 pad, o[128]
 #ifndef TSA_SCORE_TILE
