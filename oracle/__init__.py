@@ -29,10 +29,11 @@ Modules:
   token  per-token indexer scoring and top-k
   cache  batch-step LRU over a fixed slot pool (RESOLVE), cache-mediated
          attention
+  append per-step KV and posting-list append with per-list free entries
 
 Parity pins: every function is checked by tests marked ``not gpu`` against
 closed forms, brute force on tiny inputs, a library routine for the dense
 special case, and the op counts the KARAT worked example prints.
 """
 
-from . import ivf, token, cache  # noqa: F401
+from . import ivf, token, cache, append  # noqa: F401
