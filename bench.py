@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--event-stride", type=int, default=7,
                     help="time the gather kernel with HIP events on every n-th timed step "
                          "(event records between kernels slow the stream a little)")
+    ap.add_argument("--grow", type=int, default=0, metavar="PREFIX",
+                    help="inverted-index workloads: build the index over the first PREFIX tokens with the "
+                         "spare rows as per-list slack, then every step decodes over the growing index and "
+                         "appends one new token per request (KV rows + posting list)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (the gather kernel is then timed "
                          "in an eager pass over the same steps after the timed region)")
@@ -82,7 +86,62 @@ def measured_traffic(workload: str):
 # inverted-index workloads
 # ----------------------------------------------------------------------------
 
+def bench_ivf_grow(args, cfg, torch, tsa, W):
+    """Decode over a growing index, then append the next token of every
+    request; the append kernel is timed with its own events."""
+    dev = "cuda"
+    B, Hq, Hkv, k, N, C = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.top_k, cfg.n_tokens, cfg.n_centroids
+    prefix = args.grow
+    total = args.warmup + args.steps
+    if not (1 <= prefix and prefix + total <= N):
+        sys.exit(f"bench: --grow needs 1 <= PREFIX and PREFIX + warmup + steps <= {N}")
+    if args.graph:
+        sys.exit("bench: --grow changes the index every step; it runs eagerly")
+    log(f"generating {cfg.name} on the GPU (growing from {prefix} tokens)")
+    p = W.ivf_problem(cfg, device=dev)
+    nq = min(cfg.steps, 64)
+    q_all = W.ivf_queries(cfg, p["centroids"], steps=nq)
+    slack = (N - prefix) // C
+    k_cache, v_cache = p["keys"], p["values"]       # rows >= prefix are rewritten by the appends
+    offsets, lens, ids = tsa.index_build_dyn(k_cache, p["centroids"], prefix, slack)
+    new_k = p["keys"][:, prefix:prefix + total].transpose(0, 1).contiguous()    # [steps][B][Hkv][d]
+    new_v = p["values"][:, prefix:prefix + total].transpose(0, 1).contiguous()
+    pos = (prefix + torch.arange(total, device=dev, dtype=torch.int32))[:, None].expand(total, B).contiguous()
+    status = torch.empty((total, B, Hkv), dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, cfg.head_dim), dtype=torch.float32, device=dev)
+    uniq = torch.empty((total, B, Hkv), dtype=torch.int32, device=dev)
+    desc = tsa.binding.ivf_desc(k_cache, p["centroids"], Hq)
+    ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
+    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+    torch.cuda.synchronize()
+
+    def call(i):
+        tsa.sparse_decode_dyn(q_all[i % nq], p["centroids"], offsets, lens, ids, k_cache, v_cache, k,
+                              out=out, uniq_out=uniq[i], ws=ws)
+        aev[i][0].record()
+        tsa.kv_append(new_k[i], new_v[i], pos[i], p["centroids"], k_cache, v_cache, offsets, lens, ids,
+                      status=status[i])
+        aev[i][1].record()
+
+    res = _timed(args, call, torch, tsa, n_distinct=total, offset=args.warmup)
+    row_bytes = 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
+    per_step = uniq.sum(dim=(1, 2)).cpu().double()[args.warmup:]
+    res["step_bytes"] = [float(x) * row_bytes for x in per_step]
+    res.update({"gathered_bytes": float(per_step.sum()) * row_bytes, "queries": B * args.steps,
+                "unique_rows_per_step": float(per_step.mean())})
+    a_ms = [aev[i][0].elapsed_time(aev[i][1]) for i in range(args.warmup, total)]
+    st = status[args.warmup:].cpu()
+    res["append"] = {"prefix_tokens": prefix, "slack_per_list": slack,
+                     "mean_us": round(sum(a_ms) / len(a_ms) * 1e3, 2),
+                     "indexed": int((st == 0).sum()), "list_full": int((st == 1).sum()),
+                     "bytes_per_launch": B * Hkv * 2 * row_bytes,
+                     "timing": "torch events around each kv_append launch on the call's stream"}
+    return res
+
+
 def bench_ivf(args, cfg, torch, tsa, W):
+    if args.grow:
+        return bench_ivf_grow(args, cfg, torch, tsa, W)
     dev = "cuda"
     B, Hq, Hkv, k = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.top_k
     log(f"generating {cfg.name} on the GPU")
@@ -396,7 +455,8 @@ def main():
     # algorithmic bytes of exactly the launches that were timed
     bytes_per_launch = sum(res["step_bytes"][i] for i in res["timed_steps"]) / len(res["timed_steps"])
     achieved = bytes_per_launch / (g_mean_ms / 1e3) / 1e9
-    traffic = measured_traffic(cfg.name)
+    workload = cfg.name + (f"+grow-from-{args.grow}" if args.grow else "")
+    traffic = measured_traffic(workload)
     copy_gbps = measure_copy_gbps(torch)
     line = {
         "metric": METRIC,
@@ -412,7 +472,7 @@ def main():
         "dtype": "f32",
         "storage_dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": cfg.batch, "context": cfg.n_tokens,
+        "config": {"workload": workload, "batch": cfg.batch, "context": cfg.n_tokens,
                    "kv_heads": cfg.n_kv_heads, "q_heads": cfg.n_q_heads, "head_dim": cfg.head_dim,
                    "top_k": cfg.top_k, "centroids": cfg.n_centroids or None,
                    "slots": cfg.n_slots or None, "parallelism": "none (1 GPU)"},
@@ -428,7 +488,7 @@ def main():
         "cpu_baseline": res.get("cpu"),
     }
     for key in ("index_build_ms", "unique_rows_per_step", "misses_per_step", "miss_rate_steady",
-                "fetched_bytes", "resolve", "indexer_bytes_per_step"):
+                "fetched_bytes", "resolve", "append", "indexer_bytes_per_step"):
         if key in res:
             line[key] = res[key]
     print(json.dumps(line), flush=True)

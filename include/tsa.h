@@ -173,6 +173,57 @@ tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void
                              void* stream);
 
 /* ------------------------------------------------------------------------
+ * Growing index: per-step KV and posting-list append.
+ *   [KARAT] worked example, step 6: after each step the new KV entry is
+ *   stored and added to its posting list; Limitations, item 3: keeping the
+ *   index current is the cost to pay as the cache grows.
+ *
+ * tsa_index_build_dyn - posting lists over the first n_prefix tokens of every
+ *   request, each list followed by `slack` free entries for later appends.
+ *   desc->n_tokens is the capacity N (rows of the K/V cache and of ids).
+ *   keys, centroids  as for tsa_index_build (rows >= n_prefix are not read)
+ *   n_prefix         1 <= n_prefix <= N
+ *   slack            >= 0, n_prefix + C * slack <= N
+ *   offsets (device, out) int32 [B][Hkv][C+1]: list c owns
+ *            ids[offsets[c] .. offsets[c+1]) (its valid entries first)
+ *   lens    (device, out) int32 [B][Hkv][C]: valid entries of each list
+ *   ids     (device, out) int32 [B][Hkv][N]: ascending token ids at the front
+ *            of every list range; free entries (and the tail) are -1
+ *   Workspace: tsa_workspace_bytes(TSA_OP_INDEX_BUILD, desc, 0, ...).
+ *
+ * tsa_kv_append - one decode step's append for every request: stores the new
+ *   token's K and V rows at row pos[b] of the caches and adds pos[b] at the
+ *   end of the valid entries of the list of the key's nearest centroid
+ *   (squared L2 in fp32, ties to the lower index), if that list has a free
+ *   entry. Positions should grow from step to step so that every list stays
+ *   in ascending id order. No workspace.
+ *   new_k, new_v (device) [B][Hkv][d], the storage dtype
+ *   pos          (device) int32 [B]
+ *   centroids    (device) as for tsa_index_build
+ *   k_cache, v_cache (device, in/out) [B][N][Hkv][d]
+ *   offsets      (device) from tsa_index_build_dyn;  lens, ids (device, in/out)
+ *   status       (device, out, nullable) int32 [B][Hkv]: 0 indexed; 1 list
+ *                full (rows stored, id not indexed: rebuild the index);
+ *                2 pos outside [0, N) (nothing stored)
+ *
+ * tsa_sparse_decode_dyn - tsa_sparse_decode over a growing index: list c is
+ *   ids[offsets[c] .. offsets[c] + lens[c]). Same arguments otherwise; with
+ *   the same lists it gives bitwise the same output as tsa_sparse_decode.
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_index_build_dyn(const tsa_ivf_desc* desc, const void* keys, const void* centroids,
+                               int32_t n_prefix, int32_t slack, int32_t* offsets, int32_t* lens,
+                               int32_t* ids, void* ws, size_t ws_bytes, void* stream);
+tsa_status tsa_kv_append(const tsa_ivf_desc* desc, const void* new_k, const void* new_v,
+                         const int32_t* pos, const void* centroids, void* k_cache, void* v_cache,
+                         const int32_t* offsets, int32_t* lens, int32_t* ids, int32_t* status,
+                         void* stream);
+tsa_status tsa_sparse_decode_dyn(const tsa_ivf_desc* desc, const void* q, const void* centroids,
+                                 const int32_t* offsets, const int32_t* lens, const int32_t* ids,
+                                 const void* k_cache, const void* v_cache, int32_t k, float* out,
+                                 int32_t* sel_out, int32_t* rows_out, int32_t* uniq_out, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * tsa_token_decode - token-level indexer top-k and attention (DSA style).
  *   [HISPARSE-NOTES] motivation (an indexer picks the top-k tokens, O(k)
  *   work per step); [HISPARSE-NEWS] the selector states the positions each

@@ -118,6 +118,19 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
     t = B.TokenDesc(1, 100, 8, 32, 128, 64, B.TSA_BF16)
     st = lib.tsa_token_decode(ctypes.byref(t), fake, fake, fake, fake, fake, 101, fake, None, fake, 1 << 30, None)
     assert st == B.TSA_ERR_INVALID_ARG
+    # growing index: prefix and slack must fit the capacity; append needs lens
+    ws_ix = B.workspace_bytes(B.OP_INDEX_BUILD, d)
+    st = lib.tsa_index_build_dyn(ctypes.byref(d), fake, fake, 0, 0, fake, fake, fake, fake, ws_ix, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"n_prefix" in lib.tsa_last_error()
+    st = lib.tsa_index_build_dyn(ctypes.byref(d), fake, fake, 60, 6, fake, fake, fake, fake, ws_ix, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"slack" in lib.tsa_last_error()   # 60 + 8 * 6 > 100
+    st = lib.tsa_index_build_dyn(ctypes.byref(d), fake, fake, 60, 5, fake, None, fake, fake, ws_ix, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"lens is NULL" in lib.tsa_last_error()
+    st = lib.tsa_kv_append(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, None, fake, None, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"lens is NULL" in lib.tsa_last_error()
+    st = lib.tsa_sparse_decode_dyn(ctypes.byref(d), fake, fake, fake, None, fake, fake, fake, 4, fake, None, None,
+                                   None, fake, ws_need, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"lens is NULL" in lib.tsa_last_error()
     # timing hook needs both events
     assert lib.tsa_time_next_gather(fake, None) == B.TSA_ERR_INVALID_ARG
     assert lib.tsa_time_next_gather(None, None) == B.TSA_OK

@@ -1,0 +1,138 @@
+"""GPU parity of the growing index (per-step KV and posting-list append,
+[KARAT] worked example step 6) against the append oracle, and of decoding
+over it against the static index."""
+
+import numpy as np
+import pytest
+import torch
+
+import top_sparse_attention_centroid_amd as tsa
+from oracle import append, ivf
+from top_sparse_attention_centroid_amd import workloads as W
+
+from helpers import GAP_MIN, MARGIN_MIN, OUT_TOL, announce, conditioned_ivf_queries, f64, out_error
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _problem(batch, n_tokens, C, Hkv=2, Hq=8, k=5):
+    cfg = W.config(2, batch=batch, n_tokens=n_tokens, n_centroids=C, top_k=k, n_kv_heads=Hkv, n_q_heads=Hq,
+                   steps=2)
+    return cfg, W.ivf_problem(cfg, device=DEV)
+
+
+def _margins_ok(keys64, cent64):
+    for b in range(keys64.shape[0]):
+        for g in range(keys64.shape[2]):
+            _, m = ivf.nearest_centroid(keys64[b, :, g], cent64[0, g])
+            assert m.min() >= MARGIN_MIN, "assignment margin too small for an exact comparison"
+
+
+def test_dynamic_build_matches_oracle():
+    cfg, p = _problem(batch=2, n_tokens=3000, C=40)
+    announce("index_build_dyn N=3000 prefix=2000 slack=20")
+    n_prefix, slack = 2000, 20
+    off, lens, ids = tsa.index_build_dyn(p["keys"], p["centroids"], n_prefix, slack)
+    torch.cuda.synchronize()
+    k64, c64 = f64(p["keys"]), f64(p["centroids"])
+    _margins_ok(k64[:, :n_prefix], c64)
+    og, lg, ig = off.cpu().numpy(), lens.cpu().numpy(), ids.cpu().numpy()
+    for b in range(cfg.batch):
+        for g in range(cfg.n_kv_heads):
+            ro, rl, ri = append.index_build_dynamic(k64[b, :, g], c64[0, g], n_prefix, slack)
+            assert np.array_equal(og[b, g], ro) and np.array_equal(lg[b, g], rl)
+            assert np.array_equal(ig[b, g], ri), f"ids differ (request {b}, head {g})"
+
+
+def test_append_steps_match_oracle_with_full_lists_and_bad_rows():
+    """Small slack: some lists fill up and report status 1; one request gets
+    a row outside the cache at one step and reports status 2."""
+    cfg, p = _problem(batch=3, n_tokens=2400, C=32)
+    announce("kv_append 160 steps, slack 2")
+    n_prefix, slack, steps = 2200, 2, 160
+    N = cfg.n_tokens
+    keys, values = p["keys"], p["values"]
+    k_cache = keys.clone()
+    v_cache = values.clone()
+    k_cache[:, n_prefix:] = 0
+    v_cache[:, n_prefix:] = 0
+    off, lens, ids = tsa.index_build_dyn(k_cache, p["centroids"], n_prefix, slack)
+    k64, c64 = f64(keys), f64(p["centroids"])
+    _margins_ok(k64, c64)
+    state = {(b, g): append.index_build_dynamic(k64[b, :, g], c64[0, g], n_prefix, slack)
+             for b in range(cfg.batch) for g in range(cfg.n_kv_heads)}
+    K_ref = f64(k_cache)
+    V_ref = f64(v_cache)
+    status = torch.empty((cfg.batch, cfg.n_kv_heads), dtype=torch.int32, device=DEV)
+    saw_full = False
+    for t in range(steps):
+        row = n_prefix + t
+        pos = torch.full((cfg.batch,), row, dtype=torch.int32, device=DEV)
+        if t == 7:
+            pos[1] = N  # outside the cache
+        new_k = keys[:, row].contiguous()
+        new_v = values[:, row].contiguous()
+        tsa.kv_append(new_k, new_v, pos, p["centroids"], k_cache, v_cache, off, lens, ids, status=status)
+        torch.cuda.synchronize()
+        ref = append.append_step(state, f64(new_k), f64(new_v), pos.cpu().numpy(), c64, K_ref, V_ref)
+        assert np.array_equal(status.cpu().numpy(), ref), f"status differs at step {t}"
+        saw_full |= bool((ref == 1).any())
+    assert saw_full, "the case was meant to fill some lists"
+    og, lg, ig = off.cpu().numpy(), lens.cpu().numpy(), ids.cpu().numpy()
+    for (b, g), (ro, rl, ri) in state.items():
+        assert np.array_equal(og[b, g], ro) and np.array_equal(lg[b, g], rl)
+        assert np.array_equal(ig[b, g], ri), f"ids differ (request {b}, head {g})"
+    # rows stored exactly where the oracle stored them (bf16 widened exactly)
+    assert np.array_equal(f64(k_cache), K_ref) and np.array_equal(f64(v_cache), V_ref)
+
+
+def test_grown_index_decodes_like_the_static_index():
+    """Build over a prefix, append the remaining tokens one step at a time,
+    then decode: the lists equal the static build over all tokens, and the
+    decode output is bitwise the static decode's (and matches the oracle)."""
+    C, n_real, n_prefix = 24, 2600, 2000
+    cfg, p = _problem(batch=2, n_tokens=n_real, C=C, Hkv=2, Hq=8, k=4)
+    announce("grow index 600 appends, then decode")
+    spare = n_real - n_prefix
+    cap = n_prefix + C * spare           # room for any split of the appends
+    B, Hkv, d = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    k_cache = torch.zeros((B, cap, Hkv, d), dtype=cfg.torch_dtype, device=DEV)
+    v_cache = torch.zeros_like(k_cache)
+    k_cache[:, :n_prefix] = p["keys"][:, :n_prefix]
+    v_cache[:, :n_prefix] = p["values"][:, :n_prefix]
+    off, lens, ids = tsa.index_build_dyn(k_cache, p["centroids"], n_prefix, spare)
+    status = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    for row in range(n_prefix, n_real):
+        pos = torch.full((B,), row, dtype=torch.int32, device=DEV)
+        tsa.kv_append(p["keys"][:, row].contiguous(), p["values"][:, row].contiguous(), pos, p["centroids"],
+                      k_cache, v_cache, off, lens, ids, status=status)
+        assert int(status.max()) == 0
+    torch.cuda.synchronize()
+    k64, c64 = f64(p["keys"]), f64(p["centroids"])
+    _margins_ok(k64, c64)
+    s_off, s_ids = tsa.index_build(p["keys"], p["centroids"])
+    og, lg, ig = off.cpu().numpy(), lens.cpu().numpy(), ids.cpu().numpy()
+    for b in range(B):
+        for g in range(Hkv):
+            c_off, c_ids = append.compact(og[b, g], lg[b, g], ig[b, g])
+            assert np.array_equal(c_off, s_off[b, g].cpu().numpy())
+            assert np.array_equal(c_ids, s_ids[b, g].cpu().numpy())
+            _, r_ids, _ = ivf.index_build(k64[b:b + 1, :, g:g + 1], c64[:, g:g + 1])
+            assert np.array_equal(c_ids, r_ids[0, 0])
+
+    q = conditioned_ivf_queries(cfg, p["centroids"], steps=1)[0]
+    k = cfg.top_k
+    sel_d = torch.empty((B, cfg.n_q_heads, k), dtype=torch.int32, device=DEV)
+    sel_s = torch.empty_like(sel_d)
+    out_d = tsa.sparse_decode_dyn(q, p["centroids"], off, lens, ids, k_cache, v_cache, k, sel_out=sel_d)
+    out_s = tsa.sparse_decode(q, p["centroids"], s_off, s_ids, p["keys"], p["values"], k, sel_out=sel_s)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_d, sel_s)
+    assert torch.equal(out_d, out_s), "growing-index decode differs from the static decode"
+    full_off, full_ids, _ = ivf.index_build(k64, c64)
+    r = ivf.sparse_decode(f64(q), c64, full_off, full_ids, k64, f64(p["values"]), k)
+    assert np.all(r["gap"] >= GAP_MIN)
+    assert np.array_equal(sel_d.cpu().numpy(), r["sel"])
+    err = out_error(out_d.cpu().numpy(), r["out"])
+    assert err <= OUT_TOL, f"output error {err}"

@@ -14,17 +14,21 @@ from .binding import (  # noqa: F401
     attend_rows,
     cache_reset,
     index_build,
+    index_build_dyn,
+    kv_append,
     lib_path,
     load,
     resolve,
     sparse_decode,
+    sparse_decode_dyn,
     time_next_gather,
     token_decode,
     workspace_bytes,
 )
 
 __all__ = [
-    "workloads", "load", "lib_path", "abi_version", "index_build", "sparse_decode", "token_decode",
+    "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "kv_append", "sparse_decode",
+    "sparse_decode_dyn", "token_decode",
     "attend_rows", "resolve", "cache_reset", "HostArray", "time_next_gather", "workspace_bytes",
     "TsaError",
 ]

@@ -47,6 +47,10 @@ _SIGNATURES = {
     "tsa_index_build": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_sparse_decode": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                           ctypes.c_size_t, _P],
+    "tsa_index_build_dyn": [ctypes.POINTER(IvfDesc), _P, _P, _I32, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_kv_append": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "tsa_sparse_decode_dyn": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
+                              ctypes.c_size_t, _P],
     "tsa_token_decode": [ctypes.POINTER(TokenDesc), _P, _P, _P, _P, _P, _I32, _P, _P, _P,
                          ctypes.c_size_t, _P],
     "tsa_resolve": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P],
@@ -205,8 +209,68 @@ def index_build(keys, centroids, *, offsets=None, ids=None, ws=None, stream=None
     return offsets, ids
 
 
+def index_build_dyn(keys, centroids, n_prefix: int, slack: Optional[int] = None, *, offsets=None, lens=None,
+                    ids=None, ws=None, stream=None):
+    """Growing index over the first n_prefix tokens, `slack` free entries per
+    list (default: the spare capacity shared evenly). Returns (offsets, lens, ids)."""
+    _dev(keys, "keys"), _dev(centroids, "centroids")
+    if centroids.dtype != keys.dtype:
+        raise ValueError("keys and centroids must share a dtype")
+    desc = ivf_desc(keys, centroids, keys.shape[2])
+    B, N, Hkv, _ = keys.shape
+    C = centroids.shape[2]
+    if slack is None:
+        slack = (N - n_prefix) // C
+    if offsets is None:
+        offsets = torch.empty((B, Hkv, C + 1), dtype=torch.int32, device=keys.device)
+    if lens is None:
+        lens = torch.empty((B, Hkv, C), dtype=torch.int32, device=keys.device)
+    if ids is None:
+        ids = torch.empty((B, Hkv, N), dtype=torch.int32, device=keys.device)
+    _i32(offsets, "offsets", (B, Hkv, C + 1))
+    _i32(lens, "lens", (B, Hkv, C))
+    _i32(ids, "ids", (B, Hkv, N))
+    ws = _workspace(OP_INDEX_BUILD, desc, 0, ws, keys.device)
+    _check(load().tsa_index_build_dyn(ctypes.byref(desc), _ptr(keys), _ptr(centroids), n_prefix, slack,
+                                      _ptr(offsets), _ptr(lens), _ptr(ids), _ptr(ws), ws.numel(), _stream(stream)))
+    return offsets, lens, ids
+
+
+def kv_append(new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids, *, status=None, stream=None):
+    """Store one new token per request at row pos[b] and add it to its posting
+    list. Returns status [B][Hkv] int32 (0 indexed, 1 list full, 2 bad row)."""
+    for t, n in ((new_k, "new_k"), (new_v, "new_v"), (centroids, "centroids"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _dev(t, n)
+    if not (new_k.dtype == new_v.dtype == centroids.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("new rows, centroids and caches must share a dtype")
+    desc = ivf_desc(k_cache, centroids, k_cache.shape[2])
+    B, N, Hkv, d = k_cache.shape
+    C = desc.n_centroids
+    if tuple(new_k.shape) != (B, Hkv, d) or tuple(new_v.shape) != (B, Hkv, d):
+        raise ValueError("new_k / new_v must be [B][Hkv][d]")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache shapes differ")
+    _i32(pos, "pos", (B,))
+    _i32(offsets, "offsets", (B, Hkv, C + 1))
+    _i32(lens, "lens", (B, Hkv, C))
+    _i32(ids, "ids", (B, Hkv, N))
+    if status is None:
+        status = torch.empty((B, Hkv), dtype=torch.int32, device=k_cache.device)
+    _i32(status, "status", (B, Hkv))
+    _check(load().tsa_kv_append(ctypes.byref(desc), _ptr(new_k), _ptr(new_v), _ptr(pos), _ptr(centroids),
+                                _ptr(k_cache), _ptr(v_cache), _ptr(offsets), _ptr(lens), _ptr(ids), _ptr(status),
+                                _stream(stream)))
+    return status
+
+
+def sparse_decode_dyn(q, centroids, offsets, lens, ids, k_cache, v_cache, k: int, **kw):
+    """sparse_decode over a growing index (list c = ids[offsets[c] : offsets[c] + lens[c]])."""
+    return sparse_decode(q, centroids, offsets, ids, k_cache, v_cache, k, lens=lens, **kw)
+
+
 def sparse_decode(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, out=None, sel_out=None,
-                  rows_out=None, uniq_out=None, ws=None, stream=None):
+                  rows_out=None, uniq_out=None, ws=None, stream=None, lens=None):
     """One retrieval-based sparse-attention decode step. Returns out [B][Hq][d] fp32."""
     for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -228,9 +292,16 @@ def sparse_decode(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, out=N
     _i32(rows_out, "rows_out", (B, Hq))
     _i32(uniq_out, "uniq_out", (B, Hkv))
     ws = _workspace(OP_SPARSE_DECODE, desc, k, ws, q.device)
-    _check(load().tsa_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(centroids), _ptr(offsets), _ptr(ids),
-                                    _ptr(k_cache), _ptr(v_cache), k, _ptr(out), _ptr(sel_out),
-                                    _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(), _stream(stream)))
+    if lens is None:
+        _check(load().tsa_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(centroids), _ptr(offsets), _ptr(ids),
+                                        _ptr(k_cache), _ptr(v_cache), k, _ptr(out), _ptr(sel_out),
+                                        _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(), _stream(stream)))
+    else:
+        _i32(lens, "lens", (B, Hkv, C))
+        _check(load().tsa_sparse_decode_dyn(ctypes.byref(desc), _ptr(q), _ptr(centroids), _ptr(offsets),
+                                            _ptr(lens), _ptr(ids), _ptr(k_cache), _ptr(v_cache), k, _ptr(out),
+                                            _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(),
+                                            _stream(stream)))
     return out
 
 

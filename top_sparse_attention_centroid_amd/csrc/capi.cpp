@@ -228,6 +228,68 @@ tsa_status launch_gather_timed(const GatherParams& gp, int dtype, int G, bool ex
 
 }  // namespace
 
+namespace {
+
+long long codebook_stride(const tsa_ivf_desc& d) {
+  return d.shared_codebook ? 0LL : static_cast<long long>(d.n_kv_heads) * d.n_centroids * kHeadDimRows;
+}
+
+tsa_status index_build_impl(const tsa_ivf_desc* desc, const void* keys, const void* centroids, int n_prefix,
+                            int slack, int32_t* offsets, int32_t* lens, int32_t* ids, void* ws, size_t ws_bytes,
+                            void* stream) {
+  REQUIRE_PTR(keys); REQUIRE_PTR(centroids); REQUIRE_PTR(offsets); REQUIRE_PTR(ids); REQUIRE_PTR(ws);
+  REQUIRE_ALIGN(keys, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(ws, 16);
+  const size_t need = index_ws(*desc);
+  if (ws_bytes < need) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const tsa_ivf_desc& d = *desc;
+  hipStream_t s = as_stream(stream);
+  AssignParams ap{keys, centroids, codebook_stride(d), static_cast<int32_t*>(ws),
+                  d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids, n_prefix};
+  hipError_t e = launch_assign(ap, d.dtype, reinterpret_cast<float*>(static_cast<char*>(ws) + index_assign_bytes(d)), s);
+  if (e != hipSuccess) return hip_fail(e, "assign launch");
+  CsrParams cp{static_cast<const int32_t*>(ws), offsets, ids, lens, d.batch, d.n_tokens, d.n_kv_heads,
+               d.n_centroids, n_prefix, slack};
+  e = launch_csr(cp, s);
+  if (e != hipSuccess) return hip_fail(e, "csr launch");
+  return ok();
+}
+
+tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const void* q, const void* centroids,
+                              const int32_t* offsets, const int32_t* lens, const int32_t* ids,
+                              const void* k_cache, const void* v_cache, int32_t k, float* out, int32_t* sel_out,
+                              int32_t* rows_out, int32_t* uniq_out, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE_PTR(q); REQUIRE_PTR(centroids); REQUIRE_PTR(offsets); REQUIRE_PTR(ids);
+  REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(out); REQUIRE_PTR(ws);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(k_cache, 16);
+  REQUIRE_ALIGN(v_cache, 16); REQUIRE_ALIGN(out, 8); REQUIRE_ALIGN(ws, 16);
+  const tsa_ivf_desc& d = *desc;
+  if (k < 1 || k > d.n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d.n_centroids);
+  const IvfLayout L = ivf_layout(d, k);
+  if (ws_bytes < L.total) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = as_stream(stream);
+
+  SelectParams selp{q, centroids, codebook_stride(d), offsets, lens, sel_out, rows_out, uniq_out,
+                    reinterpret_cast<int4*>(w + L.seg), reinterpret_cast<int32_t*>(w + L.nseg),
+                    d.batch, d.n_kv_heads, d.n_centroids, k, L.smax, d.n_tokens};
+  hipError_t e = launch_ivf_select(selp, d.dtype, L.G, s);
+  if (e != hipSuccess) return hip_fail(e, "ivf_select launch");
+
+  GatherParams gp{};
+  gp.q = q; gp.k = k_cache; gp.v = v_cache; gp.n_rows = d.n_tokens;
+  gp.rowids = ids; gp.rid_bstride = static_cast<long long>(d.n_kv_heads) * d.n_tokens; gp.rid_gstride = d.n_tokens;
+  gp.seg = reinterpret_cast<const int4*>(w + L.seg); gp.nseg = reinterpret_cast<const int32_t*>(w + L.nseg);
+  gp.counts = nullptr; gp.count_const = 0;
+  gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
+  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
+  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k)); gp.seg_rows = kSegRows;
+  gp.qscale = qscale(d.head_dim);
+  if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, true, s)) return st;
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t tsa_abi_version(void) { return TSA_ABI_VERSION; }
@@ -283,20 +345,35 @@ tsa_status tsa_index_build(const tsa_ivf_desc* desc, const void* keys, const voi
                            int32_t* offsets, int32_t* ids, void* ws, size_t ws_bytes,
                            void* stream) {
   if (tsa_status s = check_ivf(desc)) return s;
-  REQUIRE_PTR(keys); REQUIRE_PTR(centroids); REQUIRE_PTR(offsets); REQUIRE_PTR(ids); REQUIRE_PTR(ws);
-  REQUIRE_ALIGN(keys, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(ws, 16);
-  const size_t need = index_ws(*desc);
-  if (ws_bytes < need) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return index_build_impl(desc, keys, centroids, desc->n_tokens, 0, offsets, nullptr, ids, ws, ws_bytes, stream);
+}
+
+tsa_status tsa_index_build_dyn(const tsa_ivf_desc* desc, const void* keys, const void* centroids,
+                               int32_t n_prefix, int32_t slack, int32_t* offsets, int32_t* lens, int32_t* ids,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  REQUIRE_PTR(lens);
+  if (n_prefix < 1 || n_prefix > desc->n_tokens)
+    return fail(TSA_ERR_INVALID_ARG, "n_prefix=%d outside [1, N=%d]", n_prefix, desc->n_tokens);
+  if (slack < 0 || n_prefix + static_cast<long long>(desc->n_centroids) * slack > desc->n_tokens)
+    return fail(TSA_ERR_INVALID_ARG, "n_prefix + C * slack = %lld exceeds N=%d",
+                n_prefix + static_cast<long long>(desc->n_centroids) * slack, desc->n_tokens);
+  return index_build_impl(desc, keys, centroids, n_prefix, slack, offsets, lens, ids, ws, ws_bytes, stream);
+}
+
+tsa_status tsa_kv_append(const tsa_ivf_desc* desc, const void* new_k, const void* new_v, const int32_t* pos,
+                         const void* centroids, void* k_cache, void* v_cache, const int32_t* offsets,
+                         int32_t* lens, int32_t* ids, int32_t* status, void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  REQUIRE_PTR(new_k); REQUIRE_PTR(new_v); REQUIRE_PTR(pos); REQUIRE_PTR(centroids); REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache); REQUIRE_PTR(offsets); REQUIRE_PTR(lens); REQUIRE_PTR(ids);
+  REQUIRE_ALIGN(new_k, 16); REQUIRE_ALIGN(new_v, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(k_cache, 16);
+  REQUIRE_ALIGN(v_cache, 16);
   const tsa_ivf_desc& d = *desc;
-  hipStream_t s = as_stream(stream);
-  AssignParams ap{keys, centroids,
-                  d.shared_codebook ? 0LL : static_cast<long long>(d.n_kv_heads) * d.n_centroids * kHeadDimRows,
-                  static_cast<int32_t*>(ws), d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids};
-  hipError_t e = launch_assign(ap, d.dtype, reinterpret_cast<float*>(static_cast<char*>(ws) + index_assign_bytes(d)), s);
-  if (e != hipSuccess) return hip_fail(e, "assign launch");
-  CsrParams cp{static_cast<const int32_t*>(ws), offsets, ids, d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids};
-  e = launch_csr(cp, s);
-  if (e != hipSuccess) return hip_fail(e, "csr launch");
+  AppendParams ap{new_k, new_v, pos, centroids, codebook_stride(d), k_cache, v_cache, offsets, lens, ids, status,
+                  d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids};
+  hipError_t e = launch_kv_append(ap, d.dtype, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return ok();
 }
 
@@ -306,35 +383,19 @@ tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void
                              int32_t* rows_out, int32_t* uniq_out, void* ws, size_t ws_bytes,
                              void* stream) {
   if (tsa_status s = check_ivf(desc)) return s;
-  REQUIRE_PTR(q); REQUIRE_PTR(centroids); REQUIRE_PTR(offsets); REQUIRE_PTR(ids);
-  REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(out); REQUIRE_PTR(ws);
-  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(k_cache, 16);
-  REQUIRE_ALIGN(v_cache, 16); REQUIRE_ALIGN(out, 8); REQUIRE_ALIGN(ws, 16);
-  const tsa_ivf_desc& d = *desc;
-  if (k < 1 || k > d.n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d.n_centroids);
-  const IvfLayout L = ivf_layout(d, k);
-  if (ws_bytes < L.total) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
-  char* w = static_cast<char*>(ws);
-  hipStream_t s = as_stream(stream);
-  const long long cbs = d.shared_codebook ? 0LL : static_cast<long long>(d.n_kv_heads) * d.n_centroids * kHeadDimRows;
+  return sparse_decode_impl(desc, q, centroids, offsets, nullptr, ids, k_cache, v_cache, k, out, sel_out, rows_out,
+                            uniq_out, ws, ws_bytes, stream);
+}
 
-  SelectParams selp{q, centroids, cbs, offsets, sel_out, rows_out, uniq_out,
-                    reinterpret_cast<int4*>(w + L.seg), reinterpret_cast<int32_t*>(w + L.nseg),
-                    d.batch, d.n_kv_heads, d.n_centroids, k, L.smax, d.n_tokens};
-  hipError_t e = launch_ivf_select(selp, d.dtype, L.G, s);
-  if (e != hipSuccess) return hip_fail(e, "ivf_select launch");
-
-  GatherParams gp{};
-  gp.q = q; gp.k = k_cache; gp.v = v_cache; gp.n_rows = d.n_tokens;
-  gp.rowids = ids; gp.rid_bstride = static_cast<long long>(d.n_kv_heads) * d.n_tokens; gp.rid_gstride = d.n_tokens;
-  gp.seg = reinterpret_cast<const int4*>(w + L.seg); gp.nseg = reinterpret_cast<const int32_t*>(w + L.nseg);
-  gp.counts = nullptr; gp.count_const = 0;
-  gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
-  gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k)); gp.seg_rows = kSegRows;
-  gp.qscale = qscale(d.head_dim);
-  if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, true, s)) return st;
-  return ok();
+tsa_status tsa_sparse_decode_dyn(const tsa_ivf_desc* desc, const void* q, const void* centroids,
+                                 const int32_t* offsets, const int32_t* lens, const int32_t* ids,
+                                 const void* k_cache, const void* v_cache, int32_t k, float* out,
+                                 int32_t* sel_out, int32_t* rows_out, int32_t* uniq_out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  REQUIRE_PTR(lens);
+  return sparse_decode_impl(desc, q, centroids, offsets, lens, ids, k_cache, v_cache, k, out, sel_out, rows_out,
+                            uniq_out, ws, ws_bytes, stream);
 }
 
 tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const void* k_idx,

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int tid = threadIdx.x;
   const int i = blockIdx.x * 256 + tid;
-  const bool valid = i < p.N;
+  const bool valid = i < p.n_assign;
 
   float kf[kHeadDim];
   {
@@ -147,9 +147,9 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
     const int ntile = (min(kMfmaCs, p.C - c0) + 15) / 16;
     for (int kt = wave; kt < kMfmaKb / 16; kt += kMfmaWaves) {
       const int key0 = kbase + kt * 16;
-      if (key0 >= p.N) break;
-      const bf16_t* kr = keys + ((static_cast<long long>(b) * p.N + min(key0 + col, p.N - 1)) * p.Hkv + g) * kHeadDim +
-                         grp * 8;
+      if (key0 >= p.n_assign) break;
+      const bf16_t* kr =
+          keys + ((static_cast<long long>(b) * p.N + min(key0 + col, p.n_assign - 1)) * p.Hkv + g) * kHeadDim + grp * 8;
       bf16x8_t a[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
   __syncthreads();
   for (int i = tid; i < kMfmaKb; i += kMfmaWaves * kWave) {
     const int key = kbase + i;
-    if (key < p.N) p.assign[static_cast<long long>(bg) * p.N + key] = best_c[i];
+    if (key < p.n_assign) p.assign[static_cast<long long>(bg) * p.N + key] = best_c[i];
   }
 }
 
@@ -215,34 +215,40 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
   __shared__ int scan_scratch[4];
   const int bg = blockIdx.x;
   const int tid = threadIdx.x;
+  const int n = p.n_assign;
   const int32_t* a = p.assign + static_cast<long long>(bg) * p.N;
   int32_t* off = p.offsets + static_cast<long long>(bg) * (p.C + 1);
   int32_t* ids = p.ids + static_cast<long long>(bg) * p.N;
+  int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * p.C : nullptr;
 
   for (int c = tid; c < p.C; c += 256) cursor[c] = 0;
   __syncthreads();
-  for (int i = tid; i < p.N; i += 256) atomicAdd(&cursor[a[i]], 1);
+  for (int i = tid; i < n; i += 256) atomicAdd(&cursor[a[i]], 1);
   __syncthreads();
   int carry = 0;
   for (int c0 = 0; c0 < p.C; c0 += 256) {
     const int c = c0 + tid;
-    const int v = c < p.C ? cursor[c] : 0;
+    const int cnt = c < p.C ? cursor[c] : 0;
     int tot;
-    const int ex = block_exclusive_scan<4>(v, scan_scratch, &tot);
+    const int ex = block_exclusive_scan<4>(cnt + (c < p.C ? p.slack : 0), scan_scratch, &tot);
     if (c < p.C) {
-      off[c] = carry + ex;
-      cursor[c] = carry + ex;
+      const int start = carry + ex;
+      off[c] = start;
+      cursor[c] = start;
+      if (lens) lens[c] = cnt;
+      for (int j = cnt; j < cnt + p.slack; ++j) ids[start + j] = -1;  // free entries
     }
     carry += tot;
   }
-  if (tid == 0) off[p.C] = p.N;
+  if (tid == 0) off[p.C] = carry;  // n + C * slack <= N
+  for (int i = carry + tid; i < p.N; i += 256) ids[i] = -1;
   __syncthreads();
   if (tid < kWave) {
     const int lane = tid;
     const int nbits = p.C > 1 ? 32 - __clz(p.C - 1) : 0;
-    for (int i0 = 0; i0 < p.N; i0 += kWave) {
+    for (int i0 = 0; i0 < n; i0 += kWave) {
       const int i = i0 + lane;
-      const bool valid = i < p.N;
+      const bool valid = i < n;
       const int c = valid ? a[i] : 0;
       uint64_t same = __ballot(valid);
       for (int bit = 0; bit < nbits; ++bit) {
@@ -293,8 +299,15 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   const int r = lane >> 4, e = lane & 15;
 
   const int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
+  const int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * C : nullptr;
   for (int c = tid; c <= C; c += 256) loff[c] = min(max(off[c], 0), p.N);
   for (int c = tid; c < C; c += 256) lmask[c] = 0u;
+  __syncthreads();
+  // rows of list c: its whole range, or (dynamic index) the valid front part
+  auto list_len = [&](int c) {
+    const int range = max(loff[c + 1] - loff[c], 0);
+    return lens ? min(max(lens[c], 0), range) : range;
+  };
 
   {
     const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
       if (take) {
         if (sel) sel[base + prefix_count(tm)] = c;
         atomicOr(&lmask[c], 1u << h);
-        rows += max(loff[c + 1] - loff[c], 0);
+        rows += list_len(c);
       }
       base += __popcll(tm);
       eq_seen += __popcll(eqm);
@@ -376,7 +389,7 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     const int c = c0 + tid;
     const uint32_t m = c < C ? lmask[c] : 0u;
     const int start = c < C ? loff[c] : 0;
-    const int len = c < C ? max(loff[c + 1] - start, 0) : 0;
+    const int len = c < C ? list_len(c) : 0;
     const int nsg = (m != 0u && len > 0) ? (len + kSegRows - 1) / kSegRows : 0;
     uniq += m != 0u ? len : 0;
     int tot;
@@ -396,6 +409,104 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
 }
 
 // ============================================================================
+// Per-step KV and index append ([KARAT] worked example, step 6: after each
+// step the new KV entry is stored and added to its posting list). One
+// workgroup (4 waves) per (request, KV head): the new row goes to the cache;
+// its key is scored against every centroid (|c|^2 - 2 k.c, 16 lanes per
+// centroid row, DPP reduction, kAppendU rows in flight per lane group), the
+// best (distance, index) is reduced lexicographically over lane groups and
+// waves, and the id is written at the end of that list's valid entries when
+// the list still has a free one.
+// ============================================================================
+constexpr int kAppendWaves = 4;
+constexpr int kAppendU = 4;
+
+template <typename T>
+__global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendParams p) {
+  __shared__ float wbest[kAppendWaves];
+  __shared__ int wbestc[kAppendWaves];
+  const int bg = blockIdx.x;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave, r = lane >> 4, e = lane & 15;
+  const int pos = p.pos[b];
+  int32_t* st = p.status ? p.status + bg : nullptr;
+  if (pos < 0 || pos >= p.N) {
+    if (st && tid == 0) *st = 2;
+    return;
+  }
+  const long long src = static_cast<long long>(bg) * kHeadDim + e * 8;
+  if (wave == 0 && r == 0) {
+    const long long dst = ((static_cast<long long>(b) * p.N + pos) * p.Hkv + g) * kHeadDim + e * 8;
+    Raw8<T> kr, vr;
+    kr.load(static_cast<const T*>(p.new_k) + src);
+    vr.load(static_cast<const T*>(p.new_v) + src);
+    *reinterpret_cast<Raw8<T>*>(static_cast<T*>(p.k_cache) + dst) = kr;
+    *reinterpret_cast<Raw8<T>*>(static_cast<T*>(p.v_cache) + dst) = vr;
+  }
+  QFrag<T> kq;
+  kq.load(static_cast<const T*>(p.new_k) + src);
+  const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
+                static_cast<long long>(g) * p.C * kHeadDim + e * 8;
+  float best = INFINITY;
+  int bestc = p.C;
+  constexpr int kStep = kAppendWaves * kAppendU * 4;
+  for (int c0 = wave * kAppendU * 4; c0 < p.C; c0 += kStep) {
+    Raw8<T> raw[kAppendU];
+#pragma unroll
+    for (int u = 0; u < kAppendU; ++u)
+      raw[u].load(cb + static_cast<long long>(min(c0 + u * 4 + r, p.C - 1)) * kHeadDim);
+#pragma unroll
+    for (int u = 0; u < kAppendU; ++u) {
+      const int c = c0 + u * 4 + r;
+      float x[8];
+      raw[u].widen(x);
+      float n2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) n2 = fmaf(x[i], x[i], n2);
+      const float dot = group16_sum(kq.dot(raw[u]));
+      n2 = group16_sum(n2);
+      const float dist = n2 - 2.f * dot;
+      if (c < p.C && dist < best) {  // ascending c per lane group: strict < keeps the lower id
+        best = dist;
+        bestc = c;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 16; o < kWave; o <<= 1) {
+    const float d2 = __shfl_xor(best, o);
+    const int c2 = __shfl_xor(bestc, o);
+    if (d2 < best || (d2 == best && c2 < bestc)) {
+      best = d2;
+      bestc = c2;
+    }
+  }
+  if (lane == 0) {
+    wbest[wave] = best;
+    wbestc[wave] = bestc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kAppendWaves; ++w) {
+      if (wbest[w] < best || (wbest[w] == best && wbestc[w] < bestc)) {
+        best = wbest[w];
+        bestc = wbestc[w];
+      }
+    }
+    const int32_t* off = p.offsets + static_cast<long long>(bg) * (p.C + 1);
+    int32_t* lens = p.lens + static_cast<long long>(bg) * p.C;
+    const int c = min(bestc, p.C - 1);
+    const int start = off[c], end = off[c + 1], len = lens[c];
+    const bool room = start >= 0 && end <= p.N && len >= 0 && start + len < end;
+    if (room) {
+      p.ids[static_cast<long long>(bg) * p.N + start + len] = pos;
+      lens[c] = len + 1;
+    }
+    if (st) *st = room ? 0 : 1;
+  }
+}
+
+// ============================================================================
 // Launchers
 // ============================================================================
 hipError_t launch_assign(const AssignParams& p, int dtype, float* norms, hipStream_t s) {
@@ -405,12 +516,19 @@ hipError_t launch_assign(const AssignParams& p, int dtype, float* norms, hipStre
                        static_cast<const bf16_t*>(p.centroids), norms, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((p.N + kMfmaKb - 1) / kMfmaKb, p.B * p.Hkv);
+    dim3 grid((p.n_assign + kMfmaKb - 1) / kMfmaKb, p.B * p.Hkv);
     hipLaunchKernelGGL(assign_mfma_kernel, grid, dim3(kMfmaWaves * kWave), 0, s, p, static_cast<const float*>(norms));
   } else {
-    dim3 grid((p.N + 255) / 256, p.B * p.Hkv);
+    dim3 grid((p.n_assign + 255) / 256, p.B * p.Hkv);
     hipLaunchKernelGGL(assign_kernel<float>, grid, dim3(256), 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t s) {
+  const dim3 grid(p.B * p.Hkv), block(kAppendWaves * kWave);
+  if (dtype == kBF16) hipLaunchKernelGGL(kv_append_kernel<bf16_t>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(kv_append_kernel<float>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -37,15 +37,19 @@ struct AssignParams {
   long long cent_bstride;  // elements between request codebooks (0 = shared)
   int32_t* assign;         // [B][Hkv][N]
   int B, N, Hkv, C;
+  int n_assign;            // keys 0 .. n_assign-1 of every request are assigned
 };
 // norms: workspace for |c|^2 of every centroid row (bf16 path)
 hipError_t launch_assign(const AssignParams& p, int dtype, float* norms, hipStream_t s);
 
 struct CsrParams {
   const int32_t* assign;   // [B][Hkv][N]
-  int32_t* offsets;        // [B][Hkv][C+1]
-  int32_t* ids;            // [B][Hkv][N]
+  int32_t* offsets;        // [B][Hkv][C+1]: list c owns ids[offsets[c] .. offsets[c+1])
+  int32_t* ids;            // [B][Hkv][N]; free entries are -1
+  int32_t* lens;           // [B][Hkv][C] valid entries per list, or null
   int B, N, Hkv, C;
+  int n_assign;            // tokens 0 .. n_assign-1 go into the lists
+  int slack;               // free entries after every list
 };
 hipError_t launch_csr(const CsrParams& p, hipStream_t s);
 
@@ -55,6 +59,7 @@ struct SelectParams {
   const void* centroids;   // [Bc][Hkv][C][d]
   long long cent_bstride;  // elements between request codebooks (0 = shared)
   const int32_t* offsets;  // [B][Hkv][C+1]
+  const int32_t* lens;     // [B][Hkv][C] valid entries per list, or null (whole ranges)
   int32_t* sel_out;        // [B][Hq][k] or null
   int32_t* rows_out;       // [B][Hq] or null
   int32_t* uniq_out;       // [B][Hkv] or null
@@ -63,6 +68,23 @@ struct SelectParams {
   int B, Hkv, C, k, smax, N;
 };
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s);
+
+// ---------------------------------------------------------- KV + index append
+struct AppendParams {
+  const void* new_k;       // [B][Hkv][d]
+  const void* new_v;       // [B][Hkv][d]
+  const int32_t* pos;      // [B] row of the new token
+  const void* centroids;   // [Bc][Hkv][C][d]
+  long long cent_bstride;
+  void* k_cache;           // [B][N][Hkv][d]
+  void* v_cache;
+  const int32_t* offsets;  // [B][Hkv][C+1]
+  int32_t* lens;           // [B][Hkv][C]
+  int32_t* ids;            // [B][Hkv][N]
+  int32_t* status;         // [B][Hkv] or null: 0 indexed, 1 list full, 2 row out of range
+  int B, N, Hkv, C;
+};
+hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t s);
 
 // --------------------------------------------------------- gather attention
 struct GatherParams {
