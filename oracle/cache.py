@@ -29,6 +29,19 @@ events inside one step):
     stamp becomes t, and the token's K/V rows are copied from the host copy
     into the slot.
   * A slot holds one token's K and V rows for every KV head of the layer.
+
+Other replacement policies (the page compares LRU with FIFO, random and the
+offline Belady policy by miss rate; it does not define them further):
+  * FIFO: a hit leaves the slot's stamp alone, so the stamp is the step of
+    the slot's last fetch; victims by (fetch step, slot).
+  * Random: victims by a per-(request, step, slot) key from the SplitMix64
+    generator (Steele, Lea and Flood, "Fast Splittable Pseudorandom Number
+    Generators", OOPSLA 2014), then slot.
+  * Belady (priority): the caller gives, per token, the next step at which
+    it will be selected (a large value for never); victims are the resident
+    tokens needed furthest in the future, ties to the lower slot.
+  Under every policy the step's hits are protected, free slots go first, and
+  the r-th miss (ascending token order) takes the r-th victim.
 """
 
 from __future__ import annotations
@@ -37,7 +50,12 @@ import numpy as np
 
 from .ivf import attend
 
-__all__ = ["CacheState", "lru_step", "fetch_rows", "attend_slots"]
+__all__ = ["CacheState", "lru_step", "policy_step", "splitmix64", "random_key", "next_use_table",
+           "fetch_rows", "attend_slots", "POLICIES", "NEVER"]
+
+POLICIES = ("lru", "fifo", "random", "belady")
+NEVER = 2**31 - 1          # "not selected again" in a next-use table
+_M64 = (1 << 64) - 1
 
 
 class CacheState:
@@ -76,6 +94,84 @@ def lru_step(state: CacheState, selected, t: int):
         raise ValueError("more misses than evictable slots (k > n_slots?)")
     fetches = []
     for tok, v in zip(misses, victims):                        # (4) replace + fetch
+        old = st[v]
+        if old >= 0:
+            pt[old] = -1
+        pt[tok] = v
+        st[v] = tok
+        lu[v] = t
+        fetches.append((int(tok), int(v)))
+    return pt[sel].copy(), int(resident.sum()), len(misses), fetches
+
+
+def splitmix64(x: int) -> int:
+    """One output of SplitMix64 for state x (the state is advanced by the
+    golden-ratio increment, then mixed): Steele, Lea and Flood, OOPSLA 2014."""
+    z = (x + 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def random_key(seed: int, request: int, step: int, slot: int) -> int:
+    """31-bit eviction key of one slot at one step: SplitMix64 chained over
+    (seed, request, step, slot), top 31 bits."""
+    x = splitmix64(seed & _M64)
+    x = splitmix64((x + request) & _M64)
+    x = splitmix64((x + step) & _M64)
+    x = splitmix64((x + slot) & _M64)
+    return x >> 33
+
+
+def next_use_table(trace):
+    """For a selection trace [T][k] of one request: nu[t] maps token -> the
+    first step u > t that selects it (NEVER if none), as a dict per step."""
+    T = len(trace)
+    out = [None] * T
+    nxt = {}
+    for t in range(T - 1, -1, -1):
+        out[t] = dict(nxt)
+        for tok in np.asarray(trace[t]).tolist():
+            nxt[int(tok)] = t
+    return out
+
+
+def policy_step(state: CacheState, selected, t: int, policy: str = "lru", *, seed: int = 0,
+                request: int = 0, next_use=None):
+    """One RESOLVE step under a replacement policy (mutates ``state``).
+
+    policy: "lru" (== lru_step), "fifo", "random" (needs seed, request) or
+    "belady" (needs next_use: token -> next selecting step, NEVER if none;
+    tokens missing from it count as NEVER). Returns what lru_step returns.
+    """
+    if policy == "lru":
+        return lru_step(state, selected, t)
+    if policy not in POLICIES:
+        raise ValueError(f"unknown policy {policy}")
+    sel = np.asarray(selected, dtype=np.int64)
+    pt, st, lu = state.page_table, state.slot_token, state.last_use
+    resident = pt[sel] >= 0
+    hit_slots = set(pt[sel[resident]].tolist())
+    if policy != "fifo":
+        lu[pt[sel[resident]]] = t                               # bookkeeping only
+    misses = np.sort(sel[~resident])
+    cand = [s for s in range(len(st)) if s not in hit_slots]
+
+    def key(s):
+        if st[s] < 0:
+            return (0, 0, s)                                    # free slots first
+        if policy == "fifo":
+            return (1, int(lu[s]), s)
+        if policy == "random":
+            return (1, random_key(seed, request, t, s), s)
+        nu = NEVER if next_use is None else int(next_use.get(int(st[s]), NEVER))
+        return (1, -nu, s)                                      # furthest next use first
+
+    victims = sorted(cand, key=key)[: len(misses)]
+    if len(victims) < len(misses):
+        raise ValueError("more misses than evictable slots (k > n_slots?)")
+    fetches = []
+    for tok, v in zip(misses, victims):
         old = st[v]
         if old >= 0:
             pt[old] = -1
