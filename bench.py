@@ -49,6 +49,9 @@ def parse():
                     help="inverted-index workloads: build the index over the first PREFIX tokens with the "
                          "spare rows as per-list slack, then every step decodes over the growing index and "
                          "appends one new token per request (KV rows + posting list)")
+    ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random", "belady"],
+                    help="hot-cache workload: replacement policy of RESOLVE (belady = offline, from the "
+                         "trace's next-use steps)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (the gather kernel is then timed "
                          "in an eager pass over the same steps after the timed region)")
@@ -272,11 +275,22 @@ def bench_cache(args, cfg, torch, tsa, W):
 
     # events around each RESOLVE launch (same stream as the library call)
     rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    prio = None
+    if args.policy == "belady":
+        # next step that selects each token, per step (offline knowledge of the trace)
+        never = 2**31 - 1
+        prio = torch.empty((steps, B, N), dtype=torch.int32, device=dev)
+        nxt = torch.full((B, N), never, dtype=torch.int32, device=dev)
+        for t in range(steps - 1, -1, -1):
+            prio[t] = nxt
+            nxt.scatter_(1, trace[t].long(), t)
+    gpu_policy = "priority" if args.policy == "belady" else args.policy
 
     def call(i):
         rev[i][0].record()
         tsa.resolve(pt, st, lu, trace[i], i, hk.tensor, hv.tensor, pool_k, pool_v, slots_out=slots,
-                    hits=hits[i], misses=misses[i])
+                    hits=hits[i], misses=misses[i], policy=gpu_policy, seed=0x5EED,
+                    priority=None if prio is None else prio[i])
         rev[i][1].record()
         tsa.attend_rows(q[i], pool_k, pool_v, slots, out=out, ws=ws)
 
@@ -297,6 +311,7 @@ def bench_cache(args, cfg, torch, tsa, W):
     h2d = measure_h2d_gbps(torch)
     fetch_gbps = steady_bytes / (steady_ms / 1e3) / 1e9 if steady_ms > 0 else None
     res["resolve"] = {
+        "policy": args.policy,
         "mean_us": round(sum(r_ms) / len(r_ms) * 1e3, 2),
         "steady_mean_us": round(steady_ms / max(len(r_ms) - first, 1) * 1e3, 2),
         "fetch_gbps": round(fetch_gbps, 2) if fetch_gbps else None,
@@ -456,6 +471,8 @@ def main():
     bytes_per_launch = sum(res["step_bytes"][i] for i in res["timed_steps"]) / len(res["timed_steps"])
     achieved = bytes_per_launch / (g_mean_ms / 1e3) / 1e9
     workload = cfg.name + (f"+grow-from-{args.grow}" if args.grow else "")
+    if cfg.kind == "cache" and args.policy != "lru":
+        workload += f"+{args.policy}"
     traffic = measured_traffic(workload)
     copy_gbps = measure_copy_gbps(torch)
     line = {

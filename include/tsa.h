@@ -274,6 +274,43 @@ tsa_status tsa_resolve(const tsa_cache_desc* desc, int32_t* page_table, int32_t*
                        const void* host_k, const void* host_v, void* pool_k, void* pool_v,
                        int32_t* slots_out, int32_t* hits, int32_t* misses, void* stream);
 
+/* ------------------------------------------------------------------------
+ * tsa_resolve_policy - tsa_resolve under another replacement policy.
+ *   [HISPARSE-NEWS] compares LRU with FIFO, random and the offline Belady
+ *   policy by miss rate (13.4 / 17.2 / 16.1 / 8.2 % at B = 4096) without
+ *   defining them further. Under every policy the step's hits are kept,
+ *   free slots are taken first, and the r-th miss (ascending token order)
+ *   takes the r-th victim; the policies order the other slots:
+ *     TSA_EVICT_LRU       (last use, slot), as tsa_resolve
+ *     TSA_EVICT_FIFO      (fetch step, slot): a hit does not restamp
+ *     TSA_EVICT_RANDOM    (key, slot), key = top 31 bits of SplitMix64
+ *                         (Steele, Lea, Flood, OOPSLA 2014) chained over
+ *                         seed, request, step and slot:
+ *                         x = mix(seed); x = mix(x + b); x = mix(x + step);
+ *                         x = mix(x + slot); key = x >> 33, where mix(z)
+ *                         adds 0x9E3779B97F4A7C15 and applies the
+ *                         generator's output function
+ *     TSA_EVICT_PRIORITY  largest priority[b][token] first, then slot; with
+ *                         the step of each token's next selection (INT32_MAX
+ *                         for never) this is the offline Belady policy
+ *   priority (device) int32 [B][N], required for TSA_EVICT_PRIORITY, else
+ *            ignored (negative values count as 0)
+ *   Other arguments, ownership and errors as for tsa_resolve;
+ *   TSA_ERR_INVALID_ARG for an unknown policy.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  TSA_EVICT_LRU = 0,
+  TSA_EVICT_FIFO = 1,
+  TSA_EVICT_RANDOM = 2,
+  TSA_EVICT_PRIORITY = 3
+} tsa_evict_policy;
+
+tsa_status tsa_resolve_policy(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,
+                              int32_t* last_use, const int32_t* sel, int32_t k, int32_t step,
+                              int32_t policy, uint64_t seed, const int32_t* priority,
+                              const void* host_k, const void* host_v, void* pool_k, void* pool_v,
+                              int32_t* slots_out, int32_t* hits, int32_t* misses, void* stream);
+
 /* tsa_cache_reset - mark every page-table entry and slot empty (-1), so the
  * next step misses every selected token ([HISPARSE-NEWS]: the hot cache is
  * disposable, the host copy is authoritative). Uses a fill kernel. */

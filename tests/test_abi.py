@@ -114,6 +114,13 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
     st = lib.tsa_resolve(ctypes.byref(c), fake, fake, fake, fake, 16, -1, fake, fake, fake, fake, fake,
                          None, None, None)
     assert st == B.TSA_ERR_INVALID_ARG
+    # replacement policy: unknown policy, priority policy without priorities
+    st = lib.tsa_resolve_policy(ctypes.byref(c), fake, fake, fake, fake, 16, 0, 4, 0, None, fake, fake, fake,
+                                fake, fake, None, None, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"policy" in lib.tsa_last_error()
+    st = lib.tsa_resolve_policy(ctypes.byref(c), fake, fake, fake, fake, 16, 0, 3, 0, None, fake, fake, fake,
+                                fake, fake, None, None, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"priority is NULL" in lib.tsa_last_error()
     # token decode: k > N
     t = B.TokenDesc(1, 100, 8, 32, 128, 64, B.TSA_BF16)
     st = lib.tsa_token_decode(ctypes.byref(t), fake, fake, fake, fake, fake, 101, fake, None, fake, 1 << 30, None)

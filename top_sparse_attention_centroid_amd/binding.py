@@ -17,6 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsa.so"
 TSA_OK, TSA_ERR_INVALID_ARG, TSA_ERR_UNSUPPORTED, TSA_ERR_WORKSPACE, TSA_ERR_HIP = range(5)
 TSA_F32, TSA_BF16 = 0, 1
 OP_INDEX_BUILD, OP_SPARSE_DECODE, OP_TOKEN_DECODE, OP_ATTEND_ROWS = range(4)
+EVICT_POLICIES = {"lru": 0, "fifo": 1, "random": 2, "priority": 3}
 
 _I32 = ctypes.c_int32
 _P = ctypes.c_void_p
@@ -54,6 +55,8 @@ _SIGNATURES = {
     "tsa_token_decode": [ctypes.POINTER(TokenDesc), _P, _P, _P, _P, _P, _I32, _P, _P, _P,
                          ctypes.c_size_t, _P],
     "tsa_resolve": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P],
+    "tsa_resolve_policy": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _I32, _I32, _I32, ctypes.c_uint64, _P,
+                           _P, _P, _P, _P, _P, _P, _P, _P],
     "tsa_cache_reset": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P],
     "tsa_attend_rows": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_workspace_bytes": [_I32, _P, _I32, ctypes.POINTER(ctypes.c_size_t)],
@@ -346,8 +349,12 @@ def attend_rows(q, k_rows, v_rows, row_ids, row_counts=None, *, out=None, ws=Non
 
 
 def resolve(page_table, slot_token, last_use, sel, step: int, host_k, host_v, pool_k, pool_v, *,
-            slots_out=None, hits=None, misses=None, stream=None):
-    """One RESOLVE step for all requests. Returns (slots_out, hits, misses)."""
+            slots_out=None, hits=None, misses=None, stream=None, policy: str = "lru", seed: int = 0,
+            priority=None):
+    """One RESOLVE step for all requests. Returns (slots_out, hits, misses).
+
+    policy: "lru" (default), "fifo", "random" (seeded) or "priority"
+    (evict the largest priority[b][token] first; Belady with next-use steps)."""
     B, N, Hkv, d = host_k.shape
     S = pool_k.shape[1]
     k = sel.shape[1]
@@ -367,9 +374,22 @@ def resolve(page_table, slot_token, last_use, sel, step: int, host_k, host_v, po
         hits = torch.empty((B,), dtype=torch.int32, device=dev)
     if misses is None:
         misses = torch.empty((B,), dtype=torch.int32, device=dev)
-    _check(load().tsa_resolve(ctypes.byref(desc), _ptr(page_table), _ptr(slot_token), _ptr(last_use),
-                              _ptr(sel), k, step, _ptr(host_k), _ptr(host_v), _ptr(pool_k), _ptr(pool_v),
-                              _ptr(slots_out), _ptr(hits), _ptr(misses), _stream(stream)))
+    if policy not in EVICT_POLICIES:
+        raise ValueError(f"unknown policy {policy!r}; one of {sorted(EVICT_POLICIES)}")
+    if policy == "lru":
+        _check(load().tsa_resolve(ctypes.byref(desc), _ptr(page_table), _ptr(slot_token), _ptr(last_use),
+                                  _ptr(sel), k, step, _ptr(host_k), _ptr(host_v), _ptr(pool_k), _ptr(pool_v),
+                                  _ptr(slots_out), _ptr(hits), _ptr(misses), _stream(stream)))
+        return slots_out, hits, misses
+    if policy == "priority":
+        if priority is None:
+            raise ValueError("policy 'priority' needs priority [B][N] int32")
+        _dev(priority, "priority")
+        _i32(priority, "priority", (B, N))
+    _check(load().tsa_resolve_policy(ctypes.byref(desc), _ptr(page_table), _ptr(slot_token), _ptr(last_use),
+                                     _ptr(sel), k, step, EVICT_POLICIES[policy], seed & ((1 << 64) - 1),
+                                     _ptr(priority), _ptr(host_k), _ptr(host_v), _ptr(pool_k), _ptr(pool_v),
+                                     _ptr(slots_out), _ptr(hits), _ptr(misses), _stream(stream)))
     return slots_out, hits, misses
 
 

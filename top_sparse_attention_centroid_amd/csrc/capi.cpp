@@ -456,10 +456,11 @@ tsa_status tsa_attend_rows(const tsa_attn_desc* desc, const void* q, const void*
   return ok();
 }
 
-tsa_status tsa_resolve(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,
-                       int32_t* last_use, const int32_t* sel, int32_t k, int32_t step,
-                       const void* host_k, const void* host_v, void* pool_k, void* pool_v,
-                       int32_t* slots_out, int32_t* hits, int32_t* misses, void* stream) {
+tsa_status tsa_resolve_policy(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,
+                              int32_t* last_use, const int32_t* sel, int32_t k, int32_t step, int32_t policy,
+                              uint64_t seed, const int32_t* priority, const void* host_k, const void* host_v,
+                              void* pool_k, void* pool_v, int32_t* slots_out, int32_t* hits, int32_t* misses,
+                              void* stream) {
   if (tsa_status s = check_cache(desc)) return s;
   REQUIRE_PTR(page_table); REQUIRE_PTR(slot_token); REQUIRE_PTR(last_use); REQUIRE_PTR(sel);
   REQUIRE_PTR(host_k); REQUIRE_PTR(host_v); REQUIRE_PTR(pool_k); REQUIRE_PTR(pool_v); REQUIRE_PTR(slots_out);
@@ -468,12 +469,24 @@ tsa_status tsa_resolve(const tsa_cache_desc* desc, int32_t* page_table, int32_t*
   if (k < 1 || k > d.n_slots || k > kMaxTokenK)
     return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, min(S=%d, %d)]", k, d.n_slots, kMaxTokenK);
   if (step < 0 || step == INT32_MAX) return fail(TSA_ERR_INVALID_ARG, "step %d out of range", step);
+  if (policy < TSA_EVICT_LRU || policy > TSA_EVICT_PRIORITY)
+    return fail(TSA_ERR_INVALID_ARG, "unknown replacement policy %d", policy);
+  if (policy == TSA_EVICT_PRIORITY) REQUIRE_PTR(priority);
   ResolveParams rp{page_table, slot_token, last_use, sel, host_k, host_v, pool_k, pool_v, slots_out, hits,
                    misses, static_cast<long long>(d.n_kv_heads) * d.head_dim * esize(d.dtype),
-                   d.batch, d.n_tokens, d.n_slots, k, step};
+                   d.batch, d.n_tokens, d.n_slots, k, step, policy, static_cast<unsigned long long>(seed),
+                   priority};
   hipError_t e = launch_resolve(rp, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "resolve launch");
   return ok();
+}
+
+tsa_status tsa_resolve(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,
+                       int32_t* last_use, const int32_t* sel, int32_t k, int32_t step,
+                       const void* host_k, const void* host_v, void* pool_k, void* pool_v,
+                       int32_t* slots_out, int32_t* hits, int32_t* misses, void* stream) {
+  return tsa_resolve_policy(desc, page_table, slot_token, last_use, sel, k, step, TSA_EVICT_LRU, 0, nullptr,
+                            host_k, host_v, pool_k, pool_v, slots_out, hits, misses, stream);
 }
 
 tsa_status tsa_cache_reset(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,

@@ -139,8 +139,13 @@ struct ResolveParams {
   int32_t* misses;         // [B] or null
   long long row_bytes;     // Hkv * d * element size (multiple of 16)
   int B, N, S, k, step;
+  int policy;              // kEvictLru / kEvictFifo / kEvictRandom / kEvictPriority
+  unsigned long long seed; // random policy
+  const int32_t* priority; // [B][N] priority policy: evict the largest value first
 };
 hipError_t launch_resolve(const ResolveParams& p, hipStream_t s);
+
+constexpr int kEvictLru = 0, kEvictFifo = 1, kEvictRandom = 2, kEvictPriority = 3;
 
 hipError_t launch_fill_i32(int32_t* p, long long n, int32_t value, hipStream_t s);
 

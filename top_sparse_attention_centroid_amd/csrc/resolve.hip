@@ -4,19 +4,28 @@
 // KV stays in pinned host memory, HBM holds S slots per request per layer).
 //
 // One workgroup of 1024 threads per request:
-//   1. every slot gets the 64-bit key (last_use + 1) << 32 | slot in LDS
-//      (free slots, last_use = -1, get the smallest keys);
-//   2. selected tokens look up the page table; hit slots get the key of the
-//      current step, which sorts them after every evictable slot;
+//   1. every slot gets a 64-bit key (policy word) << 32 | slot in LDS; under
+//      LRU the policy word is last_use + 1, so free slots (last_use = -1)
+//      get the smallest keys;
+//   2. selected tokens look up the page table; hit slots get the largest
+//      policy word, which sorts them after every evictable slot;
 //   3. misses are ranked in selection order (block prefix sums);
 //   4. a bitonic sort of the keys in LDS orders the slots by
-//      (last_use, slot); the r-th miss takes the r-th slot;
+//      (policy word, slot); the r-th miss takes the r-th slot;
 //   5. page table, slot owners and stamps are updated in place;
 //   6. the missed tokens' K and V rows (all KV heads, contiguous in the host
 //      copy) are read straight from host-mapped memory and stored into the
 //      slots, one wave per missed token, 16 B per lane.
 // Token ids outside [0, N) are ignored (slot -1) so a bad selection cannot
 // address memory outside the tables.
+//
+// Replacement policies (the analysis compares LRU with FIFO, random and the
+// offline Belady policy by miss rate) differ only in the high word of the
+// slot key: LRU the last use, FIFO the fetch step (hits keep their stamp),
+// random a SplitMix64 key of (seed, request, step, slot) (Steele, Lea and
+// Flood, OOPSLA 2014), priority the complement of a caller-given per-token
+// value (Belady: the step of the token's next selection). Free slots sort
+// first and the step's hits last under every policy.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -24,6 +33,22 @@ namespace tsa {
 
 constexpr int kResolveThreads = 1024;
 constexpr int kResolvePer = kMaxTokenK / kResolveThreads;  // selected tokens per thread
+
+__device__ __forceinline__ unsigned long long splitmix64(unsigned long long x) {
+  unsigned long long z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// 31-bit key chained over (seed, request, step, slot).
+__device__ __forceinline__ uint32_t random_key(unsigned long long seed, int b, int step, int slot) {
+  unsigned long long x = splitmix64(seed);
+  x = splitmix64(x + static_cast<unsigned long long>(b));
+  x = splitmix64(x + static_cast<unsigned long long>(static_cast<uint32_t>(step)));
+  x = splitmix64(x + static_cast<unsigned long long>(slot));
+  return static_cast<uint32_t>(x >> 33);
+}
 
 __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams p, int spow2) {
   constexpr int NW = kResolveThreads / kWave;
@@ -37,12 +62,28 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   int32_t* st = p.slot_token + static_cast<long long>(b) * p.S;
   int32_t* lu = p.last_use + static_cast<long long>(b) * p.S;
   const int32_t* sel = p.sel + static_cast<long long>(b) * p.k;
-  const unsigned long long now = static_cast<unsigned long long>(static_cast<uint32_t>(p.step + 1)) << 32;
+  const unsigned long long hit_key = 0xFFFFFFFFull << 32;  // after every evictable slot
 
   for (int s = tid; s < spow2; s += kResolveThreads) {
-    sk[s] = s < p.S ? (static_cast<unsigned long long>(static_cast<uint32_t>(lu[s] + 1)) << 32) |
-                          static_cast<uint32_t>(s)
-                    : ~0ull;
+    unsigned long long key = ~0ull;
+    if (s < p.S) {
+      uint32_t hi;
+      if (p.policy == kEvictLru || p.policy == kEvictFifo) {
+        hi = static_cast<uint32_t>(lu[s] + 1);  // free slots carry -1
+      } else {
+        const int t = st[s];
+        if (t < 0 || t >= p.N) {
+          hi = 0;  // free
+        } else if (p.policy == kEvictRandom) {
+          hi = 1u + random_key(p.seed, b, p.step, s);
+        } else {
+          const int pr = min(max(p.priority[static_cast<long long>(b) * p.N + t], 0), 0x7FFFFFFF);
+          hi = 1u + static_cast<uint32_t>(0x7FFFFFFF - pr);
+        }
+      }
+      key = (static_cast<unsigned long long>(hi) << 32) | static_cast<uint32_t>(s);
+    }
+    sk[s] = key;
   }
   __syncthreads();
 
@@ -58,7 +99,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
         tok[j] = t;
         const int sl = pt[t];
         slot[j] = (sl >= 0 && sl < p.S) ? sl : -1;  // a corrupt entry counts as absent
-        if (slot[j] >= 0) sk[slot[j]] = now | static_cast<uint32_t>(slot[j]);
+        if (slot[j] >= 0) sk[slot[j]] = hit_key | static_cast<uint32_t>(slot[j]);
       }
     }
   }
@@ -98,7 +139,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       continue;
     }
     if (slot[j] >= 0) {
-      lu[slot[j]] = p.step;
+      if (p.policy != kEvictFifo) lu[slot[j]] = p.step;  // FIFO keeps the fetch step
     } else {
       const int v = static_cast<int>(sk[rank[j]] & 0xffffffffu);
       const int old = st[v];
