@@ -30,10 +30,11 @@ Modules:
   cache  batch-step LRU over a fixed slot pool (RESOLVE), cache-mediated
          attention
   append per-step KV and posting-list append with per-list free entries
+  variants cosine similarity; sink and window tokens beside the lists
 
 Parity pins: every function is checked by tests marked ``not gpu`` against
 closed forms, brute force on tiny inputs, a library routine for the dense
 special case, and the op counts the KARAT worked example prints.
 """
 
-from . import ivf, token, cache, append  # noqa: F401
+from . import ivf, token, cache, append, variants  # noqa: F401
