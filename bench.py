@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random", "belady"],
                     help="hot-cache workload: replacement policy of RESOLVE (belady = offline, from the "
                          "trace's next-use steps)")
+    ap.add_argument("--similarity", default="dot", choices=["dot", "cosine"],
+                    help="inverted-index workloads: centroid similarity")
+    ap.add_argument("--sink", type=int, default=0, help="inverted-index workloads: leading tokens always attended")
+    ap.add_argument("--window", type=int, default=0,
+                    help="inverted-index workloads: trailing tokens always attended")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (the gather kernel is then timed "
                          "in an eager pass over the same steps after the timed region)")
@@ -160,12 +165,25 @@ def bench_ivf(args, cfg, torch, tsa, W):
     desc = tsa.binding.ivf_desc(p["keys"], p["centroids"], Hq)
     ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
 
+    variant = args.similarity != "dot" or args.sink > 0 or args.window > 0
+    if variant:
+        ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX, desc, k), dtype=torch.uint8,
+                         device=dev)
+
     def call(i):
-        tsa.sparse_decode(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
-                          out=out, uniq_out=uniq[i % nq], ws=ws)
+        if variant:
+            tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
+                                 similarity=args.similarity, n_sink=args.sink, n_window=args.window,
+                                 out=out, uniq_out=uniq[i % nq], ws=ws)
+        else:
+            tsa.sparse_decode(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
+                              out=out, uniq_out=uniq[i % nq], ws=ws)
 
     res = _timed(args, call, torch, tsa, n_distinct=nq)
-    rows_per_set = uniq.sum(dim=(1, 2)).cpu().double()
+    # rows read per step: unique list rows, plus the sink / window rows (an
+    # upper bound: a list row inside those ranges is read once, counted twice)
+    fixed = min(args.sink + args.window, cfg.n_tokens) * B * Hkv
+    rows_per_set = uniq.sum(dim=(1, 2)).cpu().double() + fixed
     rows = sum(float(rows_per_set[i % nq]) for i in range(args.steps))
     res["step_bytes"] = [float(rows_per_set[i % nq]) * (2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4))
                          for i in range(args.steps)]
@@ -471,6 +489,11 @@ def main():
     bytes_per_launch = sum(res["step_bytes"][i] for i in res["timed_steps"]) / len(res["timed_steps"])
     achieved = bytes_per_launch / (g_mean_ms / 1e3) / 1e9
     workload = cfg.name + (f"+grow-from-{args.grow}" if args.grow else "")
+    if cfg.kind == "ivf":
+        if args.similarity != "dot":
+            workload += f"+{args.similarity}"
+        if args.sink or args.window:
+            workload += f"+sink{args.sink}+window{args.window}"
     if cfg.kind == "cache" and args.policy != "lru":
         workload += f"+{args.policy}"
     traffic = measured_traffic(workload)

@@ -74,7 +74,8 @@ typedef enum tsa_op {
   TSA_OP_INDEX_BUILD = 0,
   TSA_OP_SPARSE_DECODE = 1,
   TSA_OP_TOKEN_DECODE = 2,
-  TSA_OP_ATTEND_ROWS = 3
+  TSA_OP_ATTEND_ROWS = 3,
+  TSA_OP_SPARSE_DECODE_EX = 4
 } tsa_op;
 
 /* Inverted-index (centroid) problem. */
@@ -222,6 +223,43 @@ tsa_status tsa_sparse_decode_dyn(const tsa_ivf_desc* desc, const void* q, const 
                                  const void* k_cache, const void* v_cache, int32_t k, float* out,
                                  int32_t* sel_out, int32_t* rows_out, int32_t* uniq_out, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tsa_sparse_decode_ex - tsa_sparse_decode with the decode variants.
+ *   [KARAT] worked example, step 3: centroids are compared with the query by
+ *   cosine similarity; method details: the cores also run window-based
+ *   sparse attention (StreamingLLM) beside retrieval.
+ *   opts->similarity  TSA_SIM_DOT (q.c, as tsa_sparse_decode) or
+ *                     TSA_SIM_COSINE (q.c / |c|; 0 for a zero centroid)
+ *   opts->n_sink      the first n_sink tokens are attended by every head
+ *   opts->n_window    so are the last n_window tokens before the length
+ *                     (n_sink, n_window >= 0, n_sink + n_window <= 8192)
+ *   opts->lengths     (device, nullable) int32 [B]: current length L of each
+ *                     request (default N); both ranges are clipped to [0, L)
+ *   opts->lens        (device, nullable) list lengths of a growing index, as
+ *                     for tsa_sparse_decode_dyn
+ *   The attended set of a head is the union of its chosen lists' rows and
+ *   the two ranges; a row in both is attended once. rows_out and uniq_out
+ *   count list entries only. Workspace:
+ *   tsa_workspace_bytes(TSA_OP_SPARSE_DECODE_EX, desc, k, ...). Other
+ *   arguments as for tsa_sparse_decode.
+ * ---------------------------------------------------------------------- */
+typedef enum tsa_similarity { TSA_SIM_DOT = 0, TSA_SIM_COSINE = 1 } tsa_similarity;
+
+typedef struct tsa_decode_opts {
+  int32_t similarity;       /* tsa_similarity                               */
+  int32_t n_sink;           /* leading tokens always attended               */
+  int32_t n_window;         /* trailing tokens (before the length) attended */
+  int32_t reserved;         /* 0                                            */
+  const int32_t* lengths;   /* device [B] or NULL                           */
+  const int32_t* lens;      /* device [B][Hkv][C] or NULL                   */
+} tsa_decode_opts;
+
+tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts* opts, const void* q,
+                                const void* centroids, const int32_t* offsets, const int32_t* ids,
+                                const void* k_cache, const void* v_cache, int32_t k, float* out,
+                                int32_t* sel_out, int32_t* rows_out, int32_t* uniq_out, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * tsa_token_decode - token-level indexer top-k and attention (DSA style).

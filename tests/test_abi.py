@@ -114,6 +114,17 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
     st = lib.tsa_resolve(ctypes.byref(c), fake, fake, fake, fake, 16, -1, fake, fake, fake, fake, fake,
                          None, None, None)
     assert st == B.TSA_ERR_INVALID_ARG
+    # decode variants: bad similarity, too many fixed rows, null opts
+    ws_ex = B.workspace_bytes(B.OP_SPARSE_DECODE_EX, d, 4)
+    assert ws_ex > ws_need
+    for opts in (B.DecodeOpts(2, 0, 0, 0, None, None), B.DecodeOpts(0, 5000, 4000, 0, None, None),
+                 B.DecodeOpts(0, -1, 0, 0, None, None)):
+        st = lib.tsa_sparse_decode_ex(ctypes.byref(d), ctypes.byref(opts), fake, fake, fake, fake, fake, fake, 4,
+                                      fake, None, None, None, fake, ws_ex, None)
+        assert st == B.TSA_ERR_INVALID_ARG
+    st = lib.tsa_sparse_decode_ex(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, 4, fake, None, None,
+                                  None, fake, ws_ex, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"opts is NULL" in lib.tsa_last_error()
     # replacement policy: unknown policy, priority policy without priorities
     st = lib.tsa_resolve_policy(ctypes.byref(c), fake, fake, fake, fake, 16, 0, 4, 0, None, fake, fake, fake,
                                 fake, fake, None, None, None)

@@ -1,0 +1,188 @@
+"""GPU parity of the decode variants (cosine similarity, sink/window rows
+beside the lists, their mix with a growing index) against the variants
+oracle, and the token selector feeding the hot cache end to end."""
+
+import numpy as np
+import pytest
+import torch
+
+import top_sparse_attention_centroid_amd as tsa
+from oracle import ivf, variants
+from top_sparse_attention_centroid_amd import workloads as W
+
+from helpers import GAP_MIN, OUT_TOL, announce, f64, out_error
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _problem(seed_scale=0, **kw):
+    base = dict(batch=3, n_tokens=6000, n_centroids=64, top_k=6, n_kv_heads=2, n_q_heads=8, steps=1)
+    base.update(kw)
+    cfg = W.config(2, **base)
+    p = W.ivf_problem(cfg, device=DEV)
+    if seed_scale:
+        # unequal centroid norms, so that cosine and dot rankings differ
+        g = torch.Generator(device=DEV).manual_seed(seed_scale)
+        f = torch.rand(p["centroids"].shape[:-1] + (1,), generator=g, device=DEV) * 1.5 + 0.5
+        p["centroids"] = (p["centroids"].float() * f).to(cfg.torch_dtype)
+    return cfg, p
+
+
+def _queries(cfg, p, similarity, max_rounds=40):
+    """Queries whose oracle top-k gap (under `similarity`) is >= GAP_MIN."""
+    c64 = f64(p["centroids"])
+    G = cfg.group
+
+    def gap(qv, b, h):
+        cb = c64[0 if c64.shape[0] == 1 else b, h // G]
+        s = variants.cosine_scores(qv, cb) if similarity == "cosine" else cb @ qv
+        return ivf.selection_gap(s, cfg.top_k)
+
+    q = W.ivf_queries(cfg, p["centroids"], steps=1)[0]
+    for salt in range(1, max_rounds + 1):
+        q64 = f64(q)
+        bad = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads) if gap(q64[b, h], b, h) < GAP_MIN]
+        if not bad:
+            return q
+        fresh = W.ivf_queries(cfg, p["centroids"], steps=1, salt=salt)[0]
+        for b, h in bad:
+            q[b, h] = fresh[b, h]
+    raise RuntimeError("could not draw well-separated queries")
+
+
+def _check(cfg, p, q, off, ids, out, sel, **kw):
+    k64, v64, c64 = f64(p["keys"]), f64(p["values"]), f64(p["centroids"])
+    o64, i64 = off.cpu().numpy(), ids.cpu().numpy()
+    r = variants.sparse_decode_ex(f64(q), c64, o64, i64, k64, v64, cfg.top_k, **kw)
+    assert np.all(r["gap"] >= GAP_MIN)
+    assert np.array_equal(sel.cpu().numpy(), r["sel"]), "selection differs from the oracle"
+    err = out_error(out.cpu().numpy(), r["out"])
+    assert err <= OUT_TOL, f"output error {err}"
+    return r
+
+
+def test_cosine_selection_and_output():
+    cfg, p = _problem(seed_scale=7)
+    announce("variants: cosine")
+    off, ids = tsa.index_build(p["keys"], p["centroids"])
+    q = _queries(cfg, p, "cosine")
+    sel = torch.empty((cfg.batch, cfg.n_q_heads, cfg.top_k), dtype=torch.int32, device=DEV)
+    out = tsa.sparse_decode_ex(q, p["centroids"], off, ids, p["keys"], p["values"], cfg.top_k,
+                               similarity="cosine", sel_out=sel)
+    torch.cuda.synchronize()
+    _check(cfg, p, q, off, ids, out, sel, similarity="cosine")
+    sel_dot = torch.empty_like(sel)
+    tsa.sparse_decode(q, p["centroids"], off, ids, p["keys"], p["values"], cfg.top_k, sel_out=sel_dot)
+    torch.cuda.synchronize()
+    assert not torch.equal(sel, sel_dot), "scaled codebook should make cosine and dot choose differently"
+
+
+def test_sink_and_window_with_lengths():
+    cfg, p = _problem()
+    announce("variants: sink 64 + window 300, per-request lengths")
+    off, ids = tsa.index_build(p["keys"], p["centroids"])
+    q = _queries(cfg, p, "dot")
+    lengths = torch.tensor([6000, 4321, 777], dtype=torch.int32, device=DEV)
+    sel = torch.empty((cfg.batch, cfg.n_q_heads, cfg.top_k), dtype=torch.int32, device=DEV)
+    out = tsa.sparse_decode_ex(q, p["centroids"], off, ids, p["keys"], p["values"], cfg.top_k, n_sink=64,
+                               n_window=300, lengths=lengths, sel_out=sel)
+    torch.cuda.synchronize()
+    _check(cfg, p, q, off, ids, out, sel, n_sink=64, n_window=300, lengths=lengths.cpu().numpy())
+
+
+def test_overlapping_sink_and_window_cover_a_short_request():
+    # L = 1000 with a 600-token sink and a 700-token window: the ranges overlap
+    # and cover the whole request; list rows below L are all inside them
+    cfg, p = _problem(n_tokens=3000)
+    announce("variants: overlapping sink/window")
+    off, ids = tsa.index_build(p["keys"], p["centroids"])
+    q = _queries(cfg, p, "dot")
+    lengths = torch.tensor([1000, 1000, 2999], dtype=torch.int32, device=DEV)
+    sel = torch.empty((cfg.batch, cfg.n_q_heads, cfg.top_k), dtype=torch.int32, device=DEV)
+    out = tsa.sparse_decode_ex(q, p["centroids"], off, ids, p["keys"], p["values"], cfg.top_k, n_sink=600,
+                               n_window=700, lengths=lengths, sel_out=sel)
+    torch.cuda.synchronize()
+    _check(cfg, p, q, off, ids, out, sel, n_sink=600, n_window=700, lengths=lengths.cpu().numpy())
+
+
+def test_no_variant_is_bitwise_the_plain_decode():
+    cfg, p = _problem()
+    announce("variants: defaults == sparse_decode")
+    off, ids = tsa.index_build(p["keys"], p["centroids"])
+    q = _queries(cfg, p, "dot")
+    a = tsa.sparse_decode_ex(q, p["centroids"], off, ids, p["keys"], p["values"], cfg.top_k)
+    b = tsa.sparse_decode(q, p["centroids"], off, ids, p["keys"], p["values"], cfg.top_k)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_variants_over_a_growing_index():
+    """Cosine + sink/window over a dynamic index (list lengths) equals the
+    same variants over the compacted static lists."""
+    cfg, p = _problem(seed_scale=3, n_tokens=5000)
+    announce("variants over a growing index")
+    n_prefix = 4000
+    off, lens, ids = tsa.index_build_dyn(p["keys"], p["centroids"], n_prefix)
+    status = torch.empty((cfg.batch, cfg.n_kv_heads), dtype=torch.int32, device=DEV)
+    k_cache, v_cache = p["keys"].clone(), p["values"].clone()
+    for row in range(n_prefix, n_prefix + 200):
+        pos = torch.full((cfg.batch,), row, dtype=torch.int32, device=DEV)
+        tsa.kv_append(p["keys"][:, row].contiguous(), p["values"][:, row].contiguous(), pos, p["centroids"],
+                      k_cache, v_cache, off, lens, ids, status=status)
+    lengths = torch.full((cfg.batch,), n_prefix + 200, dtype=torch.int32, device=DEV)
+    q = _queries(cfg, p, "cosine")
+    sel = torch.empty((cfg.batch, cfg.n_q_heads, cfg.top_k), dtype=torch.int32, device=DEV)
+    out = tsa.sparse_decode_ex(q, p["centroids"], off, ids, k_cache, v_cache, cfg.top_k, similarity="cosine",
+                               n_sink=32, n_window=128, lengths=lengths, lens=lens, sel_out=sel)
+    torch.cuda.synchronize()
+    assert int(status.max()) <= 1
+    og, lg, ig = off.cpu().numpy(), lens.cpu().numpy(), ids.cpu().numpy()
+    B, Hkv, C = lg.shape
+    s_off = np.zeros((B, Hkv, C + 1), dtype=np.int64)
+    s_ids = np.full((B, Hkv, cfg.n_tokens), -1, dtype=np.int64)
+    from oracle import append
+    for b in range(B):
+        for g in range(Hkv):
+            co, ci = append.compact(og[b, g], lg[b, g], ig[b, g])
+            s_off[b, g] = co
+            s_ids[b, g, :len(ci)] = ci
+    r = variants.sparse_decode_ex(f64(q), f64(p["centroids"]), s_off, s_ids, f64(k_cache), f64(v_cache),
+                                  cfg.top_k, similarity="cosine", n_sink=32, n_window=128,
+                                  lengths=lengths.cpu().numpy())
+    assert np.all(r["gap"] >= GAP_MIN)
+    assert np.array_equal(sel.cpu().numpy(), r["sel"])
+    err = out_error(out.cpu().numpy(), r["out"])
+    assert err <= OUT_TOL, f"output error {err}"
+
+
+def test_token_selection_feeds_the_hot_cache():
+    """The indexer's selection drives RESOLVE; attention over the slots is
+    bitwise the token decode's attention over the full cache."""
+    cfg = W.config(3, batch=2, n_tokens=30_000, top_k=512, n_planted=16, steps=4)
+    announce("token selection -> RESOLVE -> attention over slots")
+    B, N, Hkv, d, k = cfg.batch, cfg.n_tokens, cfg.n_kv_heads, cfg.head_dim, cfg.top_k
+    S = 1024
+    prob = W.token_problem(cfg, device=DEV)
+    q_idx, q = W.token_queries(cfg, prob, steps=4)
+    hk = tsa.HostArray((B, N, Hkv, d), cfg.torch_dtype)
+    hv = tsa.HostArray((B, N, Hkv, d), cfg.torch_dtype)
+    hk.tensor.copy_(prob["keys"])
+    hv.tensor.copy_(prob["values"])
+    pt = torch.empty((B, N), dtype=torch.int32, device=DEV)
+    st = torch.empty((B, S), dtype=torch.int32, device=DEV)
+    lu = torch.empty((B, S), dtype=torch.int32, device=DEV)
+    tsa.cache_reset(pt, st, lu)
+    pool_k = torch.zeros((B, S, Hkv, d), dtype=cfg.torch_dtype, device=DEV)
+    pool_v = torch.zeros_like(pool_k)
+    sel = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    misses = []
+    for t in range(4):
+        out_tok = tsa.token_decode(q_idx[t], prob["k_idx"], q[t], prob["keys"], prob["values"], k, sel_out=sel)
+        slots, hits, miss = tsa.resolve(pt, st, lu, sel, t, hk.tensor, hv.tensor, pool_k, pool_v)
+        out_cache = tsa.attend_rows(q[t], pool_k, pool_v, slots)
+        torch.cuda.synchronize()
+        assert torch.equal(out_cache, out_tok), f"step {t}: cache path differs from the direct path"
+        assert torch.equal(hits + miss, torch.full_like(hits, k))
+        misses.append(int(miss.sum()))
+    assert misses[0] == B * k and min(misses[1:]) < B * k   # planted tokens stay selected and hit

@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     resolve,
     sparse_decode,
     sparse_decode_dyn,
+    sparse_decode_ex,
     time_next_gather,
     token_decode,
     workspace_bytes,
@@ -28,7 +29,7 @@ from .binding import (  # noqa: F401
 
 __all__ = [
     "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "kv_append", "sparse_decode",
-    "sparse_decode_dyn", "token_decode",
+    "sparse_decode_dyn", "sparse_decode_ex", "token_decode",
     "attend_rows", "resolve", "cache_reset", "HostArray", "time_next_gather", "workspace_bytes",
     "TsaError",
 ]

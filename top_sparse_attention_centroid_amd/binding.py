@@ -16,7 +16,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsa.so"
 
 TSA_OK, TSA_ERR_INVALID_ARG, TSA_ERR_UNSUPPORTED, TSA_ERR_WORKSPACE, TSA_ERR_HIP = range(5)
 TSA_F32, TSA_BF16 = 0, 1
-OP_INDEX_BUILD, OP_SPARSE_DECODE, OP_TOKEN_DECODE, OP_ATTEND_ROWS = range(4)
+OP_INDEX_BUILD, OP_SPARSE_DECODE, OP_TOKEN_DECODE, OP_ATTEND_ROWS, OP_SPARSE_DECODE_EX = range(5)
+SIMILARITY = {"dot": 0, "cosine": 1}
 EVICT_POLICIES = {"lru": 0, "fifo": 1, "random": 2, "priority": 3}
 
 _I32 = ctypes.c_int32
@@ -38,6 +39,11 @@ class CacheDesc(ctypes.Structure):
                 ("head_dim", _I32), ("dtype", _I32)]
 
 
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("similarity", _I32), ("n_sink", _I32), ("n_window", _I32), ("reserved", _I32),
+                ("lengths", _P), ("lens", _P)]
+
+
 class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", _I32), ("n_rows", _I32), ("n_kv_heads", _I32), ("n_q_heads", _I32),
                 ("head_dim", _I32), ("max_rows", _I32), ("dtype", _I32)]
@@ -48,6 +54,8 @@ _SIGNATURES = {
     "tsa_index_build": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_sparse_decode": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                           ctypes.c_size_t, _P],
+    "tsa_sparse_decode_ex": [ctypes.POINTER(IvfDesc), ctypes.POINTER(DecodeOpts), _P, _P, _P, _P, _P, _P, _I32,
+                             _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_index_build_dyn": [ctypes.POINTER(IvfDesc), _P, _P, _I32, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_kv_append": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "tsa_sparse_decode_dyn": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
@@ -265,6 +273,43 @@ def kv_append(new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids
                                 _ptr(k_cache), _ptr(v_cache), _ptr(offsets), _ptr(lens), _ptr(ids), _ptr(status),
                                 _stream(stream)))
     return status
+
+
+def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, similarity: str = "dot",
+                     n_sink: int = 0, n_window: int = 0, lengths=None, lens=None, out=None, sel_out=None,
+                     rows_out=None, uniq_out=None, ws=None, stream=None):
+    """Decode with the variants: cosine similarity and/or the first n_sink and
+    last n_window tokens (before lengths[b]) attended beside the lists."""
+    for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    if not (q.dtype == centroids.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, centroids, k_cache and v_cache must share a dtype")
+    if similarity not in SIMILARITY:
+        raise ValueError(f"similarity must be one of {sorted(SIMILARITY)}")
+    B, Hq, d = q.shape
+    desc = ivf_desc(k_cache, centroids, Hq)
+    if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("q / k_cache / v_cache shapes disagree")
+    Hkv, C, N = desc.n_kv_heads, desc.n_centroids, desc.n_tokens
+    _i32(offsets, "offsets", (B, Hkv, C + 1))
+    _i32(ids, "ids", (B, Hkv, N))
+    _i32(lengths, "lengths", (B,))
+    _i32(lens, "lens", (B, Hkv, C))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, d):
+        raise ValueError("out must be fp32 [B][Hq][d]")
+    _i32(sel_out, "sel_out", (B, Hq, k))
+    _i32(rows_out, "rows_out", (B, Hq))
+    _i32(uniq_out, "uniq_out", (B, Hkv))
+    opts = DecodeOpts(SIMILARITY[similarity], n_sink, n_window, 0, _ptr(lengths), _ptr(lens))
+    ws = _workspace(OP_SPARSE_DECODE_EX, desc, k, ws, q.device)
+    _check(load().tsa_sparse_decode_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(centroids),
+                                       _ptr(offsets), _ptr(ids), _ptr(k_cache), _ptr(v_cache), k, _ptr(out),
+                                       _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(),
+                                       _stream(stream)))
+    return out
 
 
 def sparse_decode_dyn(q, centroids, offsets, lens, ids, k_cache, v_cache, k: int, **kw):

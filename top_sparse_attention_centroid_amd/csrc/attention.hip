@@ -307,24 +307,39 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
                 g * kHeadDim + e * 8;
   const int32_t* rid = p.rowids + b * p.rid_bstride + g * p.rid_gstride;
   int* ids = ids_lds[wave];
+  // sink / window ranges of an explicit plan: attended through their own
+  // direct segments, so list rows inside them are skipped (empty by default)
+  int fx_sink = 0, fx_lo = 0, fx_hi = 0;
+  if constexpr (EXPLICIT) {
+    if (p.n_sink > 0 || p.n_window > 0) {
+      const int L = p.lengths ? min(max(p.lengths[b], 0), static_cast<int>(p.n_rows)) : static_cast<int>(p.n_rows);
+      fx_sink = min(p.n_sink, L);
+      fx_lo = p.n_window > 0 ? max(L - p.n_window, fx_sink) : L;
+      fx_hi = L;
+    }
+  }
 
   for (int s = w0 * NW + wave; s < nseg; s += p.W * NW) {
     int start, cnt;
     uint32_t mask;
+    bool direct = false;  // a token range [start, start + cnt) instead of list entries
     if constexpr (EXPLICIT) {
       const int4 d = p.seg[static_cast<long long>(bg) * p.smax + s];
       start = d.x;
       cnt = d.y;
       mask = static_cast<uint32_t>(d.z);
+      direct = d.w < 0;
     } else {
       start = s * p.seg_rows;
       cnt = min(p.seg_rows, total_rows - start);
       mask = (1u << G) - 1u;
     }
     for (int j = lane; j < cnt; j += kWave) {
-      const int id = rid[start + j];
+      const int id = direct ? start + j : rid[start + j];
       // ids outside [0, n_rows) are skipped, never dereferenced
-      ids[j] = static_cast<unsigned long long>(id) < static_cast<unsigned long long>(p.n_rows) ? id : -1;
+      bool ok = static_cast<unsigned long long>(id) < static_cast<unsigned long long>(p.n_rows);
+      if (!direct) ok = ok && !(id < fx_sink || (id >= fx_lo && id < fx_hi));
+      ids[j] = ok ? id : -1;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -333,7 +348,8 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
     float* part = p.partial + (static_cast<long long>(bg) * p.smax + s) * G * kPartStride;
     // A row read by a single head's pass streams past the caches; rows that a
     // second head will re-read stay cacheable so that pass hits L2.
-    if constexpr (!EXPLICIT) {
+    if (!EXPLICIT || (G > 1 && mask == (1u << G) - 1u)) {
+      // every head of the group reads these rows: score them for all heads at once
       all_heads_pass<G>(ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
     } else if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u) {
       head_passes<true>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);

@@ -78,10 +78,11 @@ struct IvfLayout {
   size_t seg = 0, nseg = 0, partial = 0, total = 0;
 };
 
-IvfLayout ivf_layout(const tsa_ivf_desc& d, int k) {
+// with_fixed: room for the sink / window segments of tsa_sparse_decode_ex
+IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false) {
   IvfLayout L;
   L.G = d.n_q_heads / d.n_kv_heads;
-  L.smax = L.G * k + ceil_div(d.n_tokens, kSegRows);
+  L.smax = L.G * k + ceil_div(d.n_tokens, kSegRows) + (with_fixed ? kMaxFixedRows / kSegRows + 2 : 0);
   const size_t bh = static_cast<size_t>(d.batch) * d.n_kv_heads;
   size_t off = 0;
   L.seg = off;    off += align_up(bh * L.smax * sizeof(int4));
@@ -254,17 +255,18 @@ tsa_status index_build_impl(const tsa_ivf_desc* desc, const void* keys, const vo
   return ok();
 }
 
-tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const void* q, const void* centroids,
-                              const int32_t* offsets, const int32_t* lens, const int32_t* ids,
-                              const void* k_cache, const void* v_cache, int32_t k, float* out, int32_t* sel_out,
-                              int32_t* rows_out, int32_t* uniq_out, void* ws, size_t ws_bytes, void* stream) {
+tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* opts, const void* q,
+                              const void* centroids, const int32_t* offsets, const int32_t* lens,
+                              const int32_t* ids, const void* k_cache, const void* v_cache, int32_t k, float* out,
+                              int32_t* sel_out, int32_t* rows_out, int32_t* uniq_out, void* ws, size_t ws_bytes,
+                              void* stream) {
   REQUIRE_PTR(q); REQUIRE_PTR(centroids); REQUIRE_PTR(offsets); REQUIRE_PTR(ids);
   REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(out); REQUIRE_PTR(ws);
   REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(k_cache, 16);
   REQUIRE_ALIGN(v_cache, 16); REQUIRE_ALIGN(out, 8); REQUIRE_ALIGN(ws, 16);
   const tsa_ivf_desc& d = *desc;
   if (k < 1 || k > d.n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d.n_centroids);
-  const IvfLayout L = ivf_layout(d, k);
+  const IvfLayout L = ivf_layout(d, k, opts != nullptr);
   if (ws_bytes < L.total) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   char* w = static_cast<char*>(ws);
   hipStream_t s = as_stream(stream);
@@ -272,6 +274,12 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const void* q, const voi
   SelectParams selp{q, centroids, codebook_stride(d), offsets, lens, sel_out, rows_out, uniq_out,
                     reinterpret_cast<int4*>(w + L.seg), reinterpret_cast<int32_t*>(w + L.nseg),
                     d.batch, d.n_kv_heads, d.n_centroids, k, L.smax, d.n_tokens};
+  if (opts) {
+    selp.cosine = opts->similarity == TSA_SIM_COSINE;
+    selp.n_sink = opts->n_sink;
+    selp.n_window = opts->n_window;
+    selp.lengths = opts->lengths;
+  }
   hipError_t e = launch_ivf_select(selp, d.dtype, L.G, s);
   if (e != hipSuccess) return hip_fail(e, "ivf_select launch");
 
@@ -282,8 +290,20 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const void* q, const voi
   gp.counts = nullptr; gp.count_const = 0;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k)); gp.seg_rows = kSegRows;
+  // expected segments: one per chosen list of the group (most lists fit one
+  // segment) plus the sink / window segments
+  int fixed_segs = 0;
+  if (opts) {
+    fixed_segs = ceil_div(std::min(opts->n_sink, d.n_tokens), kSegRows) +
+                 ceil_div(std::min(opts->n_window, d.n_tokens), kSegRows) + (opts->n_window > 0 ? 1 : 0);
+  }
+  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k + fixed_segs)); gp.seg_rows = kSegRows;
   gp.qscale = qscale(d.head_dim);
+  if (opts) {
+    gp.n_sink = opts->n_sink;
+    gp.n_window = opts->n_window;
+    gp.lengths = opts->lengths;
+  }
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, true, s)) return st;
   return ok();
 }
@@ -322,6 +342,13 @@ tsa_status tsa_workspace_bytes(int32_t op, const void* desc, int32_t k, size_t* 
       if (tsa_status s = check_ivf(d)) return s;
       if (k < 1 || k > d->n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d->n_centroids);
       *bytes = ivf_layout(*d, k).total;
+      return ok();
+    }
+    case TSA_OP_SPARSE_DECODE_EX: {
+      const auto* d = static_cast<const tsa_ivf_desc*>(desc);
+      if (tsa_status s = check_ivf(d)) return s;
+      if (k < 1 || k > d->n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d->n_centroids);
+      *bytes = ivf_layout(*d, k, true).total;
       return ok();
     }
     case TSA_OP_TOKEN_DECODE: {
@@ -383,8 +410,8 @@ tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void
                              int32_t* rows_out, int32_t* uniq_out, void* ws, size_t ws_bytes,
                              void* stream) {
   if (tsa_status s = check_ivf(desc)) return s;
-  return sparse_decode_impl(desc, q, centroids, offsets, nullptr, ids, k_cache, v_cache, k, out, sel_out, rows_out,
-                            uniq_out, ws, ws_bytes, stream);
+  return sparse_decode_impl(desc, nullptr, q, centroids, offsets, nullptr, ids, k_cache, v_cache, k, out, sel_out,
+                            rows_out, uniq_out, ws, ws_bytes, stream);
 }
 
 tsa_status tsa_sparse_decode_dyn(const tsa_ivf_desc* desc, const void* q, const void* centroids,
@@ -394,8 +421,25 @@ tsa_status tsa_sparse_decode_dyn(const tsa_ivf_desc* desc, const void* q, const 
                                  size_t ws_bytes, void* stream) {
   if (tsa_status s = check_ivf(desc)) return s;
   REQUIRE_PTR(lens);
-  return sparse_decode_impl(desc, q, centroids, offsets, lens, ids, k_cache, v_cache, k, out, sel_out, rows_out,
-                            uniq_out, ws, ws_bytes, stream);
+  return sparse_decode_impl(desc, nullptr, q, centroids, offsets, lens, ids, k_cache, v_cache, k, out, sel_out,
+                            rows_out, uniq_out, ws, ws_bytes, stream);
+}
+
+tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts* opts, const void* q,
+                                const void* centroids, const int32_t* offsets, const int32_t* ids,
+                                const void* k_cache, const void* v_cache, int32_t k, float* out,
+                                int32_t* sel_out, int32_t* rows_out, int32_t* uniq_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  REQUIRE_PTR(opts);
+  if (opts->similarity != TSA_SIM_DOT && opts->similarity != TSA_SIM_COSINE)
+    return fail(TSA_ERR_INVALID_ARG, "unknown similarity %d", opts->similarity);
+  if (opts->n_sink < 0 || opts->n_window < 0 ||
+      static_cast<long long>(opts->n_sink) + opts->n_window > kMaxFixedRows)
+    return fail(TSA_ERR_INVALID_ARG, "n_sink=%d, n_window=%d: each >= 0 and together <= %d", opts->n_sink,
+                opts->n_window, kMaxFixedRows);
+  return sparse_decode_impl(desc, opts, q, centroids, offsets, opts->lens, ids, k_cache, v_cache, k, out, sel_out,
+                            rows_out, uniq_out, ws, ws_bytes, stream);
 }
 
 tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const void* k_idx,

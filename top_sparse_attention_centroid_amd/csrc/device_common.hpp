@@ -102,6 +102,20 @@ struct QFrag<float> {
   }
 };
 
+// Sum of squares of 8 elements (bf16 pairs through v_dot2, exact products).
+__device__ __forceinline__ float sq8(const Raw8<bf16_t>& r) {
+  float acc = dot2_bf16(r.v.x, r.v.x, 0.f);
+  acc = dot2_bf16(r.v.y, r.v.y, acc);
+  acc = dot2_bf16(r.v.z, r.v.z, acc);
+  return dot2_bf16(r.v.w, r.v.w, acc);
+}
+__device__ __forceinline__ float sq8(const Raw8<float>& r) {
+  float s = r.a.x * r.a.x;
+  s = fmaf(r.a.y, r.a.y, s); s = fmaf(r.a.z, r.a.z, s); s = fmaf(r.a.w, r.a.w, s);
+  s = fmaf(r.b.x, r.b.x, s); s = fmaf(r.b.y, r.b.y, s); s = fmaf(r.b.z, r.b.z, s);
+  return fmaf(r.b.w, r.b.w, s);
+}
+
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
   Raw8<T> r;

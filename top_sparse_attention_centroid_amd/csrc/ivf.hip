@@ -327,9 +327,14 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * 16 + r;
+        float inv = 1.f;
+        if (p.cosine) {  // cosine similarity: q.c / |c| (1/|q| ranks nothing differently)
+          const float n2 = group16_sum(sq8(raw[u]));
+          inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float sc = group16_sum(qf[h].dot(raw[u]));
+          const float sc = group16_sum(qf[h].dot(raw[u])) * inv;
           if (e == 0 && c < C) keys[h * C + c] = order_key(sc);
         }
       }
@@ -400,6 +405,24 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
                                  static_cast<int>(m), c);
     }
     carry += tot;
+  }
+  // Fixed token ranges attended beside the lists by every head of the group
+  // (the first n_sink tokens and the last n_window before the request's
+  // length), as direct segments (list -1); the gather skips list rows that
+  // fall inside them, so each row is attended once.
+  if (p.n_sink > 0 || p.n_window > 0) {
+    const int L = p.lengths ? min(max(p.lengths[b], 0), p.N) : p.N;
+    const int sink_hi = min(p.n_sink, L);
+    const int win_lo = p.n_window > 0 ? max(L - p.n_window, sink_hi) : L;
+    const int nsink = (sink_hi + kSegRows - 1) / kSegRows;
+    const int nwin = (L - win_lo + kSegRows - 1) / kSegRows;
+    const int all = (1 << G) - 1;
+    for (int j = tid; j < nsink + nwin; j += 256) {
+      const int start = j < nsink ? j * kSegRows : win_lo + (j - nsink) * kSegRows;
+      const int cnt = min(kSegRows, (j < nsink ? sink_hi : L) - start);
+      if (carry + j < p.smax) seg[carry + j] = make_int4(start, cnt, all, -1);
+    }
+    carry += nsink + nwin;
   }
   uniq = block_sum<4>(uniq, scan_scratch);
   if (tid == 0) {

@@ -23,6 +23,7 @@ constexpr int kTokHistBits = 12;          // top bits of the score key in the th
 constexpr int kTokHistBins = 1 << kTokHistBits;
 constexpr int kMaxTokFilterChunks = 4096; // N <= kTokFilterTile * kMaxTokFilterChunks
 constexpr int kMaxCentroids = 4096;
+constexpr int kMaxFixedRows = 8192;   // sink + window rows of one decode
 constexpr int kMaxSlots = 4096;
 constexpr int kMaxTokenK = 4096;
 
@@ -63,9 +64,12 @@ struct SelectParams {
   int32_t* sel_out;        // [B][Hq][k] or null
   int32_t* rows_out;       // [B][Hq] or null
   int32_t* uniq_out;       // [B][Hkv] or null
-  int4* seg;               // [B*Hkv][smax]: {start, count, head mask, list}
+  int4* seg;               // [B*Hkv][smax]: {start, count, head mask, list}; list -1 = token range
   int32_t* nseg;           // [B*Hkv]
   int B, Hkv, C, k, smax, N;
+  int cosine;              // score q.c / |c| instead of q.c
+  int n_sink, n_window;    // token ranges attended beside the lists
+  const int32_t* lengths;  // [B] current length per request, or null (N)
 };
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s);
 
@@ -102,6 +106,8 @@ struct GatherParams {
   int count_max;           // implicit: capacity of each request's row-id array
   int seg_rows;            // implicit: rows per segment (<= kSegRows)
   float* partial;          // [B*Hkv][smax][G][kPartStride]
+  int n_sink, n_window;    // explicit plans: list rows inside these ranges are skipped
+  const int32_t* lengths;  // [B] or null (n_rows)
   float* out;              // [B][Hq][d]
   int B, Hkv, smax, W;     // W: workgroups per (request, KV head), 4 segments each in flight
   float qscale;            // log2(e) / sqrt(d)
