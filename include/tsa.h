@@ -347,7 +347,60 @@ tsa_status tsa_resolve_policy(const tsa_cache_desc* desc, int32_t* page_table, i
                               int32_t* last_use, const int32_t* sel, int32_t k, int32_t step,
                               int32_t policy, uint64_t seed, const int32_t* priority,
                               const void* host_k, const void* host_v, void* pool_k, void* pool_v,
-                              int32_t* slots_out, int32_t* hits, int32_t* misses, void* stream);
+                              int32_t* slots_out, int32_t* hits, int32_t* misses, int32_t* miss_tok,
+                              int32_t* miss_slot, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Layer groups that share one selection: cross-layer prefetch.
+ *   [HISPARSE-NOTES] method 3: some models reuse the indexer's selection
+ *   across a group of layers, so the rows every later layer of the group
+ *   needs are known exactly once the first layer's selection is; they can be
+ *   fetched ahead while earlier layers attend. [HISPARSE-NEWS]: exposed host
+ *   IO falls from 7-8 ms to about 3 ms per token with prefetch.
+ *
+ * tsa_resolve_policy's miss_tok / miss_slot (device, out, nullable, both or
+ *   neither) int32 [B][k]: the step's missed tokens in miss order and the
+ *   slot each took (the first misses[b] entries are valid).
+ *
+ * tsa_fetch_rows - copy the rows of a miss list from one more layer's host
+ *   copy into that layer's pool (same slots): the fetch part of RESOLVE
+ *   without the table update. Arguments as for tsa_resolve.
+ *
+ * tsa_hier_group_step - one decode step of a layer group sharing `sel`:
+ *   RESOLVE once (tables, miss list, layer 0's rows) on `stream`; the other
+ *   layers' rows on `fetch_stream`; each layer's attention over its pool on
+ *   `stream` once its rows are in. Per layer j (layers[j], a host array):
+ *   host_k/host_v (host-mapped [B][N][Hkv][d]), pool_k/pool_v (device
+ *   [B][S][Hkv][d]), q (device [B][Hq][d]), out (device fp32 [B][Hq][d]).
+ *   fetch_stream NULL: everything runs in order on `stream`. n_layers <= 17
+ *   (one fetch launch covers the other layers of the group).
+ *   events: two caller-created hipEvent_t (timing may be disabled): the fork
+ *   to fetch_stream and the join back to `stream`; required when
+ *   fetch_stream is given and n_layers > 1. misses, miss_tok, miss_slot are
+ *   required when n_layers > 1.
+ *   Workspace: tsa_workspace_bytes(TSA_OP_ATTEND_ROWS) of the attn desc
+ *   {B, S, Hkv, n_q_heads, d, max_rows = k, dtype}.
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_fetch_rows(const tsa_cache_desc* desc, const int32_t* miss_tok, const int32_t* miss_slot,
+                          const int32_t* misses, int32_t k, const void* host_k, const void* host_v,
+                          void* pool_k, void* pool_v, void* stream);
+
+typedef struct tsa_layer_io {
+  const void* host_k;
+  const void* host_v;
+  void* pool_k;
+  void* pool_v;
+  const void* q;
+  float* out;
+} tsa_layer_io;
+
+tsa_status tsa_hier_group_step(const tsa_cache_desc* desc, int32_t n_q_heads, int32_t n_layers,
+                               const tsa_layer_io* layers, int32_t* page_table, int32_t* slot_token,
+                               int32_t* last_use, const int32_t* sel, int32_t k, int32_t step,
+                               int32_t policy, uint64_t seed, const int32_t* priority,
+                               int32_t* slots_out, int32_t* hits, int32_t* misses, int32_t* miss_tok,
+                               int32_t* miss_slot, void* ws, size_t ws_bytes, void* stream,
+                               void* fetch_stream, void* const* events);
 
 /* tsa_cache_reset - mark every page-table entry and slot empty (-1), so the
  * next step misses every selected token ([HISPARSE-NEWS]: the hot cache is

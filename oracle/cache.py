@@ -30,6 +30,10 @@ events inside one step):
     into the slot.
   * A slot holds one token's K and V rows for every KV head of the layer.
 
+A layer group that shares one selection (a model reusing the indexer's
+choice across layers) keeps one set of tables; every layer's pool receives
+the same missed tokens' rows of its own host copy.
+
 Other replacement policies (the page compares LRU with FIFO, random and the
 offline Belady policy by miss rate; it does not define them further):
   * FIFO: a hit leaves the slot's stamp alone, so the stamp is the step of
@@ -50,7 +54,7 @@ import numpy as np
 
 from .ivf import attend
 
-__all__ = ["CacheState", "lru_step", "policy_step", "splitmix64", "random_key", "next_use_table",
+__all__ = ["CacheState", "lru_step", "policy_step", "group_step", "splitmix64", "random_key", "next_use_table",
            "fetch_rows", "attend_slots", "POLICIES", "NEVER"]
 
 POLICIES = ("lru", "fifo", "random", "belady")
@@ -180,6 +184,21 @@ def policy_step(state: CacheState, selected, t: int, policy: str = "lru", *, see
         lu[v] = t
         fetches.append((int(tok), int(v)))
     return pt[sel].copy(), int(resident.sum()), len(misses), fetches
+
+
+def group_step(state: CacheState, selected, t: int, hosts, pools, policy: str = "lru", **kw):
+    """One RESOLVE step for a group of layers that share the selection
+    ([HISPARSE-NOTES] method 3: a layer group reuses the indexer's choice).
+
+    The slot tables are shared: a shared selection drives every layer's
+    cache through the same decisions. The missed tokens' rows are copied for
+    every layer. hosts: [(host_k, host_v)] per layer ([N][Hkv][d]);
+    pools: [(pool_k, pool_v)] per layer ([S][Hkv][d], written in place).
+    Returns what policy_step returns."""
+    slots, h, m, fetches = policy_step(state, selected, t, policy, **kw)
+    for (hk, hv), (pk, pv) in zip(hosts, pools):
+        fetch_rows(pk, pv, hk, hv, fetches)
+    return slots, h, m, fetches
 
 
 def fetch_rows(pool_k, pool_v, host_k, host_v, fetches):

@@ -127,11 +127,26 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
     assert st == B.TSA_ERR_INVALID_ARG and b"opts is NULL" in lib.tsa_last_error()
     # replacement policy: unknown policy, priority policy without priorities
     st = lib.tsa_resolve_policy(ctypes.byref(c), fake, fake, fake, fake, 16, 0, 4, 0, None, fake, fake, fake,
-                                fake, fake, None, None, None)
+                                fake, fake, None, None, None, None, None)
     assert st == B.TSA_ERR_INVALID_ARG and b"policy" in lib.tsa_last_error()
     st = lib.tsa_resolve_policy(ctypes.byref(c), fake, fake, fake, fake, 16, 0, 3, 0, None, fake, fake, fake,
-                                fake, fake, None, None, None)
+                                fake, fake, None, None, None, None, None)
     assert st == B.TSA_ERR_INVALID_ARG and b"priority is NULL" in lib.tsa_last_error()
+    st = lib.tsa_resolve_policy(ctypes.byref(c), fake, fake, fake, fake, 16, 0, 0, 0, None, fake, fake, fake,
+                                fake, fake, None, None, fake, None, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"miss_tok and miss_slot" in lib.tsa_last_error()
+    # layer group: no layers, a NULL layer pointer, events missing for a fetch stream
+    io = (B.LayerIO * 2)(B.LayerIO(fake, fake, fake, fake, fake, fake), B.LayerIO(fake, None, fake, fake, fake, fake))
+    ws_at = B.workspace_bytes(B.OP_ATTEND_ROWS, B.AttnDesc(2, 64, 8, 32, 128, 16, B.TSA_BF16))
+    st = lib.tsa_hier_group_step(ctypes.byref(c), 32, 0, ctypes.cast(io, ctypes.c_void_p), fake, fake, fake, fake,
+                                 16, 0, 0, 0, None, fake, fake, fake, fake, fake, fake, ws_at, None, None, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"n_layers" in lib.tsa_last_error()
+    st = lib.tsa_hier_group_step(ctypes.byref(c), 32, 2, ctypes.cast(io, ctypes.c_void_p), fake, fake, fake, fake,
+                                 16, 0, 0, 0, None, fake, fake, fake, fake, fake, fake, ws_at, None, None, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"layers[1]" in lib.tsa_last_error()
+    st = lib.tsa_hier_group_step(ctypes.byref(c), 32, 2, ctypes.cast(io, ctypes.c_void_p), fake, fake, fake, fake,
+                                 16, 0, 0, 0, None, fake, fake, fake, fake, fake, fake, ws_at, None, fake, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"events is NULL" in lib.tsa_last_error()
     # token decode: k > N
     t = B.TokenDesc(1, 100, 8, 32, 128, 64, B.TSA_BF16)
     st = lib.tsa_token_decode(ctypes.byref(t), fake, fake, fake, fake, fake, 101, fake, None, fake, 1 << 30, None)

@@ -144,3 +144,29 @@ def test_next_use_table():
     assert nu[1] == {1: 2, 4: 3}
     assert nu[3] == {}
     assert cache.next_use_table([[5]])[0].get(5, cache.NEVER) == cache.NEVER
+
+
+def test_layer_group_shares_tables_and_keeps_every_pool_exact():
+    """A group of layers sharing the selection: the tables evolve as for one
+    layer, and every layer's pool holds its own rows of each resident token,
+    so attention through the cache equals direct attention in every layer."""
+    rng = np.random.default_rng(21)
+    N, S, Hkv, d, Hq, L, T = 200, 48, 2, 8, 4, 3, 12
+    hosts = [(rng.standard_normal((N, Hkv, d)), rng.standard_normal((N, Hkv, d))) for _ in range(L)]
+    pools = [(np.zeros((S, Hkv, d)), np.zeros((S, Hkv, d))) for _ in range(L)]
+    grp, single = cache.CacheState(N, S), cache.CacheState(N, S)
+    sel = rng.choice(N, size=32, replace=False)
+    for t in range(T):
+        keep = rng.choice(sel, size=24, replace=False)
+        fresh = rng.choice(np.setdiff1d(np.arange(N), sel), size=8, replace=False)
+        sel = np.concatenate([keep, fresh])
+        slots, h, m, _ = cache.group_step(grp, sel, t, hosts, pools)
+        s1, h1, m1, _ = cache.lru_step(single, sel, t)
+        assert np.array_equal(slots, s1) and (h, m) == (h1, m1)
+        assert np.array_equal(grp.page_table, single.page_table)
+        res = np.flatnonzero(grp.slot_token >= 0)
+        for (hk, hv), (pk, pv) in zip(hosts, pools):
+            assert np.array_equal(pk[res], hk[grp.slot_token[res]]) and np.array_equal(pv[res], hv[grp.slot_token[res]])
+            q = rng.standard_normal((Hq, d))
+            direct = cache.attend_slots(q, hk, hv, sel)
+            assert np.array_equal(cache.attend_slots(q, pk, pv, slots), direct)

@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     abi_version,
     attend_rows,
     cache_reset,
+    fetch_rows,
+    hier_group_step,
     index_build,
     index_build_dyn,
     kv_append,
@@ -30,6 +32,6 @@ from .binding import (  # noqa: F401
 __all__ = [
     "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "kv_append", "sparse_decode",
     "sparse_decode_dyn", "sparse_decode_ex", "token_decode",
-    "attend_rows", "resolve", "cache_reset", "HostArray", "time_next_gather", "workspace_bytes",
+    "attend_rows", "resolve", "cache_reset", "fetch_rows", "hier_group_step", "HostArray", "time_next_gather", "workspace_bytes",
     "TsaError",
 ]

@@ -44,6 +44,10 @@ class DecodeOpts(ctypes.Structure):
                 ("lengths", _P), ("lens", _P)]
 
 
+class LayerIO(ctypes.Structure):
+    _fields_ = [("host_k", _P), ("host_v", _P), ("pool_k", _P), ("pool_v", _P), ("q", _P), ("out", _P)]
+
+
 class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", _I32), ("n_rows", _I32), ("n_kv_heads", _I32), ("n_q_heads", _I32),
                 ("head_dim", _I32), ("max_rows", _I32), ("dtype", _I32)]
@@ -64,7 +68,10 @@ _SIGNATURES = {
                          ctypes.c_size_t, _P],
     "tsa_resolve": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P],
     "tsa_resolve_policy": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _I32, _I32, _I32, ctypes.c_uint64, _P,
-                           _P, _P, _P, _P, _P, _P, _P, _P],
+                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "tsa_fetch_rows": [ctypes.POINTER(CacheDesc), _P, _P, _P, _I32, _P, _P, _P, _P, _P],
+    "tsa_hier_group_step": [ctypes.POINTER(CacheDesc), _I32, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                            ctypes.c_uint64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P],
     "tsa_cache_reset": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P],
     "tsa_attend_rows": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_workspace_bytes": [_I32, _P, _I32, ctypes.POINTER(ctypes.c_size_t)],
@@ -434,7 +441,73 @@ def resolve(page_table, slot_token, last_use, sel, step: int, host_k, host_v, po
     _check(load().tsa_resolve_policy(ctypes.byref(desc), _ptr(page_table), _ptr(slot_token), _ptr(last_use),
                                      _ptr(sel), k, step, EVICT_POLICIES[policy], seed & ((1 << 64) - 1),
                                      _ptr(priority), _ptr(host_k), _ptr(host_v), _ptr(pool_k), _ptr(pool_v),
-                                     _ptr(slots_out), _ptr(hits), _ptr(misses), _stream(stream)))
+                                     _ptr(slots_out), _ptr(hits), _ptr(misses), None, None, _stream(stream)))
+    return slots_out, hits, misses
+
+
+def fetch_rows(miss_tok, miss_slot, misses, host_k, host_v, pool_k, pool_v, *, stream=None):
+    """Copy the rows of a miss list from one more layer's host copy into its pool."""
+    B, N, Hkv, d = host_k.shape
+    S = pool_k.shape[1]
+    k = miss_tok.shape[1]
+    desc = cache_desc(host_k, S)
+    _i32(miss_tok, "miss_tok", (B, k))
+    _i32(miss_slot, "miss_slot", (B, k))
+    _i32(misses, "misses", (B,))
+    if host_k.is_cuda or host_v.is_cuda:
+        raise ValueError("host_k / host_v must be host-mapped memory (host_alloc)")
+    _check(load().tsa_fetch_rows(ctypes.byref(desc), _ptr(miss_tok), _ptr(miss_slot), _ptr(misses), k,
+                                 _ptr(host_k), _ptr(host_v), _ptr(pool_k), _ptr(pool_v), _stream(stream)))
+
+
+def hier_group_step(layers, page_table, slot_token, last_use, sel, step: int, *, policy: str = "lru",
+                    seed: int = 0, priority=None, slots_out=None, hits=None, misses=None, miss_tok=None,
+                    miss_slot=None, ws=None, stream=None, fetch_stream=None, events=None):
+    """One decode step of a layer group sharing `sel`. layers: list of dicts
+    with host_k, host_v (host-mapped), pool_k, pool_v, q, out (device). With
+    fetch_stream (and two events) the later layers' rows are fetched on that
+    stream while the first layer attends. Returns (slots, hits, misses)."""
+    L0 = layers[0]
+    B, N, Hkv, d = L0["host_k"].shape
+    S = L0["pool_k"].shape[1]
+    Hq = L0["q"].shape[1]
+    k = sel.shape[1]
+    desc = cache_desc(L0["host_k"], S)
+    dev = L0["pool_k"].device
+    if policy not in EVICT_POLICIES:
+        raise ValueError(f"unknown policy {policy!r}")
+    for name, t in (("slots_out", slots_out), ("miss_tok", miss_tok), ("miss_slot", miss_slot)):
+        _i32(t, name, (B, k))
+    slots_out = torch.empty((B, k), dtype=torch.int32, device=dev) if slots_out is None else slots_out
+    hits = torch.empty((B,), dtype=torch.int32, device=dev) if hits is None else hits
+    misses = torch.empty((B,), dtype=torch.int32, device=dev) if misses is None else misses
+    if len(layers) > 1:
+        miss_tok = torch.empty((B, k), dtype=torch.int32, device=dev) if miss_tok is None else miss_tok
+        miss_slot = torch.empty((B, k), dtype=torch.int32, device=dev) if miss_slot is None else miss_slot
+    arr = (LayerIO * len(layers))()
+    for j, L in enumerate(layers):
+        if L["host_k"].is_cuda or L["host_v"].is_cuda:
+            raise ValueError("host_k / host_v must be host-mapped memory (host_alloc)")
+        if tuple(L["pool_k"].shape) != (B, S, Hkv, d) or tuple(L["out"].shape) != (B, Hq, d):
+            raise ValueError(f"layer {j}: pool or out shape disagrees with layer 0")
+        arr[j] = LayerIO(_ptr(L["host_k"]), _ptr(L["host_v"]), _ptr(L["pool_k"]), _ptr(L["pool_v"]),
+                         _ptr(L["q"]), _ptr(L["out"]))
+    adesc = attn_desc(L0["pool_k"], Hq, k)
+    ws = _workspace(OP_ATTEND_ROWS, adesc, 0, ws, dev)
+    ev_arr = None
+    if fetch_stream is not None and len(layers) > 1:
+        if events is None or len(events) < 2:
+            raise ValueError("fetch_stream needs two events (fork and join)")
+        for ev in events[:2]:
+            if not ev.cuda_event:
+                ev.record()
+        ev_arr = (_P * 2)(events[0].cuda_event, events[1].cuda_event)
+    _check(load().tsa_hier_group_step(ctypes.byref(desc), Hq, len(layers), ctypes.cast(arr, _P), _ptr(page_table),
+                                      _ptr(slot_token), _ptr(last_use), _ptr(sel), k, step, EVICT_POLICIES[policy],
+                                      seed & ((1 << 64) - 1), _ptr(priority), _ptr(slots_out), _ptr(hits),
+                                      _ptr(misses), _ptr(miss_tok), _ptr(miss_slot), _ptr(ws), ws.numel(),
+                                      _stream(stream), _stream(fetch_stream) if fetch_stream is not None else None,
+                                      ctypes.cast(ev_arr, _P) if ev_arr is not None else None))
     return slots_out, hits, misses
 
 

@@ -72,6 +72,27 @@ int row_seg_rows(long long pairs, int max_rows) {
   return kRowSegRows;
 }
 
+// Fetch of a miss list for `layers` layers. Host reads have long latency and
+// clog the memory pipeline of the CUs that issue them, so the fetch is kept
+// on a few CUs: about kFetchWorkgroups large workgroups in all, which still
+// keep the host link busy, and leave the other CUs to attention running
+// beside it.
+#ifndef TSA_FETCH_WGS
+#define TSA_FETCH_WGS 64
+#endif
+constexpr long long kFetchWorkgroups = TSA_FETCH_WGS;
+FetchParams fetch_params(const tsa_cache_desc& d, const int32_t* miss_tok, const int32_t* miss_slot,
+                         const int32_t* misses, int k, int layers) {
+  FetchParams fp{};
+  fp.miss_tok = miss_tok; fp.miss_slot = miss_slot; fp.misses = misses;
+  fp.n_layers = layers;
+  const long long units = static_cast<long long>(d.batch) * std::max(layers, 1);
+  fp.split = static_cast<int>(std::min<long long>(32, std::max<long long>(1, kFetchWorkgroups / units)));
+  fp.row_bytes = static_cast<long long>(d.n_kv_heads) * d.head_dim * esize(d.dtype);
+  fp.B = d.batch; fp.N = d.n_tokens; fp.S = d.n_slots; fp.k = k;
+  return fp;
+}
+
 // ----------------------------------------------------------------- layouts
 struct IvfLayout {
   int G = 0, smax = 0;
@@ -504,7 +525,7 @@ tsa_status tsa_resolve_policy(const tsa_cache_desc* desc, int32_t* page_table, i
                               int32_t* last_use, const int32_t* sel, int32_t k, int32_t step, int32_t policy,
                               uint64_t seed, const int32_t* priority, const void* host_k, const void* host_v,
                               void* pool_k, void* pool_v, int32_t* slots_out, int32_t* hits, int32_t* misses,
-                              void* stream) {
+                              int32_t* miss_tok, int32_t* miss_slot, void* stream) {
   if (tsa_status s = check_cache(desc)) return s;
   REQUIRE_PTR(page_table); REQUIRE_PTR(slot_token); REQUIRE_PTR(last_use); REQUIRE_PTR(sel);
   REQUIRE_PTR(host_k); REQUIRE_PTR(host_v); REQUIRE_PTR(pool_k); REQUIRE_PTR(pool_v); REQUIRE_PTR(slots_out);
@@ -516,10 +537,12 @@ tsa_status tsa_resolve_policy(const tsa_cache_desc* desc, int32_t* page_table, i
   if (policy < TSA_EVICT_LRU || policy > TSA_EVICT_PRIORITY)
     return fail(TSA_ERR_INVALID_ARG, "unknown replacement policy %d", policy);
   if (policy == TSA_EVICT_PRIORITY) REQUIRE_PTR(priority);
+  if ((miss_tok == nullptr) != (miss_slot == nullptr))
+    return fail(TSA_ERR_INVALID_ARG, "miss_tok and miss_slot must both be given or both be NULL");
   ResolveParams rp{page_table, slot_token, last_use, sel, host_k, host_v, pool_k, pool_v, slots_out, hits,
                    misses, static_cast<long long>(d.n_kv_heads) * d.head_dim * esize(d.dtype),
                    d.batch, d.n_tokens, d.n_slots, k, step, policy, static_cast<unsigned long long>(seed),
-                   priority};
+                   priority, miss_tok, miss_slot};
   hipError_t e = launch_resolve(rp, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "resolve launch");
   return ok();
@@ -530,7 +553,91 @@ tsa_status tsa_resolve(const tsa_cache_desc* desc, int32_t* page_table, int32_t*
                        const void* host_k, const void* host_v, void* pool_k, void* pool_v,
                        int32_t* slots_out, int32_t* hits, int32_t* misses, void* stream) {
   return tsa_resolve_policy(desc, page_table, slot_token, last_use, sel, k, step, TSA_EVICT_LRU, 0, nullptr,
-                            host_k, host_v, pool_k, pool_v, slots_out, hits, misses, stream);
+                            host_k, host_v, pool_k, pool_v, slots_out, hits, misses, nullptr, nullptr, stream);
+}
+
+tsa_status tsa_fetch_rows(const tsa_cache_desc* desc, const int32_t* miss_tok, const int32_t* miss_slot,
+                          const int32_t* misses, int32_t k, const void* host_k, const void* host_v, void* pool_k,
+                          void* pool_v, void* stream) {
+  if (tsa_status s = check_cache(desc)) return s;
+  REQUIRE_PTR(miss_tok); REQUIRE_PTR(miss_slot); REQUIRE_PTR(misses);
+  REQUIRE_PTR(host_k); REQUIRE_PTR(host_v); REQUIRE_PTR(pool_k); REQUIRE_PTR(pool_v);
+  REQUIRE_ALIGN(host_k, 16); REQUIRE_ALIGN(host_v, 16); REQUIRE_ALIGN(pool_k, 16); REQUIRE_ALIGN(pool_v, 16);
+  const tsa_cache_desc& d = *desc;
+  if (k < 1 || k > d.n_slots || k > kMaxTokenK)
+    return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, min(S=%d, %d)]", k, d.n_slots, kMaxTokenK);
+  FetchParams fp = fetch_params(d, miss_tok, miss_slot, misses, k, 1);
+  fp.host_k[0] = host_k; fp.host_v[0] = host_v; fp.pool_k[0] = pool_k; fp.pool_v[0] = pool_v;
+  hipError_t e = launch_fetch_rows(fp, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "fetch_rows launch");
+  return ok();
+}
+
+tsa_status tsa_hier_group_step(const tsa_cache_desc* desc, int32_t n_q_heads, int32_t n_layers,
+                               const tsa_layer_io* layers, int32_t* page_table, int32_t* slot_token,
+                               int32_t* last_use, const int32_t* sel, int32_t k, int32_t step, int32_t policy,
+                               uint64_t seed, const int32_t* priority, int32_t* slots_out, int32_t* hits,
+                               int32_t* misses, int32_t* miss_tok, int32_t* miss_slot, void* ws, size_t ws_bytes,
+                               void* stream, void* fetch_stream, void* const* events) {
+  if (tsa_status s = check_cache(desc)) return s;
+  REQUIRE_PTR(layers); REQUIRE_PTR(slots_out);
+  if (n_layers < 1 || n_layers > kMaxFetchLayers + 1)
+    return fail(TSA_ERR_INVALID_ARG, "n_layers=%d outside [1, %d]", n_layers, kMaxFetchLayers + 1);
+  const tsa_cache_desc& d = *desc;
+  const tsa_attn_desc ad{d.batch, d.n_slots, d.n_kv_heads, n_q_heads, d.head_dim, k, d.dtype};
+  if (tsa_status s = check_attn(&ad)) return s;
+  if (n_layers > 1) {
+    REQUIRE_PTR(misses); REQUIRE_PTR(miss_tok); REQUIRE_PTR(miss_slot);
+    if (fetch_stream) {
+      REQUIRE_PTR(events);
+      if (!events[0] || !events[1]) return fail(TSA_ERR_INVALID_ARG, "events[0] and events[1] must be given");
+    }
+  }
+  for (int j = 0; j < n_layers; ++j) {
+    const tsa_layer_io& L = layers[j];
+    if (!L.host_k || !L.host_v || !L.pool_k || !L.pool_v || !L.q || !L.out)
+      return fail(TSA_ERR_INVALID_ARG, "layers[%d] has a NULL pointer", j);
+    if (!aligned(L.host_k, 16) || !aligned(L.host_v, 16) || !aligned(L.pool_k, 16) || !aligned(L.pool_v, 16) ||
+        !aligned(L.q, 16) || !aligned(L.out, 8))
+      return fail(TSA_ERR_INVALID_ARG, "layers[%d] has a misaligned pointer", j);
+  }
+  const size_t need = rows_layout(ad).total;
+  if (ws_bytes < need) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = as_stream(stream);
+  hipStream_t fs = fetch_stream ? as_stream(fetch_stream) : nullptr;
+
+  // RESOLVE once for the group: tables, miss list and the first layer's rows
+  if (tsa_status st = tsa_resolve_policy(desc, page_table, slot_token, last_use, sel, k, step, policy, seed,
+                                         priority, layers[0].host_k, layers[0].host_v, layers[0].pool_k,
+                                         layers[0].pool_v, slots_out, hits, misses,
+                                         n_layers > 1 ? miss_tok : nullptr, n_layers > 1 ? miss_slot : nullptr,
+                                         stream))
+    return st;
+  // the other layers' rows: one launch for the whole group
+  FetchParams fp = fetch_params(d, miss_tok, miss_slot, misses, k, n_layers - 1);
+  for (int j = 1; j < n_layers; ++j) {
+    fp.host_k[j - 1] = layers[j].host_k; fp.host_v[j - 1] = layers[j].host_v;
+    fp.pool_k[j - 1] = layers[j].pool_k; fp.pool_v[j - 1] = layers[j].pool_v;
+  }
+  hipError_t e = hipSuccess;
+  if (n_layers > 1 && fs) {
+    // prefetch: the rows stream in on the second stream while layer 0 attends
+    e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(fs, static_cast<hipEvent_t>(events[0]), 0);
+    if (e == hipSuccess) e = launch_fetch_rows(fp, fs);
+    if (e == hipSuccess) e = hipEventRecord(static_cast<hipEvent_t>(events[1]), fs);
+    if (e != hipSuccess) return hip_fail(e, "layer prefetch");
+  }
+  for (int j = 0; j < n_layers; ++j) {
+    if (j == 1) {
+      e = fs ? hipStreamWaitEvent(s, static_cast<hipEvent_t>(events[1]), 0) : launch_fetch_rows(fp, s);
+      if (e != hipSuccess) return hip_fail(e, "layer fetch");
+    }
+    if (tsa_status st = tsa_attend_rows(&ad, layers[j].q, layers[j].pool_k, layers[j].pool_v, slots_out, nullptr,
+                                        layers[j].out, ws, ws_bytes, stream))
+      return st;
+  }
+  return ok();
 }
 
 tsa_status tsa_cache_reset(const tsa_cache_desc* desc, int32_t* page_table, int32_t* slot_token,

@@ -148,8 +148,28 @@ struct ResolveParams {
   int policy;              // kEvictLru / kEvictFifo / kEvictRandom / kEvictPriority
   unsigned long long seed; // random policy
   const int32_t* priority; // [B][N] priority policy: evict the largest value first
+  int32_t* miss_tok;       // [B][k] or null: missed tokens in miss order
+  int32_t* miss_slot;      // [B][k] or null: the slot each took
 };
 hipError_t launch_resolve(const ResolveParams& p, hipStream_t s);
+
+// Copies the rows of a miss list (from a RESOLVE of the same selection) from
+// the host copies of up to kMaxFetchLayers layers into their pools.
+constexpr int kMaxFetchLayers = 16;
+struct FetchParams {
+  const int32_t* miss_tok;   // [B][k]
+  const int32_t* miss_slot;  // [B][k]
+  const int32_t* misses;     // [B]
+  const void* host_k[kMaxFetchLayers];  // per layer [B][N][Hkv][d] host-mapped
+  const void* host_v[kMaxFetchLayers];
+  void* pool_k[kMaxFetchLayers];        // per layer [B][S][Hkv][d]
+  void* pool_v[kMaxFetchLayers];
+  int n_layers;
+  int split;                 // workgroups per (request, layer)
+  long long row_bytes;
+  int B, N, S, k;
+};
+hipError_t launch_fetch_rows(const FetchParams& p, hipStream_t s);
 
 constexpr int kEvictLru = 0, kEvictFifo = 1, kEvictRandom = 2, kEvictPriority = 3;
 

@@ -50,6 +50,45 @@ __device__ __forceinline__ uint32_t random_key(unsigned long long seed, int b, i
   return static_cast<uint32_t>(x >> 33);
 }
 
+// Fetch of one request's missed tokens: one wave per token (waves w0,
+// w0 + wstride, ...); lanes stride over its 16-B chunks, K and V rows loaded
+// together so each lane keeps four 16-B host reads in flight.
+__device__ __forceinline__ void fetch_missed(const int32_t* mtok, const int32_t* mslot, int n_miss, int b, int N,
+                                             int S, long long row_bytes, const void* host_k, const void* host_v,
+                                             void* pool_k, void* pool_v, int w0, int wstride) {
+  const int chunks = static_cast<int>(row_bytes / 16);
+  const int lane = lane_id();
+  const char* hk = static_cast<const char*>(host_k);
+  const char* hv = static_cast<const char*>(host_v);
+  char* pk = static_cast<char*>(pool_k);
+  char* pv = static_cast<char*>(pool_v);
+  for (int r = w0; r < n_miss; r += wstride) {
+    const int tk = mtok[r], sl = mslot[r];
+    if (tk < 0 || tk >= N || sl < 0 || sl >= S) continue;  // never addresses outside the arrays
+    const long long src = (static_cast<long long>(b) * N + tk) * row_bytes;
+    const long long dst = (static_cast<long long>(b) * S + sl) * row_bytes;
+    const uint4* sk4 = reinterpret_cast<const uint4*>(hk + src);
+    const uint4* sv4 = reinterpret_cast<const uint4*>(hv + src);
+    uint4* dk4 = reinterpret_cast<uint4*>(pk + dst);
+    uint4* dv4 = reinterpret_cast<uint4*>(pv + dst);
+    for (int c = lane; c < chunks; c += 2 * kWave) {
+      const bool two = c + kWave < chunks;
+      const uint4 k0 = sk4[c], v0 = sv4[c];
+      uint4 k1 = k0, v1 = v0;
+      if (two) {
+        k1 = sk4[c + kWave];
+        v1 = sv4[c + kWave];
+      }
+      dk4[c] = k0;
+      dv4[c] = v0;
+      if (two) {
+        dk4[c + kWave] = k1;
+        dv4[c + kWave] = v1;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams p, int spow2) {
   constexpr int NW = kResolveThreads / kWave;
   extern __shared__ unsigned long long lds[];
@@ -159,37 +198,34 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   }
   __syncthreads();
 
-  // Fetch: one wave per missed token; lanes stride over its 16-B chunks, K and
-  // V rows loaded together so each lane keeps four 16-B host reads in flight.
-  const int chunks = static_cast<int>(p.row_bytes / 16);
-  const int lane = lane_id(), wave = tid / kWave;
-  const char* hk = static_cast<const char*>(p.host_k);
-  const char* hv = static_cast<const char*>(p.host_v);
-  char* pk = static_cast<char*>(p.pool_k);
-  char* pv = static_cast<char*>(p.pool_v);
-  for (int r = wave; r < n_miss; r += NW) {
-    const long long src = (static_cast<long long>(b) * p.N + miss_tok[r]) * p.row_bytes;
-    const long long dst = (static_cast<long long>(b) * p.S + miss_slot[r]) * p.row_bytes;
-    const uint4* sk4 = reinterpret_cast<const uint4*>(hk + src);
-    const uint4* sv4 = reinterpret_cast<const uint4*>(hv + src);
-    uint4* dk4 = reinterpret_cast<uint4*>(pk + dst);
-    uint4* dv4 = reinterpret_cast<uint4*>(pv + dst);
-    for (int c = lane; c < chunks; c += 2 * kWave) {
-      const bool two = c + kWave < chunks;
-      const uint4 k0 = sk4[c], v0 = sv4[c];
-      uint4 k1 = k0, v1 = v0;
-      if (two) {
-        k1 = sk4[c + kWave];
-        v1 = sv4[c + kWave];
-      }
-      dk4[c] = k0;
-      dv4[c] = v0;
-      if (two) {
-        dk4[c + kWave] = k1;
-        dv4[c + kWave] = v1;
-      }
+  if (p.miss_tok) {  // the miss list, for the other layers of a layer group
+    for (int r = tid; r < n_miss; r += kResolveThreads) {
+      p.miss_tok[static_cast<long long>(b) * p.k + r] = miss_tok[r];
+      p.miss_slot[static_cast<long long>(b) * p.k + r] = miss_slot[r];
     }
   }
+  fetch_missed(miss_tok, miss_slot, n_miss, b, p.N, p.S, p.row_bytes, p.host_k, p.host_v, p.pool_k, p.pool_v,
+               tid / kWave, kResolveThreads / kWave);
+}
+
+// grid (B, layers, split): workgroup z of (request, layer) takes every
+// split-th wave's share of the request's misses
+#ifndef TSA_FETCH_THREADS
+#define TSA_FETCH_THREADS 1024
+#endif
+constexpr int kFetchThreads = TSA_FETCH_THREADS;
+__global__ __launch_bounds__(kFetchThreads) void fetch_rows_kernel(FetchParams p) {
+  constexpr int NW = kFetchThreads / kWave;
+  const int b = blockIdx.x, layer = blockIdx.y, z = blockIdx.z;
+  const int n = min(max(p.misses[b], 0), p.k);
+  fetch_missed(p.miss_tok + static_cast<long long>(b) * p.k, p.miss_slot + static_cast<long long>(b) * p.k, n, b,
+               p.N, p.S, p.row_bytes, p.host_k[layer], p.host_v[layer], p.pool_k[layer], p.pool_v[layer],
+               z * NW + static_cast<int>(threadIdx.x) / kWave, p.split * NW);
+}
+
+hipError_t launch_fetch_rows(const FetchParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(fetch_rows_kernel, dim3(p.B, p.n_layers, p.split), dim3(kFetchThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_resolve(const ResolveParams& p, hipStream_t s) {
