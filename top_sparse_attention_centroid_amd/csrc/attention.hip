@@ -20,6 +20,7 @@
 namespace tsa {
 
 constexpr int kGatherWaves = kGatherWavesPerBlock;  // each wave owns whole segments
+constexpr int kSegsPerWave = kGatherSegsPerWave;    // segments a wave is planned to take
 #ifndef TSA_GATHER_UNROLL
 #define TSA_GATHER_UNROLL 8
 #endif
@@ -28,6 +29,12 @@ constexpr int kGatherWaves = kGatherWavesPerBlock;  // each wave owns whole segm
 #endif
 #ifndef TSA_GATHER_PIPE
 #define TSA_GATHER_PIPE 0  // 1: double-buffer batches in registers
+#endif
+#ifndef TSA_GATHER_TAIL
+#define TSA_GATHER_TAIL 0  // 1: a half-size batch for the last rows of a segment
+#endif
+#ifndef TSA_GATHER_FULLMASK_ALL
+#define TSA_GATHER_FULLMASK_ALL 1  // explicit segments read by every head: one all-heads pass
 #endif
 #ifndef TSA_GATHER_WAVES_PER_EU
 #define TSA_GATHER_WAVES_PER_EU 0
@@ -70,22 +77,22 @@ __device__ __forceinline__ void merge_into(HeadState& a, float m2, float l2, con
 
 // K and V rows of one batch: lane group r = lane / 16 takes rows r, r+4, ...
 // of the batch; raw bits stay in registers until scored.
-template <typename T>
+template <typename T, int U = kGatherUnroll>
 struct Batch {
-  Raw8<T> k[kGatherUnroll], v[kGatherUnroll];
-  bool valid[kGatherUnroll];
+  Raw8<T> k[U], v[U];
+  bool valid[U];
 };
 
 // Straight-line issue: every lane loads, rows past the segment end or with a
 // rejected id load row 0 of the request (always in bounds) and are masked at
 // scoring. Without control flow around the loads the compiler keeps all of
 // them in flight (a predicated load would force a wait for every earlier one).
-template <bool STREAM, typename T>
-__device__ __forceinline__ void issue_batch(Batch<T>& bt, const int* ids, int base, int cnt, int r,
+template <bool STREAM, typename T, int U>
+__device__ __forceinline__ void issue_batch(Batch<T, U>& bt, const int* ids, int base, int cnt, int r,
                                             const T* kb, const T* vb, long long row_stride) {
-  int row[kGatherUnroll];
+  int row[U];
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int j = base + u * 4 + r;
     const int id = ids[min(j, kSegRows - 1)];
     bt.valid[u] = (j < cnt) & (id >= 0);
@@ -93,36 +100,36 @@ __device__ __forceinline__ void issue_batch(Batch<T>& bt, const int* ids, int ba
   }
   if constexpr (STREAM) {
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) bt.k[u].load_stream(kb + row[u] * row_stride);
+    for (int u = 0; u < U; ++u) bt.k[u].load_stream(kb + row[u] * row_stride);
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) bt.v[u].load_stream(vb + row[u] * row_stride);
+    for (int u = 0; u < U; ++u) bt.v[u].load_stream(vb + row[u] * row_stride);
   } else {
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) bt.k[u].load(kb + row[u] * row_stride);
+    for (int u = 0; u < U; ++u) bt.k[u].load(kb + row[u] * row_stride);
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) bt.v[u].load(vb + row[u] * row_stride);
+    for (int u = 0; u < U; ++u) bt.v[u].load(vb + row[u] * row_stride);
   }
 }
 
 // Scores the batch's rows for one head, then folds them into the state with
 // one max update per batch (one rescale of o instead of one per row).
-template <typename T>
-__device__ __forceinline__ void consume_batch(const Batch<T>& bt, HeadState& st, const QFrag<T>& qf,
+template <typename T, int U>
+__device__ __forceinline__ void consume_batch(const Batch<T, U>& bt, HeadState& st, const QFrag<T>& qf,
                                               float qscale) {
-  float sc[kGatherUnroll];
+  float sc[U];
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u)
+  for (int u = 0; u < U; ++u)
     sc[u] = bt.valid[u] ? group16_sum(qf.dot(bt.k[u])) * qscale : kMaskedScore;
   float mb = sc[0];
 #pragma unroll
-  for (int u = 1; u < kGatherUnroll; ++u) mb = fmaxf(mb, sc[u]);
+  for (int u = 1; u < U; ++u) mb = fmaxf(mb, sc[u]);
   const float mn = fmaxf(st.m, mb);
   const float a = fast_exp2(st.m - mn);
   st.l *= a;
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.o[i] *= a;
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     float vx[8];
     bt.v[u].widen(vx);
     const float pw = fast_exp2(sc[u] - mn);
@@ -164,6 +171,19 @@ __device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int c
       consume_batch(A, st, qf, qscale);
       issue_batch<STREAM>(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride);
       consume_batch(Bb, st, qf, qscale);
+    }
+#elif TSA_GATHER_TAIL
+    // full batches while more than half a batch remains, then one half batch
+    int base = 0;
+    for (; base + kBatchRows / 2 < cnt; base += kBatchRows) {
+      Batch<T> A;
+      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride);
+      consume_batch(A, st, qf, qscale);
+    }
+    if (base < cnt) {
+      Batch<T, kGatherUnroll / 2> A;
+      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride);
+      consume_batch(A, st, qf, qscale);
     }
 #else
     for (int base = 0; base < cnt; base += kBatchRows) {
@@ -278,27 +298,39 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
   const int bg = blockIdx.x / p.W, w0 = blockIdx.x % p.W;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
 
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int r = lane >> 4, e = lane & 15;
+  const int s_first = w0 * NW + wave;
+  const int stride = p.W * NW;
+
+  // A wave takes segments s_first, s_first + stride, ... (about kSegsPerWave
+  // of them). Everything its first rows depend on is requested together:
+  // the segment count, the group's queries (block-wide, staged to LDS) and
+  // the descriptors of all its segments; then the first segment's row ids.
+  // While a segment's rows stream, the next segment's row ids are already
+  // in flight into registers, so only the first segment waits for them.
   int nseg, total_rows = 0;
+  int4 dq[kSegsPerWave];
   if constexpr (EXPLICIT) {
     nseg = p.nseg[bg];
+#pragma unroll
+    for (int i = 0; i < kSegsPerWave; ++i)
+      dq[i] = p.seg[static_cast<long long>(bg) * p.smax + min(s_first + i * stride, p.smax - 1)];
   } else {
     // clamp a device-side count to the planned capacity (never trusted)
     total_rows = min(max(p.counts ? p.counts[b] : p.count_const, 0), p.count_max);
     nseg = (total_rows + p.seg_rows - 1) / p.seg_rows;
+#pragma unroll
+    for (int i = 0; i < kSegsPerWave; ++i) dq[i] = make_int4(0, 0, 0, 0);
   }
-  if (w0 * NW >= nseg) return;
-
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int r = lane >> 4, e = lane & 15;
-  {
-    const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
-    for (int i = tid; i < G * kHeadDim / 8; i += NW * kWave) {
-      Raw8<T> x;
-      x.load(qb + i * 8);
-      *reinterpret_cast<Raw8<T>*>(qs + i * 8) = x;
-    }
-  }
-  __syncthreads();
+  constexpr int kQParts = G * kHeadDim / 8;  // 16-B (bf16) or 32-B (fp32) pieces of the group's queries
+  constexpr int kQPer = (kQParts + NW * kWave - 1) / (NW * kWave);
+  Raw8<T> qpart[kQPer];
+  const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i)
+    if (tid + i * NW * kWave < kQParts) qpart[i].load(qb + (tid + i * NW * kWave) * 8);
+  if (w0 * NW >= nseg) return;  // uniform over the block
 
   const long long row_stride = static_cast<long long>(p.Hkv) * kHeadDim;
   const T* kb = static_cast<const T*>(p.k) + static_cast<long long>(b) * p.n_rows * row_stride +
@@ -319,27 +351,74 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
     }
   }
 
-  for (int s = w0 * NW + wave; s < nseg; s += p.W * NW) {
+  // segment s: rows [start, start + cnt) of the list or token range, its head mask
+  struct Seg {
     int start, cnt;
     uint32_t mask;
-    bool direct = false;  // a token range [start, start + cnt) instead of list entries
+    bool direct;  // a token range [start, start + cnt) instead of list entries
+  };
+  auto seg_of = [&](int s, int4 d) {
+    Seg sg;
     if constexpr (EXPLICIT) {
-      const int4 d = p.seg[static_cast<long long>(bg) * p.smax + s];
-      start = d.x;
-      cnt = d.y;
-      mask = static_cast<uint32_t>(d.z);
-      direct = d.w < 0;
+      sg.start = d.x;
+      sg.cnt = min(max(d.y, 0), kSegRows);
+      sg.mask = static_cast<uint32_t>(d.z);
+      sg.direct = d.w < 0;
     } else {
-      start = s * p.seg_rows;
-      cnt = min(p.seg_rows, total_rows - start);
-      mask = (1u << G) - 1u;
+      sg.start = s * p.seg_rows;
+      sg.cnt = min(p.seg_rows, total_rows - sg.start);
+      sg.mask = (1u << G) - 1u;
+      sg.direct = false;
     }
-    for (int j = lane; j < cnt; j += kWave) {
-      const int id = direct ? start + j : rid[start + j];
+    return sg;
+  };
+  constexpr int kIdsPerLane = kSegRows / kWave;
+  // a segment's row ids into registers: straight-line loads at clamped
+  // positions (cnt >= 1 for every planned segment), filtered when stored
+  auto load_ids = [&](const Seg& sg, int (&dst)[kIdsPerLane]) {
+#pragma unroll
+    for (int i = 0; i < kIdsPerLane; ++i) {
+      const int j = min(lane + i * kWave, max(sg.cnt - 1, 0));
+      dst[i] = sg.direct ? sg.start + j : rid[sg.start + j];
+    }
+  };
+  auto store_ids = [&](const Seg& sg, const int (&src)[kIdsPerLane]) {
+#pragma unroll
+    for (int i = 0; i < kIdsPerLane; ++i) {
+      const int j = lane + i * kWave;
+      const int id = src[i];
       // ids outside [0, n_rows) are skipped, never dereferenced
       bool ok = static_cast<unsigned long long>(id) < static_cast<unsigned long long>(p.n_rows);
-      if (!direct) ok = ok && !(id < fx_sink || (id >= fx_lo && id < fx_hi));
-      ids[j] = ok ? id : -1;
+      if (!sg.direct) ok = ok && !(id < fx_sink || (id >= fx_lo && id < fx_hi));
+      if (j < sg.cnt) ids[j] = ok ? id : -1;
+    }
+  };
+
+  Seg cur = seg_of(s_first, dq[0]);
+  int cid[kIdsPerLane];
+  if (s_first < nseg && cur.cnt > 0) load_ids(cur, cid);
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i)
+    if (tid + i * NW * kWave < kQParts) *reinterpret_cast<Raw8<T>*>(qs + (tid + i * NW * kWave) * 8) = qpart[i];
+  if (s_first < nseg && cur.cnt > 0) store_ids(cur, cid);
+  __syncthreads();
+
+  for (int it = 0, s = s_first; s < nseg; ++it, s += stride) {
+    const int cnt = cur.cnt;
+    const uint32_t mask = cur.mask;
+    // the next segment's row ids fly while this one's rows stream
+    const int sn = s + stride;
+    Seg nxt;
+    int nid[kIdsPerLane];
+    const bool has_next = sn < nseg;
+    if (has_next) {
+      int4 dn = make_int4(0, 0, 0, 0);
+      if constexpr (EXPLICIT) {
+        dn = it + 1 < kSegsPerWave ? dq[(it + 1) % kSegsPerWave]
+                                   : p.seg[static_cast<long long>(bg) * p.smax + sn];
+      }
+      nxt = seg_of(sn, dn);
+      if (nxt.cnt > 0) load_ids(nxt, nid);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -348,7 +427,7 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
     float* part = p.partial + (static_cast<long long>(bg) * p.smax + s) * G * kPartStride;
     // A row read by a single head's pass streams past the caches; rows that a
     // second head will re-read stay cacheable so that pass hits L2.
-    if (!EXPLICIT || (G > 1 && mask == (1u << G) - 1u)) {
+    if (!EXPLICIT || (TSA_GATHER_FULLMASK_ALL && G > 1 && mask == (1u << G) - 1u)) {
       // every head of the group reads these rows: score them for all heads at once
       all_heads_pass<G>(ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
     } else if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u) {
@@ -358,6 +437,10 @@ __global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_at
     }
     // the next segment overwrites this wave's id staging area
     __builtin_amdgcn_wave_barrier();
+    if (has_next) {
+      cur = nxt;
+      if (cur.cnt > 0) store_ids(cur, nid);
+    }
   }
 }
 

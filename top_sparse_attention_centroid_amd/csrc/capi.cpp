@@ -58,7 +58,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 // Workgroups per (request, KV head) for gather_attn: one wave per expected
 // segment; short-lived workgroups let the dispatcher balance uneven segments.
 int gather_blocks_per_head(int expected_segments) {
-  return std::max(1, ceil_div(expected_segments, kGatherWavesPerBlock));
+  return std::max(1, ceil_div(expected_segments, kGatherWavesPerBlock * kGatherSegsPerWave));
 }
 
 // Rows per attention segment for per-request row lists: the longest of
@@ -311,14 +311,17 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
   gp.counts = nullptr; gp.count_const = 0;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  // expected segments: one per chosen list of the group (most lists fit one
-  // segment) plus the sink / window segments
+  // expected segments: per chosen list of the group, its average length
+  // N / C in 256-row segments (rounded up, with room for a ragged tail), plus
+  // the sink / window segments
+  const int per_list = std::max(1, static_cast<int>((2LL * d.n_tokens / d.n_centroids + kSegRows) / (2 * kSegRows)) +
+                                       (d.n_tokens / d.n_centroids > kSegRows / 2 ? 1 : 0));
   int fixed_segs = 0;
   if (opts) {
     fixed_segs = ceil_div(std::min(opts->n_sink, d.n_tokens), kSegRows) +
                  ceil_div(std::min(opts->n_window, d.n_tokens), kSegRows) + (opts->n_window > 0 ? 1 : 0);
   }
-  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k + fixed_segs)); gp.seg_rows = kSegRows;
+  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k * per_list + fixed_segs)); gp.seg_rows = kSegRows;
   gp.qscale = qscale(d.head_dim);
   if (opts) {
     gp.n_sink = opts->n_sink;

@@ -12,7 +12,14 @@ namespace tsa {
 constexpr int kHeadDimRows = 128;   // d: elements per row (head_dim)
 constexpr int kSegRows = 256;       // max rows per attention segment (one wave's work unit)
 constexpr int kRowSegRows = 64;       // shortest segment for per-request row lists (token / slot paths)
-constexpr int kGatherWavesPerBlock = 4;
+#ifndef TSA_GATHER_WPB
+#define TSA_GATHER_WPB 1
+#endif
+constexpr int kGatherWavesPerBlock = TSA_GATHER_WPB;  // waves (segments in flight) per gather workgroup
+#ifndef TSA_GATHER_SPW
+#define TSA_GATHER_SPW 1
+#endif
+constexpr int kGatherSegsPerWave = TSA_GATHER_SPW;  // segments each gather wave is planned to take
 constexpr int kPartStride = 132;    // floats per partial state: m, l, 2 pad, o[128]
 #ifndef TSA_SCORE_TILE
 #define TSA_SCORE_TILE 2048
@@ -109,7 +116,7 @@ struct GatherParams {
   int n_sink, n_window;    // explicit plans: list rows inside these ranges are skipped
   const int32_t* lengths;  // [B] or null (n_rows)
   float* out;              // [B][Hq][d]
-  int B, Hkv, smax, W;     // W: workgroups per (request, KV head), 4 segments each in flight
+  int B, Hkv, smax, W;     // W: workgroups per (request, KV head)
   float qscale;            // log2(e) / sqrt(d)
 };
 hipError_t launch_gather(const GatherParams& p, int dtype, int G, bool explicit_plan,
