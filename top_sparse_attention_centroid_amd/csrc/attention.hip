@@ -19,7 +19,11 @@
 
 namespace tsa {
 
-constexpr int kGatherWaves = kGatherWavesPerBlock;  // each wave owns whole segments
+// waves per workgroup: explicit plans (uneven segments) run one wave per
+// workgroup so a finished segment frees its slot at once; row lists (equal
+// segments) run several
+template <bool EXPLICIT>
+constexpr int gather_waves() { return EXPLICIT ? kGatherWavesExplicit : kGatherWavesRows; }
 constexpr int kSegsPerWave = kGatherSegsPerWave;    // segments a wave is planned to take
 #ifndef TSA_GATHER_UNROLL
 #define TSA_GATHER_UNROLL 8
@@ -291,8 +295,8 @@ __device__ __forceinline__ void all_heads_pass(const int* ids, int cnt, int r, i
 }
 
 template <typename T, int G, bool EXPLICIT>
-__global__ __launch_bounds__(kGatherWaves * kWave) TSA_GATHER_OCC void gather_attn_kernel(GatherParams p) {
-  constexpr int NW = kGatherWaves;
+__global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC void gather_attn_kernel(GatherParams p) {
+  constexpr int NW = gather_waves<EXPLICIT>();
   __shared__ __align__(16) T qs[G * kHeadDim];
   __shared__ int ids_lds[NW][kSegRows];
   const int bg = blockIdx.x / p.W, w0 = blockIdx.x % p.W;
@@ -520,7 +524,7 @@ __global__ __launch_bounds__(512) void combine_kernel(GatherParams p) {
 
 template <typename T, bool EXPLICIT>
 static void gather_dispatch(const GatherParams& p, int G, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(p.B * p.Hkv * p.W)), block(kGatherWaves * kWave);
+  const dim3 grid(static_cast<unsigned>(p.B * p.Hkv * p.W)), block(gather_waves<EXPLICIT>() * kWave);
   switch (G) {
     case 1: hipLaunchKernelGGL((gather_attn_kernel<T, 1, EXPLICIT>), grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL((gather_attn_kernel<T, 2, EXPLICIT>), grid, block, 0, s, p); break;

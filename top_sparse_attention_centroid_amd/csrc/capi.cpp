@@ -57,15 +57,19 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // Workgroups per (request, KV head) for gather_attn: one wave per expected
 // segment; short-lived workgroups let the dispatcher balance uneven segments.
-int gather_blocks_per_head(int expected_segments) {
-  return std::max(1, ceil_div(expected_segments, kGatherWavesPerBlock * kGatherSegsPerWave));
+int gather_blocks_per_head(int expected_segments, bool explicit_plan) {
+  const int waves = explicit_plan ? kGatherWavesExplicit : kGatherWavesRows;
+  return std::max(1, ceil_div(expected_segments, waves * kGatherSegsPerWave));
 }
 
 // Rows per attention segment for per-request row lists: the longest of
 // 256 / 128 / 64 rows that still gives at least 2048 segments (8 waves per
 // CU). Longer segments write fewer partial softmax states; shorter ones keep
 // every CU busy when the batch is small.
-constexpr long long kMinRowSegments = 2048;
+#ifndef TSA_MIN_ROW_SEGS
+#define TSA_MIN_ROW_SEGS 2048
+#endif
+constexpr long long kMinRowSegments = TSA_MIN_ROW_SEGS;
 int row_seg_rows(long long pairs, int max_rows) {
   for (int r = kSegRows; r > kRowSegRows; r >>= 1)
     if (pairs * ceil_div(max_rows, r) >= kMinRowSegments) return r;
@@ -321,7 +325,7 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
     fixed_segs = ceil_div(std::min(opts->n_sink, d.n_tokens), kSegRows) +
                  ceil_div(std::min(opts->n_window, d.n_tokens), kSegRows) + (opts->n_window > 0 ? 1 : 0);
   }
-  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k * per_list + fixed_segs)); gp.seg_rows = kSegRows;
+  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k * per_list + fixed_segs), true); gp.seg_rows = kSegRows;
   gp.qscale = qscale(d.head_dim);
   if (opts) {
     gp.n_sink = opts->n_sink;
@@ -493,7 +497,7 @@ tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const
   gp.seg = nullptr; gp.nseg = nullptr; gp.counts = nullptr; gp.count_const = k; gp.count_max = k;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  gp.W = gather_blocks_per_head(L.smax); gp.seg_rows = L.seg_rows;
+  gp.W = gather_blocks_per_head(L.smax, false); gp.seg_rows = L.seg_rows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
   return ok();
@@ -518,7 +522,7 @@ tsa_status tsa_attend_rows(const tsa_attn_desc* desc, const void* q, const void*
   gp.count_max = d.max_rows;
   gp.partial = static_cast<float*>(ws); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  gp.W = gather_blocks_per_head(L.smax); gp.seg_rows = L.seg_rows;
+  gp.W = gather_blocks_per_head(L.smax, false); gp.seg_rows = L.seg_rows;
   gp.qscale = qscale(d.head_dim);
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, false, s)) return st;
   return ok();

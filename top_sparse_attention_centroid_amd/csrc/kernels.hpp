@@ -15,7 +15,11 @@ constexpr int kRowSegRows = 64;       // shortest segment for per-request row li
 #ifndef TSA_GATHER_WPB
 #define TSA_GATHER_WPB 1
 #endif
-constexpr int kGatherWavesPerBlock = TSA_GATHER_WPB;  // waves (segments in flight) per gather workgroup
+#ifndef TSA_GATHER_WPB_ROWS
+#define TSA_GATHER_WPB_ROWS 4
+#endif
+constexpr int kGatherWavesExplicit = TSA_GATHER_WPB;    // gather waves per workgroup, IVF plans
+constexpr int kGatherWavesRows = TSA_GATHER_WPB_ROWS;   // ... per-request row lists
 #ifndef TSA_GATHER_SPW
 #define TSA_GATHER_SPW 1
 #endif
