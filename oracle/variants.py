@@ -1,5 +1,6 @@
-"""Oracle for the inverted-index decode variants: cosine similarity and a
-fixed sink/window set attended beside the retrieved lists.
+"""Oracle for the inverted-index decode variants: cosine similarity, a
+fixed sink/window set attended beside the retrieved lists, and lists built
+with several assignments per key.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring): plain fp64 numpy.
 
@@ -11,11 +12,16 @@ Sources, by page and section:
     - Method details, last item: the general-purpose cores also run
       window-based sparse attention (StreamingLLM) beside cluster- and
       retrieval-based schemes.
+    - How, index structure: a KV entry is placed into several posting lists
+      according to its key.
 
 Readings (each also listed in the design notes):
   * Cosine: s_c = q.c / |c|. The factor 1/|q| is the same for every centroid
     of one query and is left out (it changes no ranking). A zero centroid
     scores 0.
+  * Multi-assignment: each key joins its m nearest lists (squared L2, ties
+    to the lower index; m = 1 is the plain index). A token in several chosen
+    lists is attended once: the retrieved set is the union of the lists.
   * Sink/window (StreamingLLM's pattern of the first tokens plus the most
     recent ones): the first n_sink tokens and the last n_window tokens before
     the request's current length L are attended in every step, in addition
@@ -29,7 +35,8 @@ import numpy as np
 
 from .ivf import attend, retrieved_rows, selection_gap, top_k
 
-__all__ = ["cosine_scores", "fixed_rows", "decode_head_ex", "sparse_decode_ex"]
+__all__ = ["cosine_scores", "fixed_rows", "decode_head_ex", "sparse_decode_ex", "nearest_centroids",
+           "posting_lists_multi", "index_build_multi"]
 
 
 def _f64(x):
@@ -96,3 +103,66 @@ def sparse_decode_ex(q, centroids, offsets, ids, K, V, k: int, *, similarity: st
                                             similarity=similarity, n_sink=n_sink, n_window=n_window, length=L)
         out[b, h], sel[b, h], gap[b, h], n_rows[b, h] = o, lists, gp, len(rows)
     return {"out": out, "sel": sel, "gap": gap, "n_rows": n_rows}
+
+
+def nearest_centroids(keys, centroids, m: int):
+    """The m nearest centroids of every key by squared Euclidean distance,
+    nearest first, ties to the lower index. keys [n][d], centroids [C][d].
+    Returns (assign [n][m], gap [n]) where gap = (d2_(m+1) - d2_(m)) / d2_(m)
+    is the relative margin that decides the m-th choice (inf if m == C)."""
+    K = _f64(keys)
+    Cn = _f64(centroids)
+    d2 = np.sum(K * K, axis=1)[:, None] - 2.0 * (K @ Cn.T) + np.sum(Cn * Cn, axis=1)[None, :]
+    d2 = np.maximum(d2, 0.0)
+    C = Cn.shape[0]
+    order = np.lexsort((np.broadcast_to(np.arange(C), d2.shape), d2), axis=1)  # distance, then index
+    assign = order[:, :m]
+    if m >= C:
+        return assign, np.full(K.shape[0], np.inf)
+    dm = np.take_along_axis(d2, order[:, m - 1:m], axis=1)[:, 0]
+    dn = np.take_along_axis(d2, order[:, m:m + 1], axis=1)[:, 0]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        gap = np.where(dm > 0, (dn - dm) / dm, np.inf)
+    return assign, gap
+
+
+def posting_lists_multi(assign, n_lists: int):
+    """CSR lists from an m-way assignment [n][m]: list c holds every token
+    that chose it, ascending. Returns offsets [C+1], ids [n*m], and alt
+    [n*m]: for each entry, the token's other chosen lists (m - 1 of them,
+    in the token's order of preference; shape [n*m][m-1])."""
+    a = np.asarray(assign, dtype=np.int64)
+    n, m = a.shape
+    offsets = np.zeros(n_lists + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(np.bincount(a.ravel(), minlength=n_lists))
+    ids = np.empty(n * m, dtype=np.int64)
+    alt = np.empty((n * m, max(m - 1, 0)), dtype=np.int64)
+    fill = offsets[:-1].copy()
+    for i in range(n):               # ascending token ids inside every list
+        for r in range(m):
+            c = a[i, r]
+            ids[fill[c]] = i
+            alt[fill[c]] = np.delete(a[i], r)
+            fill[c] += 1
+    return offsets, ids, alt
+
+
+def index_build_multi(keys, centroids, m: int):
+    """m-way posting lists for every (request, KV head): keys [B][N][Hkv][d],
+    centroids [Bc][Hkv][C][d]. Returns offsets [B][Hkv][C+1],
+    ids [B][Hkv][N*m], alt [B][Hkv][N*m][m-1] and the smallest m-th-choice
+    margin seen."""
+    K = np.asarray(keys)
+    Cn = np.asarray(centroids)
+    B, N, Hkv, _ = K.shape
+    C = Cn.shape[2]
+    offsets = np.empty((B, Hkv, C + 1), dtype=np.int64)
+    ids = np.empty((B, Hkv, N * m), dtype=np.int64)
+    alt = np.empty((B, Hkv, N * m, max(m - 1, 0)), dtype=np.int64)
+    margin = np.inf
+    for b in range(B):
+        for g in range(Hkv):
+            a, gap = nearest_centroids(K[b, :, g], Cn[0 if Cn.shape[0] == 1 else b, g], m)
+            offsets[b, g], ids[b, g], alt[b, g] = posting_lists_multi(a, C)
+            margin = min(margin, float(gap.min()))
+    return offsets, ids, alt, margin

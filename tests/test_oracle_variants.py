@@ -106,3 +106,48 @@ def test_no_variant_is_the_plain_decode():
     r = ivf.decode_head(q, cent, off, ids, K, V, k)
     assert np.array_equal(lists, r.lists) and np.array_equal(rows, r.rows)
     assert np.array_equal(o, r.out)
+
+
+def test_nearest_centroids_brute_force_and_m1():
+    rng = np.random.default_rng(8)
+    C, d = 9, 6
+    cent = rng.standard_normal((C, d))
+    keys = rng.standard_normal((40, d))
+    a, gap = variants.nearest_centroids(keys, cent, 3)
+    for i in range(40):
+        d2 = [float(np.sum((keys[i] - cent[c]) ** 2)) for c in range(C)]
+        order = sorted(range(C), key=lambda c: (d2[c], c))
+        assert a[i].tolist() == order[:3]
+    # m = 1 is the plain assignment
+    a1, _ = variants.nearest_centroids(keys, cent, 1)
+    assert np.array_equal(a1[:, 0], ivf.nearest_centroid(keys, cent)[0])
+    # ties go to the lower index: a key midway between centroids 0 and 1
+    c2 = np.array([[1.0, 0.0], [-1.0, 0.0], [0.0, 5.0]])
+    a2, _ = variants.nearest_centroids(np.array([[0.0, 0.0]]), c2, 2)
+    assert a2[0].tolist() == [0, 1]
+
+
+def test_multi_assignment_lists_and_dedup_in_the_union():
+    rng = np.random.default_rng(9)
+    N, C, d, m = 300, 10, 8, 2
+    cent, K = _clustered(rng, N, C, d)
+    V = rng.standard_normal((N, d))
+    a, _ = variants.nearest_centroids(K, cent, m)
+    off, ids, alt = variants.posting_lists_multi(a, C)
+    assert off[-1] == N * m
+    for c in range(C):
+        lst = ids[off[c]:off[c + 1]]
+        assert np.all(np.diff(lst) > 0)                          # ascending, each token once per list
+        assert np.array_equal(np.sort(lst), np.flatnonzero((a == c).any(axis=1)))
+        for e in range(off[c], off[c + 1]):                       # alt names the token's other list
+            assert set(alt[e].tolist()) | {c} == set(a[ids[e]].tolist())
+    # every token appears in exactly m lists
+    assert np.array_equal(np.bincount(ids, minlength=N), np.full(N, m))
+    # the decode attends the union once: masked attention over it
+    q = cent[3] + 0.1 * rng.standard_normal(d)
+    o, lists, rows, _ = variants.decode_head_ex(q, cent, off, ids, K, V, 3)
+    keep = np.zeros(N, dtype=bool)
+    for c in lists:
+        keep[ids[off[c]:off[c + 1]]] = True
+    assert np.array_equal(rows, np.flatnonzero(keep))
+    assert np.allclose(o, _masked_dense(q, K, V, keep), rtol=0, atol=1e-12)
