@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--similarity", default="dot", choices=["dot", "cosine"],
                     help="inverted-index workloads: centroid similarity")
     ap.add_argument("--sink", type=int, default=0, help="inverted-index workloads: leading tokens always attended")
+    ap.add_argument("--assign", type=int, default=1, choices=[1, 2],
+                    help="inverted-index workloads: lists per key (2: every key joins its two nearest lists)")
     ap.add_argument("--window", type=int, default=0,
                     help="inverted-index workloads: trailing tokens always attended")
     ap.add_argument("--layers", type=int, default=1,
@@ -161,7 +163,11 @@ def bench_ivf(args, cfg, torch, tsa, W):
     nq = min(cfg.steps, 64)
     q_all = W.ivf_queries(cfg, p["centroids"], steps=nq)
     t0 = time.perf_counter()
-    offsets, ids = tsa.index_build(p["keys"], p["centroids"])
+    alt = None
+    if args.assign == 2:
+        offsets, ids, alt = tsa.index_build_multi(p["keys"], p["centroids"], 2)
+    else:
+        offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     torch.cuda.synchronize()
     index_ms = (time.perf_counter() - t0) * 1e3
     out = torch.empty((B, Hq, cfg.head_dim), dtype=torch.float32, device=dev)
@@ -169,15 +175,15 @@ def bench_ivf(args, cfg, torch, tsa, W):
     desc = tsa.binding.ivf_desc(p["keys"], p["centroids"], Hq)
     ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
 
-    variant = args.similarity != "dot" or args.sink > 0 or args.window > 0
+    variant = args.similarity != "dot" or args.sink > 0 or args.window > 0 or alt is not None
     if variant:
-        ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX, desc, k), dtype=torch.uint8,
-                         device=dev)
+        op = tsa.binding.OP_SPARSE_DECODE_EX_MULTI if alt is not None else tsa.binding.OP_SPARSE_DECODE_EX
+        ws = torch.empty(tsa.workspace_bytes(op, desc, k), dtype=torch.uint8, device=dev)
 
     def call(i):
         if variant:
             tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
-                                 similarity=args.similarity, n_sink=args.sink, n_window=args.window,
+                                 similarity=args.similarity, n_sink=args.sink, n_window=args.window, alt=alt,
                                  out=out, uniq_out=uniq[i % nq], ws=ws)
         else:
             tsa.sparse_decode(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
@@ -185,7 +191,9 @@ def bench_ivf(args, cfg, torch, tsa, W):
 
     res = _timed(args, call, torch, tsa, n_distinct=nq)
     # rows read per step: unique list rows, plus the sink / window rows (an
-    # upper bound: a list row inside those ranges is read once, counted twice)
+    # upper bound: a list row inside those ranges is read once, counted twice;
+    # with two lists per key, list entries: a token in two chosen lists of the
+    # group counts twice)
     fixed = min(args.sink + args.window, cfg.n_tokens) * B * Hkv
     rows_per_set = uniq.sum(dim=(1, 2)).cpu().double() + fixed
     rows = sum(float(rows_per_set[i % nq]) for i in range(args.steps))
@@ -576,6 +584,8 @@ def main():
             workload += f"+{args.similarity}"
         if args.sink or args.window:
             workload += f"+sink{args.sink}+window{args.window}"
+        if args.assign == 2:
+            workload += "+two-lists-per-key"
     if cfg.kind == "cache" and args.policy != "lru":
         workload += f"+{args.policy}"
     if cfg.kind == "cache" and args.layers > 1:

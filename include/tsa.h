@@ -75,7 +75,9 @@ typedef enum tsa_op {
   TSA_OP_SPARSE_DECODE = 1,
   TSA_OP_TOKEN_DECODE = 2,
   TSA_OP_ATTEND_ROWS = 3,
-  TSA_OP_SPARSE_DECODE_EX = 4
+  TSA_OP_SPARSE_DECODE_EX = 4,
+  TSA_OP_INDEX_BUILD_MULTI = 5,      /* tsa_index_build_multi with m = 2 */
+  TSA_OP_SPARSE_DECODE_EX_MULTI = 6  /* tsa_sparse_decode_ex with assign_per_key = 2 */
 } tsa_op;
 
 /* Inverted-index (centroid) problem. */
@@ -174,6 +176,23 @@ tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void
                              void* stream);
 
 /* ------------------------------------------------------------------------
+ * tsa_index_build_multi - posting lists in which every key joins its m
+ *   nearest lists ([KARAT] How, index structure: an entry is placed into
+ *   several lists by its key), m = 1 or 2 (squared L2 in fp32, nearest
+ *   first, ties to the lower index).
+ *   offsets (device, out) int32 [B][Hkv][C+1] over N * m entries
+ *   ids     (device, out) int32 [B][Hkv][N*m]: ascending token ids per list
+ *   alt     (device, out) int32 [B][Hkv][N*m] (m = 2; NULL for m = 1): for
+ *           each entry, the token's other list
+ *   Workspace: tsa_workspace_bytes(TSA_OP_INDEX_BUILD_MULTI, desc, 0, ...)
+ *   for m = 2 (TSA_OP_INDEX_BUILD for m = 1). Decode with
+ *   tsa_sparse_decode_ex and opts->assign_per_key = m.
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_index_build_multi(const tsa_ivf_desc* desc, const void* keys, const void* centroids,
+                                 int32_t m, int32_t* offsets, int32_t* ids, int32_t* alt, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Growing index: per-step KV and posting-list append.
  *   [KARAT] worked example, step 6: after each step the new KV entry is
  *   stored and added to its posting list; Limitations, item 3: keeping the
@@ -238,11 +257,18 @@ tsa_status tsa_sparse_decode_dyn(const tsa_ivf_desc* desc, const void* q, const 
  *                     request (default N); both ranges are clipped to [0, L)
  *   opts->lens        (device, nullable) list lengths of a growing index, as
  *                     for tsa_sparse_decode_dyn
+ *   opts->assign_per_key  0 or 1: one list per token; 2: ids and alt come
+ *                     from tsa_index_build_multi with m = 2 ([B][Hkv][2N]);
+ *                     a token in two chosen lists of a head is attended once
+ *                     (through the lower-numbered list); not with lens
+ *   opts->alt         (device) int32 [B][Hkv][2N] from tsa_index_build_multi,
+ *                     required when assign_per_key is 2
  *   The attended set of a head is the union of its chosen lists' rows and
  *   the two ranges; a row in both is attended once. rows_out and uniq_out
  *   count list entries only. Workspace:
- *   tsa_workspace_bytes(TSA_OP_SPARSE_DECODE_EX, desc, k, ...). Other
- *   arguments as for tsa_sparse_decode.
+ *   tsa_workspace_bytes(TSA_OP_SPARSE_DECODE_EX, desc, k, ...), or
+ *   TSA_OP_SPARSE_DECODE_EX_MULTI with assign_per_key 2. Other arguments as
+ *   for tsa_sparse_decode.
  * ---------------------------------------------------------------------- */
 typedef enum tsa_similarity { TSA_SIM_DOT = 0, TSA_SIM_COSINE = 1 } tsa_similarity;
 
@@ -250,9 +276,10 @@ typedef struct tsa_decode_opts {
   int32_t similarity;       /* tsa_similarity                               */
   int32_t n_sink;           /* leading tokens always attended               */
   int32_t n_window;         /* trailing tokens (before the length) attended */
-  int32_t reserved;         /* 0                                            */
+  int32_t assign_per_key;   /* 0 / 1 / 2 lists per token                    */
   const int32_t* lengths;   /* device [B] or NULL                           */
   const int32_t* lens;      /* device [B][Hkv][C] or NULL                   */
+  const int32_t* alt;       /* device [B][Hkv][2N] or NULL                  */
 } tsa_decode_opts;
 
 tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts* opts, const void* q,

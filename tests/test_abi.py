@@ -117,11 +117,18 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
     # decode variants: bad similarity, too many fixed rows, null opts
     ws_ex = B.workspace_bytes(B.OP_SPARSE_DECODE_EX, d, 4)
     assert ws_ex > ws_need
-    for opts in (B.DecodeOpts(2, 0, 0, 0, None, None), B.DecodeOpts(0, 5000, 4000, 0, None, None),
-                 B.DecodeOpts(0, -1, 0, 0, None, None)):
+    for opts in (B.DecodeOpts(2, 0, 0, 0, None, None, None), B.DecodeOpts(0, 5000, 4000, 0, None, None, None),
+                 B.DecodeOpts(0, -1, 0, 0, None, None, None), B.DecodeOpts(0, 0, 0, 2, None, None, None),
+                 B.DecodeOpts(0, 0, 0, 3, None, None, None)):
         st = lib.tsa_sparse_decode_ex(ctypes.byref(d), ctypes.byref(opts), fake, fake, fake, fake, fake, fake, 4,
                                       fake, None, None, None, fake, ws_ex, None)
         assert st == B.TSA_ERR_INVALID_ARG
+    assert B.workspace_bytes(B.OP_SPARSE_DECODE_EX_MULTI, d, 4) > ws_ex
+    assert B.workspace_bytes(B.OP_INDEX_BUILD_MULTI, d) > B.workspace_bytes(B.OP_INDEX_BUILD, d)
+    st = lib.tsa_index_build_multi(ctypes.byref(d), fake, fake, 3, fake, fake, fake, fake, 1 << 30, None)
+    assert st == B.TSA_ERR_UNSUPPORTED
+    st = lib.tsa_index_build_multi(ctypes.byref(d), fake, fake, 2, fake, fake, None, fake, 1 << 30, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"alt is NULL" in lib.tsa_last_error()
     st = lib.tsa_sparse_decode_ex(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, 4, fake, None, None,
                                   None, fake, ws_ex, None)
     assert st == B.TSA_ERR_INVALID_ARG and b"opts is NULL" in lib.tsa_last_error()

@@ -186,3 +186,64 @@ def test_token_selection_feeds_the_hot_cache():
         assert torch.equal(hits + miss, torch.full_like(hits, k))
         misses.append(int(miss.sum()))
     assert misses[0] == B * k and min(misses[1:]) < B * k   # planted tokens stay selected and hit
+
+
+def _two_way_keys(cfg, centroids, seed):
+    """Keys between two centroids (0.6 c_a + 0.4 c_b + 0.1 noise, a != b): a
+    clear first and second nearest list and a wide margin to the third."""
+    g = torch.Generator().manual_seed(seed)
+    B, N, Hkv, d = cfg.batch, cfg.n_tokens, cfg.n_kv_heads, cfg.head_dim
+    C = centroids.shape[2]
+    cent = centroids.float().cpu()
+    a = torch.randint(0, C, (B, N, Hkv), generator=g)
+    b = (a + torch.randint(1, C, (B, N, Hkv), generator=g)) % C
+    head = torch.arange(Hkv)[None, None, :].expand(B, N, Hkv)
+    keys = 0.6 * cent[0][head, a] + 0.4 * cent[0][head, b] + 0.1 * torch.randn((B, N, Hkv, d), generator=g)
+    return keys.to(cfg.torch_dtype).to(DEV)
+
+
+def test_two_way_lists_build_and_decode():
+    """Every key in its two nearest lists: lists and alt exact against the
+    oracle; decode attends each token once per head (union of the lists),
+    alone and with cosine + sink/window."""
+    cfg, p = _problem(n_tokens=4000, n_centroids=32, top_k=5)
+    announce("variants: two lists per key")
+    p["keys"] = _two_way_keys(cfg, p["centroids"], 17)
+    off, ids, alt = tsa.index_build_multi(p["keys"], p["centroids"], 2)
+    torch.cuda.synchronize()
+    k64, c64 = f64(p["keys"]), f64(p["centroids"])
+    r_off, r_ids, r_alt, margin = variants.index_build_multi(k64, c64, 2)
+    assert margin >= 1e-3, f"second-choice margin {margin} too small for an exact comparison"
+    assert np.array_equal(off.cpu().numpy(), r_off)
+    assert np.array_equal(ids.cpu().numpy(), r_ids)
+    assert np.array_equal(alt.cpu().numpy(), r_alt[..., 0])
+    # one list per key through the same entry point equals the plain build
+    o1, i1, a1 = tsa.index_build_multi(p["keys"], p["centroids"], 1)
+    s_off, s_ids = tsa.index_build(p["keys"], p["centroids"])
+    torch.cuda.synchronize()
+    assert a1 is None and torch.equal(o1, s_off) and torch.equal(i1, s_ids)
+
+    for kw in ({}, {"similarity": "cosine", "n_sink": 16, "n_window": 200}):
+        q = _queries(cfg, p, kw.get("similarity", "dot"))
+        sel = torch.empty((cfg.batch, cfg.n_q_heads, cfg.top_k), dtype=torch.int32, device=DEV)
+        out = tsa.sparse_decode_ex(q, p["centroids"], off, ids, p["keys"], p["values"], cfg.top_k, alt=alt,
+                                   sel_out=sel, **kw)
+        torch.cuda.synchronize()
+        r = variants.sparse_decode_ex(f64(q), c64, r_off, r_ids, k64, f64(p["values"]), cfg.top_k, **kw)
+        assert np.all(r["gap"] >= GAP_MIN)
+        assert np.array_equal(sel.cpu().numpy(), r["sel"])
+        err = out_error(out.cpu().numpy(), r["out"])
+        assert err <= OUT_TOL, f"output error {err} ({kw})"
+        if not kw:
+            # the case does hold tokens in two chosen lists of one head: counting
+            # them twice would move the output well past the bar
+            G = cfg.group
+            worst = 0.0
+            for b in range(cfg.batch):
+                for h in range(cfg.n_q_heads):
+                    g = h // G
+                    lists = r["sel"][b, h]
+                    rows = np.concatenate([r_ids[b, g][r_off[b, g][c]:r_off[b, g][c + 1]] for c in lists])
+                    o2, _ = ivf.attend(f64(q)[b, h], k64[b, rows, g], f64(p["values"])[b, rows, g])
+                    worst = max(worst, out_error(out.cpu().numpy()[b, h], o2))
+            assert worst > 10 * OUT_TOL, "no token was in two chosen lists; the case tests nothing"

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     hier_group_step,
     index_build,
     index_build_dyn,
+    index_build_multi,
     kv_append,
     lib_path,
     load,
@@ -30,7 +31,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "kv_append", "sparse_decode",
+    "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "index_build_multi", "kv_append", "sparse_decode",
     "sparse_decode_dyn", "sparse_decode_ex", "token_decode",
     "attend_rows", "resolve", "cache_reset", "fetch_rows", "hier_group_step", "HostArray", "time_next_gather", "workspace_bytes",
     "TsaError",

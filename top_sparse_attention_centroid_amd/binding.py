@@ -16,7 +16,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsa.so"
 
 TSA_OK, TSA_ERR_INVALID_ARG, TSA_ERR_UNSUPPORTED, TSA_ERR_WORKSPACE, TSA_ERR_HIP = range(5)
 TSA_F32, TSA_BF16 = 0, 1
-OP_INDEX_BUILD, OP_SPARSE_DECODE, OP_TOKEN_DECODE, OP_ATTEND_ROWS, OP_SPARSE_DECODE_EX = range(5)
+(OP_INDEX_BUILD, OP_SPARSE_DECODE, OP_TOKEN_DECODE, OP_ATTEND_ROWS, OP_SPARSE_DECODE_EX, OP_INDEX_BUILD_MULTI,
+ OP_SPARSE_DECODE_EX_MULTI) = range(7)
 SIMILARITY = {"dot": 0, "cosine": 1}
 EVICT_POLICIES = {"lru": 0, "fifo": 1, "random": 2, "priority": 3}
 
@@ -40,8 +41,8 @@ class CacheDesc(ctypes.Structure):
 
 
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("similarity", _I32), ("n_sink", _I32), ("n_window", _I32), ("reserved", _I32),
-                ("lengths", _P), ("lens", _P)]
+    _fields_ = [("similarity", _I32), ("n_sink", _I32), ("n_window", _I32), ("assign_per_key", _I32),
+                ("lengths", _P), ("lens", _P), ("alt", _P)]
 
 
 class LayerIO(ctypes.Structure):
@@ -60,6 +61,7 @@ _SIGNATURES = {
                           ctypes.c_size_t, _P],
     "tsa_sparse_decode_ex": [ctypes.POINTER(IvfDesc), ctypes.POINTER(DecodeOpts), _P, _P, _P, _P, _P, _P, _I32,
                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_index_build_multi": [ctypes.POINTER(IvfDesc), _P, _P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_index_build_dyn": [ctypes.POINTER(IvfDesc), _P, _P, _I32, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_kv_append": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "tsa_sparse_decode_dyn": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
@@ -282,11 +284,37 @@ def kv_append(new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids
     return status
 
 
+def index_build_multi(keys, centroids, m: int = 2, *, offsets=None, ids=None, alt=None, ws=None, stream=None):
+    """Posting lists where every key joins its m nearest lists (m = 1 or 2).
+    Returns (offsets [B][Hkv][C+1], ids [B][Hkv][N*m], alt [B][Hkv][N*m] or None)."""
+    _dev(keys, "keys"), _dev(centroids, "centroids")
+    if centroids.dtype != keys.dtype:
+        raise ValueError("keys and centroids must share a dtype")
+    desc = ivf_desc(keys, centroids, keys.shape[2])
+    B, N, Hkv, _ = keys.shape
+    C = centroids.shape[2]
+    if offsets is None:
+        offsets = torch.empty((B, Hkv, C + 1), dtype=torch.int32, device=keys.device)
+    if ids is None:
+        ids = torch.empty((B, Hkv, N * m), dtype=torch.int32, device=keys.device)
+    if alt is None and m == 2:
+        alt = torch.empty((B, Hkv, N * m), dtype=torch.int32, device=keys.device)
+    _i32(offsets, "offsets", (B, Hkv, C + 1))
+    _i32(ids, "ids", (B, Hkv, N * m))
+    _i32(alt, "alt", (B, Hkv, N * m))
+    ws = _workspace(OP_INDEX_BUILD_MULTI if m == 2 else OP_INDEX_BUILD, desc, 0, ws, keys.device)
+    _check(load().tsa_index_build_multi(ctypes.byref(desc), _ptr(keys), _ptr(centroids), m, _ptr(offsets), _ptr(ids),
+                                        _ptr(alt), _ptr(ws), ws.numel(), _stream(stream)))
+    return offsets, ids, alt
+
+
 def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, similarity: str = "dot",
-                     n_sink: int = 0, n_window: int = 0, lengths=None, lens=None, out=None, sel_out=None,
-                     rows_out=None, uniq_out=None, ws=None, stream=None):
+                     n_sink: int = 0, n_window: int = 0, lengths=None, lens=None, alt=None, out=None,
+                     sel_out=None, rows_out=None, uniq_out=None, ws=None, stream=None):
     """Decode with the variants: cosine similarity and/or the first n_sink and
-    last n_window tokens (before lengths[b]) attended beside the lists."""
+    last n_window tokens (before lengths[b]) attended beside the lists; with
+    `alt` (from index_build_multi, m = 2) every token sits in two lists and is
+    attended once per head."""
     for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
@@ -299,8 +327,10 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
     if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != B or k_cache.shape[3] != d:
         raise ValueError("q / k_cache / v_cache shapes disagree")
     Hkv, C, N = desc.n_kv_heads, desc.n_centroids, desc.n_tokens
+    m = 2 if alt is not None else 1
     _i32(offsets, "offsets", (B, Hkv, C + 1))
-    _i32(ids, "ids", (B, Hkv, N))
+    _i32(ids, "ids", (B, Hkv, N * m))
+    _i32(alt, "alt", (B, Hkv, N * m))
     _i32(lengths, "lengths", (B,))
     _i32(lens, "lens", (B, Hkv, C))
     if out is None:
@@ -310,8 +340,8 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
     _i32(sel_out, "sel_out", (B, Hq, k))
     _i32(rows_out, "rows_out", (B, Hq))
     _i32(uniq_out, "uniq_out", (B, Hkv))
-    opts = DecodeOpts(SIMILARITY[similarity], n_sink, n_window, 0, _ptr(lengths), _ptr(lens))
-    ws = _workspace(OP_SPARSE_DECODE_EX, desc, k, ws, q.device)
+    opts = DecodeOpts(SIMILARITY[similarity], n_sink, n_window, m, _ptr(lengths), _ptr(lens), _ptr(alt))
+    ws = _workspace(OP_SPARSE_DECODE_EX_MULTI if m == 2 else OP_SPARSE_DECODE_EX, desc, k, ws, q.device)
     _check(load().tsa_sparse_decode_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(centroids),
                                        _ptr(offsets), _ptr(ids), _ptr(k_cache), _ptr(v_cache), k, _ptr(out),
                                        _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(),

@@ -93,13 +93,16 @@ struct Batch {
 // them in flight (a predicated load would force a wait for every earlier one).
 template <bool STREAM, typename T, int U>
 __device__ __forceinline__ void issue_batch(Batch<T, U>& bt, const int* ids, int base, int cnt, int r,
-                                            const T* kb, const T* vb, long long row_stride) {
+                                            const T* kb, const T* vb, long long row_stride,
+                                            const uint32_t* dup = nullptr, int h = 0) {
   int row[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = base + u * 4 + r;
     const int id = ids[min(j, kSegRows - 1)];
-    bt.valid[u] = (j < cnt) & (id >= 0);
+    // dup: heads that attend this token through another (lower) chosen list
+    const bool twice = dup ? ((dup[min(j, kSegRows - 1)] >> h) & 1u) : false;
+    bt.valid[u] = (j < cnt) & (id >= 0) & !twice;
     row[u] = bt.valid[u] ? id : 0;
   }
   if constexpr (STREAM) {
@@ -160,7 +163,7 @@ __device__ __forceinline__ void consume_batch(const Batch<T, U>& bt, HeadState& 
 template <bool STREAM, typename T>
 __device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int cnt, int r, int e, const T* kb,
                                             const T* vb, long long row_stride, const T* qs, float qscale,
-                                            float* part) {
+                                            float* part, const uint32_t* dup = nullptr) {
   for (uint32_t hm = mask; hm != 0u; hm &= hm - 1u) {
     const int h = __builtin_ctz(hm);
     QFrag<T> qf;
@@ -169,11 +172,11 @@ __device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int c
     st.init();
 #if TSA_GATHER_PIPE
     Batch<T> A, Bb;
-    issue_batch<STREAM>(A, ids, 0, cnt, r, kb, vb, row_stride);
+    issue_batch<STREAM>(A, ids, 0, cnt, r, kb, vb, row_stride, dup, h);
     for (int base = 0; base < cnt; base += 2 * kBatchRows) {
-      issue_batch<STREAM>(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride);
+      issue_batch<STREAM>(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(A, st, qf, qscale);
-      issue_batch<STREAM>(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride);
+      issue_batch<STREAM>(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(Bb, st, qf, qscale);
     }
 #elif TSA_GATHER_TAIL
@@ -181,18 +184,18 @@ __device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int c
     int base = 0;
     for (; base + kBatchRows / 2 < cnt; base += kBatchRows) {
       Batch<T> A;
-      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride);
+      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(A, st, qf, qscale);
     }
     if (base < cnt) {
       Batch<T, kGatherUnroll / 2> A;
-      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride);
+      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(A, st, qf, qscale);
     }
 #else
     for (int base = 0; base < cnt; base += kBatchRows) {
       Batch<T> A;
-      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride);
+      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(A, st, qf, qscale);
     }
 #endif
@@ -299,6 +302,7 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
   constexpr int NW = gather_waves<EXPLICIT>();
   __shared__ __align__(16) T qs[G * kHeadDim];
   __shared__ int ids_lds[NW][kSegRows];
+  __shared__ uint32_t dup_lds[EXPLICIT ? NW : 1][EXPLICIT ? kSegRows : 1];
   const int bg = blockIdx.x / p.W, w0 = blockIdx.x % p.W;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
 
@@ -360,6 +364,7 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
     int start, cnt;
     uint32_t mask;
     bool direct;  // a token range [start, start + cnt) instead of list entries
+    int list;     // the posting list (explicit plans)
   };
   auto seg_of = [&](int s, int4 d) {
     Seg sg;
@@ -368,13 +373,31 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
       sg.cnt = min(max(d.y, 0), kSegRows);
       sg.mask = static_cast<uint32_t>(d.z);
       sg.direct = d.w < 0;
+      sg.list = d.w;
     } else {
       sg.start = s * p.seg_rows;
       sg.cnt = min(p.seg_rows, total_rows - sg.start);
       sg.mask = (1u << G) - 1u;
       sg.direct = false;
+      sg.list = -1;
     }
     return sg;
+  };
+  // 2-way lists: a token sits in two lists; for each head the entry of the
+  // lower chosen list is the one attended (per-row duplicate head masks)
+  const bool two_way = EXPLICIT && p.alt != nullptr;
+  uint32_t* dup = two_way ? dup_lds[EXPLICIT ? wave : 0] : nullptr;
+  const int32_t* altb = two_way ? p.alt + b * p.rid_bstride + g * p.rid_gstride : nullptr;
+  auto stage_dup = [&](const Seg& sg) {
+    if (!two_way) return;
+    for (int j = lane; j < sg.cnt; j += kWave) {
+      uint32_t dm = 0u;
+      if (!sg.direct) {
+        const int other = altb[sg.start + j];
+        if (other >= 0 && other < sg.list && other < p.C) dm = p.lmask[static_cast<long long>(bg) * p.C + other];
+      }
+      dup[j] = dm;
+    }
   };
   constexpr int kIdsPerLane = kSegRows / kWave;
   // a segment's row ids into registers: straight-line loads at clamped
@@ -404,7 +427,10 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
 #pragma unroll
   for (int i = 0; i < kQPer; ++i)
     if (tid + i * NW * kWave < kQParts) *reinterpret_cast<Raw8<T>*>(qs + (tid + i * NW * kWave) * 8) = qpart[i];
-  if (s_first < nseg && cur.cnt > 0) store_ids(cur, cid);
+  if (s_first < nseg && cur.cnt > 0) {
+    store_ids(cur, cid);
+    stage_dup(cur);
+  }
   __syncthreads();
 
   for (int it = 0, s = s_first; s < nseg; ++it, s += stride) {
@@ -431,19 +457,22 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
     float* part = p.partial + (static_cast<long long>(bg) * p.smax + s) * G * kPartStride;
     // A row read by a single head's pass streams past the caches; rows that a
     // second head will re-read stay cacheable so that pass hits L2.
-    if (!EXPLICIT || (TSA_GATHER_FULLMASK_ALL && G > 1 && mask == (1u << G) - 1u)) {
+    if (!EXPLICIT || (TSA_GATHER_FULLMASK_ALL && G > 1 && mask == (1u << G) - 1u && !two_way)) {
       // every head of the group reads these rows: score them for all heads at once
       all_heads_pass<G>(ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
     } else if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u) {
-      head_passes<true>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
+      head_passes<true>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);
     } else {
-      head_passes<false>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
+      head_passes<false>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);
     }
     // the next segment overwrites this wave's id staging area
     __builtin_amdgcn_wave_barrier();
     if (has_next) {
       cur = nxt;
-      if (cur.cnt > 0) store_ids(cur, nid);
+      if (cur.cnt > 0) {
+        store_ids(cur, nid);
+        stage_dup(cur);
+      }
     }
   }
 }

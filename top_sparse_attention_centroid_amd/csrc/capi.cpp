@@ -100,19 +100,21 @@ FetchParams fetch_params(const tsa_cache_desc& d, const int32_t* miss_tok, const
 // ----------------------------------------------------------------- layouts
 struct IvfLayout {
   int G = 0, smax = 0;
-  size_t seg = 0, nseg = 0, partial = 0, total = 0;
+  size_t seg = 0, nseg = 0, partial = 0, lmask = 0, total = 0;
 };
 
-// with_fixed: room for the sink / window segments of tsa_sparse_decode_ex
-IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false) {
+// with_fixed: room for the sink / window segments of tsa_sparse_decode_ex;
+// m: lists per token (2: twice the list entries and the chosen-list masks)
+IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false, int m = 1) {
   IvfLayout L;
   L.G = d.n_q_heads / d.n_kv_heads;
-  L.smax = L.G * k + ceil_div(d.n_tokens, kSegRows) + (with_fixed ? kMaxFixedRows / kSegRows + 2 : 0);
+  L.smax = L.G * k + ceil_div(d.n_tokens * m, kSegRows) + (with_fixed ? kMaxFixedRows / kSegRows + 2 : 0);
   const size_t bh = static_cast<size_t>(d.batch) * d.n_kv_heads;
   size_t off = 0;
   L.seg = off;    off += align_up(bh * L.smax * sizeof(int4));
   L.nseg = off;   off += align_up(bh * sizeof(int32_t));
   L.partial = off; off += align_up(bh * L.smax * L.G * kPartStride * sizeof(float));
+  L.lmask = off;   off += m > 1 ? align_up(bh * d.n_centroids * sizeof(uint32_t)) : 0;
   L.total = off;
   return L;
 }
@@ -156,12 +158,12 @@ RowsLayout rows_layout(const tsa_attn_desc& d) {
   return L;
 }
 
-size_t index_assign_bytes(const tsa_ivf_desc& d) {
-  return align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * d.n_tokens * sizeof(int32_t));
+size_t index_assign_bytes(const tsa_ivf_desc& d, int m = 1) {
+  return align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * d.n_tokens * m * sizeof(int32_t));
 }
-size_t index_ws(const tsa_ivf_desc& d) {
+size_t index_ws(const tsa_ivf_desc& d, int m = 1) {
   const size_t bc = d.shared_codebook ? 1 : static_cast<size_t>(d.batch);
-  return index_assign_bytes(d) + align_up(bc * d.n_kv_heads * d.n_centroids * sizeof(float));
+  return index_assign_bytes(d, m) + align_up(bc * d.n_kv_heads * d.n_centroids * sizeof(float));
 }
 
 // ------------------------------------------------------------- validation
@@ -262,19 +264,20 @@ long long codebook_stride(const tsa_ivf_desc& d) {
 
 tsa_status index_build_impl(const tsa_ivf_desc* desc, const void* keys, const void* centroids, int n_prefix,
                             int slack, int32_t* offsets, int32_t* lens, int32_t* ids, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            void* stream, int m = 1, int32_t* alt = nullptr) {
   REQUIRE_PTR(keys); REQUIRE_PTR(centroids); REQUIRE_PTR(offsets); REQUIRE_PTR(ids); REQUIRE_PTR(ws);
   REQUIRE_ALIGN(keys, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(ws, 16);
-  const size_t need = index_ws(*desc);
+  const size_t need = index_ws(*desc, m);
   if (ws_bytes < need) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   const tsa_ivf_desc& d = *desc;
   hipStream_t s = as_stream(stream);
   AssignParams ap{keys, centroids, codebook_stride(d), static_cast<int32_t*>(ws),
-                  d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids, n_prefix};
-  hipError_t e = launch_assign(ap, d.dtype, reinterpret_cast<float*>(static_cast<char*>(ws) + index_assign_bytes(d)), s);
+                  d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids, n_prefix, m};
+  hipError_t e =
+      launch_assign(ap, d.dtype, reinterpret_cast<float*>(static_cast<char*>(ws) + index_assign_bytes(d, m)), s);
   if (e != hipSuccess) return hip_fail(e, "assign launch");
-  CsrParams cp{static_cast<const int32_t*>(ws), offsets, ids, lens, d.batch, d.n_tokens, d.n_kv_heads,
-               d.n_centroids, n_prefix, slack};
+  CsrParams cp{static_cast<const int32_t*>(ws), offsets, ids, lens, alt, d.batch, d.n_tokens, d.n_kv_heads,
+               d.n_centroids, n_prefix, slack, m};
   e = launch_csr(cp, s);
   if (e != hipSuccess) return hip_fail(e, "csr launch");
   return ok();
@@ -291,7 +294,8 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
   REQUIRE_ALIGN(v_cache, 16); REQUIRE_ALIGN(out, 8); REQUIRE_ALIGN(ws, 16);
   const tsa_ivf_desc& d = *desc;
   if (k < 1 || k > d.n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d.n_centroids);
-  const IvfLayout L = ivf_layout(d, k, opts != nullptr);
+  const int m = opts && opts->assign_per_key == 2 ? 2 : 1;
+  const IvfLayout L = ivf_layout(d, k, opts != nullptr, m);
   if (ws_bytes < L.total) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   char* w = static_cast<char*>(ws);
   hipStream_t s = as_stream(stream);
@@ -299,18 +303,21 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
   SelectParams selp{q, centroids, codebook_stride(d), offsets, lens, sel_out, rows_out, uniq_out,
                     reinterpret_cast<int4*>(w + L.seg), reinterpret_cast<int32_t*>(w + L.nseg),
                     d.batch, d.n_kv_heads, d.n_centroids, k, L.smax, d.n_tokens};
+  selp.n_entries = d.n_tokens * m;
   if (opts) {
     selp.cosine = opts->similarity == TSA_SIM_COSINE;
     selp.n_sink = opts->n_sink;
     selp.n_window = opts->n_window;
     selp.lengths = opts->lengths;
   }
+  if (m == 2) selp.lmask_out = reinterpret_cast<uint32_t*>(w + L.lmask);
   hipError_t e = launch_ivf_select(selp, d.dtype, L.G, s);
   if (e != hipSuccess) return hip_fail(e, "ivf_select launch");
 
   GatherParams gp{};
   gp.q = q; gp.k = k_cache; gp.v = v_cache; gp.n_rows = d.n_tokens;
-  gp.rowids = ids; gp.rid_bstride = static_cast<long long>(d.n_kv_heads) * d.n_tokens; gp.rid_gstride = d.n_tokens;
+  gp.rowids = ids; gp.rid_bstride = static_cast<long long>(d.n_kv_heads) * d.n_tokens * m;
+  gp.rid_gstride = static_cast<long long>(d.n_tokens) * m;
   gp.seg = reinterpret_cast<const int4*>(w + L.seg); gp.nseg = reinterpret_cast<const int32_t*>(w + L.nseg);
   gp.counts = nullptr; gp.count_const = 0;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
@@ -318,8 +325,9 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
   // expected segments: per chosen list of the group, its average length
   // N / C in 256-row segments (rounded up, with room for a ragged tail), plus
   // the sink / window segments
-  const int per_list = std::max(1, static_cast<int>((2LL * d.n_tokens / d.n_centroids + kSegRows) / (2 * kSegRows)) +
-                                       (d.n_tokens / d.n_centroids > kSegRows / 2 ? 1 : 0));
+  const long long avg_list = static_cast<long long>(d.n_tokens) * m / d.n_centroids;
+  const int per_list = std::max(1, static_cast<int>((2LL * avg_list + kSegRows) / (2 * kSegRows)) +
+                                       (avg_list > kSegRows / 2 ? 1 : 0));
   int fixed_segs = 0;
   if (opts) {
     fixed_segs = ceil_div(std::min(opts->n_sink, d.n_tokens), kSegRows) +
@@ -331,6 +339,11 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
     gp.n_sink = opts->n_sink;
     gp.n_window = opts->n_window;
     gp.lengths = opts->lengths;
+  }
+  if (m == 2) {
+    gp.alt = opts->alt;
+    gp.lmask = reinterpret_cast<const uint32_t*>(w + L.lmask);
+    gp.C = d.n_centroids;
   }
   if (tsa_status st = launch_gather_timed(gp, d.dtype, L.G, true, s)) return st;
   return ok();
@@ -379,6 +392,19 @@ tsa_status tsa_workspace_bytes(int32_t op, const void* desc, int32_t k, size_t* 
       *bytes = ivf_layout(*d, k, true).total;
       return ok();
     }
+    case TSA_OP_INDEX_BUILD_MULTI: {
+      const auto* d = static_cast<const tsa_ivf_desc*>(desc);
+      if (tsa_status s = check_ivf(d)) return s;
+      *bytes = index_ws(*d, 2);
+      return ok();
+    }
+    case TSA_OP_SPARSE_DECODE_EX_MULTI: {
+      const auto* d = static_cast<const tsa_ivf_desc*>(desc);
+      if (tsa_status s = check_ivf(d)) return s;
+      if (k < 1 || k > d->n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d->n_centroids);
+      *bytes = ivf_layout(*d, k, true, 2).total;
+      return ok();
+    }
     case TSA_OP_TOKEN_DECODE: {
       const auto* d = static_cast<const tsa_token_desc*>(desc);
       if (tsa_status s = check_token(d, k)) return s;
@@ -414,6 +440,18 @@ tsa_status tsa_index_build_dyn(const tsa_ivf_desc* desc, const void* keys, const
     return fail(TSA_ERR_INVALID_ARG, "n_prefix + C * slack = %lld exceeds N=%d",
                 n_prefix + static_cast<long long>(desc->n_centroids) * slack, desc->n_tokens);
   return index_build_impl(desc, keys, centroids, n_prefix, slack, offsets, lens, ids, ws, ws_bytes, stream);
+}
+
+tsa_status tsa_index_build_multi(const tsa_ivf_desc* desc, const void* keys, const void* centroids, int32_t m,
+                                 int32_t* offsets, int32_t* ids, int32_t* alt, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  if (m != 1 && m != 2) return fail(TSA_ERR_UNSUPPORTED, "m=%d: 1 or 2 lists per token", m);
+  if (m > desc->n_centroids) return fail(TSA_ERR_INVALID_ARG, "m=%d > C=%d", m, desc->n_centroids);
+  if (m == 2) REQUIRE_PTR(alt);
+  if (static_cast<long long>(desc->n_tokens) * m > INT32_MAX) return fail(TSA_ERR_UNSUPPORTED, "N * m exceeds int32");
+  return index_build_impl(desc, keys, centroids, desc->n_tokens, 0, offsets, nullptr, ids, ws, ws_bytes, stream, m,
+                          m == 2 ? alt : nullptr);
 }
 
 tsa_status tsa_kv_append(const tsa_ivf_desc* desc, const void* new_k, const void* new_v, const int32_t* pos,
@@ -466,6 +504,14 @@ tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts*
       static_cast<long long>(opts->n_sink) + opts->n_window > kMaxFixedRows)
     return fail(TSA_ERR_INVALID_ARG, "n_sink=%d, n_window=%d: each >= 0 and together <= %d", opts->n_sink,
                 opts->n_window, kMaxFixedRows);
+  if (opts->assign_per_key < 0 || opts->assign_per_key > 2)
+    return fail(TSA_ERR_INVALID_ARG, "assign_per_key=%d is not 0, 1 or 2", opts->assign_per_key);
+  if (opts->assign_per_key == 2) {
+    if (!opts->alt) return fail(TSA_ERR_INVALID_ARG, "opts->alt is NULL for 2 lists per token");
+    if (opts->lens) return fail(TSA_ERR_UNSUPPORTED, "a growing index with 2 lists per token");
+    if (static_cast<long long>(desc->n_tokens) * 2 > INT32_MAX)
+      return fail(TSA_ERR_UNSUPPORTED, "2 * N exceeds int32");
+  }
   return sparse_decode_impl(desc, opts, q, centroids, offsets, opts->lens, ids, k_cache, v_cache, k, out, sel_out,
                             rows_out, uniq_out, ws, ws_bytes, stream);
 }

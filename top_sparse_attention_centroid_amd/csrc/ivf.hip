@@ -17,7 +17,44 @@ namespace tsa {
 // ============================================================================
 constexpr int kAssignTile = 32;
 
-template <typename T>
+// The M best (distance, centroid) pairs seen so far, best first; order is
+// lexicographic, so an equal distance keeps the lower centroid id.
+template <int M>
+struct TopM {
+  float d[M];
+  int c[M];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      d[i] = INFINITY;
+      c[i] = 0x7fffffff;
+    }
+  }
+  __device__ __forceinline__ static bool less(float d1, int c1, float d2, int c2) {
+    return d1 < d2 || (d1 == d2 && c1 < c2);
+  }
+  __device__ __forceinline__ void push(float dd, int cc) {
+    if (M == 1) {
+      if (less(dd, cc, d[0], c[0])) {
+        d[0] = dd;
+        c[0] = cc;
+      }
+      return;
+    }
+    if (less(dd, cc, d[0], c[0])) {
+      d[M - 1] = d[0];
+      c[M - 1] = c[0];
+      d[0] = dd;
+      c[0] = cc;
+    } else if (less(dd, cc, d[M - 1], c[M - 1])) {
+      d[M - 1] = dd;
+      c[M - 1] = cc;
+    }
+  }
+};
+static_assert(sizeof(TopM<2>) > 0, "M is 1 or 2");
+
+template <typename T, int M>
 __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
   __shared__ float4 tile[kAssignTile][kHeadDim / 4];
   __shared__ float norm2[kAssignTile];
@@ -41,8 +78,8 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
   }
   const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
                 static_cast<long long>(g) * p.C * kHeadDim;
-  float best = INFINITY;
-  int bestc = 0;
+  TopM<M> top;
+  top.init();
   for (int c0 = 0; c0 < p.C; c0 += kAssignTile) {
     __syncthreads();
     for (int idx = tid; idx < kAssignTile * (kHeadDim / 8); idx += 256) {
@@ -74,11 +111,13 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         a2 = fmaf(kf[4 * t + 2], v.z, a2);
         a3 = fmaf(kf[4 * t + 3], v.w, a3);
       }
-      const float dist = norm2[j] - 2.f * ((a0 + a1) + (a2 + a3));
-      if (dist < best) { best = dist; bestc = c0 + j; }
+      top.push(norm2[j] - 2.f * ((a0 + a1) + (a2 + a3)), c0 + j);
     }
   }
-  if (valid) p.assign[static_cast<long long>(bg) * p.N + i] = bestc;
+  if (valid) {
+#pragma unroll
+    for (int r = 0; r < M; ++r) p.assign[(static_cast<long long>(bg) * p.N + i) * M + r] = top.c[r];
+  }
 }
 
 // ============================================================================
@@ -116,11 +155,12 @@ __global__ __launch_bounds__(256) void centroid_norms_kernel(const bf16_t* cent,
 // against all staged 16-centroid tiles, reduces each key's best over the 16
 // lanes of its row group, and folds it into the per-key best kept in LDS
 // (strict <, so a tie keeps the earlier stage's lower centroid id).
+template <int M>
 __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignParams p, const float* norms) {
   __shared__ __align__(16) bf16_t cs[kMfmaCs * kCentPad];
   __shared__ float cn[kMfmaCs];
-  __shared__ float best_d[kMfmaKb];
-  __shared__ int best_c[kMfmaKb];
+  __shared__ float best_d[kMfmaKb * M];
+  __shared__ int best_c[kMfmaKb * M];
   const int bg = blockIdx.y;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -130,9 +170,9 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
   const bf16_t* cb = static_cast<const bf16_t*>(p.centroids) + b * p.cent_bstride +
                      static_cast<long long>(g) * p.C * kHeadDim;
   const float* nb = norms + (p.cent_bstride ? (static_cast<long long>(b) * p.Hkv + g) : g) * p.C;
-  for (int i = tid; i < kMfmaKb; i += kMfmaWaves * kWave) {
+  for (int i = tid; i < kMfmaKb * M; i += kMfmaWaves * kWave) {
     best_d[i] = INFINITY;
-    best_c[i] = 0;
+    best_c[i] = 0x7fffffff;
   }
   for (int c0 = 0; c0 < p.C; c0 += kMfmaCs) {
     __syncthreads();
@@ -153,8 +193,9 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
       bf16x8_t a[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
-      float best[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
-      int bid[4] = {0, 0, 0, 0};
+      TopM<M> best[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) best[i].init();
       for (int t = 0; t < ntile; ++t) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         const bf16_t* brow = cs + (t * 16 + col) * kCentPad + grp * 8;
@@ -165,42 +206,51 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
         const int c = c0 + t * 16 + col;
         const float cnv = cn[t * 16 + col];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float d = cnv - 2.f * acc[i];
-          if (c < p.C && d < best[i]) {
-            best[i] = d;
-            bid[i] = c;
-          }
-        }
+        for (int i = 0; i < 4; ++i)
+          if (c < p.C) best[i].push(cnv - 2.f * acc[i], c);
       }
+      // the 16 lanes of a row group hold disjoint centroid columns: merge
+      // their top-M lists by exchanging them over lane distances 8, 4, 2, 1
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) {
-          const float d2 = __shfl_xor(best[i], off);
-          const int c2 = __shfl_xor(bid[i], off);
-          if (d2 < best[i] || (d2 == best[i] && c2 < bid[i])) {
-            best[i] = d2;
-            bid[i] = c2;
+          float od[M];
+          int oc[M];
+#pragma unroll
+          for (int r = 0; r < M; ++r) {
+            od[r] = __shfl_xor(best[i].d[r], off);
+            oc[r] = __shfl_xor(best[i].c[r], off);
           }
+#pragma unroll
+          for (int r = 0; r < M; ++r) best[i].push(od[r], oc[r]);
         }
       }
       if (col == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kl = kt * 16 + grp * 4 + i;
-          if (best[i] < best_d[kl]) {
-            best_d[kl] = best[i];
-            best_c[kl] = bid[i];
+          TopM<M> t;
+#pragma unroll
+          for (int r = 0; r < M; ++r) {
+            t.d[r] = best_d[kl * M + r];
+            t.c[r] = best_c[kl * M + r];
+          }
+#pragma unroll
+          for (int r = 0; r < M; ++r) t.push(best[i].d[r], best[i].c[r]);
+#pragma unroll
+          for (int r = 0; r < M; ++r) {
+            best_d[kl * M + r] = t.d[r];
+            best_c[kl * M + r] = t.c[r];
           }
         }
       }
     }
   }
   __syncthreads();
-  for (int i = tid; i < kMfmaKb; i += kMfmaWaves * kWave) {
-    const int key = kbase + i;
-    if (key < p.n_assign) p.assign[static_cast<long long>(bg) * p.N + key] = best_c[i];
+  for (int i = tid; i < kMfmaKb * M; i += kMfmaWaves * kWave) {
+    const int key = kbase + i / M;
+    if (key < p.n_assign) p.assign[(static_cast<long long>(bg) * p.N + key) * M + i % M] = best_c[i];
   }
 }
 
@@ -215,10 +265,13 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
   __shared__ int scan_scratch[4];
   const int bg = blockIdx.x;
   const int tid = threadIdx.x;
-  const int n = p.n_assign;
-  const int32_t* a = p.assign + static_cast<long long>(bg) * p.N;
+  const int m = p.m;
+  const int n = p.n_assign * m;  // (token, list) entries, token-major
+  const long long cap = static_cast<long long>(p.N) * m;
+  const int32_t* a = p.assign + static_cast<long long>(bg) * cap;
   int32_t* off = p.offsets + static_cast<long long>(bg) * (p.C + 1);
-  int32_t* ids = p.ids + static_cast<long long>(bg) * p.N;
+  int32_t* ids = p.ids + static_cast<long long>(bg) * cap;
+  int32_t* alt = p.alt ? p.alt + static_cast<long long>(bg) * cap : nullptr;
   int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * p.C : nullptr;
 
   for (int c = tid; c < p.C; c += 256) cursor[c] = 0;
@@ -240,8 +293,8 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
     }
     carry += tot;
   }
-  if (tid == 0) off[p.C] = carry;  // n + C * slack <= N
-  for (int i = carry + tid; i < p.N; i += 256) ids[i] = -1;
+  if (tid == 0) off[p.C] = carry;  // n + C * slack <= N * m
+  for (long long i = carry + tid; i < cap; i += 256) ids[i] = -1;
   __syncthreads();
   if (tid < kWave) {
     const int lane = tid;
@@ -259,7 +312,8 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
       if (valid) {
         const int rank = prefix_count(same);
         const int pos = cursor[c] + rank;
-        ids[pos] = i;
+        ids[pos] = i / m;                       // entries of one token are adjacent: ascending ids per list
+        if (alt) alt[pos] = a[i ^ 1];           // m == 2: the token's other list
         if (rank == __popcll(same) - 1) cursor[c] = pos + 1;
       }
     }
@@ -300,7 +354,7 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
 
   const int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
   const int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * C : nullptr;
-  for (int c = tid; c <= C; c += 256) loff[c] = min(max(off[c], 0), p.N);
+  for (int c = tid; c <= C; c += 256) loff[c] = min(max(off[c], 0), p.n_entries);
   for (int c = tid; c < C; c += 256) lmask[c] = 0u;
   __syncthreads();
   // rows of list c: its whole range, or (dynamic index) the valid front part
@@ -387,6 +441,8 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     if (p.rows_out && lane == 0) p.rows_out[static_cast<long long>(b) * p.Hkv * G + qh] = rows;
   }
   __syncthreads();
+  if (p.lmask_out)  // the chosen lists' head masks, for the gather's duplicate test
+    for (int c = tid; c < C; c += 256) p.lmask_out[static_cast<long long>(bg) * C + c] = lmask[c];
 
   int4* seg = p.seg + static_cast<long long>(bg) * p.smax;
   int carry = 0, uniq = 0;
@@ -540,10 +596,14 @@ hipError_t launch_assign(const AssignParams& p, int dtype, float* norms, hipStre
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((p.n_assign + kMfmaKb - 1) / kMfmaKb, p.B * p.Hkv);
-    hipLaunchKernelGGL(assign_mfma_kernel, grid, dim3(kMfmaWaves * kWave), 0, s, p, static_cast<const float*>(norms));
+    if (p.m == 2)
+      hipLaunchKernelGGL(assign_mfma_kernel<2>, grid, dim3(kMfmaWaves * kWave), 0, s, p, static_cast<const float*>(norms));
+    else
+      hipLaunchKernelGGL(assign_mfma_kernel<1>, grid, dim3(kMfmaWaves * kWave), 0, s, p, static_cast<const float*>(norms));
   } else {
     dim3 grid((p.n_assign + 255) / 256, p.B * p.Hkv);
-    hipLaunchKernelGGL(assign_kernel<float>, grid, dim3(256), 0, s, p);
+    if (p.m == 2) hipLaunchKernelGGL((assign_kernel<float, 2>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((assign_kernel<float, 1>), grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

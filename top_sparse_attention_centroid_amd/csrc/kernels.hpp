@@ -47,9 +47,10 @@ struct AssignParams {
   const void* keys;        // [B][N][Hkv][d]
   const void* centroids;   // [Bc][Hkv][C][d]
   long long cent_bstride;  // elements between request codebooks (0 = shared)
-  int32_t* assign;         // [B][Hkv][N]
+  int32_t* assign;         // [B][Hkv][N][m]: the key's m nearest centroids, nearest first
   int B, N, Hkv, C;
   int n_assign;            // keys 0 .. n_assign-1 of every request are assigned
+  int m;                   // assignments per key (1 or 2)
 };
 // norms: workspace for |c|^2 of every centroid row (bf16 path)
 hipError_t launch_assign(const AssignParams& p, int dtype, float* norms, hipStream_t s);
@@ -59,9 +60,11 @@ struct CsrParams {
   int32_t* offsets;        // [B][Hkv][C+1]: list c owns ids[offsets[c] .. offsets[c+1])
   int32_t* ids;            // [B][Hkv][N]; free entries are -1
   int32_t* lens;           // [B][Hkv][C] valid entries per list, or null
+  int32_t* alt;            // [B][Hkv][N*m] (m == 2): each entry's other list, or null
   int B, N, Hkv, C;
   int n_assign;            // tokens 0 .. n_assign-1 go into the lists
   int slack;               // free entries after every list
+  int m;                   // lists per token (ids and alt hold N * m entries)
 };
 hipError_t launch_csr(const CsrParams& p, hipStream_t s);
 
@@ -81,6 +84,8 @@ struct SelectParams {
   int cosine;              // score q.c / |c| instead of q.c
   int n_sink, n_window;    // token ranges attended beside the lists
   const int32_t* lengths;  // [B] current length per request, or null (N)
+  int n_entries;           // list entries per (request, KV head): N, or N * m with m lists per token
+  uint32_t* lmask_out;     // [B][Hkv][C] head mask of every chosen list, or null
 };
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s);
 
@@ -119,6 +124,9 @@ struct GatherParams {
   float* partial;          // [B*Hkv][smax][G][kPartStride]
   int n_sink, n_window;    // explicit plans: list rows inside these ranges are skipped
   const int32_t* lengths;  // [B] or null (n_rows)
+  const int32_t* alt;      // explicit plans over 2-way lists: each entry's other list, or null
+  const uint32_t* lmask;   // [B*Hkv][C] head masks of the chosen lists (with alt)
+  int C;                   // lists per (request, KV head) (with alt)
   float* out;              // [B][Hq][d]
   int B, Hkv, smax, W;     // W: workgroups per (request, KV head)
   float qscale;            // log2(e) / sqrt(d)
