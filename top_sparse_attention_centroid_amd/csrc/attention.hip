@@ -91,7 +91,7 @@ struct Batch {
 // rejected id load row 0 of the request (always in bounds) and are masked at
 // scoring. Without control flow around the loads the compiler keeps all of
 // them in flight (a predicated load would force a wait for every earlier one).
-template <bool STREAM, typename T, int U>
+template <bool STREAM, bool DUP = false, typename T, int U>
 __device__ __forceinline__ void issue_batch(Batch<T, U>& bt, const int* ids, int base, int cnt, int r,
                                             const T* kb, const T* vb, long long row_stride,
                                             const uint32_t* dup = nullptr, int h = 0) {
@@ -101,7 +101,8 @@ __device__ __forceinline__ void issue_batch(Batch<T, U>& bt, const int* ids, int
     const int j = base + u * 4 + r;
     const int id = ids[min(j, kSegRows - 1)];
     // dup: heads that attend this token through another (lower) chosen list
-    const bool twice = dup ? ((dup[min(j, kSegRows - 1)] >> h) & 1u) : false;
+    bool twice = false;
+    if constexpr (DUP) twice = (dup[min(j, kSegRows - 1)] >> h) & 1u;
     bt.valid[u] = (j < cnt) & (id >= 0) & !twice;
     row[u] = bt.valid[u] ? id : 0;
   }
@@ -160,10 +161,10 @@ __device__ __forceinline__ void consume_batch(const Batch<T, U>& bt, HeadState& 
 // four lane groups then merge and lanes 0..15 write the head's partial state.
 // For each query head in `mask`: one pass over the segment's rows, then the
 // four 16-lane row groups merge and lanes 0..15 write the head's partial.
-template <bool STREAM, typename T>
+template <bool STREAM, bool DUP, typename T>
 __device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int cnt, int r, int e, const T* kb,
                                             const T* vb, long long row_stride, const T* qs, float qscale,
-                                            float* part, const uint32_t* dup = nullptr) {
+                                            float* part, const uint32_t* dup) {
   for (uint32_t hm = mask; hm != 0u; hm &= hm - 1u) {
     const int h = __builtin_ctz(hm);
     QFrag<T> qf;
@@ -172,11 +173,11 @@ __device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int c
     st.init();
 #if TSA_GATHER_PIPE
     Batch<T> A, Bb;
-    issue_batch<STREAM>(A, ids, 0, cnt, r, kb, vb, row_stride, dup, h);
+    issue_batch<STREAM, DUP>(A, ids, 0, cnt, r, kb, vb, row_stride, dup, h);
     for (int base = 0; base < cnt; base += 2 * kBatchRows) {
-      issue_batch<STREAM>(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride, dup, h);
+      issue_batch<STREAM, DUP>(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(A, st, qf, qscale);
-      issue_batch<STREAM>(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride, dup, h);
+      issue_batch<STREAM, DUP>(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(Bb, st, qf, qscale);
     }
 #elif TSA_GATHER_TAIL
@@ -184,18 +185,18 @@ __device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int c
     int base = 0;
     for (; base + kBatchRows / 2 < cnt; base += kBatchRows) {
       Batch<T> A;
-      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
+      issue_batch<STREAM, DUP>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(A, st, qf, qscale);
     }
     if (base < cnt) {
       Batch<T, kGatherUnroll / 2> A;
-      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
+      issue_batch<STREAM, DUP>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(A, st, qf, qscale);
     }
 #else
     for (int base = 0; base < cnt; base += kBatchRows) {
       Batch<T> A;
-      issue_batch<STREAM>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
+      issue_batch<STREAM, DUP>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(A, st, qf, qscale);
     }
 #endif
@@ -297,12 +298,13 @@ __device__ __forceinline__ void all_heads_pass(const int* ids, int cnt, int r, i
   }
 }
 
-template <typename T, int G, bool EXPLICIT>
+// DUP: explicit plans over 2-way lists, with per-row duplicate head masks
+template <typename T, int G, bool EXPLICIT, bool DUP>
 __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC void gather_attn_kernel(GatherParams p) {
   constexpr int NW = gather_waves<EXPLICIT>();
   __shared__ __align__(16) T qs[G * kHeadDim];
   __shared__ int ids_lds[NW][kSegRows];
-  __shared__ uint32_t dup_lds[EXPLICIT ? NW : 1][EXPLICIT ? kSegRows : 1];
+  __shared__ uint32_t dup_lds[DUP ? NW : 1][DUP ? kSegRows : 1];
   const int bg = blockIdx.x / p.W, w0 = blockIdx.x % p.W;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
 
@@ -385,11 +387,11 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
   };
   // 2-way lists: a token sits in two lists; for each head the entry of the
   // lower chosen list is the one attended (per-row duplicate head masks)
-  const bool two_way = EXPLICIT && p.alt != nullptr;
-  uint32_t* dup = two_way ? dup_lds[EXPLICIT ? wave : 0] : nullptr;
+  constexpr bool two_way = DUP;
+  uint32_t* dup = DUP ? dup_lds[DUP ? wave : 0] : nullptr;
   const int32_t* altb = two_way ? p.alt + b * p.rid_bstride + g * p.rid_gstride : nullptr;
   auto stage_dup = [&](const Seg& sg) {
-    if (!two_way) return;
+    if constexpr (!DUP) return;
     for (int j = lane; j < sg.cnt; j += kWave) {
       uint32_t dm = 0u;
       if (!sg.direct) {
@@ -461,9 +463,9 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
       // every head of the group reads these rows: score them for all heads at once
       all_heads_pass<G>(ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
     } else if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u) {
-      head_passes<true>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);
+      head_passes<true, DUP>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);
     } else {
-      head_passes<false>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);
+      head_passes<false, DUP>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);
     }
     // the next segment overwrites this wave's id staging area
     __builtin_amdgcn_wave_barrier();
@@ -551,25 +553,27 @@ __global__ __launch_bounds__(512) void combine_kernel(GatherParams p) {
   *reinterpret_cast<float2*>(o) = make_float2(O0 * inv, O1 * inv);
 }
 
-template <typename T, bool EXPLICIT>
+template <typename T, bool EXPLICIT, bool DUP>
 static void gather_dispatch(const GatherParams& p, int G, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(p.B * p.Hkv * p.W)), block(gather_waves<EXPLICIT>() * kWave);
   switch (G) {
-    case 1: hipLaunchKernelGGL((gather_attn_kernel<T, 1, EXPLICIT>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gather_attn_kernel<T, 2, EXPLICIT>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((gather_attn_kernel<T, 4, EXPLICIT>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((gather_attn_kernel<T, 8, EXPLICIT>), grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((gather_attn_kernel<T, 1, EXPLICIT, DUP>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gather_attn_kernel<T, 2, EXPLICIT, DUP>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gather_attn_kernel<T, 4, EXPLICIT, DUP>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((gather_attn_kernel<T, 8, EXPLICIT, DUP>), grid, block, 0, s, p); break;
   }
 }
 
 hipError_t launch_gather(const GatherParams& p, int dtype, int G, bool explicit_plan,
                          hipStream_t s) {
   if (dtype == kBF16) {
-    if (explicit_plan) gather_dispatch<bf16_t, true>(p, G, s);
-    else gather_dispatch<bf16_t, false>(p, G, s);
+    if (explicit_plan && p.alt) gather_dispatch<bf16_t, true, true>(p, G, s);
+    else if (explicit_plan) gather_dispatch<bf16_t, true, false>(p, G, s);
+    else gather_dispatch<bf16_t, false, false>(p, G, s);
   } else {
-    if (explicit_plan) gather_dispatch<float, true>(p, G, s);
-    else gather_dispatch<float, false>(p, G, s);
+    if (explicit_plan && p.alt) gather_dispatch<float, true, true>(p, G, s);
+    else if (explicit_plan) gather_dispatch<float, true, false>(p, G, s);
+    else gather_dispatch<float, false, false>(p, G, s);
   }
   return hipGetLastError();
 }
