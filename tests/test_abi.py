@@ -55,6 +55,16 @@ def test_workspace_sizes_and_validation(lib):
     n = B.workspace_bytes(B.OP_SPARSE_DECODE, d, 16)
     G, smax = 4, 4 * 16 + 32768 // 256
     assert n >= 64 * 8 * smax * G * 132 * 4
+    # 512 groups fill the chip with 256-row plan segments: no finer cut (128-row
+    # segments would need this many partial states)
+    assert n < 64 * 8 * (4 * 16 + 32768 // 128) * G * 132 * 4
+    # one request with 100-row lists: 8 groups x 40 lists would give 320 waves, so
+    # lists are cut into 32-row segments (the shortest), and the scores get a
+    # buffer of their own
+    one = B.IvfDesc(1, 100_000, 8, 32, 128, 1000, 0, B.TSA_BF16)
+    n1 = B.workspace_bytes(B.OP_SPARSE_DECODE, one, 10)
+    assert n1 >= 8 * (4 * 10 + 100_000 // 32) * G * 132 * 4 + 8 * G * 1000 * 4
+    assert n1 < 8 * (4 * 10 + 100_000 // 16) * G * 132 * 4
     assert B.workspace_bytes(B.OP_INDEX_BUILD, d) >= 64 * 8 * 32768 * 4
     with pytest.raises(B.TsaError, match="INVALID_ARG"):
         B.workspace_bytes(B.OP_SPARSE_DECODE, d, 0)

@@ -167,3 +167,65 @@ def test_karat_shape_full_size():
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     ref = _check_index(p, [0], offsets, ids)
     _decode_and_check(cfg, p, ref, [0], steps=2)
+
+
+@pytest.mark.parametrize("C,k", [(300, 10), (300, 64), (300, 100), (1000, 10)])
+def test_top_k_paths_and_ties(C, k):
+    """Selections through every search of the k-th largest score: the short
+    candidate search (k <= 64, several keys per lane), its fallback when more
+    than 64 keys reach the candidate bound (an all-zero query ties every
+    list), and the full search (k > 64). Bit-exact against the oracle's top-k,
+    ties to the lower list id; outputs against the oracle."""
+    cfg = W.config(1, batch=2, n_tokens=8000, n_kv_heads=2, n_q_heads=8, n_centroids=C, top_k=k, steps=1,
+                   shared_codebook=True, seed=31)
+    announce(f"ivf top-k paths C={C} k={k}")
+    p = _problem(cfg)
+    offsets, ids = tsa.index_build(p["keys"], p["centroids"])
+    ref = _check_index(p, range(cfg.batch), offsets, ids)
+    q = conditioned_ivf_queries(cfg, p["centroids"], 1)[0].clone()
+    zero = {(0, 1), (1, 6)}
+    for b, h in zero:
+        q[b, h] = 0
+    B, Hq, G = cfg.batch, cfg.n_q_heads, cfg.group
+    sel = torch.empty((B, Hq, k), dtype=torch.int32, device=DEV)
+    out = tsa.sparse_decode(q, p["centroids"], offsets, ids, p["keys"], p["values"], k, sel_out=sel)
+    torch.cuda.synchronize()
+    q64, c64, K, V = f64(q), f64(p["centroids"]), f64(p["keys"]), f64(p["values"])
+    sel_g, out_g = sel.cpu().numpy(), out.cpu().numpy()
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            r = ivf.decode_head(q64[b, h], c64[0, g], ref[b][0][g], ref[b][1][g], K[b, :, g], V[b, :, g], k)
+            if (b, h) in zero:
+                assert np.array_equal(sel_g[b, h], np.arange(k)), "all-equal scores must take the lowest list ids"
+            assert np.array_equal(sel_g[b, h], r.lists), f"selection differs (request {b}, head {h})"
+            assert out_error(out_g[b, h], r.out) <= OUT_TOL
+
+
+def test_split_and_fused_scoring_choose_the_same_lists():
+    """Small batches score the centroids in a launch of their own, large ones
+    inside the selection kernel; both run the same per-tile contraction, so a
+    request selects the same lists either way (and both outputs match the
+    oracle)."""
+    cfg = W.config(2, batch=16, n_tokens=2048, n_centroids=200, top_k=12, steps=1)  # 128 groups: fused
+    announce("ivf split vs fused scoring")
+    p = _problem(cfg)
+    offsets, ids = tsa.index_build(p["keys"], p["centroids"])
+    q = conditioned_ivf_queries(cfg, p["centroids"], 1)[0].clone()
+    q[1, 3] = 0  # every list ties: the candidate search falls back to the full one
+    B, Hq, k = cfg.batch, cfg.n_q_heads, cfg.top_k
+    sel_big = torch.empty((B, Hq, k), dtype=torch.int32, device=DEV)
+    out_big = tsa.sparse_decode(q, p["centroids"], offsets, ids, p["keys"], p["values"], k, sel_out=sel_big)
+    n = 2  # 16 groups: split
+    sel_small = torch.empty((n, Hq, k), dtype=torch.int32, device=DEV)
+    out_small = tsa.sparse_decode(q[:n].contiguous(), p["centroids"], offsets[:n].contiguous(), ids[:n].contiguous(),
+                                  p["keys"][:n].contiguous(), p["values"][:n].contiguous(), k, sel_out=sel_small)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_small, sel_big[:n])
+    assert np.array_equal(sel_big[1, 3].cpu().numpy(), np.arange(k))
+    ref = _check_index(p, [0], offsets, ids)
+    r = ivf.sparse_decode(f64(q[0:1]), f64(p["centroids"]), ref[0][0][None], ref[0][1][None],
+                          f64(p["keys"][0:1]), f64(p["values"][0:1]), k)
+    assert np.array_equal(sel_small[0].cpu().numpy(), r["sel"][0])
+    assert out_error(out_small[0].cpu().numpy(), r["out"][0]) <= OUT_TOL
+    assert out_error(out_big[0].cpu().numpy(), r["out"][0]) <= OUT_TOL

@@ -490,15 +490,25 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
-// combine: one wave per query head. Lanes read 64 segment descriptors and
+// combine: NS waves per query head. Wave `part` of head h takes the head's
+// segments part, part + NS, ...; its lanes read 64 segment descriptors and
 // partial (m, l) at once, so the log-sum-exp weights come from two wave
-// reductions; the o vectors of the head's segments are then accumulated with
-// four independent loads in flight per lane.
-template <int G, bool EXPLICIT>
-__global__ __launch_bounds__(512) void combine_kernel(GatherParams p) {
+// reductions; the o vectors are then accumulated with eight independent
+// loads in flight per lane. With NS > 1 (small batches, where the merge is
+// a chain of round trips) the descriptors and (m, l) are requested together
+// and the NS partial states of a head are merged through LDS in a fixed
+// order; with NS = 1 (large batches) only the head's own (m, l) are read.
+constexpr int kCombineWavesSmall = 16;  // waves per workgroup when the batch is small
+
+template <int G, int NS, bool EXPLICIT>
+__global__ __launch_bounds__(G * NS * kWave) void combine_kernel(GatherParams p) {
+  constexpr int kU = 8;
+  __shared__ float sm_m[G][NS], sm_l[G][NS];
+  __shared__ float2 sm_o[NS > 1 ? G : 1][NS > 1 ? NS : 1][kWave];
   const int bg = blockIdx.x;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
-  const int h = threadIdx.x / kWave, lane = lane_id();
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int h = wave / NS, part = wave % NS;
   int nseg;
   if constexpr (EXPLICIT) {
     nseg = p.nseg[bg];
@@ -508,15 +518,32 @@ __global__ __launch_bounds__(512) void combine_kernel(GatherParams p) {
   }
   float M = kEmptyMax, L = 0.f, O0 = 0.f, O1 = 0.f;
   const float* base = p.partial + static_cast<long long>(bg) * p.smax * G * kPartStride + h * kPartStride;
-  for (int s0 = 0; s0 < nseg; s0 += kWave) {
-    const int s = s0 + lane;
-    bool mine = s < nseg;
-    if constexpr (EXPLICIT) {
-      if (mine) mine = (static_cast<uint32_t>(p.seg[static_cast<long long>(bg) * p.smax + s].z) >> h) & 1u;
+  const int n_mine = nseg > part ? (nseg - part + NS - 1) / NS : 0;  // segments part + i * NS
+  for (int i0 = 0; i0 < n_mine; i0 += kWave) {
+    const int s = part + (i0 + lane) * NS;
+    const bool in_range = i0 + lane < n_mine;
+    // descriptor and partial (m, l) requested together; the (m, l) of a
+    // segment whose mask leaves this head out are never written and never used
+    const float* ph = base + static_cast<long long>(in_range ? s : 0) * G * kPartStride;
+    float pm = kMaskedScore, pl = 0.f;
+    bool mine = in_range;
+    if constexpr (NS > 1) {
+      const float pm_raw = ph[0], pl_raw = ph[1];
+      if constexpr (EXPLICIT) {
+        const int z = p.seg[static_cast<long long>(bg) * p.smax + (in_range ? s : 0)].z;
+        mine = mine && ((static_cast<uint32_t>(z) >> h) & 1u);
+      }
+      pm = mine ? pm_raw : kMaskedScore;
+      pl = mine ? pl_raw : 0.f;
+    } else {
+      if constexpr (EXPLICIT) {
+        if (mine) mine = (static_cast<uint32_t>(p.seg[static_cast<long long>(bg) * p.smax + s].z) >> h) & 1u;
+      }
+      if (mine) {
+        pm = ph[0];
+        pl = ph[1];
+      }
     }
-    const float* ph = base + static_cast<long long>(s) * G * kPartStride;
-    const float pm = mine ? ph[0] : kMaskedScore;
-    const float pl = mine ? ph[1] : 0.f;
     const float Mn = fmaxf(M, wave_max_f(pm));
     const float w = mine ? fast_exp2(pm - Mn) : 0.f;
     const float a = fast_exp2(M - Mn);
@@ -526,26 +553,49 @@ __global__ __launch_bounds__(512) void combine_kernel(GatherParams p) {
     M = Mn;
     uint64_t bal = __ballot(mine);
     while (bal) {
-      int j[4];
-      float wj[4];
-      float2 po[4];
+      int j[kU];
+      float wj[kU];
+      float2 po[kU];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kU; ++u) {
         j[u] = bal ? __builtin_ctzll(bal) : -1;
         if (bal) bal &= bal - 1;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int jj = j[u] < 0 ? 0 : j[u];  // j < 0: reload segment s0 (in range), weight 0
+      for (int u = 0; u < kU; ++u) {
+        const int jj = j[u] < 0 ? 0 : j[u];  // j < 0: reload segment `part` (in range), weight 0
         wj[u] = j[u] < 0 ? 0.f : __shfl(w, jj);
-        po[u] = *reinterpret_cast<const float2*>(base + static_cast<long long>(s0 + jj) * G * kPartStride +
-                                                 4 + lane * 2);
+        po[u] = *reinterpret_cast<const float2*>(
+            base + static_cast<long long>(j[u] < 0 ? part : part + (i0 + jj) * NS) * G * kPartStride + 4 + lane * 2);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kU; ++u) {
         O0 = fmaf(wj[u], po[u].x, O0);
         O1 = fmaf(wj[u], po[u].y, O1);
       }
+    }
+  }
+  if constexpr (NS > 1) {
+    if (lane == 0) {
+      sm_m[h][part] = M;
+      sm_l[h][part] = L;
+    }
+    sm_o[h][part][lane] = make_float2(O0, O1);
+    __syncthreads();
+    if (part != 0) return;
+    M = kEmptyMax;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) M = fmaxf(M, sm_m[h][j]);
+    L = 0.f;
+    O0 = 0.f;
+    O1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float a = fast_exp2(sm_m[h][j] - M);
+      const float2 o = sm_o[h][j][lane];
+      L = fmaf(sm_l[h][j], a, L);
+      O0 = fmaf(o.x, a, O0);
+      O1 = fmaf(o.y, a, O1);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -578,14 +628,28 @@ hipError_t launch_gather(const GatherParams& p, int dtype, int G, bool explicit_
   return hipGetLastError();
 }
 
+template <int G, int NS, bool EXPLICIT>
+static void combine_launch(const GatherParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((combine_kernel<G, NS, EXPLICIT>), dim3(static_cast<unsigned>(p.B * p.Hkv)),
+                     dim3(G * NS * kWave), 0, s, p);
+}
+
+// One wave per head once the batch alone gives every CU a few waves;
+// otherwise kCombineWavesSmall waves per workgroup.
+template <int G, bool EXPLICIT>
+static void combine_dispatch_g(const GatherParams& p, hipStream_t s) {
+  constexpr int NS = kCombineWavesSmall / G > 1 ? kCombineWavesSmall / G : 1;
+  if (static_cast<long long>(p.B) * p.Hkv * G >= 1024) combine_launch<G, 1, EXPLICIT>(p, s);
+  else combine_launch<G, NS, EXPLICIT>(p, s);
+}
+
 template <bool EXPLICIT>
 static void combine_dispatch(const GatherParams& p, int G, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(p.B * p.Hkv)), block(G * kWave);
   switch (G) {
-    case 1: hipLaunchKernelGGL((combine_kernel<1, EXPLICIT>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((combine_kernel<2, EXPLICIT>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((combine_kernel<4, EXPLICIT>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((combine_kernel<8, EXPLICIT>), grid, block, 0, s, p); break;
+    case 1: combine_dispatch_g<1, EXPLICIT>(p, s); break;
+    case 2: combine_dispatch_g<2, EXPLICIT>(p, s); break;
+    case 4: combine_dispatch_g<4, EXPLICIT>(p, s); break;
+    default: combine_dispatch_g<8, EXPLICIT>(p, s); break;
   }
 }
 

@@ -99,22 +99,66 @@ FetchParams fetch_params(const tsa_cache_desc& d, const int32_t* miss_tok, const
 
 // ----------------------------------------------------------------- layouts
 struct IvfLayout {
-  int G = 0, smax = 0;
-  size_t seg = 0, nseg = 0, partial = 0, lmask = 0, total = 0;
+  int G = 0, smax = 0, seg_rows = 0;
+  bool split_score = false;
+  size_t seg = 0, nseg = 0, partial = 0, lmask = 0, keys = 0, total = 0;
 };
+
+// Centroid scoring runs as its own launch (one wave per 16 centroids) when
+// the batch has fewer (request, KV head) groups than this: one select
+// workgroup per group would read the whole codebook through a few CUs.
+// bf16 data only.
+#ifndef TSA_SPLIT_SCORE_BELOW
+#define TSA_SPLIT_SCORE_BELOW 128
+#endif
+constexpr long long kSplitScoreBelow = TSA_SPLIT_SCORE_BELOW;
+
+// Plan segments expected for one chosen list with `rows`-row segments: its
+// average length N * m / C in segments, rounded, plus room for a ragged tail.
+int ivf_list_segs(const tsa_ivf_desc& d, int m, int rows) {
+  const long long avg_list = static_cast<long long>(d.n_tokens) * m / d.n_centroids;
+  return std::max(1, static_cast<int>((2LL * avg_list + rows) / (2 * rows)) + (avg_list > rows / 2 ? 1 : 0));
+}
+
+// Rows per plan segment of an inverted-index decode: the longest of 256,
+// 128, 64, 32 rows for which the batch still expects kMinIvfSegments
+// segments (one wave each, 8 per CU). Large batches keep 256-row segments
+// and write the fewest partial states; a single request cuts its lists finer
+// so that enough waves stream rows at once. A segment count bound per
+// (request, KV head) keeps the worst-case workspace of long contexts in check.
+#ifndef TSA_MIN_IVF_SEGS
+#define TSA_MIN_IVF_SEGS 2048
+#endif
+constexpr long long kMinIvfSegments = TSA_MIN_IVF_SEGS;
+constexpr int kIvfMinSegRows = 32;
+constexpr long long kIvfMaxPlanSegs = 16384;
+int ivf_seg_rows(const tsa_ivf_desc& d, int k, int m) {
+  const long long bh = static_cast<long long>(d.batch) * d.n_kv_heads;
+  const long long gk = static_cast<long long>(d.n_q_heads / d.n_kv_heads) * k;
+  const long long entries = static_cast<long long>(d.n_tokens) * m;
+  int r = kSegRows;
+  while (r > kIvfMinSegRows && bh * gk * ivf_list_segs(d, m, r) < kMinIvfSegments &&
+         (entries + r / 2 - 1) / (r / 2) <= kIvfMaxPlanSegs)
+    r >>= 1;
+  return r;
+}
 
 // with_fixed: room for the sink / window segments of tsa_sparse_decode_ex;
 // m: lists per token (2: twice the list entries and the chosen-list masks)
 IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false, int m = 1) {
   IvfLayout L;
   L.G = d.n_q_heads / d.n_kv_heads;
-  L.smax = L.G * k + ceil_div(d.n_tokens * m, kSegRows) + (with_fixed ? kMaxFixedRows / kSegRows + 2 : 0);
+  L.seg_rows = ivf_seg_rows(d, k, m);
+  L.smax = L.G * k + ceil_div(static_cast<long long>(d.n_tokens) * m, L.seg_rows) +
+           (with_fixed ? kMaxFixedRows / L.seg_rows + 2 : 0);
   const size_t bh = static_cast<size_t>(d.batch) * d.n_kv_heads;
   size_t off = 0;
   L.seg = off;    off += align_up(bh * L.smax * sizeof(int4));
   L.nseg = off;   off += align_up(bh * sizeof(int32_t));
   L.partial = off; off += align_up(bh * L.smax * L.G * kPartStride * sizeof(float));
   L.lmask = off;   off += m > 1 ? align_up(bh * d.n_centroids * sizeof(uint32_t)) : 0;
+  L.split_score = d.dtype == TSA_BF16 && static_cast<long long>(bh) < kSplitScoreBelow;
+  L.keys = off;    off += L.split_score ? align_up(bh * L.G * d.n_centroids * sizeof(uint32_t)) : 0;
   L.total = off;
   return L;
 }
@@ -311,6 +355,8 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
     selp.lengths = opts->lengths;
   }
   if (m == 2) selp.lmask_out = reinterpret_cast<uint32_t*>(w + L.lmask);
+  selp.seg_rows = L.seg_rows;
+  if (L.split_score) selp.keys = reinterpret_cast<uint32_t*>(w + L.keys);
   hipError_t e = launch_ivf_select(selp, d.dtype, L.G, s);
   if (e != hipSuccess) return hip_fail(e, "ivf_select launch");
 
@@ -322,18 +368,15 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
   gp.counts = nullptr; gp.count_const = 0;
   gp.partial = reinterpret_cast<float*>(w + L.partial); gp.out = out;
   gp.B = d.batch; gp.Hkv = d.n_kv_heads; gp.smax = L.smax;
-  // expected segments: per chosen list of the group, its average length
-  // N / C in 256-row segments (rounded up, with room for a ragged tail), plus
-  // the sink / window segments
-  const long long avg_list = static_cast<long long>(d.n_tokens) * m / d.n_centroids;
-  const int per_list = std::max(1, static_cast<int>((2LL * avg_list + kSegRows) / (2 * kSegRows)) +
-                                       (avg_list > kSegRows / 2 ? 1 : 0));
+  // expected segments: those of every chosen list of the group, plus the
+  // sink / window segments
   int fixed_segs = 0;
   if (opts) {
-    fixed_segs = ceil_div(std::min(opts->n_sink, d.n_tokens), kSegRows) +
-                 ceil_div(std::min(opts->n_window, d.n_tokens), kSegRows) + (opts->n_window > 0 ? 1 : 0);
+    fixed_segs = ceil_div(std::min(opts->n_sink, d.n_tokens), L.seg_rows) +
+                 ceil_div(std::min(opts->n_window, d.n_tokens), L.seg_rows) + (opts->n_window > 0 ? 1 : 0);
   }
-  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k * per_list + fixed_segs), true); gp.seg_rows = kSegRows;
+  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k * ivf_list_segs(d, m, L.seg_rows) + fixed_segs), true);
+  gp.seg_rows = L.seg_rows;
   gp.qscale = qscale(d.head_dim);
   if (opts) {
     gp.n_sink = opts->n_sink;

@@ -4,6 +4,8 @@
 //
 // [KARAT] = paper-daily digest "Heterogeneous LLM Serving with General-Purpose
 // Processing-Near-Memory for Retrieval-Based Sparse Attention".
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -325,9 +327,11 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 // KV group, fused in one workgroup (4 waves) per (request, KV head).
 //
 // Scoring ([KARAT] worked example, step 3): s[h][c] = q[h] . centroid[g][c],
-// raw dot product in fp32; 16 lanes cover one 128-element centroid row (8
-// elements each) and reduce through DPP, four rows per wave load. Scores go to
-// LDS as order-preserving keys, next to the list offsets.
+// raw dot product with fp32 accumulation. bf16 data runs it on matrix cores
+// (score_lists_mfma below); fp32 data on the vector units, 16 lanes per
+// 128-element centroid row (8 elements each) reduced through DPP, four rows
+// per wave load. Scores go to LDS as order-preserving keys, next to the list
+// offsets.
 //
 // Top-k ([KARAT] How: the top-k most similar lists): wave w owns query heads
 // w, w + 4 of the group and holds that head's keys in registers, KPL per lane
@@ -337,8 +341,84 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 // emitted in ascending order through ballot prefix counts.
 //
 // Plan: the union of the group's chosen lists with a head bitmask per list,
-// each list cut into segments of at most kSegRows rows, ascending list order.
+// each list cut into segments of at most seg_rows rows, ascending list order.
 // ============================================================================
+// Scores of one KV group as a dense contraction on matrix cores: 16x16x32
+// bf16 MFMAs, fp32 accumulation. The A operand holds the group's query heads
+// in rows 0..G-1 (rows G..15 repeat head G-1 and are dropped); each
+// 16-centroid B tile is read straight from memory, since every centroid row
+// is used once per group. The calling wave scores tiles [t_begin, t_end),
+// kSelTiles of them in flight. Lane l of a result tile holds centroid l % 16
+// for heads (l / 16) * 4 .. +4; the order key of s[h][c] goes to
+// keys[h * C + c]. Cosine scaling divides by |c|, summed from the same B
+// fragments (each lane squares 32 of the row's elements; the four lanes of a
+// column add theirs).
+constexpr int kSelTiles = 8;
+
+template <int G>
+__device__ __forceinline__ void score_tiles_mfma(const SelectParams& p, int b, int g, int t_begin, int t_end,
+                                                 uint32_t* keys) {
+  const int C = p.C;
+  const int lane = lane_id(), col = lane & 15, grp = lane >> 4;
+  const bf16_t* qr = static_cast<const bf16_t*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim +
+                     min(col, G - 1) * kHeadDim + grp * 8;
+  bf16x8_t a[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8_t*>(qr + ks * 32);
+  const bf16_t* cb = static_cast<const bf16_t*>(p.centroids) + b * p.cent_bstride +
+                     static_cast<long long>(g) * C * kHeadDim + grp * 8;
+  for (int t0 = t_begin; t0 < t_end; t0 += kSelTiles) {
+    bf16x8_t bt[kSelTiles][4];
+#pragma unroll
+    for (int u = 0; u < kSelTiles; ++u) {
+      if (t0 + u < t_end) {
+        const bf16_t* row = cb + static_cast<long long>(min((t0 + u) * 16 + col, C - 1)) * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) bt[u][ks] = *reinterpret_cast<const bf16x8_t*>(row + ks * 32);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSelTiles; ++u) {
+      if (t0 + u >= t_end) break;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bt[u][ks], acc, 0, 0, 0);
+      float inv = 1.f;
+      if (p.cosine) {  // q.c / |c| (1/|q| ranks nothing differently)
+        float n2 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          Raw8<bf16_t> r;
+          r.v = __builtin_bit_cast(uint4, bt[u][ks]);
+          n2 += sq8(r);
+        }
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
+      }
+      const int c = (t0 + u) * 16 + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = grp * 4 + i;
+        if (h < G && c < C) keys[h * C + c] = order_key(acc[i] * inv);
+      }
+    }
+  }
+}
+
+// Scoring as its own launch, for batches too small to fill the chip with one
+// workgroup per (request, KV head): grid (ceil(C / 64), B * Hkv), each wave
+// one 16-centroid tile, keys to p.keys.
+template <int G>
+__global__ __launch_bounds__(256) void centroid_score_kernel(SelectParams p) {
+  const int bg = blockIdx.y;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int t = blockIdx.x * 4 + static_cast<int>(threadIdx.x) / kWave;
+  const int ntile = (p.C + 15) / 16;
+  if (t >= ntile) return;  // uniform over the wave
+  score_tiles_mfma<G>(p, b, g, t, t + 1, p.keys + static_cast<long long>(bg) * G * p.C);
+}
+
 template <typename T, int G, int KPL>
 __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   extern __shared__ uint32_t smem[];
@@ -347,6 +427,7 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   uint32_t* lmask = smem + G * C;                     // [C]
   int* loff = reinterpret_cast<int*>(smem + (G + 1) * C);  // [C+1], clamped to [0, N]
   __shared__ int scan_scratch[4];
+  __shared__ uint32_t cand_lds[4][kWave];
   const int bg = blockIdx.x;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -356,6 +437,22 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   const int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * C : nullptr;
   for (int c = tid; c <= C; c += 256) loff[c] = min(max(off[c], 0), p.n_entries);
   for (int c = tid; c < C; c += 256) lmask[c] = 0u;
+  if (p.keys) {  // scored by centroid_score_kernel: staged beside the offsets, 16 loads in flight
+    const uint32_t* kg = p.keys + static_cast<long long>(bg) * G * C;
+    for (int i0 = 0; i0 < G * C; i0 += 16 * 256) {
+      uint32_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = i0 + u * 256 + tid;
+        v[u] = i < G * C ? kg[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = i0 + u * 256 + tid;
+        if (i < G * C) keys[i] = v[u];
+      }
+    }
+  }
   __syncthreads();
   // rows of list c: its whole range, or (dynamic index) the valid front part
   auto list_len = [&](int c) {
@@ -363,7 +460,13 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     return lens ? min(max(lens[c], 0), range) : range;
   };
 
-  {
+  if (p.keys) {
+    // scored by centroid_score_kernel
+  } else if constexpr (std::is_same<T, bf16_t>::value) {
+    const int ntile = (C + 15) / 16;
+    const int per_wave = (ntile + 3) / 4;
+    score_tiles_mfma<G>(p, b, g, wave * per_wave, min(ntile, (wave + 1) * per_wave), keys);
+  } else {
     const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
     QFrag<T> qf[G];
 #pragma unroll
@@ -406,13 +509,57 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
       const int c = j * kWave + lane;
       kk[j] = c < C ? kh[c] : 0u;
     }
+    // thr = the k-th largest key: the largest t with #{keys >= t} >= k, found
+    // bit by bit. With several keys per lane the search first runs over a
+    // short candidate list: the k-th largest of the 64 lane maxima, t1, has
+    // at least k keys at or above it, so thr >= t1 and every key >= thr is
+    // among the keys >= t1. When at most 64 keys pass that bound they are
+    // compacted to LDS, one per lane, and the search over them gives the same
+    // thr; otherwise it runs over all keys.
     uint32_t thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      int cnt = 0;
+    bool found = false;
+    if (KPL > 1 && k <= kWave) {
+      uint32_t lmax = kk[0];
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(kk[j] >= cand));
-      if (cnt >= k) thr = cand;
+      for (int j = 1; j < KPL; ++j) lmax = max(lmax, kk[j]);
+      uint32_t t1 = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = t1 | (1u << bit);
+        if (__popcll(__ballot(lmax >= cand)) >= k) t1 = cand;
+      }
+      int n_cand = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) n_cand += __popcll(__ballot(kk[j] >= t1));
+      if (n_cand <= kWave) {
+        uint32_t* cl = cand_lds[wave];
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const bool in = kk[j] >= t1;
+          const uint64_t m = __ballot(in);
+          if (in) cl[base + prefix_count(m)] = kk[j];
+          base += __popcll(m);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint32_t x = lane < n_cand ? cl[lane] : 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = thr | (1u << bit);
+          if (__popcll(__ballot(x >= cand)) >= k) thr = cand;
+        }
+        found = true;
+        __builtin_amdgcn_wave_barrier();  // the next head of this wave reuses cl
+      }
+    }
+    if (!found) {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(kk[j] >= cand));
+        if (cnt >= k) thr = cand;
+      }
     }
     int n_gt = 0;
 #pragma unroll
@@ -444,23 +591,30 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   if (p.lmask_out)  // the chosen lists' head masks, for the gather's duplicate test
     for (int c = tid; c < C; c += 256) p.lmask_out[static_cast<long long>(bg) * C + c] = lmask[c];
 
+  // thread t plans lists [t * per, (t + 1) * per): one block scan of the
+  // per-thread segment counts places every list's segments in list order
   int4* seg = p.seg + static_cast<long long>(bg) * p.smax;
-  int carry = 0, uniq = 0;
-  for (int c0 = 0; c0 < C; c0 += 256) {
-    const int c = c0 + tid;
-    const uint32_t m = c < C ? lmask[c] : 0u;
-    const int start = c < C ? loff[c] : 0;
-    const int len = c < C ? list_len(c) : 0;
-    const int nsg = (m != 0u && len > 0) ? (len + kSegRows - 1) / kSegRows : 0;
-    uniq += m != 0u ? len : 0;
-    int tot;
-    const int pos = carry + block_exclusive_scan<4>(nsg, scan_scratch, &tot);
-    for (int j = 0; j < nsg; ++j) {
-      if (pos + j < p.smax)
-        seg[pos + j] = make_int4(start + j * kSegRows, min(kSegRows, len - j * kSegRows),
-                                 static_cast<int>(m), c);
+  const int sr = min(max(p.seg_rows, 1), kSegRows);
+  const int per = (C + 255) / 256;
+  const int c_lo = tid * per, c_hi = min(C, c_lo + per);
+  int my_segs = 0, uniq = 0;
+  for (int c = c_lo; c < c_hi; ++c) {
+    const int len = list_len(c);
+    if (lmask[c] != 0u && len > 0) {
+      my_segs += (len + sr - 1) / sr;
+      uniq += len;
     }
-    carry += tot;
+  }
+  int carry;
+  int pos = block_exclusive_scan<4>(my_segs, scan_scratch, &carry);
+  for (int c = c_lo; c < c_hi; ++c) {
+    const uint32_t m = lmask[c];
+    const int len = list_len(c);
+    if (m == 0u || len <= 0) continue;
+    const int start = loff[c];
+    for (int j = 0; j * sr < len; ++j, ++pos) {
+      if (pos < p.smax) seg[pos] = make_int4(start + j * sr, min(sr, len - j * sr), static_cast<int>(m), c);
+    }
   }
   // Fixed token ranges attended beside the lists by every head of the group
   // (the first n_sink tokens and the last n_window before the request's
@@ -470,12 +624,12 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     const int L = p.lengths ? min(max(p.lengths[b], 0), p.N) : p.N;
     const int sink_hi = min(p.n_sink, L);
     const int win_lo = p.n_window > 0 ? max(L - p.n_window, sink_hi) : L;
-    const int nsink = (sink_hi + kSegRows - 1) / kSegRows;
-    const int nwin = (L - win_lo + kSegRows - 1) / kSegRows;
+    const int nsink = (sink_hi + sr - 1) / sr;
+    const int nwin = (L - win_lo + sr - 1) / sr;
     const int all = (1 << G) - 1;
     for (int j = tid; j < nsink + nwin; j += 256) {
-      const int start = j < nsink ? j * kSegRows : win_lo + (j - nsink) * kSegRows;
-      const int cnt = min(kSegRows, (j < nsink ? sink_hi : L) - start);
+      const int start = j < nsink ? j * sr : win_lo + (j - nsink) * sr;
+      const int cnt = min(sr, (j < nsink ? sink_hi : L) - start);
       if (carry + j < p.smax) seg[carry + j] = make_int4(start, cnt, all, -1);
     }
     carry += nsink + nwin;
@@ -639,7 +793,23 @@ static void select_dispatch(const SelectParams& p, int G, size_t lds, hipStream_
   else select_dispatch_g<T, kMaxCentroids / 64>(p, G, lds, s);
 }
 
+template <int G>
+static void score_dispatch_g(const SelectParams& p, hipStream_t s) {
+  const dim3 grid((p.C + 63) / 64, p.B * p.Hkv);
+  hipLaunchKernelGGL(centroid_score_kernel<G>, grid, dim3(256), 0, s, p);
+}
+
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s) {
+  if (p.keys) {  // bf16 only (checked by the caller)
+    switch (G) {
+      case 1: score_dispatch_g<1>(p, s); break;
+      case 2: score_dispatch_g<2>(p, s); break;
+      case 4: score_dispatch_g<4>(p, s); break;
+      default: score_dispatch_g<8>(p, s); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const size_t lds = (static_cast<size_t>(G + 1) * p.C + p.C + 1) * sizeof(uint32_t);
   if (dtype == kBF16) select_dispatch<bf16_t>(p, G, lds, s);
   else select_dispatch<float>(p, G, lds, s);

@@ -86,6 +86,9 @@ struct SelectParams {
   const int32_t* lengths;  // [B] current length per request, or null (N)
   int n_entries;           // list entries per (request, KV head): N, or N * m with m lists per token
   uint32_t* lmask_out;     // [B][Hkv][C] head mask of every chosen list, or null
+  int seg_rows;            // rows per plan segment (<= kSegRows)
+  uint32_t* keys;          // [B*Hkv][G][C] order keys of the scores, computed by centroid_score_kernel
+                           // (bf16 only), or null: the select kernel scores the centroids itself
 };
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s);
 
