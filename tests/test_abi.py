@@ -192,3 +192,29 @@ def test_binding_refuses_host_tensors():
     c = torch.zeros((1, 1, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device tensor"):
         B.index_build(x, c)
+
+
+def _ivf_ws(B_, N, Hkv, Hq, C, k, rows, split):
+    """Workspace bytes of a plain sparse decode whose lists are cut into
+    `rows`-row plan segments (layout: descriptors, counts, partial states,
+    score keys when scoring is its own launch; each region 256-B aligned)."""
+    def al(x):
+        return (x + 255) // 256 * 256
+    G, bh = Hq // Hkv, B_ * Hkv
+    smax = G * k + -(-N // rows)
+    return al(bh * smax * 16) + al(bh * 4) + al(bh * smax * G * 132 * 4) + (al(bh * G * C * 4) if split else 0)
+
+
+@pytest.mark.parametrize("k,rows", [(8, 64), (12, 128), (16, 256)])
+def test_plan_segment_length_follows_the_expected_wave_count(lib, k, rows):
+    # 2 requests x 8 KV heads, lists of ~200 rows (N / C): the longest segment
+    # length for which 16 groups x 4k lists give >= 2048 segments
+    d = B.IvfDesc(2, 6400, 8, 32, 128, 32, 1, B.TSA_BF16)
+    assert B.workspace_bytes(B.OP_SPARSE_DECODE, d, k) == _ivf_ws(2, 6400, 8, 32, 32, k, rows, split=True)
+
+
+def test_plan_segment_length_at_the_benchmark_shapes(lib):
+    big = B.IvfDesc(64, 32768, 8, 32, 128, 256, 1, B.TSA_BF16)
+    assert B.workspace_bytes(B.OP_SPARSE_DECODE, big, 16) == _ivf_ws(64, 32768, 8, 32, 256, 16, 256, split=False)
+    one = B.IvfDesc(1, 100_000, 8, 32, 128, 1000, 0, B.TSA_BF16)
+    assert B.workspace_bytes(B.OP_SPARSE_DECODE, one, 10) == _ivf_ws(1, 100_000, 8, 32, 1000, 10, 32, split=True)

@@ -229,3 +229,16 @@ def test_split_and_fused_scoring_choose_the_same_lists():
     assert np.array_equal(sel_small[0].cpu().numpy(), r["sel"][0])
     assert out_error(out_small[0].cpu().numpy(), r["out"][0]) <= OUT_TOL
     assert out_error(out_big[0].cpu().numpy(), r["out"][0]) <= OUT_TOL
+
+
+@pytest.mark.parametrize("k", [8, 12, 16])
+def test_plan_segment_lengths(k):
+    """2 requests x 8 KV heads with ~200-row lists: k = 8, 12, 16 cut the lists
+    into 64-, 128- and 256-row plan segments (several per list, ragged tails).
+    Selections, row counts and outputs against the oracle."""
+    cfg = W.config(2, batch=2, n_tokens=6400, n_centroids=32, top_k=k, steps=1, seed=41 + k)
+    announce(f"ivf plan segments k={k}")
+    p = _problem(cfg)
+    offsets, ids = tsa.index_build(p["keys"], p["centroids"])
+    ref = _check_index(p, range(cfg.batch), offsets, ids)
+    _decode_and_check(cfg, p, ref, range(cfg.batch), steps=1)
