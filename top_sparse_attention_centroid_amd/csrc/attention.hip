@@ -38,7 +38,7 @@ constexpr int kSegsPerWave = kGatherSegsPerWave;    // segments a wave is planne
 #define TSA_GATHER_TAIL 0  // 1: a half-size batch for the last rows of a segment
 #endif
 #ifndef TSA_GATHER_FULLMASK_ALL
-#define TSA_GATHER_FULLMASK_ALL 1  // explicit segments read by two or more heads: one all-heads pass
+#define TSA_GATHER_FULLMASK_ALL 1  // explicit segments read by every head (or, with multi_all, two or more): one all-heads pass
 #endif
 #ifndef TSA_GATHER_WAVES_PER_EU
 #define TSA_GATHER_WAVES_PER_EU 0
@@ -154,9 +154,10 @@ __device__ __forceinline__ void consume_batch(const Batch<T, U>& bt, HeadState& 
 // uneven segments across CUs. Per segment: row ids -> wave-private LDS in one
 // round trip; then, for each query head in the segment's mask, one pass over
 // the rows in batches of kBatchRows (16 lanes per row, all loads of a batch in
-// flight together); segments that two or more heads read take one all-heads
-// pass instead (every row loaded once). With 2-way lists a second head's pass
-// re-reads the rows the first pass just brought into L2. The four lane groups
+// flight together); segments that every head reads (in large batches, two or
+// more heads) take one all-heads pass instead (every row loaded once).
+// Otherwise a second head's pass re-reads the rows the first pass just
+// brought into L2. The four lane groups
 // then merge and lanes 0..15 write the head's partial state.
 // For each query head in `mask`: one pass over the segment's rows, then the
 // four 16-lane row groups merge and lanes 0..15 write the head's partial.
@@ -457,12 +458,18 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
 
     float* part = p.partial + (static_cast<long long>(bg) * p.smax + s) * G * kPartStride;
     // Rows read by one head stream past the caches in that head's pass. Rows
-    // that two or more heads read are loaded once, also non-temporally, and
-    // scored for every head of the group in one pass; the partial states of
-    // heads outside the mask are written and never merged. (2-way lists keep
-    // per-head passes: their duplicate masks differ per head, and the second
-    // pass re-reads the rows from L2.)
-    if (!EXPLICIT || (TSA_GATHER_FULLMASK_ALL && G > 1 && (mask & (mask - 1u)) != 0u && !two_way)) {
+    // that every head of the group reads are loaded once and scored for all
+    // heads in one pass; with multi_all (large batches, bound by bandwidth)
+    // so are rows that two or more heads read, the partial states of heads
+    // outside the mask being written and never merged. Otherwise such rows
+    // stay cacheable, one pass per head, the later passes hitting L2: a
+    // small batch is bound by the latency of its waves, which the extra
+    // heads' arithmetic would lengthen. (2-way lists keep per-head passes:
+    // their duplicate masks differ per head.)
+    const bool all_heads =
+        !EXPLICIT || (TSA_GATHER_FULLMASK_ALL && G > 1 && !two_way &&
+                      (mask == (1u << G) - 1u || (p.multi_all && (mask & (mask - 1u)) != 0u)));
+    if (all_heads) {
       all_heads_pass<G>(ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
     } else if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u) {
       head_passes<true, DUP>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);

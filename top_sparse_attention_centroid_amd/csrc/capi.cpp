@@ -100,18 +100,20 @@ FetchParams fetch_params(const tsa_cache_desc& d, const int32_t* miss_tok, const
 // ----------------------------------------------------------------- layouts
 struct IvfLayout {
   int G = 0, smax = 0, seg_rows = 0;
-  bool split_score = false;
+  bool small_batch = false, split_score = false;
   size_t seg = 0, nseg = 0, partial = 0, lmask = 0, keys = 0, total = 0;
 };
 
-// Centroid scoring runs as its own launch (one wave per 16 centroids) when
-// the batch has fewer (request, KV head) groups than this: one select
-// workgroup per group would read the whole codebook through a few CUs.
-// bf16 data only.
-#ifndef TSA_SPLIT_SCORE_BELOW
-#define TSA_SPLIT_SCORE_BELOW 128
+// A batch with fewer (request, KV head) groups than this is small: its decode
+// is bound by the latency of a few workgroups rather than by bandwidth. Then
+// centroid scoring runs as its own launch (one wave per 16 centroids; bf16
+// data), since one select workgroup per group would read the whole codebook
+// through a few CUs; and list segments that several heads chose get one
+// cacheable pass per head instead of one all-heads pass.
+#ifndef TSA_SMALL_BATCH_GROUPS
+#define TSA_SMALL_BATCH_GROUPS 128
 #endif
-constexpr long long kSplitScoreBelow = TSA_SPLIT_SCORE_BELOW;
+constexpr long long kSmallBatchGroups = TSA_SMALL_BATCH_GROUPS;
 
 // Plan segments expected for one chosen list with `rows`-row segments: its
 // average length N * m / C in segments, rounded, plus room for a ragged tail.
@@ -157,7 +159,8 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false, int 
   L.nseg = off;   off += align_up(bh * sizeof(int32_t));
   L.partial = off; off += align_up(bh * L.smax * L.G * kPartStride * sizeof(float));
   L.lmask = off;   off += m > 1 ? align_up(bh * d.n_centroids * sizeof(uint32_t)) : 0;
-  L.split_score = d.dtype == TSA_BF16 && static_cast<long long>(bh) < kSplitScoreBelow;
+  L.small_batch = static_cast<long long>(bh) < kSmallBatchGroups;
+  L.split_score = d.dtype == TSA_BF16 && L.small_batch;
   L.keys = off;    off += L.split_score ? align_up(bh * L.G * d.n_centroids * sizeof(uint32_t)) : 0;
   L.total = off;
   return L;
@@ -377,6 +380,7 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
   }
   gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k * ivf_list_segs(d, m, L.seg_rows) + fixed_segs), true);
   gp.seg_rows = L.seg_rows;
+  gp.multi_all = L.small_batch ? 0 : 1;
   gp.qscale = qscale(d.head_dim);
   if (opts) {
     gp.n_sink = opts->n_sink;

@@ -328,17 +328,19 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 //
 // Scoring ([KARAT] worked example, step 3): s[h][c] = q[h] . centroid[g][c],
 // raw dot product with fp32 accumulation. bf16 data runs it on matrix cores
-// (score_lists_mfma below); fp32 data on the vector units, 16 lanes per
-// 128-element centroid row (8 elements each) reduced through DPP, four rows
-// per wave load. Scores go to LDS as order-preserving keys, next to the list
-// offsets.
+// (score_tiles_mfma below), inside this workgroup or, for small batches, in
+// centroid_score_kernel beforehand; fp32 data on the vector units, 16 lanes
+// per 128-element centroid row (8 elements each) reduced through DPP, four
+// rows per wave load. Scores go to LDS as order-preserving keys, next to the
+// list offsets.
 //
 // Top-k ([KARAT] How: the top-k most similar lists): wave w owns query heads
 // w, w + 4 of the group and holds that head's keys in registers, KPL per lane
 // (C <= 64 * KPL). The k-th largest key T is found bit by bit (MSB first)
-// with ballot counts; keys above it are taken, then keys equal to it in
-// ascending list order until k are taken (ties -> lower list id). Lists are
-// emitted in ascending order through ballot prefix counts.
+// with ballot counts, over a short candidate list when one suffices (see the
+// kernel); keys above it are taken, then keys equal to it in ascending list
+// order until k are taken (ties -> lower list id). Lists are emitted in
+// ascending order through ballot prefix counts.
 //
 // Plan: the union of the group's chosen lists with a head bitmask per list,
 // each list cut into segments of at most seg_rows rows, ascending list order.
@@ -428,6 +430,7 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   int* loff = reinterpret_cast<int*>(smem + (G + 1) * C);  // [C+1], clamped to [0, N]
   __shared__ int scan_scratch[4];
   __shared__ uint32_t cand_lds[4][kWave];
+  __shared__ int cand_list_lds[4][kWave];
   const int bg = blockIdx.x;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -514,10 +517,14 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     // short candidate list: the k-th largest of the 64 lane maxima, t1, has
     // at least k keys at or above it, so thr >= t1 and every key >= thr is
     // among the keys >= t1. When at most 64 keys pass that bound they are
-    // compacted to LDS, one per lane, and the search over them gives the same
-    // thr; otherwise it runs over all keys.
+    // compacted to LDS with their list ids, one per lane in ascending list
+    // order; the search over them gives the same thr, and the lists are
+    // emitted from them in one pass. Otherwise search and emission run over
+    // all keys.
     uint32_t thr = 0;
     bool found = false;
+    uint32_t x = 0u;  // compacted candidate key of this lane (0: none)
+    int xc = 0;       // its list
     if (KPL > 1 && k <= kWave) {
       uint32_t lmax = kk[0];
 #pragma unroll
@@ -532,18 +539,23 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
       for (int j = 0; j < KPL; ++j) n_cand += __popcll(__ballot(kk[j] >= t1));
       if (n_cand <= kWave) {
         uint32_t* cl = cand_lds[wave];
+        int* cli = cand_list_lds[wave];
         int base = 0;
 #pragma unroll
         for (int j = 0; j < KPL; ++j) {
           const bool in = kk[j] >= t1;
           const uint64_t m = __ballot(in);
-          if (in) cl[base + prefix_count(m)] = kk[j];
+          if (in) {
+            cl[base + prefix_count(m)] = kk[j];
+            cli[base + prefix_count(m)] = j * kWave + lane;
+          }
           base += __popcll(m);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint32_t x = lane < n_cand ? cl[lane] : 0u;
+        x = lane < n_cand ? cl[lane] : 0u;
+        xc = lane < n_cand ? cli[lane] : 0;
         for (int bit = 31; bit >= 0; --bit) {
           const uint32_t cand = thr | (1u << bit);
           if (__popcll(__ballot(x >= cand)) >= k) thr = cand;
@@ -561,28 +573,42 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
         if (cnt >= k) thr = cand;
       }
     }
-    int n_gt = 0;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) n_gt += __popcll(__ballot(kk[j] > thr));
-    const int need_eq = k - n_gt;
     const int qh = g * G + h;
     int32_t* sel = p.sel_out ? p.sel_out + (static_cast<long long>(b) * p.Hkv * G + qh) * k : nullptr;
-    int base = 0, eq_seen = 0, rows = 0;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const int c = j * kWave + lane;
-      const bool gt = kk[j] > thr;
-      const bool eq = kk[j] == thr;
-      const uint64_t eqm = __ballot(eq);
-      const bool take = gt || (eq && eq_seen + prefix_count(eqm) < need_eq);
+    int rows = 0;
+    if (found) {
+      // thr >= t1 > 0, so lanes without a candidate (x = 0) take nothing
+      const int need_eq = k - __popcll(__ballot(x > thr));
+      const bool eq = x == thr;
+      const bool take = x > thr || (eq && prefix_count(__ballot(eq)) < need_eq);
       const uint64_t tm = __ballot(take);
       if (take) {
-        if (sel) sel[base + prefix_count(tm)] = c;
-        atomicOr(&lmask[c], 1u << h);
-        rows += list_len(c);
+        if (sel) sel[prefix_count(tm)] = xc;
+        atomicOr(&lmask[xc], 1u << h);
+        rows = list_len(xc);
       }
-      base += __popcll(tm);
-      eq_seen += __popcll(eqm);
+    } else {
+      int n_gt = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) n_gt += __popcll(__ballot(kk[j] > thr));
+      const int need_eq = k - n_gt;
+      int base = 0, eq_seen = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int c = j * kWave + lane;
+        const bool gt = kk[j] > thr;
+        const bool eq = kk[j] == thr;
+        const uint64_t eqm = __ballot(eq);
+        const bool take = gt || (eq && eq_seen + prefix_count(eqm) < need_eq);
+        const uint64_t tm = __ballot(take);
+        if (take) {
+          if (sel) sel[base + prefix_count(tm)] = c;
+          atomicOr(&lmask[c], 1u << h);
+          rows += list_len(c);
+        }
+        base += __popcll(tm);
+        eq_seen += __popcll(eqm);
+      }
     }
     rows = wave_sum_i(rows);
     if (p.rows_out && lane == 0) p.rows_out[static_cast<long long>(b) * p.Hkv * G + qh] = rows;

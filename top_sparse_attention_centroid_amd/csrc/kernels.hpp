@@ -130,6 +130,7 @@ struct GatherParams {
   const int32_t* alt;      // explicit plans over 2-way lists: each entry's other list, or null
   const uint32_t* lmask;   // [B*Hkv][C] head masks of the chosen lists (with alt)
   int C;                   // lists per (request, KV head) (with alt)
+  int multi_all;           // explicit plans: segments chosen by two or more heads take one all-heads pass
   float* out;              // [B][Hq][d]
   int B, Hkv, smax, W;     // W: workgroups per (request, KV head)
   float qscale;            // log2(e) / sqrt(d)
