@@ -242,3 +242,19 @@ def test_plan_segment_lengths(k):
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     ref = _check_index(p, range(cfg.batch), offsets, ids)
     _decode_and_check(cfg, p, ref, range(cfg.batch), steps=1)
+
+
+@pytest.mark.parametrize("dtype,G,C,k", [("bf16", 4, 2048, 10), ("bf16", 4, 2048, 100), ("bf16", 8, 1500, 12),
+                                         ("f32", 2, 1200, 8)])
+def test_large_codebooks(dtype, G, C, k):
+    """Codebooks above 1024 centroids (64 keys per lane in the selection),
+    with k on both sides of the 64-key candidate bound; bf16 scores on
+    matrix cores, fp32 on the vector units. Index, selections, row counts and
+    outputs against the oracle."""
+    cfg = W.config(1, batch=2, n_tokens=20_000, n_kv_heads=2, n_q_heads=2 * G, n_centroids=C, top_k=k,
+                   dtype=dtype, steps=1, shared_codebook=False, seed=51 + k)
+    announce(f"ivf large codebook dtype={dtype} G={G} C={C} k={k}")
+    p = _problem(cfg)
+    offsets, ids = tsa.index_build(p["keys"], p["centroids"])
+    ref = _check_index(p, range(cfg.batch), offsets, ids)
+    _decode_and_check(cfg, p, ref, range(cfg.batch), steps=1)
