@@ -499,25 +499,28 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
-// combine: NS waves per query head. Wave `part` of head h takes the head's
-// segments part, part + NS, ...; its lanes read 64 segment descriptors and
-// partial (m, l) at once, so the log-sum-exp weights come from two wave
-// reductions; the o vectors are then accumulated with eight independent
-// loads in flight per lane. With NS > 1 (small batches, where the merge is
-// a chain of round trips) the descriptors and (m, l) are requested together
-// and the NS partial states of a head are merged through LDS in a fixed
-// order; with NS = 1 (large batches) only the head's own (m, l) are read.
-constexpr int kCombineWavesSmall = 16;  // waves per workgroup when the batch is small
+// combine: a workgroup merges GH query heads of one (request, KV head), NS
+// waves per head. Wave `part` of head h takes the head's segments part,
+// part + NS, ...; its lanes read 64 segment descriptors and partial (m, l)
+// at once, so the log-sum-exp weights come from two wave reductions; the o
+// vectors are then accumulated with eight independent loads in flight per
+// lane. Large batches run GH = G heads with one wave each and read only the
+// head's own (m, l). Small batches, where the merge is a chain of round
+// trips, run one head per workgroup with kCombineWavesSmall waves: the
+// descriptors and (m, l) are requested together, and the NS partial states
+// of the head are merged through LDS in a fixed order.
+constexpr int kCombineWavesSmall = 16;  // waves per head when the batch is small
 
-template <int G, int NS, bool EXPLICIT>
-__global__ __launch_bounds__(G * NS * kWave) void combine_kernel(GatherParams p) {
+template <int G, int GH, int NS, bool EXPLICIT>
+__global__ __launch_bounds__(GH * NS * kWave) void combine_kernel(GatherParams p) {
   constexpr int kU = 8;
-  __shared__ float sm_m[G][NS], sm_l[G][NS];
-  __shared__ float2 sm_o[NS > 1 ? G : 1][NS > 1 ? NS : 1][kWave];
-  const int bg = blockIdx.x;
+  __shared__ float sm_m[GH][NS], sm_l[GH][NS];
+  __shared__ float2 sm_o[NS > 1 ? GH : 1][NS > 1 ? NS : 1][kWave];
+  const int bg = blockIdx.x / (G / GH);
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int h = wave / NS, part = wave % NS;
+  const int hl = wave / NS, part = wave % NS;           // head within the workgroup
+  const int h = (blockIdx.x % (G / GH)) * GH + hl;      // head within the group
   int nseg;
   if constexpr (EXPLICIT) {
     nseg = p.nseg[bg];
@@ -586,23 +589,23 @@ __global__ __launch_bounds__(G * NS * kWave) void combine_kernel(GatherParams p)
   }
   if constexpr (NS > 1) {
     if (lane == 0) {
-      sm_m[h][part] = M;
-      sm_l[h][part] = L;
+      sm_m[hl][part] = M;
+      sm_l[hl][part] = L;
     }
-    sm_o[h][part][lane] = make_float2(O0, O1);
+    sm_o[hl][part][lane] = make_float2(O0, O1);
     __syncthreads();
     if (part != 0) return;
     M = kEmptyMax;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) M = fmaxf(M, sm_m[h][j]);
+    for (int j = 0; j < NS; ++j) M = fmaxf(M, sm_m[hl][j]);
     L = 0.f;
     O0 = 0.f;
     O1 = 0.f;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const float a = fast_exp2(sm_m[h][j] - M);
-      const float2 o = sm_o[h][j][lane];
-      L = fmaf(sm_l[h][j], a, L);
+      const float a = fast_exp2(sm_m[hl][j] - M);
+      const float2 o = sm_o[hl][j][lane];
+      L = fmaf(sm_l[hl][j], a, L);
       O0 = fmaf(o.x, a, O0);
       O1 = fmaf(o.y, a, O1);
     }
@@ -637,19 +640,24 @@ hipError_t launch_gather(const GatherParams& p, int dtype, int G, bool explicit_
   return hipGetLastError();
 }
 
-template <int G, int NS, bool EXPLICIT>
+template <int G, int GH, int NS, bool EXPLICIT>
 static void combine_launch(const GatherParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((combine_kernel<G, NS, EXPLICIT>), dim3(static_cast<unsigned>(p.B * p.Hkv)),
-                     dim3(G * NS * kWave), 0, s, p);
+  hipLaunchKernelGGL((combine_kernel<G, GH, NS, EXPLICIT>), dim3(static_cast<unsigned>(p.B * p.Hkv * (G / GH))),
+                     dim3(GH * NS * kWave), 0, s, p);
 }
 
-// One wave per head once the batch alone gives every CU a few waves;
-// otherwise kCombineWavesSmall waves per workgroup.
+// One wave per head once the batch alone gives every CU a few waves.
+// Otherwise several waves per head: a workgroup of kCombineWavesSmall waves
+// per head when each (request, KV head) has many segments (64 or more
+// planned), else the group's heads share one workgroup of
+// kCombineWavesSmall waves.
 template <int G, bool EXPLICIT>
 static void combine_dispatch_g(const GatherParams& p, hipStream_t s) {
-  constexpr int NS = kCombineWavesSmall / G > 1 ? kCombineWavesSmall / G : 1;
-  if (static_cast<long long>(p.B) * p.Hkv * G >= 1024) combine_launch<G, 1, EXPLICIT>(p, s);
-  else combine_launch<G, NS, EXPLICIT>(p, s);
+  constexpr int NS = kCombineWavesSmall / G;
+  const long long segs = static_cast<long long>(p.W) * (EXPLICIT ? kGatherWavesExplicit : kGatherWavesRows);
+  if (static_cast<long long>(p.B) * p.Hkv * G >= 1024) combine_launch<G, G, 1, EXPLICIT>(p, s);
+  else if (segs >= 64) combine_launch<G, 1, kCombineWavesSmall, EXPLICIT>(p, s);
+  else combine_launch<G, G, NS, EXPLICIT>(p, s);
 }
 
 template <bool EXPLICIT>
