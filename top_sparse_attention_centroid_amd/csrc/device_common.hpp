@@ -203,6 +203,40 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   return before + x - v;
 }
 
+// block_exclusive_scan of v that also returns the block total of u in the
+// same two barriers. `scratch` holds 2 * NW ints.
+template <int NW>
+__device__ __forceinline__ int block_exclusive_scan_and_sum(int v, int u, int* scratch, int* total_v,
+                                                            int* total_u) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) u += __shfl_xor(u, o);
+  if (lane == kWave - 1) {
+    scratch[wave] = x;
+    scratch[NW + wave] = u;
+  }
+  __syncthreads();
+  int before = 0, all = 0, all_u = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = scratch[w];
+    before += (w < wave) ? t : 0;
+    all += t;
+    all_u += scratch[NW + w];
+  }
+  __syncthreads();
+  *total_v = all;
+  *total_u = all_u;
+  return before + x - v;
+}
+
 template <int NW>
 __device__ __forceinline__ int block_sum(int v, int* scratch) {
   int total;

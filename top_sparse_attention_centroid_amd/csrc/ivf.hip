@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   uint32_t* keys = smem;                              // [G][C]
   uint32_t* lmask = smem + G * C;                     // [C]
   int* loff = reinterpret_cast<int*>(smem + (G + 1) * C);  // [C+1], clamped to [0, N]
-  __shared__ int scan_scratch[4];
+  __shared__ int scan_scratch[8];
   __shared__ uint32_t cand_lds[4][kWave];
   __shared__ int cand_list_lds[4][kWave];
   const int bg = blockIdx.x;
@@ -631,8 +631,8 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
       uniq += len;
     }
   }
-  int carry;
-  int pos = block_exclusive_scan<4>(my_segs, scan_scratch, &carry);
+  int carry, uniq_all;
+  int pos = block_exclusive_scan_and_sum<4>(my_segs, uniq, scan_scratch, &carry, &uniq_all);
   for (int c = c_lo; c < c_hi; ++c) {
     const uint32_t m = lmask[c];
     const int len = list_len(c);
@@ -660,10 +660,9 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     }
     carry += nsink + nwin;
   }
-  uniq = block_sum<4>(uniq, scan_scratch);
   if (tid == 0) {
     p.nseg[bg] = min(carry, p.smax);
-    if (p.uniq_out) p.uniq_out[bg] = uniq;
+    if (p.uniq_out) p.uniq_out[bg] = uniq_all;
   }
 }
 
