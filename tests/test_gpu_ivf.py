@@ -258,3 +258,31 @@ def test_large_codebooks(dtype, G, C, k):
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     ref = _check_index(p, range(cfg.batch), offsets, ids)
     _decode_and_check(cfg, p, ref, range(cfg.batch), steps=1)
+
+
+def test_split_and_fused_cosine_scores_choose_the_same_lists():
+    """Cosine scoring (q.c / |c|) inside the selection kernel (128 groups) and in
+    its own launch (16 groups) chooses the same lists for the same requests."""
+    cfg = W.config(2, batch=16, n_tokens=2048, n_centroids=200, top_k=12, steps=1, seed=7)
+    announce("ivf split vs fused cosine scoring")
+    p = _problem(cfg)
+    # centroids of very different norms, so cosine and dot rankings differ
+    scale = torch.exp(torch.linspace(-1.5, 1.5, cfg.n_centroids, device=DEV)).view(1, 1, -1, 1)
+    cent = (p["centroids"].float() * scale).to(p["centroids"].dtype)
+    offsets, ids = tsa.index_build(p["keys"], cent)
+    q = conditioned_ivf_queries(cfg, cent, 1)[0]
+    B, Hq, k = cfg.batch, cfg.n_q_heads, cfg.top_k
+    sel_big = torch.empty((B, Hq, k), dtype=torch.int32, device=DEV)
+    out_big = tsa.sparse_decode_ex(q, cent, offsets, ids, p["keys"], p["values"], k, similarity="cosine",
+                                   sel_out=sel_big)
+    n = 2
+    sel_small = torch.empty((n, Hq, k), dtype=torch.int32, device=DEV)
+    out_small = tsa.sparse_decode_ex(q[:n].contiguous(), cent, offsets[:n].contiguous(), ids[:n].contiguous(),
+                                     p["keys"][:n].contiguous(), p["values"][:n].contiguous(), k,
+                                     similarity="cosine", sel_out=sel_small)
+    sel_dot = torch.empty_like(sel_big)
+    tsa.sparse_decode(q, cent, offsets, ids, p["keys"], p["values"], k, sel_out=sel_dot)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_small, sel_big[:n])
+    assert not torch.equal(sel_big, sel_dot), "the scaled codebook should make cosine and dot choose differently"
+    assert out_error(out_small.cpu().numpy(), out_big[:n].cpu().numpy()) <= 1e-4
