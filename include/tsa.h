@@ -167,7 +167,11 @@ tsa_status tsa_index_build(const tsa_ivf_desc* desc, const void* keys, const voi
  *              whole KV group (the union over its query heads' lists)
  *   Workspace: tsa_workspace_bytes(TSA_OP_SPARSE_DECODE, desc, k, ...).
  *   Scores are fp32; the chosen lists equal the exact top-k whenever the
- *   k-th and (k+1)-th scores differ by more than fp32 rounding.
+ *   k-th and (k+1)-th scores differ by more than fp32 rounding. Results are
+ *   bitwise reproducible for a given desc and k. How the chosen rows are
+ *   grouped for the softmax merge depends on the batch shape, so one request
+ *   decoded within batches of different sizes selects the same lists and
+ *   gets outputs that agree to fp32 rounding.
  * ---------------------------------------------------------------------- */
 tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void* centroids,
                              const int32_t* offsets, const int32_t* ids, const void* k_cache,

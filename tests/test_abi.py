@@ -86,7 +86,7 @@ def test_workspace_sizes_and_validation(lib):
     with pytest.raises(B.TsaError, match="UNSUPPORTED"):
         B.workspace_bytes(B.OP_TOKEN_DECODE, B.TokenDesc(1, 4096 * 4096 + 1, 8, 32, 128, 64, 1), 4096)
     a = B.AttnDesc(32, 4096, 8, 32, 128, 2048, B.TSA_BF16)
-    # 32 x 8 row lists of 2048: 256-row segments (2048 of them), G = 4 partial states each
+    # 32 x 8 row lists of 2048 rows: 256-row segments (2048 of them), G = 4 partial states each
     assert B.workspace_bytes(B.OP_ATTEND_ROWS, a) == 32 * 8 * (2048 // 256) * 4 * 132 * 4
     small = B.AttnDesc(2, 4096, 8, 32, 128, 2048, B.TSA_BF16)   # few lists: 64-row segments
     assert B.workspace_bytes(B.OP_ATTEND_ROWS, small) == 2 * 8 * (2048 // 64) * 4 * 132 * 4

@@ -7,13 +7,14 @@
 // with the head mask of the GQA group's query heads that chose them, so a row
 // chosen by several heads of the group is read from HBM once. Each wave owns
 // whole segments: 16 lanes cover one 256-B bf16 row (16 B each), a wave load
-// instruction fetches 4 rows, and a batch of rows is in flight while the
-// previous batch is scored (double buffering in registers). Each lane group
-// keeps an online-softmax state (running max m, sum l, output o) in the log2
-// domain; the four lane groups merge by lane shuffles and the segment writes
-// one partial (m, l, o) per masked head.
-// combine: one wave per query head merges the partials of its segments with
-// the log-sum-exp rule and writes o / l (zero when nothing was selected).
+// instruction fetches 4 rows, and every load of a batch of rows is issued
+// before any arithmetic on it; latency is hidden by many resident waves.
+// Each lane group keeps an online-softmax state (running max m, sum l,
+// output o) in the log2 domain; the four lane groups merge by lane shuffles
+// and the segment writes one partial (m, l, o) per masked head.
+// combine: merges each query head's partials with the log-sum-exp rule (one
+// wave per head in large batches, several in small ones) and writes o / l
+// (zero when nothing was selected).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
