@@ -59,6 +59,12 @@ def parse():
                     help="inverted-index workloads: lists per key (2: every key joins its two nearest lists)")
     ap.add_argument("--window", type=int, default=0,
                     help="inverted-index workloads: trailing tokens always attended")
+    ap.add_argument("--popularity", type=float, default=0.0,
+                    help="hot-cache workload: selection trace with token popularity (standard deviation of "
+                         "the log-normal token weights; 0 = uniform draws)")
+    ap.add_argument("--recency", type=float, default=0.0,
+                    help="hot-cache workload: share of each step's new tokens drawn from tokens dropped within "
+                         "the last 8 steps (0 = none)")
     ap.add_argument("--layers", type=int, default=1,
                     help="hot-cache workload: a group of this many layers sharing each step's selection "
                          "(batch divided by the layer count, so host memory stays the same); the later "
@@ -566,6 +572,10 @@ def main():
 
     tsa.load()
     cfg = W.config(args.config)
+    if args.popularity or args.recency:
+        if cfg.kind != "cache":
+            sys.exit("bench: --popularity / --recency shape the hot-cache workload's selection trace")
+        cfg = cfg.replace(popularity_sd=args.popularity, recency=args.recency)
     kind = {"ivf": bench_ivf, "token": bench_token, "cache": bench_cache}[cfg.kind]
     res = kind(args, cfg, torch, tsa, W)
 
@@ -586,6 +596,8 @@ def main():
             workload += f"+sink{args.sink}+window{args.window}"
         if args.assign == 2:
             workload += "+two-lists-per-key"
+    if cfg.kind == "cache" and (cfg.popularity_sd or cfg.recency):
+        workload += f"+popularity{cfg.popularity_sd:g}+recency{cfg.recency:g}"
     if cfg.kind == "cache" and args.policy != "lru":
         workload += f"+{args.policy}"
     if cfg.kind == "cache" and args.layers > 1:

@@ -29,12 +29,17 @@ def _next_use_dense(trace_np, N):
     return out
 
 
+@pytest.mark.parametrize("locality", [False, True])
 @pytest.mark.parametrize("policy", ["fifo", "random", "belady"])
-def test_policy_matches_oracle(policy):
+def test_policy_matches_oracle(policy, locality):
+    """Uniform trace, and a trace with popularity and recency (returning
+    tokens, where the policies evict differently)."""
     steps = 10
     cfg = W.config(4, batch=3, n_tokens=4000, n_slots=400, top_k=256, overlap=170, steps=steps,
                    n_kv_heads=2, n_q_heads=8)
-    announce(f"resolve policy {policy}")
+    if locality:
+        cfg = cfg.replace(popularity_sd=2.0, recency=0.3)
+    announce(f"resolve policy {policy} locality={locality}")
     B, N, S, Hkv, d = cfg.batch, cfg.n_tokens, cfg.n_slots, cfg.n_kv_heads, cfg.head_dim
     prob = W.cache_problem(cfg, device=DEV)
     hk = tsa.HostArray((B, N, Hkv, d), cfg.torch_dtype)

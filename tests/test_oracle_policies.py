@@ -170,3 +170,24 @@ def test_layer_group_shares_tables_and_keeps_every_pool_exact():
             q = rng.standard_normal((Hq, d))
             direct = cache.attend_slots(q, hk, hv, sel)
             assert np.array_equal(cache.attend_slots(q, pk, pv, slots), direct)
+
+
+def test_a_trace_with_locality_orders_the_policies_as_real_selections_do():
+    """[HISPARSE-NEWS] ranks the policies by miss rate on real selection
+    traces: Belady (offline) lowest, then LRU, random, FIFO. A uniform
+    synthetic trace makes the online policies coincide (a dropped token is no
+    likelier to return than any other). With popular tokens that persist and
+    recently dropped tokens that return, the oracle gives the same order."""
+    from top_sparse_attention_centroid_amd import workloads as W
+
+    cfg = W.config(4, batch=1, n_tokens=16384, n_slots=512, top_k=256, overlap=218, steps=50,
+                   popularity_sd=2.0, recency=0.3)
+    tr = W.selection_trace(cfg).numpy()[:, 0]
+    nu = cache.next_use_table(tr)
+    rate = {}
+    for pol in ("lru", "fifo", "random", "belady"):
+        st = cache.CacheState(cfg.n_tokens, cfg.n_slots)
+        m = [cache.policy_step(st, sel, t, pol, seed=0x5EED, request=0, next_use=nu[t])[2] for t, sel in enumerate(tr)]
+        rate[pol] = np.mean(m[1:]) / cfg.top_k
+    assert rate["belady"] < rate["lru"] < rate["random"] < rate["fifo"], rate
+

@@ -1,5 +1,6 @@
 """The seeded input generators: determinism, shapes and the trace's overlap."""
 
+import numpy as np
 import torch
 
 from top_sparse_attention_centroid_amd import workloads as W
@@ -63,3 +64,27 @@ def test_token_problem_plants_tokens():
     assert q_idx.shape == (2, 2, 64) and q.shape == (2, 2, 32, 128)
     s = (p["k_idx"][0].float() @ q_idx[0, 0].float())
     assert s[p["planted"][0]].min() > s.median() + 50
+
+
+def test_locality_trace_keeps_the_overlap_and_returns_dropped_tokens():
+    cfg = W.config(4, batch=2, n_tokens=6000, top_k=300, overlap=255, steps=30, popularity_sd=2.0, recency=0.3)
+    tr = W.selection_trace(cfg).numpy()
+    assert np.array_equal(tr, W.selection_trace(cfg).numpy())  # seeded
+    returned = 0
+    for b in range(cfg.batch):
+        seen_dropped = set()
+        for t in range(tr.shape[0]):
+            row = tr[t, b]
+            assert np.all(np.diff(row) > 0) and row.min() >= 0 and row.max() < cfg.n_tokens
+            if t:
+                prev = tr[t - 1, b]
+                assert len(np.intersect1d(row, prev)) == cfg.overlap
+                new = np.setdiff1d(row, prev)
+                returned += len(np.intersect1d(new, np.fromiter(seen_dropped, dtype=np.int64)))
+                seen_dropped |= set(np.setdiff1d(prev, row).tolist())
+    # about 30 % of the 45 new tokens per step come back from recent drops
+    assert returned >= 0.25 * 45 * (tr.shape[0] - 2) * cfg.batch
+    # the uniform generator is untouched by the new fields' defaults
+    base = W.config(4, batch=1, n_tokens=3000, top_k=200, overlap=170, steps=4)
+    assert base.popularity_sd == 0 and base.recency == 0
+

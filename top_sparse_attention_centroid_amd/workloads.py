@@ -99,6 +99,13 @@ class WorkloadConfig:
     # hierarchical cache workload
     n_slots: int = 0
     overlap: int = 0
+    # selection-trace locality (0 = uniform draws): token popularity
+    # (standard deviation of the log-normal weights) and recency (the share
+    # of each step's new tokens drawn from tokens dropped within the last
+    # recency_window steps)
+    popularity_sd: float = 0.0
+    recency: float = 0.0
+    recency_window: int = 8
 
     @property
     def group(self) -> int:
@@ -286,6 +293,8 @@ def selection_trace(cfg: WorkloadConfig, steps: Optional[int] = None) -> torch.T
     Drawn on the CPU so the trace is the same whatever device consumes it.
     """
     steps = cfg.steps if steps is None else steps
+    if cfg.popularity_sd > 0 or cfg.recency > 0:
+        return _selection_trace_local(cfg, steps)
     B, N, k, keep = cfg.batch, cfg.n_tokens, cfg.top_k, cfg.overlap
     assert 0 <= keep <= k <= N
     g = _gen(cfg.seed, "trace", "cpu")
@@ -300,6 +309,55 @@ def selection_trace(cfg: WorkloadConfig, steps: Optional[int] = None) -> torch.T
             pool = torch.randperm(N, generator=g)
             fresh = pool[~taken[pool]][: k - keep]
             cur = torch.cat([kept, fresh]).sort().values
+            out[t, b] = cur.to(torch.int32)
+    return out
+
+
+def _selection_trace_local(cfg: WorkloadConfig, steps: int) -> torch.Tensor:
+    """A selection trace with the locality of real ones: popular tokens stay
+    selected longer and come back more often, and recently dropped tokens
+    return. Every token of a request has a fixed log-normal weight
+    exp(popularity_sd * z). Step 0 draws k tokens without replacement with
+    probability proportional to the weights; step t+1 keeps ``overlap`` of
+    step t's tokens the same way, then draws round(recency * (k - overlap))
+    new tokens, by weight, from the tokens dropped within the last
+    ``recency_window`` steps (as many as there are), and the rest by weight
+    from every token step t did not select. Consecutive steps share exactly
+    ``overlap`` tokens. Weighted draws use Gumbel top-m (log-weight plus
+    standard Gumbel noise, the m largest). Drawn on the CPU in fp64.
+    """
+    B, N, k, keep = cfg.batch, cfg.n_tokens, cfg.top_k, cfg.overlap
+    assert 0 <= keep <= k <= N and 0.0 <= cfg.recency <= 1.0 and cfg.recency_window >= 1
+    g = _gen(cfg.seed, "trace", "cpu")
+    out = torch.empty((steps, B, k), dtype=torch.int32)
+    never = -(1 << 62)
+    for b in range(B):
+        lw = cfg.popularity_sd * torch.randn(N, generator=g, dtype=torch.float64)
+
+        def draw(idx, m):
+            if m <= 0:
+                return idx[:0]
+            u = torch.rand(idx.numel(), generator=g, dtype=torch.float64).clamp_min(1e-300)
+            return idx[torch.topk(lw[idx] - torch.log(-torch.log(u)), m).indices]
+
+        cur = draw(torch.arange(N), k).sort().values
+        out[0, b] = cur.to(torch.int32)
+        last_drop = torch.full((N,), never, dtype=torch.int64)
+        for t in range(1, steps):
+            kept = draw(cur, keep)
+            in_cur = torch.zeros(N, dtype=torch.bool)
+            in_cur[cur] = True
+            n_new = k - keep
+            pool = torch.nonzero((last_drop >= t - cfg.recency_window) & ~in_cur).flatten()
+            back = draw(pool, min(int(round(cfg.recency * n_new)), pool.numel()))
+            excl = in_cur.clone()
+            excl[back] = True
+            fresh = draw(torch.nonzero(~excl).flatten(), n_new - back.numel())
+            nxt = torch.cat([kept, back, fresh]).sort().values
+            in_nxt = torch.zeros(N, dtype=torch.bool)
+            in_nxt[nxt] = True
+            last_drop[cur[~in_nxt[cur]]] = t
+            cur = nxt
             out[t, b] = cur.to(torch.int32)
     return out
 
