@@ -88,6 +88,17 @@ def gather_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def gather_kernel_name(cfg, args) -> str:
+    """The gather kernel libtsa launches for this workload: merged sets of
+    plan segments for inverted-index batches of at least 128 bf16
+    (request, KV head) groups with up to 4 query heads per KV head and one
+    list per key; one wave per segment (or per row-list segment) otherwise."""
+    groups = cfg.batch * cfg.n_kv_heads
+    if cfg.kind == "ivf" and groups >= 128 and cfg.dtype == "bf16" and cfg.group <= 4 and args.assign == 1:
+        return "gather_merge_kernel"
+    return "gather_attn_kernel"
+
+
 def measured_traffic(workload: str):
     """HBM bytes per gather launch from the committed counter summary, if it was
     taken on the current kernel source and this workload; else None."""
@@ -625,7 +636,7 @@ def main():
         "gathered_kv_gbps": round(gb_s, 1),
         "gathered_kv_frac_of_peak": round(gb_s / HBM_PEAK_GBPS, 4),
         "graph": bool(args.graph),
-        "roofline": {"bound": "hbm", "kernel": "gather_attn", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": gather_kernel_name(cfg, args), "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": round(bytes_per_launch),
                      "mean_launch_us": round(g_mean_ms * 1e3, 2), "timing": res["kernel_timing"],

@@ -9,6 +9,10 @@ import pytest
 
 from top_sparse_attention_centroid_amd import binding as B
 
+# floats per partial softmax state in the workspace: five whole 128-byte
+# lines (m, l and zero fill; then o[128])
+PART_FLOATS = 160
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tsa.h")
 
@@ -54,17 +58,17 @@ def test_workspace_sizes_and_validation(lib):
     d = B.IvfDesc(64, 32768, 8, 32, 128, 256, 1, B.TSA_BF16)
     n = B.workspace_bytes(B.OP_SPARSE_DECODE, d, 16)
     G, smax = 4, 4 * 16 + 32768 // 256
-    assert n >= 64 * 8 * smax * G * 132 * 4
+    assert n >= 64 * 8 * smax * G * PART_FLOATS * 4
     # 512 groups fill the chip with 256-row plan segments: no finer cut (128-row
     # segments would need this many partial states)
-    assert n < 64 * 8 * (4 * 16 + 32768 // 128) * G * 132 * 4
+    assert n < 64 * 8 * (4 * 16 + 32768 // 128) * G * PART_FLOATS * 4
     # one request with 100-row lists: 8 groups x 40 lists would give 320 waves, so
     # lists are cut into 32-row segments (the shortest), and the scores get a
     # buffer of their own
     one = B.IvfDesc(1, 100_000, 8, 32, 128, 1000, 0, B.TSA_BF16)
     n1 = B.workspace_bytes(B.OP_SPARSE_DECODE, one, 10)
-    assert n1 >= 8 * (4 * 10 + 100_000 // 32) * G * 132 * 4 + 8 * G * 1000 * 4
-    assert n1 < 8 * (4 * 10 + 100_000 // 16) * G * 132 * 4
+    assert n1 >= 8 * (4 * 10 + 100_000 // 32) * G * PART_FLOATS * 4 + 8 * G * 1000 * 4
+    assert n1 < 8 * (4 * 10 + 100_000 // 16) * G * PART_FLOATS * 4
     assert B.workspace_bytes(B.OP_INDEX_BUILD, d) >= 64 * 8 * 32768 * 4
     with pytest.raises(B.TsaError, match="INVALID_ARG"):
         B.workspace_bytes(B.OP_SPARSE_DECODE, d, 0)
@@ -87,9 +91,9 @@ def test_workspace_sizes_and_validation(lib):
         B.workspace_bytes(B.OP_TOKEN_DECODE, B.TokenDesc(1, 4096 * 4096 + 1, 8, 32, 128, 64, 1), 4096)
     a = B.AttnDesc(32, 4096, 8, 32, 128, 2048, B.TSA_BF16)
     # 32 x 8 row lists of 2048 rows: 256-row segments (2048 of them), G = 4 partial states each
-    assert B.workspace_bytes(B.OP_ATTEND_ROWS, a) == 32 * 8 * (2048 // 256) * 4 * 132 * 4
+    assert B.workspace_bytes(B.OP_ATTEND_ROWS, a) == 32 * 8 * (2048 // 256) * 4 * PART_FLOATS * 4
     small = B.AttnDesc(2, 4096, 8, 32, 128, 2048, B.TSA_BF16)   # few lists: 64-row segments
-    assert B.workspace_bytes(B.OP_ATTEND_ROWS, small) == 2 * 8 * (2048 // 64) * 4 * 132 * 4
+    assert B.workspace_bytes(B.OP_ATTEND_ROWS, small) == 2 * 8 * (2048 // 64) * 4 * PART_FLOATS * 4
 
 
 def test_calls_reject_bad_arguments_before_any_launch(lib):
@@ -202,7 +206,7 @@ def _ivf_ws(B_, N, Hkv, Hq, C, k, rows, split):
         return (x + 255) // 256 * 256
     G, bh = Hq // Hkv, B_ * Hkv
     smax = G * k + -(-N // rows)
-    return al(bh * smax * 16) + al(bh * 4) + al(bh * smax * G * 132 * 4) + (al(bh * G * C * 4) if split else 0)
+    return al(bh * smax * 16) + al(bh * 4) + al(bh * smax * G * PART_FLOATS * 4) + (al(bh * G * C * 4) if split else 0)
 
 
 @pytest.mark.parametrize("k,rows", [(8, 64), (12, 128), (16, 256)])

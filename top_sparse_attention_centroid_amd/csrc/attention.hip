@@ -80,6 +80,18 @@ __device__ __forceinline__ void merge_into(HeadState& a, float m2, float l2, con
   a.m = M;
 }
 
+// Writes a merged state (every lane group holds the same values after the
+// shuffle merge): lanes 0..15 write o, lanes 16..23 the header line
+// (m, l, zeros), so each 128-byte line of the record is written in full.
+__device__ __forceinline__ void store_state(float* ph, const HeadState& st, int r, int e) {
+  if (r == 0) {
+    *reinterpret_cast<float4*>(ph + kPartO + e * 8) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
+    *reinterpret_cast<float4*>(ph + kPartO + 4 + e * 8) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
+  } else if (r == 1 && e < kPartO / 4) {
+    *reinterpret_cast<float4*>(ph + e * 4) = e == 0 ? make_float4(st.m, st.l, 0.f, 0.f) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
 // K and V rows of one batch: lane group r = lane / 16 takes rows r, r+4, ...
 // of the batch; raw bits stay in registers until scored.
 template <typename T, int U = kGatherUnroll>
@@ -162,12 +174,13 @@ __device__ __forceinline__ void consume_batch(const Batch<T, U>& bt, HeadState& 
 // then merge and lanes 0..15 write the head's partial state.
 // For each query head in `mask`: one pass over the segment's rows, then the
 // four 16-lane row groups merge and lanes 0..15 write the head's partial.
+// One query head's pass over rows ids[0, cnt): the returned state is merged
+// over the four lane groups (every lane holds it; lanes 0..15 own o).
 template <bool STREAM, bool DUP, typename T>
-__device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int cnt, int r, int e, const T* kb,
-                                            const T* vb, long long row_stride, const T* qs, float qscale,
-                                            float* part, const uint32_t* dup) {
-  for (uint32_t hm = mask; hm != 0u; hm &= hm - 1u) {
-    const int h = __builtin_ctz(hm);
+__device__ __forceinline__ HeadState head_pass(int h, const int* ids, int cnt, int r, int e, const T* kb,
+                                               const T* vb, long long row_stride, const T* qs, float qscale,
+                                               const uint32_t* dup) {
+  {
     QFrag<T> qf;
     qf.load(qs + h * kHeadDim + e * 8);
     HeadState st;
@@ -210,26 +223,32 @@ __device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int c
       for (int t = 0; t < 8; ++t) o2[t] = __shfl_xor(st.o[t], x);
       merge_into(st, m2, l2, o2);
     }
-    if (r == 0) {
-      float* ph = part + h * kPartStride;
-      *reinterpret_cast<float4*>(ph + 4 + e * 8) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
-      *reinterpret_cast<float4*>(ph + 8 + e * 8) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
-      if (e == 0) {
-        ph[0] = st.m;
-        ph[1] = st.l;
-      }
-    }
+    return st;
+  }
+}
+
+template <bool STREAM, bool DUP, typename T>
+__device__ __forceinline__ void head_passes(uint32_t mask, const int* ids, int cnt, int r, int e, const T* kb,
+                                            const T* vb, long long row_stride, const T* qs, float qscale,
+                                            float* part, const uint32_t* dup) {
+  for (uint32_t hm = mask; hm != 0u; hm &= hm - 1u) {
+    const int h = __builtin_ctz(hm);
+    const HeadState st = head_pass<STREAM, DUP>(h, ids, cnt, r, e, kb, vb, row_stride, qs, qscale, dup);
+    store_state(part + h * kPartStride, st, r, e);
   }
 }
 
 // Row lists shared by every head of the group (token selections, hot-cache
 // slots): one pass scores each batch of rows for all G heads, so a row is
 // loaded into registers once; G online-softmax states per lane group.
-template <int G, typename T>
-__device__ __forceinline__ void all_heads_pass(const int* ids, int cnt, int r, int e, const T* kb, const T* vb,
-                                               long long row_stride, const T* qs, float qscale, float* part) {
+// `row_heads(j)` gives the heads that attend row j (a row outside a head's
+// set is scored and dropped for it); the states come back merged over the
+// four lane groups.
+template <int G, typename T, typename RowHeads>
+__device__ __forceinline__ void all_heads_states(HeadState (&st)[G], const int* ids, int cnt, int r, int e,
+                                                 const T* kb, const T* vb, long long row_stride, const T* qs,
+                                                 float qscale, RowHeads row_heads) {
   QFrag<T> qf[G];
-  HeadState st[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     qf[h].load(qs + h * kHeadDim + e * 8);
@@ -239,12 +258,14 @@ __device__ __forceinline__ void all_heads_pass(const int* ids, int cnt, int r, i
     Raw8<T> k[kUnrollAll], v[kUnrollAll];
     bool valid[kUnrollAll];
     int row[kUnrollAll];
+    uint32_t heads[kUnrollAll];
 #pragma unroll
     for (int u = 0; u < kUnrollAll; ++u) {
       const int j = base + u * 4 + r;
       const int id = ids[min(j, kSegRows - 1)];
       valid[u] = (j < cnt) & (id >= 0);
       row[u] = valid[u] ? id : 0;
+      heads[u] = row_heads(j);
     }
 #pragma unroll
     for (int u = 0; u < kUnrollAll; ++u) k[u].load_stream(kb + row[u] * row_stride);
@@ -255,7 +276,7 @@ __device__ __forceinline__ void all_heads_pass(const int* ids, int cnt, int r, i
       float sc[kUnrollAll];
 #pragma unroll
       for (int u = 0; u < kUnrollAll; ++u)
-        sc[u] = valid[u] ? group16_sum(qf[h].dot(k[u])) * qscale : kMaskedScore;
+        sc[u] = valid[u] && ((heads[u] >> h) & 1u) ? group16_sum(qf[h].dot(k[u])) * qscale : kMaskedScore;
       float mb = sc[0];
 #pragma unroll
       for (int u = 1; u < kUnrollAll; ++u) mb = fmaxf(mb, sc[u]);
@@ -287,15 +308,19 @@ __device__ __forceinline__ void all_heads_pass(const int* ids, int cnt, int r, i
       for (int t = 0; t < 8; ++t) o2[t] = __shfl_xor(st[h].o[t], x);
       merge_into(st[h], m2, l2, o2);
     }
-    if (r == 0) {
-      float* ph = part + h * kPartStride;
-      *reinterpret_cast<float4*>(ph + 4 + e * 8) = make_float4(st[h].o[0], st[h].o[1], st[h].o[2], st[h].o[3]);
-      *reinterpret_cast<float4*>(ph + 8 + e * 8) = make_float4(st[h].o[4], st[h].o[5], st[h].o[6], st[h].o[7]);
-      if (e == 0) {
-        ph[0] = st[h].m;
-        ph[1] = st[h].l;
-      }
-    }
+  }
+}
+
+template <int G, typename T>
+__device__ __forceinline__ void all_heads_pass(uint32_t mask, const int* ids, int cnt, int r, int e, const T* kb,
+                                               const T* vb, long long row_stride, const T* qs, float qscale,
+                                               float* part) {
+  HeadState st[G];
+  all_heads_states<G>(st, ids, cnt, r, e, kb, vb, row_stride, qs, qscale, [](int) { return ~0u; });
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    // heads outside the mask were scored with the others but are not merged
+    if ((mask >> h) & 1u) store_state(part + h * kPartStride, st[h], r, e);
   }
 }
 
@@ -461,8 +486,8 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
     // Rows read by one head stream past the caches in that head's pass. Rows
     // that every head of the group reads are loaded once and scored for all
     // heads in one pass; with multi_all (large batches, bound by bandwidth)
-    // so are rows that two or more heads read, the partial states of heads
-    // outside the mask being written and never merged. Otherwise such rows
+    // so are rows that two or more heads read (heads outside the mask are
+    // scored and dropped; only the mask's states are written). Otherwise such rows
     // stay cacheable, one pass per head, the later passes hitting L2: a
     // small batch is bound by the latency of its waves, which the extra
     // heads' arithmetic would lengthen. (2-way lists keep per-head passes:
@@ -471,7 +496,7 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
         !EXPLICIT || (TSA_GATHER_FULLMASK_ALL && G > 1 && !two_way &&
                       (mask == (1u << G) - 1u || (p.multi_all && (mask & (mask - 1u)) != 0u)));
     if (all_heads) {
-      all_heads_pass<G>(ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
+      all_heads_pass<G>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
     } else if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u) {
       head_passes<true, DUP>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);
     } else {
@@ -486,6 +511,146 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
         stage_dup(cur);
       }
     }
+  }
+}
+
+// gather_merge: explicit plans in large batches. A workgroup of kMergeWaves
+// waves takes kMergeWaves consecutive plan segments of one (request, KV
+// head), a segment per wave; the plan lists the single-head lists head by
+// head, so they mostly share one head. The waves merge their states per
+// head through LDS and the workgroup writes one partial state per head of
+// the set instead of one per segment and head: each written state costs its
+// wave a store round trip before the wave retires, and the HBM a write-back
+// amid the row stream. Set t covers segments [t * kMergeWaves,
+// (t + 1) * kMergeWaves); its states sit at segment slot t * kMergeWaves.
+// (Splitting a set's rows evenly over the waves, or aligning each head class
+// to a set with empty segments, measured slower: the first adds a barrier
+// between staging and streaming, the second idle waves.)
+template <typename T, int G>
+__global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(GatherParams p) {
+  constexpr int NW = kMergeWaves;
+  constexpr int kHeadsPerWave = (G + NW - 1) / NW;  // heads each wave merges
+  __shared__ __align__(16) T qs[G * kHeadDim];
+  __shared__ int ids_lds[NW][kSegRows];
+  __shared__ float sm_m[NW][G], sm_l[NW][G];
+  __shared__ __align__(16) float sm_o[NW][G][kHeadDim];
+  const int bg = blockIdx.x / p.W, w0 = blockIdx.x % p.W;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int r = lane >> 4, e = lane & 15;
+
+  const int nseg = min(max(p.nseg[bg], 0), p.smax);
+  constexpr int kQParts = G * kHeadDim / 8;
+  constexpr int kQPer = (kQParts + NW * kWave - 1) / (NW * kWave);
+  Raw8<T> qpart[kQPer];
+  const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i)
+    if (tid + i * NW * kWave < kQParts) qpart[i].load(qb + (tid + i * NW * kWave) * 8);
+  if (w0 * NW >= nseg) return;  // uniform over the block
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i)
+    if (tid + i * NW * kWave < kQParts) *reinterpret_cast<Raw8<T>*>(qs + (tid + i * NW * kWave) * 8) = qpart[i];
+
+  const long long row_stride = static_cast<long long>(p.Hkv) * kHeadDim;
+  const T* kb = static_cast<const T*>(p.k) + static_cast<long long>(b) * p.n_rows * row_stride +
+                g * kHeadDim + e * 8;
+  const T* vb = static_cast<const T*>(p.v) + static_cast<long long>(b) * p.n_rows * row_stride +
+                g * kHeadDim + e * 8;
+  const int32_t* rid = p.rowids + b * p.rid_bstride + g * p.rid_gstride;
+  int* ids = ids_lds[wave];
+  // sink / window ranges: list rows inside them are skipped (attended
+  // through their own direct segments)
+  int fx_sink = 0, fx_lo = 0, fx_hi = 0;
+  if (p.n_sink > 0 || p.n_window > 0) {
+    const int L = p.lengths ? min(max(p.lengths[b], 0), static_cast<int>(p.n_rows)) : static_cast<int>(p.n_rows);
+    fx_sink = min(p.n_sink, L);
+    fx_lo = p.n_window > 0 ? max(L - p.n_window, fx_sink) : L;
+    fx_hi = L;
+  }
+
+  for (int t = w0; t * NW < nseg; t += p.W) {  // uniform over the block
+    const int s0 = t * NW;
+    // every wave reads the set's descriptors (the same addresses): its own
+    // segment, and the head masks of all of them
+    uint32_t msk[NW];
+    int my_start = 0, my_cnt = 0;
+    bool my_direct = false;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const bool in = s0 + i < nseg;
+      const int4 d = p.seg[static_cast<long long>(bg) * p.smax + min(s0 + i, nseg - 1)];
+      msk[i] = in ? static_cast<uint32_t>(d.z) & ((1u << G) - 1u) : 0u;
+      if (i == wave) {
+        my_start = d.x;
+        my_cnt = in ? min(max(d.y, 0), kSegRows) : 0;
+        my_direct = d.w < 0;
+      }
+    }
+    uint32_t U = 0u, my_mask = 0u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      U |= msk[i];
+      my_mask = i == wave ? msk[i] : my_mask;
+    }
+    // the wave's row ids into its LDS area; ids outside [0, n_rows) are
+    // skipped, never dereferenced
+    for (int j = lane; j < my_cnt; j += kWave) {
+      const int id = my_direct ? my_start + j : rid[my_start + j];
+      bool ok = static_cast<unsigned long long>(id) < static_cast<unsigned long long>(p.n_rows);
+      if (!my_direct) ok = ok && !(id < fx_sink || (id >= fx_lo && id < fx_hi));
+      ids[j] = ok ? id : -1;
+    }
+    __syncthreads();  // queries staged (first set); the ids are wave-private
+
+    auto put = [&](int h, const HeadState& st) {
+      if (r == 0) {
+        *reinterpret_cast<float4*>(&sm_o[wave][h][e * 8]) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
+        *reinterpret_cast<float4*>(&sm_o[wave][h][e * 8 + 4]) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
+        if (e == 0) {
+          sm_m[wave][h] = st.m;
+          sm_l[wave][h] = st.l;
+        }
+      }
+    };
+    if (my_mask != 0u && (my_mask & (my_mask - 1u)) == 0u) {
+      const int h = __builtin_ctz(my_mask);
+      put(h, head_pass<TSA_GATHER_NT != 0, false>(h, ids, my_cnt, r, e, kb, vb, row_stride, qs, p.qscale,
+                                                  nullptr));
+    } else if (my_mask != 0u) {  // a list several heads chose, or a sink / window range
+      HeadState st[G];
+      all_heads_states<G>(st, ids, my_cnt, r, e, kb, vb, row_stride, qs, p.qscale, [](int) { return ~0u; });
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if ((my_mask >> h) & 1u) put(h, st[h]);
+    }
+    __syncthreads();
+
+    // wave w merges heads w, w + NW, ... of the set: log-sum-exp over the
+    // states of the waves whose segment the head attended, in wave order
+#pragma unroll
+    for (int hh = 0; hh < kHeadsPerWave; ++hh) {
+      const int h = wave + hh * NW;
+      if (h >= G || !((U >> h) & 1u)) continue;  // uniform over the wave
+      float M = kEmptyMax;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) M = (msk[i] >> h) & 1u ? fmaxf(M, sm_m[i][h]) : M;
+      float L = 0.f, O0 = 0.f, O1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        if (!((msk[i] >> h) & 1u)) continue;
+        const float a = fast_exp2(sm_m[i][h] - M);
+        const float2 o = *reinterpret_cast<const float2*>(&sm_o[i][h][lane * 2]);
+        L = fmaf(sm_l[i][h], a, L);
+        O0 = fmaf(o.x, a, O0);
+        O1 = fmaf(o.y, a, O1);
+      }
+      float* ph = p.partial + ((static_cast<long long>(bg) * p.smax + s0) * G + h) * kPartStride;
+      *reinterpret_cast<float2*>(ph + kPartO + lane * 2) = make_float2(O0, O1);
+      if (lane < kPartO / 4)
+        *reinterpret_cast<float4*>(ph + lane * 4) = lane == 0 ? make_float4(M, L, 0.f, 0.f) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if ((t + p.W) * NW < nseg) __syncthreads();  // the next set reuses the LDS
   }
 }
 
@@ -522,35 +687,45 @@ __global__ __launch_bounds__(GH * NS * kWave) void combine_kernel(GatherParams p
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int hl = wave / NS, part = wave % NS;           // head within the workgroup
   const int h = (blockIdx.x % (G / GH)) * GH + hl;      // head within the group
-  int nseg;
+  // records: one per segment, or with merged sets (gather_merge_kernel) one
+  // per set of kMergeWaves segments at slot set * kMergeWaves, covering the
+  // heads of all its segments
+  int nseg, rs = 1;
   if constexpr (EXPLICIT) {
-    nseg = p.nseg[bg];
+    nseg = min(max(p.nseg[bg], 0), p.smax);
+    if (p.merge) rs = kMergeWaves;
   } else {
     const int rows = min(max(p.counts ? p.counts[b] : p.count_const, 0), p.count_max);
     nseg = (rows + p.seg_rows - 1) / p.seg_rows;
   }
+  const int nrec = (nseg + rs - 1) / rs;
+  const int4* segs = p.seg + static_cast<long long>(bg) * p.smax;
+  auto rec_heads = [&](int t) {  // heads whose state record t holds (explicit plans)
+    uint32_t m = static_cast<uint32_t>(segs[t * rs].z);
+    for (int i = 1; i < rs; ++i)
+      if (t * rs + i < nseg) m |= static_cast<uint32_t>(segs[t * rs + i].z);
+    return m;
+  };
+  const long long rec_stride = static_cast<long long>(rs) * G * kPartStride;  // floats between records
   float M = kEmptyMax, L = 0.f, O0 = 0.f, O1 = 0.f;
   const float* base = p.partial + static_cast<long long>(bg) * p.smax * G * kPartStride + h * kPartStride;
-  const int n_mine = nseg > part ? (nseg - part + NS - 1) / NS : 0;  // segments part + i * NS
+  const int n_mine = nrec > part ? (nrec - part + NS - 1) / NS : 0;  // records part + i * NS
   for (int i0 = 0; i0 < n_mine; i0 += kWave) {
     const int s = part + (i0 + lane) * NS;
     const bool in_range = i0 + lane < n_mine;
     // descriptor and partial (m, l) requested together; the (m, l) of a
-    // segment whose mask leaves this head out are never written and never used
-    const float* ph = base + static_cast<long long>(in_range ? s : 0) * G * kPartStride;
+    // record whose heads leave this head out are never written and never used
+    const float* ph = base + (in_range ? s : 0) * rec_stride;
     float pm = kMaskedScore, pl = 0.f;
     bool mine = in_range;
     if constexpr (NS > 1) {
       const float pm_raw = ph[0], pl_raw = ph[1];
-      if constexpr (EXPLICIT) {
-        const int z = p.seg[static_cast<long long>(bg) * p.smax + (in_range ? s : 0)].z;
-        mine = mine && ((static_cast<uint32_t>(z) >> h) & 1u);
-      }
+      if constexpr (EXPLICIT) mine = mine && ((rec_heads(in_range ? s : 0) >> h) & 1u);
       pm = mine ? pm_raw : kMaskedScore;
       pl = mine ? pl_raw : 0.f;
     } else {
       if constexpr (EXPLICIT) {
-        if (mine) mine = (static_cast<uint32_t>(p.seg[static_cast<long long>(bg) * p.smax + s].z) >> h) & 1u;
+        if (mine) mine = (rec_heads(s) >> h) & 1u;
       }
       if (mine) {
         pm = ph[0];
@@ -578,8 +753,8 @@ __global__ __launch_bounds__(GH * NS * kWave) void combine_kernel(GatherParams p
       for (int u = 0; u < kU; ++u) {
         const int jj = j[u] < 0 ? 0 : j[u];  // j < 0: reload segment `part` (in range), weight 0
         wj[u] = j[u] < 0 ? 0.f : __shfl(w, jj);
-        po[u] = *reinterpret_cast<const float2*>(
-            base + static_cast<long long>(j[u] < 0 ? part : part + (i0 + jj) * NS) * G * kPartStride + 4 + lane * 2);
+        po[u] = *reinterpret_cast<const float2*>(base + (j[u] < 0 ? part : part + (i0 + jj) * NS) * rec_stride +
+                                                 kPartO + lane * 2);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -627,8 +802,21 @@ static void gather_dispatch(const GatherParams& p, int G, hipStream_t s) {
   }
 }
 
+// Merged sets run for bf16 with up to 4 query heads per KV head (the
+// caller sets p.merge only then; wider states would spill registers).
 hipError_t launch_gather(const GatherParams& p, int dtype, int G, bool explicit_plan,
                          hipStream_t s) {
+  if (explicit_plan && p.merge) {
+    if (dtype != kBF16 || p.alt) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(p.B * p.Hkv * p.W)), block(kMergeWaves * kWave);
+    switch (G) {
+      case 1: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 1>), grid, block, 0, s, p); break;
+      case 2: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 2>), grid, block, 0, s, p); break;
+      case 4: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 4>), grid, block, 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (dtype == kBF16) {
     if (explicit_plan && p.alt) gather_dispatch<bf16_t, true, true>(p, G, s);
     else if (explicit_plan) gather_dispatch<bf16_t, true, false>(p, G, s);

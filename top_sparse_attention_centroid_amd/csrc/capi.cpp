@@ -100,7 +100,7 @@ FetchParams fetch_params(const tsa_cache_desc& d, const int32_t* miss_tok, const
 // ----------------------------------------------------------------- layouts
 struct IvfLayout {
   int G = 0, smax = 0, seg_rows = 0;
-  bool small_batch = false, split_score = false;
+  bool small_batch = false, split_score = false, merge = false;
   size_t seg = 0, nseg = 0, partial = 0, lmask = 0, keys = 0, total = 0;
 };
 
@@ -151,15 +151,20 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false, int 
   IvfLayout L;
   L.G = d.n_q_heads / d.n_kv_heads;
   L.seg_rows = ivf_seg_rows(d, k, m);
+  const size_t bh = static_cast<size_t>(d.batch) * d.n_kv_heads;
+  L.small_batch = static_cast<long long>(bh) < kSmallBatchGroups;
+  // Large bf16 batches (bound by HBM) with up to 4 query heads per KV head
+  // gather in merged sets of kMergeWaves segments; small ones, bound by the
+  // latency of their waves, keep a wave per segment, and so do 2-way lists
+  // (per-row duplicate masks), fp32 and wider groups.
+  L.merge = !L.small_batch && m == 1 && d.dtype == TSA_BF16 && L.G <= 4;
   L.smax = L.G * k + ceil_div(static_cast<long long>(d.n_tokens) * m, L.seg_rows) +
            (with_fixed ? kMaxFixedRows / L.seg_rows + 2 : 0);
-  const size_t bh = static_cast<size_t>(d.batch) * d.n_kv_heads;
   size_t off = 0;
   L.seg = off;    off += align_up(bh * L.smax * sizeof(int4));
   L.nseg = off;   off += align_up(bh * sizeof(int32_t));
   L.partial = off; off += align_up(bh * L.smax * L.G * kPartStride * sizeof(float));
   L.lmask = off;   off += m > 1 ? align_up(bh * d.n_centroids * sizeof(uint32_t)) : 0;
-  L.small_batch = static_cast<long long>(bh) < kSmallBatchGroups;
   L.split_score = d.dtype == TSA_BF16 && L.small_batch;
   L.keys = off;    off += L.split_score ? align_up(bh * L.G * d.n_centroids * sizeof(uint32_t)) : 0;
   L.total = off;
@@ -378,9 +383,11 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
     fixed_segs = ceil_div(std::min(opts->n_sink, d.n_tokens), L.seg_rows) +
                  ceil_div(std::min(opts->n_window, d.n_tokens), L.seg_rows) + (opts->n_window > 0 ? 1 : 0);
   }
-  gp.W = gather_blocks_per_head(std::min(L.smax, L.G * k * ivf_list_segs(d, m, L.seg_rows) + fixed_segs), true);
+  const int expected_segs = std::min(L.smax, L.G * k * ivf_list_segs(d, m, L.seg_rows) + fixed_segs);
   gp.seg_rows = L.seg_rows;
   gp.multi_all = L.small_batch ? 0 : 1;
+  gp.merge = L.merge ? 1 : 0;
+  gp.W = L.merge ? std::max(1, ceil_div(expected_segs, kMergeWaves)) : gather_blocks_per_head(expected_segs, true);
   gp.qscale = qscale(d.head_dim);
   if (opts) {
     gp.n_sink = opts->n_sink;

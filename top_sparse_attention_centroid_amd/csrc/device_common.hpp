@@ -237,6 +237,55 @@ __device__ __forceinline__ int block_exclusive_scan_and_sum(int v, int u, int* s
   return before + x - v;
 }
 
+// Exclusive block scan of NC per-thread counts at once, classes placed one
+// after another: pos[k] = (items of all classes below k) + (items of class k
+// held by lower threads). Items therefore land class by class, each class in
+// thread order. Also sums `u` over the block into *total_u and the counts
+// of every class into *total. `scratch` holds NW * (NC + 1) ints; two
+// barriers.
+template <int NW, int NC>
+__device__ __forceinline__ void block_class_scan(const int (&cnt)[NC], int (&pos)[NC], int u, int* scratch,
+                                                 int* total, int* total_u) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  int x[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    x[c] = cnt[c];
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x[c], o);
+      if (lane >= o) x[c] += y;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) u += __shfl_xor(u, o);
+  if (lane == kWave - 1) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) scratch[wave * (NC + 1) + c] = x[c];
+    scratch[wave * (NC + 1) + NC] = u;
+  }
+  __syncthreads();
+  int base = 0, all_u = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int t = scratch[w * (NC + 1) + c];
+      before += (w < wave) ? t : 0;
+      all += t;
+    }
+    pos[c] = base + before + x[c] - cnt[c];
+    base += all;
+  }
+#pragma unroll
+  for (int w = 0; w < NW; ++w) all_u += scratch[w * (NC + 1) + NC];
+  __syncthreads();
+  *total = base;
+  *total_u = all_u;
+}
+
 template <int NW>
 __device__ __forceinline__ int block_sum(int v, int* scratch) {
   int total;

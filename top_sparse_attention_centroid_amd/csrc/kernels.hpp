@@ -24,7 +24,21 @@ constexpr int kGatherWavesRows = TSA_GATHER_WPB_ROWS;   // ... per-request row l
 #define TSA_GATHER_SPW 1
 #endif
 constexpr int kGatherSegsPerWave = TSA_GATHER_SPW;  // segments each gather wave is planned to take
-constexpr int kPartStride = 132;    // floats per partial state: m, l, 2 pad, o[128]
+// A partial softmax state is five whole 128-byte lines: line 0 holds m, l and
+// zero fill, lines 1-4 hold o[128]. One wave writes every byte of each line,
+// so no line reaches HBM partly written (HBM3E spends its mask pins on ECC,
+// so a partial line write becomes a read-modify-write in the memory
+// controller). Records stay line-aligned when the workspace is 128-byte
+// aligned, as every device allocation is.
+constexpr int kPartStride = 160;    // floats per partial state
+#ifndef TSA_MERGE_WAVES
+#define TSA_MERGE_WAVES 3
+#endif
+// waves (and plan segments) per merging gather workgroup; at the batched
+// 64 x 32K decode 3 measured best (2: fewer states merged, 4 and up: a
+// workgroup waits longer for its longest segment, 6 also loses occupancy)
+constexpr int kMergeWaves = TSA_MERGE_WAVES;
+constexpr int kPartO = 32;          // offset of o[128] within the state
 #ifndef TSA_SCORE_TILE
 #define TSA_SCORE_TILE 2048
 #endif
@@ -131,6 +145,8 @@ struct GatherParams {
   const uint32_t* lmask;   // [B*Hkv][C] head masks of the chosen lists (with alt)
   int C;                   // lists per (request, KV head) (with alt)
   int multi_all;           // explicit plans: segments chosen by two or more heads take one all-heads pass
+  int merge;               // explicit plans: kMergeWaves consecutive segments per workgroup, rows split
+                           // evenly over its waves, one partial state per head per set (0: a wave per segment)
   float* out;              // [B][Hq][d]
   int B, Hkv, smax, W;     // W: workgroups per (request, KV head)
   float qscale;            // log2(e) / sqrt(d)
