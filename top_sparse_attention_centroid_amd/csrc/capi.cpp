@@ -364,6 +364,7 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
   }
   if (m == 2) selp.lmask_out = reinterpret_cast<uint32_t*>(w + L.lmask);
   selp.seg_rows = L.seg_rows;
+  selp.class_order = L.merge ? 1 : 0;
   if (L.split_score) selp.keys = reinterpret_cast<uint32_t*>(w + L.keys);
   hipError_t e = launch_ivf_select(selp, d.dtype, L.G, s);
   if (e != hipSuccess) return hip_fail(e, "ivf_select launch");

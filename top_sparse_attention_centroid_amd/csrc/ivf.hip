@@ -617,48 +617,70 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   if (p.lmask_out)  // the chosen lists' head masks, for the gather's duplicate test
     for (int c = tid; c < C; c += 256) p.lmask_out[static_cast<long long>(bg) * C + c] = lmask[c];
 
-  // thread t plans lists [t * per, (t + 1) * per). Segments are ordered by
-  // head class: the lists only head 0 chose, then those only head 1 chose,
-  // ..., then the lists several heads chose; within a class, list order.
-  // Consecutive segments then mostly share one head, so a gather workgroup
-  // that takes several of them merges their states into one per head. One
-  // block scan of the per-thread counts of every class places them.
+  // thread t plans lists [t * per, (t + 1) * per). For merged gather sets
+  // the segments are ordered by head class: the lists only head 0 chose,
+  // then those only head 1 chose, ..., then the lists several heads chose;
+  // within a class, list order. Consecutive segments then mostly share one
+  // head, so a gather workgroup that takes several of them merges their
+  // states into one per head. Otherwise they follow list order. One block
+  // scan of the per-thread counts (of every class) places them.
   int4* seg = p.seg + static_cast<long long>(bg) * p.smax;
   const int sr = min(max(p.seg_rows, 1), kSegRows);
   const int per = (C + 255) / 256;
   const int c_lo = tid * per, c_hi = min(C, c_lo + per);
   auto class_of = [&](uint32_t m) { return (m & (m - 1u)) == 0u ? static_cast<int>(__builtin_ctz(m)) : G; };
-  int cls_segs[G + 1], cls_pos[G + 1];
-#pragma unroll
-  for (int c = 0; c <= G; ++c) cls_segs[c] = 0;
-  int uniq = 0;
-  for (int c = c_lo; c < c_hi; ++c) {
-    const uint32_t m = lmask[c];
-    const int len = list_len(c);
-    if (m != 0u && len > 0) {
-      const int cl = class_of(m), ns = (len + sr - 1) / sr;
-#pragma unroll
-      for (int x = 0; x <= G; ++x) cls_segs[x] += x == cl ? ns : 0;
-      uniq += len;
-    }
-  }
   int carry, uniq_all;
-  block_class_scan<4, G + 1>(cls_segs, cls_pos, uniq, class_scratch, &carry, &uniq_all);
-  for (int c = c_lo; c < c_hi; ++c) {
-    const uint32_t m = lmask[c];
-    const int len = list_len(c);
-    if (m == 0u || len <= 0) continue;
-    const int start = loff[c], cl = class_of(m), ns = (len + sr - 1) / sr;
-    int pos = 0;
+  if (p.class_order) {
+    int cls_segs[G + 1], cls_pos[G + 1];
 #pragma unroll
-    for (int x = 0; x <= G; ++x) {
-      if (x == cl) {
-        pos = cls_pos[x];
-        cls_pos[x] += ns;
+    for (int c = 0; c <= G; ++c) cls_segs[c] = 0;
+    int uniq = 0;
+    for (int c = c_lo; c < c_hi; ++c) {
+      const uint32_t m = lmask[c];
+      const int len = list_len(c);
+      if (m != 0u && len > 0) {
+        const int cl = class_of(m), ns = (len + sr - 1) / sr;
+#pragma unroll
+        for (int x = 0; x <= G; ++x) cls_segs[x] += x == cl ? ns : 0;
+        uniq += len;
       }
     }
-    for (int j = 0; j < ns; ++j, ++pos) {
-      if (pos < p.smax) seg[pos] = make_int4(start + j * sr, min(sr, len - j * sr), static_cast<int>(m), c);
+    block_class_scan<4, G + 1>(cls_segs, cls_pos, uniq, class_scratch, &carry, &uniq_all);
+    for (int c = c_lo; c < c_hi; ++c) {
+      const uint32_t m = lmask[c];
+      const int len = list_len(c);
+      if (m == 0u || len <= 0) continue;
+      const int start = loff[c], cl = class_of(m), ns = (len + sr - 1) / sr;
+      int pos = 0;
+#pragma unroll
+      for (int x = 0; x <= G; ++x) {
+        if (x == cl) {
+          pos = cls_pos[x];
+          cls_pos[x] += ns;
+        }
+      }
+      for (int j = 0; j < ns; ++j, ++pos) {
+        if (pos < p.smax) seg[pos] = make_int4(start + j * sr, min(sr, len - j * sr), static_cast<int>(m), c);
+      }
+    }
+  } else {
+    int my_segs = 0, uniq = 0;
+    for (int c = c_lo; c < c_hi; ++c) {
+      const int len = list_len(c);
+      if (lmask[c] != 0u && len > 0) {
+        my_segs += (len + sr - 1) / sr;
+        uniq += len;
+      }
+    }
+    int pos = block_exclusive_scan_and_sum<4>(my_segs, uniq, class_scratch, &carry, &uniq_all);
+    for (int c = c_lo; c < c_hi; ++c) {
+      const uint32_t m = lmask[c];
+      const int len = list_len(c);
+      if (m == 0u || len <= 0) continue;
+      const int start = loff[c];
+      for (int j = 0; j * sr < len; ++j, ++pos) {
+        if (pos < p.smax) seg[pos] = make_int4(start + j * sr, min(sr, len - j * sr), static_cast<int>(m), c);
+      }
     }
   }
   // Fixed token ranges attended beside the lists by every head of the group

@@ -103,6 +103,7 @@ struct SelectParams {
   int seg_rows;            // rows per plan segment (<= kSegRows)
   uint32_t* keys;          // [B*Hkv][G][C] order keys of the scores, computed by centroid_score_kernel
                            // (bf16 only), or null: the select kernel scores the centroids itself
+  int class_order;         // 1: plan segments by head class (merged gather sets), 0: list order
 };
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s);
 
