@@ -25,9 +25,11 @@ def _capture(fn):
     return g
 
 
-def test_graph_sparse_decode_replays():
-    cfg = W.config(2, batch=6, n_tokens=9000, n_centroids=96, top_k=7, steps=3)
-    announce("graph sparse_decode")
+# 6 requests: a wave per plan segment; 16 x 8 KV heads: merged gather sets
+@pytest.mark.parametrize("batch,n_tokens", [(6, 9000), (16, 4096)])
+def test_graph_sparse_decode_replays(batch, n_tokens):
+    cfg = W.config(2, batch=batch, n_tokens=n_tokens, n_centroids=96, top_k=7, steps=3)
+    announce(f"graph sparse_decode, {batch} requests")
     p = W.ivf_problem(cfg, device=DEV)
     q = W.ivf_queries(cfg, p["centroids"], steps=3)
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
