@@ -114,3 +114,42 @@ def test_merged_sets_loop_over_a_long_list():
     assert rows[:, 0].min().item() >= N * 3 // 4
     err = out_error(out.cpu().numpy(), r["out"])
     assert err <= OUT_TOL, f"output error {err}"
+
+
+def test_merged_sets_empty_groups():
+    # 32 requests x 4 KV heads = 128 groups, bf16, 2 query heads per KV head.
+    # Small centroids live in dims 0..63; three far centroids in dims 64..127
+    # own no keys. Requests b % 3 == 0: both heads of every group query a far
+    # centroid, so the group has no plan segment at all; b % 3 == 1: head 0
+    # far, head 1 small; b % 3 == 2: both small. Empty heads must come out
+    # exactly zero with 0 rows; the rest match the oracle.
+    g = torch.Generator().manual_seed(3)
+    B, N, Hkv, G, C, d = 32, 600, 4, 2, 8, 128
+    cent = torch.zeros(1, Hkv, C, d)
+    cent[0, :, :5, :64] = torch.randn(Hkv, 5, 64, generator=g)
+    cent[0, :, 5:, 64:] = 40.0 * torch.randn(Hkv, 3, 64, generator=g)
+    comp = torch.randint(0, 5, (B, N, Hkv), generator=g)
+    keys = cent[0][torch.arange(Hkv)[None, None, :], comp] + 0.3 * torch.randn(B, N, Hkv, d, generator=g)
+    vals = torch.randn(B, N, Hkv, d, generator=g)
+    target = torch.empty(B, Hkv * G, dtype=torch.long)
+    for b in range(B):
+        for h in range(Hkv * G):
+            far = (b % 3 == 0) or (b % 3 == 1 and h % G == 0)
+            target[b, h] = 5 + (b + h) % 3 if far else (b + h) % 5
+    q = cent[0][torch.arange(Hkv * G)[None, :] // G, target]
+    announce("merged sets: groups and heads with empty selections")
+    keys, vals, cent, q = (x.to(torch.bfloat16).to(DEV) for x in (keys, vals, cent, q))
+    offsets, ids = _index_checked({"keys": keys, "centroids": cent})
+    rows = torch.empty((B, Hkv * G), dtype=torch.int32, device=DEV)
+    sel = torch.empty((B, Hkv * G, 1), dtype=torch.int32, device=DEV)
+    out = tsa.sparse_decode(q, cent, offsets, ids, keys, vals, 1, rows_out=rows, sel_out=sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy()[..., 0], target.numpy())
+    r = ivf.sparse_decode(f64(q), f64(cent), offsets.cpu().numpy(), ids.cpu().numpy(), f64(keys), f64(vals), 1)
+    assert np.array_equal(sel.cpu().numpy(), r["sel"])
+    assert np.array_equal(rows.cpu().numpy(), r["n_rows"])
+    o = out.cpu().numpy()
+    empty = target.numpy() >= 5
+    assert empty.any() and (~empty).any()
+    assert np.all(rows.cpu().numpy()[empty] == 0) and np.all(o[empty] == 0.0)
+    assert out_error(o[~empty], r["out"][~empty]) <= OUT_TOL
