@@ -12,6 +12,9 @@
 // Each lane group keeps an online-softmax state (running max m, sum l,
 // output o) in the log2 domain; the four lane groups merge by lane shuffles
 // and the segment writes one partial (m, l, o) per masked head.
+// gather_merge (large bf16 batches of inverted-index plans): the same wave
+// work, but kMergeWaves waves of a workgroup take consecutive segments and
+// merge their states per head in LDS, so the set writes one partial per head.
 // combine: merges each query head's partials with the log-sum-exp rule (one
 // wave per head in large batches, several in small ones) and writes o / l
 // (zero when nothing was selected).
