@@ -117,11 +117,13 @@ def test_no_variant_is_bitwise_the_plain_decode():
     assert torch.equal(a, b)
 
 
-def test_variants_over_a_growing_index():
+# 3 x 2 KV heads: a wave per plan segment; 16 x 8: merged gather sets
+@pytest.mark.parametrize("batch,n_kv_heads", [(3, 2), (16, 8)])
+def test_variants_over_a_growing_index(batch, n_kv_heads):
     """Cosine + sink/window over a dynamic index (list lengths) equals the
     same variants over the compacted static lists."""
-    cfg, p = _problem(seed_scale=3, n_tokens=5000)
-    announce("variants over a growing index")
+    cfg, p = _problem(seed_scale=3, n_tokens=5000, batch=batch, n_kv_heads=n_kv_heads, n_q_heads=4 * n_kv_heads)
+    announce(f"variants over a growing index, {batch} x {n_kv_heads} KV heads")
     n_prefix = 4000
     off, lens, ids = tsa.index_build_dyn(p["keys"], p["centroids"], n_prefix)
     status = torch.empty((cfg.batch, cfg.n_kv_heads), dtype=torch.int32, device=DEV)
