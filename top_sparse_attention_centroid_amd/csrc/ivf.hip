@@ -139,6 +139,10 @@ constexpr int kMfmaCs = 256;      // centroids per LDS stage
 constexpr int kMfmaKb = 1024;     // keys per workgroup
 constexpr int kMfmaWaves = 8;
 constexpr int kCentPad = 136;     // LDS row stride in elements (128 + 8)
+#ifndef TSA_ASSIGN_TILES
+#define TSA_ASSIGN_TILES 2
+#endif
+constexpr int kAssignTiles = TSA_ASSIGN_TILES;  // 16-key tiles scored per pass over the staged centroids
 
 __global__ __launch_bounds__(256) void centroid_norms_kernel(const bf16_t* cent, float* norms, long long rows) {
   const long long row = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) / 16;
@@ -187,63 +191,84 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
     for (int i = tid; i < kMfmaCs; i += kMfmaWaves * kWave) cn[i] = nb[min(c0 + i, p.C - 1)];
     __syncthreads();
     const int ntile = (min(kMfmaCs, p.C - c0) + 15) / 16;
-    for (int kt = wave; kt < kMfmaKb / 16; kt += kMfmaWaves) {
-      const int key0 = kbase + kt * 16;
-      if (key0 >= p.n_assign) break;
-      const bf16_t* kr =
-          keys + ((static_cast<long long>(b) * p.N + min(key0 + col, p.n_assign - 1)) * p.Hkv + g) * kHeadDim + grp * 8;
-      bf16x8_t a[4];
+    // A pass scores kAssignTiles of the wave's 16-key tiles (kt, kt +
+    // kMfmaWaves, ...) against the staged centroids: each B fragment read
+    // from LDS feeds kAssignTiles MFMA chains (LDS reads, not the matrix
+    // cores, bound this loop), and the tiles' keys are requested together.
+    constexpr int NT = kAssignTiles;
+    constexpr int kTiles = kMfmaKb / 16;
+    for (int kt = wave; kt < kTiles; kt += NT * kMfmaWaves) {
+      if (kbase + kt * 16 >= p.n_assign) break;
+      bool on[NT];
+      bf16x8_t a[NT][4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
-      TopM<M> best[4];
+      for (int j = 0; j < NT; ++j) {
+        const int ktj = kt + j * kMfmaWaves;
+        on[j] = ktj < kTiles && kbase + ktj * 16 < p.n_assign;  // uniform over the wave
+        const int key = min(kbase + min(ktj, kTiles - 1) * 16 + col, p.n_assign - 1);  // clamped: in bounds
+        const bf16_t* kr = keys + ((static_cast<long long>(b) * p.N + key) * p.Hkv + g) * kHeadDim + grp * 8;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) best[i].init();
+        for (int ks = 0; ks < 4; ++ks) a[j][ks] = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
+      }
+      TopM<M> best[NT][4];
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) best[j][i].init();
       for (int t = 0; t < ntile; ++t) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         const bf16_t* brow = cs + (t * 16 + col) * kCentPad + grp * 8;
+        bf16x8_t bfr[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], *reinterpret_cast<const bf16x8_t*>(brow + ks * 32),
-                                                        acc, 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks) bfr[ks] = *reinterpret_cast<const bf16x8_t*>(brow + ks * 32);
         const int c = c0 + t * 16 + col;
         const float cnv = cn[t * 16 + col];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (c < p.C) best[i].push(cnv - 2.f * acc[i], c);
-      }
-      // the 16 lanes of a row group hold disjoint centroid columns: merge
-      // their top-M lists by exchanging them over lane distances 8, 4, 2, 1
+        for (int j = 0; j < NT; ++j) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+          for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][ks], bfr[ks], acc, 0, 0, 0);
 #pragma unroll
-        for (int off = 8; off > 0; off >>= 1) {
-          float od[M];
-          int oc[M];
-#pragma unroll
-          for (int r = 0; r < M; ++r) {
-            od[r] = __shfl_xor(best[i].d[r], off);
-            oc[r] = __shfl_xor(best[i].c[r], off);
-          }
-#pragma unroll
-          for (int r = 0; r < M; ++r) best[i].push(od[r], oc[r]);
+          for (int i = 0; i < 4; ++i)
+            if (c < p.C) best[j][i].push(cnv - 2.f * acc[i], c);
         }
       }
-      if (col == 0) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if (!on[j]) continue;  // uniform over the wave
+        // the 16 lanes of a row group hold disjoint centroid columns: merge
+        // their top-M lists by exchanging them over lane distances 8, 4, 2, 1
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kl = kt * 16 + grp * 4 + i;
-          TopM<M> t;
 #pragma unroll
-          for (int r = 0; r < M; ++r) {
-            t.d[r] = best_d[kl * M + r];
-            t.c[r] = best_c[kl * M + r];
+          for (int off = 8; off > 0; off >>= 1) {
+            float od[M];
+            int oc[M];
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+              od[r] = __shfl_xor(best[j][i].d[r], off);
+              oc[r] = __shfl_xor(best[j][i].c[r], off);
+            }
+#pragma unroll
+            for (int r = 0; r < M; ++r) best[j][i].push(od[r], oc[r]);
           }
+        }
+        if (col == 0) {
 #pragma unroll
-          for (int r = 0; r < M; ++r) t.push(best[i].d[r], best[i].c[r]);
+          for (int i = 0; i < 4; ++i) {
+            const int kl = (kt + j * kMfmaWaves) * 16 + grp * 4 + i;
+            TopM<M> tm;
 #pragma unroll
-          for (int r = 0; r < M; ++r) {
-            best_d[kl * M + r] = t.d[r];
-            best_c[kl * M + r] = t.c[r];
+            for (int r = 0; r < M; ++r) {
+              tm.d[r] = best_d[kl * M + r];
+              tm.c[r] = best_c[kl * M + r];
+            }
+#pragma unroll
+            for (int r = 0; r < M; ++r) tm.push(best[j][i].d[r], best[j][i].c[r]);
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+              best_d[kl * M + r] = tm.d[r];
+              best_c[kl * M + r] = tm.c[r];
+            }
           }
         }
       }
