@@ -282,6 +282,107 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
 }
 
 // ============================================================================
+// Index build, step 2 for static lists that fit in LDS (one list per token,
+// no free entries, N <= kCsrStage, C <= kCsrMaxC): the four waves each take a
+// quarter of the tokens. Per-wave LDS histograms give every wave its own
+// cursor per list (lists ordered by token, waves in token order, so ids stay
+// ascending inside a list); each wave places its tokens with the same ballot
+// ranking as below, into an LDS copy of the (request, KV head)'s ids, which is
+// then written out with coalesced stores. Scattered 4-byte stores straight to
+// memory cost a 16-byte write each (4x the ids' bytes) and one wave per
+// workgroup placed all the tokens.
+// ============================================================================
+constexpr int kCsrStage = 32768;  // token ids staged in LDS (128 KiB)
+constexpr int kCsrMaxC = 1024;    // lists with per-wave counters in LDS
+constexpr int kCsrWaves = 4;
+constexpr int kCsrBatch = 16;     // 64-token chunks whose list ids a wave requests together
+
+__global__ __launch_bounds__(kCsrWaves * kWave) void csr_staged_kernel(CsrParams p) {
+  __shared__ int stage[kCsrStage];
+  __shared__ int hist[kCsrWaves][kCsrMaxC];  // counts, then cursors
+  __shared__ int scan_scratch[kCsrWaves];
+  const int bg = blockIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int n = p.n_assign, C = p.C;
+  const int32_t* a = p.assign + static_cast<long long>(bg) * p.N;
+  int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
+  int32_t* ids = p.ids + static_cast<long long>(bg) * p.N;
+  const int lo = wave * n / kCsrWaves, hi = (wave + 1) * n / kCsrWaves;  // this wave's tokens
+
+  // a wave's list ids arrive kCsrBatch chunks of 64 at a time (one memory
+  // round trip per batch, not per chunk): -1 past the wave's range
+  auto load_batch = [&](int i0, int (&cc)[kCsrBatch]) {
+    int raw[kCsrBatch];
+#pragma unroll
+    for (int u = 0; u < kCsrBatch; ++u) raw[u] = a[min(i0 + u * kWave + lane, hi - 1)];  // straight-line, in range
+#pragma unroll
+    for (int u = 0; u < kCsrBatch; ++u) cc[u] = i0 + u * kWave + lane < hi ? min(max(raw[u], 0), C - 1) : -1;
+  };
+  for (int i = tid; i < kCsrWaves * kCsrMaxC; i += kCsrWaves * kWave) hist[i / kCsrMaxC][i % kCsrMaxC] = 0;
+  __syncthreads();
+  for (int i0 = lo; i0 < hi; i0 += kCsrBatch * kWave) {
+    int cc[kCsrBatch];
+    load_batch(i0, cc);
+#pragma unroll
+    for (int u = 0; u < kCsrBatch; ++u)
+      if (cc[u] >= 0) atomicAdd(&hist[wave][cc[u]], 1);
+  }
+  __syncthreads();
+  // list starts by one block scan of the totals; each wave's cursor follows
+  // the lower waves' entries of the list
+  int carry = 0;
+  for (int c0 = 0; c0 < C; c0 += kCsrWaves * kWave) {
+    const int c = c0 + tid;
+    int cnt[kCsrWaves], tot_c = 0;
+#pragma unroll
+    for (int w = 0; w < kCsrWaves; ++w) {
+      cnt[w] = c < C ? hist[w][c] : 0;
+      tot_c += cnt[w];
+    }
+    int tot;
+    const int ex = block_exclusive_scan<kCsrWaves>(tot_c, scan_scratch, &tot);
+    if (c < C) {
+      int run = carry + ex;
+      off[c] = run;
+#pragma unroll
+      for (int w = 0; w < kCsrWaves; ++w) {
+        hist[w][c] = run;
+        run += cnt[w];
+      }
+    }
+    carry += tot;
+  }
+  if (tid == 0) off[C] = carry;  // == n
+  __syncthreads();
+  const int nbits = C > 1 ? 32 - __clz(C - 1) : 0;
+  int* cur = hist[wave];
+  for (int i0 = lo; i0 < hi; i0 += kCsrBatch * kWave) {
+    int cc[kCsrBatch];
+    load_batch(i0, cc);
+#pragma unroll
+    for (int u = 0; u < kCsrBatch; ++u) {
+      const int i = i0 + u * kWave + lane;
+      const bool valid = cc[u] >= 0;
+      const int c = valid ? cc[u] : 0;
+      uint64_t same = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (c >> bit) & 1;
+        const uint64_t bal = __ballot(set);
+        same &= set ? bal : ~bal;
+      }
+      if (valid) {
+        const int rank = prefix_count(same);
+        const int pos = cur[c] + rank;
+        stage[pos] = i;
+        if (rank == __popcll(same) - 1) cur[c] = pos + 1;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < p.N; i += kCsrWaves * kWave) ids[i] = i < n ? stage[i] : -1;
+}
+
+// ============================================================================
 // Index build, step 2: CSR posting lists, token ids ascending inside a list.
 // One workgroup per (request, KV head): LDS histogram, exclusive scan, then a
 // single wave walks the tokens in order; lanes sharing a list find each other
@@ -861,7 +962,10 @@ hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_csr(const CsrParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(csr_kernel, dim3(p.B * p.Hkv), dim3(256), p.C * sizeof(int), s, p);
+  if (p.m == 1 && !p.alt && !p.lens && p.slack == 0 && p.N <= kCsrStage && p.C <= kCsrMaxC)
+    hipLaunchKernelGGL(csr_staged_kernel, dim3(p.B * p.Hkv), dim3(kCsrWaves * kWave), 0, s, p);
+  else
+    hipLaunchKernelGGL(csr_kernel, dim3(p.B * p.Hkv), dim3(256), p.C * sizeof(int), s, p);
   return hipGetLastError();
 }
 
