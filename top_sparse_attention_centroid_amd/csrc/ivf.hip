@@ -282,35 +282,37 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
 }
 
 // ============================================================================
-// Index build, step 2 for static lists that fit in LDS (one list per token,
-// no free entries, N <= kCsrStage, C <= kCsrMaxC): the four waves each take a
-// quarter of the tokens. Per-wave LDS histograms give every wave its own
-// cursor per list (lists ordered by token, waves in token order, so ids stay
-// ascending inside a list); each wave places its tokens with the same ballot
-// ranking as below, into an LDS copy of the (request, KV head)'s ids, which is
-// then written out with coalesced stores. Scattered 4-byte stores straight to
-// memory cost a 16-byte write each (4x the ids' bytes) and one wave per
-// workgroup placed all the tokens.
+// Index build, step 2 for static lists (one list per token, no free entries,
+// C <= kCsrMaxC): the NW waves of a workgroup each take a contiguous share of
+// the tokens. Per-wave LDS histograms give every wave its own cursor per list
+// (lists ordered by token, waves in token order, so ids stay ascending inside
+// a list); each wave places its tokens with the same ballot ranking as
+// csr_kernel below, its list ids requested kCsrBatch chunks at a time. With
+// STAGED (N <= kCsrStage) the ids go to an LDS copy of the (request, KV
+// head)'s list, written out with coalesced stores; otherwise straight to
+// memory (long contexts, where few workgroups need many waves). The
+// one-wave csr_kernel placed every token itself and wrote each 4-byte id
+// straight to memory (a 16-byte write each).
 // ============================================================================
 constexpr int kCsrStage = 32768;  // token ids staged in LDS (128 KiB)
 constexpr int kCsrMaxC = 1024;    // lists with per-wave counters in LDS
-constexpr int kCsrWaves = 4;
 constexpr int kCsrBatch = 16;     // 64-token chunks whose list ids a wave requests together
 
-__global__ __launch_bounds__(kCsrWaves * kWave) void csr_staged_kernel(CsrParams p) {
-  __shared__ int stage[kCsrStage];
-  __shared__ int hist[kCsrWaves][kCsrMaxC];  // counts, then cursors
-  __shared__ int scan_scratch[kCsrWaves];
+template <int NW, bool STAGED>
+__global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
+  __shared__ int stage[STAGED ? kCsrStage : 1];
+  __shared__ int hist[NW][kCsrMaxC];  // counts, then cursors
+  __shared__ int scan_scratch[NW];
   const int bg = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int n = p.n_assign, C = p.C;
   const int32_t* a = p.assign + static_cast<long long>(bg) * p.N;
   int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
   int32_t* ids = p.ids + static_cast<long long>(bg) * p.N;
-  const int lo = wave * n / kCsrWaves, hi = (wave + 1) * n / kCsrWaves;  // this wave's tokens
+  const int lo = static_cast<int>(static_cast<long long>(wave) * n / NW);
+  const int hi = static_cast<int>(static_cast<long long>(wave + 1) * n / NW);  // this wave's tokens
 
-  // a wave's list ids arrive kCsrBatch chunks of 64 at a time (one memory
-  // round trip per batch, not per chunk): -1 past the wave's range
+  // list ids of kCsrBatch chunks of 64 in one round trip: -1 past the range
   auto load_batch = [&](int i0, int (&cc)[kCsrBatch]) {
     int raw[kCsrBatch];
 #pragma unroll
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(kCsrWaves * kWave) void csr_staged_kernel(CsrParams
 #pragma unroll
     for (int u = 0; u < kCsrBatch; ++u) cc[u] = i0 + u * kWave + lane < hi ? min(max(raw[u], 0), C - 1) : -1;
   };
-  for (int i = tid; i < kCsrWaves * kCsrMaxC; i += kCsrWaves * kWave) hist[i / kCsrMaxC][i % kCsrMaxC] = 0;
+  for (int i = tid; i < NW * kCsrMaxC; i += NW * kWave) hist[i / kCsrMaxC][i % kCsrMaxC] = 0;
   __syncthreads();
   for (int i0 = lo; i0 < hi; i0 += kCsrBatch * kWave) {
     int cc[kCsrBatch];
@@ -331,23 +333,19 @@ __global__ __launch_bounds__(kCsrWaves * kWave) void csr_staged_kernel(CsrParams
   // list starts by one block scan of the totals; each wave's cursor follows
   // the lower waves' entries of the list
   int carry = 0;
-  for (int c0 = 0; c0 < C; c0 += kCsrWaves * kWave) {
+  for (int c0 = 0; c0 < C; c0 += NW * kWave) {
     const int c = c0 + tid;
-    int cnt[kCsrWaves], tot_c = 0;
-#pragma unroll
-    for (int w = 0; w < kCsrWaves; ++w) {
-      cnt[w] = c < C ? hist[w][c] : 0;
-      tot_c += cnt[w];
-    }
+    int tot_c = 0;
+    for (int w = 0; w < NW; ++w) tot_c += c < C ? hist[w][c] : 0;
     int tot;
-    const int ex = block_exclusive_scan<kCsrWaves>(tot_c, scan_scratch, &tot);
+    const int ex = block_exclusive_scan<NW>(tot_c, scan_scratch, &tot);
     if (c < C) {
       int run = carry + ex;
       off[c] = run;
-#pragma unroll
-      for (int w = 0; w < kCsrWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
+        const int cnt = hist[w][c];
         hist[w][c] = run;
-        run += cnt[w];
+        run += cnt;
       }
     }
     carry += tot;
@@ -373,13 +371,18 @@ __global__ __launch_bounds__(kCsrWaves * kWave) void csr_staged_kernel(CsrParams
       if (valid) {
         const int rank = prefix_count(same);
         const int pos = cur[c] + rank;
-        stage[pos] = i;
+        if constexpr (STAGED) stage[pos] = i;
+        else ids[pos] = i;
         if (rank == __popcll(same) - 1) cur[c] = pos + 1;
       }
     }
   }
-  __syncthreads();
-  for (int i = tid; i < p.N; i += kCsrWaves * kWave) ids[i] = i < n ? stage[i] : -1;
+  if constexpr (STAGED) {
+    __syncthreads();
+    for (int i = tid; i < p.N; i += NW * kWave) ids[i] = i < n ? stage[i] : -1;
+  } else {
+    for (int i = n + tid; i < p.N; i += NW * kWave) ids[i] = -1;  // tokens not indexed yet
+  }
 }
 
 // ============================================================================
@@ -961,11 +964,19 @@ hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Static lists with up to kCsrMaxC lists: 4 waves staging in LDS when a
+// (request, KV head)'s ids fit there (128 KiB + counters leaves one
+// workgroup per CU), else 16 waves writing to memory; other indexes (2-way
+// lists, free entries, more lists) take csr_kernel.
 hipError_t launch_csr(const CsrParams& p, hipStream_t s) {
-  if (p.m == 1 && !p.alt && !p.lens && p.slack == 0 && p.N <= kCsrStage && p.C <= kCsrMaxC)
-    hipLaunchKernelGGL(csr_staged_kernel, dim3(p.B * p.Hkv), dim3(kCsrWaves * kWave), 0, s, p);
+  const dim3 grid(p.B * p.Hkv);
+  const bool fast = p.m == 1 && !p.alt && !p.lens && p.slack == 0 && p.C <= kCsrMaxC;
+  if (fast && p.N <= kCsrStage)
+    hipLaunchKernelGGL((csr_waves_kernel<4, true>), grid, dim3(4 * kWave), 0, s, p);
+  else if (fast)
+    hipLaunchKernelGGL((csr_waves_kernel<16, false>), grid, dim3(16 * kWave), 0, s, p);
   else
-    hipLaunchKernelGGL(csr_kernel, dim3(p.B * p.Hkv), dim3(256), p.C * sizeof(int), s, p);
+    hipLaunchKernelGGL(csr_kernel, grid, dim3(256), p.C * sizeof(int), s, p);
   return hipGetLastError();
 }
 
