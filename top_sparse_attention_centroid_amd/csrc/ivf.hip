@@ -282,9 +282,8 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
 }
 
 // ============================================================================
-// Index build, step 2 for static lists (one list per token, no free entries,
-// C <= kCsrMaxC): the NW waves of a workgroup each take a contiguous share of
-// the tokens. Per-wave LDS histograms give every wave its own cursor per list
+// Index build, step 2 for codebooks of up to kCsrMaxC lists: the NW waves of
+// a workgroup each take a contiguous share of the (token, list) entries. Per-wave LDS histograms give every wave its own cursor per list
 // (lists ordered by token, waves in token order, so ids stay ascending inside
 // a list); each wave places its tokens with the same ballot ranking as
 // csr_kernel below, its list ids requested kCsrBatch chunks at a time. With
@@ -305,12 +304,20 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
   __shared__ int scan_scratch[NW];
   const int bg = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int n = p.n_assign, C = p.C;
-  const int32_t* a = p.assign + static_cast<long long>(bg) * p.N;
+  const int C = p.C, m = p.m;
+  const int n = p.n_assign * m;                          // (token, list) entries, token-major
+  const long long cap = static_cast<long long>(p.N) * m;
+  const int32_t* a = p.assign + static_cast<long long>(bg) * cap;
   int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
-  int32_t* ids = p.ids + static_cast<long long>(bg) * p.N;
+  int32_t* ids = p.ids + static_cast<long long>(bg) * cap;
+  int32_t* alt = p.alt ? p.alt + static_cast<long long>(bg) * cap : nullptr;
+  int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * C : nullptr;
   const int lo = static_cast<int>(static_cast<long long>(wave) * n / NW);
-  const int hi = static_cast<int>(static_cast<long long>(wave + 1) * n / NW);  // this wave's tokens
+  const int hi = static_cast<int>(static_cast<long long>(wave + 1) * n / NW);  // this wave's entries
+  auto put_id = [&](long long pos, int v) {
+    if constexpr (STAGED) stage[pos] = v;
+    else ids[pos] = v;
+  };
 
   // list ids of kCsrBatch chunks of 64 in one round trip: -1 past the range
   auto load_batch = [&](int i0, int (&cc)[kCsrBatch]) {
@@ -321,6 +328,8 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
     for (int u = 0; u < kCsrBatch; ++u) cc[u] = i0 + u * kWave + lane < hi ? min(max(raw[u], 0), C - 1) : -1;
   };
   for (int i = tid; i < NW * kCsrMaxC; i += NW * kWave) hist[i / kCsrMaxC][i % kCsrMaxC] = 0;
+  if constexpr (STAGED)
+    for (int i = tid; i < cap; i += NW * kWave) stage[i] = -1;  // free entries and the tail stay -1
   __syncthreads();
   for (int i0 = lo; i0 < hi; i0 += kCsrBatch * kWave) {
     int cc[kCsrBatch];
@@ -330,18 +339,22 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
       if (cc[u] >= 0) atomicAdd(&hist[wave][cc[u]], 1);
   }
   __syncthreads();
-  // list starts by one block scan of the totals; each wave's cursor follows
-  // the lower waves' entries of the list
+  // list starts by one block scan of the totals (plus the free entries after
+  // every list); each wave's cursor follows the lower waves' entries
   int carry = 0;
   for (int c0 = 0; c0 < C; c0 += NW * kWave) {
     const int c = c0 + tid;
     int tot_c = 0;
     for (int w = 0; w < NW; ++w) tot_c += c < C ? hist[w][c] : 0;
     int tot;
-    const int ex = block_exclusive_scan<NW>(tot_c, scan_scratch, &tot);
+    const int ex = block_exclusive_scan<NW>(tot_c + (c < C ? p.slack : 0), scan_scratch, &tot);
     if (c < C) {
-      int run = carry + ex;
-      off[c] = run;
+      const int start = carry + ex;
+      off[c] = start;
+      if (lens) lens[c] = tot_c;
+      if constexpr (!STAGED)
+        for (int j = tot_c; j < tot_c + p.slack; ++j) ids[start + j] = -1;  // free entries
+      int run = start;
       for (int w = 0; w < NW; ++w) {
         const int cnt = hist[w][c];
         hist[w][c] = run;
@@ -350,7 +363,9 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
     }
     carry += tot;
   }
-  if (tid == 0) off[C] = carry;  // == n
+  if (tid == 0) off[C] = carry;  // n + C * slack <= N * m
+  if constexpr (!STAGED)
+    for (long long i = carry + tid; i < cap; i += NW * kWave) ids[i] = -1;  // entries not in use yet
   __syncthreads();
   const int nbits = C > 1 ? 32 - __clz(C - 1) : 0;
   int* cur = hist[wave];
@@ -371,17 +386,15 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
       if (valid) {
         const int rank = prefix_count(same);
         const int pos = cur[c] + rank;
-        if constexpr (STAGED) stage[pos] = i;
-        else ids[pos] = i;
+        put_id(pos, i / m);                  // entries of one token are adjacent: ascending ids per list
+        if (alt) alt[pos] = a[min(i ^ 1, n - 1)];  // m == 2: the token's other list
         if (rank == __popcll(same) - 1) cur[c] = pos + 1;
       }
     }
   }
   if constexpr (STAGED) {
     __syncthreads();
-    for (int i = tid; i < p.N; i += NW * kWave) ids[i] = i < n ? stage[i] : -1;
-  } else {
-    for (int i = n + tid; i < p.N; i += NW * kWave) ids[i] = -1;  // tokens not indexed yet
+    for (int i = tid; i < cap; i += NW * kWave) ids[i] = stage[i];
   }
 }
 
@@ -964,16 +977,16 @@ hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Static lists with up to kCsrMaxC lists: 4 waves staging in LDS when a
-// (request, KV head)'s ids fit there (128 KiB + counters leaves one
-// workgroup per CU), else 16 waves writing to memory; other indexes (2-way
-// lists, free entries, more lists) take csr_kernel.
+// Up to kCsrMaxC lists: 4 waves staging the ids in LDS when a (request, KV
+// head)'s ids fit there and no second array is written (128 KiB + counters
+// leaves one workgroup per CU), else 16 waves writing to memory; larger
+// codebooks take csr_kernel.
 hipError_t launch_csr(const CsrParams& p, hipStream_t s) {
   const dim3 grid(p.B * p.Hkv);
-  const bool fast = p.m == 1 && !p.alt && !p.lens && p.slack == 0 && p.C <= kCsrMaxC;
-  if (fast && p.N <= kCsrStage)
+  const long long cap = static_cast<long long>(p.N) * p.m;
+  if (p.C <= kCsrMaxC && !p.alt && cap <= kCsrStage)
     hipLaunchKernelGGL((csr_waves_kernel<4, true>), grid, dim3(4 * kWave), 0, s, p);
-  else if (fast)
+  else if (p.C <= kCsrMaxC)
     hipLaunchKernelGGL((csr_waves_kernel<16, false>), grid, dim3(16 * kWave), 0, s, p);
   else
     hipLaunchKernelGGL(csr_kernel, grid, dim3(256), p.C * sizeof(int), s, p);
