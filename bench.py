@@ -91,10 +91,10 @@ def gather_source_sha() -> str:
 def gather_kernel_name(cfg, args) -> str:
     """The gather kernel libtsa launches for this workload: merged sets of
     plan segments for inverted-index batches of at least 128 bf16
-    (request, KV head) groups with up to 4 query heads per KV head and one
-    list per key; one wave per segment (or per row-list segment) otherwise."""
+    (request, KV head) groups with up to 4 query heads per KV head; one wave
+    per segment (or per row-list segment) otherwise."""
     groups = cfg.batch * cfg.n_kv_heads
-    if cfg.kind == "ivf" and groups >= 128 and cfg.dtype == "bf16" and cfg.group <= 4 and args.assign == 1:
+    if cfg.kind == "ivf" and groups >= 128 and cfg.dtype == "bf16" and cfg.group <= 4:
         return "gather_merge_kernel"
     return "gather_attn_kernel"
 

@@ -153,3 +153,27 @@ def test_merged_sets_empty_groups():
     assert empty.any() and (~empty).any()
     assert np.all(rows.cpu().numpy()[empty] == 0) and np.all(o[empty] == 0.0)
     assert out_error(o[~empty], r["out"][~empty]) <= OUT_TOL
+
+
+@pytest.mark.parametrize("batch", [2, 16])
+def test_workspace_contents_never_reach_the_output(batch):
+    # Records a head does not own stay unwritten; whatever the caller's
+    # workspace held before (here NaN bit patterns, then zeros) must not
+    # change the output. 2 x 8 groups: a wave per segment; 16 x 8: merged sets.
+    cfg = W.config(2, batch=batch, n_tokens=4096, n_centroids=24, top_k=6, steps=1, seed=53)
+    announce(f"workspace contents, {batch} requests")
+    p = W.ivf_problem(cfg, device=DEV)
+    offsets, ids = tsa.index_build(p["keys"], p["centroids"])
+    q = conditioned_ivf_queries(cfg, p["centroids"], 1)[0]
+    desc = tsa.binding.ivf_desc(p["keys"], p["centroids"], cfg.n_q_heads)
+    nbytes = tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX, desc, cfg.top_k)
+    lengths = torch.tensor([4096 - 97 * b for b in range(batch)], dtype=torch.int32, device=DEV)
+    outs = []
+    for fill in (0xFF, 0x00):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        for kw in ({}, {"n_sink": 64, "n_window": 300, "lengths": lengths}):
+            outs.append(tsa.sparse_decode_ex(q, p["centroids"], offsets, ids, p["keys"], p["values"], cfg.top_k,
+                                             ws=ws, **kw))
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(o).all()) for o in outs)
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3])

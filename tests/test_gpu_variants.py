@@ -190,9 +190,12 @@ def test_token_selection_feeds_the_hot_cache():
     assert misses[0] == B * k and min(misses[1:]) < B * k   # planted tokens stay selected and hit
 
 
-def _two_way_keys(cfg, centroids, seed):
+def _two_way_keys(cfg, centroids, seed, min_gap=None):
     """Keys between two centroids (0.6 c_a + 0.4 c_b + 0.1 noise, a != b): a
-    clear first and second nearest list and a wide margin to the third."""
+    clear first and second nearest list and a wide margin to the third.
+    With min_gap, keys whose second-vs-third choice margin (as the oracle
+    measures it on the stored values) is below it get fresh noise until
+    none is left (many keys reach deeper into the margin's tail)."""
     g = torch.Generator().manual_seed(seed)
     B, N, Hkv, d = cfg.batch, cfg.n_tokens, cfg.n_kv_heads, cfg.head_dim
     C = centroids.shape[2]
@@ -200,17 +203,38 @@ def _two_way_keys(cfg, centroids, seed):
     a = torch.randint(0, C, (B, N, Hkv), generator=g)
     b = (a + torch.randint(1, C, (B, N, Hkv), generator=g)) % C
     head = torch.arange(Hkv)[None, None, :].expand(B, N, Hkv)
-    keys = 0.6 * cent[0][head, a] + 0.4 * cent[0][head, b] + 0.1 * torch.randn((B, N, Hkv, d), generator=g)
-    return keys.to(cfg.torch_dtype).to(DEV)
+    keys = (0.6 * cent[0][head, a] + 0.4 * cent[0][head, b] + 0.1 * torch.randn((B, N, Hkv, d), generator=g))
+    keys = keys.to(cfg.torch_dtype)
+    if min_gap is not None:
+        c64 = centroids.double().cpu().numpy()
+        for _ in range(20):
+            redrawn = 0
+            for bi in range(B):
+                for gi in range(Hkv):
+                    _, gap = variants.nearest_centroids(keys[bi, :, gi].double().numpy(), c64[0, gi], 2)
+                    bad = torch.from_numpy(np.nonzero(gap < min_gap)[0])
+                    if len(bad):
+                        redrawn += len(bad)
+                        fresh = (0.6 * cent[0, gi][a[bi, bad, gi]] + 0.4 * cent[0, gi][b[bi, bad, gi]]
+                                 + 0.1 * torch.randn((len(bad), d), generator=g))
+                        keys[bi, bad, gi] = fresh.to(cfg.torch_dtype)
+            if redrawn == 0:
+                break
+        else:
+            raise RuntimeError("could not draw keys with the required second-choice margin")
+    return keys.to(DEV)
 
 
-def test_two_way_lists_build_and_decode():
+# 3 x 2 KV heads: a wave per plan segment; 16 x 8: merged gather sets
+@pytest.mark.parametrize("batch,n_kv_heads", [(3, 2), (16, 8)])
+def test_two_way_lists_build_and_decode(batch, n_kv_heads):
     """Every key in its two nearest lists: lists and alt exact against the
     oracle; decode attends each token once per head (union of the lists),
     alone and with cosine + sink/window."""
-    cfg, p = _problem(n_tokens=4000, n_centroids=32, top_k=5)
-    announce("variants: two lists per key")
-    p["keys"] = _two_way_keys(cfg, p["centroids"], 17)
+    cfg, p = _problem(n_tokens=4000, n_centroids=32, top_k=5, batch=batch, n_kv_heads=n_kv_heads,
+                      n_q_heads=4 * n_kv_heads)
+    announce(f"variants: two lists per key, {batch} x {n_kv_heads} KV heads")
+    p["keys"] = _two_way_keys(cfg, p["centroids"], 17, min_gap=2e-3 if batch * n_kv_heads >= 128 else None)
     off, ids, alt = tsa.index_build_multi(p["keys"], p["centroids"], 2)
     torch.cuda.synchronize()
     k64, c64 = f64(p["keys"]), f64(p["centroids"])

@@ -529,12 +529,16 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
 // (Splitting a set's rows evenly over the waves, or aligning each head class
 // to a set with empty segments, measured slower: the first adds a barrier
 // between staging and streaming, the second idle waves.)
-template <typename T, int G>
+// DUP: 2-way lists, whose rows carry per-head duplicate masks (each head
+// attends a token through the lower of its two chosen lists); every head of
+// a segment then takes its own pass.
+template <typename T, int G, bool DUP>
 __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(GatherParams p) {
   constexpr int NW = kMergeWaves;
   constexpr int kHeadsPerWave = (G + NW - 1) / NW;  // heads each wave merges
   __shared__ __align__(16) T qs[G * kHeadDim];
   __shared__ int ids_lds[NW][kSegRows];
+  __shared__ uint32_t dup_lds[DUP ? NW : 1][DUP ? kSegRows : 1];
   __shared__ float sm_m[NW][G], sm_l[NW][G];
   __shared__ __align__(16) float sm_o[NW][G][kHeadDim];
   const int bg = blockIdx.x / p.W, w0 = blockIdx.x % p.W;
@@ -562,6 +566,8 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(Gathe
                 g * kHeadDim + e * 8;
   const int32_t* rid = p.rowids + b * p.rid_bstride + g * p.rid_gstride;
   int* ids = ids_lds[wave];
+  uint32_t* dup = dup_lds[DUP ? wave : 0];
+  const int32_t* altb = DUP ? p.alt + b * p.rid_bstride + g * p.rid_gstride : nullptr;
   // sink / window ranges: list rows inside them are skipped (attended
   // through their own direct segments)
   int fx_sink = 0, fx_lo = 0, fx_hi = 0;
@@ -577,7 +583,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(Gathe
     // every wave reads the set's descriptors (the same addresses): its own
     // segment, and the head masks of all of them
     uint32_t msk[NW];
-    int my_start = 0, my_cnt = 0;
+    int my_start = 0, my_cnt = 0, my_list = -1;
     bool my_direct = false;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
@@ -588,6 +594,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(Gathe
         my_start = d.x;
         my_cnt = in ? min(max(d.y, 0), kSegRows) : 0;
         my_direct = d.w < 0;
+        my_list = d.w;
       }
     }
     uint32_t U = 0u, my_mask = 0u;
@@ -603,6 +610,14 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(Gathe
       bool ok = static_cast<unsigned long long>(id) < static_cast<unsigned long long>(p.n_rows);
       if (!my_direct) ok = ok && !(id < fx_sink || (id >= fx_lo && id < fx_hi));
       ids[j] = ok ? id : -1;
+      if constexpr (DUP) {  // heads that attend this token through a lower chosen list
+        uint32_t dm = 0u;
+        if (!my_direct) {
+          const int other = altb[my_start + j];
+          if (other >= 0 && other < my_list && other < p.C) dm = p.lmask[static_cast<long long>(bg) * p.C + other];
+        }
+        dup[j] = dm;
+      }
     }
     __syncthreads();  // queries staged (first set); the ids are wave-private
 
@@ -616,10 +631,15 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(Gathe
         }
       }
     };
-    if (my_mask != 0u && (my_mask & (my_mask - 1u)) == 0u) {
+    if (DUP && (my_mask & (my_mask - 1u)) != 0u) {
+      // several heads with per-head duplicate masks: a cacheable pass each
+      for (uint32_t hm = my_mask; hm != 0u; hm &= hm - 1u) {
+        const int h = __builtin_ctz(hm);
+        put(h, head_pass<false, DUP>(h, ids, my_cnt, r, e, kb, vb, row_stride, qs, p.qscale, dup));
+      }
+    } else if (my_mask != 0u && (my_mask & (my_mask - 1u)) == 0u) {
       const int h = __builtin_ctz(my_mask);
-      put(h, head_pass<TSA_GATHER_NT != 0, false>(h, ids, my_cnt, r, e, kb, vb, row_stride, qs, p.qscale,
-                                                  nullptr));
+      put(h, head_pass<TSA_GATHER_NT != 0, DUP>(h, ids, my_cnt, r, e, kb, vb, row_stride, qs, p.qscale, dup));
     } else if (my_mask != 0u) {  // a list several heads chose, or a sink / window range
       HeadState st[G];
       all_heads_states<G>(st, ids, my_cnt, r, e, kb, vb, row_stride, qs, p.qscale, [](int) { return ~0u; });
@@ -754,15 +774,18 @@ __global__ __launch_bounds__(GH * NS * kWave) void combine_kernel(GatherParams p
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int jj = j[u] < 0 ? 0 : j[u];  // j < 0: reload segment `part` (in range), weight 0
+        // j < 0: a padding slot reloads record `part` (in range, so the load
+        // stays straight-line) and is never added: that record need not hold
+        // this head's state, and its stale bits may be NaN (0 * NaN = NaN)
+        const int jj = j[u] < 0 ? 0 : j[u];
         wj[u] = j[u] < 0 ? 0.f : __shfl(w, jj);
         po[u] = *reinterpret_cast<const float2*>(base + (j[u] < 0 ? part : part + (i0 + jj) * NS) * rec_stride +
                                                  kPartO + lane * 2);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        O0 = fmaf(wj[u], po[u].x, O0);
-        O1 = fmaf(wj[u], po[u].y, O1);
+        O0 = j[u] < 0 ? O0 : fmaf(wj[u], po[u].x, O0);
+        O1 = j[u] < 0 ? O1 : fmaf(wj[u], po[u].y, O1);
       }
     }
   }
@@ -810,13 +833,22 @@ static void gather_dispatch(const GatherParams& p, int G, hipStream_t s) {
 hipError_t launch_gather(const GatherParams& p, int dtype, int G, bool explicit_plan,
                          hipStream_t s) {
   if (explicit_plan && p.merge) {
-    if (dtype != kBF16 || p.alt) return hipErrorInvalidValue;
+    if (dtype != kBF16) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(p.B * p.Hkv * p.W)), block(kMergeWaves * kWave);
-    switch (G) {
-      case 1: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 1>), grid, block, 0, s, p); break;
-      case 2: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 2>), grid, block, 0, s, p); break;
-      case 4: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 4>), grid, block, 0, s, p); break;
-      default: return hipErrorInvalidValue;
+    if (p.alt) {
+      switch (G) {
+        case 1: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 1, true>), grid, block, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 2, true>), grid, block, 0, s, p); break;
+        case 4: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 4, true>), grid, block, 0, s, p); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (G) {
+        case 1: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 1, false>), grid, block, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 2, false>), grid, block, 0, s, p); break;
+        case 4: hipLaunchKernelGGL((gather_merge_kernel<bf16_t, 4, false>), grid, block, 0, s, p); break;
+        default: return hipErrorInvalidValue;
+      }
     }
     return hipGetLastError();
   }

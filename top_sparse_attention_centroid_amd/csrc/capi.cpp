@@ -155,9 +155,9 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false, int 
   L.small_batch = static_cast<long long>(bh) < kSmallBatchGroups;
   // Large bf16 batches (bound by HBM) with up to 4 query heads per KV head
   // gather in merged sets of kMergeWaves segments; small ones, bound by the
-  // latency of their waves, keep a wave per segment, and so do 2-way lists
-  // (per-row duplicate masks), fp32 and wider groups.
-  L.merge = !L.small_batch && m == 1 && d.dtype == TSA_BF16 && L.G <= 4;
+  // latency of their waves, keep a wave per segment, and so do fp32 and
+  // wider groups.
+  L.merge = !L.small_batch && d.dtype == TSA_BF16 && L.G <= 4;
   L.smax = L.G * k + ceil_div(static_cast<long long>(d.n_tokens) * m, L.seg_rows) +
            (with_fixed ? kMaxFixedRows / L.seg_rows + 2 : 0);
   size_t off = 0;
