@@ -114,3 +114,26 @@ def test_token_workload_full_size_sampled():
     cfg = W.config(3)
     announce(f"token {cfg.name} full size")
     _run(cfg, 2, range(cfg.batch), [0, 9])
+
+
+def test_token_workspace_contents_never_reach_the_output():
+    # The row-list attention merges partial states like the inverted-index
+    # path: a workspace holding NaN bit patterns, then zeros, before the call
+    # gives bitwise equal, finite outputs and the same selection.
+    cfg = W.config(3, batch=3, n_tokens=20_001, top_k=1000, n_planted=64, steps=1)
+    announce("token workspace contents")
+    prob = W.token_problem(cfg, device=DEV)
+    q_idx, q = W.token_queries(cfg, prob, steps=1)
+    B, k = cfg.batch, cfg.top_k
+    desc = tsa.binding.token_desc(prob["k_idx"], prob["keys"], cfg.n_q_heads)
+    nbytes = tsa.workspace_bytes(tsa.binding.OP_TOKEN_DECODE, desc, k)
+    outs, sels = [], []
+    for fill in (0xFF, 0x00):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        sel = torch.empty((B, k), dtype=torch.int32, device=DEV)
+        outs.append(tsa.token_decode(q_idx[0], prob["k_idx"], q[0], prob["keys"], prob["values"], k, sel_out=sel,
+                                     ws=ws))
+        sels.append(sel)
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(o).all()) for o in outs)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(sels[0], sels[1])
