@@ -116,12 +116,14 @@ def test_token_workload_full_size_sampled():
     _run(cfg, 2, range(cfg.batch), [0, 9])
 
 
-def test_token_workspace_contents_never_reach_the_output():
+# a small and a large batch (3 and 16 requests x 8 KV heads)
+@pytest.mark.parametrize("batch", [3, 16])
+def test_token_workspace_contents_never_reach_the_output(batch):
     # The row-list attention merges partial states like the inverted-index
     # path: a workspace holding NaN bit patterns, then zeros, before the call
     # gives bitwise equal, finite outputs and the same selection.
-    cfg = W.config(3, batch=3, n_tokens=20_001, top_k=1000, n_planted=64, steps=1)
-    announce("token workspace contents")
+    cfg = W.config(3, batch=batch, n_tokens=20_001, top_k=1000, n_planted=64, steps=1)
+    announce(f"token workspace contents, {batch} requests")
     prob = W.token_problem(cfg, device=DEV)
     q_idx, q = W.token_queries(cfg, prob, steps=1)
     B, k = cfg.batch, cfg.top_k
