@@ -177,3 +177,25 @@ def test_workspace_contents_never_reach_the_output(batch):
     torch.cuda.synchronize()
     assert all(bool(torch.isfinite(o).all()) for o in outs)
     assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3])
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_merged_sets_fewer_query_heads_than_waves(G):
+    # 16 x 8 groups with 1 or 2 query heads per KV head: some waves of a set
+    # merge no head; every request and head against the oracle.
+    cfg = W.config(2, batch=16, n_tokens=4096, n_kv_heads=8, n_q_heads=8 * G, n_centroids=24, top_k=6, steps=1,
+                   seed=54 + G)
+    announce(f"merged sets, {G} query heads per KV head")
+    p = W.ivf_problem(cfg, device=DEV)
+    offsets, ids = _index_checked(p)
+    q = conditioned_ivf_queries(cfg, p["centroids"], 1)[0]
+    B, Hq, k = cfg.batch, cfg.n_q_heads, cfg.top_k
+    sel = torch.empty((B, Hq, k), dtype=torch.int32, device=DEV)
+    out = tsa.sparse_decode(q, p["centroids"], offsets, ids, p["keys"], p["values"], k, sel_out=sel)
+    torch.cuda.synchronize()
+    r = ivf.sparse_decode(f64(q), f64(p["centroids"]), offsets.cpu().numpy(), ids.cpu().numpy(), f64(p["keys"]),
+                          f64(p["values"]), k)
+    assert np.all(r["gap"] >= GAP_MIN)
+    assert np.array_equal(sel.cpu().numpy(), r["sel"])
+    err = out_error(out.cpu().numpy(), r["out"])
+    assert err <= OUT_TOL, f"output error {err}"
