@@ -29,10 +29,11 @@ def _margins_ok(keys64, cent64):
             assert m.min() >= MARGIN_MIN, "assignment margin too small for an exact comparison"
 
 
-def test_dynamic_build_matches_oracle():
-    cfg, p = _problem(batch=2, n_tokens=3000, C=40)
-    announce("index_build_dyn N=3000 prefix=2000 slack=20")
-    n_prefix, slack = 2000, 20
+# N = 3000: lists built in LDS; N = 40,000: built straight in memory
+@pytest.mark.parametrize("n_tokens,n_prefix,slack", [(3000, 2000, 20), (40_000, 30_000, 100)])
+def test_dynamic_build_matches_oracle(n_tokens, n_prefix, slack):
+    cfg, p = _problem(batch=2, n_tokens=n_tokens, C=40)
+    announce(f"index_build_dyn N={n_tokens} prefix={n_prefix} slack={slack}")
     off, lens, ids = tsa.index_build_dyn(p["keys"], p["centroids"], n_prefix, slack)
     torch.cuda.synchronize()
     k64, c64 = f64(p["keys"]), f64(p["centroids"])
