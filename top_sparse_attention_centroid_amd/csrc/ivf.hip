@@ -124,13 +124,18 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
 
 // ============================================================================
 // Index build, step 1 on matrix cores (bf16): the same nearest-centroid search
-// as a dense contraction keys x centroids^T (16x16x32 bf16 MFMA, fp32
-// accumulate). Each wave keeps a 16-key A tile (4 fragments cover d = 128) in
-// registers and runs it against 16-centroid B tiles read from LDS (rows padded
-// so the 16 lanes of a fragment read distinct banks). Lane l of a 16x16 result holds centroid column l % 16
-// for keys (l / 16) * 4 .. +4; it keeps the best |c|^2 - 2 k.c per key over
-// ascending centroids (strict <), then the 16 lanes of each row group reduce
-// with the lexicographic order (distance, centroid id).
+// as a dense contraction centroids x keys^T (16x16x32 bf16 MFMA, fp32
+// accumulate). Each wave keeps a 16-key tile (4 fragments cover d = 128) in
+// registers as the B operand and runs 16-centroid A tiles read from LDS
+// against it (rows padded so the 16 lanes of a fragment read distinct banks).
+// The accumulator starts at -|c|^2 / 2, so the MFMA chain yields
+// s = k.c - |c|^2 / 2 and the nearest centroid is the largest s
+// (|k - c|^2 = |k|^2 - 2 s); padding rows start at -inf and never win. Lane l
+// of a 16x16 result holds key column l % 16 for centroid rows (l / 16) * 4 ..
+// +4, so each lane follows one key: it keeps the key's best M values of s over
+// its centroids in ascending id order (strict >, so a tie keeps the lower id)
+// with compares and selects only, and the four lanes that share the key merge
+// their lists on d = -2 s with the lexicographic order (distance, centroid id).
 // ============================================================================
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -140,7 +145,7 @@ constexpr int kMfmaKb = 1024;     // keys per workgroup
 constexpr int kMfmaWaves = 8;
 constexpr int kCentPad = 136;     // LDS row stride in elements (128 + 8)
 #ifndef TSA_ASSIGN_TILES
-#define TSA_ASSIGN_TILES 2
+#define TSA_ASSIGN_TILES 4
 #endif
 constexpr int kAssignTiles = TSA_ASSIGN_TILES;  // 16-key tiles scored per pass over the staged centroids
 
@@ -158,13 +163,13 @@ __global__ __launch_bounds__(256) void centroid_norms_kernel(const bf16_t* cent,
 
 // A workgroup owns kMfmaKb keys of one (request, KV head). Centroids are
 // staged kMfmaCs at a time; for each stage every wave runs its 16-key tiles
-// against all staged 16-centroid tiles, reduces each key's best over the 16
-// lanes of its row group, and folds it into the per-key best kept in LDS
-// (strict <, so a tie keeps the earlier stage's lower centroid id).
+// against all staged 16-centroid tiles and folds each key's best into the
+// per-key best kept in LDS (strict <, so a tie keeps the earlier stage's lower
+// centroid id).
 template <int M>
 __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignParams p, const float* norms) {
   __shared__ __align__(16) bf16_t cs[kMfmaCs * kCentPad];
-  __shared__ float cn[kMfmaCs];
+  __shared__ __align__(16) float hn[kMfmaCs];  // -|c|^2 / 2 of the staged centroids, -inf past C
   __shared__ float best_d[kMfmaKb * M];
   __shared__ int best_c[kMfmaKb * M];
   const int bg = blockIdx.y;
@@ -188,13 +193,14 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
       *reinterpret_cast<uint4*>(cs + row * kCentPad + part * 8) =
           *reinterpret_cast<const uint4*>(cb + static_cast<long long>(c) * kHeadDim + part * 8);
     }
-    for (int i = tid; i < kMfmaCs; i += kMfmaWaves * kWave) cn[i] = nb[min(c0 + i, p.C - 1)];
+    for (int i = tid; i < kMfmaCs; i += kMfmaWaves * kWave)
+      hn[i] = c0 + i < p.C ? -0.5f * nb[c0 + i] : -INFINITY;
     __syncthreads();
     const int ntile = (min(kMfmaCs, p.C - c0) + 15) / 16;
     // A pass scores kAssignTiles of the wave's 16-key tiles (kt, kt +
-    // kMfmaWaves, ...) against the staged centroids: each B fragment read
-    // from LDS feeds kAssignTiles MFMA chains (LDS reads, not the matrix
-    // cores, bound this loop), and the tiles' keys are requested together.
+    // kMfmaWaves, ...) against the staged centroids: each centroid fragment
+    // read from LDS feeds kAssignTiles MFMA chains, and the tiles' keys are
+    // requested together.
     constexpr int NT = kAssignTiles;
     constexpr int kTiles = kMfmaKb / 16;
     for (int kt = wave; kt < kTiles; kt += NT * kMfmaWaves) {
@@ -210,65 +216,82 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) a[j][ks] = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
       }
-      TopM<M> best[NT][4];
+      // the lane's key in tile j: its best M values of s, best first
+      float bs[NT][M];
+      int bc[NT][M];
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) best[j][i].init();
+        for (int r = 0; r < M; ++r) {
+          bs[j][r] = -INFINITY;
+          bc[j][r] = 0x7fffffff;
+        }
       for (int t = 0; t < ntile; ++t) {
-        const bf16_t* brow = cs + (t * 16 + col) * kCentPad + grp * 8;
-        bf16x8_t bfr[4];
+        const bf16_t* crow = cs + (t * 16 + col) * kCentPad + grp * 8;
+        bf16x8_t cfr[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) bfr[ks] = *reinterpret_cast<const bf16x8_t*>(brow + ks * 32);
-        const int c = c0 + t * 16 + col;
-        const float cnv = cn[t * 16 + col];
+        for (int ks = 0; ks < 4; ++ks) cfr[ks] = *reinterpret_cast<const bf16x8_t*>(crow + ks * 32);
+        const f32x4_t h = *reinterpret_cast<const f32x4_t*>(hn + t * 16 + grp * 4);
+        const int cr = c0 + t * 16 + grp * 4;  // centroid of accumulator row 0
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t acc = h;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][ks], bfr[ks], acc, 0, 0, 0);
+          for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cfr[ks], a[j][ks], acc, 0, 0, 0);
+          // rows hold ascending centroids: strict > keeps the lower id of a
+          // tie; -inf padding never passes
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (c < p.C) best[j][i].push(cnv - 2.f * acc[i], c);
+          for (int i = 0; i < 4; ++i) {
+            float* v = bs[j];
+            int* id = bc[j];
+            const bool t0 = acc[i] > v[0];
+            if constexpr (M == 2) {
+              const bool t1 = acc[i] > v[1];
+              v[1] = t0 ? v[0] : (t1 ? acc[i] : v[1]);
+              id[1] = t0 ? id[0] : (t1 ? cr + i : id[1]);
+            }
+            v[0] = t0 ? acc[i] : v[0];
+            id[0] = t0 ? cr + i : id[0];
+          }
         }
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         if (!on[j]) continue;  // uniform over the wave
-        // the 16 lanes of a row group hold disjoint centroid columns: merge
-        // their top-M lists by exchanging them over lane distances 8, 4, 2, 1
+        TopM<M> best;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int off = 8; off > 0; off >>= 1) {
-            float od[M];
-            int oc[M];
-#pragma unroll
-            for (int r = 0; r < M; ++r) {
-              od[r] = __shfl_xor(best[j][i].d[r], off);
-              oc[r] = __shfl_xor(best[j][i].c[r], off);
-            }
-#pragma unroll
-            for (int r = 0; r < M; ++r) best[j][i].push(od[r], oc[r]);
-          }
+        for (int r = 0; r < M; ++r) {
+          best.d[r] = -2.f * bs[j][r];  // exact scaling: the order reverses, ties stay ties
+          best.c[r] = bc[j][r];
         }
-        if (col == 0) {
+        // lanes col, col + 16, col + 32, col + 48 hold the key's disjoint
+        // centroid rows: merge their lists over lane distances 16 and 32
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kl = (kt + j * kMfmaWaves) * 16 + grp * 4 + i;
-            TopM<M> tm;
+        for (int off = 16; off < kWave; off <<= 1) {
+          float od[M];
+          int oc[M];
 #pragma unroll
-            for (int r = 0; r < M; ++r) {
-              tm.d[r] = best_d[kl * M + r];
-              tm.c[r] = best_c[kl * M + r];
-            }
+          for (int r = 0; r < M; ++r) {
+            od[r] = __shfl_xor(best.d[r], off);
+            oc[r] = __shfl_xor(best.c[r], off);
+          }
 #pragma unroll
-            for (int r = 0; r < M; ++r) tm.push(best[j][i].d[r], best[j][i].c[r]);
+          for (int r = 0; r < M; ++r) best.push(od[r], oc[r]);
+        }
+        if (grp == 0) {
+          const int kl = (kt + j * kMfmaWaves) * 16 + col;
+          TopM<M> tm;
 #pragma unroll
-            for (int r = 0; r < M; ++r) {
-              best_d[kl * M + r] = tm.d[r];
-              best_c[kl * M + r] = tm.c[r];
-            }
+          for (int r = 0; r < M; ++r) {
+            tm.d[r] = best_d[kl * M + r];
+            tm.c[r] = best_c[kl * M + r];
+          }
+#pragma unroll
+          for (int r = 0; r < M; ++r) tm.push(best.d[r], best.c[r]);
+#pragma unroll
+          for (int r = 0; r < M; ++r) {
+            best_d[kl * M + r] = tm.d[r];
+            best_c[kl * M + r] = tm.c[r];
           }
         }
       }
