@@ -37,6 +37,8 @@ constexpr int kFilterThreads = 256;
 constexpr int kFinalThreads = 1024;
 constexpr int kHistShift = 32 - kTokHistBits;
 constexpr int kFinalLdsCands = 8192;  // candidates the final kernel stages in LDS
+constexpr int kRadixBits = 10;        // digit of the final kernel's radix select
+constexpr int kRadixBins = 1 << kRadixBits;
 
 // The threshold bin of a request: the highest bin t with
 // count(bins >= t) >= k, and the count of keys in bins above t. NT threads,
@@ -193,11 +195,14 @@ __global__ __launch_bounds__(kFinalThreads) void token_final_kernel(TokenSelectP
   __shared__ int coff[kMaxTokFilterChunks + 1];
   __shared__ uint32_t lkey[kFinalLdsCands];
   __shared__ int32_t lid[kFinalLdsCands];
-  __shared__ int hist[NW * 256];
+  __shared__ int hist[kRadixBins];
   __shared__ int scratch[NW];
   __shared__ int misc[2];
   const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int nf = p.nfchunk;
+  // the first chunk counts are requested before the histogram is scanned, so
+  // the two round trips overlap
+  const int cnt0 = tid < nf ? p.cand_cnt[static_cast<long long>(b) * nf + tid] : 0;
   int tbin, above;
   threshold_bin<kFinalThreads>(p.hist + static_cast<long long>(b) * kTokHistBins, p.k, scratch, misc, &tbin,
                                &above);
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(kFinalThreads) void token_final_kernel(TokenSelectP
   int run = 0;
   for (int c0 = 0; c0 < nf; c0 += kFinalThreads) {
     const int c = c0 + tid;
-    const int v = c < nf ? p.cand_cnt[static_cast<long long>(b) * nf + c] : 0;
+    const int v = c0 == 0 ? cnt0 : (c < nf ? p.cand_cnt[static_cast<long long>(b) * nf + c] : 0);
     int total;
     const int excl = block_exclusive_scan<NW>(v, scratch, &total);
     if (c < nf) coff[c] = run + excl;
@@ -232,84 +237,72 @@ __global__ __launch_bounds__(kFinalThreads) void token_final_kernel(TokenSelectP
   auto key_at = [&](int m) { return staged ? lkey[m] : ck[cand_index(coff, nf, m)]; };
   auto id_at = [&](int m) { return staged ? lid[m] : cid[cand_index(coff, nf, m)]; };
 
-  // radix select of the (k - above)-th largest key inside the threshold bin
+  // radix select of the (k - above)-th largest key inside the threshold bin:
+  // two passes over 10-bit digits of the low 20 bits, one shared histogram
+  // bin per thread (the bin's keys spread over many digits, so its atomics
+  // rarely collide), the digit found by a block scan from the top
+  static_assert(kHistShift == 2 * kRadixBits && kRadixBins == kFinalThreads, "two digits, one bin per thread");
   uint32_t prefix = static_cast<uint32_t>(tbin) << kHistShift;
   uint32_t pmask = ~0u << kHistShift;
   int krem = p.k - above;
-  for (int shift = kHistShift - 8; shift > -8; shift -= 8) {
-    const int sh = shift < 0 ? 0 : shift;
-    const uint32_t dmask = (shift < 0 ? (1u << (shift + 8)) : 256u) - 1u;
-    for (int i = tid; i < NW * 256; i += kFinalThreads) hist[i] = 0;
-    __syncthreads();
-    int* wh = hist + wave * 256;
-    for (int m = tid; m < M; m += kFinalThreads) {
-      const uint32_t key = key_at(m);
-      if ((key & pmask) == prefix) atomicAdd(&wh[(key >> sh) & dmask], 1);
+  for (int sh = kRadixBits; sh >= 0; sh -= kRadixBits) {
+    hist[tid] = 0;
+    if (tid == 0) {
+      misc[0] = 0;  // unreachable: the keys under the prefix number at least krem
+      misc[1] = krem;
     }
     __syncthreads();
-    if (wave == 0) {
-      int cq[4], t = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        cq[q] = 0;
-        for (int w = 0; w < NW; ++w) cq[q] += hist[w * 256 + lane * 4 + q];
-        t += cq[q];
-      }
-      int x = t;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_down(x, o);
-        if (lane + o < kWave) x += y;
-      }
-      int a = x - t;  // keys in the digits of higher lanes
-      int best = -1, best_a = 0;
-#pragma unroll
-      for (int q = 3; q >= 0; --q) {
-        if (best < 0 && a + cq[q] >= krem) {
-          best = lane * 4 + q;
-          best_a = a;
-        }
-        a += cq[q];
-      }
-      int d = best, da = best_a;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const int od = __shfl_xor(d, o), oa = __shfl_xor(da, o);
-        if (od > d) {
-          d = od;
-          da = oa;
-        }
-      }
-      if (lane == 0) {
-        misc[0] = d;
-        misc[1] = krem - da;
-      }
+    for (int m = tid; m < M; m += kFinalThreads) {
+      const uint32_t key = key_at(m);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (kRadixBins - 1)], 1);
+    }
+    __syncthreads();
+    const int v = hist[tid];
+    int total;
+    const int excl = block_exclusive_scan<NW>(v, scratch, &total);
+    const int a = total - excl - v;  // keys under the prefix with a higher digit
+    if (a < krem && a + v >= krem) {
+      misc[0] = tid;
+      misc[1] = krem - a;
     }
     __syncthreads();
     prefix |= static_cast<uint32_t>(misc[0]) << sh;
-    pmask |= dmask << sh;
+    pmask |= static_cast<uint32_t>(kRadixBins - 1) << sh;
     krem = misc[1];
     __syncthreads();
   }
   const uint32_t Tk = prefix;
   const int need_eq = krem;
 
-  // ordered emission: keys above Tk, then the first need_eq keys equal to Tk
+  // ordered emission: keys above Tk, then the first need_eq keys equal to Tk.
+  // Each thread takes kEmitPer consecutive candidates, so one block scan
+  // places kEmitPer * kFinalThreads of them (counts below 2^16 per round).
+  constexpr int kEmitPer = 4;
   int32_t* sel = p.sel + static_cast<long long>(b) * p.k;
   int run_gt = 0, run_eq = 0;
-  for (int m0 = 0; m0 < M; m0 += kFinalThreads) {
-    const int m = m0 + tid;
-    bool gt = false, eq = false;
-    if (m < M) {
-      const uint32_t key = key_at(m);
-      gt = key > Tk;
-      eq = key == Tk;
+  for (int m0 = 0; m0 < M; m0 += kEmitPer * kFinalThreads) {
+    const int mb = m0 + tid * kEmitPer;
+    bool gt[kEmitPer], eq[kEmitPer];
+    int v = 0;
+#pragma unroll
+    for (int u = 0; u < kEmitPer; ++u) {
+      gt[u] = eq[u] = false;
+      if (mb + u < M) {
+        const uint32_t key = key_at(mb + u);
+        gt[u] = key > Tk;
+        eq[u] = key == Tk;
+      }
+      v += (gt[u] ? 1 : 0) | (eq[u] ? 1 << 16 : 0);
     }
-    const int v = (gt ? 1 : 0) | (eq ? 1 << 16 : 0);
     int total;
     const int excl = block_exclusive_scan<NW>(v, scratch, &total);
-    const int gt_before = run_gt + (excl & 0xffff), eq_before = run_eq + (excl >> 16);
-    if (gt || (eq && eq_before < need_eq)) sel[gt_before + min(eq_before, need_eq)] = id_at(m);
+    int gt_before = run_gt + (excl & 0xffff), eq_before = run_eq + (excl >> 16);
+#pragma unroll
+    for (int u = 0; u < kEmitPer; ++u) {
+      if (gt[u] || (eq[u] && eq_before < need_eq)) sel[gt_before + min(eq_before, need_eq)] = id_at(mb + u);
+      gt_before += gt[u] ? 1 : 0;
+      eq_before += eq[u] ? 1 : 0;
+    }
     run_gt += total & 0xffff;
     run_eq += total >> 16;
   }
