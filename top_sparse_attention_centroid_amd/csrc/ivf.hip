@@ -318,12 +318,13 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
 // ============================================================================
 constexpr int kCsrStage = 32768;  // token ids staged in LDS (128 KiB)
 constexpr int kCsrMaxC = 1024;    // lists with per-wave counters in LDS
+constexpr int kCsrSmallC = 256;   // lists whose 16 waves' counters fit beside the LDS stage
 constexpr int kCsrBatch = 16;     // 64-token chunks whose list ids a wave requests together
 
-template <int NW, bool STAGED>
+template <int NW, bool STAGED, int MAXC = kCsrMaxC>
 __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
   __shared__ int stage[STAGED ? kCsrStage : 1];
-  __shared__ int hist[NW][kCsrMaxC];  // counts, then cursors
+  __shared__ int hist[NW][MAXC];  // counts, then cursors (C <= MAXC)
   __shared__ int scan_scratch[NW];
   const int bg = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
 #pragma unroll
     for (int u = 0; u < kCsrBatch; ++u) cc[u] = i0 + u * kWave + lane < hi ? min(max(raw[u], 0), C - 1) : -1;
   };
-  for (int i = tid; i < NW * kCsrMaxC; i += NW * kWave) hist[i / kCsrMaxC][i % kCsrMaxC] = 0;
+  for (int i = tid; i < NW * MAXC; i += NW * kWave) hist[i / MAXC][i % MAXC] = 0;
   if constexpr (STAGED)
     for (int i = tid; i < cap; i += NW * kWave) stage[i] = -1;  // free entries and the tail stay -1
   __syncthreads();
@@ -1000,14 +1001,17 @@ hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Up to kCsrMaxC lists: 4 waves staging the ids in LDS when a (request, KV
-// head)'s ids fit there and no second array is written (128 KiB + counters
-// leaves one workgroup per CU), else 16 waves writing to memory; larger
-// codebooks take csr_kernel.
+// Up to kCsrMaxC lists: the ids staged in LDS when a (request, KV head)'s ids
+// fit there and no second array is written (128 KiB leaves one workgroup per
+// CU: 16 waves when the counters of up to kCsrSmallC lists fit beside the
+// stage, else 4), else 16 waves writing to memory; larger codebooks take
+// csr_kernel.
 hipError_t launch_csr(const CsrParams& p, hipStream_t s) {
   const dim3 grid(p.B * p.Hkv);
   const long long cap = static_cast<long long>(p.N) * p.m;
-  if (p.C <= kCsrMaxC && !p.alt && cap <= kCsrStage)
+  if (p.C <= kCsrSmallC && !p.alt && cap <= kCsrStage)
+    hipLaunchKernelGGL((csr_waves_kernel<16, true, kCsrSmallC>), grid, dim3(16 * kWave), 0, s, p);
+  else if (p.C <= kCsrMaxC && !p.alt && cap <= kCsrStage)
     hipLaunchKernelGGL((csr_waves_kernel<4, true>), grid, dim3(4 * kWave), 0, s, p);
   else if (p.C <= kCsrMaxC)
     hipLaunchKernelGGL((csr_waves_kernel<16, false>), grid, dim3(16 * kWave), 0, s, p);
