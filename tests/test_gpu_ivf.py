@@ -94,6 +94,19 @@ def test_ragged_shapes(dtype, G):
     _decode_and_check(cfg, p, ref, range(cfg.batch), steps=2)
 
 
+# bf16 nearest-centroid search on matrix cores: fewer keys than one 16-key
+# tile, and codebooks whose last 256-centroid stage holds 1 or 16 centroids
+@pytest.mark.parametrize("n_tokens,C", [(1, 3), (5, 257), (17, 16), (600, 272)])
+def test_index_build_tile_and_stage_edges(n_tokens, C):
+    cfg = W.config(1, batch=2, n_tokens=n_tokens, n_kv_heads=2, n_q_heads=8, n_centroids=C, top_k=1,
+                   steps=1, seed=5 + C)
+    announce(f"ivf index build edges N={n_tokens} C={C}")
+    p = _problem(cfg)
+    offsets, ids = tsa.index_build(p["keys"], p["centroids"])
+    torch.cuda.synchronize()
+    _check_index(p, range(cfg.batch), offsets, ids)
+
+
 def test_selecting_every_list_is_dense_attention():
     cfg = W.config(1, batch=2, n_tokens=777, n_kv_heads=2, n_q_heads=8, n_centroids=5, top_k=5,
                    steps=1, shared_codebook=True, seed=21)
