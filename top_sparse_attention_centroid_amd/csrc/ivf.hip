@@ -336,8 +336,9 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
   int32_t* ids = p.ids + static_cast<long long>(bg) * cap;
   int32_t* alt = p.alt ? p.alt + static_cast<long long>(bg) * cap : nullptr;
   int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * C : nullptr;
-  const int lo = static_cast<int>(static_cast<long long>(wave) * n / NW);
-  const int hi = static_cast<int>(static_cast<long long>(wave + 1) * n / NW);  // this wave's entries
+  // this wave's entries, whole tokens (a multiple of m) each
+  const int lo = static_cast<int>(static_cast<long long>(wave) * n / NW / m * m);
+  const int hi = static_cast<int>(static_cast<long long>(wave + 1) * n / NW / m * m);
   auto put_id = [&](long long pos, int v) {
     if constexpr (STAGED) stage[pos] = v;
     else ids[pos] = v;
@@ -407,11 +408,15 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
         const uint64_t bal = __ballot(set);
         same &= set ? bal : ~bal;
       }
+      // m == 2: a token's two entries sit in lanes 2t and 2t + 1 of one
+      // batch (ranges and batches start on even entries), so its other list
+      // is the neighbouring lane's
+      const int other = alt ? __shfl_xor(cc[u], 1) : 0;
       if (valid) {
         const int rank = prefix_count(same);
         const int pos = cur[c] + rank;
         put_id(pos, i / m);                  // entries of one token are adjacent: ascending ids per list
-        if (alt) alt[pos] = a[min(i ^ 1, n - 1)];  // m == 2: the token's other list
+        if (alt) alt[pos] = other;
         if (rank == __popcll(same) - 1) cur[c] = pos + 1;
       }
     }
