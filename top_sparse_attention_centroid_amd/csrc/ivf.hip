@@ -417,7 +417,7 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
         const int pos = cur[c] + rank;
         put_id(pos, i / m);                  // entries of one token are adjacent: ascending ids per list
         if (alt) alt[pos] = other;
-        if (rank == __popcll(same) - 1) cur[c] = pos + 1;
+        if (rank == static_cast<int>(__popcll(same)) - 1) cur[c] = pos + 1;
       }
     }
   }
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
         const int pos = cursor[c] + rank;
         ids[pos] = i / m;                       // entries of one token are adjacent: ascending ids per list
         if (alt) alt[pos] = a[i ^ 1];           // m == 2: the token's other list
-        if (rank == __popcll(same) - 1) cursor[c] = pos + 1;
+        if (rank == static_cast<int>(__popcll(same)) - 1) cursor[c] = pos + 1;
       }
     }
   }
@@ -703,7 +703,7 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
       uint32_t t1 = 0;
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = t1 | (1u << bit);
-        if (__popcll(__ballot(lmax >= cand)) >= k) t1 = cand;
+        if (static_cast<int>(__popcll(__ballot(lmax >= cand))) >= k) t1 = cand;
       }
       int n_cand = 0;
 #pragma unroll
@@ -729,7 +729,7 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
         xc = lane < n_cand ? cli[lane] : 0;
         for (int bit = 31; bit >= 0; --bit) {
           const uint32_t cand = thr | (1u << bit);
-          if (__popcll(__ballot(x >= cand)) >= k) thr = cand;
+          if (static_cast<int>(__popcll(__ballot(x >= cand))) >= k) thr = cand;
         }
         found = true;
         __builtin_amdgcn_wave_barrier();  // the next head of this wave reuses cl

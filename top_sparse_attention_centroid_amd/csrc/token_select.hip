@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kFinalThreads) void token_final_kernel(TokenSelectP
   __shared__ int hist[kRadixBins];
   __shared__ int scratch[NW];
   __shared__ int misc[2];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int nf = p.nfchunk;
   // the first chunk counts are requested before the histogram is scanned, so
   // the two round trips overlap
