@@ -46,6 +46,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
+    "squared_distances_near",
     "nearest_centroid",
     "posting_lists",
     "index_build",
@@ -68,40 +69,75 @@ def _f64(x) -> np.ndarray:
 # Index build
 # ----------------------------------------------------------------------------
 
+def squared_distances_near(keys, centroids, m: int, chunk: int = 4096):
+    """Squared Euclidean distances sum_t (k_t - c_t)^2, evaluated term by term
+    in fp64, for every centroid that can be one of the m + 1 nearest of each
+    key; +inf for the others.
+
+    [KARAT] How, index structure (an entry goes to a list by its key); the
+    tiny workload names the rule: nearest centroid.
+
+    Which centroids need the direct sum is decided from the cheap expansion
+    e_c = |k|^2 - 2 k.c + |c|^2 (one fp64 matrix product), with a rounding
+    bound instead of trust: both e_c and the direct sum are within
+    b_c = gamma (|k| + |c|)^2 of the exact distance, gamma = (d+3) u /
+    (1 - (d+3) u) and u = 2^-53 (the textbook bound for a length-d fp64 dot
+    product; every term is at most (|k| + |c|)^2 in total). Let U be the
+    (m+1)-th smallest e_c + 2 b_c over the centroids: at least m + 1 direct
+    sums are <= U, so a centroid with e_c - 2 b_c > U has a direct sum larger
+    than the (m+1)-th smallest and cannot be among the m + 1 nearest. Every
+    other centroid gets its direct sum. Near-ties, and large keys whose
+    expansion cancels, therefore fall back to the direct sum for as many
+    centroids as the bound requires (all of them, if need be).
+
+    keys [n][d], centroids [C][d]. Returns d2 [n][C] fp64.
+    """
+    K = _f64(keys)
+    Cn = _f64(centroids)
+    n, d = K.shape
+    C = Cn.shape[0]
+    u = 2.0 ** -53
+    gamma = (d + 3) * u / (1.0 - (d + 3) * u)
+    out = np.full((n, C), np.inf)
+    c2 = np.sum(Cn * Cn, axis=1)
+    cn = np.sqrt(c2)
+    M = min(m + 1, C)
+    for s in range(0, n, chunk):
+        Kc = K[s:s + chunk]
+        k2 = np.sum(Kc * Kc, axis=1)
+        e = k2[:, None] - 2.0 * (Kc @ Cn.T) + c2[None, :]
+        b = gamma * (np.sqrt(k2)[:, None] + cn[None, :]) ** 2
+        U = np.partition(e + 2.0 * b, M - 1, axis=1)[:, M - 1]
+        rows, cols = np.nonzero(e - 2.0 * b <= U[:, None])
+        step = max(1, (1 << 22) // max(d, 1))          # bound the temporary to ~32 MB
+        for t in range(0, rows.shape[0], step):
+            r, c = rows[t:t + step], cols[t:t + step]
+            diff = Kc[r] - Cn[c]
+            out[s + r, c] = np.sum(diff * diff, axis=1)
+    return out
+
+
 def nearest_centroid(keys, centroids, chunk: int = 4096):
     """Nearest centroid of every key by squared Euclidean distance.
 
     [KARAT] How, index structure (entries go to lists by their key); reading:
     single assignment to the nearest centroid, ties -> lower centroid index.
-
-    The squared distance |k - c|^2 is evaluated as |k|^2 - 2 k.c + |c|^2 with
-    the k.c block as one fp64 matrix product (the same quantity; fp64 keeps
-    the expansion's rounding near 1e-14 of |k|^2, far inside any margin the
-    workloads use).
+    The deciding distances are the direct sums of (k_t - c_t)^2
+    (``squared_distances_near``).
 
     keys [n][d], centroids [C][d]. Returns (assign [n] int64, margin [n]) where
     margin = (d2_second - d2_best) / d2_best, the relative distance gap that
     decides the assignment (inf when the key sits on its centroid).
     """
-    K = _f64(keys)
-    Cn = _f64(centroids)
-    n = K.shape[0]
-    assign = np.empty(n, dtype=np.int64)
-    margin = np.empty(n, dtype=np.float64)
-    c2 = np.sum(Cn * Cn, axis=1)
-    for s in range(0, n, chunk):
-        Kc = K[s:s + chunk]
-        d2 = np.sum(Kc * Kc, axis=1)[:, None] - 2.0 * (Kc @ Cn.T) + c2[None, :]   # [m][C]
-        d2 = np.maximum(d2, 0.0)
-        best = np.argmin(d2, axis=1)                              # first minimum
-        assign[s:s + chunk] = best
-        if Cn.shape[0] > 1:
-            part = np.partition(d2, 1, axis=1)
-            d_best, d_second = part[:, 0], part[:, 1]
-            with np.errstate(divide="ignore", invalid="ignore"):
-                margin[s:s + chunk] = np.where(d_best > 0, (d_second - d_best) / d_best, np.inf)
-        else:
-            margin[s:s + chunk] = np.inf
+    d2 = squared_distances_near(keys, centroids, 1, chunk)
+    n, C = d2.shape
+    assign = np.argmin(d2, axis=1)                                  # first minimum: lower index
+    if C == 1:
+        return assign, np.full(n, np.inf)
+    part = np.partition(d2, 1, axis=1)
+    d_best, d_second = part[:, 0], part[:, 1]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        margin = np.where(d_best > 0, (d_second - d_best) / d_best, np.inf)
     return assign, margin
 
 

@@ -33,7 +33,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .ivf import attend, retrieved_rows, selection_gap, top_k
+from .ivf import attend, retrieved_rows, selection_gap, squared_distances_near, top_k
 
 __all__ = ["cosine_scores", "fixed_rows", "decode_head_ex", "sparse_decode_ex", "nearest_centroids",
            "posting_lists_multi", "index_build_multi"]
@@ -112,8 +112,7 @@ def nearest_centroids(keys, centroids, m: int):
     is the relative margin that decides the m-th choice (inf if m == C)."""
     K = _f64(keys)
     Cn = _f64(centroids)
-    d2 = np.sum(K * K, axis=1)[:, None] - 2.0 * (K @ Cn.T) + np.sum(Cn * Cn, axis=1)[None, :]
-    d2 = np.maximum(d2, 0.0)
+    d2 = squared_distances_near(K, Cn, m)    # direct sums for every centroid that can rank <= m + 1
     C = Cn.shape[0]
     order = np.lexsort((np.broadcast_to(np.arange(C), d2.shape), d2), axis=1)  # distance, then index
     assign = order[:, :m]

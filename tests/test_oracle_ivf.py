@@ -5,6 +5,7 @@ routine for the dense special case, the KARAT worked example's counts)."""
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -30,7 +31,7 @@ def test_keys_on_centroids_land_in_their_own_list():
     perm = rng.integers(0, C, size=200)
     a, margin = ivf.nearest_centroid(cent[perm], cent)
     assert np.array_equal(a, perm)
-    assert np.all(margin > 1e10)  # the key sits on its centroid: relative gap unbounded
+    assert np.all(np.isinf(margin))  # the key sits on its centroid: distance exactly 0
 
 
 def test_perturbed_keys_keep_their_centroid():
@@ -56,6 +57,56 @@ def test_equidistant_key_goes_to_lower_centroid():
         cent[i] = [0, 100.0 + i, 0]
     a, margin = ivf.nearest_centroid(np.zeros((1, 3)), cent)
     assert a[0] == 2 and margin[0] == 0.0
+
+
+def _exact_d2(x, c):
+    """Squared distance of two fp64 vectors in exact rational arithmetic."""
+    return sum((Fraction(float(a)) - Fraction(float(b))) ** 2 for a, b in zip(x, c))
+
+
+@pytest.mark.parametrize("offset", [0.0, 1.0e6])
+def test_near_ties_match_exact_rational_distances(offset):
+    # Keys on the far side of the bisector of two centroids at relative
+    # margins 1e-4 ... 1e-8, checked against brute-force distances in exact
+    # rational arithmetic. With a common offset of 1e6 every |k|^2 and |c|^2
+    # is ~1e14, so an expansion |k|^2 - 2k.c + |c|^2 alone would lose the
+    # decision (its rounding is ~1e-2 against gaps of ~1e-7).
+    rng = np.random.default_rng(21)
+    C, d = 10, 48
+    cent = offset + 10.0 * rng.standard_normal((C, d))
+    keys, want_margin = [], []
+    for r in (1e-4, 1e-5, 1e-6, 1e-7, 1e-8):
+        for side in (1.0, -1.0):
+            a, b = rng.choice(C, 2, replace=False)
+            D = np.linalg.norm(cent[a] - cent[b])
+            u = (cent[a] - cent[b]) / D
+            w = rng.standard_normal(d)
+            w -= (w @ u) * u
+            w *= 3.0 / np.linalg.norm(w)
+            t = r * (D * D / 4 + 9.0) / (2 * D)
+            keys.append((cent[a] + cent[b]) / 2 + side * t * u + w)
+            want_margin.append(r)
+    keys = np.array(keys)
+    a, margin = ivf.nearest_centroid(keys, cent)
+    for i, x in enumerate(keys):
+        d2 = [_exact_d2(x, c) for c in cent]
+        best = min(range(C), key=lambda j: (d2[j], j))
+        second = min((d2[j] for j in range(C) if j != best))
+        exact_margin = float((second - d2[best]) / d2[best])
+        assert a[i] == best
+        assert 0.3 * want_margin[i] < exact_margin < 3 * want_margin[i]
+        assert abs(margin[i] - exact_margin) <= 1e-4 * exact_margin
+
+
+def test_nearest_candidates_cover_every_centroid_when_all_tie():
+    # A key equidistant from every centroid: the direct sums all tie and the
+    # lowest index wins, with a zero margin.
+    C, d = 7, 5
+    cent = np.zeros((C, d))
+    for c in range(C):
+        cent[c, c % d] = 2.0 if c < d else -2.0
+    a, margin = ivf.nearest_centroid(np.zeros((3, d)), cent)
+    assert np.array_equal(a, [0, 0, 0]) and np.all(margin == 0.0)
 
 
 def test_squared_distance_not_dot_product():
@@ -341,3 +392,42 @@ def test_sparse_decode_batch_layout_and_gqa():
     part = ivf.sparse_decode(q, cent, off, ids, K, V, k, heads=[(1, 3)])
     assert np.array_equal(part["out"][1, 3], res["out"][1, 3])
     assert np.isnan(part["out"][0, 0]).all()
+
+
+def test_gqa_groups_are_contiguous_query_heads():
+    # Query head h must read KV head h div (Hq/Hkv): contiguous groups. Each
+    # of the three reads is pinned by a construction whose output names the
+    # KV head it came from (Hq = 8, Hkv = 2; the interleaved reading h mod Hkv
+    # gives 0,1,0,1,... and fails).
+    B, N, Hkv, G, d = 1, 16, 2, 4, 8
+    Hq = Hkv * G
+    want = np.arange(Hq) // G
+    e0 = np.zeros(d)
+    e0[0] = 1.0
+    q = np.broadcast_to(e0, (B, Hq, d)).copy()
+    # (1) centroids: KV head g's codebook puts list g far ahead of the others.
+    cent = np.full((1, Hkv, Hkv, d), 0.0)
+    for g in range(Hkv):
+        cent[0, g, :, 0] = -10.0
+        cent[0, g, g, 0] = 10.0
+    K = np.zeros((B, N, Hkv, d))
+    V = np.zeros((B, N, Hkv, d))
+    off, ids, _ = ivf.index_build(K, cent)
+    res = ivf.sparse_decode(q, cent, off, ids, K, V, 1)
+    assert np.array_equal(res["sel"][0, :, 0], want)
+    # (2) keys: every list chosen (dense); KV head g's only large logit is
+    # token g, and V row i holds the value i in every KV head.
+    K = np.zeros((B, N, Hkv, d))
+    for g in range(Hkv):
+        K[0, g, g, 0] = 1000.0 * math.sqrt(d)
+    V = np.broadcast_to(np.arange(N, dtype=float)[None, :, None, None], (B, N, Hkv, d)).copy()
+    off, ids, _ = ivf.index_build(K, cent)
+    res = ivf.sparse_decode(q, cent, off, ids, K, V, Hkv)
+    assert np.array_equal(res["out"][0], np.broadcast_to(want[:, None].astype(float), (Hq, d)))
+    # (3) values: uniform weights (all keys zero) over N = 16 rows, KV head g's
+    # values all equal g; the mean is exact in binary.
+    K = np.zeros((B, N, Hkv, d))
+    V = np.broadcast_to(np.arange(Hkv, dtype=float)[None, None, :, None], (B, N, Hkv, d)).copy()
+    off, ids, _ = ivf.index_build(K, cent)
+    res = ivf.sparse_decode(q, cent, off, ids, K, V, Hkv)
+    assert np.array_equal(res["out"][0], np.broadcast_to(want[:, None].astype(float), (Hq, d)))

@@ -97,6 +97,49 @@ def _check_state(st: cache.CacheState, sel, t):
     assert np.all(lu <= t) and np.all((lu >= 0) == (tok >= 0))
 
 
+def test_token_decode_gqa_groups_are_contiguous_query_heads():
+    # Query head h reads KV head h div (Hq/Hkv). Keys: KV head g's only large
+    # logit is token g, and V row i holds i, so head h's output names the KV
+    # head its keys came from. Values: zero keys give uniform weights over
+    # N = 16 rows and KV head g's values all equal g. The interleaved reading
+    # h mod Hkv gives 0,1,0,1,... and fails both.
+    B, N, Hkv, G, d, di = 1, 16, 2, 4, 8, 4
+    Hq = Hkv * G
+    want = (np.arange(Hq) // G).astype(float)
+    q_idx = np.ones((B, di))
+    k_idx = np.zeros((B, N, di))
+    q = np.zeros((B, Hq, d))
+    q[..., 0] = 1.0
+    K = np.zeros((B, N, Hkv, d))
+    for g in range(Hkv):
+        K[0, g, g, 0] = 1000.0 * np.sqrt(d)
+    V = np.broadcast_to(np.arange(N, dtype=float)[None, :, None, None], (B, N, Hkv, d)).copy()
+    res = token.token_decode(q_idx, k_idx, q, K, V, N)
+    assert np.array_equal(res["out"][0], np.broadcast_to(want[:, None], (Hq, d)))
+    K = np.zeros((B, N, Hkv, d))
+    V = np.broadcast_to(np.arange(Hkv, dtype=float)[None, None, :, None], (B, N, Hkv, d)).copy()
+    res = token.token_decode(q_idx, k_idx, q, K, V, N)
+    assert np.array_equal(res["out"][0], np.broadcast_to(want[:, None], (Hq, d)))
+
+
+def test_attend_slots_gqa_groups_are_contiguous_query_heads():
+    # The same two constructions through the hot pool (slot s holds token s).
+    S, Hkv, G, d = 16, 2, 4, 8
+    Hq = Hkv * G
+    want = np.broadcast_to((np.arange(Hq) // G).astype(float)[:, None], (Hq, d))
+    q = np.zeros((Hq, d))
+    q[:, 0] = 1.0
+    slots = np.arange(S)
+    pk = np.zeros((S, Hkv, d))
+    for g in range(Hkv):
+        pk[g, g, 0] = 1000.0 * np.sqrt(d)
+    pv = np.broadcast_to(np.arange(S, dtype=float)[:, None, None], (S, Hkv, d)).copy()
+    assert np.array_equal(cache.attend_slots(q, pk, pv, slots), want)
+    pk = np.zeros((S, Hkv, d))
+    pv = np.broadcast_to(np.arange(Hkv, dtype=float)[None, :, None], (S, Hkv, d)).copy()
+    assert np.array_equal(cache.attend_slots(q, pk, pv, slots), want)
+
+
 def test_first_step_misses_everything_and_fills_free_slots_in_order():
     st = cache.CacheState(100, 8)
     slots, hits, misses, fetches = cache.lru_step(st, [40, 3, 77, 12], 0)

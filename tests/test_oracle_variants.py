@@ -151,3 +151,27 @@ def test_multi_assignment_lists_and_dedup_in_the_union():
         keep[ids[off[c]:off[c + 1]]] = True
     assert np.array_equal(rows, np.flatnonzero(keep))
     assert np.allclose(o, _masked_dense(q, K, V, keep), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("sim", ["dot", "cosine"])
+def test_variant_decode_gqa_groups_are_contiguous_query_heads(sim):
+    # Query head h reads KV head h div (Hq/Hkv): KV head g's codebook puts
+    # list g first (its selection names g), and with zero keys over N = 16
+    # rows whose values equal the KV head's index, the output does too. The
+    # interleaved reading h mod Hkv gives 0,1,0,1,... and fails.
+    B, N, Hkv, G, d = 1, 16, 2, 4, 8
+    Hq = Hkv * G
+    want = np.arange(Hq) // G
+    q = np.zeros((B, Hq, d))
+    q[..., 0] = 1.0
+    cent = np.zeros((1, Hkv, Hkv, d))
+    for g in range(Hkv):
+        cent[0, g, :, 0] = -10.0
+        cent[0, g, g, 0] = 10.0
+    K = np.zeros((B, N, Hkv, d))
+    V = np.broadcast_to(np.arange(Hkv, dtype=float)[None, None, :, None], (B, N, Hkv, d)).copy()
+    off, ids, _ = ivf.index_build(K, cent)
+    res = variants.sparse_decode_ex(q, cent, off, ids, K, V, 1, similarity=sim)
+    assert np.array_equal(res["sel"][0, :, 0], want)
+    res = variants.sparse_decode_ex(q, cent, off, ids, K, V, Hkv, similarity=sim)
+    assert np.array_equal(res["out"][0], np.broadcast_to(want[:, None].astype(float), (Hq, d)))
