@@ -121,31 +121,6 @@ def test_no_variant_is_bitwise_the_plain_decode():
 # padding; C = 300: two codebook stages, the second ending inside a tile.
 # N = 3001 and 2500 leave a last workgroup with a partial 16-key tile and
 # idle key tiles in its last pass.
-@pytest.mark.parametrize("n_tokens,C", [(3001, 2), (3001, 7), (2500, 300)])
-def test_two_way_index_build_ragged_shapes(n_tokens, C):
-    cfg, p = _problem(n_tokens=n_tokens, n_centroids=C, top_k=2, batch=2, n_kv_heads=2, n_q_heads=8)
-    announce(f"variants: two lists per key, index build N={n_tokens} C={C}")
-    p["keys"] = _two_way_keys(cfg, p["centroids"], 23 + C, min_gap=1e-3 if C > 2 else None)
-    off, ids, alt = tsa.index_build_multi(p["keys"], p["centroids"], 2)
-    s_off, s_ids = tsa.index_build(p["keys"], p["centroids"])
-    torch.cuda.synchronize()
-    k64, c64 = f64(p["keys"]), f64(p["centroids"])
-    r_off, r_ids, r_alt, margin = variants.index_build_multi(k64, c64, 2)
-    assert margin >= 1e-3, f"assignment margin {margin} too small for an exact comparison"
-    assert np.array_equal(off.cpu().numpy(), r_off)
-    assert np.array_equal(ids.cpu().numpy(), r_ids)
-    assert np.array_equal(alt.cpu().numpy(), r_alt[..., 0])
-    # the nearest list of each key, from the one-list build, is its first choice
-    r1_off, r1_ids, _, margin1 = variants.index_build_multi(k64, c64, 1)
-    assert margin1 >= 1e-3, f"first-choice margin {margin1} too small for an exact comparison"
-    assert np.array_equal(s_off.cpu().numpy(), r1_off)
-    assert np.array_equal(s_ids.cpu().numpy(), r1_ids)
-    if C == 2:
-        # both lists hold every token
-        assert np.all(r_off[..., -1] == 2 * n_tokens)
-
-
-# 3 x 2 KV heads: a wave per plan segment; 16 x 8: merged gather sets
 @pytest.mark.parametrize("batch,n_kv_heads", [(3, 2), (16, 8)])
 def test_variants_over_a_growing_index(batch, n_kv_heads):
     """Cosine + sink/window over a dynamic index (list lengths) equals the

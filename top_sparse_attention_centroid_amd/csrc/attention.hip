@@ -29,30 +29,9 @@ namespace tsa {
 template <bool EXPLICIT>
 constexpr int gather_waves() { return EXPLICIT ? kGatherWavesExplicit : kGatherWavesRows; }
 constexpr int kSegsPerWave = kGatherSegsPerWave;    // segments a wave is planned to take
-#ifndef TSA_GATHER_UNROLL
-#define TSA_GATHER_UNROLL 8
-#endif
-#ifndef TSA_GATHER_NT
-#define TSA_GATHER_NT 1  // K/V rows are read once per call: non-temporal loads
-#endif
-#ifndef TSA_GATHER_PIPE
-#define TSA_GATHER_PIPE 0  // 1: double-buffer batches in registers
-#endif
-#ifndef TSA_GATHER_TAIL
-#define TSA_GATHER_TAIL 0  // 1: a half-size batch for the last rows of a segment
-#endif
-#ifndef TSA_GATHER_FULLMASK_ALL
-#define TSA_GATHER_FULLMASK_ALL 1  // explicit segments read by every head (or, with multi_all, two or more): one all-heads pass
-#endif
-#ifndef TSA_GATHER_WAVES_PER_EU
-#define TSA_GATHER_WAVES_PER_EU 0
-#endif
-#if TSA_GATHER_WAVES_PER_EU
-#define TSA_GATHER_OCC __attribute__((amdgpu_waves_per_eu(TSA_GATHER_WAVES_PER_EU, TSA_GATHER_WAVES_PER_EU)))
-#else
-#define TSA_GATHER_OCC
-#endif
-constexpr int kGatherUnroll = TSA_GATHER_UNROLL;  // rows per 16-lane group per batch
+constexpr int kGatherUnroll = 8;  // rows per 16-lane group per batch
+// K/V rows that one head reads are read once per call: non-temporal loads
+constexpr bool kGatherStream = true;
 constexpr int kBatchRows = 4 * kGatherUnroll;      // rows per wave per batch
 constexpr int kUnrollAll = 4;                      // all-heads pass: rows per lane group per batch
 constexpr int kBatchRowsAll = 4 * kUnrollAll;
@@ -188,35 +167,11 @@ __device__ __forceinline__ HeadState head_pass(int h, const int* ids, int cnt, i
     qf.load(qs + h * kHeadDim + e * 8);
     HeadState st;
     st.init();
-#if TSA_GATHER_PIPE
-    Batch<T> A, Bb;
-    issue_batch<STREAM, DUP>(A, ids, 0, cnt, r, kb, vb, row_stride, dup, h);
-    for (int base = 0; base < cnt; base += 2 * kBatchRows) {
-      issue_batch<STREAM, DUP>(Bb, ids, base + kBatchRows, cnt, r, kb, vb, row_stride, dup, h);
-      consume_batch(A, st, qf, qscale);
-      issue_batch<STREAM, DUP>(A, ids, base + 2 * kBatchRows, cnt, r, kb, vb, row_stride, dup, h);
-      consume_batch(Bb, st, qf, qscale);
-    }
-#elif TSA_GATHER_TAIL
-    // full batches while more than half a batch remains, then one half batch
-    int base = 0;
-    for (; base + kBatchRows / 2 < cnt; base += kBatchRows) {
-      Batch<T> A;
-      issue_batch<STREAM, DUP>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
-      consume_batch(A, st, qf, qscale);
-    }
-    if (base < cnt) {
-      Batch<T, kGatherUnroll / 2> A;
-      issue_batch<STREAM, DUP>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
-      consume_batch(A, st, qf, qscale);
-    }
-#else
     for (int base = 0; base < cnt; base += kBatchRows) {
       Batch<T> A;
       issue_batch<STREAM, DUP>(A, ids, base, cnt, r, kb, vb, row_stride, dup, h);
       consume_batch(A, st, qf, qscale);
     }
-#endif
 #pragma unroll
     for (int x = 16; x <= 32; x <<= 1) {
       float o2[8];
@@ -329,7 +284,7 @@ __device__ __forceinline__ void all_heads_pass(uint32_t mask, const int* ids, in
 
 // DUP: explicit plans over 2-way lists, with per-row duplicate head masks
 template <typename T, int G, bool EXPLICIT, bool DUP>
-__global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC void gather_attn_kernel(GatherParams p) {
+__global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) void gather_attn_kernel(GatherParams p) {
   constexpr int NW = gather_waves<EXPLICIT>();
   __shared__ __align__(16) T qs[G * kHeadDim];
   __shared__ int ids_lds[NW][kSegRows];
@@ -496,11 +451,11 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) TSA_GATHER_OCC vo
     // heads' arithmetic would lengthen. (2-way lists keep per-head passes:
     // their duplicate masks differ per head.)
     const bool all_heads =
-        !EXPLICIT || (TSA_GATHER_FULLMASK_ALL && G > 1 && !two_way &&
+        !EXPLICIT || (G > 1 && !two_way &&
                       (mask == (1u << G) - 1u || (p.multi_all && (mask & (mask - 1u)) != 0u)));
     if (all_heads) {
       all_heads_pass<G>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part);
-    } else if (TSA_GATHER_NT && (mask & (mask - 1u)) == 0u) {
+    } else if (kGatherStream && (mask & (mask - 1u)) == 0u) {
       head_passes<true, DUP>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);
     } else {
       head_passes<false, DUP>(mask, ids, cnt, r, e, kb, vb, row_stride, qs, p.qscale, part, dup);
@@ -639,7 +594,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(Gathe
       }
     } else if (my_mask != 0u && (my_mask & (my_mask - 1u)) == 0u) {
       const int h = __builtin_ctz(my_mask);
-      put(h, head_pass<TSA_GATHER_NT != 0, DUP>(h, ids, my_cnt, r, e, kb, vb, row_stride, qs, p.qscale, dup));
+      put(h, head_pass<kGatherStream, DUP>(h, ids, my_cnt, r, e, kb, vb, row_stride, qs, p.qscale, dup));
     } else if (my_mask != 0u) {  // a list several heads chose, or a sink / window range
       HeadState st[G];
       all_heads_states<G>(st, ids, my_cnt, r, e, kb, vb, row_stride, qs, p.qscale, [](int) { return ~0u; });

@@ -66,10 +66,7 @@ int gather_blocks_per_head(int expected_segments, bool explicit_plan) {
 // 256 / 128 / 64 rows that still gives at least 2048 segments (8 waves per
 // CU). Longer segments write fewer partial softmax states; shorter ones keep
 // every CU busy when the batch is small.
-#ifndef TSA_MIN_ROW_SEGS
-#define TSA_MIN_ROW_SEGS 2048
-#endif
-constexpr long long kMinRowSegments = TSA_MIN_ROW_SEGS;
+constexpr long long kMinRowSegments = 2048;
 int row_seg_rows(long long pairs, int max_rows) {
   for (int r = kSegRows; r > kRowSegRows; r >>= 1)
     if (pairs * ceil_div(max_rows, r) >= kMinRowSegments) return r;
@@ -81,10 +78,7 @@ int row_seg_rows(long long pairs, int max_rows) {
 // on a few CUs: about kFetchWorkgroups large workgroups in all, which still
 // keep the host link busy, and leave the other CUs to attention running
 // beside it.
-#ifndef TSA_FETCH_WGS
-#define TSA_FETCH_WGS 64
-#endif
-constexpr long long kFetchWorkgroups = TSA_FETCH_WGS;
+constexpr long long kFetchWorkgroups = 64;
 FetchParams fetch_params(const tsa_cache_desc& d, const int32_t* miss_tok, const int32_t* miss_slot,
                          const int32_t* misses, int k, int layers) {
   FetchParams fp{};
@@ -110,10 +104,7 @@ struct IvfLayout {
 // data), since one select workgroup per group would read the whole codebook
 // through a few CUs; and list segments that several heads chose get one
 // cacheable pass per head instead of one all-heads pass.
-#ifndef TSA_SMALL_BATCH_GROUPS
-#define TSA_SMALL_BATCH_GROUPS 128
-#endif
-constexpr long long kSmallBatchGroups = TSA_SMALL_BATCH_GROUPS;
+constexpr long long kSmallBatchGroups = 128;
 
 // Plan segments expected for one chosen list with `rows`-row segments: its
 // average length N * m / C in segments, rounded, plus room for a ragged tail.
@@ -128,10 +119,7 @@ int ivf_list_segs(const tsa_ivf_desc& d, int m, int rows) {
 // and write the fewest partial states; a single request cuts its lists finer
 // so that enough waves stream rows at once. A segment count bound per
 // (request, KV head) keeps the worst-case workspace of long contexts in check.
-#ifndef TSA_MIN_IVF_SEGS
-#define TSA_MIN_IVF_SEGS 2048
-#endif
-constexpr long long kMinIvfSegments = TSA_MIN_IVF_SEGS;
+constexpr long long kMinIvfSegments = 2048;
 constexpr int kIvfMinSegRows = 32;
 constexpr long long kIvfMaxPlanSegs = 16384;
 int ivf_seg_rows(const tsa_ivf_desc& d, int k, int m) {

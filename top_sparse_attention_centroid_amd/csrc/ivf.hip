@@ -144,10 +144,7 @@ constexpr int kMfmaCs = 256;      // centroids per LDS stage
 constexpr int kMfmaKb = 1024;     // keys per workgroup
 constexpr int kMfmaWaves = 8;
 constexpr int kCentPad = 136;     // LDS row stride in elements (128 + 8)
-#ifndef TSA_ASSIGN_TILES
-#define TSA_ASSIGN_TILES 4
-#endif
-constexpr int kAssignTiles = TSA_ASSIGN_TILES;  // 16-key tiles scored per pass over the staged centroids
+constexpr int kAssignTiles = 4;  // 16-key tiles scored per pass over the staged centroids
 
 __global__ __launch_bounds__(256) void centroid_norms_kernel(const bf16_t* cent, float* norms, long long rows) {
   const long long row = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) / 16;

@@ -12,18 +12,9 @@ namespace tsa {
 constexpr int kHeadDimRows = 128;   // d: elements per row (head_dim)
 constexpr int kSegRows = 256;       // max rows per attention segment (one wave's work unit)
 constexpr int kRowSegRows = 64;       // shortest segment for per-request row lists (token / slot paths)
-#ifndef TSA_GATHER_WPB
-#define TSA_GATHER_WPB 1
-#endif
-#ifndef TSA_GATHER_WPB_ROWS
-#define TSA_GATHER_WPB_ROWS 4
-#endif
-constexpr int kGatherWavesExplicit = TSA_GATHER_WPB;    // gather waves per workgroup, IVF plans
-constexpr int kGatherWavesRows = TSA_GATHER_WPB_ROWS;   // ... per-request row lists
-#ifndef TSA_GATHER_SPW
-#define TSA_GATHER_SPW 1
-#endif
-constexpr int kGatherSegsPerWave = TSA_GATHER_SPW;  // segments each gather wave is planned to take
+constexpr int kGatherWavesExplicit = 1;    // gather waves per workgroup, IVF plans
+constexpr int kGatherWavesRows = 4;   // ... per-request row lists
+constexpr int kGatherSegsPerWave = 1;  // segments each gather wave is planned to take
 // A partial softmax state is five whole 128-byte lines: line 0 holds m, l and
 // zero fill, lines 1-4 hold o[128]. One wave writes every byte of each line,
 // so no line reaches HBM partly written (HBM3E spends its mask pins on ECC,
@@ -31,18 +22,12 @@ constexpr int kGatherSegsPerWave = TSA_GATHER_SPW;  // segments each gather wave
 // controller). Records stay line-aligned when the workspace is 128-byte
 // aligned, as every device allocation is.
 constexpr int kPartStride = 160;    // floats per partial state
-#ifndef TSA_MERGE_WAVES
-#define TSA_MERGE_WAVES 3
-#endif
 // waves (and plan segments) per merging gather workgroup; at the batched
 // 64 x 32K decode 3 measured best (2: fewer states merged, 4 and up: a
 // workgroup waits longer for its longest segment, 6 also loses occupancy)
-constexpr int kMergeWaves = TSA_MERGE_WAVES;
+constexpr int kMergeWaves = 3;
 constexpr int kPartO = 32;          // offset of o[128] within the state
-#ifndef TSA_SCORE_TILE
-#define TSA_SCORE_TILE 2048
-#endif
-constexpr int kTokScoreTile = TSA_SCORE_TILE;  // indexer tokens scored per workgroup
+constexpr int kTokScoreTile = 2048;  // indexer tokens scored per workgroup
 constexpr int kTokFilterTile = 4096;      // score keys filtered per workgroup
 constexpr int kTokHistBits = 12;          // top bits of the score key in the threshold histogram
 constexpr int kTokHistBins = 1 << kTokHistBits;

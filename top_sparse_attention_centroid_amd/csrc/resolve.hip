@@ -210,10 +210,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 
 // grid (B, layers, split): workgroup z of (request, layer) takes every
 // split-th wave's share of the request's misses
-#ifndef TSA_FETCH_THREADS
-#define TSA_FETCH_THREADS 1024
-#endif
-constexpr int kFetchThreads = TSA_FETCH_THREADS;
+constexpr int kFetchThreads = 1024;
 __global__ __launch_bounds__(kFetchThreads) void fetch_rows_kernel(FetchParams p) {
   constexpr int NW = kFetchThreads / kWave;
   const int b = blockIdx.x, layer = blockIdx.y, z = blockIdx.z;

@@ -29,10 +29,7 @@ namespace tsa {
 
 constexpr int kIdxDim = 64;
 constexpr int kScoreThreads = 256;
-#ifndef TSA_SCORE_UNROLL
-#define TSA_SCORE_UNROLL 8
-#endif
-constexpr int kScoreUnroll = TSA_SCORE_UNROLL;  // 16-B loads in flight per lane
+constexpr int kScoreUnroll = 8;  // 16-B loads in flight per lane
 constexpr int kFilterThreads = 256;
 constexpr int kFinalThreads = 1024;
 constexpr int kHistShift = 32 - kTokHistBits;
