@@ -32,7 +32,7 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def _library_small_batch_groups():
     with open(os.path.join(ROOT, "top_sparse_attention_centroid_amd", "csrc", "capi.cpp")) as f:
-        m = re.search(r"#define TSA_SMALL_BATCH_GROUPS (\d+)", f.read())
+        m = re.search(r"constexpr long long kSmallBatchGroups = (\d+);", f.read())
     assert m, "capi.cpp no longer defines the small-batch threshold"
     return int(m.group(1))
 
