@@ -36,7 +36,16 @@ def _check_index(p, requests, offsets, ids):
     return ref
 
 
-def _decode_and_check(cfg, p, ref_lists, requests, steps, q=None):
+def _f32(t: torch.Tensor) -> np.ndarray:
+    """Host copy widened to fp32 (exact for bf16 and fp32 storage); the oracle
+    widens it to fp64 itself."""
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def _decode_and_check(cfg, p, ref_lists, requests, steps, q=None, sel_requests=()):
+    """Decodes `steps` steps of the whole batch and checks `requests` in full
+    (selection, row counts, unique rows, outputs) against the oracle's own
+    index; `sel_requests` get their selections checked too (scores alone)."""
     B, Hq, Hkv, k = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.top_k
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     if q is None:
@@ -44,8 +53,8 @@ def _decode_and_check(cfg, p, ref_lists, requests, steps, q=None):
     sel = torch.empty((B, Hq, k), dtype=torch.int32, device=DEV)
     rows = torch.empty((B, Hq), dtype=torch.int32, device=DEV)
     uniq = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
-    K64 = {b: f64(p["keys"][b:b + 1]) for b in requests}
-    V64 = {b: f64(p["values"][b:b + 1]) for b in requests}
+    K64 = {b: _f32(p["keys"][b:b + 1]) for b in requests}
+    V64 = {b: _f32(p["values"][b:b + 1]) for b in requests}
     cent64 = f64(p["centroids"])
     for t in range(steps):
         out = tsa.sparse_decode(q[t], p["centroids"], offsets, ids, p["keys"], p["values"], k,
@@ -53,6 +62,12 @@ def _decode_and_check(cfg, p, ref_lists, requests, steps, q=None):
         torch.cuda.synchronize()
         q64 = f64(q[t])
         out_g, sel_g, rows_g, uniq_g = out.cpu().numpy(), sel.cpu().numpy(), rows.cpu().numpy(), uniq.cpu().numpy()
+        for b in sel_requests:
+            cb = cent64[0 if cent64.shape[0] == 1 else b]
+            for h in range(Hq):
+                s_bh = ivf.centroid_scores(q64[b, h], cb[h // (Hq // Hkv)])
+                assert ivf.selection_gap(s_bh, k) >= GAP_MIN
+                assert np.array_equal(sel_g[b, h], ivf.top_k(s_bh, k)), f"selection differs (step {t}, {b}, {h})"
         for b in requests:
             off_b = ref_lists[b][0][None]
             ids_b = ref_lists[b][1][None]
@@ -155,17 +170,18 @@ def test_empty_selection_gives_zero_and_flag():
     assert out_error(o[0, 1], r.out) <= OUT_TOL
 
 
-def test_batched_workload_full_size_sampled():
-    """64 requests x 32K tokens, shared codebook C=256, top-16: every request is
-    decoded on the GPU; two sampled requests are checked in full by the oracle
-    (its own index, its own selection)."""
+def test_batched_workload_full_size():
+    """64 requests x 32K tokens, shared codebook C=256, top-16: the selections
+    of all 64 requests are checked; eight requests spread over the batch
+    (including the last) are checked in full by the oracle (its own index,
+    its own selection, row counts and outputs)."""
     cfg = W.config(2)
     announce(f"ivf {cfg.name} full size")
     p = _problem(cfg)
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
-    sample = [0, 41]
+    sample = [0, 9, 18, 27, 36, 45, 54, 63]
     ref = _check_index(p, sample, offsets, ids)
-    q = _decode_and_check(cfg, p, ref, sample, steps=2)
+    q = _decode_and_check(cfg, p, ref, sample, steps=2, sel_requests=range(cfg.batch))
     # determinism: a second identical call is bitwise identical
     o1 = tsa.sparse_decode(q[0], p["centroids"], offsets, ids, p["keys"], p["values"], cfg.top_k)
     o2 = tsa.sparse_decode(q[0], p["centroids"], offsets, ids, p["keys"], p["values"], cfg.top_k)

@@ -13,7 +13,7 @@ import top_sparse_attention_centroid_amd as tsa
 from oracle import cache
 from top_sparse_attention_centroid_amd import workloads as W
 
-from helpers import announce
+from helpers import OUT_TOL, announce, f64, out_error
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -62,6 +62,9 @@ def test_layer_group_prefetch(policy):
     fetch_stream = torch.cuda.Stream()
     events = [torch.cuda.Event(), torch.cuda.Event()]
     ref = {b: cache.CacheState(N, S) for b in range(B)}
+    hosts = [[(f64(L["kf"][b]), f64(L["vf"][b])) for L in lay] for b in range(B)]
+    Hkv, d = cfg.n_kv_heads, cfg.head_dim
+    ref_pools = [[(np.zeros((S, Hkv, d)), np.zeros((S, Hkv, d))) for _ in lay] for b in range(B)]
     for t in range(steps):
         results = []
         for (pt, st, lu, pools, outs), fs in ((over, fetch_stream), (inorder, None)):
@@ -80,10 +83,16 @@ def test_layer_group_prefetch(policy):
             assert torch.equal(out_i[j], direct)
         sg, pt_g = s_o.cpu().numpy(), over[0].cpu().numpy()
         for b in range(B):
-            r_slots, r_h, r_m, _ = cache.policy_step(ref[b], tr_np[t, b], t, policy)
+            # the oracle's group step: one shared set of tables, every layer's
+            # own rows fetched into its own pool; then attention per layer
+            r_slots, r_h, r_m, _ = cache.group_step(ref[b], tr_np[t, b], t, hosts[b], ref_pools[b], policy)
             assert np.array_equal(sg[b], r_slots), f"slots differ (step {t}, request {b})"
             assert (int(h_o[b]), int(m_o[b])) == (r_h, r_m)
             assert np.array_equal(pt_g[b], ref[b].page_table)
+            for j, L in enumerate(lay):
+                o = cache.attend_slots(f64(L["q"][t, b]), ref_pools[b][j][0], ref_pools[b][j][1], r_slots)
+                err = out_error(out_o[j][b].cpu().numpy(), o)
+                assert err <= OUT_TOL, f"output error {err} (step {t}, layer {j}, request {b})"
     # every layer's pool holds its own rows of every resident token
     st_g = over[1].cpu()
     for j, L in enumerate(lay):

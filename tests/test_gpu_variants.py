@@ -7,10 +7,10 @@ import pytest
 import torch
 
 import top_sparse_attention_centroid_amd as tsa
-from oracle import ivf, variants
+from oracle import append, cache, ivf, token, variants
 from top_sparse_attention_centroid_amd import workloads as W
 
-from helpers import GAP_MIN, OUT_TOL, announce, f64, out_error
+from helpers import GAP_MIN, MARGIN_MIN, OUT_TOL, announce, condition_token_keys, f64, out_error
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -22,10 +22,21 @@ def _problem(seed_scale=0, **kw):
     cfg = W.config(2, **base)
     p = W.ivf_problem(cfg, device=DEV)
     if seed_scale:
-        # unequal centroid norms, so that cosine and dot rankings differ
+        # unequal centroid norms, so that cosine and dot rankings differ; every
+        # key moves with its own centre (its nearest unscaled centroid, found
+        # by the oracle), so it keeps a wide assignment margin
         g = torch.Generator(device=DEV).manual_seed(seed_scale)
         f = torch.rand(p["centroids"].shape[:-1] + (1,), generator=g, device=DEV) * 1.5 + 0.5
-        p["centroids"] = (p["centroids"].float() * f).to(cfg.torch_dtype)
+        c32 = p["centroids"].float()
+        keys = p["keys"].float()
+        c64 = f64(p["centroids"])
+        for b in range(cfg.batch):
+            for h in range(cfg.n_kv_heads):
+                comp, _ = ivf.nearest_centroid(f64(p["keys"][b, :, h]), c64[0, h])
+                comp = torch.from_numpy(comp).to(DEV)
+                keys[b, :, h] += (f[0, h, comp] - 1.0) * c32[0, h, comp]
+        p["keys"] = keys.to(cfg.torch_dtype)
+        p["centroids"] = (c32 * f).to(cfg.torch_dtype)
     return cfg, p
 
 
@@ -52,9 +63,15 @@ def _queries(cfg, p, similarity, max_rounds=40):
 
 
 def _check(cfg, p, q, off, ids, out, sel, **kw):
+    """The oracle builds its own posting lists (every assignment margin must
+    be wide enough for an exact comparison), which must equal the GPU's, then
+    decodes over them; the selection must match exactly and the output within
+    OUT_TOL."""
     k64, v64, c64 = f64(p["keys"]), f64(p["values"]), f64(p["centroids"])
-    o64, i64 = off.cpu().numpy(), ids.cpu().numpy()
-    r = variants.sparse_decode_ex(f64(q), c64, o64, i64, k64, v64, cfg.top_k, **kw)
+    r_off, r_ids, margins = ivf.index_build(k64, c64)
+    assert margins.min() >= MARGIN_MIN, f"assignment margin {margins.min()} too small for an exact comparison"
+    assert np.array_equal(off.cpu().numpy(), r_off) and np.array_equal(ids.cpu().numpy(), r_ids)
+    r = variants.sparse_decode_ex(f64(q), c64, r_off, r_ids, k64, v64, cfg.top_k, **kw)
     assert np.all(r["gap"] >= GAP_MIN)
     assert np.array_equal(sel.cpu().numpy(), r["sel"]), "selection differs from the oracle"
     err = out_error(out.cpu().numpy(), r["out"])
@@ -141,18 +158,33 @@ def test_variants_over_a_growing_index(batch, n_kv_heads):
     out = tsa.sparse_decode_ex(q, p["centroids"], off, ids, k_cache, v_cache, cfg.top_k, similarity="cosine",
                                n_sink=32, n_window=128, lengths=lengths, lens=lens, sel_out=sel)
     torch.cuda.synchronize()
-    assert int(status.max()) <= 1
-    og, lg, ig = off.cpu().numpy(), lens.cpu().numpy(), ids.cpu().numpy()
-    B, Hkv, C = lg.shape
-    s_off = np.zeros((B, Hkv, C + 1), dtype=np.int64)
-    s_ids = np.full((B, Hkv, cfg.n_tokens), -1, dtype=np.int64)
-    from oracle import append
+    # the oracle grows its own index over the same keys: a prefix build with
+    # the same slack, then one append per row, in row order
+    k64, c64 = f64(p["keys"]), f64(p["centroids"])
+    B, Hkv, C = cfg.batch, cfg.n_kv_heads, cfg.n_centroids
+    slack = (cfg.n_tokens - n_prefix) // C
     for b in range(B):
         for g in range(Hkv):
-            co, ci = append.compact(og[b, g], lg[b, g], ig[b, g])
+            _, margin = ivf.nearest_centroid(k64[b, :n_prefix + 200, g], c64[0, g])
+            assert margin.min() >= MARGIN_MIN, f"assignment margin {margin.min()} too small for an exact comparison"
+    state = {(b, g): append.index_build_dynamic(k64[b, :, g], c64[0, g], n_prefix, slack)
+             for b in range(B) for g in range(Hkv)}
+    K_ref, V_ref = k64.copy(), f64(p["values"])
+    for row in range(n_prefix, n_prefix + 200):
+        append.append_step(state, k64[:, row], V_ref[:, row].copy(), np.full(B, row), c64, K_ref, V_ref)
+    og, lg, ig = off.cpu().numpy(), lens.cpu().numpy(), ids.cpu().numpy()
+    s_off = np.zeros((B, Hkv, C + 1), dtype=np.int64)
+    s_ids = np.full((B, Hkv, cfg.n_tokens), -1, dtype=np.int64)
+    for b in range(B):
+        for g in range(Hkv):
+            r_off, r_lens, r_ids = state[(b, g)]
+            assert np.array_equal(og[b, g], r_off) and np.array_equal(lg[b, g], r_lens)
+            assert np.array_equal(ig[b, g], r_ids), f"growing lists differ (request {b}, KV head {g})"
+            co, ci = append.compact(r_off, r_lens, r_ids)
             s_off[b, g] = co
             s_ids[b, g, :len(ci)] = ci
-    r = variants.sparse_decode_ex(f64(q), f64(p["centroids"]), s_off, s_ids, f64(k_cache), f64(v_cache),
+    assert int(status.max()) <= 1
+    r = variants.sparse_decode_ex(f64(q), c64, s_off, s_ids, K_ref, V_ref,
                                   cfg.top_k, similarity="cosine", n_sink=32, n_window=128,
                                   lengths=lengths.cpu().numpy())
     assert np.all(r["gap"] >= GAP_MIN)
@@ -162,14 +194,18 @@ def test_variants_over_a_growing_index(batch, n_kv_heads):
 
 
 def test_token_selection_feeds_the_hot_cache():
-    """The indexer's selection drives RESOLVE; attention over the slots is
-    bitwise the token decode's attention over the full cache."""
+    """The indexer's selection drives RESOLVE, then attention over the slots,
+    checked against the oracle's chain: its top-k over the indexer scores, its
+    LRU step on that selection (tables, hits, misses, fetched rows into its
+    own pool) and its attention over its own pool's slots. The GPU's cache
+    path is also bitwise the token decode's direct attention."""
     cfg = W.config(3, batch=2, n_tokens=30_000, top_k=512, n_planted=16, steps=4)
     announce("token selection -> RESOLVE -> attention over slots")
     B, N, Hkv, d, k = cfg.batch, cfg.n_tokens, cfg.n_kv_heads, cfg.head_dim, cfg.top_k
-    S = 1024
+    S, steps = 1024, 4
     prob = W.token_problem(cfg, device=DEV)
-    q_idx, q = W.token_queries(cfg, prob, steps=4)
+    q_idx, q = W.token_queries(cfg, prob, steps=steps)
+    k_idx = condition_token_keys(q_idx, prob["k_idx"], k, steps)
     hk = tsa.HostArray((B, N, Hkv, d), cfg.torch_dtype)
     hv = tsa.HostArray((B, N, Hkv, d), cfg.torch_dtype)
     hk.tensor.copy_(prob["keys"])
@@ -181,14 +217,31 @@ def test_token_selection_feeds_the_hot_cache():
     pool_k = torch.zeros((B, S, Hkv, d), dtype=cfg.torch_dtype, device=DEV)
     pool_v = torch.zeros_like(pool_k)
     sel = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    ref = [cache.CacheState(N, S) for _ in range(B)]
+    host_k, host_v = f64(prob["keys"]), f64(prob["values"])
+    ref_pk, ref_pv = np.zeros((B, S, Hkv, d)), np.zeros((B, S, Hkv, d))
+    qi64, q64, kidx64 = f64(q_idx), f64(q), f64(k_idx)
     misses = []
-    for t in range(4):
-        out_tok = tsa.token_decode(q_idx[t], prob["k_idx"], q[t], prob["keys"], prob["values"], k, sel_out=sel)
+    for t in range(steps):
+        out_tok = tsa.token_decode(q_idx[t], k_idx, q[t], prob["keys"], prob["values"], k, sel_out=sel)
         slots, hits, miss = tsa.resolve(pt, st, lu, sel, t, hk.tensor, hv.tensor, pool_k, pool_v)
         out_cache = tsa.attend_rows(q[t], pool_k, pool_v, slots)
         torch.cuda.synchronize()
         assert torch.equal(out_cache, out_tok), f"step {t}: cache path differs from the direct path"
-        assert torch.equal(hits + miss, torch.full_like(hits, k))
+        sel_g, slots_g, hits_g, miss_g = sel.cpu().numpy(), slots.cpu().numpy(), hits.cpu().numpy(), miss.cpu().numpy()
+        pt_g, st_g, lu_g, out_g = pt.cpu().numpy(), st.cpu().numpy(), lu.cpu().numpy(), out_cache.cpu().numpy()
+        for b in range(B):
+            r_sel, gap = token.token_topk(qi64[t, b], kidx64[b], k)
+            assert gap >= GAP_MIN
+            assert np.array_equal(sel_g[b], r_sel), f"selection differs (step {t}, request {b})"
+            r_slots, r_h, r_m, fetches = cache.lru_step(ref[b], r_sel, t)
+            cache.fetch_rows(ref_pk[b], ref_pv[b], host_k[b], host_v[b], fetches)
+            assert np.array_equal(slots_g[b], r_slots) and (hits_g[b], miss_g[b]) == (r_h, r_m)
+            assert np.array_equal(pt_g[b], ref[b].page_table) and np.array_equal(st_g[b], ref[b].slot_token)
+            assert np.array_equal(lu_g[b], ref[b].last_use)
+            o = cache.attend_slots(q64[t, b], ref_pk[b], ref_pv[b], r_slots)
+            err = out_error(out_g[b], o)
+            assert err <= OUT_TOL, f"output error {err} (step {t}, request {b})"
         misses.append(int(miss.sum()))
     assert misses[0] == B * k and min(misses[1:]) < B * k   # planted tokens stay selected and hit
 
