@@ -59,6 +59,9 @@ extern "C" {
 
 #define TSA_ABI_VERSION 1
 
+/* Size of the static device scratch of tsa_sparse_decode_noalloc. */
+#define TSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
 typedef enum tsa_status {
   TSA_OK = 0,
   TSA_ERR_INVALID_ARG = 1,
@@ -178,6 +181,31 @@ tsa_status tsa_sparse_decode(const tsa_ivf_desc* desc, const void* q, const void
                              const void* v_cache, int32_t k, float* out, int32_t* sel_out,
                              int32_t* rows_out, int32_t* uniq_out, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * tsa_sparse_decode_noalloc - tsa_sparse_decode without a workspace
+ *   argument, for callers that cannot allocate device memory (code under HIP
+ *   graph capture, tight serving loops, harnesses that forbid allocation).
+ *   Computes exactly what tsa_sparse_decode computes (bitwise the same
+ *   outputs for the same desc and k), with the same arguments minus ws and
+ *   ws_bytes; it calls no allocating routine.
+ *   Its workspace is a static device array of TSA_NOALLOC_SCRATCH_BYTES
+ *   (64 MiB) inside the library: each GPU the library runs on holds one until
+ *   the process ends. A decode whose workspace
+ *   (tsa_workspace_bytes(TSA_OP_SPARSE_DECODE, ...)) exceeds it is rejected
+ *   with TSA_ERR_WORKSPACE before anything is enqueued; one 100K-token
+ *   request (8 KV / 32 query heads, C = 1000, k = 10) or 16 requests of 32K
+ *   tokens (C = 256, k = 16) fit.
+ *   Every call on one GPU shares that GPU's array, and no output depends on
+ *   what an earlier call left in it. Calls that overlap on one GPU (on
+ *   different streams or threads, without ordering between them) race on
+ *   the array and give undefined results. The stream must belong to the
+ *   current device.
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_sparse_decode_noalloc(const tsa_ivf_desc* desc, const void* q, const void* centroids,
+                                     const int32_t* offsets, const int32_t* ids, const void* k_cache,
+                                     const void* v_cache, int32_t k, float* out, int32_t* sel_out,
+                                     int32_t* rows_out, int32_t* uniq_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * tsa_index_build_multi - posting lists in which every key joins its m

@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     sparse_decode,
     sparse_decode_dyn,
     sparse_decode_ex,
+    sparse_decode_noalloc,
     time_next_gather,
     token_decode,
     workspace_bytes,
@@ -32,7 +33,7 @@ from .binding import (  # noqa: F401
 
 __all__ = [
     "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "index_build_multi", "kv_append", "sparse_decode",
-    "sparse_decode_dyn", "sparse_decode_ex", "token_decode",
+    "sparse_decode_dyn", "sparse_decode_ex", "sparse_decode_noalloc", "token_decode",
     "attend_rows", "resolve", "cache_reset", "fetch_rows", "hier_group_step", "HostArray", "time_next_gather", "workspace_bytes",
     "TsaError",
 ]

@@ -59,6 +59,7 @@ _SIGNATURES = {
     "tsa_index_build": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_sparse_decode": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                           ctypes.c_size_t, _P],
+    "tsa_sparse_decode_noalloc": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P],
     "tsa_sparse_decode_ex": [ctypes.POINTER(IvfDesc), ctypes.POINTER(DecodeOpts), _P, _P, _P, _P, _P, _P, _I32,
                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_index_build_multi": [ctypes.POINTER(IvfDesc), _P, _P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -387,6 +388,33 @@ def sparse_decode(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, out=N
                                             _ptr(lens), _ptr(ids), _ptr(k_cache), _ptr(v_cache), k, _ptr(out),
                                             _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(),
                                             _stream(stream)))
+    return out
+
+
+def sparse_decode_noalloc(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, out, sel_out=None,
+                          rows_out=None, uniq_out=None, stream=None):
+    """sparse_decode with the library's static device scratch instead of a
+    workspace: the call allocates nothing, so `out` must be given."""
+    for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
+        _dev(t, n)
+    if not (q.dtype == centroids.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, centroids, k_cache and v_cache must share a dtype")
+    B, Hq, d = q.shape
+    desc = ivf_desc(k_cache, centroids, Hq)
+    if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("q / k_cache / v_cache shapes disagree")
+    Hkv, C, N = desc.n_kv_heads, desc.n_centroids, desc.n_tokens
+    _i32(offsets, "offsets", (B, Hkv, C + 1))
+    _i32(ids, "ids", (B, Hkv, N))
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, d):
+        raise ValueError("out must be fp32 [B][Hq][d]")
+    _i32(sel_out, "sel_out", (B, Hq, k))
+    _i32(rows_out, "rows_out", (B, Hq))
+    _i32(uniq_out, "uniq_out", (B, Hkv))
+    _check(load().tsa_sparse_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(centroids), _ptr(offsets), _ptr(ids),
+                                            _ptr(k_cache), _ptr(v_cache), k, _ptr(out), _ptr(sel_out),
+                                            _ptr(rows_out), _ptr(uniq_out), _stream(stream)))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.hpp"
@@ -764,6 +765,66 @@ tsa_status tsa_host_free(void* host_ptr) {
   hipError_t e = hipHostFree(host_ptr);
   if (e != hipSuccess) return hip_fail(e, "hipHostFree");
   return ok();
+}
+
+// Allocation-free decode. The workspace of tsa_sparse_decode_noalloc is a
+// fixed array in the library's device code object instead of caller memory:
+// each GPU the library runs on holds its own copy until the process ends.
+// In host code the array's name stands for a host-side shadow, so kernels get
+// the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[TSA_NOALLOC_SCRATCH_BYTES];
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device, with the device current).
+tsa_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(TSA_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(TSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tsa_status tsa_sparse_decode_noalloc(const tsa_ivf_desc* desc, const void* q, const void* centroids,
+                                     const int32_t* offsets, const int32_t* ids, const void* k_cache,
+                                     const void* v_cache, int32_t k, float* out, int32_t* sel_out,
+                                     int32_t* rows_out, int32_t* uniq_out, void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  // every check runs before the scratch address is looked up
+  REQUIRE_PTR(q); REQUIRE_PTR(centroids); REQUIRE_PTR(offsets); REQUIRE_PTR(ids);
+  REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(out);
+  REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(k_cache, 16);
+  REQUIRE_ALIGN(v_cache, 16); REQUIRE_ALIGN(out, 8);
+  if (k < 1 || k > desc->n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, desc->n_centroids);
+  const size_t need = ivf_layout(*desc, k, false, 1).total;
+  if (need > static_cast<size_t>(TSA_NOALLOC_SCRATCH_BYTES))
+    return fail(TSA_ERR_WORKSPACE, "this decode needs %zu bytes of workspace; the static scratch holds %zu",
+                need, static_cast<size_t>(TSA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (tsa_status s = scratch_ptr(&ws)) return s;
+  return sparse_decode_impl(desc, nullptr, q, centroids, offsets, nullptr, ids, k_cache, v_cache, k, out, sel_out,
+                            rows_out, uniq_out, ws, static_cast<size_t>(TSA_NOALLOC_SCRATCH_BYTES), stream);
 }
 
 tsa_status tsa_time_next_gather(void* ev_start, void* ev_stop) {
