@@ -32,8 +32,10 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-decode queries/s + gathered-KV GB/s as % of MI355X HBM peak"
 HBM_PEAK_GBPS = 8000.0
 ROW_BYTES_BF16 = 2 * 128 * 2  # one K row + one V row, 128 bf16 each
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gather_attn_traffic.json")
-GATHER_SRC = os.path.join(ROOT, "top_sparse_attention_centroid_amd", "csrc", "attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+SRC_DIR = os.path.join(ROOT, "top_sparse_attention_centroid_amd", "csrc")
+HEADER = os.path.join(ROOT, "include", "tsa.h")
+KERNEL_NAMES = {"token_scan": "token_score_kernel", "resolve": "resolve_kernel"}
 
 
 def parse():
@@ -76,6 +78,9 @@ def parse():
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="write the HBM-traffic record of this workload's kernels from rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE passes under DIR (see record_traffic) and exit; no GPU work")
     return ap.parse_args()
 
 
@@ -83,9 +88,16 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gather_source_sha() -> str:
-    with open(GATHER_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_sha() -> str:
+    """sha256 prefix over every library source (kernels, launch and plan code,
+    the C-ABI header): counter bytes are reported only while it matches."""
+    h = hashlib.sha256()
+    files = sorted(n for n in os.listdir(SRC_DIR) if n.endswith((".hip", ".hpp", ".cpp", ".h")))
+    for path in [os.path.join(SRC_DIR, n) for n in files] + [HEADER]:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def gather_kernel_name(cfg, args) -> str:
@@ -99,16 +111,16 @@ def gather_kernel_name(cfg, args) -> str:
     return "gather_attn_kernel"
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per gather launch from the committed counter summary, if it was
-    taken on the current kernel source and this workload; else None."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    record, if it was taken on the current library source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(workload)
-    if not entry or entry.get("kernel_source_sha") != gather_source_sha():
+    entry = rec.get(f"{workload}/{kernel}")
+    if not entry or entry.get("kernel_source_sha") != kernel_source_sha():
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -219,43 +231,215 @@ def bench_ivf(args, cfg, torch, tsa, W):
     row_bytes = 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
     res.update({"gathered_bytes": rows * row_bytes, "queries": B * args.steps, "index_build_ms": index_ms,
                 "unique_rows_per_step": rows / args.steps})
-    if args.cpu_seconds > 0:
-        res["cpu"] = cpu_baseline_ivf(args, cfg, p, q_all, torch, W)
+    if args.cpu_seconds > 0 and not variant:
+        res["cpu_sample"] = ("ivf",) + cpu_sample_ivf(cfg, p, q_all, torch)
     return res
 
 
-def cpu_baseline_ivf(args, cfg, p, q_all, torch, W):
-    """The oracle on whole (request, step) decode queries of the same workload
-    until the time budget is used: queries/s on the host, single BLAS thread."""
-    import numpy as np
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload, on one
+# core and on all the host cores this process may use (one process per core,
+# one BLAS thread each, started before the GPU is touched)
+# ----------------------------------------------------------------------------
+
+CPU_SAMPLE_REQUESTS = 2      # requests of the sample (queries cycle over them and the steps)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores() -> int:
+    """Cores this process may run on, capped at the 16 a one-GPU share of the
+    host provides."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _worker_ready(_):
+    time.sleep(0.2)
+    return os.getpid()
+
+
+def start_cpu_pool(n):
+    """Worker processes for the all-cores leg, spawned before this process
+    initialises the GPU (nothing is forked from a process holding it), and
+    waited for until every one has started, so that their start-up does not
+    compete with the timed GPU region for the host's cores."""
+    import multiprocessing as mp
+    pool = mp.get_context("spawn").Pool(n)
+    for _ in range(20):
+        if len(set(pool.map(_worker_ready, range(2 * n), chunksize=1))) == n:
+            break
+    return pool
+
+
+def cpu_quota():
+    """The cgroup CPU limit of this process, in cores (None if unlimited or
+    unknown)."""
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        return None if quota == "max" else round(int(quota) / int(period), 2)
+    except (OSError, ValueError):
+        return None
+
+
+class _OracleRunner:
+    """One oracle decode query of the sample per call: the data is the
+    sample's arrays, saved as fp32 (exact for bf16) .npy files and mapped
+    read-only, so every worker shares one copy in the page cache."""
+
+    def __init__(self, kind, data_dir, offset=0):
+        import numpy as np
+
+        def ld(name):
+            return np.load(os.path.join(data_dir, name + ".npy"), mmap_mode="r")
+
+        with open(os.path.join(data_dir, "meta.json")) as f:
+            self.meta = json.load(f)
+        self.kind, self.i = kind, offset
+        self.R, self.T = self.meta["requests"], self.meta["steps"]
+        self.K = [ld(f"K{r}") for r in range(self.R)]
+        self.V = [ld(f"V{r}") for r in range(self.R)]
+        self.q = ld("q")
+        if kind == "ivf":
+            self.cent = [ld(f"cent{r}") for r in range(self.R)]
+            self.off = [ld(f"off{r}") for r in range(self.R)]
+            self.ids = [ld(f"ids{r}") for r in range(self.R)]
+        elif kind == "token":
+            self.kidx = [ld(f"kidx{r}") for r in range(self.R)]
+            self.qidx = ld("qidx")
+        else:
+            self.trace = ld("trace")
+            self._fresh_caches()
+
+    def _fresh_caches(self):
+        import numpy as np
+        from oracle import cache
+        m = self.meta
+        self.state = [cache.CacheState(m["n_tokens"], m["n_slots"]) for _ in range(self.R)]
+        shape = (m["n_slots"], m["n_kv_heads"], m["head_dim"])
+        self.pool = [(np.zeros(shape), np.zeros(shape)) for _ in range(self.R)]
+
+    def __call__(self):
+        from oracle import cache, ivf, token
+        i, R, k = self.i, self.R, self.meta["top_k"]
+        self.i += 1
+        r = i % R
+        t = (i // R) % self.T
+        if self.kind == "ivf":
+            ivf.sparse_decode(self.q[t, r:r + 1], self.cent[r], self.off[r], self.ids[r], self.K[r], self.V[r], k)
+        elif self.kind == "token":
+            token.token_decode(self.qidx[t, r:r + 1], self.kidx[r][None], self.q[t, r:r + 1], self.K[r][None],
+                               self.V[r][None], k)
+        else:
+            if t == 0 and r == 0 and i > 0:
+                self._fresh_caches()             # the trace starts over from a cold cache
+            slots, _, _, fetches = cache.lru_step(self.state[r], self.trace[t, r], t)
+            cache.fetch_rows(self.pool[r][0], self.pool[r][1], self.K[r], self.V[r], fetches)
+            cache.attend_slots(self.q[t, r], self.pool[r][0], self.pool[r][1], slots)
+
+
+def cpu_oracle_loop(task):
+    """Runs oracle queries for `seconds`; returns (queries done, seconds)."""
+    kind, data_dir, seconds, offset = task
     from threadpoolctl import threadpool_limits
-
-    from oracle import ivf
-
-    reqs = [0, 1] if cfg.batch > 1 else [0]
-    log(f"oracle baseline: building its index for requests {reqs}")
-    K = {b: p["keys"][b:b + 1].to("cpu", torch.float64).numpy() for b in reqs}
-    V = {b: p["values"][b:b + 1].to("cpu", torch.float64).numpy() for b in reqs}
-    cent = p["centroids"].to("cpu", torch.float64).numpy()
-    index = {}
-    for b in reqs:
-        cb = cent[0:1] if cent.shape[0] == 1 else cent[b:b + 1]
-        off, ids, _ = ivf.index_build(K[b], cb)
-        index[b] = (cb, off, ids)
-    q64 = q_all.to("cpu", torch.float64).numpy()
-    done = 0
     with threadpool_limits(1):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < args.cpu_seconds:
-            b = reqs[done % len(reqs)]
-            t = (done // len(reqs)) % q64.shape[0]
-            cb, off, ids = index[b]
-            ivf.sparse_decode(q64[t, b:b + 1], cb, off, ids, K[b], V[b], cfg.top_k)
+        run = _OracleRunner(kind, data_dir, offset)
+        run()                                     # page the sample in, untimed
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            run()
             done += 1
-        el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} whole decode queries (all {cfg.n_q_heads} heads) of requests {reqs} "
-                      f"over {el:.1f} s, fp64 numpy, one BLAS thread; index built untimed"}
+        return done, time.perf_counter() - t0
+
+
+def cpu_baseline(args, kind, data_dir, what, pool):
+    """Single-core leg in this process, then the all-cores leg on the pool."""
+    import shutil
+    try:
+        one, el1 = cpu_oracle_loop((kind, data_dir, args.cpu_seconds / 2, 0))
+        res = {"value": one / el1, "unit": "queries/s", "cores": 1, "kind": "oracle",
+               "sample": f"{one} {what} over {el1:.1f} s on one core (fp64 numpy, one BLAS thread)",
+               "cpu_model": cpu_model(), "cpu_quota_cores": cpu_quota(), "os_cpu_count": os.cpu_count()}
+        if pool is not None:
+            n = pool._processes
+            outs = pool.map(cpu_oracle_loop, [(kind, data_dir, args.cpu_seconds / 2, 7919 * w) for w in range(n)])
+            total = sum(c for c, _ in outs)
+            el = max(e for _, e in outs)
+            res.update({"value": sum(c / e for c, e in outs), "cores": n,
+                        "sample": f"{total} {what} over {el:.1f} s on {n} cores (one process per core, fp64 "
+                                  f"numpy, one BLAS thread each); one core: {one} in {el1:.1f} s",
+                        "single_core_value": one / el1})
+        return res
+    finally:
+        shutil.rmtree(data_dir, ignore_errors=True)
+
+
+def _sample_dir(meta, arrays):
+    """Writes the sample's arrays (fp32 / int) for the oracle workers."""
+    import tempfile
+
+    import numpy as np
+    d = tempfile.mkdtemp(prefix="tsa_oracle_", dir="/tmp")
+    for name, a in arrays.items():
+        np.save(os.path.join(d, name + ".npy"), a)
+    with open(os.path.join(d, "meta.json"), "w") as f:
+        json.dump(meta, f)
+    return d
+
+
+def _f32np(t, torch):
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def cpu_sample_ivf(cfg, p, q_all, torch):
+    from oracle import ivf
+    R = min(CPU_SAMPLE_REQUESTS, cfg.batch)
+    log(f"oracle baseline: building its index for requests 0..{R - 1}")
+    arrays = {"q": _f32np(q_all[:, :R], torch)}
+    cent = _f32np(p["centroids"], torch)
+    for r in range(R):
+        cb = cent[0:1] if cent.shape[0] == 1 else cent[r:r + 1]
+        K = _f32np(p["keys"][r:r + 1], torch)
+        off, ids, _ = ivf.index_build(K, cb)
+        arrays.update({f"K{r}": K, f"V{r}": _f32np(p["values"][r:r + 1], torch), f"cent{r}": cb,
+                       f"off{r}": off, f"ids{r}": ids})
+    meta = {"requests": R, "steps": int(q_all.shape[0]), "top_k": cfg.top_k}
+    return _sample_dir(meta, arrays), f"whole decode queries (all {cfg.n_q_heads} heads; index built untimed)"
+
+
+def cpu_sample_token(cfg, prob, q_idx, q, torch):
+    R = 1                        # one request's 200K-token K/V (fp32) is already 1.6 GB of sample
+    arrays = {"q": _f32np(q[:, :R], torch), "qidx": _f32np(q_idx[:, :R], torch)}
+    for r in range(R):
+        arrays.update({f"K{r}": _f32np(prob["keys"][r], torch), f"V{r}": _f32np(prob["values"][r], torch),
+                       f"kidx{r}": _f32np(prob["k_idx"][r], torch)})
+    meta = {"requests": R, "steps": int(q.shape[0]), "top_k": cfg.top_k}
+    return _sample_dir(meta, arrays), (f"whole decode queries (indexer top-{cfg.top_k} over {cfg.n_tokens} "
+                                       f"tokens, attention of all {cfg.n_q_heads} heads)")
+
+
+def cpu_sample_cache(cfg, hk, hv, q, trace, steps, torch):
+    R = 1                        # one request's 128K-token K/V (fp32) is already 1 GB of sample
+    arrays = {"q": _f32np(q[:steps, :R], torch), "trace": trace[:steps, :R].cpu().numpy()}
+    for r in range(R):
+        arrays.update({f"K{r}": _f32np(hk[r], torch), f"V{r}": _f32np(hv[r], torch)})
+    meta = {"requests": R, "steps": steps, "top_k": cfg.top_k, "n_tokens": cfg.n_tokens, "n_slots": cfg.n_slots,
+            "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim}
+    return _sample_dir(meta, arrays), (f"decode queries from a cold cache (LRU step, host fetch into the "
+                                       f"oracle's pool, attention of all {cfg.n_q_heads} heads over the slots)")
 
 
 # ----------------------------------------------------------------------------
@@ -277,11 +461,15 @@ def bench_token(args, cfg, torch, tsa, W):
         tsa.token_decode(q_idx[i % nq], prob["k_idx"], q[i % nq], prob["keys"], prob["values"], k,
                          out=out, ws=ws)
 
-    res = _timed(args, call, torch, tsa, n_distinct=nq)
+    res = _timed(args, call, torch, tsa, n_distinct=nq, kernels=("gather", "token_scan"))
     res["gathered_bytes"] = args.steps * B * cfg.n_kv_heads * k * ROW_BYTES_BF16
     res["step_bytes"] = [B * cfg.n_kv_heads * k * ROW_BYTES_BF16] * args.steps
+    # the scan reads every indexer key (d_idx bf16) and writes one 4-byte score key per token
+    res["kernel_step_bytes"] = {"token_scan": [B * cfg.n_tokens * (cfg.idx_dim * 2 + 4)] * args.steps}
     res["queries"] = B * args.steps
     res["indexer_bytes_per_step"] = B * cfg.n_tokens * cfg.idx_dim * 2
+    if args.cpu_seconds > 0:
+        res["cpu_sample"] = ("token",) + cpu_sample_token(cfg, prob, q_idx, q, torch)
     return res
 
 
@@ -428,6 +616,7 @@ def bench_cache(args, cfg, torch, tsa, W):
     res["miss_rate_steady"] = float(m[args.warmup:].double().mean() / k)
     fetched = m[args.warmup:].double().sum(dim=1) * Hkv * d * 2 * 2  # K and V rows per miss
     res["fetched_bytes"] = float(fetched.sum())
+    res["counter_bytes"] = {"resolve": [float(x) for x in fetched]}
     r_ms = [rev[i][0].elapsed_time(rev[i][1]) for i in range(args.warmup, steps)]
     # steady state: steps after the first (step 0 misses every slot)
     first = 1 if args.warmup == 0 else 0
@@ -445,29 +634,34 @@ def bench_cache(args, cfg, torch, tsa, W):
         "frac_of_h2d": round(fetch_gbps / h2d, 4) if fetch_gbps else None,
         "timing": "torch events around each resolve launch on the call's stream",
     }
+    if args.cpu_seconds > 0:
+        res["cpu_sample"] = ("cache",) + cpu_sample_cache(cfg, hk.tensor, hv.tensor, q, trace, min(steps, 64), torch)
     return res
 
 
-def _timed(args, call, torch, tsa, n_distinct, offset=0):
+def _timed(args, call, torch, tsa, n_distinct, offset=0, kernels=("gather",)):
     """Warm up, then time args.steps steps (step i runs call(i + offset)).
 
-    Eager (default): every step launches directly, with the library's
-    gather-timing events armed around its gather kernel, so the kernel is
-    timed inside the timed region. With --graph each distinct step
-    (i mod n_distinct) is captured once into a HIP graph and the timed loop
-    replays the graphs; event records captured in a graph do not bracket the
-    kernel, so the gather kernel is then timed by an eager pass over the same
-    steps after the timed region.
+    Eager (default): every step launches directly; on every event-stride-th
+    step the library records HIP events around the launches of `kernels`
+    (the gather-attention kernel, the token indexer scan) on the call's
+    stream, so those kernels are timed inside the timed region. With --graph
+    each distinct step (i mod n_distinct) is captured once into a HIP graph
+    and the timed loop replays the graphs; event records captured in a graph
+    do not bracket the kernels, so they are then timed by an eager pass over
+    the same steps after the timed region.
     """
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
+    which = {"gather": tsa.binding.TIMED_GATHER, "token_scan": tsa.binding.TIMED_TOKEN_SCAN}
 
-    def new_events(n):
-        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    def new_events():
+        return {kn: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for kn in kernels}
 
     def eager(i, ev):
-        tsa.time_next_gather(*ev)
+        for kn, (a, b) in ev.items():
+            tsa.time_next_launch(which[kn], a, b)
         call(i + offset)
 
     graphs = []
@@ -479,7 +673,7 @@ def _timed(args, call, torch, tsa, n_distinct, offset=0):
                 call(j + offset)
             graphs.append(g)
         torch.cuda.synchronize()
-    evs = new_events(args.steps)
+    evs = [new_events() for _ in range(args.steps)]
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -497,20 +691,41 @@ def _timed(args, call, torch, tsa, n_distinct, offset=0):
     t_stop.record()
     torch.cuda.synchronize()
     res = {"ms_total": t_start.elapsed_time(t_stop), "wall_s": time.perf_counter() - wall0,
-           "kernel_timing": f"events around the gather launch of every {stride}-th step inside the timed region"}
+           "kernel_timing": f"HIP events recorded by the library around the kernel's launch on every "
+                            f"{stride}-th step inside the timed region"}
     if not graphs:
         evs = [evs[i] for i in timed]
     else:
         timed = list(range(min(args.steps, n_distinct)))
-    if graphs:
-        for i in range(min(args.steps, n_distinct)):
+        for i in timed:
             eager(i, evs[i])
         evs = evs[:len(timed)]
         torch.cuda.synchronize()
-        res["kernel_timing"] = "events around each gather launch in an eager pass after the timed graph region"
-    res["gather_ms"] = [a.elapsed_time(b) for a, b in evs]
+        res["kernel_timing"] = "HIP events around each launch in an eager pass after the timed graph region"
+    res["kernel_ms"] = {kn: [ev[kn][0].elapsed_time(ev[kn][1]) for ev in evs] for kn in kernels}
+    res["gather_ms"] = res["kernel_ms"]["gather"]
     res["timed_steps"] = timed
     return res
+
+
+def measure_stream_read_gbps(torch, tsa, nbytes=8 << 30):
+    """Measured HBM read ceiling: the library's streaming-read probe (16-byte
+    non-temporal loads over every CU) over an 8 GiB buffer, best of 5."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = tsa.stream_read(buf)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        tsa.stream_read(buf, sink)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e)
+        best = ms if best is None else min(best, ms)
+    del buf
+    torch.cuda.empty_cache()
+    return nbytes / (best / 1e3) / 1e9
 
 
 # ----------------------------------------------------------------------------
@@ -567,12 +782,139 @@ def calibrate_copy(torch):
                       "gbps_read_plus_write": 2 * n / ms / 1e6}))
 
 
+def _mean(xs):
+    xs = list(xs)
+    return sum(xs) / len(xs)
+
+
+def kernel_rooflines(res, cfg, args, workload):
+    """Per timed kernel: algorithmic bytes per launch (of exactly the launches
+    that were timed) over the mean event-timed launch duration."""
+    out = {}
+    for kn, ms in res["kernel_ms"].items():
+        step_bytes = res["step_bytes"] if kn == "gather" else res["kernel_step_bytes"][kn]
+        name = gather_kernel_name(cfg, args) if kn == "gather" else KERNEL_NAMES[kn]
+        bpl = _mean(step_bytes[i] for i in res["timed_steps"])
+        mean_ms = _mean(ms)
+        achieved = bpl / (mean_ms / 1e3) / 1e9
+        traffic = measured_traffic(workload, name)
+        out[name] = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_over_algorithmic": round(traffic / bpl, 4) if traffic else None,
+                     "algorithmic_bytes_per_launch": round(bpl), "mean_launch_us": round(mean_ms * 1e3, 2),
+                     "launches_timed": len(ms), "timing": res["kernel_timing"]}
+    return out
+
+
+def counter_kernels(res, cfg, args):
+    """Mean algorithmic bytes per launch over every timed step, for each kernel
+    a counter pass attributes bytes to (with --warmup 0 these are all of the
+    run's launches of that kernel)."""
+    out = {gather_kernel_name(cfg, args): _mean(res["step_bytes"])}
+    for kn, sb in res.get("kernel_step_bytes", {}).items():
+        out[KERNEL_NAMES[kn]] = _mean(sb)
+    for kn, sb in res.get("counter_bytes", {}).items():
+        out[KERNEL_NAMES[kn]] = _mean(sb)
+    return out
+
+
+def _counter_kib(csv_path, kernel):
+    """Mean Counter_Value (KiB) per dispatch of `kernel` in a rocprofv3 counter
+    collection CSV, and the number of dispatches."""
+    import csv
+    import re
+    pat = re.compile(rf"(^|[^A-Za-z0-9_]){re.escape(kernel)}([^A-Za-z0-9_]|$)")
+    vals = []
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if pat.search(row["Kernel_Name"]):
+                vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"bench: no dispatch of {kernel} in {csv_path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def record_traffic(args):
+    """Builds HBM bytes per launch of this workload's kernels from four
+    rocprofv3 counter passes under DIR and merges them into the committed
+    traffic record:
+
+        DIR/c<N>_FETCH_SIZE/, DIR/c<N>_WRITE_SIZE/   bench.py --config N --steps K --warmup 0 --cpu-seconds 0
+                                                      under rocprofv3 --pmc FETCH_SIZE (WRITE_SIZE)
+        DIR/copy_FETCH_SIZE/, DIR/copy_WRITE_SIZE/   bench.py --calibrate-copy under the same passes
+        DIR/c<N>_FETCH_SIZE.log                      the bench run's stdout (its JSON line)
+
+    each pass written with `--output-format csv -o run`. The counters of a
+    plain 1 GiB copy (1 GiB read, 1 GiB written) give the scale from counter
+    units to bytes."""
+    d, n = args.record_traffic, args.config
+    with open(os.path.join(d, f"c{n}_FETCH_SIZE.log")) as f:
+        line = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    if line["warmup"] != 0:
+        raise SystemExit("bench: counter passes must run with --warmup 0 (every dispatch a timed step)")
+    csv_of = {c: os.path.join(d, f"c{n}_{c}", "run_counter_collection.csv") for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    copy_kib = {c: _counter_kib(os.path.join(d, f"copy_{c}", "run_counter_collection.csv"),
+                                "__amd_rocclr_copyBuffer")[0] for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    scale = {c: (1 << 30) / (copy_kib[c] * 1024) for c in copy_kib}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    workload = line["config"]["workload"]
+    bench_cmd = f"python -u bench.py --config {n} --steps {line['steps']} --warmup 0 --cpu-seconds 0"
+    for kernel, alg in line["counter_kernels"].items():
+        fetch, nf = _counter_kib(csv_of["FETCH_SIZE"], kernel)
+        write, nw = _counter_kib(csv_of["WRITE_SIZE"], kernel)
+        hbm = fetch * 1024 * scale["FETCH_SIZE"] + write * 1024 * scale["WRITE_SIZE"]
+        rec[f"{workload}/{kernel}"] = {
+            "kernel_source_sha": line["kernel_source_sha"],
+            "dispatches": [nf, nw],
+            "fetch_size_kib_per_dispatch": round(fetch, 1), "write_size_kib_per_dispatch": round(write, 1),
+            "fetch_scale_from_copy": round(scale["FETCH_SIZE"], 5),
+            "write_scale_from_copy": round(scale["WRITE_SIZE"], 5),
+            "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": round(alg),
+            "traffic_over_algorithmic": round(hbm / alg, 4) if alg else None,
+            "commands": [f"rocprofv3 --pmc {c} --output-format csv -d {d}/c{n}_{c} -o run -- {bench_cmd}"
+                         for c in ("FETCH_SIZE", "WRITE_SIZE")] +
+                        [f"rocprofv3 --pmc {c} --output-format csv -d {d}/copy_{c} -o run -- "
+                         "python -u bench.py --calibrate-copy" for c in ("FETCH_SIZE", "WRITE_SIZE")],
+        }
+        log(f"{workload}/{kernel}: {hbm / 1e6:.1f} MB per launch, {hbm / alg:.3f}x algorithmic")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
+def workload_name(cfg, args):
+    workload = cfg.name + (f"+grow-from-{args.grow}" if args.grow else "")
+    if cfg.kind == "ivf":
+        if args.similarity != "dot":
+            workload += f"+{args.similarity}"
+        if args.sink or args.window:
+            workload += f"+sink{args.sink}+window{args.window}"
+        if args.assign == 2:
+            workload += "+two-lists-per-key"
+    if cfg.kind == "cache" and (cfg.popularity_sd or cfg.recency):
+        workload += f"+popularity{cfg.popularity_sd:g}+recency{cfg.recency:g}"
+    if cfg.kind == "cache" and args.policy != "lru":
+        workload += f"+{args.policy}"
+    if cfg.kind == "cache" and args.layers > 1:
+        workload = f"hier-cache-{max(1, cfg.batch // args.layers)}x128k-{args.layers}layers"
+    return workload
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported by this build "
               "(across GPUs the decode path would shard by request, one batch slice per GPU)", file=sys.stderr)
         sys.exit(2)
+    if args.record_traffic:
+        record_traffic(args)
+        return
+    # the oracle's worker processes start before anything touches the GPU
+    pool = start_cpu_pool(host_cores()) if args.cpu_seconds > 0 and not args.calibrate_copy else None
     import torch
 
     if args.calibrate_copy:
@@ -594,27 +936,25 @@ def main():
     ms_step = res["ms_total"] / K
     value = res["queries"] / (res["ms_total"] / 1e3)
     gb_s = res["gathered_bytes"] / (res["ms_total"] / 1e3) / 1e9
-    g_ms = res["gather_ms"]
-    g_mean_ms = sum(g_ms) / len(g_ms)
-    # algorithmic bytes of exactly the launches that were timed
-    bytes_per_launch = sum(res["step_bytes"][i] for i in res["timed_steps"]) / len(res["timed_steps"])
-    achieved = bytes_per_launch / (g_mean_ms / 1e3) / 1e9
-    workload = cfg.name + (f"+grow-from-{args.grow}" if args.grow else "")
-    if cfg.kind == "ivf":
-        if args.similarity != "dot":
-            workload += f"+{args.similarity}"
-        if args.sink or args.window:
-            workload += f"+sink{args.sink}+window{args.window}"
-        if args.assign == 2:
-            workload += "+two-lists-per-key"
-    if cfg.kind == "cache" and (cfg.popularity_sd or cfg.recency):
-        workload += f"+popularity{cfg.popularity_sd:g}+recency{cfg.recency:g}"
-    if cfg.kind == "cache" and args.policy != "lru":
-        workload += f"+{args.policy}"
-    if cfg.kind == "cache" and args.layers > 1:
-        workload = f"hier-cache-{max(1, cfg.batch // args.layers)}x128k-{args.layers}layers"
-    traffic = measured_traffic(workload)
+    workload = workload_name(cfg, args)
+    kernels = kernel_rooflines(res, cfg, args, workload)
+    dominant = max(kernels.values(), key=lambda r: r["mean_launch_us"])
+    read_gbps = measure_stream_read_gbps(torch, tsa)
     copy_gbps = measure_copy_gbps(torch)
+    for r in kernels.values():
+        r["measured_read_ceiling_gbps"] = round(read_gbps, 1)
+        r["frac_of_measured_read_ceiling"] = round(r["achieved"] / read_gbps, 4)
+    roofline = dict(dominant)
+    roofline["torch_d2d_copy_gbps"] = round(copy_gbps, 1)
+    roofline["read_ceiling"] = ("the library's streaming-read probe: 16-byte non-temporal loads over every CU, "
+                                "one pass over an 8 GiB buffer, best of 5")
+    cpu = None
+    if "cpu_sample" in res:
+        kind_s, data_dir, what = res["cpu_sample"]
+        log(f"oracle baseline: {what}")
+        cpu = cpu_baseline(args, kind_s, data_dir, what, pool)
+    if pool is not None:
+        pool.terminate()
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -636,13 +976,11 @@ def main():
         "gathered_kv_gbps": round(gb_s, 1),
         "gathered_kv_frac_of_peak": round(gb_s / HBM_PEAK_GBPS, 4),
         "graph": bool(args.graph),
-        "roofline": {"bound": "hbm", "kernel": gather_kernel_name(cfg, args), "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": round(bytes_per_launch),
-                     "mean_launch_us": round(g_mean_ms * 1e3, 2), "timing": res["kernel_timing"],
-                     "torch_d2d_copy_gbps": round(copy_gbps, 1),
-                     "ratio_to_torch_copy": round(achieved / copy_gbps, 4)},
-        "cpu_baseline": res.get("cpu"),
+        "roofline": roofline,
+        "other_kernels": [r for r in kernels.values() if r is not dominant],
+        "cpu_baseline": cpu,
+        "kernel_source_sha": kernel_source_sha(),
+        "counter_kernels": counter_kernels(res, cfg, args),
     }
     for key in ("index_build_ms", "unique_rows_per_step", "misses_per_step", "miss_rate_steady",
                 "fetched_bytes", "resolve", "append", "layer_group", "indexer_bytes_per_step"):

@@ -498,6 +498,20 @@ tsa_status tsa_host_free(void* host_ptr);
  * gather-attention kernel launched by this thread. One-shot. */
 tsa_status tsa_time_next_gather(void* ev_start, void* ev_stop);
 
+/* The same for a chosen kernel: TSA_TIMED_GATHER (the gather-attention
+ * kernel, as tsa_time_next_gather) or TSA_TIMED_TOKEN_SCAN (the indexer scan
+ * of the next tsa_token_decode). One-shot per kernel. */
+enum { TSA_TIMED_GATHER = 0, TSA_TIMED_TOKEN_SCAN = 1 };
+tsa_status tsa_time_next_launch(int32_t kernel, void* ev_start, void* ev_stop);
+
+/* Measurement probe (not part of the decode path): reads `bytes` (a
+ * multiple of 16) at device address p once with 16-byte non-temporal loads
+ * over every CU, writing one word per wave to sink (device, at least
+ * tsa_stream_read_sink_bytes() bytes). Timed by the caller, it gives a
+ * measured HBM streaming-read ceiling for the device. */
+tsa_status tsa_stream_read(const void* p, size_t bytes, uint32_t* sink, size_t sink_bytes, void* stream);
+size_t tsa_stream_read_sink_bytes(void);
+
 const char* tsa_status_str(tsa_status s);
 const char* tsa_last_error(void);
 int32_t tsa_abi_version(void);

@@ -27,6 +27,8 @@ from .binding import (  # noqa: F401
     sparse_decode_ex,
     sparse_decode_noalloc,
     time_next_gather,
+    time_next_launch,
+    stream_read,
     token_decode,
     workspace_bytes,
 )
@@ -34,6 +36,6 @@ from .binding import (  # noqa: F401
 __all__ = [
     "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "index_build_multi", "kv_append", "sparse_decode",
     "sparse_decode_dyn", "sparse_decode_ex", "sparse_decode_noalloc", "token_decode",
-    "attend_rows", "resolve", "cache_reset", "fetch_rows", "hier_group_step", "HostArray", "time_next_gather", "workspace_bytes",
+    "attend_rows", "resolve", "cache_reset", "fetch_rows", "hier_group_step", "HostArray", "time_next_gather", "time_next_launch", "stream_read", "workspace_bytes",
     "TsaError",
 ]

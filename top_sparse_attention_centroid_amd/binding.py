@@ -81,6 +81,8 @@ _SIGNATURES = {
     "tsa_host_alloc": [ctypes.c_size_t, ctypes.POINTER(_P)],
     "tsa_host_free": [_P],
     "tsa_time_next_gather": [_P, _P],
+    "tsa_time_next_launch": [_I32, _P, _P],
+    "tsa_stream_read": [_P, ctypes.c_size_t, _P, ctypes.c_size_t, _P],
 }
 
 _lib = None
@@ -109,6 +111,8 @@ def load() -> ctypes.CDLL:
     lib.tsa_last_error.restype = ctypes.c_char_p
     lib.tsa_abi_version.argtypes = []
     lib.tsa_abi_version.restype = _I32
+    lib.tsa_stream_read_sink_bytes.argtypes = []
+    lib.tsa_stream_read_sink_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -603,6 +607,32 @@ def time_next_gather(ev_start: torch.cuda.Event, ev_stop: torch.cuda.Event):
         if not ev.cuda_event:  # torch creates the HIP event on its first record
             ev.record()
     _check(load().tsa_time_next_gather(_P(ev_start.cuda_event), _P(ev_stop.cuda_event)))
+
+
+TIMED_GATHER, TIMED_TOKEN_SCAN = 0, 1
+
+
+def time_next_launch(kernel: int, ev_start: torch.cuda.Event, ev_stop: torch.cuda.Event):
+    """Have the next launch of `kernel` (TIMED_GATHER or TIMED_TOKEN_SCAN) by
+    this thread record the two events around itself (on that call's stream)."""
+    for ev in (ev_start, ev_stop):
+        if not ev.cuda_event:
+            ev.record()
+    _check(load().tsa_time_next_launch(kernel, _P(ev_start.cuda_event), _P(ev_stop.cuda_event)))
+
+
+def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Measurement probe: read every byte of the device tensor `buf` once with
+    non-temporal 16-byte loads (no decode work). Returns the sink words."""
+    _dev(buf, "buf")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    need = load().tsa_stream_read_sink_bytes()
+    if sink is None:
+        sink = torch.empty(need // 4, dtype=torch.int32, device=buf.device)
+    _check(load().tsa_stream_read(_ptr(buf), nbytes, _ptr(sink), sink.numel() * 4, _stream(stream)))
+    return sink
 
 
 def abi_version() -> int:

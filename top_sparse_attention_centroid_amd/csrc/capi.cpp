@@ -20,6 +20,8 @@ namespace {
 thread_local std::string g_last_error;
 thread_local hipEvent_t g_gather_ev0 = nullptr;
 thread_local hipEvent_t g_gather_ev1 = nullptr;
+thread_local hipEvent_t g_scan_ev0 = nullptr;   // token indexer scan (tsa_time_next_launch)
+thread_local hipEvent_t g_scan_ev1 = nullptr;
 
 tsa_status fail(tsa_status s, const char* fmt, ...) {
   char buf[512];
@@ -578,6 +580,9 @@ tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const
                        reinterpret_cast<int32_t*>(w + L.hist), reinterpret_cast<uint32_t*>(w + L.cand_key),
                        reinterpret_cast<int32_t*>(w + L.cand_id), reinterpret_cast<int32_t*>(w + L.cand_cnt),
                        sel, d.batch, d.n_tokens, k, L.nfchunk};
+  tp.score_ev0 = g_scan_ev0;
+  tp.score_ev1 = g_scan_ev1;
+  g_scan_ev0 = g_scan_ev1 = nullptr;
   hipError_t e = launch_token_select(tp, d.dtype, s);
   if (e != hipSuccess) return hip_fail(e, "token_select launch");
 
@@ -828,11 +833,38 @@ tsa_status tsa_sparse_decode_noalloc(const tsa_ivf_desc* desc, const void* q, co
 }
 
 tsa_status tsa_time_next_gather(void* ev_start, void* ev_stop) {
+  return tsa_time_next_launch(TSA_TIMED_GATHER, ev_start, ev_stop);
+}
+
+tsa_status tsa_time_next_launch(int32_t kernel, void* ev_start, void* ev_stop) {
   if ((ev_start == nullptr) != (ev_stop == nullptr))
     return fail(TSA_ERR_INVALID_ARG, "give both events or neither");
-  g_gather_ev0 = static_cast<hipEvent_t>(ev_start);
-  g_gather_ev1 = static_cast<hipEvent_t>(ev_stop);
+  switch (kernel) {
+    case TSA_TIMED_GATHER:
+      g_gather_ev0 = static_cast<hipEvent_t>(ev_start);
+      g_gather_ev1 = static_cast<hipEvent_t>(ev_stop);
+      return ok();
+    case TSA_TIMED_TOKEN_SCAN:
+      g_scan_ev0 = static_cast<hipEvent_t>(ev_start);
+      g_scan_ev1 = static_cast<hipEvent_t>(ev_stop);
+      return ok();
+  }
+  return fail(TSA_ERR_INVALID_ARG, "unknown timed kernel %d", kernel);
+}
+
+tsa_status tsa_stream_read(const void* p, size_t bytes, uint32_t* sink, size_t sink_bytes, void* stream) {
+  REQUIRE_PTR(p); REQUIRE_PTR(sink);
+  REQUIRE_ALIGN(p, 16); REQUIRE_ALIGN(sink, 4);
+  if (bytes == 0 || bytes % 16) return fail(TSA_ERR_INVALID_ARG, "bytes %zu is not a positive multiple of 16", bytes);
+  const size_t need = tsa_stream_read_sink_bytes();
+  if (sink_bytes < need) return fail(TSA_ERR_WORKSPACE, "sink %zu < %zu bytes", sink_bytes, need);
+  hipError_t e = launch_stream_read(p, static_cast<long long>(bytes / 16), sink, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream_read launch");
   return ok();
+}
+
+size_t tsa_stream_read_sink_bytes(void) {
+  return static_cast<size_t>(stream_read_blocks()) * (512 / 64) * sizeof(uint32_t);
 }
 
 }  // extern "C"

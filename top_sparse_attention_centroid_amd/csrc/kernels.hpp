@@ -152,6 +152,7 @@ struct TokenSelectParams {
   int32_t* cand_cnt;       // [B][nfchunk]
   int32_t* sel;            // [B][k]
   int B, N, k, nfchunk;
+  hipEvent_t score_ev0 = nullptr, score_ev1 = nullptr;  // recorded around the scan launch when set
 };
 hipError_t launch_token_select(const TokenSelectParams& p, int dtype, hipStream_t s);
 
@@ -199,5 +200,9 @@ hipError_t launch_fetch_rows(const FetchParams& p, hipStream_t s);
 constexpr int kEvictLru = 0, kEvictFifo = 1, kEvictRandom = 2, kEvictPriority = 3;
 
 hipError_t launch_fill_i32(int32_t* p, long long n, int32_t value, hipStream_t s);
+
+// ---------------------------------------------------------------- probe
+int stream_read_blocks();
+hipError_t launch_stream_read(const void* p, long long n16, uint32_t* sink, hipStream_t s);
 
 }  // namespace tsa

@@ -310,9 +310,11 @@ static hipError_t token_select_typed(const TokenSelectParams& p, hipStream_t s) 
   hipError_t e = launch_fill_i32(p.hist, static_cast<long long>(p.B) * kTokHistBins, 0, s);
   if (e != hipSuccess) return e;
   const int nscore = (p.N + kTokScoreTile - 1) / kTokScoreTile;
+  if (p.score_ev0 && (e = hipEventRecord(p.score_ev0, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(token_score_kernel<T>, dim3(nscore, p.B), dim3(kScoreThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.score_ev1 && (e = hipEventRecord(p.score_ev1, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(token_filter_kernel, dim3(p.nfchunk, p.B), dim3(kFilterThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
