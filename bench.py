@@ -78,6 +78,7 @@ def parse():
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--gpu-phase", metavar="FILE", help=argparse.SUPPRESS)
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="write the HBM-traffic record of this workload's kernels from rocprofv3 FETCH_SIZE / "
                          "WRITE_SIZE passes under DIR (see record_traffic) and exit; no GPU work")
@@ -239,7 +240,9 @@ def bench_ivf(args, cfg, torch, tsa, W):
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload, on one
 # core and on all the host cores this process may use (one process per core,
-# one BLAS thread each, started before the GPU is touched)
+# one BLAS thread each). It runs in the parent process after the GPU run (a
+# child process) has ended: worker processes alive during the timed GPU
+# region were measured to slow the host's launches several times over.
 # ----------------------------------------------------------------------------
 
 CPU_SAMPLE_REQUESTS = 2      # requests of the sample (queries cycle over them and the steps)
@@ -272,10 +275,8 @@ def _worker_ready(_):
 
 
 def start_cpu_pool(n):
-    """Worker processes for the all-cores leg, spawned before this process
-    initialises the GPU (nothing is forked from a process holding it), and
-    waited for until every one has started, so that their start-up does not
-    compete with the timed GPU region for the host's cores."""
+    """Worker processes for the all-cores leg, waited for until every one has
+    started (the process that starts them never touches the GPU)."""
     import multiprocessing as mp
     pool = mp.get_context("spawn").Pool(n)
     for _ in range(20):
@@ -913,13 +914,47 @@ def main():
     if args.record_traffic:
         record_traffic(args)
         return
-    # the oracle's worker processes start before anything touches the GPU
-    pool = start_cpu_pool(host_cores()) if args.cpu_seconds > 0 and not args.calibrate_copy else None
+    if args.cpu_seconds > 0 and not args.calibrate_copy and not args.gpu_phase:
+        # the GPU run in a child process; this process, which never touches
+        # the GPU, then times the oracle on the sample the child wrote
+        import subprocess
+        import tempfile
+        fd, path = tempfile.mkstemp(prefix="tsa_bench_", suffix=".json", dir="/tmp")
+        os.close(fd)
+        try:
+            rc = subprocess.run([sys.executable, os.path.abspath(__file__), *sys.argv[1:], "--gpu-phase", path]).returncode
+            if rc != 0:
+                sys.exit(rc)
+            with open(path) as f:
+                line = json.load(f)
+        finally:
+            os.unlink(path)
+        sample = line.pop("cpu_sample", None)
+        if sample:
+            kind_s, data_dir, what = sample
+            log(f"oracle baseline: {what}")
+            pool = start_cpu_pool(host_cores())
+            try:
+                line["cpu_baseline"] = cpu_baseline(args, kind_s, data_dir, what, pool)
+            finally:
+                pool.terminate()
+        print(json.dumps(line), flush=True)
+        return
     import torch
 
     if args.calibrate_copy:
         calibrate_copy(torch)
         return
+    line = gpu_run(args, torch)
+    if args.gpu_phase:
+        with open(args.gpu_phase, "w") as f:
+            json.dump(line, f)
+    else:
+        line.pop("cpu_sample", None)
+        print(json.dumps(line), flush=True)
+
+
+def gpu_run(args, torch):
     import top_sparse_attention_centroid_amd as tsa
     from top_sparse_attention_centroid_amd import workloads as W
 
@@ -948,13 +983,6 @@ def main():
     roofline["torch_d2d_copy_gbps"] = round(copy_gbps, 1)
     roofline["read_ceiling"] = ("the library's streaming-read probe: 16-byte non-temporal loads over every CU, "
                                 "one pass over an 8 GiB buffer, best of 5")
-    cpu = None
-    if "cpu_sample" in res:
-        kind_s, data_dir, what = res["cpu_sample"]
-        log(f"oracle baseline: {what}")
-        cpu = cpu_baseline(args, kind_s, data_dir, what, pool)
-    if pool is not None:
-        pool.terminate()
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -978,7 +1006,7 @@ def main():
         "graph": bool(args.graph),
         "roofline": roofline,
         "other_kernels": [r for r in kernels.values() if r is not dominant],
-        "cpu_baseline": cpu,
+        "cpu_baseline": None,
         "kernel_source_sha": kernel_source_sha(),
         "counter_kernels": counter_kernels(res, cfg, args),
     }
@@ -986,7 +1014,9 @@ def main():
                 "fetched_bytes", "resolve", "append", "layer_group", "indexer_bytes_per_step"):
         if key in res:
             line[key] = res[key]
-    print(json.dumps(line), flush=True)
+    if "cpu_sample" in res:
+        line["cpu_sample"] = list(res["cpu_sample"])
+    return line
 
 
 if __name__ == "__main__":

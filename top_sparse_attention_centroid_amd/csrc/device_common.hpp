@@ -177,18 +177,27 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Inclusive prefix sum over the wave through DPP: shifts of 1, 2, 4 and 8
+// lanes within each 16-lane row, then the row totals carried across rows
+// (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3). Lanes
+// whose source lies outside the row read 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over a block of NW waves. `scratch` holds NW ints.
 // Returns the caller's exclusive prefix; *total receives the block total.
 template <int NW>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == kWave - 1) scratch[wave] = x;
   __syncthreads();
   int before = 0, all = 0;
@@ -210,14 +219,8 @@ __device__ __forceinline__ int block_exclusive_scan_and_sum(int v, int u, int* s
                                                             int* total_u) {
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) u += __shfl_xor(u, o);
+  const int x = wave_inclusive_scan(v);
+  u = wave_sum_i(u);
   if (lane == kWave - 1) {
     scratch[wave] = x;
     scratch[NW + wave] = u;
@@ -250,16 +253,8 @@ __device__ __forceinline__ void block_class_scan(const int (&cnt)[NC], int (&pos
   const int wave = threadIdx.x / kWave;
   int x[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    x[c] = cnt[c];
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(x[c], o);
-      if (lane >= o) x[c] += y;
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) u += __shfl_xor(u, o);
+  for (int c = 0; c < NC; ++c) x[c] = wave_inclusive_scan(cnt[c]);
+  u = wave_sum_i(u);
   if (lane == kWave - 1) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) scratch[wave * (NC + 1) + c] = x[c];

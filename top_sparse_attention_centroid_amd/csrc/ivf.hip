@@ -492,7 +492,7 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 
 // ============================================================================
 // Centroid scoring, top-k lists per query head, and the gather plan of the
-// KV group, fused in one workgroup (4 waves) per (request, KV head).
+// KV group, fused in one workgroup (kSelWaves waves) per (request, KV head).
 //
 // Scoring ([KARAT] worked example, step 3): s[h][c] = q[h] . centroid[g][c],
 // raw dot product with fp32 accumulation. bf16 data runs it on matrix cores
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 // list offsets.
 //
 // Top-k ([KARAT] How: the top-k most similar lists): wave w owns query heads
-// w, w + 4 of the group and holds that head's keys in registers, KPL per lane
+// w, w + NW of the group and holds that head's keys in registers, KPL per lane
 // (C <= 64 * KPL). The k-th largest key T is found bit by bit (MSB first)
 // with ballot counts, over a short candidate list when one suffices (see the
 // kernel); keys above it are taken, then keys equal to it in ascending list
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 // column add theirs).
 constexpr int kSelTiles = 8;
 
-template <int G>
+template <int G, int TILES = kSelTiles>
 __device__ __forceinline__ void score_tiles_mfma(const SelectParams& p, int b, int g, int t_begin, int t_end,
                                                  uint32_t* keys) {
   const int C = p.C;
@@ -537,10 +537,10 @@ __device__ __forceinline__ void score_tiles_mfma(const SelectParams& p, int b, i
   for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8_t*>(qr + ks * 32);
   const bf16_t* cb = static_cast<const bf16_t*>(p.centroids) + b * p.cent_bstride +
                      static_cast<long long>(g) * C * kHeadDim + grp * 8;
-  for (int t0 = t_begin; t0 < t_end; t0 += kSelTiles) {
-    bf16x8_t bt[kSelTiles][4];
+  for (int t0 = t_begin; t0 < t_end; t0 += TILES) {
+    bf16x8_t bt[TILES][4];
 #pragma unroll
-    for (int u = 0; u < kSelTiles; ++u) {
+    for (int u = 0; u < TILES; ++u) {
       if (t0 + u < t_end) {
         const bf16_t* row = cb + static_cast<long long>(min((t0 + u) * 16 + col, C - 1)) * kHeadDim;
 #pragma unroll
@@ -548,7 +548,7 @@ __device__ __forceinline__ void score_tiles_mfma(const SelectParams& p, int b, i
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSelTiles; ++u) {
+    for (int u = 0; u < TILES; ++u) {
       if (t0 + u >= t_end) break;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -589,53 +589,59 @@ __global__ __launch_bounds__(256) void centroid_score_kernel(SelectParams p) {
   score_tiles_mfma<G>(p, b, g, t, t + 1, p.keys + static_cast<long long>(bg) * G * p.C);
 }
 
-template <typename T, int G, int KPL>
-__global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
+template <typename T, int G, int KPL, int NW>
+__global__ __launch_bounds__(NW * kWave) void ivf_select_kernel(SelectParams p) {
+  constexpr int NT = NW * kWave;
   extern __shared__ uint32_t smem[];
   const int C = p.C, k = p.k;
   uint32_t* keys = smem;                              // [G][C]
   uint32_t* lmask = smem + G * C;                     // [C]
   int* loff = reinterpret_cast<int*>(smem + (G + 1) * C);  // [C+1], clamped to [0, N]
-  __shared__ int class_scratch[4 * (G + 2)];
-  __shared__ uint32_t cand_lds[4][kWave];
-  __shared__ int cand_list_lds[4][kWave];
+  int* llen = loff + C + 1;                           // [C] valid entries per list (p.lens_lds only)
+  __shared__ int class_scratch[NW * (G + 2)];
+  __shared__ uint32_t cand_lds[NW][kWave];
+  __shared__ int cand_list_lds[NW][kWave];
   const int bg = blockIdx.x;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int r = lane >> 4, e = lane & 15;
 
+  // Every global read the selection waits on is requested before the first
+  // wait: the list offsets into registers (clamped addresses, straight-line
+  // loads), then the scores' operands (or the scores themselves); the
+  // offsets reach LDS after the scoring.
   const int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
   const int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * C : nullptr;
-  for (int c = tid; c <= C; c += 256) loff[c] = min(max(off[c], 0), p.n_entries);
-  for (int c = tid; c < C; c += 256) lmask[c] = 0u;
+  constexpr int kOffPer = (KPL * kWave + NT) / NT;  // C + 1 <= 64 * KPL + 1 offsets
+  int offv[kOffPer], lenv[kOffPer];
+  // a dynamic index's list lengths are staged in LDS beside the offsets when
+  // they fit in the 64 KiB of dynamic LDS, else read where used
+  const bool lens_lds = lens && p.lens_lds;
+#pragma unroll
+  for (int i = 0; i < kOffPer; ++i) offv[i] = off[min(tid + i * NT, C)];
+  if (lens_lds) {
+#pragma unroll
+    for (int i = 0; i < kOffPer; ++i) lenv[i] = lens[min(tid + i * NT, C - 1)];
+  }
+  for (int c = tid; c < C; c += NT) lmask[c] = 0u;
   if (p.keys) {  // scored by centroid_score_kernel: staged beside the offsets, 16 loads in flight
     const uint32_t* kg = p.keys + static_cast<long long>(bg) * G * C;
-    for (int i0 = 0; i0 < G * C; i0 += 16 * 256) {
+    for (int i0 = 0; i0 < G * C; i0 += 16 * NT) {
       uint32_t v[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int i = i0 + u * 256 + tid;
+        const int i = i0 + u * NT + tid;
         v[u] = i < G * C ? kg[i] : 0u;
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int i = i0 + u * 256 + tid;
+        const int i = i0 + u * NT + tid;
         if (i < G * C) keys[i] = v[u];
       }
     }
-  }
-  __syncthreads();
-  // rows of list c: its whole range, or (dynamic index) the valid front part
-  auto list_len = [&](int c) {
-    const int range = max(loff[c + 1] - loff[c], 0);
-    return lens ? min(max(lens[c], 0), range) : range;
-  };
-
-  if (p.keys) {
-    // scored by centroid_score_kernel
   } else if constexpr (std::is_same<T, bf16_t>::value) {
     const int ntile = (C + 15) / 16;
-    const int per_wave = (ntile + 3) / 4;
+    const int per_wave = (ntile + NW - 1) / NW;
     score_tiles_mfma<G>(p, b, g, wave * per_wave, min(ntile, (wave + 1) * per_wave), keys);
   } else {
     const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
@@ -645,16 +651,16 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
                   static_cast<long long>(g) * C * kHeadDim + e * 8;
     constexpr int U = 16;  // centroid rows in flight per lane group (64 per wave)
-    for (int c0 = wave * 4; c0 < C; c0 += 16 * U) {
+    for (int c0 = wave * 4; c0 < C; c0 += 4 * NW * U) {
       Raw8<T> raw[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = min(c0 + u * 16 + r, C - 1);  // clamped: straight-line loads
+        const int c = min(c0 + u * 4 * NW + r, C - 1);  // clamped: straight-line loads
         raw[u].load(cb + static_cast<long long>(c) * kHeadDim);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * 16 + r;
+        const int c = c0 + u * 4 * NW + r;
         float inv = 1.f;
         if (p.cosine) {  // cosine similarity: q.c / |c| (1/|q| ranks nothing differently)
           const float n2 = group16_sum(sq8(raw[u]));
@@ -668,9 +674,20 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
       }
     }
   }
+#pragma unroll
+  for (int i = 0; i < kOffPer; ++i) {
+    const int c = tid + i * NT;
+    if (c <= C) loff[c] = min(max(offv[i], 0), p.n_entries);
+    if (lens_lds && c < C) llen[c] = lenv[i];
+  }
   __syncthreads();
+  // rows of list c: its whole range, or (dynamic index) the valid front part
+  auto list_len = [&](int c) {
+    const int range = max(loff[c + 1] - loff[c], 0);
+    return lens ? min(max(lens_lds ? llen[c] : lens[c], 0), range) : range;
+  };
 
-  for (int h = wave; h < G; h += 4) {
+  for (int h = wave; h < G; h += NW) {
     const uint32_t* kh = keys + h * C;
     // lane holds keys c = j * 64 + lane (ascending c by j); 0 marks "no list"
     // and sits below every real key
@@ -783,42 +800,55 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
   }
   __syncthreads();
   if (p.lmask_out)  // the chosen lists' head masks, for the gather's duplicate test
-    for (int c = tid; c < C; c += 256) p.lmask_out[static_cast<long long>(bg) * C + c] = lmask[c];
+    for (int c = tid; c < C; c += NT) p.lmask_out[static_cast<long long>(bg) * C + c] = lmask[c];
 
-  // thread t plans lists [t * per, (t + 1) * per). For merged gather sets
-  // the segments are ordered by head class: the lists only head 0 chose,
-  // then those only head 1 chose, ..., then the lists several heads chose;
-  // within a class, list order. Consecutive segments then mostly share one
-  // head, so a gather workgroup that takes several of them merges their
-  // states into one per head. Otherwise they follow list order. One block
-  // scan of the per-thread counts (of every class) places them.
+  // Thread t plans lists [t * PER, (t + 1) * PER); their head masks,
+  // offsets and lengths come from LDS once, all PER together, into
+  // registers. For merged gather sets the segments are ordered by head
+  // class: the lists only head 0 chose, then those only head 1 chose, ...,
+  // then the lists several heads chose; within a class, list order.
+  // Consecutive segments then mostly share one head, so a gather workgroup
+  // that takes several of them merges their states into one per head.
+  // Otherwise they follow list order. One block scan of the per-thread
+  // counts (of every class) places them.
   int4* seg = p.seg + static_cast<long long>(bg) * p.smax;
-  const int sr = min(max(p.seg_rows, 1), kSegRows);
-  const int per = (C + 255) / 256;
-  const int c_lo = tid * per, c_hi = min(C, c_lo + per);
-  auto class_of = [&](uint32_t m) { return (m & (m - 1u)) == 0u ? static_cast<int>(__builtin_ctz(m)) : G; };
+  // plan segments are a power of two long (they halve from kSegRows)
+  const int sr_log = 31 - __builtin_clz(static_cast<uint32_t>(min(max(p.seg_rows, 1), kSegRows)));
+  const int sr = 1 << sr_log;
+  constexpr int PER = (KPL * kWave + NT - 1) / NT;  // C <= 64 * KPL lists over NT threads
+  const int c_lo = tid * PER;
+  uint32_t lm[PER];
+  int lst[PER], lln[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = min(c_lo + i, C - 1);
+    const uint32_t m = lmask[c];
+    const int len = list_len(c);
+    const bool use = c_lo + i < C && m != 0u && len > 0;
+    lm[i] = use ? m : 0u;
+    lln[i] = use ? len : 0;
+    lst[i] = loff[c];
+  }
   int carry, uniq_all;
   if (p.class_order) {
+    // class of a chosen list: its head if one head chose it, else G
+    auto class_of = [&](uint32_t m) { return (m & (m - 1u)) == 0u ? static_cast<int>(__builtin_ctz(m)) : G; };
     int cls_segs[G + 1], cls_pos[G + 1];
 #pragma unroll
-    for (int c = 0; c <= G; ++c) cls_segs[c] = 0;
+    for (int x = 0; x <= G; ++x) cls_segs[x] = 0;
     int uniq = 0;
-    for (int c = c_lo; c < c_hi; ++c) {
-      const uint32_t m = lmask[c];
-      const int len = list_len(c);
-      if (m != 0u && len > 0) {
-        const int cl = class_of(m), ns = (len + sr - 1) / sr;
 #pragma unroll
-        for (int x = 0; x <= G; ++x) cls_segs[x] += x == cl ? ns : 0;
-        uniq += len;
-      }
+    for (int i = 0; i < PER; ++i) {
+      const int cl = lm[i] ? class_of(lm[i]) : G, ns = (lln[i] + sr - 1) >> sr_log;
+#pragma unroll
+      for (int x = 0; x <= G; ++x) cls_segs[x] += x == cl ? ns : 0;
+      uniq += lln[i];
     }
-    block_class_scan<4, G + 1>(cls_segs, cls_pos, uniq, class_scratch, &carry, &uniq_all);
-    for (int c = c_lo; c < c_hi; ++c) {
-      const uint32_t m = lmask[c];
-      const int len = list_len(c);
-      if (m == 0u || len <= 0) continue;
-      const int start = loff[c], cl = class_of(m), ns = (len + sr - 1) / sr;
+    block_class_scan<NW, G + 1>(cls_segs, cls_pos, uniq, class_scratch, &carry, &uniq_all);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (lln[i] == 0) continue;
+      const int cl = class_of(lm[i]), ns = (lln[i] + sr - 1) >> sr_log;
       int pos = 0;
 #pragma unroll
       for (int x = 0; x <= G; ++x) {
@@ -828,26 +858,26 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
         }
       }
       for (int j = 0; j < ns; ++j, ++pos) {
-        if (pos < p.smax) seg[pos] = make_int4(start + j * sr, min(sr, len - j * sr), static_cast<int>(m), c);
+        if (pos < p.smax)
+          seg[pos] = make_int4(lst[i] + (j << sr_log), min(sr, lln[i] - (j << sr_log)), static_cast<int>(lm[i]),
+                               c_lo + i);
       }
     }
   } else {
     int my_segs = 0, uniq = 0;
-    for (int c = c_lo; c < c_hi; ++c) {
-      const int len = list_len(c);
-      if (lmask[c] != 0u && len > 0) {
-        my_segs += (len + sr - 1) / sr;
-        uniq += len;
-      }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      my_segs += (lln[i] + sr - 1) >> sr_log;
+      uniq += lln[i];
     }
-    int pos = block_exclusive_scan_and_sum<4>(my_segs, uniq, class_scratch, &carry, &uniq_all);
-    for (int c = c_lo; c < c_hi; ++c) {
-      const uint32_t m = lmask[c];
-      const int len = list_len(c);
-      if (m == 0u || len <= 0) continue;
-      const int start = loff[c];
-      for (int j = 0; j * sr < len; ++j, ++pos) {
-        if (pos < p.smax) seg[pos] = make_int4(start + j * sr, min(sr, len - j * sr), static_cast<int>(m), c);
+    int pos = block_exclusive_scan_and_sum<NW>(my_segs, uniq, class_scratch, &carry, &uniq_all);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ns = (lln[i] + sr - 1) >> sr_log;
+      for (int j = 0; j < ns; ++j, ++pos) {
+        if (pos < p.smax)
+          seg[pos] = make_int4(lst[i] + (j << sr_log), min(sr, lln[i] - (j << sr_log)), static_cast<int>(lm[i]),
+                               c_lo + i);
       }
     }
   }
@@ -859,11 +889,11 @@ __global__ __launch_bounds__(256) void ivf_select_kernel(SelectParams p) {
     const int L = p.lengths ? min(max(p.lengths[b], 0), p.N) : p.N;
     const int sink_hi = min(p.n_sink, L);
     const int win_lo = p.n_window > 0 ? max(L - p.n_window, sink_hi) : L;
-    const int nsink = (sink_hi + sr - 1) / sr;
-    const int nwin = (L - win_lo + sr - 1) / sr;
+    const int nsink = (sink_hi + sr - 1) >> sr_log;
+    const int nwin = (L - win_lo + sr - 1) >> sr_log;
     const int all = (1 << G) - 1;
-    for (int j = tid; j < nsink + nwin; j += 256) {
-      const int start = j < nsink ? j * sr : win_lo + (j - nsink) * sr;
+    for (int j = tid; j < nsink + nwin; j += NT) {
+      const int start = j < nsink ? j << sr_log : win_lo + ((j - nsink) << sr_log);
       const int cnt = min(sr, (j < nsink ? sink_hi : L) - start);
       if (carry + j < p.smax) seg[carry + j] = make_int4(start, cnt, all, -1);
     }
@@ -1022,23 +1052,23 @@ hipError_t launch_csr(const CsrParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int KPL>
+template <typename T, int KPL, int NW>
 static void select_dispatch_g(const SelectParams& p, int G, size_t lds, hipStream_t s) {
-  const dim3 grid(p.B * p.Hkv);
+  const dim3 grid(p.B * p.Hkv), block(NW * kWave);
   switch (G) {
-    case 1: hipLaunchKernelGGL((ivf_select_kernel<T, 1, KPL>), grid, dim3(256), lds, s, p); break;
-    case 2: hipLaunchKernelGGL((ivf_select_kernel<T, 2, KPL>), grid, dim3(256), lds, s, p); break;
-    case 4: hipLaunchKernelGGL((ivf_select_kernel<T, 4, KPL>), grid, dim3(256), lds, s, p); break;
-    default: hipLaunchKernelGGL((ivf_select_kernel<T, 8, KPL>), grid, dim3(256), lds, s, p); break;
+    case 1: hipLaunchKernelGGL((ivf_select_kernel<T, 1, KPL, NW>), grid, block, lds, s, p); break;
+    case 2: hipLaunchKernelGGL((ivf_select_kernel<T, 2, KPL, NW>), grid, block, lds, s, p); break;
+    case 4: hipLaunchKernelGGL((ivf_select_kernel<T, 4, KPL, NW>), grid, block, lds, s, p); break;
+    default: hipLaunchKernelGGL((ivf_select_kernel<T, 8, KPL, NW>), grid, block, lds, s, p); break;
   }
 }
 
 template <typename T>
 static void select_dispatch(const SelectParams& p, int G, size_t lds, hipStream_t s) {
-  if (p.C <= 64) select_dispatch_g<T, 1>(p, G, lds, s);
-  else if (p.C <= 256) select_dispatch_g<T, 4>(p, G, lds, s);
-  else if (p.C <= 1024) select_dispatch_g<T, 16>(p, G, lds, s);
-  else select_dispatch_g<T, kMaxCentroids / 64>(p, G, lds, s);
+  if (p.C <= 64) select_dispatch_g<T, 1, kSelWaves>(p, G, lds, s);
+  else if (p.C <= 256) select_dispatch_g<T, 4, kSelWaves>(p, G, lds, s);
+  else if (p.C <= 1024) select_dispatch_g<T, 16, kSelWaves>(p, G, lds, s);
+  else select_dispatch_g<T, kMaxCentroids / 64, kSelWaves>(p, G, lds, s);
 }
 
 template <int G>
@@ -1058,9 +1088,12 @@ hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t lds = (static_cast<size_t>(G + 1) * p.C + p.C + 1) * sizeof(uint32_t);
-  if (dtype == kBF16) select_dispatch<bf16_t>(p, G, lds, s);
-  else select_dispatch<float>(p, G, lds, s);
+  size_t lds = (static_cast<size_t>(G + 1) * p.C + p.C + 1) * sizeof(uint32_t);
+  SelectParams q = p;
+  q.lens_lds = p.lens && lds + p.C * sizeof(uint32_t) <= kSelectLdsBytes;
+  if (q.lens_lds) lds += p.C * sizeof(uint32_t);
+  if (dtype == kBF16) select_dispatch<bf16_t>(q, G, lds, s);
+  else select_dispatch<float>(q, G, lds, s);
   return hipGetLastError();
 }
 

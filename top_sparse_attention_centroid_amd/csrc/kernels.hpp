@@ -89,7 +89,10 @@ struct SelectParams {
   uint32_t* keys;          // [B*Hkv][G][C] order keys of the scores, computed by centroid_score_kernel
                            // (bf16 only), or null: the select kernel scores the centroids itself
   int class_order;         // 1: plan segments by head class (merged gather sets), 0: list order
+  int lens_lds = 0;        // set by the launcher: the list lengths fit in LDS beside the offsets
 };
+constexpr int kSelWaves = 4;               // waves per select workgroup
+constexpr size_t kSelectLdsBytes = 65536;  // dynamic LDS of a select workgroup (keys, masks, offsets, lengths)
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s);
 
 // ---------------------------------------------------------- KV + index append
