@@ -127,9 +127,10 @@ def test_nearest_centroids_brute_force_and_m1():
     assert a2[0].tolist() == [0, 1]
 
 
-def test_multi_assignment_lists_and_dedup_in_the_union():
+@pytest.mark.parametrize("m", [2, 3, 4])
+def test_multi_assignment_lists_and_dedup_in_the_union(m):
     rng = np.random.default_rng(9)
-    N, C, d, m = 300, 10, 8, 2
+    N, C, d = 300, 10, 8
     cent, K = _clustered(rng, N, C, d)
     V = rng.standard_normal((N, d))
     a, _ = variants.nearest_centroids(K, cent, m)
