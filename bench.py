@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--similarity", default="dot", choices=["dot", "cosine"],
                     help="inverted-index workloads: centroid similarity")
     ap.add_argument("--sink", type=int, default=0, help="inverted-index workloads: leading tokens always attended")
-    ap.add_argument("--assign", type=int, default=1, choices=[1, 2],
-                    help="inverted-index workloads: lists per key (2: every key joins its two nearest lists)")
+    ap.add_argument("--assign", type=int, default=1, choices=[1, 2, 3, 4],
+                    help="inverted-index workloads: lists per key (m > 1: every key joins its m nearest lists; "
+                         "with --grow, appends go into all m lists or none)")
     ap.add_argument("--window", type=int, default=0,
                     help="inverted-index workloads: trailing tokens always attended")
     ap.add_argument("--popularity", type=float, default=0.0,
@@ -145,9 +146,10 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
     p = W.ivf_problem(cfg, device=dev)
     nq = min(cfg.steps, 64)
     q_all = W.ivf_queries(cfg, p["centroids"], steps=nq)
-    slack = (N - prefix) // C
+    m = args.assign
+    slack = (N - prefix) * m // C
     k_cache, v_cache = p["keys"], p["values"]       # rows >= prefix are rewritten by the appends
-    offsets, lens, ids = tsa.index_build_dyn(k_cache, p["centroids"], prefix, slack)
+    offsets, lens, ids, alt = tsa.index_build_dyn_multi(k_cache, p["centroids"], prefix, m, slack)
     new_k = p["keys"][:, prefix:prefix + total].transpose(0, 1).contiguous()    # [steps][B][Hkv][d]
     new_v = p["values"][:, prefix:prefix + total].transpose(0, 1).contiguous()
     pos = (prefix + torch.arange(total, device=dev, dtype=torch.int32))[:, None].expand(total, B).contiguous()
@@ -155,15 +157,23 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
     out = torch.empty((B, Hq, cfg.head_dim), dtype=torch.float32, device=dev)
     uniq = torch.empty((total, B, Hkv), dtype=torch.int32, device=dev)
     desc = tsa.binding.ivf_desc(k_cache, p["centroids"], Hq)
-    ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
+    if m == 1:
+        ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX_MULTI, desc, k, m), dtype=torch.uint8,
+                         device=dev)
     aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total)]
     torch.cuda.synchronize()
 
     def call(i):
-        tsa.sparse_decode_dyn(q_all[i % nq], p["centroids"], offsets, lens, ids, k_cache, v_cache, k,
-                              out=out, uniq_out=uniq[i], ws=ws)
+        if m == 1:
+            tsa.sparse_decode_dyn(q_all[i % nq], p["centroids"], offsets, lens, ids, k_cache, v_cache, k,
+                                  out=out, uniq_out=uniq[i], ws=ws)
+        else:
+            tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, k_cache, v_cache, k, lens=lens, alt=alt,
+                                 out=out, uniq_out=uniq[i], ws=ws)
         aev[i][0].record()
-        tsa.kv_append(new_k[i], new_v[i], pos[i], p["centroids"], k_cache, v_cache, offsets, lens, ids,
+        tsa.kv_append(new_k[i], new_v[i], pos[i], p["centroids"], k_cache, v_cache, offsets, lens, ids, alt=alt,
                       status=status[i])
         aev[i][1].record()
 
@@ -175,10 +185,12 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
                 "unique_rows_per_step": float(per_step.mean())})
     a_ms = [aev[i][0].elapsed_time(aev[i][1]) for i in range(args.warmup, total)]
     st = status[args.warmup:].cpu()
-    res["append"] = {"prefix_tokens": prefix, "slack_per_list": slack,
+    res["append"] = {"prefix_tokens": prefix, "slack_per_list": slack, "lists_per_key": m,
                      "mean_us": round(sum(a_ms) / len(a_ms) * 1e3, 2),
                      "indexed": int((st == 0).sum()), "list_full": int((st == 1).sum()),
                      "bytes_per_launch": B * Hkv * 2 * row_bytes,
+                     "refused_appends": "a key whose m lists are not all free joins none (status 1); "
+                                        "index_regrow lays the lists out again with fresh free entries",
                      "timing": "torch events around each kv_append launch on the call's stream"}
     return res
 
@@ -194,8 +206,8 @@ def bench_ivf(args, cfg, torch, tsa, W):
     q_all = W.ivf_queries(cfg, p["centroids"], steps=nq)
     t0 = time.perf_counter()
     alt = None
-    if args.assign == 2:
-        offsets, ids, alt = tsa.index_build_multi(p["keys"], p["centroids"], 2)
+    if args.assign > 1:
+        offsets, ids, alt = tsa.index_build_multi(p["keys"], p["centroids"], args.assign)
     else:
         offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     torch.cuda.synchronize()
@@ -207,8 +219,11 @@ def bench_ivf(args, cfg, torch, tsa, W):
 
     variant = args.similarity != "dot" or args.sink > 0 or args.window > 0 or alt is not None
     if variant:
-        op = tsa.binding.OP_SPARSE_DECODE_EX_MULTI if alt is not None else tsa.binding.OP_SPARSE_DECODE_EX
-        ws = torch.empty(tsa.workspace_bytes(op, desc, k), dtype=torch.uint8, device=dev)
+        if alt is not None:
+            need = tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX_MULTI, desc, k, args.assign)
+        else:
+            need = tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX, desc, k)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
     def call(i):
         if variant:
@@ -222,8 +237,8 @@ def bench_ivf(args, cfg, torch, tsa, W):
     res = _timed(args, call, torch, tsa, n_distinct=nq)
     # rows read per step: unique list rows, plus the sink / window rows (an
     # upper bound: a list row inside those ranges is read once, counted twice;
-    # with two lists per key, list entries: a token in two chosen lists of the
-    # group counts twice)
+    # with m lists per key, list entries: a token in several chosen lists of
+    # the group counts once per list)
     fixed = min(args.sink + args.window, cfg.n_tokens) * B * Hkv
     rows_per_set = uniq.sum(dim=(1, 2)).cpu().double() + fixed
     rows = sum(float(rows_per_set[i % nq]) for i in range(args.steps))
@@ -894,8 +909,8 @@ def workload_name(cfg, args):
             workload += f"+{args.similarity}"
         if args.sink or args.window:
             workload += f"+sink{args.sink}+window{args.window}"
-        if args.assign == 2:
-            workload += "+two-lists-per-key"
+        if args.assign > 1:
+            workload += f"+{args.assign}-lists-per-key"
     if cfg.kind == "cache" and (cfg.popularity_sd or cfg.recency):
         workload += f"+popularity{cfg.popularity_sd:g}+recency{cfg.recency:g}"
     if cfg.kind == "cache" and args.policy != "lru":

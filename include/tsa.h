@@ -79,8 +79,8 @@ typedef enum tsa_op {
   TSA_OP_TOKEN_DECODE = 2,
   TSA_OP_ATTEND_ROWS = 3,
   TSA_OP_SPARSE_DECODE_EX = 4,
-  TSA_OP_INDEX_BUILD_MULTI = 5,      /* tsa_index_build_multi with m = 2 */
-  TSA_OP_SPARSE_DECODE_EX_MULTI = 6  /* tsa_sparse_decode_ex with assign_per_key = 2 */
+  TSA_OP_INDEX_BUILD_MULTI = 5,      /* tsa_index_build_multi (m = 2; any m: tsa_workspace_bytes_multi) */
+  TSA_OP_SPARSE_DECODE_EX_MULTI = 6  /* tsa_sparse_decode_ex with assign_per_key = m (likewise)       */
 } tsa_op;
 
 /* Inverted-index (centroid) problem. */
@@ -210,19 +210,26 @@ tsa_status tsa_sparse_decode_noalloc(const tsa_ivf_desc* desc, const void* q, co
 /* ------------------------------------------------------------------------
  * tsa_index_build_multi - posting lists in which every key joins its m
  *   nearest lists ([KARAT] How, index structure: an entry is placed into
- *   several lists by its key), m = 1 or 2 (squared L2 in fp32, nearest
- *   first, ties to the lower index).
+ *   several lists by its key), 1 <= m <= 4 and m <= C (squared L2 in fp32,
+ *   nearest first, ties to the lower index).
  *   offsets (device, out) int32 [B][Hkv][C+1] over N * m entries
  *   ids     (device, out) int32 [B][Hkv][N*m]: ascending token ids per list
- *   alt     (device, out) int32 [B][Hkv][N*m] (m = 2; NULL for m = 1): for
- *           each entry, the token's other list
- *   Workspace: tsa_workspace_bytes(TSA_OP_INDEX_BUILD_MULTI, desc, 0, ...)
- *   for m = 2 (TSA_OP_INDEX_BUILD for m = 1). Decode with
- *   tsa_sparse_decode_ex and opts->assign_per_key = m.
+ *   alt     (device, out) int32 [B][Hkv][N*m][m-1] (NULL for m = 1): for
+ *           each entry, the token's other m - 1 lists, in the token's order
+ *           of preference
+ *   Workspace: tsa_workspace_bytes_multi(TSA_OP_INDEX_BUILD_MULTI, desc, 0,
+ *   m, ...). Decode with tsa_sparse_decode_ex and opts->assign_per_key = m.
+ *   TSA_ERR_UNSUPPORTED for m outside [1, 4] or N * m beyond int32.
  * ---------------------------------------------------------------------- */
 tsa_status tsa_index_build_multi(const tsa_ivf_desc* desc, const void* keys, const void* centroids,
                                  int32_t m, int32_t* offsets, int32_t* ids, int32_t* alt, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/* tsa_workspace_bytes for the m-way operations: TSA_OP_INDEX_BUILD_MULTI
+ * (k unused) and TSA_OP_SPARSE_DECODE_EX_MULTI (k = top-k) with m lists per
+ * key (tsa_workspace_bytes sizes them for m = 2); other ops as
+ * tsa_workspace_bytes. */
+tsa_status tsa_workspace_bytes_multi(int32_t op, const void* desc, int32_t k, int32_t m, size_t* bytes);
 
 /* ------------------------------------------------------------------------
  * Growing index: per-step KV and posting-list append.
@@ -276,6 +283,55 @@ tsa_status tsa_sparse_decode_dyn(const tsa_ivf_desc* desc, const void* q, const 
                                  size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Growing m-way index (several lists per key, [KARAT] How, index
+ * structure; appended every step, worked example step 6).
+ *
+ * tsa_index_build_dyn_multi - tsa_index_build_dyn in which every key of the
+ *   prefix joins its m nearest lists (1 <= m <= 4, m <= C). The lists hold
+ *   N * m entries: n_prefix * m + C * slack <= N * m.
+ *   offsets, lens  as for tsa_index_build_dyn, over N * m entries
+ *   ids     (device, out) int32 [B][Hkv][N*m]; free entries -1
+ *   alt     (device, out) int32 [B][Hkv][N*m][m-1] (NULL for m = 1): each
+ *           valid entry's other lists (free entries are not written)
+ *   Workspace: tsa_workspace_bytes_multi(TSA_OP_INDEX_BUILD_MULTI, desc, 0, m).
+ *
+ * tsa_kv_append_multi - tsa_kv_append into an m-way growing index: the key
+ *   joins its m nearest lists, each at the end of its valid entries with
+ *   its other lists in alt, when every one of them has a free entry; else
+ *   it joins none (status 1; its K and V rows are stored either way).
+ *   No workspace.
+ *
+ * tsa_index_regrow - repairs a growing index whose lists ran full: lays the
+ *   same lists out again, in separate output arrays of the same shapes, each
+ *   list keeping its valid entries (and alt rows) in order at the front of
+ *   a range with `slack` free entries after them (slack < 0: the largest
+ *   slack every list can get, (N * m - total valid) / C). Nothing is
+ *   reassigned; appends that reported a full list can then be made again.
+ *   m, offsets, lens, ids, alt   the index (alt NULL for m = 1)
+ *   *_out   (device, out) the new index; no output may alias an input
+ *   status  (device, out, nullable) int32 [B][Hkv]: 0 done; 1 the valid
+ *           entries plus the free ones exceed N * m (that group's outputs
+ *           are not written)
+ *   Lengths are clamped to their list's range and ranges to [0, N * m).
+ *   No workspace.
+ *
+ * Decode a growing m-way index with tsa_sparse_decode_ex, opts->lens and
+ * opts->assign_per_key = m.
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_index_build_dyn_multi(const tsa_ivf_desc* desc, const void* keys, const void* centroids,
+                                     int32_t n_prefix, int32_t slack, int32_t m, int32_t* offsets,
+                                     int32_t* lens, int32_t* ids, int32_t* alt, void* ws, size_t ws_bytes,
+                                     void* stream);
+tsa_status tsa_kv_append_multi(const tsa_ivf_desc* desc, int32_t m, const void* new_k, const void* new_v,
+                               const int32_t* pos, const void* centroids, void* k_cache, void* v_cache,
+                               const int32_t* offsets, int32_t* lens, int32_t* ids, int32_t* alt,
+                               int32_t* status, void* stream);
+tsa_status tsa_index_regrow(const tsa_ivf_desc* desc, int32_t m, const int32_t* offsets, const int32_t* lens,
+                            const int32_t* ids, const int32_t* alt, int32_t slack, int32_t* offsets_out,
+                            int32_t* lens_out, int32_t* ids_out, int32_t* alt_out, int32_t* status,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
  * tsa_sparse_decode_ex - tsa_sparse_decode with the decode variants.
  *   [KARAT] worked example, step 3: centroids are compared with the query by
  *   cosine similarity; method details: the cores also run window-based
@@ -289,12 +345,14 @@ tsa_status tsa_sparse_decode_dyn(const tsa_ivf_desc* desc, const void* q, const 
  *                     request (default N); both ranges are clipped to [0, L)
  *   opts->lens        (device, nullable) list lengths of a growing index, as
  *                     for tsa_sparse_decode_dyn
- *   opts->assign_per_key  0 or 1: one list per token; 2: ids and alt come
- *                     from tsa_index_build_multi with m = 2 ([B][Hkv][2N]);
- *                     a token in two chosen lists of a head is attended once
- *                     (through the lower-numbered list); not with lens
- *   opts->alt         (device) int32 [B][Hkv][2N] from tsa_index_build_multi,
- *                     required when assign_per_key is 2
+ *   opts->assign_per_key  0 or 1: one list per token; m in 2..4: ids and alt
+ *                     come from tsa_index_build_multi (or, with lens, from
+ *                     tsa_index_build_dyn_multi and tsa_kv_append_multi)
+ *                     with that m ([B][Hkv][N*m]); a token in several chosen
+ *                     lists of a head is attended once (through the
+ *                     lowest-numbered of them)
+ *   opts->alt         (device) int32 [B][Hkv][N*m][m-1] from the m-way build,
+ *                     required when assign_per_key is 2 or more
  *   The attended set of a head is the union of its chosen lists' rows and
  *   the two ranges; a row in both is attended once. rows_out and uniq_out
  *   count list entries only. Workspace:
@@ -308,10 +366,10 @@ typedef struct tsa_decode_opts {
   int32_t similarity;       /* tsa_similarity                               */
   int32_t n_sink;           /* leading tokens always attended               */
   int32_t n_window;         /* trailing tokens (before the length) attended */
-  int32_t assign_per_key;   /* 0 / 1 / 2 lists per token                    */
+  int32_t assign_per_key;   /* 0 or 1 .. 4 lists per token                  */
   const int32_t* lengths;   /* device [B] or NULL                           */
   const int32_t* lens;      /* device [B][Hkv][C] or NULL                   */
-  const int32_t* alt;       /* device [B][Hkv][2N] or NULL                  */
+  const int32_t* alt;       /* device [B][Hkv][N*m][m-1] or NULL            */
 } tsa_decode_opts;
 
 tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts* opts, const void* q,

@@ -99,6 +99,7 @@ def test_workspace_sizes_and_validation(lib):
 def test_calls_reject_bad_arguments_before_any_launch(lib):
     d = B.IvfDesc(2, 100, 2, 8, 128, 8, 1, B.TSA_BF16)
     fake = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: validation fails first
+    fake2 = ctypes.c_void_p(0x20000)       # a second such pointer
     odd = ctypes.c_void_p(0x10001)
     args = [ctypes.byref(d), fake, fake, fake, fake, fake, fake]
     ws_need = B.workspace_bytes(B.OP_SPARSE_DECODE, d, 4)
@@ -139,9 +140,41 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
         assert st == B.TSA_ERR_INVALID_ARG
     assert B.workspace_bytes(B.OP_SPARSE_DECODE_EX_MULTI, d, 4) > ws_ex
     assert B.workspace_bytes(B.OP_INDEX_BUILD_MULTI, d) > B.workspace_bytes(B.OP_INDEX_BUILD, d)
-    st = lib.tsa_index_build_multi(ctypes.byref(d), fake, fake, 3, fake, fake, fake, fake, 1 << 30, None)
+    for m in (0, 5):
+        st = lib.tsa_index_build_multi(ctypes.byref(d), fake, fake, m, fake, fake, fake, fake, 1 << 30, None)
+        assert st == B.TSA_ERR_UNSUPPORTED
+    for m in (2, 3, 4):
+        st = lib.tsa_index_build_multi(ctypes.byref(d), fake, fake, m, fake, fake, None, fake, 1 << 30, None)
+        assert st == B.TSA_ERR_INVALID_ARG and b"alt is NULL" in lib.tsa_last_error()
+    # m-way workspaces grow with m; m outside [1, 4] is refused
+    ws_m = [B.workspace_bytes(B.OP_INDEX_BUILD_MULTI, d, 0, m) for m in (1, 2, 3, 4)]
+    assert ws_m[0] == B.workspace_bytes(B.OP_INDEX_BUILD, d) and ws_m == sorted(ws_m) and len(set(ws_m)) == 4
+    assert B.workspace_bytes(B.OP_INDEX_BUILD_MULTI, d, 0, 2) == B.workspace_bytes(B.OP_INDEX_BUILD_MULTI, d)
+    assert B.workspace_bytes(B.OP_SPARSE_DECODE_EX_MULTI, d, 4, 4) > B.workspace_bytes(B.OP_SPARSE_DECODE_EX_MULTI, d, 4)
+    n = ctypes.c_size_t()
+    assert lib.tsa_workspace_bytes_multi(B.OP_INDEX_BUILD_MULTI, ctypes.cast(ctypes.pointer(d), ctypes.c_void_p), 0,
+                                         5, ctypes.byref(n)) == B.TSA_ERR_UNSUPPORTED
+    # growing m-way index: capacity N * m, alt and lens required
+    st = lib.tsa_index_build_dyn_multi(ctypes.byref(d), fake, fake, 10, d.n_tokens, 2, fake, fake, fake, fake,
+                                       fake, 1 << 30, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"exceeds" in lib.tsa_last_error()
+    st = lib.tsa_index_build_dyn_multi(ctypes.byref(d), fake, fake, 10, 0, 3, fake, fake, fake, None, fake,
+                                       1 << 30, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"alt is NULL" in lib.tsa_last_error()
+    st = lib.tsa_index_build_dyn_multi(ctypes.byref(d), fake, fake, 10, 0, 2, fake, None, fake, fake, fake,
+                                       1 << 30, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"lens is NULL" in lib.tsa_last_error()
+    st = lib.tsa_kv_append_multi(ctypes.byref(d), 2, fake, fake, fake, fake, fake, fake, fake, fake, fake, None,
+                                 None, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"alt is NULL" in lib.tsa_last_error()
+    st = lib.tsa_kv_append_multi(ctypes.byref(d), 5, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                 None, None)
     assert st == B.TSA_ERR_UNSUPPORTED
-    st = lib.tsa_index_build_multi(ctypes.byref(d), fake, fake, 2, fake, fake, None, fake, 1 << 30, None)
+    # regrow: separate outputs, alt for m >= 2
+    st = lib.tsa_index_regrow(ctypes.byref(d), 1, fake, fake, fake, None, -1, fake2, fake2, fake, None, None, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"alias" in lib.tsa_last_error()
+    st = lib.tsa_index_regrow(ctypes.byref(d), 2, fake, fake, fake, None, -1, fake2, fake2, fake2, fake2, None,
+                              None)
     assert st == B.TSA_ERR_INVALID_ARG and b"alt is NULL" in lib.tsa_last_error()
     st = lib.tsa_sparse_decode_ex(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, 4, fake, None, None,
                                   None, fake, ws_ex, None)

@@ -298,7 +298,7 @@ def test_two_way_index_build_ragged_shapes(n_tokens, C):
     assert margin >= 1e-3, f"assignment margin {margin} too small for an exact comparison"
     assert np.array_equal(off.cpu().numpy(), r_off)
     assert np.array_equal(ids.cpu().numpy(), r_ids)
-    assert np.array_equal(alt.cpu().numpy(), r_alt[..., 0])
+    assert np.array_equal(alt.cpu().numpy(), r_alt)
     # the nearest list of each key, from the one-list build, is its first choice
     r1_off, r1_ids, _, margin1 = variants.index_build_multi(k64, c64, 1)
     assert margin1 >= 1e-3, f"first-choice margin {margin1} too small for an exact comparison"
@@ -326,7 +326,7 @@ def test_two_way_lists_build_and_decode(batch, n_kv_heads):
     assert margin >= 1e-3, f"second-choice margin {margin} too small for an exact comparison"
     assert np.array_equal(off.cpu().numpy(), r_off)
     assert np.array_equal(ids.cpu().numpy(), r_ids)
-    assert np.array_equal(alt.cpu().numpy(), r_alt[..., 0])
+    assert np.array_equal(alt.cpu().numpy(), r_alt)
     # one list per key through the same entry point equals the plain build
     o1, i1, a1 = tsa.index_build_multi(p["keys"], p["centroids"], 1)
     s_off, s_ids = tsa.index_build(p["keys"], p["centroids"])

@@ -18,6 +18,8 @@ from .binding import (  # noqa: F401
     index_build,
     index_build_dyn,
     index_build_multi,
+    index_build_dyn_multi,
+    index_regrow,
     kv_append,
     lib_path,
     load,
@@ -34,7 +36,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "index_build_multi", "kv_append", "sparse_decode",
+    "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "index_build_multi", "index_build_dyn_multi", "index_regrow", "kv_append", "sparse_decode",
     "sparse_decode_dyn", "sparse_decode_ex", "sparse_decode_noalloc", "token_decode",
     "attend_rows", "resolve", "cache_reset", "fetch_rows", "hier_group_step", "HostArray", "time_next_gather", "time_next_launch", "stream_read", "workspace_bytes",
     "TsaError",

@@ -78,6 +78,11 @@ _SIGNATURES = {
     "tsa_cache_reset": [ctypes.POINTER(CacheDesc), _P, _P, _P, _P],
     "tsa_attend_rows": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_workspace_bytes": [_I32, _P, _I32, ctypes.POINTER(ctypes.c_size_t)],
+    "tsa_workspace_bytes_multi": [_I32, _P, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)],
+    "tsa_index_build_dyn_multi": [ctypes.POINTER(IvfDesc), _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P],
+    "tsa_kv_append_multi": [ctypes.POINTER(IvfDesc), _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "tsa_index_regrow": [ctypes.POINTER(IvfDesc), _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P],
     "tsa_host_alloc": [ctypes.c_size_t, ctypes.POINTER(_P)],
     "tsa_host_free": [_P],
     "tsa_time_next_gather": [_P, _P],
@@ -166,14 +171,18 @@ def _i32(t: Optional[torch.Tensor], name: str, shape):
         raise ValueError(f"{name} must be int32 {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
 
 
-def workspace_bytes(op: int, desc, k: int = 0) -> int:
+def workspace_bytes(op: int, desc, k: int = 0, m: Optional[int] = None) -> int:
+    """Workspace of an operation; m (lists per key) for the m-way operations."""
     n = ctypes.c_size_t()
-    _check(load().tsa_workspace_bytes(op, ctypes.cast(ctypes.pointer(desc), _P), k, ctypes.byref(n)))
+    if m is None:
+        _check(load().tsa_workspace_bytes(op, ctypes.cast(ctypes.pointer(desc), _P), k, ctypes.byref(n)))
+    else:
+        _check(load().tsa_workspace_bytes_multi(op, ctypes.cast(ctypes.pointer(desc), _P), k, m, ctypes.byref(n)))
     return n.value
 
 
-def _workspace(op, desc, k, ws, device) -> torch.Tensor:
-    need = workspace_bytes(op, desc, k)
+def _workspace(op, desc, k, ws, device, m: Optional[int] = None) -> torch.Tensor:
+    need = workspace_bytes(op, desc, k, m)
     if ws is None:
         return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     if ws.numel() * ws.element_size() < need:
@@ -261,9 +270,11 @@ def index_build_dyn(keys, centroids, n_prefix: int, slack: Optional[int] = None,
     return offsets, lens, ids
 
 
-def kv_append(new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids, *, status=None, stream=None):
+def kv_append(new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids, *, alt=None, status=None,
+              stream=None):
     """Store one new token per request at row pos[b] and add it to its posting
-    list. Returns status [B][Hkv] int32 (0 indexed, 1 list full, 2 bad row)."""
+    list (with `alt`, an m-way index: to its m nearest lists, all or none).
+    Returns status [B][Hkv] int32 (0 indexed, 1 a list full, 2 bad row)."""
     for t, n in ((new_k, "new_k"), (new_v, "new_v"), (centroids, "centroids"), (k_cache, "k_cache"),
                  (v_cache, "v_cache")):
         _dev(t, n)
@@ -276,22 +287,38 @@ def kv_append(new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids
         raise ValueError("new_k / new_v must be [B][Hkv][d]")
     if tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("k_cache and v_cache shapes differ")
+    m = _lists_per_key(alt, B, Hkv, N)
     _i32(pos, "pos", (B,))
     _i32(offsets, "offsets", (B, Hkv, C + 1))
     _i32(lens, "lens", (B, Hkv, C))
-    _i32(ids, "ids", (B, Hkv, N))
+    _i32(ids, "ids", (B, Hkv, N * m))
     if status is None:
         status = torch.empty((B, Hkv), dtype=torch.int32, device=k_cache.device)
     _i32(status, "status", (B, Hkv))
-    _check(load().tsa_kv_append(ctypes.byref(desc), _ptr(new_k), _ptr(new_v), _ptr(pos), _ptr(centroids),
-                                _ptr(k_cache), _ptr(v_cache), _ptr(offsets), _ptr(lens), _ptr(ids), _ptr(status),
-                                _stream(stream)))
+    _check(load().tsa_kv_append_multi(ctypes.byref(desc), m, _ptr(new_k), _ptr(new_v), _ptr(pos), _ptr(centroids),
+                                      _ptr(k_cache), _ptr(v_cache), _ptr(offsets), _ptr(lens), _ptr(ids), _ptr(alt),
+                                      _ptr(status), _stream(stream)))
     return status
 
 
+def _alt_shape(B, Hkv, N, m):
+    return (B, Hkv, N * m, m - 1)
+
+
+def _lists_per_key(alt, B, Hkv, N) -> int:
+    """m of an m-way index from its alt array ([B][Hkv][N*m][m-1]; None: 1)."""
+    if alt is None:
+        return 1
+    if alt.dim() != 4 or alt.shape[3] < 1:
+        raise ValueError(f"alt must be int32 [B][Hkv][N*m][m-1], got {tuple(alt.shape)}")
+    m = alt.shape[3] + 1
+    _i32(alt, "alt", _alt_shape(B, Hkv, N, m))
+    return m
+
+
 def index_build_multi(keys, centroids, m: int = 2, *, offsets=None, ids=None, alt=None, ws=None, stream=None):
-    """Posting lists where every key joins its m nearest lists (m = 1 or 2).
-    Returns (offsets [B][Hkv][C+1], ids [B][Hkv][N*m], alt [B][Hkv][N*m] or None)."""
+    """Posting lists where every key joins its m nearest lists (1 <= m <= 4).
+    Returns (offsets [B][Hkv][C+1], ids [B][Hkv][N*m], alt [B][Hkv][N*m][m-1] or None)."""
     _dev(keys, "keys"), _dev(centroids, "centroids")
     if centroids.dtype != keys.dtype:
         raise ValueError("keys and centroids must share a dtype")
@@ -302,15 +329,78 @@ def index_build_multi(keys, centroids, m: int = 2, *, offsets=None, ids=None, al
         offsets = torch.empty((B, Hkv, C + 1), dtype=torch.int32, device=keys.device)
     if ids is None:
         ids = torch.empty((B, Hkv, N * m), dtype=torch.int32, device=keys.device)
-    if alt is None and m == 2:
-        alt = torch.empty((B, Hkv, N * m), dtype=torch.int32, device=keys.device)
+    if alt is None and m > 1:
+        alt = torch.empty(_alt_shape(B, Hkv, N, m), dtype=torch.int32, device=keys.device)
     _i32(offsets, "offsets", (B, Hkv, C + 1))
     _i32(ids, "ids", (B, Hkv, N * m))
-    _i32(alt, "alt", (B, Hkv, N * m))
-    ws = _workspace(OP_INDEX_BUILD_MULTI if m == 2 else OP_INDEX_BUILD, desc, 0, ws, keys.device)
+    if m > 1:
+        _i32(alt, "alt", _alt_shape(B, Hkv, N, m))
+    ws = _workspace(OP_INDEX_BUILD_MULTI, desc, 0, ws, keys.device, m)
     _check(load().tsa_index_build_multi(ctypes.byref(desc), _ptr(keys), _ptr(centroids), m, _ptr(offsets), _ptr(ids),
-                                        _ptr(alt), _ptr(ws), ws.numel(), _stream(stream)))
-    return offsets, ids, alt
+                                        _ptr(alt if m > 1 else None), _ptr(ws), ws.numel(), _stream(stream)))
+    return offsets, ids, (alt if m > 1 else None)
+
+
+def index_build_dyn_multi(keys, centroids, n_prefix: int, m: int, slack: Optional[int] = None, *, offsets=None,
+                          lens=None, ids=None, alt=None, ws=None, stream=None):
+    """Growing m-way index over the first n_prefix tokens with `slack` free
+    entries per list (default: the spare entries shared evenly).
+    Returns (offsets, lens, ids [B][Hkv][N*m], alt [B][Hkv][N*m][m-1] or None)."""
+    _dev(keys, "keys"), _dev(centroids, "centroids")
+    if centroids.dtype != keys.dtype:
+        raise ValueError("keys and centroids must share a dtype")
+    desc = ivf_desc(keys, centroids, keys.shape[2])
+    B, N, Hkv, _ = keys.shape
+    C = centroids.shape[2]
+    if slack is None:
+        slack = (N * m - n_prefix * m) // C
+    dev = keys.device
+    offsets = torch.empty((B, Hkv, C + 1), dtype=torch.int32, device=dev) if offsets is None else offsets
+    lens = torch.empty((B, Hkv, C), dtype=torch.int32, device=dev) if lens is None else lens
+    ids = torch.empty((B, Hkv, N * m), dtype=torch.int32, device=dev) if ids is None else ids
+    if alt is None and m > 1:
+        alt = torch.empty(_alt_shape(B, Hkv, N, m), dtype=torch.int32, device=dev)
+    _i32(offsets, "offsets", (B, Hkv, C + 1))
+    _i32(lens, "lens", (B, Hkv, C))
+    _i32(ids, "ids", (B, Hkv, N * m))
+    if m > 1:
+        _i32(alt, "alt", _alt_shape(B, Hkv, N, m))
+    ws = _workspace(OP_INDEX_BUILD_MULTI, desc, 0, ws, dev, m)
+    _check(load().tsa_index_build_dyn_multi(ctypes.byref(desc), _ptr(keys), _ptr(centroids), n_prefix, slack, m,
+                                            _ptr(offsets), _ptr(lens), _ptr(ids), _ptr(alt if m > 1 else None),
+                                            _ptr(ws), ws.numel(), _stream(stream)))
+    return offsets, lens, ids, (alt if m > 1 else None)
+
+
+def index_regrow(offsets, lens, ids, alt=None, slack: int = -1, *, out=None, status=None, stream=None):
+    """Lay a growing index out again with `slack` free entries after every
+    list (-1: as many as fit for every list), into new arrays (or `out`, a
+    tuple (offsets, lens, ids, alt)). Returns ((offsets, lens, ids, alt), status)."""
+    for t, n in ((offsets, "offsets"), (lens, "lens"), (ids, "ids")):
+        _dev(t, n)
+    B, Hkv, C1 = offsets.shape
+    C = C1 - 1
+    cap = ids.shape[2]
+    m = 1 if alt is None else alt.shape[3] + 1
+    if cap % m:
+        raise ValueError("ids must hold N * m entries")
+    N = cap // m
+    _i32(offsets, "offsets", (B, Hkv, C + 1))
+    _i32(lens, "lens", (B, Hkv, C))
+    _i32(ids, "ids", (B, Hkv, cap))
+    if alt is not None:
+        _i32(alt, "alt", _alt_shape(B, Hkv, N, m))
+    if out is None:
+        out = (torch.empty_like(offsets), torch.empty_like(lens), torch.empty_like(ids),
+               None if alt is None else torch.empty_like(alt))
+    if status is None:
+        status = torch.empty((B, Hkv), dtype=torch.int32, device=ids.device)
+    _i32(status, "status", (B, Hkv))
+    desc = IvfDesc(B, N, Hkv, Hkv, 128, C, 1, 1)
+    _check(load().tsa_index_regrow(ctypes.byref(desc), m, _ptr(offsets), _ptr(lens), _ptr(ids), _ptr(alt), slack,
+                                   _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(out[3]), _ptr(status),
+                                   _stream(stream)))
+    return out, status
 
 
 def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, similarity: str = "dot",
@@ -318,8 +408,9 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
                      sel_out=None, rows_out=None, uniq_out=None, ws=None, stream=None):
     """Decode with the variants: cosine similarity and/or the first n_sink and
     last n_window tokens (before lengths[b]) attended beside the lists; with
-    `alt` (from index_build_multi, m = 2) every token sits in two lists and is
-    attended once per head."""
+    `alt` (an m-way index from index_build_multi or index_build_dyn_multi)
+    every token sits in m lists and is attended once per head; with `lens`,
+    a growing index."""
     for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
@@ -332,10 +423,9 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
     if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != B or k_cache.shape[3] != d:
         raise ValueError("q / k_cache / v_cache shapes disagree")
     Hkv, C, N = desc.n_kv_heads, desc.n_centroids, desc.n_tokens
-    m = 2 if alt is not None else 1
+    m = _lists_per_key(alt, B, Hkv, N)
     _i32(offsets, "offsets", (B, Hkv, C + 1))
     _i32(ids, "ids", (B, Hkv, N * m))
-    _i32(alt, "alt", (B, Hkv, N * m))
     _i32(lengths, "lengths", (B,))
     _i32(lens, "lens", (B, Hkv, C))
     if out is None:
@@ -346,7 +436,8 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
     _i32(rows_out, "rows_out", (B, Hq))
     _i32(uniq_out, "uniq_out", (B, Hkv))
     opts = DecodeOpts(SIMILARITY[similarity], n_sink, n_window, m, _ptr(lengths), _ptr(lens), _ptr(alt))
-    ws = _workspace(OP_SPARSE_DECODE_EX_MULTI if m == 2 else OP_SPARSE_DECODE_EX, desc, k, ws, q.device)
+    ws = (_workspace(OP_SPARSE_DECODE_EX_MULTI, desc, k, ws, q.device, m) if m > 1
+          else _workspace(OP_SPARSE_DECODE_EX, desc, k, ws, q.device))
     _check(load().tsa_sparse_decode_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(centroids),
                                        _ptr(offsets), _ptr(ids), _ptr(k_cache), _ptr(v_cache), k, _ptr(out),
                                        _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(),

@@ -282,7 +282,20 @@ __device__ __forceinline__ void all_heads_pass(uint32_t mask, const int* ids, in
   }
 }
 
-// DUP: explicit plans over 2-way lists, with per-row duplicate head masks
+// Heads of the group that attend an m-way list entry through a lower chosen
+// list: the OR of the chosen-list head masks of the entry's other lists
+// (alt row of w = m - 1 ids) that are numbered below `list`.
+__device__ __forceinline__ uint32_t dup_heads(const int32_t* alt_row, int w, int list, const uint32_t* lmask,
+                                              int C) {
+  uint32_t dm = 0u;
+  for (int q = 0; q < w; ++q) {
+    const int other = alt_row[q];
+    if (other >= 0 && other < list && other < C) dm |= lmask[other];
+  }
+  return dm;
+}
+
+// DUP: explicit plans over m-way lists, with per-row duplicate head masks
 template <typename T, int G, bool EXPLICIT, bool DUP>
 __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) void gather_attn_kernel(GatherParams p) {
   constexpr int NW = gather_waves<EXPLICIT>();
@@ -369,19 +382,17 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) void gather_attn_
     }
     return sg;
   };
-  // 2-way lists: a token sits in two lists; for each head the entry of the
-  // lower chosen list is the one attended (per-row duplicate head masks)
+  // m-way lists: a token sits in m lists; for each head the entry of the
+  // lowest chosen list is the one attended (per-row duplicate head masks)
   constexpr bool two_way = DUP;
   uint32_t* dup = DUP ? dup_lds[DUP ? wave : 0] : nullptr;
-  const int32_t* altb = two_way ? p.alt + b * p.rid_bstride + g * p.rid_gstride : nullptr;
+  const int32_t* altb = two_way ? p.alt + (b * p.rid_bstride + g * p.rid_gstride) * p.alt_w : nullptr;
   auto stage_dup = [&](const Seg& sg) {
     if constexpr (!DUP) return;
     for (int j = lane; j < sg.cnt; j += kWave) {
       uint32_t dm = 0u;
-      if (!sg.direct) {
-        const int other = altb[sg.start + j];
-        if (other >= 0 && other < sg.list && other < p.C) dm = p.lmask[static_cast<long long>(bg) * p.C + other];
-      }
+      if (!sg.direct) dm = dup_heads(altb + static_cast<long long>(sg.start + j) * p.alt_w, p.alt_w, sg.list,
+                                     p.lmask + static_cast<long long>(bg) * p.C, p.C);
       dup[j] = dm;
     }
   };
@@ -448,7 +459,7 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) void gather_attn_
     // scored and dropped; only the mask's states are written). Otherwise such rows
     // stay cacheable, one pass per head, the later passes hitting L2: a
     // small batch is bound by the latency of its waves, which the extra
-    // heads' arithmetic would lengthen. (2-way lists keep per-head passes:
+    // heads' arithmetic would lengthen. (m-way lists keep per-head passes:
     // their duplicate masks differ per head.)
     const bool all_heads =
         !EXPLICIT || (G > 1 && !two_way &&
@@ -484,9 +495,9 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) void gather_attn_
 // (Splitting a set's rows evenly over the waves, or aligning each head class
 // to a set with empty segments, measured slower: the first adds a barrier
 // between staging and streaming, the second idle waves.)
-// DUP: 2-way lists, whose rows carry per-head duplicate masks (each head
-// attends a token through the lower of its two chosen lists); every head of
-// a segment then takes its own pass.
+// DUP: m-way lists, whose rows carry per-head duplicate masks (each head
+// attends a token through the lowest of its chosen lists that hold it);
+// every head of a segment then takes its own pass.
 template <typename T, int G, bool DUP>
 __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(GatherParams p) {
   constexpr int NW = kMergeWaves;
@@ -522,7 +533,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(Gathe
   const int32_t* rid = p.rowids + b * p.rid_bstride + g * p.rid_gstride;
   int* ids = ids_lds[wave];
   uint32_t* dup = dup_lds[DUP ? wave : 0];
-  const int32_t* altb = DUP ? p.alt + b * p.rid_bstride + g * p.rid_gstride : nullptr;
+  const int32_t* altb = DUP ? p.alt + (b * p.rid_bstride + g * p.rid_gstride) * p.alt_w : nullptr;
   // sink / window ranges: list rows inside them are skipped (attended
   // through their own direct segments)
   int fx_sink = 0, fx_lo = 0, fx_hi = 0;
@@ -566,12 +577,9 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(Gathe
       if (!my_direct) ok = ok && !(id < fx_sink || (id >= fx_lo && id < fx_hi));
       ids[j] = ok ? id : -1;
       if constexpr (DUP) {  // heads that attend this token through a lower chosen list
-        uint32_t dm = 0u;
-        if (!my_direct) {
-          const int other = altb[my_start + j];
-          if (other >= 0 && other < my_list && other < p.C) dm = p.lmask[static_cast<long long>(bg) * p.C + other];
-        }
-        dup[j] = dm;
+        dup[j] = my_direct ? 0u
+                           : dup_heads(altb + static_cast<long long>(my_start + j) * p.alt_w, p.alt_w, my_list,
+                                       p.lmask + static_cast<long long>(bg) * p.C, p.C);
       }
     }
     __syncthreads();  // queries staged (first set); the ids are wave-private

@@ -231,6 +231,14 @@ tsa_status check_ivf(const tsa_ivf_desc* d) {
   return check_dtype(d->dtype);
 }
 
+// lists per key of a multi-way index
+tsa_status check_m(const tsa_ivf_desc* d, int m) {
+  if (m < 1 || m > kMaxAssign) return fail(TSA_ERR_UNSUPPORTED, "m=%d: 1 to %d lists per key", m, kMaxAssign);
+  if (m > d->n_centroids) return fail(TSA_ERR_INVALID_ARG, "m=%d > C=%d", m, d->n_centroids);
+  if (static_cast<long long>(d->n_tokens) * m > INT32_MAX) return fail(TSA_ERR_UNSUPPORTED, "N * m exceeds int32");
+  return TSA_OK;
+}
+
 tsa_status check_token(const tsa_token_desc* d, int k) {
   if (!d) return fail(TSA_ERR_INVALID_ARG, "desc is NULL");
   if (d->batch <= 0 || d->n_tokens <= 0 || d->n_kv_heads <= 0 || d->n_q_heads <= 0 ||
@@ -337,7 +345,7 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
   REQUIRE_ALIGN(v_cache, 16); REQUIRE_ALIGN(out, 8); REQUIRE_ALIGN(ws, 16);
   const tsa_ivf_desc& d = *desc;
   if (k < 1 || k > d.n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d.n_centroids);
-  const int m = opts && opts->assign_per_key == 2 ? 2 : 1;
+  const int m = opts && opts->assign_per_key > 1 ? opts->assign_per_key : 1;
   const IvfLayout L = ivf_layout(d, k, opts != nullptr, m);
   if (ws_bytes < L.total) return fail(TSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   char* w = static_cast<char*>(ws);
@@ -353,7 +361,7 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
     selp.n_window = opts->n_window;
     selp.lengths = opts->lengths;
   }
-  if (m == 2) selp.lmask_out = reinterpret_cast<uint32_t*>(w + L.lmask);
+  if (m > 1) selp.lmask_out = reinterpret_cast<uint32_t*>(w + L.lmask);
   selp.seg_rows = L.seg_rows;
   selp.class_order = L.merge ? 1 : 0;
   if (L.split_score) selp.keys = reinterpret_cast<uint32_t*>(w + L.keys);
@@ -386,8 +394,9 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
     gp.n_window = opts->n_window;
     gp.lengths = opts->lengths;
   }
-  if (m == 2) {
+  if (m > 1) {
     gp.alt = opts->alt;
+    gp.alt_w = m - 1;
     gp.lmask = reinterpret_cast<const uint32_t*>(w + L.lmask);
     gp.C = d.n_centroids;
   }
@@ -413,6 +422,22 @@ const char* tsa_status_str(tsa_status s) {
 }
 
 const char* tsa_last_error(void) { return g_last_error.c_str(); }
+
+tsa_status tsa_workspace_bytes_multi(int32_t op, const void* desc, int32_t k, int32_t m, size_t* bytes) {
+  REQUIRE_PTR(bytes);
+  REQUIRE_PTR(desc);
+  if (op != TSA_OP_INDEX_BUILD_MULTI && op != TSA_OP_SPARSE_DECODE_EX_MULTI) return tsa_workspace_bytes(op, desc, k, bytes);
+  const auto* d = static_cast<const tsa_ivf_desc*>(desc);
+  if (tsa_status s = check_ivf(d)) return s;
+  if (tsa_status s = check_m(d, m)) return s;
+  if (op == TSA_OP_INDEX_BUILD_MULTI) {
+    *bytes = index_ws(*d, m);
+    return ok();
+  }
+  if (k < 1 || k > d->n_centroids) return fail(TSA_ERR_INVALID_ARG, "k=%d outside [1, C=%d]", k, d->n_centroids);
+  *bytes = ivf_layout(*d, k, true, m).total;
+  return ok();
+}
 
 tsa_status tsa_workspace_bytes(int32_t op, const void* desc, int32_t k, size_t* bytes) {
   REQUIRE_PTR(bytes);
@@ -492,27 +517,75 @@ tsa_status tsa_index_build_multi(const tsa_ivf_desc* desc, const void* keys, con
                                  int32_t* offsets, int32_t* ids, int32_t* alt, void* ws, size_t ws_bytes,
                                  void* stream) {
   if (tsa_status s = check_ivf(desc)) return s;
-  if (m != 1 && m != 2) return fail(TSA_ERR_UNSUPPORTED, "m=%d: 1 or 2 lists per token", m);
-  if (m > desc->n_centroids) return fail(TSA_ERR_INVALID_ARG, "m=%d > C=%d", m, desc->n_centroids);
-  if (m == 2) REQUIRE_PTR(alt);
-  if (static_cast<long long>(desc->n_tokens) * m > INT32_MAX) return fail(TSA_ERR_UNSUPPORTED, "N * m exceeds int32");
+  if (tsa_status s = check_m(desc, m)) return s;
+  if (m > 1) REQUIRE_PTR(alt);
   return index_build_impl(desc, keys, centroids, desc->n_tokens, 0, offsets, nullptr, ids, ws, ws_bytes, stream, m,
-                          m == 2 ? alt : nullptr);
+                          m > 1 ? alt : nullptr);
 }
 
-tsa_status tsa_kv_append(const tsa_ivf_desc* desc, const void* new_k, const void* new_v, const int32_t* pos,
-                         const void* centroids, void* k_cache, void* v_cache, const int32_t* offsets,
-                         int32_t* lens, int32_t* ids, int32_t* status, void* stream) {
+tsa_status tsa_index_build_dyn_multi(const tsa_ivf_desc* desc, const void* keys, const void* centroids,
+                                     int32_t n_prefix, int32_t slack, int32_t m, int32_t* offsets, int32_t* lens,
+                                     int32_t* ids, int32_t* alt, void* ws, size_t ws_bytes, void* stream) {
   if (tsa_status s = check_ivf(desc)) return s;
+  if (tsa_status s = check_m(desc, m)) return s;
+  REQUIRE_PTR(lens);
+  if (m > 1) REQUIRE_PTR(alt);
+  if (n_prefix < 1 || n_prefix > desc->n_tokens)
+    return fail(TSA_ERR_INVALID_ARG, "n_prefix=%d outside [1, N=%d]", n_prefix, desc->n_tokens);
+  const long long need = static_cast<long long>(n_prefix) * m + static_cast<long long>(desc->n_centroids) * slack;
+  if (slack < 0 || need > static_cast<long long>(desc->n_tokens) * m)
+    return fail(TSA_ERR_INVALID_ARG, "n_prefix * m + C * slack = %lld exceeds N * m = %lld", need,
+                static_cast<long long>(desc->n_tokens) * m);
+  return index_build_impl(desc, keys, centroids, n_prefix, slack, offsets, lens, ids, ws, ws_bytes, stream, m,
+                          m > 1 ? alt : nullptr);
+}
+
+tsa_status tsa_kv_append_multi(const tsa_ivf_desc* desc, int32_t m, const void* new_k, const void* new_v,
+                               const int32_t* pos, const void* centroids, void* k_cache, void* v_cache,
+                               const int32_t* offsets, int32_t* lens, int32_t* ids, int32_t* alt, int32_t* status,
+                               void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  if (tsa_status s = check_m(desc, m)) return s;
   REQUIRE_PTR(new_k); REQUIRE_PTR(new_v); REQUIRE_PTR(pos); REQUIRE_PTR(centroids); REQUIRE_PTR(k_cache);
   REQUIRE_PTR(v_cache); REQUIRE_PTR(offsets); REQUIRE_PTR(lens); REQUIRE_PTR(ids);
+  if (m > 1) REQUIRE_PTR(alt);
   REQUIRE_ALIGN(new_k, 16); REQUIRE_ALIGN(new_v, 16); REQUIRE_ALIGN(centroids, 16); REQUIRE_ALIGN(k_cache, 16);
   REQUIRE_ALIGN(v_cache, 16);
   const tsa_ivf_desc& d = *desc;
   AppendParams ap{new_k, new_v, pos, centroids, codebook_stride(d), k_cache, v_cache, offsets, lens, ids, status,
                   d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids};
+  ap.m = m;
+  ap.alt = m > 1 ? alt : nullptr;
   hipError_t e = launch_kv_append(ap, d.dtype, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  return ok();
+}
+
+tsa_status tsa_kv_append(const tsa_ivf_desc* desc, const void* new_k, const void* new_v, const int32_t* pos,
+                         const void* centroids, void* k_cache, void* v_cache, const int32_t* offsets,
+                         int32_t* lens, int32_t* ids, int32_t* status, void* stream) {
+  return tsa_kv_append_multi(desc, 1, new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids, nullptr,
+                             status, stream);
+}
+
+tsa_status tsa_index_regrow(const tsa_ivf_desc* desc, int32_t m, const int32_t* offsets, const int32_t* lens,
+                            const int32_t* ids, const int32_t* alt, int32_t slack, int32_t* offsets_out,
+                            int32_t* lens_out, int32_t* ids_out, int32_t* alt_out, int32_t* status, void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  if (tsa_status s = check_m(desc, m)) return s;
+  REQUIRE_PTR(offsets); REQUIRE_PTR(lens); REQUIRE_PTR(ids);
+  REQUIRE_PTR(offsets_out); REQUIRE_PTR(lens_out); REQUIRE_PTR(ids_out);
+  if (m > 1) {
+    REQUIRE_PTR(alt);
+    REQUIRE_PTR(alt_out);
+  }
+  if (ids_out == ids || offsets_out == offsets || lens_out == lens || (m > 1 && alt_out == alt))
+    return fail(TSA_ERR_INVALID_ARG, "regrow writes separate output arrays (an output aliases its input)");
+  RegrowParams rp{offsets, lens, ids, m > 1 ? alt : nullptr, offsets_out, lens_out, ids_out,
+                  m > 1 ? alt_out : nullptr, status, desc->batch, desc->n_kv_heads, desc->n_centroids,
+                  desc->n_tokens * m, m, slack};
+  hipError_t e = launch_regrow(rp, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "regrow launch");
   return ok();
 }
 
@@ -550,13 +623,11 @@ tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts*
       static_cast<long long>(opts->n_sink) + opts->n_window > kMaxFixedRows)
     return fail(TSA_ERR_INVALID_ARG, "n_sink=%d, n_window=%d: each >= 0 and together <= %d", opts->n_sink,
                 opts->n_window, kMaxFixedRows);
-  if (opts->assign_per_key < 0 || opts->assign_per_key > 2)
-    return fail(TSA_ERR_INVALID_ARG, "assign_per_key=%d is not 0, 1 or 2", opts->assign_per_key);
-  if (opts->assign_per_key == 2) {
-    if (!opts->alt) return fail(TSA_ERR_INVALID_ARG, "opts->alt is NULL for 2 lists per token");
-    if (opts->lens) return fail(TSA_ERR_UNSUPPORTED, "a growing index with 2 lists per token");
-    if (static_cast<long long>(desc->n_tokens) * 2 > INT32_MAX)
-      return fail(TSA_ERR_UNSUPPORTED, "2 * N exceeds int32");
+  if (opts->assign_per_key < 0 || opts->assign_per_key > kMaxAssign)
+    return fail(TSA_ERR_INVALID_ARG, "assign_per_key=%d outside [0, %d]", opts->assign_per_key, kMaxAssign);
+  if (opts->assign_per_key > 1) {
+    if (tsa_status s = check_m(desc, opts->assign_per_key)) return s;
+    if (!opts->alt) return fail(TSA_ERR_INVALID_ARG, "opts->alt is NULL for %d lists per token", opts->assign_per_key);
   }
   return sparse_decode_impl(desc, opts, q, centroids, offsets, opts->lens, ids, k_cache, v_cache, k, out, sel_out,
                             rows_out, uniq_out, ws, ws_bytes, stream);

@@ -20,7 +20,10 @@ namespace tsa {
 constexpr int kAssignTile = 32;
 
 // The M best (distance, centroid) pairs seen so far, best first; order is
-// lexicographic, so an equal distance keeps the lower centroid id.
+// lexicographic, so an equal distance keeps the lower centroid id. A new
+// pair is inserted by one pass of compare-and-swap down the list (the
+// displaced pair carried on), which keeps the list sorted and drops the
+// worst.
 template <int M>
 struct TopM {
   float d[M];
@@ -36,25 +39,19 @@ struct TopM {
     return d1 < d2 || (d1 == d2 && c1 < c2);
   }
   __device__ __forceinline__ void push(float dd, int cc) {
-    if (M == 1) {
-      if (less(dd, cc, d[0], c[0])) {
-        d[0] = dd;
-        c[0] = cc;
-      }
-      return;
-    }
-    if (less(dd, cc, d[0], c[0])) {
-      d[M - 1] = d[0];
-      c[M - 1] = c[0];
-      d[0] = dd;
-      c[0] = cc;
-    } else if (less(dd, cc, d[M - 1], c[M - 1])) {
-      d[M - 1] = dd;
-      c[M - 1] = cc;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const bool sw = less(dd, cc, d[i], c[i]);
+      const float td = d[i];
+      const int tc = c[i];
+      d[i] = sw ? dd : td;
+      c[i] = sw ? cc : tc;
+      dd = sw ? td : dd;
+      cc = sw ? tc : cc;
     }
   }
 };
-static_assert(sizeof(TopM<2>) > 0, "M is 1 or 2");
+static_assert(kMaxAssign >= 1 && kMaxAssign <= 4, "lists per key");
 
 template <typename T, int M>
 __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
@@ -239,16 +236,21 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
           // tie; -inf padding never passes
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float* v = bs[j];
-            int* id = bc[j];
-            const bool t0 = acc[i] > v[0];
-            if constexpr (M == 2) {
-              const bool t1 = acc[i] > v[1];
-              v[1] = t0 ? v[0] : (t1 ? acc[i] : v[1]);
-              id[1] = t0 ? id[0] : (t1 ? cr + i : id[1]);
+            // insert (acc[i], cr + i) into the list, ordered by s
+            // descending, then id ascending: the carried pair moves down past
+            // every pair after it in that order
+            float v = acc[i];
+            int id = cr + i;
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+              const float tv = bs[j][r];
+              const int ti = bc[j][r];
+              const bool sw = v > tv || (v == tv && id < ti);
+              bs[j][r] = sw ? v : tv;
+              bc[j][r] = sw ? id : ti;
+              v = sw ? tv : v;
+              id = sw ? ti : id;
             }
-            v[0] = t0 ? acc[i] : v[0];
-            id[0] = t0 ? cr + i : id[0];
           }
         }
       }
@@ -331,8 +333,15 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
   const int32_t* a = p.assign + static_cast<long long>(bg) * cap;
   int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
   int32_t* ids = p.ids + static_cast<long long>(bg) * cap;
-  int32_t* alt = p.alt ? p.alt + static_cast<long long>(bg) * cap : nullptr;
+  int32_t* alt = p.alt ? p.alt + static_cast<long long>(bg) * cap * (m - 1) : nullptr;
   int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * C : nullptr;
+  // entry i (token i / m's choice i % m) placed at pos: its alt row holds
+  // the token's other m - 1 lists, in the token's order of preference
+  auto put_alt = [&](long long pos, int i) {
+    const int tok = i / m, r = i - tok * m;
+    for (int q = 0; q < m - 1; ++q)
+      alt[pos * (m - 1) + q] = min(max(a[static_cast<long long>(tok) * m + q + (q >= r ? 1 : 0)], 0), C - 1);
+  };
   // this wave's entries, whole tokens (a multiple of m) each
   const int lo = static_cast<int>(static_cast<long long>(wave) * n / NW / m * m);
   const int hi = static_cast<int>(static_cast<long long>(wave + 1) * n / NW / m * m);
@@ -405,15 +414,11 @@ __global__ __launch_bounds__(NW * kWave) void csr_waves_kernel(CsrParams p) {
         const uint64_t bal = __ballot(set);
         same &= set ? bal : ~bal;
       }
-      // m == 2: a token's two entries sit in lanes 2t and 2t + 1 of one
-      // batch (ranges and batches start on even entries), so its other list
-      // is the neighbouring lane's
-      const int other = alt ? __shfl_xor(cc[u], 1) : 0;
       if (valid) {
         const int rank = prefix_count(same);
         const int pos = cur[c] + rank;
         put_id(pos, i / m);                  // entries of one token are adjacent: ascending ids per list
-        if (alt) alt[pos] = other;
+        if (alt) put_alt(pos, i);
         if (rank == static_cast<int>(__popcll(same)) - 1) cur[c] = pos + 1;
       }
     }
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
   const int32_t* a = p.assign + static_cast<long long>(bg) * cap;
   int32_t* off = p.offsets + static_cast<long long>(bg) * (p.C + 1);
   int32_t* ids = p.ids + static_cast<long long>(bg) * cap;
-  int32_t* alt = p.alt ? p.alt + static_cast<long long>(bg) * cap : nullptr;
+  int32_t* alt = p.alt ? p.alt + static_cast<long long>(bg) * cap * (m - 1) : nullptr;
   int32_t* lens = p.lens ? p.lens + static_cast<long long>(bg) * p.C : nullptr;
 
   for (int c = tid; c < p.C; c += 256) cursor[c] = 0;
@@ -483,7 +488,10 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
         const int rank = prefix_count(same);
         const int pos = cursor[c] + rank;
         ids[pos] = i / m;                       // entries of one token are adjacent: ascending ids per list
-        if (alt) alt[pos] = a[i ^ 1];           // m == 2: the token's other list
+        if (alt) {                              // the token's other lists, in its order of preference
+          const int tok = i / m, r = i - tok * m;
+          for (int q = 0; q < m - 1; ++q) alt[static_cast<long long>(pos) * (m - 1) + q] = a[tok * m + q + (q >= r ? 1 : 0)];
+        }
         if (rank == static_cast<int>(__popcll(same)) - 1) cursor[c] = pos + 1;
       }
     }
@@ -911,17 +919,18 @@ __global__ __launch_bounds__(NW * kWave) void ivf_select_kernel(SelectParams p) 
 // workgroup (4 waves) per (request, KV head): the new row goes to the cache;
 // its key is scored against every centroid (|c|^2 - 2 k.c, 16 lanes per
 // centroid row, DPP reduction, kAppendU rows in flight per lane group), the
-// best (distance, index) is reduced lexicographically over lane groups and
-// waves, and the id is written at the end of that list's valid entries when
-// the list still has a free one.
+// M best (distance, index) pairs are merged lexicographically over lane
+// groups and waves, and the id is written at the end of the valid entries of
+// each of the M lists (with its other lists in alt) when every one of them
+// still has a free entry, else into none.
 // ============================================================================
 constexpr int kAppendWaves = 4;
 constexpr int kAppendU = 4;
 
-template <typename T>
+template <typename T, int M>
 __global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendParams p) {
-  __shared__ float wbest[kAppendWaves];
-  __shared__ int wbestc[kAppendWaves];
+  __shared__ float wbest[kAppendWaves][M];
+  __shared__ int wbestc[kAppendWaves][M];
   const int bg = blockIdx.x;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave, r = lane >> 4, e = lane & 15;
@@ -944,8 +953,8 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendP
   kq.load(static_cast<const T*>(p.new_k) + src);
   const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
                 static_cast<long long>(g) * p.C * kHeadDim + e * 8;
-  float best = INFINITY;
-  int bestc = p.C;
+  TopM<M> top;  // this lane group's M nearest, by (distance, centroid)
+  top.init();
   constexpr int kStep = kAppendWaves * kAppendU * 4;
   for (int c0 = wave * kAppendU * 4; c0 < p.C; c0 += kStep) {
     Raw8<T> raw[kAppendU];
@@ -962,45 +971,142 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendP
       for (int i = 0; i < 8; ++i) n2 = fmaf(x[i], x[i], n2);
       const float dot = group16_sum(kq.dot(raw[u]));
       n2 = group16_sum(n2);
-      const float dist = n2 - 2.f * dot;
-      if (c < p.C && dist < best) {  // ascending c per lane group: strict < keeps the lower id
-        best = dist;
-        bestc = c;
-      }
+      if (c < p.C) top.push(n2 - 2.f * dot, c);
     }
   }
+  // merge the lane groups' lists, then the waves'
 #pragma unroll
   for (int o = 16; o < kWave; o <<= 1) {
-    const float d2 = __shfl_xor(best, o);
-    const int c2 = __shfl_xor(bestc, o);
-    if (d2 < best || (d2 == best && c2 < bestc)) {
-      best = d2;
-      bestc = c2;
+    float od[M];
+    int oc[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      od[i] = __shfl_xor(top.d[i], o);
+      oc[i] = __shfl_xor(top.c[i], o);
     }
+#pragma unroll
+    for (int i = 0; i < M; ++i) top.push(od[i], oc[i]);
   }
   if (lane == 0) {
-    wbest[wave] = best;
-    wbestc[wave] = bestc;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      wbest[wave][i] = top.d[i];
+      wbestc[wave][i] = top.c[i];
+    }
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < kAppendWaves; ++w) {
-      if (wbest[w] < best || (wbest[w] == best && wbestc[w] < bestc)) {
-        best = wbest[w];
-        bestc = wbestc[w];
-      }
-    }
+    for (int w = 1; w < kAppendWaves; ++w)
+#pragma unroll
+      for (int i = 0; i < M; ++i) top.push(wbest[w][i], wbestc[w][i]);
+    // the key joins its M lists only if every one has a free entry
+    const long long cap = static_cast<long long>(p.N) * M;
     const int32_t* off = p.offsets + static_cast<long long>(bg) * (p.C + 1);
     int32_t* lens = p.lens + static_cast<long long>(bg) * p.C;
-    const int c = min(bestc, p.C - 1);
-    const int start = off[c], end = off[c + 1], len = lens[c];
-    const bool room = start >= 0 && end <= p.N && len >= 0 && start + len < end;
+    int start[M], len[M];
+    bool room = true;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int c = min(max(top.c[i], 0), p.C - 1);
+      start[i] = off[c];
+      len[i] = lens[c];
+      const int end = off[c + 1];
+      room = room && start[i] >= 0 && end <= cap && len[i] >= 0 && start[i] + len[i] < end;
+    }
     if (room) {
-      p.ids[static_cast<long long>(bg) * p.N + start + len] = pos;
-      lens[c] = len + 1;
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const long long e = static_cast<long long>(bg) * cap + start[i] + len[i];
+        p.ids[e] = pos;
+        if constexpr (M > 1) {  // the token's other lists, in its order of preference
+#pragma unroll
+          for (int q = 0; q < M - 1; ++q) p.alt[e * (M - 1) + q] = top.c[q + (q >= i ? 1 : 0)];
+        }
+        lens[min(max(top.c[i], 0), p.C - 1)] = len[i] + 1;
+      }
     }
     if (st) *st = room ? 0 : 1;
   }
+}
+
+// Regrow: one workgroup per kRegrowChunk output entries of one (request, KV
+// head). Each workgroup scans the lists' lengths (clamped to their ranges)
+// into the new offsets, in LDS; an output entry finds its list by binary
+// search and copies the list's entry (and its alt row) at the same place
+// from the front of the old range, or writes -1 past the valid entries.
+// When the valid entries plus the free ones exceed the capacity, nothing is
+// written but the status.
+__global__ __launch_bounds__(256) void regrow_kernel(RegrowParams p) {
+  __shared__ int noff[kMaxCentroids + 1];
+  __shared__ int soff[kMaxCentroids];
+  __shared__ int nlen[kMaxCentroids];
+  __shared__ int scratch[8];
+  const int bg = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int C = p.C, w = p.m - 1;
+  const long long cap = p.cap;
+  const int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
+  const int32_t* lens = p.lens + static_cast<long long>(bg) * C;
+  // clamped valid lengths and their total
+  int my_total = 0;
+  for (int c = tid; c < C; c += 256) {
+    const int lo = min(max(off[c], 0), p.cap), hi = min(max(off[c + 1], lo), p.cap);
+    const int n = min(max(lens[c], 0), hi - lo);
+    soff[c] = lo;
+    nlen[c] = n;
+    my_total += n;
+  }
+  const int total = block_sum<4>(my_total, scratch);
+  int slack = p.slack;
+  if (slack < 0) slack = static_cast<int>((cap - total) / C);
+  const bool fits = slack >= 0 && total + static_cast<long long>(C) * slack <= cap;
+  if (!fits) {
+    if (blockIdx.x == 0 && tid == 0 && p.status) p.status[bg] = 1;
+    return;  // uniform over the block
+  }
+  // new offsets: exclusive scan of (len + slack), 256 lists per round
+  int carry = 0;
+  for (int c0 = 0; c0 < C; c0 += 256) {
+    const int c = c0 + tid;
+    int tot;
+    const int ex = block_exclusive_scan<4>(c < C ? nlen[c] + slack : 0, scratch, &tot);
+    if (c < C) noff[c] = carry + ex;
+    carry += tot;
+  }
+  if (tid == 0) noff[C] = carry;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int c = tid; c <= C; c += 256) p.offsets_out[static_cast<long long>(bg) * (C + 1) + c] = noff[c];
+    for (int c = tid; c < C; c += 256) p.lens_out[static_cast<long long>(bg) * C + c] = nlen[c];
+    if (tid == 0 && p.status) p.status[bg] = 0;
+  }
+  const int32_t* ids = p.ids + static_cast<long long>(bg) * cap;
+  int32_t* ids_out = p.ids_out + static_cast<long long>(bg) * cap;
+  const int32_t* alt = w > 0 ? p.alt + static_cast<long long>(bg) * cap * w : nullptr;
+  int32_t* alt_out = w > 0 ? p.alt_out + static_cast<long long>(bg) * cap * w : nullptr;
+  const long long e_lo = static_cast<long long>(blockIdx.x) * kRegrowChunk;
+  const long long e_hi = min(cap, e_lo + kRegrowChunk);
+  for (long long e = e_lo + tid; e < e_hi; e += 256) {
+    int src = -1;
+    if (e < carry) {
+      int lo = 0, hi = C - 1;  // the last list whose new offset is <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (noff[mid] <= e) lo = mid;
+        else hi = mid - 1;
+      }
+      const int j = static_cast<int>(e - noff[lo]);
+      if (j < nlen[lo]) src = soff[lo] + j;
+    }
+    ids_out[e] = src >= 0 ? ids[src] : -1;
+    for (int q = 0; q < w; ++q) alt_out[e * w + q] = src >= 0 ? alt[static_cast<long long>(src) * w + q] : -1;
+  }
+}
+
+hipError_t launch_regrow(const RegrowParams& p, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((p.cap + kRegrowChunk - 1) / kRegrowChunk), p.B * p.Hkv);
+  hipLaunchKernelGGL(regrow_kernel, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 // ============================================================================
@@ -1013,23 +1119,43 @@ hipError_t launch_assign(const AssignParams& p, int dtype, float* norms, hipStre
                        static_cast<const bf16_t*>(p.centroids), norms, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((p.n_assign + kMfmaKb - 1) / kMfmaKb, p.B * p.Hkv);
-    if (p.m == 2)
-      hipLaunchKernelGGL(assign_mfma_kernel<2>, grid, dim3(kMfmaWaves * kWave), 0, s, p, static_cast<const float*>(norms));
-    else
-      hipLaunchKernelGGL(assign_mfma_kernel<1>, grid, dim3(kMfmaWaves * kWave), 0, s, p, static_cast<const float*>(norms));
+    dim3 grid((p.n_assign + kMfmaKb - 1) / kMfmaKb, p.B * p.Hkv), block(kMfmaWaves * kWave);
+    const float* nf = norms;
+    switch (p.m) {
+      case 1: hipLaunchKernelGGL(assign_mfma_kernel<1>, grid, block, 0, s, p, nf); break;
+      case 2: hipLaunchKernelGGL(assign_mfma_kernel<2>, grid, block, 0, s, p, nf); break;
+      case 3: hipLaunchKernelGGL(assign_mfma_kernel<3>, grid, block, 0, s, p, nf); break;
+      default: hipLaunchKernelGGL(assign_mfma_kernel<4>, grid, block, 0, s, p, nf); break;
+    }
   } else {
     dim3 grid((p.n_assign + 255) / 256, p.B * p.Hkv);
-    if (p.m == 2) hipLaunchKernelGGL((assign_kernel<float, 2>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((assign_kernel<float, 1>), grid, dim3(256), 0, s, p);
+    switch (p.m) {
+      case 1: hipLaunchKernelGGL((assign_kernel<float, 1>), grid, dim3(256), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((assign_kernel<float, 2>), grid, dim3(256), 0, s, p); break;
+      case 3: hipLaunchKernelGGL((assign_kernel<float, 3>), grid, dim3(256), 0, s, p); break;
+      default: hipLaunchKernelGGL((assign_kernel<float, 4>), grid, dim3(256), 0, s, p); break;
+    }
   }
   return hipGetLastError();
 }
 
 hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t s) {
   const dim3 grid(p.B * p.Hkv), block(kAppendWaves * kWave);
-  if (dtype == kBF16) hipLaunchKernelGGL(kv_append_kernel<bf16_t>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(kv_append_kernel<float>, grid, block, 0, s, p);
+  if (dtype == kBF16) {
+    switch (p.m) {
+      case 1: hipLaunchKernelGGL((kv_append_kernel<bf16_t, 1>), grid, block, 0, s, p); break;
+      case 2: hipLaunchKernelGGL((kv_append_kernel<bf16_t, 2>), grid, block, 0, s, p); break;
+      case 3: hipLaunchKernelGGL((kv_append_kernel<bf16_t, 3>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((kv_append_kernel<bf16_t, 4>), grid, block, 0, s, p); break;
+    }
+  } else {
+    switch (p.m) {
+      case 1: hipLaunchKernelGGL((kv_append_kernel<float, 1>), grid, block, 0, s, p); break;
+      case 2: hipLaunchKernelGGL((kv_append_kernel<float, 2>), grid, block, 0, s, p); break;
+      case 3: hipLaunchKernelGGL((kv_append_kernel<float, 3>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((kv_append_kernel<float, 4>), grid, block, 0, s, p); break;
+    }
+  }
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ constexpr int kTokHistBits = 12;          // top bits of the score key in the th
 constexpr int kTokHistBins = 1 << kTokHistBits;
 constexpr int kMaxTokFilterChunks = 4096; // N <= kTokFilterTile * kMaxTokFilterChunks
 constexpr int kMaxCentroids = 4096;
+constexpr int kMaxAssign = 4;          // lists per key of a multi-way index
 constexpr int kMaxFixedRows = 8192;   // sink + window rows of one decode
 constexpr int kMaxSlots = 4096;
 constexpr int kMaxTokenK = 4096;
@@ -59,7 +60,7 @@ struct CsrParams {
   int32_t* offsets;        // [B][Hkv][C+1]: list c owns ids[offsets[c] .. offsets[c+1])
   int32_t* ids;            // [B][Hkv][N]; free entries are -1
   int32_t* lens;           // [B][Hkv][C] valid entries per list, or null
-  int32_t* alt;            // [B][Hkv][N*m] (m == 2): each entry's other list, or null
+  int32_t* alt;            // [B][Hkv][N*m][m-1] (m >= 2): each entry's other lists, or null
   int B, N, Hkv, C;
   int n_assign;            // tokens 0 .. n_assign-1 go into the lists
   int slack;               // free entries after every list
@@ -106,11 +107,30 @@ struct AppendParams {
   void* v_cache;
   const int32_t* offsets;  // [B][Hkv][C+1]
   int32_t* lens;           // [B][Hkv][C]
-  int32_t* ids;            // [B][Hkv][N]
-  int32_t* status;         // [B][Hkv] or null: 0 indexed, 1 list full, 2 row out of range
+  int32_t* ids;            // [B][Hkv][N*m]
+  int32_t* status;         // [B][Hkv] or null: 0 indexed, 1 a list full, 2 row out of range
   int B, N, Hkv, C;
+  int m = 1;               // lists per key: the key joins its m nearest lists, all or none
+  int32_t* alt = nullptr;  // [B][Hkv][N*m][m-1] (m >= 2): each entry's other lists
 };
 hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t s);
+
+// Re-layout of a growing index with `slack` free entries after every list
+// (slack < 0: as many as fit for every list), into separate output arrays.
+struct RegrowParams {
+  const int32_t* offsets;  // [B][Hkv][C+1]
+  const int32_t* lens;     // [B][Hkv][C]
+  const int32_t* ids;      // [B][Hkv][cap]
+  const int32_t* alt;      // [B][Hkv][cap][m-1] or null (m == 1)
+  int32_t* offsets_out;
+  int32_t* lens_out;
+  int32_t* ids_out;
+  int32_t* alt_out;
+  int32_t* status;         // [B][Hkv] or null: 0 done, 1 the lists do not fit (outputs untouched)
+  int B, Hkv, C, cap, m, slack;
+};
+constexpr int kRegrowChunk = 4096;   // output entries per regrow workgroup
+hipError_t launch_regrow(const RegrowParams& p, hipStream_t s);
 
 // --------------------------------------------------------- gather attention
 struct GatherParams {
@@ -130,7 +150,9 @@ struct GatherParams {
   float* partial;          // [B*Hkv][smax][G][kPartStride]
   int n_sink, n_window;    // explicit plans: list rows inside these ranges are skipped
   const int32_t* lengths;  // [B] or null (n_rows)
-  const int32_t* alt;      // explicit plans over 2-way lists: each entry's other list, or null
+  const int32_t* alt;      // explicit plans over m-way lists: each entry's other lists
+                           // ([entry][alt_w]), or null
+  int alt_w;               // m - 1 (with alt)
   const uint32_t* lmask;   // [B*Hkv][C] head masks of the chosen lists (with alt)
   int C;                   // lists per (request, KV head) (with alt)
   int multi_all;           // explicit plans: segments chosen by two or more heads take one all-heads pass
