@@ -659,21 +659,24 @@ def _timed(args, call, torch, tsa, n_distinct, offset=0, kernels=("gather",)):
     """Warm up, then time args.steps steps (step i runs call(i + offset)).
 
     Eager (default): every step launches directly; on every event-stride-th
-    step the library records HIP events around the launches of `kernels`
-    (the gather-attention kernel, the token indexer scan) on the call's
-    stream, so those kernels are timed inside the timed region. With --graph
-    each distinct step (i mod n_distinct) is captured once into a HIP graph
-    and the timed loop replays the graphs; event records captured in a graph
-    do not bracket the kernels, so they are then timed by an eager pass over
-    the same steps after the timed region.
+    step the library records HIP events around the gather-attention kernel's
+    launch on the call's stream, so that kernel is timed inside the timed
+    region. Other kernels in `kernels` (the token indexer scan) are timed the
+    same way in an eager pass over the same steps after the timed region:
+    event records placed inside the indexer's launch sequence were measured
+    to slow the whole timed region of the token workload (0.20-0.35 ms per
+    step against 0.128 ms without them). With --graph each distinct step
+    (i mod n_distinct) is captured once into a HIP graph and the timed loop
+    replays the graphs; event records captured in a graph do not bracket the
+    kernels, so every kernel is then timed in the eager pass.
     """
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
     which = {"gather": tsa.binding.TIMED_GATHER, "token_scan": tsa.binding.TIMED_TOKEN_SCAN}
 
-    def new_events():
-        return {kn: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for kn in kernels}
+    def new_events(names):
+        return {kn: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for kn in names}
 
     def eager(i, ev):
         for kn, (a, b) in ev.items():
@@ -689,7 +692,9 @@ def _timed(args, call, torch, tsa, n_distinct, offset=0, kernels=("gather",)):
                 call(j + offset)
             graphs.append(g)
         torch.cuda.synchronize()
-    evs = [new_events() for _ in range(args.steps)]
+    inner = [] if graphs else [kn for kn in kernels if kn == "gather"]
+    post = [kn for kn in kernels if kn not in inner]
+    evs = [new_events(inner) for _ in range(args.steps)]
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -706,20 +711,24 @@ def _timed(args, call, torch, tsa, n_distinct, offset=0, kernels=("gather",)):
             call(i + offset)
     t_stop.record()
     torch.cuda.synchronize()
-    res = {"ms_total": t_start.elapsed_time(t_stop), "wall_s": time.perf_counter() - wall0,
-           "kernel_timing": f"HIP events recorded by the library around the kernel's launch on every "
-                            f"{stride}-th step inside the timed region"}
-    if not graphs:
-        evs = [evs[i] for i in timed]
-    else:
+    res = {"ms_total": t_start.elapsed_time(t_stop), "wall_s": time.perf_counter() - wall0}
+    if graphs:
         timed = list(range(min(args.steps, n_distinct)))
+    kernel_ms = {kn: [evs[i][kn][0].elapsed_time(evs[i][kn][1]) for i in timed] for kn in inner}
+    timing = {kn: f"HIP events recorded by the library around the kernel's launch on every {stride}-th step "
+                  "inside the timed region" for kn in inner}
+    if post:
+        pev = {i: new_events(post) for i in timed}
         for i in timed:
-            eager(i, evs[i])
-        evs = evs[:len(timed)]
+            eager(i, pev[i])
         torch.cuda.synchronize()
-        res["kernel_timing"] = "HIP events around each launch in an eager pass after the timed graph region"
-    res["kernel_ms"] = {kn: [ev[kn][0].elapsed_time(ev[kn][1]) for ev in evs] for kn in kernels}
-    res["gather_ms"] = res["kernel_ms"]["gather"]
+        for kn in post:
+            kernel_ms[kn] = [pev[i][kn][0].elapsed_time(pev[i][kn][1]) for i in timed]
+            timing[kn] = ("HIP events recorded by the library around each launch in an eager pass over the same "
+                          "steps after the timed region")
+    res["kernel_ms"] = kernel_ms
+    res["kernel_timing"] = timing
+    res["gather_ms"] = kernel_ms["gather"]
     res["timed_steps"] = timed
     return res
 
@@ -818,7 +827,7 @@ def kernel_rooflines(res, cfg, args, workload):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "traffic_over_algorithmic": round(traffic / bpl, 4) if traffic else None,
                      "algorithmic_bytes_per_launch": round(bpl), "mean_launch_us": round(mean_ms * 1e3, 2),
-                     "launches_timed": len(ms), "timing": res["kernel_timing"]}
+                     "launches_timed": len(ms), "timing": res["kernel_timing"][kn]}
     return out
 
 

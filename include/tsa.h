@@ -563,10 +563,11 @@ enum { TSA_TIMED_GATHER = 0, TSA_TIMED_TOKEN_SCAN = 1 };
 tsa_status tsa_time_next_launch(int32_t kernel, void* ev_start, void* ev_stop);
 
 /* Measurement probe (not part of the decode path): reads `bytes` (a
- * multiple of 16) at device address p once with 16-byte non-temporal loads
- * over every CU, writing one word per wave to sink (device, at least
- * tsa_stream_read_sink_bytes() bytes). Timed by the caller, it gives a
- * measured HBM streaming-read ceiling for the device. */
+ * multiple of 16) at device address p once with 16-byte non-temporal loads,
+ * each workgroup sweeping a contiguous chunk, writing one word per wave to
+ * sink (device, at least tsa_stream_read_sink_bytes() bytes; the XOR of all
+ * sink words is the XOR of the buffer's 32-bit words). Timed by the caller,
+ * it gives a measured HBM streaming-read ceiling for the device. */
 tsa_status tsa_stream_read(const void* p, size_t bytes, uint32_t* sink, size_t sink_bytes, void* stream);
 size_t tsa_stream_read_sink_bytes(void);
 

@@ -297,7 +297,7 @@ __device__ __forceinline__ uint32_t dup_heads(const int32_t* alt_row, int w, int
 
 // DUP: explicit plans over m-way lists, with per-row duplicate head masks
 template <typename T, int G, bool EXPLICIT, bool DUP>
-__global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) void gather_attn_kernel(GatherParams p) {
+__device__ __forceinline__ void gather_attn_body(const GatherParams& p) {
   constexpr int NW = gather_waves<EXPLICIT>();
   __shared__ __align__(16) T qs[G * kHeadDim];
   __shared__ int ids_lds[NW][kSegRows];
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) void gather_attn_
 // attends a token through the lowest of its chosen lists that hold it);
 // every head of a segment then takes its own pass.
 template <typename T, int G, bool DUP>
-__global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(GatherParams p) {
+__device__ __forceinline__ void gather_merge_body(const GatherParams& p) {
   constexpr int NW = kMergeWaves;
   constexpr int kHeadsPerWave = (G + NW - 1) / NW;  // heads each wave merges
   __shared__ __align__(16) T qs[G * kHeadDim];
@@ -663,16 +663,15 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 // of the head are merged through LDS in a fixed order.
 constexpr int kCombineWavesSmall = 16;  // waves per head when the batch is small
 
-template <int G, int GH, int NS, bool EXPLICIT>
-__global__ __launch_bounds__(GH * NS * kWave) void combine_kernel(GatherParams p) {
+// The calling wave's share of query head h's partial states in group bg:
+// records part, part + NS, ... merged into (M, L, O0, O1), lane l holding
+// o[2l], o[2l + 1].
+template <int G, int NS, bool EXPLICIT>
+__device__ __forceinline__ void combine_partials(const GatherParams& p, int bg, int h, int part, float& M, float& L,
+                                                 float& O0, float& O1) {
   constexpr int kU = 8;
-  __shared__ float sm_m[GH][NS], sm_l[GH][NS];
-  __shared__ float2 sm_o[NS > 1 ? GH : 1][NS > 1 ? NS : 1][kWave];
-  const int bg = blockIdx.x / (G / GH);
-  const int b = bg / p.Hkv, g = bg % p.Hkv;
-  const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int hl = wave / NS, part = wave % NS;           // head within the workgroup
-  const int h = (blockIdx.x % (G / GH)) * GH + hl;      // head within the group
+  const int b = bg / p.Hkv;
+  const int lane = lane_id();
   // records: one per segment, or with merged sets (gather_merge_kernel) one
   // per set of kMergeWaves segments at slot set * kMergeWaves, covering the
   // heads of all its segments
@@ -693,7 +692,8 @@ __global__ __launch_bounds__(GH * NS * kWave) void combine_kernel(GatherParams p
     return m;
   };
   const long long rec_stride = static_cast<long long>(rs) * G * kPartStride;  // floats between records
-  float M = kEmptyMax, L = 0.f, O0 = 0.f, O1 = 0.f;
+  M = kEmptyMax;
+  L = O0 = O1 = 0.f;
   const float* base = p.partial + static_cast<long long>(bg) * p.smax * G * kPartStride + h * kPartStride;
   const int n_mine = nrec > part ? (nrec - part + NS - 1) / NS : 0;  // records part + i * NS
   for (int i0 = 0; i0 < n_mine; i0 += kWave) {
@@ -752,6 +752,26 @@ __global__ __launch_bounds__(GH * NS * kWave) void combine_kernel(GatherParams p
       }
     }
   }
+}
+
+// o / l of query head h of group bg (zero when nothing was selected)
+template <int G>
+__device__ __forceinline__ void write_head_out(const GatherParams& p, int bg, int h, float L, float O0, float O1) {
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float* o = p.out + (static_cast<long long>(bg) * G + h) * kHeadDim + lane_id() * 2;
+  *reinterpret_cast<float2*>(o) = make_float2(O0 * inv, O1 * inv);
+}
+
+template <int G, int GH, int NS, bool EXPLICIT>
+__global__ __launch_bounds__(GH * NS * kWave) void combine_kernel(GatherParams p) {
+  __shared__ float sm_m[GH][NS], sm_l[GH][NS];
+  __shared__ float2 sm_o[NS > 1 ? GH : 1][NS > 1 ? NS : 1][kWave];
+  const int bg = blockIdx.x / (G / GH);
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int hl = wave / NS, part = wave % NS;           // head within the workgroup
+  const int h = (blockIdx.x % (G / GH)) * GH + hl;      // head within the group
+  float M, L, O0, O1;
+  combine_partials<G, NS, EXPLICIT>(p, bg, h, part, M, L, O0, O1);
   if constexpr (NS > 1) {
     if (lane == 0) {
       sm_m[hl][part] = M;
@@ -775,9 +795,17 @@ __global__ __launch_bounds__(GH * NS * kWave) void combine_kernel(GatherParams p
       O1 = fmaf(o.y, a, O1);
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* o = p.out + ((static_cast<long long>(b) * p.Hkv + g) * G + h) * kHeadDim + lane * 2;
-  *reinterpret_cast<float2*>(o) = make_float2(O0 * inv, O1 * inv);
+  write_head_out<G>(p, bg, h, L, O0, O1);
+}
+
+template <typename T, int G, bool EXPLICIT, bool DUP>
+__global__ __launch_bounds__(gather_waves<EXPLICIT>() * kWave) void gather_attn_kernel(GatherParams p) {
+  gather_attn_body<T, G, EXPLICIT, DUP>(p);
+}
+
+template <typename T, int G, bool DUP>
+__global__ __launch_bounds__(kMergeWaves * kWave) void gather_merge_kernel(GatherParams p) {
+  gather_merge_body<T, G, DUP>(p);
 }
 
 template <typename T, bool EXPLICIT, bool DUP>

@@ -935,7 +935,7 @@ tsa_status tsa_stream_read(const void* p, size_t bytes, uint32_t* sink, size_t s
 }
 
 size_t tsa_stream_read_sink_bytes(void) {
-  return static_cast<size_t>(stream_read_blocks()) * (512 / 64) * sizeof(uint32_t);
+  return static_cast<size_t>(stream_read_blocks()) * stream_read_waves_per_block() * sizeof(uint32_t);
 }
 
 }  // extern "C"

@@ -237,20 +237,20 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void assign_mfma_kernel(AssignP
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             // insert (acc[i], cr + i) into the list, ordered by s
-            // descending, then id ascending: the carried pair moves down past
-            // every pair after it in that order
-            float v = acc[i];
-            int id = cr + i;
+            // descending, then id ascending: the new id is above every id in
+            // the list, so it goes before the first strictly smaller s, and
+            // the entries from there on move down one place
+            const float v = acc[i];
+            bool gt[M];
 #pragma unroll
-            for (int r = 0; r < M; ++r) {
-              const float tv = bs[j][r];
-              const int ti = bc[j][r];
-              const bool sw = v > tv || (v == tv && id < ti);
-              bs[j][r] = sw ? v : tv;
-              bc[j][r] = sw ? id : ti;
-              v = sw ? tv : v;
-              id = sw ? ti : id;
+            for (int r = 0; r < M; ++r) gt[r] = v > bs[j][r];
+#pragma unroll
+            for (int r = M - 1; r >= 1; --r) {
+              bs[j][r] = gt[r - 1] ? bs[j][r - 1] : (gt[r] ? v : bs[j][r]);
+              bc[j][r] = gt[r - 1] ? bc[j][r - 1] : (gt[r] ? cr + i : bc[j][r]);
             }
+            bs[j][0] = gt[0] ? v : bs[j][0];
+            bc[j][0] = gt[0] ? cr + i : bc[j][0];
           }
         }
       }

@@ -228,6 +228,7 @@ hipError_t launch_fill_i32(int32_t* p, long long n, int32_t value, hipStream_t s
 
 // ---------------------------------------------------------------- probe
 int stream_read_blocks();
+int stream_read_waves_per_block();
 hipError_t launch_stream_read(const void* p, long long n16, uint32_t* sink, hipStream_t s);
 
 }  // namespace tsa

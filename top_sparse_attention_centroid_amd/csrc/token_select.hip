@@ -135,9 +135,8 @@ __global__ __launch_bounds__(kFilterThreads) void token_filter_kernel(TokenSelec
   const int start = c * kTokFilterTile;
   const int n = min(kTokFilterTile, p.N - start);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  int tbin, above;
-  threshold_bin<kFilterThreads>(p.hist + static_cast<long long>(b) * kTokHistBins, p.k, scratch, misc, &tbin,
-                                &above);
+  // the chunk's keys are requested before the histogram is read, so the two
+  // round trips overlap
   const long long base = static_cast<long long>(b) * p.N + start;
   uint32_t kk[PER];
 #pragma unroll
@@ -145,6 +144,9 @@ __global__ __launch_bounds__(kFilterThreads) void token_filter_kernel(TokenSelec
     const int i = j * kFilterThreads + tid;
     kk[j] = p.keys[base + min(i, n - 1)];
   }
+  int tbin, above;
+  threshold_bin<kFilterThreads>(p.hist + static_cast<long long>(b) * kTokHistBins, p.k, scratch, misc, &tbin,
+                                &above);
   uint64_t bal[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
@@ -224,10 +226,30 @@ __global__ __launch_bounds__(kFinalThreads) void token_final_kernel(TokenSelectP
   // through the chunk offsets each time.
   const bool staged = M <= kFinalLdsCands;
   if (staged) {
-    for (int m = tid; m < M; m += kFinalThreads) {
-      const long long ci = cand_index(coff, nf, m);
-      lkey[m] = ck[ci];
-      lid[m] = cid[ci];
+    // every thread's candidates located first, then all their loads in
+    // flight together (a slot past M reloads candidate 0 and is dropped)
+    constexpr int kStagePer = kFinalLdsCands / kFinalThreads;
+    static_assert(kStagePer * kFinalThreads == kFinalLdsCands, "whole rounds of candidates per thread");
+    long long ci[kStagePer];
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) {
+      const int m = tid + u * kFinalThreads;
+      ci[u] = m < M ? cand_index(coff, nf, m) : 0;
+    }
+    uint32_t kv[kStagePer];
+    int32_t iv[kStagePer];
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) {
+      kv[u] = ck[ci[u]];
+      iv[u] = cid[ci[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) {
+      const int m = tid + u * kFinalThreads;
+      if (m < M) {
+        lkey[m] = kv[u];
+        lid[m] = iv[u];
+      }
     }
     __syncthreads();
   }
