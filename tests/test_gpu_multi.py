@@ -257,3 +257,19 @@ def test_regrow_reports_lists_that_do_not_fit():
     torch.cuda.synchronize()
     assert torch.equal(status, torch.ones_like(status))
     assert all(int(t.min()) == -7 and int(t.max()) == -7 for t in out[:3])
+
+
+@pytest.mark.parametrize("m", [2, 3])
+def test_m_way_build_with_a_large_codebook(m):
+    """C above the per-wave counter limit (1024 lists): the posting lists and
+    alt rows come from the one-workgroup CSR kernel."""
+    cfg, p = _problem(batch=1, n_kv_heads=2, n_q_heads=8, n_tokens=2500, n_centroids=1100, top_k=8)
+    announce(f"multi: {m} lists per key, C = 1100")
+    p["keys"] = _m_way_keys(cfg, p["centroids"], m, 110 + m)
+    off, ids, alt = tsa.index_build_multi(p["keys"], p["centroids"], m)
+    torch.cuda.synchronize()
+    r_off, r_ids, r_alt, margin = variants.index_build_multi(f64(p["keys"]), f64(p["centroids"]), m)
+    assert margin >= 1e-3, f"m-th choice margin {margin} too small for an exact comparison"
+    assert np.array_equal(off.cpu().numpy(), r_off)
+    assert np.array_equal(ids.cpu().numpy(), r_ids)
+    assert _same_alt_rows(alt.cpu().numpy(), r_alt, np.ones(r_ids.shape, dtype=bool))
