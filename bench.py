@@ -51,6 +51,9 @@ def parse():
                     help="inverted-index workloads: build the index over the first PREFIX tokens with the "
                          "spare rows as per-list slack, then every step decodes over the growing index and "
                          "appends one new token per request (KV rows + posting list)")
+    ap.add_argument("--slack", type=int, default=-1,
+                    help="with --grow: free entries after every list (-1: the spare entries shared evenly); "
+                         "a small slack makes lists run full, and the regrow that repairs them is timed")
     ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random", "belady"],
                     help="hot-cache workload: replacement policy of RESOLVE (belady = offline, from the "
                          "trace's next-use steps)")
@@ -147,7 +150,7 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
     nq = min(cfg.steps, 64)
     q_all = W.ivf_queries(cfg, p["centroids"], steps=nq)
     m = args.assign
-    slack = (N - prefix) * m // C
+    slack = (N - prefix) * m // C if args.slack < 0 else args.slack
     k_cache, v_cache = p["keys"], p["values"]       # rows >= prefix are rewritten by the appends
     offsets, lens, ids, alt = tsa.index_build_dyn_multi(k_cache, p["centroids"], prefix, m, slack)
     new_k = p["keys"][:, prefix:prefix + total].transpose(0, 1).contiguous()    # [steps][B][Hkv][d]
@@ -162,7 +165,6 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
     else:
         ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX_MULTI, desc, k, m), dtype=torch.uint8,
                          device=dev)
-    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total)]
     torch.cuda.synchronize()
 
     def call(i):
@@ -172,10 +174,8 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
         else:
             tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, k_cache, v_cache, k, lens=lens, alt=alt,
                                  out=out, uniq_out=uniq[i], ws=ws)
-        aev[i][0].record()
         tsa.kv_append(new_k[i], new_v[i], pos[i], p["centroids"], k_cache, v_cache, offsets, lens, ids, alt=alt,
                       status=status[i])
-        aev[i][1].record()
 
     res = _timed(args, call, torch, tsa, n_distinct=total, offset=args.warmup)
     row_bytes = 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
@@ -183,15 +183,56 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
     res["step_bytes"] = [float(x) * row_bytes for x in per_step]
     res.update({"gathered_bytes": float(per_step.sum()) * row_bytes, "queries": B * args.steps,
                 "unique_rows_per_step": float(per_step.mean())})
-    a_ms = [aev[i][0].elapsed_time(aev[i][1]) for i in range(args.warmup, total)]
     st = status[args.warmup:].cpu()
+    # the append kernel, timed after the timed region (event records inside
+    # it slow the whole eager step): the timed steps' appends again, on
+    # copies of the lists (the K/V rows are rewritten with the same values)
+    lens_c, ids_c = lens.clone(), ids.clone()
+    alt_c = None if alt is None else alt.clone()
+    st_c = torch.empty_like(status[0])
+    aev = {}
+    for j in res["timed_steps"]:
+        i = j + args.warmup
+        aev[i] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        tsa.time_next_launch(tsa.binding.TIMED_APPEND, *aev[i])
+        tsa.kv_append(new_k[i], new_v[i], pos[i], p["centroids"], k_cache, v_cache, offsets, lens_c, ids_c,
+                      alt=alt_c, status=st_c)
+    torch.cuda.synchronize()
+    a_ms = [a.elapsed_time(b) for a, b in aev.values()]
+    del lens_c, ids_c, alt_c
+    # repair of the grown index: the same lists laid out again with the
+    # largest slack that fits, its kernel timed with events over five runs
+    # (after the timed region; the arrays are written to a second set)
+    out_arrays = (torch.empty_like(offsets), torch.empty_like(lens), torch.empty_like(ids),
+                  None if alt is None else torch.empty_like(alt))
+    rstat = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    r_ms = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tsa.time_next_launch(tsa.binding.TIMED_REGROW, e0, e1)
+        tsa.index_regrow(offsets, lens, ids, alt, -1, out=out_arrays, status=rstat)
+        torch.cuda.synchronize()
+        r_ms.append(e0.elapsed_time(e1))
+    # every output entry is written once and every valid entry read once
+    # (m ints per entry: the id and its m - 1 other lists)
+    cap = ids.shape[-1]
+    valid = int(lens.clamp(min=0).sum())
+    r_bytes = (B * Hkv * cap + valid) * m * 4
+    r_mean = sum(r_ms) / len(r_ms)
+    res["regrow"] = {"mean_us": round(r_mean * 1e3, 2), "min_us": round(min(r_ms) * 1e3, 2),
+                     "capacity_per_group": cap, "valid_entries": valid, "bytes_per_launch": r_bytes,
+                     "gbps": round(r_bytes / (r_mean * 1e-3) / 1e9, 1), "groups_that_fit": int((rstat == 0).sum()),
+                     "timing": "HIP events recorded by the library around the regrow kernel "
+                               "(tsa_time_next_launch), 5 runs after the timed region"}
     res["append"] = {"prefix_tokens": prefix, "slack_per_list": slack, "lists_per_key": m,
                      "mean_us": round(sum(a_ms) / len(a_ms) * 1e3, 2),
                      "indexed": int((st == 0).sum()), "list_full": int((st == 1).sum()),
                      "bytes_per_launch": B * Hkv * 2 * row_bytes,
                      "refused_appends": "a key whose m lists are not all free joins none (status 1); "
                                         "index_regrow lays the lists out again with fresh free entries",
-                     "timing": "torch events around each kv_append launch on the call's stream"}
+                     "timing": "HIP events recorded by the library around the kv_append kernel "
+                               "(tsa_time_next_launch), the timed steps' appends repeated on copies of the lists "
+                               "after the timed region"}
     return res
 
 
@@ -914,6 +955,8 @@ def record_traffic(args):
 def workload_name(cfg, args):
     workload = cfg.name + (f"+grow-from-{args.grow}" if args.grow else "")
     if cfg.kind == "ivf":
+        if args.grow and args.slack >= 0:
+            workload += f"+slack{args.slack}"
         if args.similarity != "dot":
             workload += f"+{args.similarity}"
         if args.sink or args.window:
@@ -1035,7 +1078,7 @@ def gpu_run(args, torch):
         "counter_kernels": counter_kernels(res, cfg, args),
     }
     for key in ("index_build_ms", "unique_rows_per_step", "misses_per_step", "miss_rate_steady",
-                "fetched_bytes", "resolve", "append", "layer_group", "indexer_bytes_per_step"):
+                "fetched_bytes", "resolve", "append", "regrow", "layer_group", "indexer_bytes_per_step"):
         if key in res:
             line[key] = res[key]
     if "cpu_sample" in res:

@@ -557,9 +557,12 @@ tsa_status tsa_host_free(void* host_ptr);
 tsa_status tsa_time_next_gather(void* ev_start, void* ev_stop);
 
 /* The same for a chosen kernel: TSA_TIMED_GATHER (the gather-attention
- * kernel, as tsa_time_next_gather) or TSA_TIMED_TOKEN_SCAN (the indexer scan
- * of the next tsa_token_decode). One-shot per kernel. */
-enum { TSA_TIMED_GATHER = 0, TSA_TIMED_TOKEN_SCAN = 1 };
+ * kernel, as tsa_time_next_gather), TSA_TIMED_TOKEN_SCAN (the indexer scan
+ * of the next tsa_token_decode), TSA_TIMED_APPEND (the kernel of the next
+ * tsa_kv_append / tsa_kv_append_multi) or TSA_TIMED_REGROW (the kernel of
+ * the next tsa_index_regrow). One-shot per kernel; a call that fails
+ * validation before its launch leaves the events armed. */
+enum { TSA_TIMED_GATHER = 0, TSA_TIMED_TOKEN_SCAN = 1, TSA_TIMED_APPEND = 2, TSA_TIMED_REGROW = 3 };
 tsa_status tsa_time_next_launch(int32_t kernel, void* ev_start, void* ev_stop);
 
 /* Measurement probe (not part of the decode path): reads `bytes` (a

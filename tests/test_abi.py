@@ -221,6 +221,11 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
     # timing hook needs both events
     assert lib.tsa_time_next_gather(fake, None) == B.TSA_ERR_INVALID_ARG
     assert lib.tsa_time_next_gather(None, None) == B.TSA_OK
+    for kind in (B.TIMED_GATHER, B.TIMED_TOKEN_SCAN, B.TIMED_APPEND, B.TIMED_REGROW):
+        assert lib.tsa_time_next_launch(kind, None, fake) == B.TSA_ERR_INVALID_ARG
+        assert lib.tsa_time_next_launch(kind, None, None) == B.TSA_OK     # disarms
+    assert lib.tsa_time_next_launch(4, None, None) == B.TSA_ERR_INVALID_ARG
+    assert b"unknown timed kernel" in lib.tsa_last_error()
 
 
 def test_binding_refuses_host_tensors():

@@ -700,12 +700,13 @@ def time_next_gather(ev_start: torch.cuda.Event, ev_stop: torch.cuda.Event):
     _check(load().tsa_time_next_gather(_P(ev_start.cuda_event), _P(ev_stop.cuda_event)))
 
 
-TIMED_GATHER, TIMED_TOKEN_SCAN = 0, 1
+TIMED_GATHER, TIMED_TOKEN_SCAN, TIMED_APPEND, TIMED_REGROW = 0, 1, 2, 3
 
 
 def time_next_launch(kernel: int, ev_start: torch.cuda.Event, ev_stop: torch.cuda.Event):
-    """Have the next launch of `kernel` (TIMED_GATHER or TIMED_TOKEN_SCAN) by
-    this thread record the two events around itself (on that call's stream)."""
+    """Have the next launch of `kernel` (TIMED_GATHER, TIMED_TOKEN_SCAN,
+    TIMED_APPEND or TIMED_REGROW) by this thread record the two events around
+    itself (on that call's stream)."""
     for ev in (ev_start, ev_stop):
         if not ev.cuda_event:
             ev.record()

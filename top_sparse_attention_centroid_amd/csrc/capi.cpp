@@ -22,6 +22,20 @@ thread_local hipEvent_t g_gather_ev0 = nullptr;
 thread_local hipEvent_t g_gather_ev1 = nullptr;
 thread_local hipEvent_t g_scan_ev0 = nullptr;   // token indexer scan (tsa_time_next_launch)
 thread_local hipEvent_t g_scan_ev1 = nullptr;
+thread_local hipEvent_t g_append_ev[2] = {nullptr, nullptr};   // kv_append (tsa_time_next_launch)
+thread_local hipEvent_t g_regrow_ev[2] = {nullptr, nullptr};   // regrow (tsa_time_next_launch)
+
+// Records the one-shot event pair `ev` (if set) around one launch on s.
+template <typename Launch>
+hipError_t launch_between(hipEvent_t (&ev)[2], hipStream_t s, Launch&& launch) {
+  hipEvent_t e0 = ev[0], e1 = ev[1];
+  ev[0] = ev[1] = nullptr;
+  hipError_t e;
+  if (e0 && (e = hipEventRecord(e0, s)) != hipSuccess) return e;
+  if ((e = launch()) != hipSuccess) return e;
+  if (e1 && (e = hipEventRecord(e1, s)) != hipSuccess) return e;
+  return hipSuccess;
+}
 
 tsa_status fail(tsa_status s, const char* fmt, ...) {
   char buf[512];
@@ -556,7 +570,8 @@ tsa_status tsa_kv_append_multi(const tsa_ivf_desc* desc, int32_t m, const void* 
                   d.batch, d.n_tokens, d.n_kv_heads, d.n_centroids};
   ap.m = m;
   ap.alt = m > 1 ? alt : nullptr;
-  hipError_t e = launch_kv_append(ap, d.dtype, as_stream(stream));
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = launch_between(g_append_ev, s, [&] { return launch_kv_append(ap, d.dtype, s); });
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return ok();
 }
@@ -584,7 +599,8 @@ tsa_status tsa_index_regrow(const tsa_ivf_desc* desc, int32_t m, const int32_t* 
   RegrowParams rp{offsets, lens, ids, m > 1 ? alt : nullptr, offsets_out, lens_out, ids_out,
                   m > 1 ? alt_out : nullptr, status, desc->batch, desc->n_kv_heads, desc->n_centroids,
                   desc->n_tokens * m, m, slack};
-  hipError_t e = launch_regrow(rp, as_stream(stream));
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = launch_between(g_regrow_ev, s, [&] { return launch_regrow(rp, s); });
   if (e != hipSuccess) return hip_fail(e, "regrow launch");
   return ok();
 }
@@ -918,6 +934,14 @@ tsa_status tsa_time_next_launch(int32_t kernel, void* ev_start, void* ev_stop) {
     case TSA_TIMED_TOKEN_SCAN:
       g_scan_ev0 = static_cast<hipEvent_t>(ev_start);
       g_scan_ev1 = static_cast<hipEvent_t>(ev_stop);
+      return ok();
+    case TSA_TIMED_APPEND:
+      g_append_ev[0] = static_cast<hipEvent_t>(ev_start);
+      g_append_ev[1] = static_cast<hipEvent_t>(ev_stop);
+      return ok();
+    case TSA_TIMED_REGROW:
+      g_regrow_ev[0] = static_cast<hipEvent_t>(ev_start);
+      g_regrow_ev[1] = static_cast<hipEvent_t>(ev_stop);
       return ok();
   }
   return fail(TSA_ERR_INVALID_ARG, "unknown timed kernel %d", kernel);

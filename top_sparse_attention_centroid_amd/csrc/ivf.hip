@@ -924,45 +924,39 @@ __global__ __launch_bounds__(NW * kWave) void ivf_select_kernel(SelectParams p) 
 // each of the M lists (with its other lists in alt) when every one of them
 // still has a free entry, else into none.
 // ============================================================================
-constexpr int kAppendWaves = 4;
-constexpr int kAppendU = 4;
+// One workgroup per (request, KV head); its NW waves split the codebook,
+// append_unroll<T>() centroids per lane group in flight. With only B * Hkv
+// workgroups the scan is bound by loads in flight per CU, so small batches
+// with large codebooks take up to 16 waves. The position is checked only
+// after the scan, so that its load overlaps the codebook's.
+template <typename T>
+constexpr int append_unroll() { return sizeof(T) == 2 ? 16 : 8; }
 
-template <typename T, int M>
-__global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendParams p) {
-  __shared__ float wbest[kAppendWaves][M];
-  __shared__ int wbestc[kAppendWaves][M];
+template <typename T, int M, int NW>
+__global__ __launch_bounds__(NW * kWave) void kv_append_kernel(AppendParams p) {
+  constexpr int U = append_unroll<T>();
+  __shared__ float wbest[NW][M];
+  __shared__ int wbestc[NW][M];
   const int bg = blockIdx.x;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave, r = lane >> 4, e = lane & 15;
   const int pos = p.pos[b];
   int32_t* st = p.status ? p.status + bg : nullptr;
-  if (pos < 0 || pos >= p.N) {
-    if (st && tid == 0) *st = 2;
-    return;
-  }
   const long long src = static_cast<long long>(bg) * kHeadDim + e * 8;
-  if (wave == 0 && r == 0) {
-    const long long dst = ((static_cast<long long>(b) * p.N + pos) * p.Hkv + g) * kHeadDim + e * 8;
-    Raw8<T> kr, vr;
-    kr.load(static_cast<const T*>(p.new_k) + src);
-    vr.load(static_cast<const T*>(p.new_v) + src);
-    *reinterpret_cast<Raw8<T>*>(static_cast<T*>(p.k_cache) + dst) = kr;
-    *reinterpret_cast<Raw8<T>*>(static_cast<T*>(p.v_cache) + dst) = vr;
-  }
   QFrag<T> kq;
   kq.load(static_cast<const T*>(p.new_k) + src);
   const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
                 static_cast<long long>(g) * p.C * kHeadDim + e * 8;
   TopM<M> top;  // this lane group's M nearest, by (distance, centroid)
   top.init();
-  constexpr int kStep = kAppendWaves * kAppendU * 4;
-  for (int c0 = wave * kAppendU * 4; c0 < p.C; c0 += kStep) {
-    Raw8<T> raw[kAppendU];
+  constexpr int kStep = NW * U * 4;
+  for (int c0 = wave * U * 4; c0 < p.C; c0 += kStep) {
+    Raw8<T> raw[U];
 #pragma unroll
-    for (int u = 0; u < kAppendU; ++u)
+    for (int u = 0; u < U; ++u)
       raw[u].load(cb + static_cast<long long>(min(c0 + u * 4 + r, p.C - 1)) * kHeadDim);
 #pragma unroll
-    for (int u = 0; u < kAppendU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int c = c0 + u * 4 + r;
       float x[8];
       raw[u].widen(x);
@@ -994,9 +988,21 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendP
       wbestc[wave][i] = top.c[i];
     }
   }
+  if (pos < 0 || pos >= p.N) {  // uniform: nothing is written but the status
+    if (st && tid == 0) *st = 2;
+    return;
+  }
+  if (wave == 0 && r == 0) {
+    const long long dst = ((static_cast<long long>(b) * p.N + pos) * p.Hkv + g) * kHeadDim + e * 8;
+    Raw8<T> kr, vr;
+    kr.load(static_cast<const T*>(p.new_k) + src);
+    vr.load(static_cast<const T*>(p.new_v) + src);
+    *reinterpret_cast<Raw8<T>*>(static_cast<T*>(p.k_cache) + dst) = kr;
+    *reinterpret_cast<Raw8<T>*>(static_cast<T*>(p.v_cache) + dst) = vr;
+  }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < kAppendWaves; ++w)
+    for (int w = 1; w < NW; ++w)
 #pragma unroll
       for (int i = 0; i < M; ++i) top.push(wbest[w][i], wbestc[w][i]);
     // the key joins its M lists only if every one has a free entry
@@ -1036,6 +1042,7 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendP
 // from the front of the old range, or writes -1 past the valid entries.
 // When the valid entries plus the free ones exceed the capacity, nothing is
 // written but the status.
+template <int W>  // m - 1: the alt entries per list entry
 __global__ __launch_bounds__(256) void regrow_kernel(RegrowParams p) {
   __shared__ int noff[kMaxCentroids + 1];
   __shared__ int soff[kMaxCentroids];
@@ -1043,7 +1050,7 @@ __global__ __launch_bounds__(256) void regrow_kernel(RegrowParams p) {
   __shared__ int scratch[8];
   const int bg = blockIdx.y;
   const int tid = threadIdx.x;
-  const int C = p.C, w = p.m - 1;
+  const int C = p.C;
   const long long cap = p.cap;
   const int32_t* off = p.offsets + static_cast<long long>(bg) * (C + 1);
   const int32_t* lens = p.lens + static_cast<long long>(bg) * C;
@@ -1082,30 +1089,69 @@ __global__ __launch_bounds__(256) void regrow_kernel(RegrowParams p) {
   }
   const int32_t* ids = p.ids + static_cast<long long>(bg) * cap;
   int32_t* ids_out = p.ids_out + static_cast<long long>(bg) * cap;
-  const int32_t* alt = w > 0 ? p.alt + static_cast<long long>(bg) * cap * w : nullptr;
-  int32_t* alt_out = w > 0 ? p.alt_out + static_cast<long long>(bg) * cap * w : nullptr;
   const long long e_lo = static_cast<long long>(blockIdx.x) * kRegrowChunk;
   const long long e_hi = min(cap, e_lo + kRegrowChunk);
-  for (long long e = e_lo + tid; e < e_hi; e += 256) {
-    int src = -1;
-    if (e < carry) {
-      int lo = 0, hi = C - 1;  // the last list whose new offset is <= e
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (noff[mid] <= e) lo = mid;
-        else hi = mid - 1;
-      }
-      const int j = static_cast<int>(e - noff[lo]);
-      if (j < nlen[lo]) src = soff[lo] + j;
+  // every entry's source first, then all loads, then all stores, so that
+  // the loads of a thread's entries are in flight together
+  // list of each entry: the last list whose new offset is <= the entry, by
+  // a branch-free binary search run for all of a thread's entries in step
+  int top_step = 1;
+  while (top_step * 2 < C) top_step *= 2;
+  int li[kRegrowPer];
+#pragma unroll
+  for (int i = 0; i < kRegrowPer; ++i) li[i] = 0;
+  for (int step = top_step; step > 0; step >>= 1) {
+#pragma unroll
+    for (int i = 0; i < kRegrowPer; ++i) {
+      const long long e = e_lo + tid + i * 256;
+      const int cand = li[i] + step;
+      if (cand < C && noff[cand] <= e) li[i] = cand;
     }
-    ids_out[e] = src >= 0 ? ids[src] : -1;
-    for (int q = 0; q < w; ++q) alt_out[e * w + q] = src >= 0 ? alt[static_cast<long long>(src) * w + q] : -1;
+  }
+  int src[kRegrowPer];
+#pragma unroll
+  for (int i = 0; i < kRegrowPer; ++i) {
+    const long long e = e_lo + tid + i * 256;
+    src[i] = -1;
+    if (e < e_hi && e < carry) {
+      const int j = static_cast<int>(e - noff[li[i]]);
+      if (j < nlen[li[i]]) src[i] = soff[li[i]] + j;
+    }
+  }
+  int v[kRegrowPer];
+#pragma unroll
+  for (int i = 0; i < kRegrowPer; ++i) v[i] = src[i] >= 0 ? ids[src[i]] : -1;
+#pragma unroll
+  for (int i = 0; i < kRegrowPer; ++i) {
+    const long long e = e_lo + tid + i * 256;
+    if (e < e_hi) ids_out[e] = v[i];
+  }
+  if constexpr (W > 0) {
+    const int32_t* alt = p.alt + static_cast<long long>(bg) * cap * W;
+    int32_t* alt_out = p.alt_out + static_cast<long long>(bg) * cap * W;
+    int a[kRegrowPer][W];
+#pragma unroll
+    for (int i = 0; i < kRegrowPer; ++i)
+#pragma unroll
+      for (int q = 0; q < W; ++q) a[i][q] = src[i] >= 0 ? alt[static_cast<long long>(src[i]) * W + q] : -1;
+#pragma unroll
+    for (int i = 0; i < kRegrowPer; ++i) {
+      const long long e = e_lo + tid + i * 256;
+      if (e < e_hi)
+#pragma unroll
+        for (int q = 0; q < W; ++q) alt_out[e * W + q] = a[i][q];
+    }
   }
 }
 
 hipError_t launch_regrow(const RegrowParams& p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((p.cap + kRegrowChunk - 1) / kRegrowChunk), p.B * p.Hkv);
-  hipLaunchKernelGGL(regrow_kernel, grid, dim3(256), 0, s, p);
+  switch (p.m) {
+    case 1: hipLaunchKernelGGL(regrow_kernel<0>, grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL(regrow_kernel<1>, grid, dim3(256), 0, s, p); break;
+    case 3: hipLaunchKernelGGL(regrow_kernel<2>, grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL(regrow_kernel<3>, grid, dim3(256), 0, s, p); break;
+  }
   return hipGetLastError();
 }
 
@@ -1139,22 +1185,32 @@ hipError_t launch_assign(const AssignParams& p, int dtype, float* norms, hipStre
   return hipGetLastError();
 }
 
+template <typename T, int NW>
+static void append_dispatch(const AppendParams& p, hipStream_t s) {
+  const dim3 grid(p.B * p.Hkv), block(NW * kWave);
+  switch (p.m) {
+    case 1: hipLaunchKernelGGL((kv_append_kernel<T, 1, NW>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((kv_append_kernel<T, 2, NW>), grid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL((kv_append_kernel<T, 3, NW>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((kv_append_kernel<T, 4, NW>), grid, block, 0, s, p); break;
+  }
+}
+
 hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t s) {
-  const dim3 grid(p.B * p.Hkv), block(kAppendWaves * kWave);
+  // A wave takes append_unroll<T>() * 4 centroids per pass. While the
+  // workgroups alone do not fill the CUs, enough waves for about one pass
+  // over the codebook (16 at most); otherwise 4.
+  const int per_wave = (dtype == kBF16 ? append_unroll<bf16_t>() : append_unroll<float>()) * 4;
+  const bool few = static_cast<long long>(p.B) * p.Hkv < 256;
+  const int nw = !few || p.C <= 4 * per_wave ? 4 : (p.C <= 8 * per_wave ? 8 : 16);
   if (dtype == kBF16) {
-    switch (p.m) {
-      case 1: hipLaunchKernelGGL((kv_append_kernel<bf16_t, 1>), grid, block, 0, s, p); break;
-      case 2: hipLaunchKernelGGL((kv_append_kernel<bf16_t, 2>), grid, block, 0, s, p); break;
-      case 3: hipLaunchKernelGGL((kv_append_kernel<bf16_t, 3>), grid, block, 0, s, p); break;
-      default: hipLaunchKernelGGL((kv_append_kernel<bf16_t, 4>), grid, block, 0, s, p); break;
-    }
+    if (nw == 16) append_dispatch<bf16_t, 16>(p, s);
+    else if (nw == 8) append_dispatch<bf16_t, 8>(p, s);
+    else append_dispatch<bf16_t, 4>(p, s);
   } else {
-    switch (p.m) {
-      case 1: hipLaunchKernelGGL((kv_append_kernel<float, 1>), grid, block, 0, s, p); break;
-      case 2: hipLaunchKernelGGL((kv_append_kernel<float, 2>), grid, block, 0, s, p); break;
-      case 3: hipLaunchKernelGGL((kv_append_kernel<float, 3>), grid, block, 0, s, p); break;
-      default: hipLaunchKernelGGL((kv_append_kernel<float, 4>), grid, block, 0, s, p); break;
-    }
+    if (nw == 16) append_dispatch<float, 16>(p, s);
+    else if (nw == 8) append_dispatch<float, 8>(p, s);
+    else append_dispatch<float, 4>(p, s);
   }
   return hipGetLastError();
 }

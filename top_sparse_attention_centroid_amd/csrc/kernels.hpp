@@ -130,6 +130,7 @@ struct RegrowParams {
   int B, Hkv, C, cap, m, slack;
 };
 constexpr int kRegrowChunk = 4096;   // output entries per regrow workgroup
+constexpr int kRegrowPer = kRegrowChunk / 256;   // output entries per regrow thread
 hipError_t launch_regrow(const RegrowParams& p, hipStream_t s);
 
 // --------------------------------------------------------- gather attention
