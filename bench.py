@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--slack", type=int, default=-1,
                     help="with --grow: free entries after every list (-1: the spare entries shared evenly); "
                          "a small slack makes lists run full, and the regrow that repairs them is timed")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "staged", "fused", "split"],
+                    help="inverted-index decode: the library's choice, the staged launches, the fused single "
+                         "launch or the split per-head launches (the last two: small plain decodes)")
     ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random", "belady"],
                     help="hot-cache workload: replacement policy of RESOLVE (belady = offline, from the "
                          "trace's next-use steps)")
@@ -105,15 +108,56 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+# the library's automatic choice of an inverted-index decode's launches
+FUSED_MAX_HEADS, FUSED_MAX_ROWS, FUSED_MAX_CODEBOOK = 256, 512, 65536
+HEAD_MAX_C, HEAD_MAX_K = 1024, 64
+SMALL_BATCH_GROUPS = 128
+
+
+def ivf_schedule(cfg, args):
+    """The launches libtsa runs this inverted-index decode with: "fused" (one
+    workgroup per query head, one launch) when every head's work fits one CU,
+    "split" (scoring, shares of every head's rows, combine) for other small
+    bf16 batches, "staged" (scoring and plan, gather, combine) otherwise;
+    only plain decodes (one list per key, no sink or window rows, C <= 1024,
+    k <= 64) take the per-head ones. None for other workloads."""
+    if cfg.kind != "ivf":
+        return None
+    schedule = getattr(args, "schedule", "auto")
+    if schedule != "auto":
+        return schedule
+    plain = (getattr(args, "assign", 1) <= 1 and getattr(args, "sink", 0) == 0 and getattr(args, "window", 0) == 0
+             and cfg.n_centroids <= HEAD_MAX_C and cfg.top_k <= HEAD_MAX_K)
+    if not plain:
+        return "staged"
+    rows = cfg.top_k * cfg.n_tokens // cfg.n_centroids
+    codebook = cfg.n_centroids * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
+    if cfg.batch * cfg.n_q_heads <= FUSED_MAX_HEADS and rows <= FUSED_MAX_ROWS and codebook <= FUSED_MAX_CODEBOOK:
+        return "fused"
+    if cfg.dtype == "bf16" and cfg.batch * cfg.n_kv_heads < SMALL_BATCH_GROUPS:
+        return "split"
+    return "staged"
+
+
 def gather_kernel_name(cfg, args) -> str:
-    """The gather kernel libtsa launches for this workload: merged sets of
-    plan segments for inverted-index batches of at least 128 bf16
-    (request, KV head) groups with up to 4 query heads per KV head; one wave
-    per segment (or per row-list segment) otherwise."""
+    """The kernel libtsa runs the gather in for this workload: the per-head
+    decode kernel under the fused and split schedules; under the staged one,
+    merged sets of plan segments for inverted-index batches of at least 128
+    bf16 (request, KV head) groups with up to 4 query heads per KV head, one
+    wave per segment (or per row-list segment) otherwise."""
+    if ivf_schedule(cfg, args) in ("fused", "split"):
+        return "ivf_head_kernel"
     groups = cfg.batch * cfg.n_kv_heads
-    if cfg.kind == "ivf" and groups >= 128 and cfg.dtype == "bf16" and cfg.group <= 4:
+    if cfg.kind == "ivf" and groups >= SMALL_BATCH_GROUPS and cfg.dtype == "bf16" and cfg.group <= 4:
         return "gather_merge_kernel"
     return "gather_attn_kernel"
+
+
+def codebook_bytes(cfg) -> int:
+    """Bytes of the centroids one decode step scores (every KV head's codebook
+    of every request; a shared codebook counts once per request here, as
+    each request's scoring reads it)."""
+    return cfg.batch * cfg.n_kv_heads * cfg.n_centroids * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
 
 
 def measured_traffic(workload: str, kernel: str):
@@ -160,20 +204,20 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
     out = torch.empty((B, Hq, cfg.head_dim), dtype=torch.float32, device=dev)
     uniq = torch.empty((total, B, Hkv), dtype=torch.int32, device=dev)
     desc = tsa.binding.ivf_desc(k_cache, p["centroids"], Hq)
-    if m == 1:
-        ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
+    if m == 1:  # the options' workspace covers the plain decode too
+        ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX, desc, k), dtype=torch.uint8, device=dev)
     else:
         ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX_MULTI, desc, k, m), dtype=torch.uint8,
                          device=dev)
     torch.cuda.synchronize()
 
     def call(i):
-        if m == 1:
+        if m == 1 and args.schedule == "auto":
             tsa.sparse_decode_dyn(q_all[i % nq], p["centroids"], offsets, lens, ids, k_cache, v_cache, k,
                                   out=out, uniq_out=uniq[i], ws=ws)
         else:
             tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, k_cache, v_cache, k, lens=lens, alt=alt,
-                                 out=out, uniq_out=uniq[i], ws=ws)
+                                 out=out, uniq_out=uniq[i], ws=ws, schedule=args.schedule)
         tsa.kv_append(new_k[i], new_v[i], pos[i], p["centroids"], k_cache, v_cache, offsets, lens, ids, alt=alt,
                       status=status[i])
 
@@ -183,6 +227,8 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
     res["step_bytes"] = [float(x) * row_bytes for x in per_step]
     res.update({"gathered_bytes": float(per_step.sum()) * row_bytes, "queries": B * args.steps,
                 "unique_rows_per_step": float(per_step.mean())})
+    if ivf_schedule(cfg, args) == "fused":
+        res["gather_launch_bytes"] = [x + codebook_bytes(cfg) for x in res["step_bytes"]]
     st = status[args.warmup:].cpu()
     # the append kernel, timed after the timed region (event records inside
     # it slow the whole eager step): the timed steps' appends again, on
@@ -258,7 +304,8 @@ def bench_ivf(args, cfg, torch, tsa, W):
     desc = tsa.binding.ivf_desc(p["keys"], p["centroids"], Hq)
     ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
 
-    variant = args.similarity != "dot" or args.sink > 0 or args.window > 0 or alt is not None
+    variant = (args.similarity != "dot" or args.sink > 0 or args.window > 0 or alt is not None
+               or args.schedule != "auto")
     if variant:
         if alt is not None:
             need = tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX_MULTI, desc, k, args.assign)
@@ -270,7 +317,7 @@ def bench_ivf(args, cfg, torch, tsa, W):
         if variant:
             tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
                                  similarity=args.similarity, n_sink=args.sink, n_window=args.window, alt=alt,
-                                 out=out, uniq_out=uniq[i % nq], ws=ws)
+                                 out=out, uniq_out=uniq[i % nq], ws=ws, schedule=args.schedule)
         else:
             tsa.sparse_decode(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
                               out=out, uniq_out=uniq[i % nq], ws=ws)
@@ -288,6 +335,9 @@ def bench_ivf(args, cfg, torch, tsa, W):
     row_bytes = 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
     res.update({"gathered_bytes": rows * row_bytes, "queries": B * args.steps, "index_build_ms": index_ms,
                 "unique_rows_per_step": rows / args.steps})
+    if ivf_schedule(cfg, args) == "fused":
+        # the fused kernel also scores the codebook: its bytes once per group
+        res["gather_launch_bytes"] = [x + codebook_bytes(cfg) for x in res["step_bytes"]]
     if args.cpu_seconds > 0 and not variant:
         res["cpu_sample"] = ("ivf",) + cpu_sample_ivf(cfg, p, q_all, torch)
     return res
@@ -858,7 +908,8 @@ def kernel_rooflines(res, cfg, args, workload):
     that were timed) over the mean event-timed launch duration."""
     out = {}
     for kn, ms in res["kernel_ms"].items():
-        step_bytes = res["step_bytes"] if kn == "gather" else res["kernel_step_bytes"][kn]
+        step_bytes = res.get("gather_launch_bytes", res["step_bytes"]) if kn == "gather" else \
+            res["kernel_step_bytes"][kn]
         name = gather_kernel_name(cfg, args) if kn == "gather" else KERNEL_NAMES[kn]
         bpl = _mean(step_bytes[i] for i in res["timed_steps"])
         mean_ms = _mean(ms)
@@ -876,7 +927,7 @@ def counter_kernels(res, cfg, args):
     """Mean algorithmic bytes per launch over every timed step, for each kernel
     a counter pass attributes bytes to (with --warmup 0 these are all of the
     run's launches of that kernel)."""
-    out = {gather_kernel_name(cfg, args): _mean(res["step_bytes"])}
+    out = {gather_kernel_name(cfg, args): _mean(res.get("gather_launch_bytes", res["step_bytes"]))}
     for kn, sb in res.get("kernel_step_bytes", {}).items():
         out[KERNEL_NAMES[kn]] = _mean(sb)
     for kn, sb in res.get("counter_bytes", {}).items():
@@ -963,6 +1014,8 @@ def workload_name(cfg, args):
             workload += f"+sink{args.sink}+window{args.window}"
         if args.assign > 1:
             workload += f"+{args.assign}-lists-per-key"
+        if args.schedule != "auto":
+            workload += f"+{args.schedule}"
     if cfg.kind == "cache" and (cfg.popularity_sd or cfg.recency):
         workload += f"+popularity{cfg.popularity_sd:g}+recency{cfg.recency:g}"
     if cfg.kind == "cache" and args.policy != "lru":

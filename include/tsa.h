@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 1
+#define TSA_ABI_VERSION 2
 
 /* Size of the static device scratch of tsa_sparse_decode_noalloc. */
 #define TSA_NOALLOC_SCRATCH_BYTES (64u << 20)
@@ -353,6 +353,7 @@ tsa_status tsa_index_regrow(const tsa_ivf_desc* desc, int32_t m, const int32_t* 
  *                     lowest-numbered of them)
  *   opts->alt         (device) int32 [B][Hkv][N*m][m-1] from the m-way build,
  *                     required when assign_per_key is 2 or more
+ *   opts->schedule    tsa_schedule (0: AUTO)
  *   The attended set of a head is the union of its chosen lists' rows and
  *   the two ranges; a row in both is attended once. rows_out and uniq_out
  *   count list entries only. Workspace:
@@ -362,6 +363,29 @@ tsa_status tsa_index_regrow(const tsa_ivf_desc* desc, int32_t m, const int32_t* 
  * ---------------------------------------------------------------------- */
 typedef enum tsa_similarity { TSA_SIM_DOT = 0, TSA_SIM_COSINE = 1 } tsa_similarity;
 
+/* How the launches of one decode are laid out (the results are the same
+ * lists, row counts and, to rounding, outputs):
+ *   TSA_SCHED_AUTO    the library's choice (below)
+ *   TSA_SCHED_STAGED  scoring, top-k + gather plan per (request, KV head),
+ *                     gather over plan segments, combine
+ *   TSA_SCHED_FUSED   one workgroup per (request, query head) scores, selects
+ *                     and attends in one launch
+ *   TSA_SCHED_SPLIT   scoring, then S workgroups per (request, query head)
+ *                     each select the head's lists and attend a share of its
+ *                     rows, then combine (bf16 only)
+ * FUSED and SPLIT take plain list decodes only: one list per token, no sink
+ * or window, C <= 1024, k <= 64 (else TSA_ERR_UNSUPPORTED). AUTO takes FUSED
+ * when every head's work fits one CU (B * Hq <= 256, about k * N / C <= 512
+ * rows a head, a codebook of at most 64 KiB per KV head), else SPLIT for bf16
+ * batches of fewer than 128 (request, KV head) groups, else STAGED.
+ * tsa_sparse_decode and tsa_sparse_decode_dyn use AUTO. */
+typedef enum tsa_schedule {
+  TSA_SCHED_AUTO = 0,
+  TSA_SCHED_STAGED = 1,
+  TSA_SCHED_FUSED = 2,
+  TSA_SCHED_SPLIT = 3
+} tsa_schedule;
+
 typedef struct tsa_decode_opts {
   int32_t similarity;       /* tsa_similarity                               */
   int32_t n_sink;           /* leading tokens always attended               */
@@ -370,6 +394,7 @@ typedef struct tsa_decode_opts {
   const int32_t* lengths;   /* device [B] or NULL                           */
   const int32_t* lens;      /* device [B][Hkv][C] or NULL                   */
   const int32_t* alt;       /* device [B][Hkv][N*m][m-1] or NULL            */
+  int32_t schedule;         /* tsa_schedule                                 */
 } tsa_decode_opts;
 
 tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts* opts, const void* q,

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tsa_abi_version() == 1
+    assert lib.tsa_abi_version() == B.ABI_VERSION == 2
     assert lib.tsa_status_str(B.TSA_ERR_WORKSPACE) == b"TSA_ERR_WORKSPACE"
     assert lib.tsa_status_str(99) == b"TSA_ERR_UNKNOWN"
 
@@ -138,6 +138,32 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
         st = lib.tsa_sparse_decode_ex(ctypes.byref(d), ctypes.byref(opts), fake, fake, fake, fake, fake, fake, 4,
                                       fake, None, None, None, fake, ws_ex, None)
         assert st == B.TSA_ERR_INVALID_ARG
+    # schedule: an unknown value; the fused schedule for decodes it does not take
+    for bad in (-1, 4):
+        opts = B.DecodeOpts(0, 0, 0, 0, None, None, None, bad)
+        st = lib.tsa_sparse_decode_ex(ctypes.byref(d), ctypes.byref(opts), fake, fake, fake, fake, fake, fake, 4,
+                                      fake, None, None, None, fake, ws_ex, None)
+        assert st == B.TSA_ERR_INVALID_ARG and b"unknown schedule" in lib.tsa_last_error()
+    d_f32 = B.IvfDesc(2, 100, 2, 8, 128, 8, 1, B.TSA_F32)
+    opts = B.DecodeOpts(0, 0, 0, 0, None, None, None, B.SCHEDULE["split"])
+    st = lib.tsa_sparse_decode_ex(ctypes.byref(d_f32), ctypes.byref(opts), fake, fake, fake, fake, fake, fake, 4,
+                                  fake, None, None, None, fake, 1 << 30, None)
+    assert st == B.TSA_ERR_UNSUPPORTED and b"bf16" in lib.tsa_last_error()
+    fused = B.SCHEDULE["fused"]
+    d_wide = B.IvfDesc(2, 5000, 2, 8, 128, 2000, 1, B.TSA_BF16)
+    ws_wide = B.workspace_bytes(B.OP_SPARSE_DECODE_EX, d_wide, 65)
+    for desc, opts, kk in ((d, B.DecodeOpts(0, 4, 0, 0, None, None, None, fused), 4),     # sink rows
+                           (d, B.DecodeOpts(0, 0, 2, 0, None, None, None, fused), 4),     # window rows
+                           (d, B.DecodeOpts(0, 0, 0, 2, None, None, 0x30000, fused), 4),  # two lists per key
+                           (d_wide, B.DecodeOpts(0, 0, 0, 0, None, None, None, fused), 4),    # C > 1024
+                           (d_wide, B.DecodeOpts(0, 0, 0, 0, None, None, None, fused), 65)):  # k > 64
+        st = lib.tsa_sparse_decode_ex(ctypes.byref(desc), ctypes.byref(opts), fake, fake, fake, fake, fake, fake,
+                                      kk, fake, None, None, None, fake, ws_wide, None)
+        assert st == B.TSA_ERR_UNSUPPORTED and b"fused and split" in lib.tsa_last_error(), (opts.n_sink, kk)
+        opts.schedule = B.SCHEDULE["split"]
+        st = lib.tsa_sparse_decode_ex(ctypes.byref(desc), ctypes.byref(opts), fake, fake, fake, fake, fake, fake,
+                                      kk, fake, None, None, None, fake, ws_wide, None)
+        assert st == B.TSA_ERR_UNSUPPORTED and b"fused and split" in lib.tsa_last_error(), (opts.n_sink, kk)
     assert B.workspace_bytes(B.OP_SPARSE_DECODE_EX_MULTI, d, 4) > ws_ex
     assert B.workspace_bytes(B.OP_INDEX_BUILD_MULTI, d) > B.workspace_bytes(B.OP_INDEX_BUILD, d)
     for m in (0, 5):
@@ -236,15 +262,17 @@ def test_binding_refuses_host_tensors():
         B.index_build(x, c)
 
 
-def _ivf_ws(B_, N, Hkv, Hq, C, k, rows, split):
+def _ivf_ws(B_, N, Hkv, Hq, C, k, rows, keys):
     """Workspace bytes of a plain sparse decode whose lists are cut into
     `rows`-row plan segments (layout: descriptors, counts, partial states,
-    score keys when scoring is its own launch; each region 256-B aligned)."""
+    and for bf16 the score keys of a scoring launch of its own, which the
+    staged path's small batches and every split decode use; each region 256-B
+    aligned)."""
     def al(x):
         return (x + 255) // 256 * 256
     G, bh = Hq // Hkv, B_ * Hkv
     smax = G * k + -(-N // rows)
-    return al(bh * smax * 16) + al(bh * 4) + al(bh * smax * G * PART_FLOATS * 4) + (al(bh * G * C * 4) if split else 0)
+    return al(bh * smax * 16) + al(bh * 4) + al(bh * smax * G * PART_FLOATS * 4) + (al(bh * G * C * 4) if keys else 0)
 
 
 @pytest.mark.parametrize("k,rows", [(8, 64), (12, 128), (16, 256)])
@@ -252,11 +280,11 @@ def test_plan_segment_length_follows_the_expected_wave_count(lib, k, rows):
     # 2 requests x 8 KV heads, lists of ~200 rows (N / C): the longest segment
     # length for which 16 groups x 4k lists give >= 2048 segments
     d = B.IvfDesc(2, 6400, 8, 32, 128, 32, 1, B.TSA_BF16)
-    assert B.workspace_bytes(B.OP_SPARSE_DECODE, d, k) == _ivf_ws(2, 6400, 8, 32, 32, k, rows, split=True)
+    assert B.workspace_bytes(B.OP_SPARSE_DECODE, d, k) == _ivf_ws(2, 6400, 8, 32, 32, k, rows, keys=True)
 
 
 def test_plan_segment_length_at_the_benchmark_shapes(lib):
     big = B.IvfDesc(64, 32768, 8, 32, 128, 256, 1, B.TSA_BF16)
-    assert B.workspace_bytes(B.OP_SPARSE_DECODE, big, 16) == _ivf_ws(64, 32768, 8, 32, 256, 16, 256, split=False)
+    assert B.workspace_bytes(B.OP_SPARSE_DECODE, big, 16) == _ivf_ws(64, 32768, 8, 32, 256, 16, 256, keys=True)
     one = B.IvfDesc(1, 100_000, 8, 32, 128, 1000, 0, B.TSA_BF16)
-    assert B.workspace_bytes(B.OP_SPARSE_DECODE, one, 10) == _ivf_ws(1, 100_000, 8, 32, 1000, 10, 32, split=True)
+    assert B.workspace_bytes(B.OP_SPARSE_DECODE, one, 10) == _ivf_ws(1, 100_000, 8, 32, 1000, 10, 32, keys=True)

@@ -38,20 +38,50 @@ def _library_small_batch_groups():
     return int(m.group(1))
 
 
+def _library_constant(fname, name):
+    with open(os.path.join(ROOT, "top_sparse_attention_centroid_amd", "csrc", fname)) as f:
+        m = re.search(rf"constexpr (?:long long|int) {name} = (\d+);", f.read())
+    assert m, f"{fname} no longer defines {name}"
+    return int(m.group(1))
+
+
 def test_roofline_kernel_label_follows_the_library_dispatch(bench):
     from top_sparse_attention_centroid_amd import workloads as W
 
     threshold = _library_small_batch_groups()
-    names = {}
+    assert bench.SMALL_BATCH_GROUPS == threshold
+    assert bench.FUSED_MAX_HEADS == _library_constant("capi.cpp", "kFusedMaxHeads")
+    assert bench.FUSED_MAX_ROWS == _library_constant("capi.cpp", "kFusedMaxRows")
+    assert bench.FUSED_MAX_CODEBOOK == _library_constant("capi.cpp", "kFusedMaxCodebook")
+    assert bench.HEAD_MAX_C == _library_constant("kernels.hpp", "kHeadMaxC")
+    assert bench.HEAD_MAX_K == _library_constant("kernels.hpp", "kHeadMaxK")
+
+    class Auto:
+        schedule, assign, sink, window = "auto", 1, 0, 0
+
+    class Staged(Auto):
+        schedule = "staged"
+
+    names, staged, sched = {}, {}, {}
     for i in range(5):
         cfg = W.config(i)
-        names[cfg.name] = bench.gather_kernel_name(cfg, None)
+        names[cfg.name] = bench.gather_kernel_name(cfg, Auto)
+        staged[cfg.name] = bench.gather_kernel_name(cfg, Staged)
+        sched[cfg.name] = bench.ivf_schedule(cfg, Auto)
         merged = (cfg.kind == "ivf" and cfg.batch * cfg.n_kv_heads >= threshold and cfg.dtype == "bf16"
                   and cfg.group <= 4)
-        assert (names[cfg.name] == "gather_merge_kernel") == merged, cfg.name
+        assert (staged[cfg.name] == "gather_merge_kernel") == merged, cfg.name
+    assert sched == {"tiny-ivf-f32": "fused", "karat-ivf-100k": "split", "batched-ivf-64x32k": "staged",
+                     "token-topk-16x200k": None, "hier-cache-32x128k": None}
     assert names["batched-ivf-64x32k"] == "gather_merge_kernel"
-    assert names["karat-ivf-100k"] == "gather_attn_kernel"
+    assert names["karat-ivf-100k"] == names["tiny-ivf-f32"] == "ivf_head_kernel"
+    assert staged["karat-ivf-100k"] == "gather_attn_kernel"
     assert names["token-topk-16x200k"] == "gather_attn_kernel"
+
+    class TwoLists(Auto):
+        assign = 2
+    assert bench.gather_kernel_name(W.config(1), TwoLists) == "gather_attn_kernel"
+    assert bench.ivf_schedule(W.config(0), None) == "fused"
 
 
 def test_stored_traffic_is_used_only_for_the_source_it_was_taken_on(bench, tmp_path, monkeypatch):

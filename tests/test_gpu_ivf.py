@@ -42,7 +42,15 @@ def _f32(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float32).numpy()
 
 
-def _decode_and_check(cfg, p, ref_lists, requests, steps, q=None, sel_requests=()):
+def _decode(schedule, q, p, offsets, ids, k, **kw):
+    """One decode step under `schedule`: "auto" through tsa_sparse_decode (the
+    library's choice), "staged" or "fused" through tsa_sparse_decode_ex."""
+    if schedule == "auto":
+        return tsa.sparse_decode(q, p["centroids"], offsets, ids, p["keys"], p["values"], k, **kw)
+    return tsa.sparse_decode_ex(q, p["centroids"], offsets, ids, p["keys"], p["values"], k, schedule=schedule, **kw)
+
+
+def _decode_and_check(cfg, p, ref_lists, requests, steps, q=None, sel_requests=(), schedule="auto"):
     """Decodes `steps` steps of the whole batch and checks `requests` in full
     (selection, row counts, unique rows, outputs) against the oracle's own
     index; `sel_requests` get their selections checked too (scores alone)."""
@@ -57,8 +65,7 @@ def _decode_and_check(cfg, p, ref_lists, requests, steps, q=None, sel_requests=(
     V64 = {b: _f32(p["values"][b:b + 1]) for b in requests}
     cent64 = f64(p["centroids"])
     for t in range(steps):
-        out = tsa.sparse_decode(q[t], p["centroids"], offsets, ids, p["keys"], p["values"], k,
-                                sel_out=sel, rows_out=rows, uniq_out=uniq)
+        out = _decode(schedule, q[t], p, offsets, ids, k, sel_out=sel, rows_out=rows, uniq_out=uniq)
         torch.cuda.synchronize()
         q64 = f64(q[t])
         out_g, sel_g, rows_g, uniq_g = out.cpu().numpy(), sel.cpu().numpy(), rows.cpu().numpy(), uniq.cpu().numpy()
@@ -87,26 +94,31 @@ def _decode_and_check(cfg, p, ref_lists, requests, steps, q=None, sel_requests=(
     return q
 
 
-def test_tiny_fp32_workload():
+@pytest.mark.parametrize("schedule", ["auto", "staged"])
+def test_tiny_fp32_workload(schedule):
     cfg = W.config(0)
-    announce(f"ivf {cfg.name}")
+    announce(f"ivf {cfg.name} schedule={schedule}")
     p = _problem(cfg)
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     ref = _check_index(p, [0], offsets, ids)
-    _decode_and_check(cfg, p, ref, [0], steps=4)
+    _decode_and_check(cfg, p, ref, [0], steps=4, schedule=schedule)
 
 
+@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
-def test_ragged_shapes(dtype, G):
-    # N not a multiple of any tile, odd C, lists longer than one segment
+def test_ragged_shapes(dtype, G, schedule):
+    if schedule == "split" and dtype == "f32":
+        pytest.skip("the split decode scores bf16 codebooks only")
+    # N not a multiple of any tile, odd C, lists longer than one segment (and,
+    # fused, than one round of a head's rows over the workgroup's waves)
     cfg = W.config(1, batch=3, n_tokens=3001, n_kv_heads=2, n_q_heads=2 * G, n_centroids=7,
                    top_k=3, dtype=dtype, steps=2, shared_codebook=(G % 2 == 0), seed=11 + G)
-    announce(f"ivf ragged dtype={dtype} G={G}")
+    announce(f"ivf ragged dtype={dtype} G={G} schedule={schedule}")
     p = _problem(cfg)
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     ref = _check_index(p, range(cfg.batch), offsets, ids)
-    _decode_and_check(cfg, p, ref, range(cfg.batch), steps=2)
+    _decode_and_check(cfg, p, ref, range(cfg.batch), steps=2, schedule=schedule)
 
 
 # bf16 nearest-centroid search on matrix cores: fewer keys than one 16-key
@@ -188,18 +200,24 @@ def test_batched_workload_full_size():
     assert torch.equal(o1, o2)
 
 
-def test_karat_shape_full_size():
-    """1 request x 100,000 tokens, 8 KV / 32 query heads, C=1000 per KV head, top-10."""
+@pytest.mark.parametrize("schedule", ["auto", "fused", "staged"])
+def test_karat_shape_full_size(schedule):
+    """1 request x 100,000 tokens, 8 KV / 32 query heads, C=1000 per KV head,
+    top-10: the split launches (the library's choice here), the fused single
+    launch and the staged launches."""
     cfg = W.config(1)
-    announce(f"ivf {cfg.name} full size")
+    announce(f"ivf {cfg.name} full size schedule={schedule}")
     p = _problem(cfg)
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     ref = _check_index(p, [0], offsets, ids)
-    _decode_and_check(cfg, p, ref, [0], steps=2)
+    _decode_and_check(cfg, p, ref, [0], steps=2, schedule=schedule)
 
 
+@pytest.mark.parametrize("schedule", ["auto", "staged", "fused", "split"])
 @pytest.mark.parametrize("C,k", [(300, 10), (300, 64), (300, 100), (1000, 10)])
-def test_top_k_paths_and_ties(C, k):
+def test_top_k_paths_and_ties(C, k, schedule):
+    if schedule in ("fused", "split") and k > 64:
+        pytest.skip("the per-head decodes hold k <= 64 lists")
     """Selections through every search of the k-th largest score: the short
     candidate search (k <= 64, several keys per lane), its fallback when more
     than 64 keys reach the candidate bound (an all-zero query ties every
@@ -207,7 +225,7 @@ def test_top_k_paths_and_ties(C, k):
     ties to the lower list id; outputs against the oracle."""
     cfg = W.config(1, batch=2, n_tokens=8000, n_kv_heads=2, n_q_heads=8, n_centroids=C, top_k=k, steps=1,
                    shared_codebook=True, seed=31)
-    announce(f"ivf top-k paths C={C} k={k}")
+    announce(f"ivf top-k paths C={C} k={k} schedule={schedule}")
     p = _problem(cfg)
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     ref = _check_index(p, range(cfg.batch), offsets, ids)
@@ -217,7 +235,7 @@ def test_top_k_paths_and_ties(C, k):
         q[b, h] = 0
     B, Hq, G = cfg.batch, cfg.n_q_heads, cfg.group
     sel = torch.empty((B, Hq, k), dtype=torch.int32, device=DEV)
-    out = tsa.sparse_decode(q, p["centroids"], offsets, ids, p["keys"], p["values"], k, sel_out=sel)
+    out = _decode(schedule, q, p, offsets, ids, k, sel_out=sel)
     torch.cuda.synchronize()
     q64, c64, K, V = f64(q), f64(p["centroids"]), f64(p["keys"]), f64(p["values"])
     sel_g, out_g = sel.cpu().numpy(), out.cpu().numpy()
@@ -232,11 +250,12 @@ def test_top_k_paths_and_ties(C, k):
 
 
 def test_split_and_fused_scoring_choose_the_same_lists():
-    """Small batches score the centroids in a launch of their own, large ones
-    inside the selection kernel; both run the same per-tile contraction, so a
-    request selects the same lists either way (and both outputs match the
+    """Staged small batches score the centroids in a launch of their own,
+    large ones inside the selection kernel, and the fused decode inside its
+    one workgroup per head; all run the same per-tile contraction, so a
+    request selects the same lists every way (and the outputs match the
     oracle)."""
-    cfg = W.config(2, batch=16, n_tokens=2048, n_centroids=200, top_k=12, steps=1)  # 128 groups: fused
+    cfg = W.config(2, batch=16, n_tokens=2048, n_centroids=200, top_k=12, steps=1)  # 128 groups: in-select
     announce("ivf split vs fused scoring")
     p = _problem(cfg)
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
@@ -245,18 +264,29 @@ def test_split_and_fused_scoring_choose_the_same_lists():
     B, Hq, k = cfg.batch, cfg.n_q_heads, cfg.top_k
     sel_big = torch.empty((B, Hq, k), dtype=torch.int32, device=DEV)
     out_big = tsa.sparse_decode(q, p["centroids"], offsets, ids, p["keys"], p["values"], k, sel_out=sel_big)
-    n = 2  # 16 groups: split
+    n = 2  # 16 groups: split (staged) or fused
+    part = {"centroids": p["centroids"], "keys": p["keys"][:n].contiguous(), "values": p["values"][:n].contiguous()}
     sel_small = torch.empty((n, Hq, k), dtype=torch.int32, device=DEV)
-    out_small = tsa.sparse_decode(q[:n].contiguous(), p["centroids"], offsets[:n].contiguous(), ids[:n].contiguous(),
-                                  p["keys"][:n].contiguous(), p["values"][:n].contiguous(), k, sel_out=sel_small)
+    out_small = _decode("staged", q[:n].contiguous(), part, offsets[:n].contiguous(), ids[:n].contiguous(), k,
+                        sel_out=sel_small)
+    sel_fused = torch.empty((n, Hq, k), dtype=torch.int32, device=DEV)
+    out_fused = _decode("fused", q[:n].contiguous(), part, offsets[:n].contiguous(), ids[:n].contiguous(), k,
+                        sel_out=sel_fused)
+    sel_split = torch.empty((n, Hq, k), dtype=torch.int32, device=DEV)
+    out_split = _decode("split", q[:n].contiguous(), part, offsets[:n].contiguous(), ids[:n].contiguous(), k,
+                        sel_out=sel_split)
     torch.cuda.synchronize()
     assert torch.equal(sel_small, sel_big[:n])
+    assert torch.equal(sel_fused, sel_big[:n])
+    assert torch.equal(sel_split, sel_big[:n])
     assert np.array_equal(sel_big[1, 3].cpu().numpy(), np.arange(k))
     ref = _check_index(p, [0], offsets, ids)
     r = ivf.sparse_decode(f64(q[0:1]), f64(p["centroids"]), ref[0][0][None], ref[0][1][None],
                           f64(p["keys"][0:1]), f64(p["values"][0:1]), k)
     assert np.array_equal(sel_small[0].cpu().numpy(), r["sel"][0])
     assert out_error(out_small[0].cpu().numpy(), r["out"][0]) <= OUT_TOL
+    assert out_error(out_fused[0].cpu().numpy(), r["out"][0]) <= OUT_TOL
+    assert out_error(out_split[0].cpu().numpy(), r["out"][0]) <= OUT_TOL
     assert out_error(out_big[0].cpu().numpy(), r["out"][0]) <= OUT_TOL
 
 
@@ -270,7 +300,7 @@ def test_plan_segment_lengths(k):
     p = _problem(cfg)
     offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     ref = _check_index(p, range(cfg.batch), offsets, ids)
-    _decode_and_check(cfg, p, ref, range(cfg.batch), steps=1)
+    _decode_and_check(cfg, p, ref, range(cfg.batch), steps=1, schedule="staged")
 
 
 @pytest.mark.parametrize("dtype,G,C,k", [("bf16", 4, 2048, 10), ("bf16", 4, 2048, 100), ("bf16", 8, 1500, 12),
@@ -305,13 +335,20 @@ def test_split_and_fused_cosine_scores_choose_the_same_lists():
     out_big = tsa.sparse_decode_ex(q, cent, offsets, ids, p["keys"], p["values"], k, similarity="cosine",
                                    sel_out=sel_big)
     n = 2
-    sel_small = torch.empty((n, Hq, k), dtype=torch.int32, device=DEV)
-    out_small = tsa.sparse_decode_ex(q[:n].contiguous(), cent, offsets[:n].contiguous(), ids[:n].contiguous(),
-                                     p["keys"][:n].contiguous(), p["values"][:n].contiguous(), k,
-                                     similarity="cosine", sel_out=sel_small)
+    small = {}
+    for schedule in ("staged", "fused", "split"):
+        sel_small = torch.empty((n, Hq, k), dtype=torch.int32, device=DEV)
+        out_small = tsa.sparse_decode_ex(q[:n].contiguous(), cent, offsets[:n].contiguous(), ids[:n].contiguous(),
+                                         p["keys"][:n].contiguous(), p["values"][:n].contiguous(), k,
+                                         similarity="cosine", sel_out=sel_small, schedule=schedule)
+        small[schedule] = (sel_small, out_small)
     sel_dot = torch.empty_like(sel_big)
     tsa.sparse_decode(q, cent, offsets, ids, p["keys"], p["values"], k, sel_out=sel_dot)
     torch.cuda.synchronize()
+    sel_small, out_small = small["staged"]
     assert torch.equal(sel_small, sel_big[:n])
+    for schedule in ("fused", "split"):
+        assert torch.equal(small[schedule][0], sel_big[:n])
+        assert out_error(small[schedule][1].cpu().numpy(), out_big[:n].cpu().numpy()) <= 1e-4
     assert not torch.equal(sel_big, sel_dot), "the scaled codebook should make cosine and dot choose differently"
     assert out_error(out_small.cpu().numpy(), out_big[:n].cpu().numpy()) <= 1e-4

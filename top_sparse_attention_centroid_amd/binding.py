@@ -19,6 +19,8 @@ TSA_F32, TSA_BF16 = 0, 1
 (OP_INDEX_BUILD, OP_SPARSE_DECODE, OP_TOKEN_DECODE, OP_ATTEND_ROWS, OP_SPARSE_DECODE_EX, OP_INDEX_BUILD_MULTI,
  OP_SPARSE_DECODE_EX_MULTI) = range(7)
 SIMILARITY = {"dot": 0, "cosine": 1}
+SCHEDULE = {"auto": 0, "staged": 1, "fused": 2, "split": 3}
+ABI_VERSION = 2  # TSA_ABI_VERSION of include/tsa.h
 EVICT_POLICIES = {"lru": 0, "fifo": 1, "random": 2, "priority": 3}
 
 _I32 = ctypes.c_int32
@@ -42,7 +44,7 @@ class CacheDesc(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("similarity", _I32), ("n_sink", _I32), ("n_window", _I32), ("assign_per_key", _I32),
-                ("lengths", _P), ("lens", _P), ("alt", _P)]
+                ("lengths", _P), ("lens", _P), ("alt", _P), ("schedule", _I32)]
 
 
 class LayerIO(ctypes.Structure):
@@ -118,6 +120,9 @@ def load() -> ctypes.CDLL:
     lib.tsa_abi_version.restype = _I32
     lib.tsa_stream_read_sink_bytes.argtypes = []
     lib.tsa_stream_read_sink_bytes.restype = ctypes.c_size_t
+    if lib.tsa_abi_version() != ABI_VERSION:  # the structs below follow one layout
+        raise ImportError(f"{_LIB_PATH} has ABI {lib.tsa_abi_version()}, this binding expects {ABI_VERSION}; "
+                          "rebuild it")
     _lib = lib
     return lib
 
@@ -405,12 +410,16 @@ def index_regrow(offsets, lens, ids, alt=None, slack: int = -1, *, out=None, sta
 
 def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, similarity: str = "dot",
                      n_sink: int = 0, n_window: int = 0, lengths=None, lens=None, alt=None, out=None,
-                     sel_out=None, rows_out=None, uniq_out=None, ws=None, stream=None):
+                     sel_out=None, rows_out=None, uniq_out=None, ws=None, stream=None, schedule: str = "auto"):
     """Decode with the variants: cosine similarity and/or the first n_sink and
     last n_window tokens (before lengths[b]) attended beside the lists; with
     `alt` (an m-way index from index_build_multi or index_build_dyn_multi)
     every token sits in m lists and is attended once per head; with `lens`,
-    a growing index."""
+    a growing index. `schedule`: "auto", "staged" (scoring, select + plan,
+    gather, combine launches), "fused" (one launch) or "split" (scoring, a
+    select + attend launch over shares of each head's rows, combine); fused
+    and split take plain decodes (one list per key, no sink or window,
+    C <= 1024, k <= 64), split bf16 only."""
     for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
@@ -418,6 +427,8 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
         raise ValueError("q, centroids, k_cache and v_cache must share a dtype")
     if similarity not in SIMILARITY:
         raise ValueError(f"similarity must be one of {sorted(SIMILARITY)}")
+    if schedule not in SCHEDULE:
+        raise ValueError(f"schedule must be one of {sorted(SCHEDULE)}")
     B, Hq, d = q.shape
     desc = ivf_desc(k_cache, centroids, Hq)
     if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != B or k_cache.shape[3] != d:
@@ -435,7 +446,8 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
     _i32(sel_out, "sel_out", (B, Hq, k))
     _i32(rows_out, "rows_out", (B, Hq))
     _i32(uniq_out, "uniq_out", (B, Hkv))
-    opts = DecodeOpts(SIMILARITY[similarity], n_sink, n_window, m, _ptr(lengths), _ptr(lens), _ptr(alt))
+    opts = DecodeOpts(SIMILARITY[similarity], n_sink, n_window, m, _ptr(lengths), _ptr(lens), _ptr(alt),
+                      SCHEDULE[schedule])
     ws = (_workspace(OP_SPARSE_DECODE_EX_MULTI, desc, k, ws, q.device, m) if m > 1
           else _workspace(OP_SPARSE_DECODE_EX, desc, k, ws, q.device))
     _check(load().tsa_sparse_decode_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(centroids),

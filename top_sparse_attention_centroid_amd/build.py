@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtsa.so")
 
-SOURCES = ["ivf.hip", "attention.hip", "token_select.hip", "resolve.hip", "probe.hip", "capi.cpp"]
+SOURCES = ["ivf.hip", "attention.hip", "decode_heads.hip", "token_select.hip", "resolve.hip", "probe.hip", "capi.cpp"]
 
 ARCH = "gfx950"
 

@@ -18,12 +18,11 @@ using namespace tsa;
 namespace {
 
 thread_local std::string g_last_error;
-thread_local hipEvent_t g_gather_ev0 = nullptr;
-thread_local hipEvent_t g_gather_ev1 = nullptr;
+thread_local hipEvent_t g_gather_evs[2] = {nullptr, nullptr};   // gather (tsa_time_next_launch)
 thread_local hipEvent_t g_scan_ev0 = nullptr;   // token indexer scan (tsa_time_next_launch)
 thread_local hipEvent_t g_scan_ev1 = nullptr;
-thread_local hipEvent_t g_append_ev[2] = {nullptr, nullptr};   // kv_append (tsa_time_next_launch)
-thread_local hipEvent_t g_regrow_ev[2] = {nullptr, nullptr};   // regrow (tsa_time_next_launch)
+thread_local hipEvent_t g_append_evs[2] = {nullptr, nullptr};   // kv_append (tsa_time_next_launch)
+thread_local hipEvent_t g_regrow_evs[2] = {nullptr, nullptr};   // regrow (tsa_time_next_launch)
 
 // Records the one-shot event pair `ev` (if set) around one launch on s.
 template <typename Launch>
@@ -170,8 +169,10 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false, int 
   L.nseg = off;   off += align_up(bh * sizeof(int32_t));
   L.partial = off; off += align_up(bh * L.smax * L.G * kPartStride * sizeof(float));
   L.lmask = off;   off += m > 1 ? align_up(bh * d.n_centroids * sizeof(uint32_t)) : 0;
+  // the scores of a separate scoring launch: the staged path's small bf16
+  // batches and every split decode (any bf16 batch may ask for one)
   L.split_score = d.dtype == TSA_BF16 && L.small_batch;
-  L.keys = off;    off += L.split_score ? align_up(bh * L.G * d.n_centroids * sizeof(uint32_t)) : 0;
+  L.keys = off;    off += d.dtype == TSA_BF16 ? align_up(bh * L.G * d.n_centroids * sizeof(uint32_t)) : 0;
   L.total = off;
   return L;
 }
@@ -302,18 +303,8 @@ tsa_status check_cache(const tsa_cache_desc* d) {
 
 tsa_status launch_gather_timed(const GatherParams& gp, int dtype, int G, bool explicit_plan,
                                hipStream_t s) {
-  hipEvent_t e0 = g_gather_ev0, e1 = g_gather_ev1;
-  g_gather_ev0 = g_gather_ev1 = nullptr;
-  if (e0) {
-    hipError_t e = hipEventRecord(e0, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
-  hipError_t e = launch_gather(gp, dtype, G, explicit_plan, s);
+  hipError_t e = launch_between(g_gather_evs, s, [&] { return launch_gather(gp, dtype, G, explicit_plan, s); });
   if (e != hipSuccess) return hip_fail(e, "gather_attn launch");
-  if (e1) {
-    e = hipEventRecord(e1, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
   e = launch_combine(gp, G, explicit_plan, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return TSA_OK;
@@ -348,6 +339,52 @@ tsa_status index_build_impl(const tsa_ivf_desc* desc, const void* keys, const vo
   return ok();
 }
 
+// The per-head schedules (fused, split) take plain list decodes whose
+// codebook and k fit one workgroup: one list per token, no sink or window
+// rows, C <= kHeadMaxC, k <= kHeadMaxK.
+bool head_qualifies(const tsa_ivf_desc& d, int k, const tsa_decode_opts* opts) {
+  if (opts && (opts->assign_per_key > 1 || opts->n_sink > 0 || opts->n_window > 0)) return false;
+  return d.n_centroids <= kHeadMaxC && k <= kHeadMaxK;
+}
+
+// AUTO takes the fused decode when every head's work fits one CU (a CU reads
+// some 40 GB/s, so a head's rows and its group's codebook must be small):
+// at most kFusedMaxHeads heads, about kFusedMaxRows rows a head and
+// kFusedMaxCodebook bytes of codebook per KV head. Otherwise bf16 batches of
+// fewer than kSmallBatchGroups groups take the split decode, which spreads
+// the scoring and every head's rows over many CUs; the rest the staged path.
+constexpr long long kFusedMaxHeads = 256;
+constexpr long long kFusedMaxRows = 512;
+constexpr long long kFusedMaxCodebook = 65536;  // 64 KiB
+
+int resolve_schedule(const tsa_ivf_desc& d, int k, const tsa_decode_opts* opts) {
+  const int sched = opts ? opts->schedule : TSA_SCHED_AUTO;
+  if (sched != TSA_SCHED_AUTO) return sched;  // FUSED / SPLIT checked to qualify by the caller
+  if (!head_qualifies(d, k, opts)) return TSA_SCHED_STAGED;
+  const long long rows = static_cast<long long>(k) * d.n_tokens / d.n_centroids;
+  const long long codebook = static_cast<long long>(d.n_centroids) * d.head_dim * esize(d.dtype);
+  if (static_cast<long long>(d.batch) * d.n_q_heads <= kFusedMaxHeads && rows <= kFusedMaxRows &&
+      codebook <= kFusedMaxCodebook)
+    return TSA_SCHED_FUSED;
+  if (d.dtype == TSA_BF16 && static_cast<long long>(d.batch) * d.n_kv_heads < kSmallBatchGroups)
+    return TSA_SCHED_SPLIT;
+  return TSA_SCHED_STAGED;
+}
+
+// Split decode: shares per query head so that each of a share's kSplitWaves
+// waves attends about one batch (32 rows) of an average head (k * N / C rows),
+// at most kSplitMaxWorkgroups workgroups in all, and G * S partial records
+// within the plan's smax per group.
+constexpr long long kSplitRowsPerShare = kSplitWaves * 32;
+constexpr long long kSplitMaxWorkgroups = 2048;
+int split_shares(const tsa_ivf_desc& d, int k, const IvfLayout& L) {
+  const long long rows = static_cast<long long>(k) * d.n_tokens / d.n_centroids;
+  long long S = std::max(1LL, (rows + kSplitRowsPerShare - 1) / kSplitRowsPerShare);
+  S = std::min(S, std::max(1LL, kSplitMaxWorkgroups / (static_cast<long long>(d.batch) * d.n_q_heads)));
+  S = std::min(S, static_cast<long long>(L.smax / L.G));
+  return static_cast<int>(std::max(1LL, S));
+}
+
 tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* opts, const void* q,
                               const void* centroids, const int32_t* offsets, const int32_t* lens,
                               const int32_t* ids, const void* k_cache, const void* v_cache, int32_t k, float* out,
@@ -374,6 +411,30 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
     selp.n_sink = opts->n_sink;
     selp.n_window = opts->n_window;
     selp.lengths = opts->lengths;
+  }
+  const int sched = resolve_schedule(d, k, opts);
+  if (sched == TSA_SCHED_FUSED || sched == TSA_SCHED_SPLIT) {
+    HeadDecodeParams hp{};
+    hp.s = selp;
+    hp.ids = ids; hp.k = k_cache; hp.v = v_cache; hp.out = out;
+    hp.qscale = qscale(d.head_dim);
+    hp.Hq = d.n_q_heads;
+    if (sched == TSA_SCHED_FUSED) {
+      // the one kernel of the step answers the gather timing hook
+      hipError_t e = launch_between(g_gather_evs, s, [&] { return launch_fused_decode(hp, d.dtype, L.G, s); });
+      if (e != hipSuccess) return hip_fail(e, "fused decode launch");
+      return ok();
+    }
+    hp.s.keys = reinterpret_cast<uint32_t*>(w + L.keys);
+    hp.partial = reinterpret_cast<float*>(w + L.partial);
+    hp.S = split_shares(d, k, L);
+    hipError_t e = launch_centroid_score(hp.s, L.G, s);
+    if (e != hipSuccess) return hip_fail(e, "centroid_score launch");
+    e = launch_between(g_gather_evs, s, [&] { return launch_split_decode(hp, L.G, s); });
+    if (e != hipSuccess) return hip_fail(e, "split decode launch");
+    e = launch_split_combine(hp, L.G, s);
+    if (e != hipSuccess) return hip_fail(e, "split combine launch");
+    return ok();
   }
   if (m > 1) selp.lmask_out = reinterpret_cast<uint32_t*>(w + L.lmask);
   selp.seg_rows = L.seg_rows;
@@ -571,7 +632,7 @@ tsa_status tsa_kv_append_multi(const tsa_ivf_desc* desc, int32_t m, const void* 
   ap.m = m;
   ap.alt = m > 1 ? alt : nullptr;
   const hipStream_t s = as_stream(stream);
-  hipError_t e = launch_between(g_append_ev, s, [&] { return launch_kv_append(ap, d.dtype, s); });
+  hipError_t e = launch_between(g_append_evs, s, [&] { return launch_kv_append(ap, d.dtype, s); });
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return ok();
 }
@@ -600,7 +661,7 @@ tsa_status tsa_index_regrow(const tsa_ivf_desc* desc, int32_t m, const int32_t* 
                   m > 1 ? alt_out : nullptr, status, desc->batch, desc->n_kv_heads, desc->n_centroids,
                   desc->n_tokens * m, m, slack};
   const hipStream_t s = as_stream(stream);
-  hipError_t e = launch_between(g_regrow_ev, s, [&] { return launch_regrow(rp, s); });
+  hipError_t e = launch_between(g_regrow_evs, s, [&] { return launch_regrow(rp, s); });
   if (e != hipSuccess) return hip_fail(e, "regrow launch");
   return ok();
 }
@@ -645,6 +706,13 @@ tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts*
     if (tsa_status s = check_m(desc, opts->assign_per_key)) return s;
     if (!opts->alt) return fail(TSA_ERR_INVALID_ARG, "opts->alt is NULL for %d lists per token", opts->assign_per_key);
   }
+  if (opts->schedule < TSA_SCHED_AUTO || opts->schedule > TSA_SCHED_SPLIT)
+    return fail(TSA_ERR_INVALID_ARG, "unknown schedule %d", opts->schedule);
+  if ((opts->schedule == TSA_SCHED_FUSED || opts->schedule == TSA_SCHED_SPLIT) && !head_qualifies(*desc, k, opts))
+    return fail(TSA_ERR_UNSUPPORTED, "the fused and split decodes need one list per token, no sink or window, "
+                "C <= %d and k <= %d", kHeadMaxC, kHeadMaxK);
+  if (opts->schedule == TSA_SCHED_SPLIT && desc->dtype != TSA_BF16)
+    return fail(TSA_ERR_UNSUPPORTED, "the split decode scores bf16 codebooks only");
   return sparse_decode_impl(desc, opts, q, centroids, offsets, opts->lens, ids, k_cache, v_cache, k, out, sel_out,
                             rows_out, uniq_out, ws, ws_bytes, stream);
 }
@@ -928,20 +996,20 @@ tsa_status tsa_time_next_launch(int32_t kernel, void* ev_start, void* ev_stop) {
     return fail(TSA_ERR_INVALID_ARG, "give both events or neither");
   switch (kernel) {
     case TSA_TIMED_GATHER:
-      g_gather_ev0 = static_cast<hipEvent_t>(ev_start);
-      g_gather_ev1 = static_cast<hipEvent_t>(ev_stop);
+      g_gather_evs[0] = static_cast<hipEvent_t>(ev_start);
+      g_gather_evs[1] = static_cast<hipEvent_t>(ev_stop);
       return ok();
     case TSA_TIMED_TOKEN_SCAN:
       g_scan_ev0 = static_cast<hipEvent_t>(ev_start);
       g_scan_ev1 = static_cast<hipEvent_t>(ev_stop);
       return ok();
     case TSA_TIMED_APPEND:
-      g_append_ev[0] = static_cast<hipEvent_t>(ev_start);
-      g_append_ev[1] = static_cast<hipEvent_t>(ev_stop);
+      g_append_evs[0] = static_cast<hipEvent_t>(ev_start);
+      g_append_evs[1] = static_cast<hipEvent_t>(ev_stop);
       return ok();
     case TSA_TIMED_REGROW:
-      g_regrow_ev[0] = static_cast<hipEvent_t>(ev_start);
-      g_regrow_ev[1] = static_cast<hipEvent_t>(ev_stop);
+      g_regrow_evs[0] = static_cast<hipEvent_t>(ev_start);
+      g_regrow_evs[1] = static_cast<hipEvent_t>(ev_stop);
       return ok();
   }
   return fail(TSA_ERR_INVALID_ARG, "unknown timed kernel %d", kernel);

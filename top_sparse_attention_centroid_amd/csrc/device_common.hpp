@@ -63,6 +63,8 @@ struct Raw8<float> {
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));   // MFMA 16x16x32 bf16 operand
+typedef float f32x4_t __attribute__((ext_vector_type(4)));     // MFMA 16x16 fp32 result
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,

@@ -8,6 +8,7 @@
 
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "select_common.hpp"
 
 namespace tsa {
 
@@ -134,8 +135,6 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
 // with compares and selects only, and the four lanes that share the key merge
 // their lists on d = -2 s with the lexicographic order (distance, centroid id).
 // ============================================================================
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaCs = 256;      // centroids per LDS stage
 constexpr int kMfmaKb = 1024;     // keys per workgroup
@@ -521,69 +520,6 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 // Plan: the union of the group's chosen lists with a head bitmask per list,
 // each list cut into segments of at most seg_rows rows, ascending list order.
 // ============================================================================
-// Scores of one KV group as a dense contraction on matrix cores: 16x16x32
-// bf16 MFMAs, fp32 accumulation. The A operand holds the group's query heads
-// in rows 0..G-1 (rows G..15 repeat head G-1 and are dropped); each
-// 16-centroid B tile is read straight from memory, since every centroid row
-// is used once per group. The calling wave scores tiles [t_begin, t_end),
-// kSelTiles of them in flight. Lane l of a result tile holds centroid l % 16
-// for heads (l / 16) * 4 .. +4; the order key of s[h][c] goes to
-// keys[h * C + c]. Cosine scaling divides by |c|, summed from the same B
-// fragments (each lane squares 32 of the row's elements; the four lanes of a
-// column add theirs).
-constexpr int kSelTiles = 8;
-
-template <int G, int TILES = kSelTiles>
-__device__ __forceinline__ void score_tiles_mfma(const SelectParams& p, int b, int g, int t_begin, int t_end,
-                                                 uint32_t* keys) {
-  const int C = p.C;
-  const int lane = lane_id(), col = lane & 15, grp = lane >> 4;
-  const bf16_t* qr = static_cast<const bf16_t*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim +
-                     min(col, G - 1) * kHeadDim + grp * 8;
-  bf16x8_t a[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8_t*>(qr + ks * 32);
-  const bf16_t* cb = static_cast<const bf16_t*>(p.centroids) + b * p.cent_bstride +
-                     static_cast<long long>(g) * C * kHeadDim + grp * 8;
-  for (int t0 = t_begin; t0 < t_end; t0 += TILES) {
-    bf16x8_t bt[TILES][4];
-#pragma unroll
-    for (int u = 0; u < TILES; ++u) {
-      if (t0 + u < t_end) {
-        const bf16_t* row = cb + static_cast<long long>(min((t0 + u) * 16 + col, C - 1)) * kHeadDim;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) bt[u][ks] = *reinterpret_cast<const bf16x8_t*>(row + ks * 32);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TILES; ++u) {
-      if (t0 + u >= t_end) break;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bt[u][ks], acc, 0, 0, 0);
-      float inv = 1.f;
-      if (p.cosine) {  // q.c / |c| (1/|q| ranks nothing differently)
-        float n2 = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          Raw8<bf16_t> r;
-          r.v = __builtin_bit_cast(uint4, bt[u][ks]);
-          n2 += sq8(r);
-        }
-        n2 += __shfl_xor(n2, 16);
-        n2 += __shfl_xor(n2, 32);
-        inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
-      }
-      const int c = (t0 + u) * 16 + col;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = grp * 4 + i;
-        if (h < G && c < C) keys[h * C + c] = order_key(acc[i] * inv);
-      }
-    }
-  }
-}
-
 // Scoring as its own launch, for batches too small to fill the chip with one
 // workgroup per (request, KV head): grid (ceil(C / 64), B * Hkv), each wave
 // one 16-centroid tile, keys to p.keys.
@@ -607,8 +543,7 @@ __global__ __launch_bounds__(NW * kWave) void ivf_select_kernel(SelectParams p) 
   int* loff = reinterpret_cast<int*>(smem + (G + 1) * C);  // [C+1], clamped to [0, N]
   int* llen = loff + C + 1;                           // [C] valid entries per list (p.lens_lds only)
   __shared__ int class_scratch[NW * (G + 2)];
-  __shared__ uint32_t cand_lds[NW][kWave];
-  __shared__ int cand_list_lds[NW][kWave];
+  __shared__ __align__(16) uint64_t cand_lds[NW][2 * kWave];
   const int bg = blockIdx.x;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -652,35 +587,7 @@ __global__ __launch_bounds__(NW * kWave) void ivf_select_kernel(SelectParams p) 
     const int per_wave = (ntile + NW - 1) / NW;
     score_tiles_mfma<G>(p, b, g, wave * per_wave, min(ntile, (wave + 1) * per_wave), keys);
   } else {
-    const T* qb = static_cast<const T*>(p.q) + (static_cast<long long>(b) * p.Hkv + g) * G * kHeadDim;
-    QFrag<T> qf[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) qf[h].load(qb + h * kHeadDim + e * 8);
-    const T* cb = static_cast<const T*>(p.centroids) + b * p.cent_bstride +
-                  static_cast<long long>(g) * C * kHeadDim + e * 8;
-    constexpr int U = 16;  // centroid rows in flight per lane group (64 per wave)
-    for (int c0 = wave * 4; c0 < C; c0 += 4 * NW * U) {
-      Raw8<T> raw[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = min(c0 + u * 4 * NW + r, C - 1);  // clamped: straight-line loads
-        raw[u].load(cb + static_cast<long long>(c) * kHeadDim);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * 4 * NW + r;
-        float inv = 1.f;
-        if (p.cosine) {  // cosine similarity: q.c / |c| (1/|q| ranks nothing differently)
-          const float n2 = group16_sum(sq8(raw[u]));
-          inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float sc = group16_sum(qf[h].dot(raw[u])) * inv;
-          if (e == 0 && c < C) keys[h * C + c] = order_key(sc);
-        }
-      }
-    }
+    score_rows_valu<T, G, NW, 16>(p, b, g, wave, keys);
   }
 #pragma unroll
   for (int i = 0; i < kOffPer; ++i) {
@@ -705,104 +612,14 @@ __global__ __launch_bounds__(NW * kWave) void ivf_select_kernel(SelectParams p) 
       const int c = j * kWave + lane;
       kk[j] = c < C ? kh[c] : 0u;
     }
-    // thr = the k-th largest key: the largest t with #{keys >= t} >= k, found
-    // bit by bit. With several keys per lane the search first runs over a
-    // short candidate list: the k-th largest of the 64 lane maxima, t1, has
-    // at least k keys at or above it, so thr >= t1 and every key >= thr is
-    // among the keys >= t1. When at most 64 keys pass that bound they are
-    // compacted to LDS with their list ids, one per lane in ascending list
-    // order; the search over them gives the same thr, and the lists are
-    // emitted from them in one pass. Otherwise search and emission run over
-    // all keys.
-    uint32_t thr = 0;
-    bool found = false;
-    uint32_t x = 0u;  // compacted candidate key of this lane (0: none)
-    int xc = 0;       // its list
-    if (KPL > 1 && k <= kWave) {
-      uint32_t lmax = kk[0];
-#pragma unroll
-      for (int j = 1; j < KPL; ++j) lmax = max(lmax, kk[j]);
-      uint32_t t1 = 0;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = t1 | (1u << bit);
-        if (static_cast<int>(__popcll(__ballot(lmax >= cand))) >= k) t1 = cand;
-      }
-      int n_cand = 0;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) n_cand += __popcll(__ballot(kk[j] >= t1));
-      if (n_cand <= kWave) {
-        uint32_t* cl = cand_lds[wave];
-        int* cli = cand_list_lds[wave];
-        int base = 0;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          const bool in = kk[j] >= t1;
-          const uint64_t m = __ballot(in);
-          if (in) {
-            cl[base + prefix_count(m)] = kk[j];
-            cli[base + prefix_count(m)] = j * kWave + lane;
-          }
-          base += __popcll(m);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        x = lane < n_cand ? cl[lane] : 0u;
-        xc = lane < n_cand ? cli[lane] : 0;
-        for (int bit = 31; bit >= 0; --bit) {
-          const uint32_t cand = thr | (1u << bit);
-          if (static_cast<int>(__popcll(__ballot(x >= cand))) >= k) thr = cand;
-        }
-        found = true;
-        __builtin_amdgcn_wave_barrier();  // the next head of this wave reuses cl
-      }
-    }
-    if (!found) {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(kk[j] >= cand));
-        if (cnt >= k) thr = cand;
-      }
-    }
     const int qh = g * G + h;
     int32_t* sel = p.sel_out ? p.sel_out + (static_cast<long long>(b) * p.Hkv * G + qh) * k : nullptr;
     int rows = 0;
-    if (found) {
-      // thr >= t1 > 0, so lanes without a candidate (x = 0) take nothing
-      const int need_eq = k - __popcll(__ballot(x > thr));
-      const bool eq = x == thr;
-      const bool take = x > thr || (eq && prefix_count(__ballot(eq)) < need_eq);
-      const uint64_t tm = __ballot(take);
-      if (take) {
-        if (sel) sel[prefix_count(tm)] = xc;
-        atomicOr(&lmask[xc], 1u << h);
-        rows = list_len(xc);
-      }
-    } else {
-      int n_gt = 0;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) n_gt += __popcll(__ballot(kk[j] > thr));
-      const int need_eq = k - n_gt;
-      int base = 0, eq_seen = 0;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        const int c = j * kWave + lane;
-        const bool gt = kk[j] > thr;
-        const bool eq = kk[j] == thr;
-        const uint64_t eqm = __ballot(eq);
-        const bool take = gt || (eq && eq_seen + prefix_count(eqm) < need_eq);
-        const uint64_t tm = __ballot(take);
-        if (take) {
-          if (sel) sel[base + prefix_count(tm)] = c;
-          atomicOr(&lmask[c], 1u << h);
-          rows += list_len(c);
-        }
-        base += __popcll(tm);
-        eq_seen += __popcll(eqm);
-      }
-    }
+    topk_lists<KPL>(kk, k, cand_lds[wave], [&](int c, int pos) {
+      if (sel) sel[pos] = c;
+      atomicOr(&lmask[c], 1u << h);
+      rows += list_len(c);
+    });
     rows = wave_sum_i(rows);
     if (p.rows_out && lane == 0) p.rows_out[static_cast<long long>(b) * p.Hkv * G + qh] = rows;
   }
@@ -1259,15 +1076,19 @@ static void score_dispatch_g(const SelectParams& p, hipStream_t s) {
   hipLaunchKernelGGL(centroid_score_kernel<G>, grid, dim3(256), 0, s, p);
 }
 
+hipError_t launch_centroid_score(const SelectParams& p, int G, hipStream_t s) {
+  switch (G) {
+    case 1: score_dispatch_g<1>(p, s); break;
+    case 2: score_dispatch_g<2>(p, s); break;
+    case 4: score_dispatch_g<4>(p, s); break;
+    default: score_dispatch_g<8>(p, s); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s) {
   if (p.keys) {  // bf16 only (checked by the caller)
-    switch (G) {
-      case 1: score_dispatch_g<1>(p, s); break;
-      case 2: score_dispatch_g<2>(p, s); break;
-      case 4: score_dispatch_g<4>(p, s); break;
-      default: score_dispatch_g<8>(p, s); break;
-    }
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_centroid_score(p, G, s);
     if (e != hipSuccess) return e;
   }
   size_t lds = (static_cast<size_t>(G + 1) * p.C + p.C + 1) * sizeof(uint32_t);

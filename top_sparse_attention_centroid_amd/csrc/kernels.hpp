@@ -96,6 +96,35 @@ constexpr int kSelWaves = 4;               // waves per select workgroup
 constexpr size_t kSelectLdsBytes = 65536;  // dynamic LDS of a select workgroup (keys, masks, offsets, lengths)
 hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_t s);
 
+// ------------------------------------------- per-head decode (small batches)
+// Fused: one workgroup of kFusedWaves waves per (request, query head) scores
+// the KV group's codebook, selects the group's heads' top-k lists, gathers its
+// own head's rows and writes its output, in one launch with no workspace.
+// Split: centroid_score_kernel first; then S workgroups of kSplitWaves waves
+// per query head each select the head's lists from the scores and attend
+// share s of its rows, writing a partial state per share (record h * S + s
+// of the group), which split_combine_kernel merges per head.
+struct HeadDecodeParams {
+  SelectParams s;          // q, centroids, offsets, lens, the sel / rows / uniq outputs, sizes,
+                           // cosine, n_entries; split: keys (the scores), smax
+  const int32_t* ids;      // [B][Hkv][n_entries]
+  const void* k;           // [B][N][Hkv][d]
+  const void* v;
+  float* out;              // [B][Hq][d] (fused)
+  float* partial;          // [B*Hkv][smax][G][kPartStride] (split)
+  float qscale;            // log2(e) / sqrt(d)
+  int Hq;
+  int S;                   // split: workgroups per query head (G * S <= smax)
+};
+constexpr int kFusedWaves = 16;
+constexpr int kSplitWaves = 4;
+constexpr int kHeadMaxC = 1024;   // lists of a group held in one workgroup's LDS
+constexpr int kHeadMaxK = 64;     // chosen lists of a head, one per lane
+hipError_t launch_fused_decode(const HeadDecodeParams& p, int dtype, int G, hipStream_t s);
+hipError_t launch_split_decode(const HeadDecodeParams& p, int G, hipStream_t s);  // bf16 only
+hipError_t launch_split_combine(const HeadDecodeParams& p, int G, hipStream_t s);
+hipError_t launch_centroid_score(const SelectParams& p, int G, hipStream_t s);     // bf16; writes p.keys
+
 // ---------------------------------------------------------- KV + index append
 struct AppendParams {
   const void* new_k;       // [B][Hkv][d]
