@@ -27,7 +27,6 @@ constexpr int kPartStride = 160;    // floats per partial state
 // workgroup waits longer for its longest segment, 6 also loses occupancy)
 constexpr int kMergeWaves = 3;
 constexpr int kPartO = 32;          // offset of o[128] within the state
-constexpr int kTokScoreTile = 2048;  // indexer tokens scored per workgroup
 constexpr int kTokFilterTile = 4096;      // score keys filtered per workgroup
 constexpr int kTokHistBits = 12;          // top bits of the score key in the threshold histogram
 constexpr int kTokHistBins = 1 << kTokHistBits;

@@ -6,10 +6,10 @@
 // The selection is the k largest scores under the total order (score desc,
 // token id asc), emitted in ascending id order. Three kernels:
 //   score  -- streams the indexer keys (d_idx = 64 bf16 = 128 B per token,
-//             8 lanes x 16 B), writes one order-preserving 32-bit key per
-//             token and adds every key's top 12 bits to a per-request
-//             histogram (one LDS histogram per workgroup, flushed with
-//             global atomics).
+//             8 lanes x 16 B), each workgroup an equal share of a request,
+//             writes one order-preserving 32-bit key per token and adds
+//             every key's top 12 bits to a per-request histogram (one LDS
+//             histogram per workgroup, flushed once with global atomics).
 //   filter -- every workgroup reads the histogram, finds the threshold bin
 //             (the highest bin at which the count from the top reaches k)
 //             and compacts the keys at or above it, in id order, into its
@@ -22,6 +22,8 @@
 // hold the whole selection and the result is exact for any score
 // distribution (ties included); only the work of the final kernel grows
 // with the number of keys that share the threshold bin.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -30,6 +32,9 @@ namespace tsa {
 constexpr int kIdxDim = 64;
 constexpr int kScoreThreads = 256;
 constexpr int kScoreUnroll = 8;  // 16-B loads in flight per lane
+constexpr int kTokScoreTile = 2048;  // tokens per LDS-staged sub-tile of a scan workgroup
+constexpr long long kScoreWorkgroups = 1024;  // scan workgroups per launch: 4 per CU
+constexpr long long kScoreMinShare = 1024;    // fewest tokens a scan workgroup takes
 constexpr int kFilterThreads = 256;
 constexpr int kFinalThreads = 1024;
 constexpr int kHistShift = 32 - kTokHistBits;
@@ -78,45 +83,53 @@ __device__ __forceinline__ void threshold_bin(const int32_t* hist, int k, int* s
   __syncthreads();
 }
 
+// Workgroup x of request b scans tokens [x * N / X, (x + 1) * N / X), X =
+// gridDim.x, in sub-tiles of kTokScoreTile staged through LDS, so that each
+// wave round's keys leave as whole lines; its LDS histogram covers its whole
+// share and is flushed once. X is chosen so that the B * X workgroups fill
+// every CU the same number of times (a grid of fixed tiles left a last
+// partial round of workgroups running alone). Scores: bf16 dot2 products,
+// 8 lanes a token.
 template <typename T>
 __global__ __launch_bounds__(kScoreThreads) void token_score_kernel(TokenSelectParams p) {
   constexpr int NW = kScoreThreads / kWave;
   __shared__ uint32_t sk[kTokScoreTile];
   __shared__ int h[kTokHistBins];
   const int b = blockIdx.y;
-  const int start = blockIdx.x * kTokScoreTile;
-  const int n = min(kTokScoreTile, p.N - start);
+  const int share_lo = static_cast<int>(static_cast<long long>(p.N) * blockIdx.x / gridDim.x);
+  const int share_hi = static_cast<int>(static_cast<long long>(p.N) * (blockIdx.x + 1) / gridDim.x);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int e = lane & 7, tq = lane >> 3;
   for (int i = tid; i < kTokHistBins; i += kScoreThreads) h[i] = 0;
 
-  float qf[8];
-  load8(static_cast<const T*>(p.q_idx) + static_cast<long long>(b) * kIdxDim + e * 8, qf);
-  const T* kb = static_cast<const T*>(p.k_idx) + (static_cast<long long>(b) * p.N + start) * kIdxDim + e * 8;
-  for (int iw = wave * 8; iw < n; iw += NW * 8 * kScoreUnroll) {
-    Raw8<T> raw[kScoreUnroll];
+  QFrag<T> qv;
+  qv.load(static_cast<const T*>(p.q_idx) + static_cast<long long>(b) * kIdxDim + e * 8);
+  for (int start = share_lo; start < share_hi; start += kTokScoreTile) {
+    const int n = min(kTokScoreTile, share_hi - start);
+    const T* kb = static_cast<const T*>(p.k_idx) + (static_cast<long long>(b) * p.N + start) * kIdxDim + e * 8;
+    for (int iw = wave * 8; iw < n; iw += NW * 8 * kScoreUnroll) {
+      Raw8<T> raw[kScoreUnroll];
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int i = min(iw + u * NW * 8 + tq, n - 1);  // clamped: straight-line loads
-      raw[u].load_stream(kb + static_cast<long long>(i) * kIdxDim);
-    }
+      for (int u = 0; u < kScoreUnroll; ++u) {
+        const int i = min(iw + u * NW * 8 + tq, n - 1);  // clamped: straight-line loads
+        raw[u].load_stream(kb + static_cast<long long>(i) * kIdxDim);
+      }
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int i = iw + u * NW * 8 + tq;
-      float x[8];
-      raw[u].widen(x);
-      const float sc = group8_sum(dot8(qf, x));
-      if (e == 0 && i < n) sk[i] = order_key(sc);
+      for (int u = 0; u < kScoreUnroll; ++u) {
+        const int i = iw + u * NW * 8 + tq;
+        const float sc = group8_sum(qv.dot(raw[u]));
+        if (e == 0 && i < n) sk[i] = order_key(sc);
+      }
     }
+    __syncthreads();
+    uint32_t* kout = p.keys + static_cast<long long>(b) * p.N + start;
+    for (int i = tid; i < n; i += kScoreThreads) {
+      const uint32_t kv = sk[i];
+      kout[i] = kv;
+      atomicAdd(&h[kv >> kHistShift], 1);
+    }
+    __syncthreads();  // the next sub-tile overwrites sk
   }
-  __syncthreads();
-  uint32_t* kout = p.keys + static_cast<long long>(b) * p.N + start;
-  for (int i = tid; i < n; i += kScoreThreads) {
-    const uint32_t kv = sk[i];
-    kout[i] = kv;
-    atomicAdd(&h[kv >> kHistShift], 1);
-  }
-  __syncthreads();
   int32_t* gh = p.hist + static_cast<long long>(b) * kTokHistBins;
   for (int i = tid; i < kTokHistBins; i += kScoreThreads) {
     const int c = h[i];
@@ -331,7 +344,11 @@ template <typename T>
 static hipError_t token_select_typed(const TokenSelectParams& p, hipStream_t s) {
   hipError_t e = launch_fill_i32(p.hist, static_cast<long long>(p.B) * kTokHistBins, 0, s);
   if (e != hipSuccess) return e;
-  const int nscore = (p.N + kTokScoreTile - 1) / kTokScoreTile;
+  // shares per request: kScoreWorkgroups in all (every CU the same number of
+  // workgroups), at least kScoreMinShare tokens each, at least one
+  const long long want = (kScoreWorkgroups + p.B - 1) / p.B;
+  const long long most = (static_cast<long long>(p.N) + kScoreMinShare - 1) / kScoreMinShare;
+  const int nscore = static_cast<int>(std::max(1LL, std::min(want, most)));
   if (p.score_ev0 && (e = hipEventRecord(p.score_ev0, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(token_score_kernel<T>, dim3(nscore, p.B), dim3(kScoreThreads), 0, s, p);
   e = hipGetLastError();
