@@ -979,6 +979,9 @@ def record_traffic(args):
     except (OSError, ValueError):
         rec = {}
     workload = line["config"]["workload"]
+    # the workload's entries taken on another source no longer describe it
+    rec = {key: v for key, v in rec.items()
+           if key.split("/")[0] != workload or v.get("kernel_source_sha") == line["kernel_source_sha"]}
     bench_cmd = f"python -u bench.py --config {n} --steps {line['steps']} --warmup 0 --cpu-seconds 0"
     for kernel, alg in line["counter_kernels"].items():
         fetch, nf = _counter_kib(csv_of["FETCH_SIZE"], kernel)
