@@ -104,12 +104,11 @@ def test_tiny_fp32_workload(schedule):
     _decode_and_check(cfg, p, ref, [0], steps=4, schedule=schedule)
 
 
-@pytest.mark.parametrize("schedule", ["fused", "split", "staged"])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+# the split schedule scores bf16 codebooks only
+@pytest.mark.parametrize("dtype,schedule", [("f32", "fused"), ("f32", "staged"), ("bf16", "fused"),
+                                            ("bf16", "split"), ("bf16", "staged")])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_ragged_shapes(dtype, G, schedule):
-    if schedule == "split" and dtype == "f32":
-        pytest.skip("the split decode scores bf16 codebooks only")
     # N not a multiple of any tile, odd C, lists longer than one segment (and,
     # fused, than one round of a head's rows over the workgroup's waves)
     cfg = W.config(1, batch=3, n_tokens=3001, n_kv_heads=2, n_q_heads=2 * G, n_centroids=7,
@@ -213,11 +212,10 @@ def test_karat_shape_full_size(schedule):
     _decode_and_check(cfg, p, ref, [0], steps=2, schedule=schedule)
 
 
-@pytest.mark.parametrize("schedule", ["auto", "staged", "fused", "split"])
-@pytest.mark.parametrize("C,k", [(300, 10), (300, 64), (300, 100), (1000, 10)])
+# the per-head schedules hold k <= 64 lists
+@pytest.mark.parametrize("C,k,schedule", [(C, k, s) for C, k in ((300, 10), (300, 64), (300, 100), (1000, 10))
+                                          for s in ("auto", "staged", "fused", "split") if k <= 64 or s in ("auto", "staged")])
 def test_top_k_paths_and_ties(C, k, schedule):
-    if schedule in ("fused", "split") and k > 64:
-        pytest.skip("the per-head decodes hold k <= 64 lists")
     """Selections through every search of the k-th largest score: the short
     candidate search (k <= 64, several keys per lane), its fallback when more
     than 64 keys reach the candidate bound (an all-zero query ties every
