@@ -150,10 +150,13 @@ def test_selecting_every_list_is_dense_attention():
     assert out_error(out.cpu().numpy(), ref) <= OUT_TOL
 
 
-def test_empty_selection_gives_zero_and_flag():
+@pytest.mark.parametrize("dtype,schedule", [("f32", "auto"), ("f32", "staged"), ("bf16", "fused"),
+                                            ("bf16", "split"), ("bf16", "staged")])
+def test_empty_selection_gives_zero_and_flag(dtype, schedule):
     # Small centroids live in dims 0..63, three far centroids in dims 64..127 and
-    # own no keys. Head 0's query is a far centroid, so its top-1 list is empty;
-    # head 1's query is small centroid 1 itself (orthogonal to every far one).
+    # own no keys. Head 0's query is a far centroid, so its top-1 list is empty
+    # (under the split schedule every share of head 0 attends no row); head 1's
+    # query is small centroid 1 itself (orthogonal to every far one).
     g = torch.Generator().manual_seed(0)
     B, N, Hkv, G, C, d = 1, 600, 1, 2, 8, 128
     cent = torch.zeros(1, Hkv, C, d)
@@ -163,12 +166,14 @@ def test_empty_selection_gives_zero_and_flag():
     keys = (cent[0, 0, comp] + 0.3 * torch.randn(N, d, generator=g)).view(B, N, Hkv, d)
     vals = torch.randn(B, N, Hkv, d, generator=g)
     q = torch.stack([cent[0, 0, 6], cent[0, 0, 1]]).view(B, G, d)
-    announce("ivf empty selection")
-    keys, vals, cent, q = (x.to(DEV) for x in (keys, vals, cent, q))
+    announce(f"ivf empty selection dtype={dtype} schedule={schedule}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    keys, vals, cent, q = (x.to(DEV, dt) for x in (keys, vals, cent, q))
     offsets, ids = tsa.index_build(keys, cent)
     rows = torch.empty((B, G), dtype=torch.int32, device=DEV)
     sel = torch.empty((B, G, 1), dtype=torch.int32, device=DEV)
-    out = tsa.sparse_decode(q, cent, offsets, ids, keys, vals, 1, rows_out=rows, sel_out=sel)
+    p = {"centroids": cent, "keys": keys, "values": vals}
+    out = _decode(schedule, q, p, offsets, ids, 1, rows_out=rows, sel_out=sel)
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     assert sel[0, 0, 0].item() == 6 and sel[0, 1, 0].item() == 1
