@@ -252,6 +252,49 @@ def test_top_k_paths_and_ties(C, k, schedule):
             assert out_error(out_g[b, h], r.out) <= OUT_TOL
 
 
+@pytest.mark.parametrize("k", [3, 5, 7])
+def test_exact_ties_among_the_top_lists(k):
+    """Five identical centroid rows (lists 7, 100, 101, 102, 103) hold the
+    largest score of a query that equals them: their scores tie exactly, in
+    the candidate ranking of the selection. k = 3 takes three of the five
+    (the lowest ids), k = 5 all of them, k = 7 all plus the next two. The
+    lists of every schedule equal the oracle's top-k (ties to the lower id);
+    outputs agree across schedules. (Keys assigned to identical centroids
+    tie too, so the index is not compared with the oracle's here.)"""
+    cfg = W.config(1, batch=2, n_tokens=8000, n_kv_heads=2, n_q_heads=8, n_centroids=300, top_k=k, steps=1,
+                   shared_codebook=True, seed=33)
+    announce(f"ivf exact ties k={k}")
+    p = _problem(cfg)
+    cent = p["centroids"].clone()
+    for c in (100, 101, 102, 103):
+        cent[:, :, c] = cent[:, :, 7]
+    p = dict(p, centroids=cent)
+    offsets, ids = tsa.index_build(p["keys"], cent)
+    q = W.ivf_queries(cfg, cent, steps=1)[0].clone()
+    q[0, 1] = cent[0, 0, 7]      # request 0, head 1 (KV head 0)
+    q[1, 6] = cent[0, 1, 7]      # request 1, head 6 (KV head 1)
+    B, Hq, G = cfg.batch, cfg.n_q_heads, cfg.group
+    q64, c64 = f64(q), f64(cent)
+    # the tied heads against the oracle (the other heads' random queries are
+    # not conditioned on a score gap: they are compared across schedules only)
+    want = {(b, h): ivf.top_k(ivf.centroid_scores(q64[b, h], c64[0, h // G]), k) for b, h in ((0, 1), (1, 6))}
+    tied = [7, 100, 101, 102, 103]
+    for w in want.values():  # the oracle's own reading of the ties
+        assert set(tied[:min(k, 5)]) <= set(w.tolist()) and (k > 5 or not set(tied[k:]) & set(w.tolist()))
+    outs, sels = {}, {}
+    for schedule in ("staged", "fused", "split"):
+        sel = torch.empty((B, Hq, k), dtype=torch.int32, device=DEV)
+        outs[schedule] = _decode(schedule, q, p, offsets, ids, k, sel_out=sel)
+        torch.cuda.synchronize()
+        sels[schedule] = sel
+        sel_g = sel.cpu().numpy()
+        for (b, h), w in want.items():
+            assert np.array_equal(sel_g[b, h], w), f"{schedule}: selection differs (request {b}, head {h})"
+    for schedule in ("fused", "split"):
+        assert torch.equal(sels[schedule], sels["staged"])
+        assert out_error(outs[schedule].cpu().numpy(), outs["staged"].cpu().numpy()) <= 1e-4
+
+
 def test_split_and_fused_scoring_choose_the_same_lists():
     """Staged small batches score the centroids in a launch of their own,
     large ones inside the selection kernel, and the fused decode inside its
