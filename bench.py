@@ -313,16 +313,16 @@ def bench_ivf(args, cfg, torch, tsa, W):
             need = tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX, desc, k)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
-    def call(i):
+    def decode(i, bind=False):
         if variant:
-            tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
-                                 similarity=args.similarity, n_sink=args.sink, n_window=args.window, alt=alt,
-                                 out=out, uniq_out=uniq[i % nq], ws=ws, schedule=args.schedule)
-        else:
-            tsa.sparse_decode(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
-                              out=out, uniq_out=uniq[i % nq], ws=ws)
+            return tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
+                                        similarity=args.similarity, n_sink=args.sink, n_window=args.window,
+                                        alt=alt, out=out, uniq_out=uniq[i % nq], ws=ws, schedule=args.schedule,
+                                        bind=bind)
+        return tsa.sparse_decode(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
+                                 out=out, uniq_out=uniq[i % nq], ws=ws, bind=bind)
 
-    res = _timed(args, call, torch, tsa, n_distinct=nq)
+    res = _timed(args, bound_steps(args, decode, nq), torch, tsa, n_distinct=nq)
     # rows read per step: unique list rows, plus the sink / window rows (an
     # upper bound: a list row inside those ranges is read once, counted twice;
     # with m lists per key, list entries: a token in several chosen lists of
@@ -564,11 +564,11 @@ def bench_token(args, cfg, torch, tsa, W):
     desc = tsa.binding.token_desc(prob["k_idx"], prob["keys"], Hq)
     ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_TOKEN_DECODE, desc, k), dtype=torch.uint8, device=dev)
 
-    def call(i):
-        tsa.token_decode(q_idx[i % nq], prob["k_idx"], q[i % nq], prob["keys"], prob["values"], k,
-                         out=out, ws=ws)
+    def decode(i, bind=False):
+        return tsa.token_decode(q_idx[i % nq], prob["k_idx"], q[i % nq], prob["keys"], prob["values"], k,
+                                out=out, ws=ws, bind=bind)
 
-    res = _timed(args, call, torch, tsa, n_distinct=nq, kernels=("gather", "token_scan"))
+    res = _timed(args, bound_steps(args, decode, nq), torch, tsa, n_distinct=nq, kernels=("gather", "token_scan"))
     res["gathered_bytes"] = args.steps * B * cfg.n_kv_heads * k * ROW_BYTES_BF16
     res["step_bytes"] = [B * cfg.n_kv_heads * k * ROW_BYTES_BF16] * args.steps
     # the scan reads every indexer key (d_idx bf16) and writes one 4-byte score key per token
@@ -744,6 +744,19 @@ def bench_cache(args, cfg, torch, tsa, W):
     if args.cpu_seconds > 0:
         res["cpu_sample"] = ("cache",) + cpu_sample_cache(cfg, hk.tensor, hv.tensor, q, trace, min(steps, 64), torch)
     return res
+
+
+def bound_steps(args, decode, n_distinct):
+    """The step function of a decode workload: decode(i) runs step i, whose
+    inputs repeat with period n_distinct. Eager runs bind each distinct
+    step's call once (the binding checks and marshals its arguments then) and
+    issue it per step as one foreign call, as a serving loop calling the C
+    ABI would; every kernel still runs each step. Graph capture records the
+    plain call on the capturing stream."""
+    if args.graph:
+        return decode
+    bound = [decode(j, bind=True) for j in range(n_distinct)]
+    return lambda i: bound[i % n_distinct]()
 
 
 def _timed(args, call, torch, tsa, n_distinct, offset=0, kernels=("gather",)):

@@ -262,6 +262,24 @@ def test_binding_refuses_host_tensors():
         B.index_build(x, c)
 
 
+def test_bound_call_reissues_its_call_and_raises_a_failure_status(lib):
+    """BoundCall issues the stored foreign call with the stored arguments on
+    every call, returns the stored result, and turns a failure status into
+    TsaError as the direct calls do."""
+    seen = []
+
+    def fn(*args):
+        seen.append(args)
+        return B.TSA_OK if len(seen) < 3 else B.TSA_ERR_INVALID_ARG
+
+    keep = object()
+    call = B.BoundCall(fn, (7, None, 3.5), (keep,), "result")
+    assert call() == "result" and call() == "result"
+    with pytest.raises(B.TsaError, match="TSA_ERR_INVALID_ARG"):
+        call()
+    assert seen == [(7, None, 3.5)] * 3
+
+
 def _ivf_ws(B_, N, Hkv, Hq, C, k, rows, keys):
     """Workspace bytes of a plain sparse decode whose lists are cut into
     `rows`-row plan segments (layout: descriptors, counts, partial states,

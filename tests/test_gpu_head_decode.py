@@ -2,7 +2,8 @@
 and against the staged launches, through the C ABI: fused (one workgroup per
 query head scores the codebook, selects the lists and attends their rows in
 one launch) and split (a scoring launch, then workgroups per share of each
-head's rows select the head's lists and attend their share, then combine).
+head's rows select the head's lists and attend their share; the head's last
+share to finish merges the shares' states).
 
 Bars as for the staged path: selected lists, per-head row counts and union
 counts bit-exact; outputs within OUT_TOL of the oracle; per-head and staged
@@ -118,3 +119,37 @@ def test_growing_index_per_head_and_staged_agree():
         assert np.array_equal(sel[0].cpu().numpy(), r["sel"][0])
         assert np.array_equal(rows[0].cpu().numpy(), r["n_rows"][0])
         assert out_error(out[0].cpu().numpy(), r["out"][0]) <= OUT_TOL
+
+
+def test_split_merge_by_the_last_share_is_repeatable():
+    """The split decode's last share to finish merges the head's records in
+    share order, whatever order the shares finish in, and each call's
+    scoring launch clears the arrival counters: forty calls in a row (two
+    inputs alternating, the second with fewer rows per head) give
+    bit-identical outputs per input, within PATH_TOL of the staged launches
+    and, for one request at the conditioned k, within OUT_TOL of the
+    oracle."""
+    cfg = W.config(1, batch=2, n_tokens=30_000, n_kv_heads=4, n_q_heads=16, n_centroids=300, top_k=10, steps=2,
+                   shared_codebook=False, seed=65)
+    announce("split merge, 40 calls")
+    p = _problem(cfg)
+    offsets, ids = tsa.index_build(p["keys"], p["centroids"])
+    ref = _check_index(p, [1], offsets, ids)
+    qs = conditioned_ivf_queries(cfg, p["centroids"], 2)
+    k_small = 3
+    first = {}
+    for i in range(40):
+        j = i % 2
+        k = cfg.top_k if j == 0 else k_small
+        out = _decode("split", qs[j], p, offsets, ids, k).clone()
+        if j not in first:
+            first[j] = out
+        else:
+            assert torch.equal(out, first[j]), f"call {i} differs from the first call on the same input"
+    for j, k in ((0, cfg.top_k), (1, k_small)):
+        staged = _decode("staged", qs[j], p, offsets, ids, k)
+        assert out_error(first[j].cpu().numpy(), staged.cpu().numpy()) <= PATH_TOL
+    # the oracle at the k the queries were conditioned for
+    r = ivf.sparse_decode(f64(qs[0][1:2]), f64(p["centroids"][1:2]), ref[1][0][None], ref[1][1][None],
+                          f64(p["keys"][1:2]), f64(p["values"][1:2]), cfg.top_k)
+    assert out_error(first[0][1].cpu().numpy(), r["out"][0]) <= OUT_TOL

@@ -8,6 +8,7 @@ entry point raises ImportError when it has not been built.
 
 from . import workloads  # noqa: F401
 from .binding import (  # noqa: F401
+    BoundCall,
     HostArray,
     TsaError,
     abi_version,
@@ -39,5 +40,5 @@ __all__ = [
     "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "index_build_multi", "index_build_dyn_multi", "index_regrow", "kv_append", "sparse_decode",
     "sparse_decode_dyn", "sparse_decode_ex", "sparse_decode_noalloc", "token_decode",
     "attend_rows", "resolve", "cache_reset", "fetch_rows", "hier_group_step", "HostArray", "time_next_gather", "time_next_launch", "stream_read", "workspace_bytes",
-    "TsaError",
+    "TsaError", "BoundCall",
 ]

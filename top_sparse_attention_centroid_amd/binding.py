@@ -138,6 +138,35 @@ def _check(status: int):
         raise TsaError(status, load().tsa_last_error().decode())
 
 
+class BoundCall:
+    """A library call whose arguments were checked and marshalled once (the
+    decode functions below with bind=True). Calling it issues the same C call
+    again -- same tensors, sizes and stream -- with no Python-side checks; the
+    C entry point still validates its arguments, and a failure status raises
+    TsaError. Every kernel of the call runs on each call; only the host work
+    shrinks, to the one foreign call (a serving loop that calls the C ABI
+    directly gets the same). Holds references to what it points at; the
+    tensors' contents may change between calls, their storage may not."""
+    __slots__ = ("_fn", "_args", "_keep", "result")
+
+    def __init__(self, fn, args, keep, result):
+        self._fn, self._args, self._keep, self.result = fn, args, keep, result
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status:
+            _check(status)
+        return self.result
+
+
+def _issue(bind: bool, fn, args: tuple, keep: tuple, result):
+    """Run the C call now, or (bind) return it as a BoundCall."""
+    if bind:
+        return BoundCall(fn, args, keep, result)
+    _check(fn(*args))
+    return result
+
+
 # ----------------------------------------------------------------------------
 # marshalling helpers
 # ----------------------------------------------------------------------------
@@ -410,7 +439,8 @@ def index_regrow(offsets, lens, ids, alt=None, slack: int = -1, *, out=None, sta
 
 def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, similarity: str = "dot",
                      n_sink: int = 0, n_window: int = 0, lengths=None, lens=None, alt=None, out=None,
-                     sel_out=None, rows_out=None, uniq_out=None, ws=None, stream=None, schedule: str = "auto"):
+                     sel_out=None, rows_out=None, uniq_out=None, ws=None, stream=None, schedule: str = "auto",
+                     bind: bool = False):
     """Decode with the variants: cosine similarity and/or the first n_sink and
     last n_window tokens (before lengths[b]) attended beside the lists; with
     `alt` (an m-way index from index_build_multi or index_build_dyn_multi)
@@ -419,7 +449,8 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
     gather, combine launches), "fused" (one launch) or "split" (scoring, a
     select + attend launch over shares of each head's rows, combine); fused
     and split take plain decodes (one list per key, no sink or window,
-    C <= 1024, k <= 64), split bf16 only."""
+    C <= 1024, k <= 64), split bf16 only. bind=True returns the call as a
+    BoundCall instead of running it."""
     for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
@@ -450,11 +481,12 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
                       SCHEDULE[schedule])
     ws = (_workspace(OP_SPARSE_DECODE_EX_MULTI, desc, k, ws, q.device, m) if m > 1
           else _workspace(OP_SPARSE_DECODE_EX, desc, k, ws, q.device))
-    _check(load().tsa_sparse_decode_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(centroids),
-                                       _ptr(offsets), _ptr(ids), _ptr(k_cache), _ptr(v_cache), k, _ptr(out),
-                                       _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(),
-                                       _stream(stream)))
-    return out
+    args = (ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(centroids), _ptr(offsets), _ptr(ids),
+            _ptr(k_cache), _ptr(v_cache), k, _ptr(out), _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws),
+            ws.numel(), _stream(stream))
+    keep = (desc, opts, q, centroids, offsets, ids, k_cache, v_cache, lengths, lens, alt, sel_out, rows_out,
+            uniq_out, ws)
+    return _issue(bind, load().tsa_sparse_decode_ex, args, keep, out)
 
 
 def sparse_decode_dyn(q, centroids, offsets, lens, ids, k_cache, v_cache, k: int, **kw):
@@ -463,8 +495,9 @@ def sparse_decode_dyn(q, centroids, offsets, lens, ids, k_cache, v_cache, k: int
 
 
 def sparse_decode(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, out=None, sel_out=None,
-                  rows_out=None, uniq_out=None, ws=None, stream=None, lens=None):
-    """One retrieval-based sparse-attention decode step. Returns out [B][Hq][d] fp32."""
+                  rows_out=None, uniq_out=None, ws=None, stream=None, lens=None, bind: bool = False):
+    """One retrieval-based sparse-attention decode step. Returns out [B][Hq][d]
+    fp32 (bind=True: the call as a BoundCall, not run)."""
     for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
@@ -485,17 +518,16 @@ def sparse_decode(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, out=N
     _i32(rows_out, "rows_out", (B, Hq))
     _i32(uniq_out, "uniq_out", (B, Hkv))
     ws = _workspace(OP_SPARSE_DECODE, desc, k, ws, q.device)
+    keep = (desc, q, centroids, offsets, ids, k_cache, v_cache, lens, sel_out, rows_out, uniq_out, ws)
+    tail = (_ptr(k_cache), _ptr(v_cache), k, _ptr(out), _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws),
+            ws.numel(), _stream(stream))
     if lens is None:
-        _check(load().tsa_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(centroids), _ptr(offsets), _ptr(ids),
-                                        _ptr(k_cache), _ptr(v_cache), k, _ptr(out), _ptr(sel_out),
-                                        _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(), _stream(stream)))
-    else:
-        _i32(lens, "lens", (B, Hkv, C))
-        _check(load().tsa_sparse_decode_dyn(ctypes.byref(desc), _ptr(q), _ptr(centroids), _ptr(offsets),
-                                            _ptr(lens), _ptr(ids), _ptr(k_cache), _ptr(v_cache), k, _ptr(out),
-                                            _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws), ws.numel(),
-                                            _stream(stream)))
-    return out
+        return _issue(bind, load().tsa_sparse_decode,
+                      (ctypes.byref(desc), _ptr(q), _ptr(centroids), _ptr(offsets), _ptr(ids)) + tail, keep, out)
+    _i32(lens, "lens", (B, Hkv, C))
+    return _issue(bind, load().tsa_sparse_decode_dyn,
+                  (ctypes.byref(desc), _ptr(q), _ptr(centroids), _ptr(offsets), _ptr(lens), _ptr(ids)) + tail,
+                  keep, out)
 
 
 def sparse_decode_noalloc(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, out, sel_out=None,
@@ -526,8 +558,9 @@ def sparse_decode_noalloc(q, centroids, offsets, ids, k_cache, v_cache, k: int, 
 
 
 def token_decode(q_idx, k_idx, q, k_cache, v_cache, k: int, *, out=None, sel_out=None, ws=None,
-                 stream=None):
-    """Token-indexer top-k + attention. Returns out [B][Hq][d] fp32."""
+                 stream=None, bind: bool = False):
+    """Token-indexer top-k + attention. Returns out [B][Hq][d] fp32
+    (bind=True: the call as a BoundCall, not run)."""
     for t, n in ((q_idx, "q_idx"), (k_idx, "k_idx"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
     if not (q_idx.dtype == k_idx.dtype == q.dtype == k_cache.dtype == v_cache.dtype):
@@ -540,10 +573,9 @@ def token_decode(q_idx, k_idx, q, k_cache, v_cache, k: int, *, out=None, sel_out
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     _i32(sel_out, "sel_out", (B, k))
     ws = _workspace(OP_TOKEN_DECODE, desc, k, ws, q.device)
-    _check(load().tsa_token_decode(ctypes.byref(desc), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k_cache),
-                                   _ptr(v_cache), k, _ptr(out), _ptr(sel_out), _ptr(ws), ws.numel(),
-                                   _stream(stream)))
-    return out
+    args = (ctypes.byref(desc), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k_cache), _ptr(v_cache), k, _ptr(out),
+            _ptr(sel_out), _ptr(ws), ws.numel(), _stream(stream))
+    return _issue(bind, load().tsa_token_decode, args, (desc, q_idx, k_idx, q, k_cache, v_cache, sel_out, ws), out)
 
 
 def attend_rows(q, k_rows, v_rows, row_ids, row_counts=None, *, out=None, ws=None, stream=None):

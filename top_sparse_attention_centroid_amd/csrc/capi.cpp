@@ -426,14 +426,15 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
       return ok();
     }
     hp.s.keys = reinterpret_cast<uint32_t*>(w + L.keys);
+    // the plan's segment region (unused here) holds the arrival counters,
+    // B * Hq of them (smax >= G)
+    hp.s.arrive = reinterpret_cast<uint32_t*>(w + L.seg);
     hp.partial = reinterpret_cast<float*>(w + L.partial);
     hp.S = split_shares(d, k, L);
     hipError_t e = launch_centroid_score(hp.s, L.G, s);
     if (e != hipSuccess) return hip_fail(e, "centroid_score launch");
     e = launch_between(g_gather_evs, s, [&] { return launch_split_decode(hp, L.G, s); });
     if (e != hipSuccess) return hip_fail(e, "split decode launch");
-    e = launch_split_combine(hp, L.G, s);
-    if (e != hipSuccess) return hip_fail(e, "split combine launch");
     return ok();
   }
   if (m > 1) selp.lmask_out = reinterpret_cast<uint32_t*>(w + L.lmask);

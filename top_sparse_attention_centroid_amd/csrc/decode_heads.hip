@@ -27,8 +27,8 @@
 //     softmax per lane group;
 //  4. the lane groups merge by shuffles, the waves through LDS; fused: wave 0
 //     writes o / l (zero when no row was selected); split: it writes the
-//     share's partial state as record h * S + s of the group, and
-//     split_combine_kernel merges each head's S records.
+//     share's partial state as record h * S + s of the group and counts in,
+//     and the head's last share to count in merges its S records.
 #include <type_traits>
 
 #include "attn_rows.hpp"
@@ -42,6 +42,65 @@ namespace tsa {
 // 4 fp32 rows, within the 128 VGPRs a wave has at 16 waves per CU
 template <typename T>
 constexpr int head_unroll() { return sizeof(T) == 2 ? kGatherUnroll : kGatherUnroll / 2; }
+
+// Split decode, end of a share (wave 0 holding the share's merged state):
+// the state goes out with agent-scope stores, which write through the XCD's
+// L2, and once the wave has seen them complete it counts in on the head's
+// arrival counter. The share that counts in last gets true and merges the
+// head. No L2 write-back is needed, since every word of a record is written
+// and read at agent scope; the counters are cleared by centroid_score_kernel,
+// launched before in the same stream.
+__device__ __forceinline__ bool publish_share(float* rec, const HeadState& st, int r, int e, uint32_t* arrive,
+                                              int S) {
+  if (r == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __hip_atomic_store(rec + kPartO + e * 8 + i, st.o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (r == 1 && e == 0) {
+    __hip_atomic_store(rec, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(rec + 1, st.l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  uint32_t n = 0;
+  if (lane_id() == 0) n = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __shfl(static_cast<int>(n), 0) == S - 1;
+}
+
+// The head's S records (rec0 + s * stride, s ascending) merged with the
+// log-sum-exp rule, o / l written to out[128] (zero when nothing was
+// selected). One wave, lane l holding o[2l], o[2l + 1]; eight records'
+// words requested before the first wait, all read at agent scope.
+__device__ __forceinline__ void merge_shares(const float* rec0, int S, long long stride, float* out) {
+  constexpr int kU = 8;
+  const int lane = lane_id();
+  auto ld = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  float M = kEmptyMax, L = 0.f, O0 = 0.f, O1 = 0.f;
+  for (int s0 = 0; s0 < S; s0 += kU) {
+    float m[kU], l[kU], o0[kU], o1[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float* ph = rec0 + min(s0 + u, S - 1) * stride;  // clamped: straight-line loads
+      m[u] = ld(ph);
+      l[u] = ld(ph + 1);
+      o0[u] = ld(ph + kPartO + lane * 2);
+      o1[u] = ld(ph + kPartO + lane * 2 + 1);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (s0 + u >= S) break;
+      const float Mn = fmaxf(M, m[u]);
+      const float a = fast_exp2(M - Mn), w = fast_exp2(m[u] - Mn);
+      L = L * a + l[u] * w;
+      O0 = O0 * a + o0[u] * w;
+      O1 = O1 * a + o1[u] * w;
+      M = Mn;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<float2*>(out + lane * 2) = make_float2(O0 * inv, O1 * inv);
+}
 
 template <typename T, int G, int KPL, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * kWave) void ivf_head_kernel(HeadDecodeParams p) {
@@ -232,9 +291,10 @@ __global__ __launch_bounds__(NW * kWave) void ivf_head_kernel(HeadDecodeParams p
     }
   }
   if constexpr (SPLIT) {
-    const int t = h * S + share;
-    float* part = p.partial + (static_cast<long long>(bg) * sp.smax + t) * G * kPartStride + h * kPartStride;
-    store_state(part, st, r, e);
+    const long long stride = static_cast<long long>(G) * kPartStride;  // floats between records
+    float* rec0 = p.partial + (static_cast<long long>(bg) * sp.smax + h * S) * stride + h * kPartStride;
+    const bool last = publish_share(rec0 + share * stride, st, r, e, sp.arrive + bh, S);
+    if (last) merge_shares(rec0, S, stride, p.out + (static_cast<long long>(b) * p.Hq + qh) * kHeadDim);
   } else {
     if (r == 0) {
       const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
@@ -243,47 +303,6 @@ __global__ __launch_bounds__(NW * kWave) void ivf_head_kernel(HeadDecodeParams p
       *reinterpret_cast<float4*>(o + 4) = make_float4(st.o[4] * inv, st.o[5] * inv, st.o[6] * inv, st.o[7] * inv);
     }
   }
-}
-
-// Split decode, last launch: merges the S partial states of each query head
-// with the log-sum-exp rule and writes o / l (zero when nothing was
-// selected). One wave per head, lane l holding o[2l], o[2l + 1]; the states
-// of eight shares are requested before the first wait.
-template <int G>
-__global__ __launch_bounds__(kWave) void split_combine_kernel(HeadDecodeParams p) {
-  constexpr int kU = 8;
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq, qh = bh % p.Hq;
-  const int g = qh / G, h = qh % G;
-  const int bg = b * p.s.Hkv + g;
-  const int lane = lane_id(), S = p.S;
-  const long long stride = static_cast<long long>(G) * kPartStride;  // floats between records
-  const float* base = p.partial + (static_cast<long long>(bg) * p.s.smax + h * S) * stride + h * kPartStride;
-  float M = kEmptyMax, L = 0.f, O0 = 0.f, O1 = 0.f;
-  for (int s0 = 0; s0 < S; s0 += kU) {
-    float m[kU], l[kU];
-    float2 o[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const float* ph = base + min(s0 + u, S - 1) * stride;  // clamped: straight-line loads
-      m[u] = ph[0];
-      l[u] = ph[1];
-      o[u] = *reinterpret_cast<const float2*>(ph + kPartO + lane * 2);
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (s0 + u >= S) break;
-      const float Mn = fmaxf(M, m[u]);
-      const float a = fast_exp2(M - Mn), w = fast_exp2(m[u] - Mn);
-      L = L * a + l[u] * w;
-      O0 = O0 * a + o[u].x * w;
-      O1 = O1 * a + o[u].y * w;
-      M = Mn;
-    }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* out = p.out + (static_cast<long long>(b) * p.Hq + qh) * kHeadDim + lane * 2;
-  *reinterpret_cast<float2*>(out) = make_float2(O0 * inv, O1 * inv);
 }
 
 template <typename T, int G, int NW, bool SPLIT>
@@ -312,17 +331,6 @@ hipError_t launch_fused_decode(const HeadDecodeParams& p, int dtype, int G, hipS
 
 hipError_t launch_split_decode(const HeadDecodeParams& p, int G, hipStream_t s) {
   head_dispatch<bf16_t, kSplitWaves, true>(p, G, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_split_combine(const HeadDecodeParams& p, int G, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(p.s.B * p.Hq)), block(kWave);
-  switch (G) {
-    case 1: hipLaunchKernelGGL(split_combine_kernel<1>, grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(split_combine_kernel<2>, grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL(split_combine_kernel<4>, grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL(split_combine_kernel<8>, grid, block, 0, s, p); break;
-  }
   return hipGetLastError();
 }
 

@@ -90,6 +90,8 @@ struct SelectParams {
                            // (bf16 only), or null: the select kernel scores the centroids itself
   int class_order;         // 1: plan segments by head class (merged gather sets), 0: list order
   int lens_lds = 0;        // set by the launcher: the list lengths fit in LDS beside the offsets
+  uint32_t* arrive = nullptr;  // [B*Hkv][G] arrival counters of the split decode, cleared by
+                               // centroid_score_kernel, or null
 };
 constexpr int kSelWaves = 4;               // waves per select workgroup
 constexpr size_t kSelectLdsBytes = 65536;  // dynamic LDS of a select workgroup (keys, masks, offsets, lengths)
@@ -102,7 +104,7 @@ hipError_t launch_ivf_select(const SelectParams& p, int dtype, int G, hipStream_
 // Split: centroid_score_kernel first; then S workgroups of kSplitWaves waves
 // per query head each select the head's lists from the scores and attend
 // share s of its rows, writing a partial state per share (record h * S + s
-// of the group), which split_combine_kernel merges per head.
+// of the group); the head's last share to finish merges the S records.
 struct HeadDecodeParams {
   SelectParams s;          // q, centroids, offsets, lens, the sel / rows / uniq outputs, sizes,
                            // cosine, n_entries; split: keys (the scores), smax
@@ -121,7 +123,6 @@ constexpr int kHeadMaxC = 1024;   // lists of a group held in one workgroup's LD
 constexpr int kHeadMaxK = 64;     // chosen lists of a head, one per lane
 hipError_t launch_fused_decode(const HeadDecodeParams& p, int dtype, int G, hipStream_t s);
 hipError_t launch_split_decode(const HeadDecodeParams& p, int G, hipStream_t s);  // bf16 only
-hipError_t launch_split_combine(const HeadDecodeParams& p, int G, hipStream_t s);
 hipError_t launch_centroid_score(const SelectParams& p, int G, hipStream_t s);     // bf16; writes p.keys
 
 // ---------------------------------------------------------- KV + index append
