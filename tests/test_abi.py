@@ -284,13 +284,15 @@ def _ivf_ws(B_, N, Hkv, Hq, C, k, rows, keys):
     """Workspace bytes of a plain sparse decode whose lists are cut into
     `rows`-row plan segments (layout: descriptors, counts, partial states,
     and for bf16 the score keys of a scoring launch of its own, which the
-    staged path's small batches and every split decode use; each region 256-B
+    staged path's small batches and every split decode use, and the split
+    decode's arrival counters, one per query head; each region 256-B
     aligned)."""
     def al(x):
         return (x + 255) // 256 * 256
     G, bh = Hq // Hkv, B_ * Hkv
     smax = G * k + -(-N // rows)
-    return al(bh * smax * 16) + al(bh * 4) + al(bh * smax * G * PART_FLOATS * 4) + (al(bh * G * C * 4) if keys else 0)
+    return (al(bh * smax * 16) + al(bh * 4) + al(bh * smax * G * PART_FLOATS * 4)
+            + (al(bh * G * C * 4) + al(bh * G * 4) if keys else 0))
 
 
 @pytest.mark.parametrize("k,rows", [(8, 64), (12, 128), (16, 256)])

@@ -115,7 +115,20 @@ __device__ __forceinline__ void consume_batch(const Batch<T, U>& bt, HeadState& 
 // Writes a merged state (every lane group holds the same values after the
 // shuffle merge): lanes 0..15 write o, lanes 16..23 the header line
 // (m, l, zeros), so each 128-byte line of the record is written in full.
-__device__ __forceinline__ void store_state(float* ph, const HeadState& st, int r, int e) {
+// agent: every word written at agent scope (write-through past the XCD's L2),
+// for a merge by another workgroup within the same launch; only m, l and o
+__device__ __forceinline__ void store_state(float* ph, const HeadState& st, int r, int e, bool agent = false) {
+  if (agent) {
+    if (r == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __hip_atomic_store(ph + kPartO + e * 8 + i, st.o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (r == 1 && e == 0) {
+      __hip_atomic_store(ph, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ph + 1, st.l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
   if (r == 0) {
     *reinterpret_cast<float4*>(ph + kPartO + e * 8) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
     *reinterpret_cast<float4*>(ph + kPartO + 4 + e * 8) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);

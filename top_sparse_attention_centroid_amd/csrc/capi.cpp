@@ -111,7 +111,7 @@ FetchParams fetch_params(const tsa_cache_desc& d, const int32_t* miss_tok, const
 struct IvfLayout {
   int G = 0, smax = 0, seg_rows = 0;
   bool small_batch = false, split_score = false, merge = false;
-  size_t seg = 0, nseg = 0, partial = 0, lmask = 0, keys = 0, total = 0;
+  size_t seg = 0, nseg = 0, partial = 0, lmask = 0, keys = 0, arrive = 0, total = 0;
 };
 
 // A batch with fewer (request, KV head) groups than this is small: its decode
@@ -173,6 +173,8 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false, int 
   // batches and every split decode (any bf16 batch may ask for one)
   L.split_score = d.dtype == TSA_BF16 && L.small_batch;
   L.keys = off;    off += d.dtype == TSA_BF16 ? align_up(bh * L.G * d.n_centroids * sizeof(uint32_t)) : 0;
+  // arrival counters of the split decode (bf16), one per query head
+  L.arrive = off;  off += d.dtype == TSA_BF16 ? align_up(bh * L.G * sizeof(uint32_t)) : 0;
   L.total = off;
   return L;
 }
@@ -426,9 +428,7 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
       return ok();
     }
     hp.s.keys = reinterpret_cast<uint32_t*>(w + L.keys);
-    // the plan's segment region (unused here) holds the arrival counters,
-    // B * Hq of them (smax >= G)
-    hp.s.arrive = reinterpret_cast<uint32_t*>(w + L.seg);
+    hp.s.arrive_heads = reinterpret_cast<uint32_t*>(w + L.arrive);
     hp.partial = reinterpret_cast<float*>(w + L.partial);
     hp.S = split_shares(d, k, L);
     hipError_t e = launch_centroid_score(hp.s, L.G, s);

@@ -52,14 +52,7 @@ constexpr int head_unroll() { return sizeof(T) == 2 ? kGatherUnroll : kGatherUnr
 // launched before in the same stream.
 __device__ __forceinline__ bool publish_share(float* rec, const HeadState& st, int r, int e, uint32_t* arrive,
                                               int S) {
-  if (r == 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __hip_atomic_store(rec + kPartO + e * 8 + i, st.o[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else if (r == 1 && e == 0) {
-    __hip_atomic_store(rec, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(rec + 1, st.l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  store_state(rec, st, r, e, true);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -293,7 +286,7 @@ __global__ __launch_bounds__(NW * kWave) void ivf_head_kernel(HeadDecodeParams p
   if constexpr (SPLIT) {
     const long long stride = static_cast<long long>(G) * kPartStride;  // floats between records
     float* rec0 = p.partial + (static_cast<long long>(bg) * sp.smax + h * S) * stride + h * kPartStride;
-    const bool last = publish_share(rec0 + share * stride, st, r, e, sp.arrive + bh, S);
+    const bool last = publish_share(rec0 + share * stride, st, r, e, sp.arrive_heads + bh, S);
     if (last) merge_shares(rec0, S, stride, p.out + (static_cast<long long>(b) * p.Hq + qh) * kHeadDim);
   } else {
     if (r == 0) {

@@ -522,14 +522,14 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 // ============================================================================
 // Scoring as its own launch, for batches too small to fill the chip with one
 // workgroup per (request, KV head): grid (ceil(C / 64), B * Hkv), each wave
-// one 16-centroid tile, keys to p.keys; with p.arrive it also clears the
-// group's arrival counters of the split decode.
+// one 16-centroid tile, keys to p.keys; with p.arrive_heads it also clears
+// the group's arrival counters of the split decode.
 template <int G>
 __global__ __launch_bounds__(256) void centroid_score_kernel(SelectParams p) {
   const int bg = blockIdx.y;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   // the split decode's arrival counters of the group, for the launch after
-  if (p.arrive && blockIdx.x == 0 && threadIdx.x < G) p.arrive[bg * G + threadIdx.x] = 0u;
+  if (p.arrive_heads && blockIdx.x == 0 && threadIdx.x < G) p.arrive_heads[bg * G + threadIdx.x] = 0u;
   const int t = blockIdx.x * 4 + static_cast<int>(threadIdx.x) / kWave;
   const int ntile = (p.C + 15) / 16;
   if (t >= ntile) return;  // uniform over the wave

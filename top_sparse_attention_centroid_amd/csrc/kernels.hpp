@@ -90,8 +90,8 @@ struct SelectParams {
                            // (bf16 only), or null: the select kernel scores the centroids itself
   int class_order;         // 1: plan segments by head class (merged gather sets), 0: list order
   int lens_lds = 0;        // set by the launcher: the list lengths fit in LDS beside the offsets
-  uint32_t* arrive = nullptr;  // [B*Hkv][G] arrival counters of the split decode, cleared by
-                               // centroid_score_kernel, or null
+  uint32_t* arrive_heads = nullptr;  // [B*Hkv][G] arrival counters of the split decode, cleared
+                                     // by centroid_score_kernel, or null
 };
 constexpr int kSelWaves = 4;               // waves per select workgroup
 constexpr size_t kSelectLdsBytes = 65536;  // dynamic LDS of a select workgroup (keys, masks, offsets, lengths)
