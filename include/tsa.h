@@ -372,7 +372,8 @@ typedef enum tsa_similarity { TSA_SIM_DOT = 0, TSA_SIM_COSINE = 1 } tsa_similari
  *                     and attends in one launch
  *   TSA_SCHED_SPLIT   scoring, then S workgroups per (request, query head)
  *                     each select the head's lists and attend a share of its
- *                     rows, then combine (bf16 only)
+ *                     rows; the head's last share to finish merges the
+ *                     shares in that launch (bf16 only)
  * FUSED and SPLIT take plain list decodes only: one list per token, no sink
  * or window, C <= 1024, k <= 64 (else TSA_ERR_UNSUPPORTED). AUTO takes FUSED
  * when every head's work fits one CU (B * Hq <= 256, about k * N / C <= 512
