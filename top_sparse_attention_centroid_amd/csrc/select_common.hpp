@@ -165,10 +165,11 @@ static_assert(kMaxCentroids <= (1 << kListBits), "list ids fit the rank value");
 // maxima above its own, ties to the lower lane); when at most 64 keys reach
 // t1, each lane appends its own, with their lists, to the wave's LDS scratch
 // (cl: 128 values, the upper half one spare slot a lane for the keys it
-// drops) at its exclusive prefix count, the candidates are ranked
-// by (key, lower list id first), the k of lowest rank are taken, and each
-// finds its place among them in ascending list order by counting the taken
-// lists below its own. Otherwise (or for k > 64) thr, the k-th largest key,
+// drops) at its exclusive prefix count, and the candidates are ranked by
+// (key, lower list id first). The candidate of rank k - 1 holds the k-th
+// largest value T; the lists whose (key, list) value reaches T are taken, in
+// ascending list order straight from the keys' own layout (ballot prefix
+// counts). Otherwise (or for k > 64) thr, the k-th largest key,
 // is searched bit by bit over all keys, keys above it are taken, then keys
 // equal to it in ascending list order until k are taken.
 template <int KPL, typename Take>
@@ -219,17 +220,24 @@ __device__ __forceinline__ void topk_lists(const uint32_t (&kk)[KPL], int k, uin
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const uint64_t xc = lane < n_cand ? cl[lane] : 0u;
-        const int c = (1 << kListBits) - 1 - static_cast<int>(xc & ((1u << kListBits) - 1));  // its list
-        const bool tk = lane < n_cand && rank_among(cl, n_cand, xc) < k;
-        __builtin_amdgcn_wave_barrier();  // every lane has read the candidates
-        // place among the taken lists in ascending list order: the taken
-        // lists below c (stored complemented, so that they count as larger)
-        cl[lane] = tk ? ~static_cast<uint64_t>(c) : 0u;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int pos = rank_among(cl, n_cand, ~static_cast<uint64_t>(c));
-        if (tk) take(c, pos);
+        const int rk = lane < n_cand ? rank_among(cl, n_cand, xc) : kWave;
+        // the k-th largest candidate value T (k <= n_cand: the keys >= t1
+        // number at least k); the taken lists are those whose value is >= T
+        const int at_k = static_cast<int>(__builtin_ctzll(__ballot(rk == k - 1)));  // one lane
+        const uint64_t T = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl(static_cast<int>(xc >> 32), at_k)))
+                            << 32) |
+                           static_cast<uint32_t>(__shfl(static_cast<int>(xc & 0xffffffffu), at_k));
+        // emitted from the keys' own layout in ascending list order, placed
+        // by ballot prefix counts (values are distinct, so exactly k)
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const int c = j * kWave + lane;
+          const bool tk = key_rank_value<kListBits>(kk[j], c) >= T;
+          const uint64_t tm = __ballot(tk);
+          if (tk) take(c, base + prefix_count(tm));
+          base += __popcll(tm);
+        }
         __builtin_amdgcn_wave_barrier();  // a later call of this wave reuses cl
         return;
       }
