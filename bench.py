@@ -211,15 +211,24 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
                          device=dev)
     torch.cuda.synchronize()
 
-    def call(i):
+    def bind_step(i):
+        """Step i's decode and append, bound once (see bound_steps)."""
         if m == 1 and args.schedule == "auto":
-            tsa.sparse_decode_dyn(q_all[i % nq], p["centroids"], offsets, lens, ids, k_cache, v_cache, k,
-                                  out=out, uniq_out=uniq[i], ws=ws)
+            dec = tsa.sparse_decode_dyn(q_all[i % nq], p["centroids"], offsets, lens, ids, k_cache, v_cache, k,
+                                        out=out, uniq_out=uniq[i], ws=ws, bind=True)
         else:
-            tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, k_cache, v_cache, k, lens=lens, alt=alt,
-                                 out=out, uniq_out=uniq[i], ws=ws, schedule=args.schedule)
-        tsa.kv_append(new_k[i], new_v[i], pos[i], p["centroids"], k_cache, v_cache, offsets, lens, ids, alt=alt,
-                      status=status[i])
+            dec = tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, k_cache, v_cache, k, lens=lens,
+                                       alt=alt, out=out, uniq_out=uniq[i], ws=ws, schedule=args.schedule, bind=True)
+        app = tsa.kv_append(new_k[i], new_v[i], pos[i], p["centroids"], k_cache, v_cache, offsets, lens, ids,
+                            alt=alt, status=status[i], bind=True)
+        return dec, app
+
+    steps = [bind_step(i) for i in range(total)]
+
+    def call(i):
+        dec, app = steps[i]
+        dec()
+        app()
 
     res = _timed(args, call, torch, tsa, n_distinct=total, offset=args.warmup)
     row_bytes = 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)

@@ -60,3 +60,40 @@ def test_bound_token_decode_matches_the_direct_call():
         assert torch.equal(got_sel, want_sel), f"step {j}: selections differ"
         assert torch.equal(got, want), f"step {j}: outputs differ"
 
+
+
+def test_bound_growing_index_steps_match_the_direct_calls():
+    """Decode over a growing index and append the step's token, three steps,
+    once through bound calls (bound before the first step) and once through
+    direct calls on copies of the same cache and lists: the same outputs,
+    statuses, lengths and list entries."""
+    cfg = W.config(1, batch=2, n_tokens=6000, n_kv_heads=2, n_q_heads=8, n_centroids=50, top_k=5, steps=3,
+                   shared_codebook=False, seed=66)
+    announce("bound growing-index steps")
+    p = W.ivf_problem(cfg, device=DEV)
+    qs = W.ivf_queries(cfg, p["centroids"], steps=3)
+    prefix, steps = 5000, 3
+    B, Hq, Hkv, k = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.top_k
+    off, lens, ids = tsa.index_build_dyn(p["keys"], p["centroids"], prefix, 20)
+    new_k = p["keys"][:, prefix:prefix + steps].transpose(0, 1).contiguous()
+    new_v = p["values"][:, prefix:prefix + steps].transpose(0, 1).contiguous()
+    pos = (prefix + torch.arange(steps, device=DEV, dtype=torch.int32))[:, None].expand(steps, B).contiguous()
+    runs = []
+    for bound in (True, False):
+        kc, vc, ln, ix = p["keys"].clone(), p["values"].clone(), lens.clone(), ids.clone()
+        out = torch.empty((steps, B, Hq, cfg.head_dim), dtype=torch.float32, device=DEV)
+        st = torch.empty((steps, B, Hkv), dtype=torch.int32, device=DEV)
+        calls = []
+        for i in range(steps):
+            kw = dict(out=out[i], bind=True) if bound else dict(out=out[i])
+            dec = lambda i=i, kw=kw: tsa.sparse_decode_dyn(qs[i], p["centroids"], off, ln, ix, kc, vc, k, **kw)
+            app = lambda i=i, b=bound: tsa.kv_append(new_k[i], new_v[i], pos[i], p["centroids"], kc, vc, off, ln, ix,
+                                                     status=st[i], bind=b)
+            calls.append((dec(), app()) if bound else (dec, app))
+        for d, a in calls:
+            d()
+            a()
+        torch.cuda.synchronize()
+        runs.append((out, st, ln, ix))
+    for a, b, what in zip(runs[0], runs[1], ("outputs", "statuses", "lengths", "list entries")):
+        assert torch.equal(a, b), f"bound and direct {what} differ"

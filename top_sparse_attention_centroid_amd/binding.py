@@ -305,10 +305,11 @@ def index_build_dyn(keys, centroids, n_prefix: int, slack: Optional[int] = None,
 
 
 def kv_append(new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids, *, alt=None, status=None,
-              stream=None):
+              stream=None, bind: bool = False):
     """Store one new token per request at row pos[b] and add it to its posting
     list (with `alt`, an m-way index: to its m nearest lists, all or none).
-    Returns status [B][Hkv] int32 (0 indexed, 1 a list full, 2 bad row)."""
+    Returns status [B][Hkv] int32 (0 indexed, 1 a list full, 2 bad row);
+    bind=True: the call as a BoundCall, not run."""
     for t, n in ((new_k, "new_k"), (new_v, "new_v"), (centroids, "centroids"), (k_cache, "k_cache"),
                  (v_cache, "v_cache")):
         _dev(t, n)
@@ -329,10 +330,10 @@ def kv_append(new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids
     if status is None:
         status = torch.empty((B, Hkv), dtype=torch.int32, device=k_cache.device)
     _i32(status, "status", (B, Hkv))
-    _check(load().tsa_kv_append_multi(ctypes.byref(desc), m, _ptr(new_k), _ptr(new_v), _ptr(pos), _ptr(centroids),
-                                      _ptr(k_cache), _ptr(v_cache), _ptr(offsets), _ptr(lens), _ptr(ids), _ptr(alt),
-                                      _ptr(status), _stream(stream)))
-    return status
+    args = (ctypes.byref(desc), m, _ptr(new_k), _ptr(new_v), _ptr(pos), _ptr(centroids), _ptr(k_cache),
+            _ptr(v_cache), _ptr(offsets), _ptr(lens), _ptr(ids), _ptr(alt), _ptr(status), _stream(stream))
+    keep = (desc, new_k, new_v, pos, centroids, k_cache, v_cache, offsets, lens, ids, alt)
+    return _issue(bind, load().tsa_kv_append_multi, args, keep, status)
 
 
 def _alt_shape(B, Hkv, N, m):
