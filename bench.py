@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--schedule", default="auto", choices=["auto", "staged", "fused", "split"],
                     help="inverted-index decode: the library's choice, the staged launches, the fused single "
                          "launch or the split per-head launches (the last two: small plain decodes)")
+    ap.add_argument("--kv-layout", default="token", choices=["token", "lists"],
+                    help="inverted-index workloads: read the chosen lists' rows from the caches by token id "
+                         "(token), or from list-major copies of the caches built once after the index "
+                         "(lists: each list one contiguous run of rows)")
     ap.add_argument("--policy", default="lru", choices=["lru", "fifo", "random", "belady"],
                     help="hot-cache workload: replacement policy of RESOLVE (belady = offline, from the "
                          "trace's next-use steps)")
@@ -189,6 +193,8 @@ def bench_ivf_grow(args, cfg, torch, tsa, W):
         sys.exit(f"bench: --grow needs 1 <= PREFIX and PREFIX + warmup + steps <= {N}")
     if args.graph:
         sys.exit("bench: --grow changes the index every step; it runs eagerly")
+    if args.kv_layout != "token":
+        sys.exit("bench: --grow reads the caches by token id (the list-major copies describe a static index)")
     log(f"generating {cfg.name} on the GPU (growing from {prefix} tokens)")
     p = W.ivf_problem(cfg, device=dev)
     nq = min(cfg.steps, 64)
@@ -308,13 +314,22 @@ def bench_ivf(args, cfg, torch, tsa, W):
         offsets, ids = tsa.index_build(p["keys"], p["centroids"])
     torch.cuda.synchronize()
     index_ms = (time.perf_counter() - t0) * 1e3
+    k_lists = v_lists = None
+    lists_ms = None
+    if args.kv_layout == "lists":
+        t0 = time.perf_counter()
+        k_lists, v_lists = tsa.kv_list_major(ids, p["keys"], p["values"])
+        torch.cuda.synchronize()
+        lists_ms = (time.perf_counter() - t0) * 1e3
     out = torch.empty((B, Hq, cfg.head_dim), dtype=torch.float32, device=dev)
     uniq = torch.empty((nq, B, Hkv), dtype=torch.int32, device=dev)
     desc = tsa.binding.ivf_desc(p["keys"], p["centroids"], Hq)
     ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE, desc, k), dtype=torch.uint8, device=dev)
 
     variant = (args.similarity != "dot" or args.sink > 0 or args.window > 0 or alt is not None
-               or args.schedule != "auto")
+               or args.schedule != "auto" or k_lists is not None)
+    # the schedule and the K/V layout change how, not what, the step computes
+    same_math = args.similarity == "dot" and args.sink == 0 and args.window == 0 and alt is None
     if variant:
         if alt is not None:
             need = tsa.workspace_bytes(tsa.binding.OP_SPARSE_DECODE_EX_MULTI, desc, k, args.assign)
@@ -327,7 +342,7 @@ def bench_ivf(args, cfg, torch, tsa, W):
             return tsa.sparse_decode_ex(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
                                         similarity=args.similarity, n_sink=args.sink, n_window=args.window,
                                         alt=alt, out=out, uniq_out=uniq[i % nq], ws=ws, schedule=args.schedule,
-                                        bind=bind)
+                                        k_lists=k_lists, v_lists=v_lists, bind=bind)
         return tsa.sparse_decode(q_all[i % nq], p["centroids"], offsets, ids, p["keys"], p["values"], k,
                                  out=out, uniq_out=uniq[i % nq], ws=ws, bind=bind)
 
@@ -344,10 +359,12 @@ def bench_ivf(args, cfg, torch, tsa, W):
     row_bytes = 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
     res.update({"gathered_bytes": rows * row_bytes, "queries": B * args.steps, "index_build_ms": index_ms,
                 "unique_rows_per_step": rows / args.steps})
+    if lists_ms is not None:
+        res["kv_lists_build_ms"] = lists_ms
     if ivf_schedule(cfg, args) == "fused":
         # the fused kernel also scores the codebook: its bytes once per group
         res["gather_launch_bytes"] = [x + codebook_bytes(cfg) for x in res["step_bytes"]]
-    if args.cpu_seconds > 0 and not variant:
+    if args.cpu_seconds > 0 and same_math:
         res["cpu_sample"] = ("ivf",) + cpu_sample_ivf(cfg, p, q_all, torch)
     return res
 
@@ -1041,6 +1058,8 @@ def workload_name(cfg, args):
             workload += f"+{args.assign}-lists-per-key"
         if args.schedule != "auto":
             workload += f"+{args.schedule}"
+        if args.kv_layout != "token":
+            workload += "+list-major-kv"
     if cfg.kind == "cache" and (cfg.popularity_sd or cfg.recency):
         workload += f"+popularity{cfg.popularity_sd:g}+recency{cfg.recency:g}"
     if cfg.kind == "cache" and args.policy != "lru":
@@ -1145,7 +1164,9 @@ def gpu_run(args, torch):
         "config": {"workload": workload, "batch": res.get("batch", cfg.batch), "context": cfg.n_tokens,
                    "kv_heads": cfg.n_kv_heads, "q_heads": cfg.n_q_heads, "head_dim": cfg.head_dim,
                    "top_k": cfg.top_k, "centroids": cfg.n_centroids or None,
-                   "slots": cfg.n_slots or None, "parallelism": "none (1 GPU)"},
+                   "slots": cfg.n_slots or None, "parallelism": "none (1 GPU)",
+                   "kv_layout": ("list-major copies" if args.kv_layout == "lists" else "token-major caches")
+                   if cfg.kind == "ivf" else None},
         "gathered_kv_gbps": round(gb_s, 1),
         "gathered_kv_frac_of_peak": round(gb_s / HBM_PEAK_GBPS, 4),
         "graph": bool(args.graph),
@@ -1155,7 +1176,7 @@ def gpu_run(args, torch):
         "kernel_source_sha": kernel_source_sha(),
         "counter_kernels": counter_kernels(res, cfg, args),
     }
-    for key in ("index_build_ms", "unique_rows_per_step", "misses_per_step", "miss_rate_steady",
+    for key in ("index_build_ms", "kv_lists_build_ms", "unique_rows_per_step", "misses_per_step", "miss_rate_steady",
                 "fetched_bytes", "resolve", "append", "regrow", "layer_group", "indexer_bytes_per_step"):
         if key in res:
             line[key] = res[key]

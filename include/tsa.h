@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 2
+#define TSA_ABI_VERSION 3
 
 /* Size of the static device scratch of tsa_sparse_decode_noalloc. */
 #define TSA_NOALLOC_SCRATCH_BYTES (64u << 20)
@@ -354,6 +354,10 @@ tsa_status tsa_index_regrow(const tsa_ivf_desc* desc, int32_t m, const int32_t* 
  *   opts->alt         (device) int32 [B][Hkv][N*m][m-1] from the m-way build,
  *                     required when assign_per_key is 2 or more
  *   opts->schedule    tsa_schedule (0: AUTO)
+ *   opts->k_lists, opts->v_lists  (device, nullable) list-major copies of
+ *                     the caches from tsa_kv_list_major for this index: the
+ *                     chosen lists' rows are read from them (plain lists
+ *                     only: assign_per_key <= 1, no sink, window or lens)
  *   The attended set of a head is the union of its chosen lists' rows and
  *   the two ranges; a row in both is attended once. rows_out and uniq_out
  *   count list entries only. Workspace:
@@ -396,7 +400,30 @@ typedef struct tsa_decode_opts {
   const int32_t* lens;      /* device [B][Hkv][C] or NULL                   */
   const int32_t* alt;       /* device [B][Hkv][N*m][m-1] or NULL            */
   int32_t schedule;         /* tsa_schedule                                 */
+  const void* k_lists;      /* device [B][Hkv][N][d] from tsa_kv_list_major */
+  const void* v_lists;      /*   or NULL (both or neither)                  */
 } tsa_decode_opts;
+
+/* ------------------------------------------------------------------------
+ * tsa_kv_list_major - the K and V rows of every (request, KV head) copied in
+ *   posting-list order, so that each list is one contiguous run of rows.
+ *   [KARAT] How, index structure: an inverted file keeps its entries by
+ *   list; a decode then reads a chosen list as one stream instead of
+ *   scattered rows.
+ *   ids        (device) int32 [B][Hkv][N] from tsa_index_build
+ *   k_cache, v_cache  (device) [B][N][Hkv][d]
+ *   k_lists, v_lists  (device, out) [B][Hkv][N][d], caller-owned:
+ *              k_lists[b][g][e] = k_cache[b][ids[b][g][e]][g], likewise v;
+ *              a row whose id lies outside [0, N) is written as zeros.
+ *   Give both to tsa_sparse_decode_ex (opts->k_lists, opts->v_lists): the
+ *   rows of the chosen lists are then read from them, with the same lists,
+ *   counts and outputs. They describe one static index: build them again
+ *   after tsa_index_build or after the caches change. With them the decode
+ *   takes one list per token, no sink or window and no growing index
+ *   (else TSA_ERR_UNSUPPORTED). No workspace.
+ * ---------------------------------------------------------------------- */
+tsa_status tsa_kv_list_major(const tsa_ivf_desc* desc, const int32_t* ids, const void* k_cache,
+                             const void* v_cache, void* k_lists, void* v_lists, void* stream);
 
 tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts* opts, const void* q,
                                 const void* centroids, const int32_t* offsets, const int32_t* ids,

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tsa_abi_version() == B.ABI_VERSION == 2
+    assert lib.tsa_abi_version() == B.ABI_VERSION == 3
     assert lib.tsa_status_str(B.TSA_ERR_WORKSPACE) == b"TSA_ERR_WORKSPACE"
     assert lib.tsa_status_str(99) == b"TSA_ERR_UNKNOWN"
 
@@ -164,6 +164,34 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
         st = lib.tsa_sparse_decode_ex(ctypes.byref(desc), ctypes.byref(opts), fake, fake, fake, fake, fake, fake,
                                       kk, fake, None, None, None, fake, ws_wide, None)
         assert st == B.TSA_ERR_UNSUPPORTED and b"fused and split" in lib.tsa_last_error(), (opts.n_sink, kk)
+    # list-major copies: both or neither, aligned, plain lists only
+    fake3, fake4 = ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000)
+    for opts, want, msg in ((B.DecodeOpts(0, 0, 0, 0, None, None, None, 0, fake3, None), B.TSA_ERR_INVALID_ARG,
+                             b"both or neither"),
+                            (B.DecodeOpts(0, 0, 0, 0, None, None, None, 0, odd, fake4), B.TSA_ERR_INVALID_ARG,
+                             b"aligned"),
+                            (B.DecodeOpts(0, 4, 0, 0, None, None, None, 0, fake3, fake4), B.TSA_ERR_UNSUPPORTED,
+                             b"plain lists"),
+                            (B.DecodeOpts(0, 0, 2, 0, None, None, None, 0, fake3, fake4), B.TSA_ERR_UNSUPPORTED,
+                             b"plain lists"),
+                            (B.DecodeOpts(0, 0, 0, 0, None, fake2, None, 0, fake3, fake4), B.TSA_ERR_UNSUPPORTED,
+                             b"plain lists"),
+                            (B.DecodeOpts(0, 0, 0, 2, None, None, 0x50000, 0, fake3, fake4),
+                             B.TSA_ERR_UNSUPPORTED, b"plain lists")):
+        st = lib.tsa_sparse_decode_ex(ctypes.byref(d), ctypes.byref(opts), fake, fake, fake, fake, fake, fake, 4,
+                                      fake, None, None, None, fake, 1 << 30, None)
+        assert st == want and msg in lib.tsa_last_error(), lib.tsa_last_error()
+    st = lib.tsa_kv_list_major(ctypes.byref(d), fake, fake, fake2, None, fake4, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"k_lists is NULL" in lib.tsa_last_error()
+    st = lib.tsa_kv_list_major(ctypes.byref(d), fake, fake, fake2, fake3, fake3, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"separate" in lib.tsa_last_error()
+    st = lib.tsa_kv_list_major(ctypes.byref(d), fake, fake, fake2, fake, fake4, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"separate" in lib.tsa_last_error()
+    st = lib.tsa_kv_list_major(ctypes.byref(d), fake, fake, fake2, odd, fake4, None)
+    assert st == B.TSA_ERR_INVALID_ARG and b"aligned" in lib.tsa_last_error()
+    d_big = B.IvfDesc(8192, 100, 16, 16, 128, 8, 1, B.TSA_BF16)
+    st = lib.tsa_kv_list_major(ctypes.byref(d_big), fake, fake, fake2, fake3, fake4, None)
+    assert st == B.TSA_ERR_UNSUPPORTED
     assert B.workspace_bytes(B.OP_SPARSE_DECODE_EX_MULTI, d, 4) > ws_ex
     assert B.workspace_bytes(B.OP_INDEX_BUILD_MULTI, d) > B.workspace_bytes(B.OP_INDEX_BUILD, d)
     for m in (0, 5):

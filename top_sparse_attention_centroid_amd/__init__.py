@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     index_build_dyn_multi,
     index_regrow,
     kv_append,
+    kv_list_major,
     lib_path,
     load,
     resolve,
@@ -37,7 +38,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "index_build_multi", "index_build_dyn_multi", "index_regrow", "kv_append", "sparse_decode",
+    "workloads", "load", "lib_path", "abi_version", "index_build", "index_build_dyn", "index_build_multi", "index_build_dyn_multi", "index_regrow", "kv_append", "kv_list_major", "sparse_decode",
     "sparse_decode_dyn", "sparse_decode_ex", "sparse_decode_noalloc", "token_decode",
     "attend_rows", "resolve", "cache_reset", "fetch_rows", "hier_group_step", "HostArray", "time_next_gather", "time_next_launch", "stream_read", "workspace_bytes",
     "TsaError", "BoundCall",

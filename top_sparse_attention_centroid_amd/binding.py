@@ -20,7 +20,7 @@ TSA_F32, TSA_BF16 = 0, 1
  OP_SPARSE_DECODE_EX_MULTI) = range(7)
 SIMILARITY = {"dot": 0, "cosine": 1}
 SCHEDULE = {"auto": 0, "staged": 1, "fused": 2, "split": 3}
-ABI_VERSION = 2  # TSA_ABI_VERSION of include/tsa.h
+ABI_VERSION = 3  # TSA_ABI_VERSION of include/tsa.h
 EVICT_POLICIES = {"lru": 0, "fifo": 1, "random": 2, "priority": 3}
 
 _I32 = ctypes.c_int32
@@ -44,7 +44,8 @@ class CacheDesc(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("similarity", _I32), ("n_sink", _I32), ("n_window", _I32), ("assign_per_key", _I32),
-                ("lengths", _P), ("lens", _P), ("alt", _P), ("schedule", _I32)]
+                ("lengths", _P), ("lens", _P), ("alt", _P), ("schedule", _I32), ("k_lists", _P),
+                ("v_lists", _P)]
 
 
 class LayerIO(ctypes.Structure):
@@ -65,6 +66,7 @@ _SIGNATURES = {
     "tsa_sparse_decode_ex": [ctypes.POINTER(IvfDesc), ctypes.POINTER(DecodeOpts), _P, _P, _P, _P, _P, _P, _I32,
                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_index_build_multi": [ctypes.POINTER(IvfDesc), _P, _P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_kv_list_major": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P],
     "tsa_index_build_dyn": [ctypes.POINTER(IvfDesc), _P, _P, _I32, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_kv_append": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "tsa_sparse_decode_dyn": [ctypes.POINTER(IvfDesc), _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
@@ -441,7 +443,7 @@ def index_regrow(offsets, lens, ids, alt=None, slack: int = -1, *, out=None, sta
 def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, similarity: str = "dot",
                      n_sink: int = 0, n_window: int = 0, lengths=None, lens=None, alt=None, out=None,
                      sel_out=None, rows_out=None, uniq_out=None, ws=None, stream=None, schedule: str = "auto",
-                     bind: bool = False):
+                     k_lists=None, v_lists=None, bind: bool = False):
     """Decode with the variants: cosine similarity and/or the first n_sink and
     last n_window tokens (before lengths[b]) attended beside the lists; with
     `alt` (an m-way index from index_build_multi or index_build_dyn_multi)
@@ -450,8 +452,10 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
     gather, combine launches), "fused" (one launch) or "split" (scoring, a
     select + attend launch over shares of each head's rows, combine); fused
     and split take plain decodes (one list per key, no sink or window,
-    C <= 1024, k <= 64), split bf16 only. bind=True returns the call as a
-    BoundCall instead of running it."""
+    C <= 1024, k <= 64), split bf16 only. k_lists / v_lists: list-major
+    copies of the caches from kv_list_major for this index, from which the
+    chosen lists' rows are then read (plain lists only). bind=True returns
+    the call as a BoundCall instead of running it."""
     for t, n in ((q, "q"), (centroids, "centroids"), (offsets, "offsets"), (ids, "ids"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
@@ -478,16 +482,45 @@ def sparse_decode_ex(q, centroids, offsets, ids, k_cache, v_cache, k: int, *, si
     _i32(sel_out, "sel_out", (B, Hq, k))
     _i32(rows_out, "rows_out", (B, Hq))
     _i32(uniq_out, "uniq_out", (B, Hkv))
+    for t, n in ((k_lists, "k_lists"), (v_lists, "v_lists")):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != k_cache.dtype or tuple(t.shape) != (B, Hkv, N, d):
+                raise ValueError(f"{n} must be {k_cache.dtype} [B][Hkv][N][d] = {(B, Hkv, N, d)}")
     opts = DecodeOpts(SIMILARITY[similarity], n_sink, n_window, m, _ptr(lengths), _ptr(lens), _ptr(alt),
-                      SCHEDULE[schedule])
+                      SCHEDULE[schedule], _ptr(k_lists), _ptr(v_lists))
     ws = (_workspace(OP_SPARSE_DECODE_EX_MULTI, desc, k, ws, q.device, m) if m > 1
           else _workspace(OP_SPARSE_DECODE_EX, desc, k, ws, q.device))
     args = (ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(centroids), _ptr(offsets), _ptr(ids),
             _ptr(k_cache), _ptr(v_cache), k, _ptr(out), _ptr(sel_out), _ptr(rows_out), _ptr(uniq_out), _ptr(ws),
             ws.numel(), _stream(stream))
     keep = (desc, opts, q, centroids, offsets, ids, k_cache, v_cache, lengths, lens, alt, sel_out, rows_out,
-            uniq_out, ws)
+            uniq_out, ws, k_lists, v_lists)
     return _issue(bind, load().tsa_sparse_decode_ex, args, keep, out)
+
+
+def kv_list_major(ids, k_cache, v_cache, *, k_lists=None, v_lists=None, stream=None):
+    """List-major copies of the caches for a static index: k_lists[b][g][e] =
+    k_cache[b][ids[b][g][e]][g] (zeros for an id outside [0, N)), likewise v.
+    Returns (k_lists, v_lists), each [B][Hkv][N][d] of the caches' dtype."""
+    for t, n in ((ids, "ids"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    if k_cache.dtype != v_cache.dtype or tuple(k_cache.shape) != tuple(v_cache.shape):
+        raise ValueError("k_cache and v_cache must share a dtype and a shape")
+    B, N, Hkv, d = k_cache.shape
+    _i32(ids, "ids", (B, Hkv, N))
+    if k_lists is None:
+        k_lists = torch.empty((B, Hkv, N, d), dtype=k_cache.dtype, device=k_cache.device)
+    if v_lists is None:
+        v_lists = torch.empty((B, Hkv, N, d), dtype=k_cache.dtype, device=k_cache.device)
+    for t, n in ((k_lists, "k_lists"), (v_lists, "v_lists")):
+        _dev(t, n)
+        if t.dtype != k_cache.dtype or tuple(t.shape) != (B, Hkv, N, d):
+            raise ValueError(f"{n} must be {k_cache.dtype} [B][Hkv][N][d] = {(B, Hkv, N, d)}")
+    desc = IvfDesc(B, N, Hkv, Hkv, d, 1, 1, _dtype_code(k_cache.dtype))
+    _check(load().tsa_kv_list_major(ctypes.byref(desc), _ptr(ids), _ptr(k_cache), _ptr(v_cache), _ptr(k_lists),
+                                    _ptr(v_lists), _stream(stream)))
+    return k_lists, v_lists
 
 
 def sparse_decode_dyn(q, centroids, offsets, lens, ids, k_cache, v_cache, k: int, **kw):

@@ -229,12 +229,19 @@ __device__ __forceinline__ void gather_attn_body(const GatherParams& p) {
     if (tid + i * NW * kWave < kQParts) qpart[i].load(qb + (tid + i * NW * kWave) * 8);
   if (w0 * NW >= nseg) return;  // uniform over the block
 
-  const long long row_stride = static_cast<long long>(p.Hkv) * kHeadDim;
-  const T* kb = static_cast<const T*>(p.k) + static_cast<long long>(b) * p.n_rows * row_stride +
-                g * kHeadDim + e * 8;
-  const T* vb = static_cast<const T*>(p.v) + static_cast<long long>(b) * p.n_rows * row_stride +
-                g * kHeadDim + e * 8;
-  const int32_t* rid = p.rowids + b * p.rid_bstride + g * p.rid_gstride;
+  // explicit plans: list segments read the list-major copies by entry when
+  // given (every segment is then a list segment)
+  const bool by_entry = EXPLICIT && p.kl != nullptr;
+  const long long ebase = b * p.rid_bstride + g * p.rid_gstride;  // first row id / entry of the group
+  const long long row_stride = by_entry ? kHeadDim : static_cast<long long>(p.Hkv) * kHeadDim;
+  const T* kb = by_entry ? static_cast<const T*>(p.kl) + ebase * kHeadDim + e * 8
+                         : static_cast<const T*>(p.k) + static_cast<long long>(b) * p.n_rows * row_stride +
+                               g * kHeadDim + e * 8;
+  const T* vb = by_entry ? static_cast<const T*>(p.vl) + ebase * kHeadDim + e * 8
+                         : static_cast<const T*>(p.v) + static_cast<long long>(b) * p.n_rows * row_stride +
+                               g * kHeadDim + e * 8;
+  const long long row_limit = by_entry ? p.rid_gstride : p.n_rows;
+  const int32_t* rid = p.rowids + ebase;
   int* ids = ids_lds[wave];
   // sink / window ranges of an explicit plan: attended through their own
   // direct segments, so list rows inside them are skipped (empty by default)
@@ -293,7 +300,7 @@ __device__ __forceinline__ void gather_attn_body(const GatherParams& p) {
 #pragma unroll
     for (int i = 0; i < kIdsPerLane; ++i) {
       const int j = min(lane + i * kWave, max(sg.cnt - 1, 0));
-      dst[i] = sg.direct ? sg.start + j : rid[sg.start + j];
+      dst[i] = sg.direct || by_entry ? sg.start + j : rid[sg.start + j];
     }
   };
   auto store_ids = [&](const Seg& sg, const int (&src)[kIdsPerLane]) {
@@ -301,8 +308,9 @@ __device__ __forceinline__ void gather_attn_body(const GatherParams& p) {
     for (int i = 0; i < kIdsPerLane; ++i) {
       const int j = lane + i * kWave;
       const int id = src[i];
-      // ids outside [0, n_rows) are skipped, never dereferenced
-      bool ok = static_cast<unsigned long long>(id) < static_cast<unsigned long long>(p.n_rows);
+      // ids outside [0, n_rows) (entries outside the group) are skipped,
+      // never dereferenced
+      bool ok = static_cast<unsigned long long>(id) < static_cast<unsigned long long>(row_limit);
       if (!sg.direct) ok = ok && !(id < fx_sink || (id >= fx_lo && id < fx_hi));
       if (j < sg.cnt) ids[j] = ok ? id : -1;
     }
@@ -415,12 +423,19 @@ __device__ __forceinline__ void gather_merge_body(const GatherParams& p) {
   for (int i = 0; i < kQPer; ++i)
     if (tid + i * NW * kWave < kQParts) *reinterpret_cast<Raw8<T>*>(qs + (tid + i * NW * kWave) * 8) = qpart[i];
 
-  const long long row_stride = static_cast<long long>(p.Hkv) * kHeadDim;
-  const T* kb = static_cast<const T*>(p.k) + static_cast<long long>(b) * p.n_rows * row_stride +
-                g * kHeadDim + e * 8;
-  const T* vb = static_cast<const T*>(p.v) + static_cast<long long>(b) * p.n_rows * row_stride +
-                g * kHeadDim + e * 8;
-  const int32_t* rid = p.rowids + b * p.rid_bstride + g * p.rid_gstride;
+  // list segments read the list-major copies by entry when given (every
+  // segment is then a list segment: no sink / window ranges, m = 1)
+  const bool by_entry = p.kl != nullptr;
+  const long long ebase = b * p.rid_bstride + g * p.rid_gstride;  // first entry of the group
+  const long long row_stride = by_entry ? kHeadDim : static_cast<long long>(p.Hkv) * kHeadDim;
+  const T* kb = by_entry ? static_cast<const T*>(p.kl) + ebase * kHeadDim + e * 8
+                         : static_cast<const T*>(p.k) + static_cast<long long>(b) * p.n_rows * row_stride +
+                               g * kHeadDim + e * 8;
+  const T* vb = by_entry ? static_cast<const T*>(p.vl) + ebase * kHeadDim + e * 8
+                         : static_cast<const T*>(p.v) + static_cast<long long>(b) * p.n_rows * row_stride +
+                               g * kHeadDim + e * 8;
+  const long long row_limit = by_entry ? p.rid_gstride : p.n_rows;  // entries of a group, or tokens
+  const int32_t* rid = p.rowids + ebase;
   int* ids = ids_lds[wave];
   uint32_t* dup = dup_lds[DUP ? wave : 0];
   const int32_t* altb = DUP ? p.alt + (b * p.rid_bstride + g * p.rid_gstride) * p.alt_w : nullptr;
@@ -462,8 +477,8 @@ __device__ __forceinline__ void gather_merge_body(const GatherParams& p) {
     // the wave's row ids into its LDS area; ids outside [0, n_rows) are
     // skipped, never dereferenced
     for (int j = lane; j < my_cnt; j += kWave) {
-      const int id = my_direct ? my_start + j : rid[my_start + j];
-      bool ok = static_cast<unsigned long long>(id) < static_cast<unsigned long long>(p.n_rows);
+      const int id = my_direct || by_entry ? my_start + j : rid[my_start + j];
+      bool ok = static_cast<unsigned long long>(id) < static_cast<unsigned long long>(row_limit);
       if (!my_direct) ok = ok && !(id < fx_sink || (id >= fx_lo && id < fx_hi));
       ids[j] = ok ? id : -1;
       if constexpr (DUP) {  // heads that attend this token through a lower chosen list

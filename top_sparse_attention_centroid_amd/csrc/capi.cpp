@@ -419,6 +419,10 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
     HeadDecodeParams hp{};
     hp.s = selp;
     hp.ids = ids; hp.k = k_cache; hp.v = v_cache; hp.out = out;
+    if (opts) {
+      hp.kl = opts->k_lists;
+      hp.vl = opts->v_lists;
+    }
     hp.qscale = qscale(d.head_dim);
     hp.Hq = d.n_q_heads;
     if (sched == TSA_SCHED_FUSED) {
@@ -469,6 +473,8 @@ tsa_status sparse_decode_impl(const tsa_ivf_desc* desc, const tsa_decode_opts* o
     gp.n_sink = opts->n_sink;
     gp.n_window = opts->n_window;
     gp.lengths = opts->lengths;
+    gp.kl = opts->k_lists;
+    gp.vl = opts->v_lists;
   }
   if (m > 1) {
     gp.alt = opts->alt;
@@ -688,6 +694,23 @@ tsa_status tsa_sparse_decode_dyn(const tsa_ivf_desc* desc, const void* q, const 
                             rows_out, uniq_out, ws, ws_bytes, stream);
 }
 
+tsa_status tsa_kv_list_major(const tsa_ivf_desc* desc, const int32_t* ids, const void* k_cache,
+                             const void* v_cache, void* k_lists, void* v_lists, void* stream) {
+  if (tsa_status s = check_ivf(desc)) return s;
+  REQUIRE_PTR(ids); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(k_lists); REQUIRE_PTR(v_lists);
+  REQUIRE_ALIGN(k_cache, 16); REQUIRE_ALIGN(v_cache, 16); REQUIRE_ALIGN(k_lists, 16); REQUIRE_ALIGN(v_lists, 16);
+  if (k_lists == v_lists || k_lists == k_cache || k_lists == v_cache || v_lists == k_cache || v_lists == v_cache)
+    return fail(TSA_ERR_INVALID_ARG, "the list-major copies must be separate arrays from each other and the caches");
+  const tsa_ivf_desc& d = *desc;
+  if (static_cast<long long>(d.batch) * d.n_kv_heads > 65535)
+    return fail(TSA_ERR_UNSUPPORTED, "batch * n_kv_heads = %lld > 65535",
+                static_cast<long long>(d.batch) * d.n_kv_heads);
+  KvListsParams kp{ids, k_cache, v_cache, k_lists, v_lists, d.batch, d.n_tokens, d.n_kv_heads};
+  const hipError_t e = launch_kv_list_major(kp, d.dtype, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv_list_major launch");
+  return ok();
+}
+
 tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts* opts, const void* q,
                                 const void* centroids, const int32_t* offsets, const int32_t* ids,
                                 const void* k_cache, const void* v_cache, int32_t k, float* out,
@@ -714,6 +737,15 @@ tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts*
                 "C <= %d and k <= %d", kHeadMaxC, kHeadMaxK);
   if (opts->schedule == TSA_SCHED_SPLIT && desc->dtype != TSA_BF16)
     return fail(TSA_ERR_UNSUPPORTED, "the split decode scores bf16 codebooks only");
+  if ((opts->k_lists == nullptr) != (opts->v_lists == nullptr))
+    return fail(TSA_ERR_INVALID_ARG, "opts->k_lists and opts->v_lists: give both or neither");
+  if (opts->k_lists) {
+    REQUIRE_ALIGN(opts->k_lists, 16);
+    REQUIRE_ALIGN(opts->v_lists, 16);
+    if (opts->assign_per_key > 1 || opts->n_sink > 0 || opts->n_window > 0 || opts->lens)
+      return fail(TSA_ERR_UNSUPPORTED, "the list-major copies take plain lists: one list per token, no sink, "
+                  "window or growing index");
+  }
   return sparse_decode_impl(desc, opts, q, centroids, offsets, opts->lens, ids, k_cache, v_cache, k, out, sel_out,
                             rows_out, uniq_out, ws, ws_bytes, stream);
 }

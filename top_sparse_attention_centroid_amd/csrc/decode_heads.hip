@@ -219,10 +219,18 @@ __global__ __launch_bounds__(NW * kWave) void ivf_head_kernel(HeadDecodeParams p
   const int r0 = static_cast<int>(static_cast<long long>(R) * share / S);
   const int r1 = static_cast<int>(static_cast<long long>(R) * (share + 1) / S);
 
-  const long long row_stride = static_cast<long long>(sp.Hkv) * kHeadDim;
-  const T* kb = static_cast<const T*>(p.k) + static_cast<long long>(b) * sp.N * row_stride + g * kHeadDim + e * 8;
-  const T* vb = static_cast<const T*>(p.v) + static_cast<long long>(b) * sp.N * row_stride + g * kHeadDim + e * 8;
-  const int32_t* rid = p.ids + (static_cast<long long>(b) * sp.Hkv + g) * sp.n_entries;
+  // rows come from the list-major copies by entry when given, else from the
+  // caches by the entry's token id
+  const bool by_entry = p.kl != nullptr;
+  const long long ebase = (static_cast<long long>(b) * sp.Hkv + g) * sp.n_entries;  // first entry of the group
+  const long long row_stride = by_entry ? kHeadDim : static_cast<long long>(sp.Hkv) * kHeadDim;
+  const T* kb = by_entry ? static_cast<const T*>(p.kl) + ebase * kHeadDim + e * 8
+                         : static_cast<const T*>(p.k) + static_cast<long long>(b) * sp.N * row_stride + g * kHeadDim +
+                               e * 8;
+  const T* vb = by_entry ? static_cast<const T*>(p.vl) + ebase * kHeadDim + e * 8
+                         : static_cast<const T*>(p.v) + static_cast<long long>(b) * sp.N * row_stride + g * kHeadDim +
+                               e * 8;
+  const int32_t* rid = p.ids + ebase;
   QFrag<T> qf;
   qf.load(static_cast<const T*>(sp.q) + (static_cast<long long>(b) * p.Hq + qh) * kHeadDim + e * 8);
   HeadState st;
@@ -241,9 +249,12 @@ __global__ __launch_bounds__(NW * kWave) void ivf_head_kernel(HeadDecodeParams p
       if (cand < k && pc <= t) li = cand;
     }
     const int s0 = __shfl(st_i, li), p0 = __shfl(pre_i, li);
-    const int id = rid[s0 + (t - p0)];
-    // ids outside [0, N) are skipped, never dereferenced
-    const bool ok = lane < BR && base + lane < r1 && static_cast<unsigned>(id) < static_cast<unsigned>(sp.N);
+    const int ent = s0 + (t - p0);
+    const int id = by_entry ? ent : rid[ent];
+    // ids outside [0, N) (entries outside [0, n_entries)) are skipped, never
+    // dereferenced
+    const bool ok = lane < BR && base + lane < r1 &&
+                    static_cast<unsigned>(id) < static_cast<unsigned>(by_entry ? sp.n_entries : sp.N);
     wid[lane] = ok ? id : -1;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

@@ -1073,6 +1073,70 @@ static void select_dispatch(const SelectParams& p, int G, size_t lds, hipStream_
   else select_dispatch_g<T, kMaxCentroids / 64, kSelWaves>(p, G, lds, s);
 }
 
+// ============================================================================
+// List-major copy of the K/V rows ([KARAT] How: an inverted file keeps its
+// entries by list, so a chosen list is read as one contiguous stream).
+// Workgroup (x, bg) copies entries [x * kListCopyRows, ...) of (request, KV
+// head) bg: a row is kPieces 16-byte pieces, one per lane; each thread first
+// reads the token ids of its kListCopyU rows, then has all their loads in
+// flight before the stores.
+// ============================================================================
+constexpr int kListCopyThreads = 256;
+constexpr int kListCopyRows = 256;  // entries per workgroup
+constexpr int kListCopyU = 4;       // rows per thread in flight
+
+template <typename T>
+__global__ __launch_bounds__(kListCopyThreads) void kv_list_major_kernel(KvListsParams p) {
+  constexpr int kPieces = kHeadDimRows * static_cast<int>(sizeof(T)) / 16;  // 16 (bf16) or 32 (fp32)
+  constexpr int kElems = 16 / static_cast<int>(sizeof(T));                  // elements per piece
+  constexpr int kRowsPerPass = kListCopyThreads / kPieces;
+  static_assert(kListCopyRows % (kRowsPerPass * kListCopyU) == 0, "whole passes");
+  const int bg = blockIdx.y;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int piece = threadIdx.x % kPieces, rsub = threadIdx.x / kPieces;
+  const long long row_stride = static_cast<long long>(p.Hkv) * kHeadDimRows;  // elements between tokens
+  const T* kb = static_cast<const T*>(p.k) + static_cast<long long>(b) * p.N * row_stride + g * kHeadDimRows +
+                piece * kElems;
+  const T* vb = static_cast<const T*>(p.v) + static_cast<long long>(b) * p.N * row_stride + g * kHeadDimRows +
+                piece * kElems;
+  const long long gbase = static_cast<long long>(bg) * p.N;  // first entry of the group
+  T* kl = static_cast<T*>(p.kl) + gbase * kHeadDimRows + piece * kElems;
+  T* vl = static_cast<T*>(p.vl) + gbase * kHeadDimRows + piece * kElems;
+  const int32_t* ids = p.ids + gbase;
+  const int e0 = blockIdx.x * kListCopyRows;
+  for (int r0 = 0; r0 < kListCopyRows; r0 += kRowsPerPass * kListCopyU) {
+    int e[kListCopyU], id[kListCopyU];
+#pragma unroll
+    for (int u = 0; u < kListCopyU; ++u) {
+      e[u] = e0 + r0 + u * kRowsPerPass + rsub;
+      id[u] = e[u] < p.N ? ids[e[u]] : -1;
+    }
+    uint4 kv[kListCopyU], vv[kListCopyU];
+#pragma unroll
+    for (int u = 0; u < kListCopyU; ++u) {
+      const bool ok = static_cast<unsigned>(id[u]) < static_cast<unsigned>(p.N);
+      const long long off = static_cast<long long>(ok ? id[u] : 0) * row_stride;  // id 0: in bounds
+      kv[u] = load16_stream(kb + off);
+      vv[u] = load16_stream(vb + off);
+      if (!ok) kv[u] = vv[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kListCopyU; ++u) {
+      if (e[u] < p.N) {
+        *reinterpret_cast<uint4*>(kl + static_cast<long long>(e[u]) * kHeadDimRows) = kv[u];
+        *reinterpret_cast<uint4*>(vl + static_cast<long long>(e[u]) * kHeadDimRows) = vv[u];
+      }
+    }
+  }
+}
+
+hipError_t launch_kv_list_major(const KvListsParams& p, int dtype, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((p.N + kListCopyRows - 1) / kListCopyRows), p.B * p.Hkv);
+  if (dtype == kBF16) hipLaunchKernelGGL(kv_list_major_kernel<bf16_t>, grid, dim3(kListCopyThreads), 0, s, p);
+  else hipLaunchKernelGGL(kv_list_major_kernel<float>, grid, dim3(kListCopyThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int G>
 static void score_dispatch_g(const SelectParams& p, hipStream_t s) {
   const dim3 grid((p.C + 63) / 64, p.B * p.Hkv);

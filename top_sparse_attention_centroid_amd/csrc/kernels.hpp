@@ -116,6 +116,8 @@ struct HeadDecodeParams {
   float qscale;            // log2(e) / sqrt(d)
   int Hq;
   int S;                   // split: workgroups per query head (G * S <= smax)
+  const void* kl = nullptr;  // list-major copies [B][Hkv][n_entries][d], read by entry instead of
+  const void* vl = nullptr;  // k / v by row id; null: k / v
 };
 constexpr int kFusedWaves = 16;
 constexpr int kSplitWaves = 4;
@@ -124,6 +126,17 @@ constexpr int kHeadMaxK = 64;     // chosen lists of a head, one per lane
 hipError_t launch_fused_decode(const HeadDecodeParams& p, int dtype, int G, hipStream_t s);
 hipError_t launch_split_decode(const HeadDecodeParams& p, int G, hipStream_t s);  // bf16 only
 hipError_t launch_centroid_score(const SelectParams& p, int G, hipStream_t s);     // bf16; writes p.keys
+
+// ------------------------------------------------------- list-major KV copy
+struct KvListsParams {
+  const int32_t* ids;      // [B][Hkv][N]
+  const void* k;           // [B][N][Hkv][d]
+  const void* v;
+  void* kl;                // [B][Hkv][N][d]
+  void* vl;
+  int B, N, Hkv;
+};
+hipError_t launch_kv_list_major(const KvListsParams& p, int dtype, hipStream_t s);
 
 // ---------------------------------------------------------- KV + index append
 struct AppendParams {
@@ -191,6 +204,9 @@ struct GatherParams {
   float* out;              // [B][Hq][d]
   int B, Hkv, smax, W;     // W: workgroups per (request, KV head)
   float qscale;            // log2(e) / sqrt(d)
+  const void* kl = nullptr;  // explicit plans: list-major copies [B][Hkv][entries][d] (row of
+  const void* vl = nullptr;  // entry e of (b, g) at rowids offset b * rid_bstride + g * rid_gstride + e),
+                             // read instead of k / v for list segments; null: k / v by row id
 };
 hipError_t launch_gather(const GatherParams& p, int dtype, int G, bool explicit_plan,
                          hipStream_t s);
