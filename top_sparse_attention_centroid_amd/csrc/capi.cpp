@@ -6,7 +6,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
+#include <atomic>
+#include <chrono>
 #include <cstdio>
+#include <random>
 #include <mutex>
 #include <string>
 
@@ -181,7 +184,8 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false, int 
 
 struct TokLayout {
   int G = 0, smax = 0, seg_rows = 0, nfchunk = 0;
-  size_t keys = 0, hist = 0, cand_key = 0, cand_id = 0, cand_cnt = 0, sel = 0, partial = 0, total = 0;
+  size_t keys = 0, hist = 0, cand_key = 0, cand_id = 0, cand_cnt = 0, sel = 0, partial = 0, epoch = 0,
+         ready = 0, total = 0;
 };
 
 TokLayout tok_layout(const tsa_token_desc& d, int k) {
@@ -200,8 +204,24 @@ TokLayout tok_layout(const tsa_token_desc& d, int k) {
   L.sel = off;      off += align_up(static_cast<size_t>(d.batch) * k * sizeof(int32_t));
   L.partial = off;
   off += align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * L.smax * L.G * kPartStride * sizeof(float));
+  // the scan's histogram-clear handshake: the workspace's epoch and one
+  // ready tag per request
+  L.epoch = off;    off += align_up(sizeof(uint64_t));
+  L.ready = off;    off += align_up(static_cast<size_t>(d.batch) * sizeof(uint64_t));
   L.total = off;
   return L;
+}
+
+// Per-call nonces of the token decode's histogram-clear tag: a process-wide
+// counter from a seed drawn once, so that calls of different processes on
+// one workspace, and a call after a failed one, get different tags too.
+uint64_t next_token_nonce() {
+  static std::atomic<uint64_t> counter{[] {
+    std::random_device rd;
+    const uint64_t t = static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count());
+    return (static_cast<uint64_t>(rd()) << 32) ^ rd() ^ (t * 0x9E3779B97F4A7C15ull);
+  }()};
+  return counter.fetch_add(1, std::memory_order_relaxed);
 }
 
 struct RowsLayout {
@@ -770,6 +790,9 @@ tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const
                        sel, d.batch, d.n_tokens, k, L.nfchunk};
   tp.score_ev0 = g_scan_ev0;
   tp.score_ev1 = g_scan_ev1;
+  tp.epoch = reinterpret_cast<uint64_t*>(w + L.epoch);
+  tp.ready = reinterpret_cast<uint64_t*>(w + L.ready);
+  tp.nonce = next_token_nonce();
   g_scan_ev0 = g_scan_ev1 = nullptr;
   hipError_t e = launch_token_select(tp, d.dtype, s);
   if (e != hipSuccess) return hip_fail(e, "token_select launch");

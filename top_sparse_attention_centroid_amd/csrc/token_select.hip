@@ -9,7 +9,9 @@
 //             8 lanes x 16 B), each workgroup an equal share of a request,
 //             writes one order-preserving 32-bit key per token and adds
 //             every key's top 12 bits to a per-request histogram (one LDS
-//             histogram per workgroup, flushed once with global atomics).
+//             histogram per workgroup, flushed once with global atomics
+//             into the request's histogram, which the request's first
+//             workgroup clears in the same launch).
 //   filter -- every workgroup reads the histogram, finds the threshold bin
 //             (the highest bin at which the count from the top reaches k)
 //             and compacts the keys at or above it, in id order, into its
@@ -83,13 +85,31 @@ __device__ __forceinline__ void threshold_bin(const int32_t* hist, int k, int* s
   __syncthreads();
 }
 
+// The tag a call publishes once its histogram is clear: the SplitMix64
+// output function (Steele, Lea and Flood, OOPSLA 2014) of the workspace's
+// epoch and the call's nonce, so that neither a workspace of zeros nor one of
+// ones, nor a tag left by an earlier call, matches it.
+__device__ __forceinline__ uint64_t ready_tag(uint64_t epoch, uint64_t nonce) {
+  uint64_t z = (epoch ^ nonce) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+constexpr uint32_t kReadySpinLimit = 1u << 20;  // about 0.2 s of s_sleep; workgroup 0 runs first
+
 // Workgroup x of request b scans tokens [x * N / X, (x + 1) * N / X), X =
 // gridDim.x, in sub-tiles of kTokScoreTile staged through LDS, so that each
 // wave round's keys leave as whole lines; its LDS histogram covers its whole
 // share and is flushed once. X is chosen so that the B * X workgroups fill
 // every CU the same number of times (a grid of fixed tiles left a last
 // partial round of workgroups running alone). Scores: bf16 dot2 products,
-// 8 lanes a token.
+// 8 lanes a token. The request's global histogram is cleared here, not by a
+// launch of its own: workgroup 0 of the request, the first of the request's
+// workgroups to be dispatched, zeroes it with agent-scope (write-through)
+// stores as it starts, and after its first sub-tile, once those stores have
+// completed, publishes the call's tag; every other workgroup waits for the
+// tag before it adds its counts, at the end of its share (a bounded wait:
+// the workgroup it waits on is already running).
 template <typename T>
 __global__ __launch_bounds__(kScoreThreads) void token_score_kernel(TokenSelectParams p) {
   constexpr int NW = kScoreThreads / kWave;
@@ -101,6 +121,15 @@ __global__ __launch_bounds__(kScoreThreads) void token_score_kernel(TokenSelectP
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int e = lane & 7, tq = lane >> 3;
   for (int i = tid; i < kTokHistBins; i += kScoreThreads) h[i] = 0;
+  int32_t* gh = p.hist + static_cast<long long>(b) * kTokHistBins;
+  const uint64_t tag = ready_tag(*p.epoch, p.nonce);
+  const bool clears = blockIdx.x == 0;
+  if (clears) {
+    uint64_t* gh64 = reinterpret_cast<uint64_t*>(gh);
+    for (int i = tid; i < kTokHistBins / 2; i += kScoreThreads)
+      __hip_atomic_store(gh64 + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  bool published = !clears;
 
   QFrag<T> qv;
   qv.load(static_cast<const T*>(p.q_idx) + static_cast<long long>(b) * kIdxDim + e * 8);
@@ -128,9 +157,33 @@ __global__ __launch_bounds__(kScoreThreads) void token_score_kernel(TokenSelectP
       kout[i] = kv;
       atomicAdd(&h[kv >> kHistShift], 1);
     }
+    if (!published) {  // the clearing stores of every wave have completed
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
     __syncthreads();  // the next sub-tile overwrites sk
+    if (!published) {
+      if (tid == 0) __hip_atomic_store(p.ready + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      published = true;
+    }
   }
-  int32_t* gh = p.hist + static_cast<long long>(b) * kTokHistBins;
+  if (!published) {  // an empty share: publish after the clearing stores alone
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(p.ready + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!clears) {
+    if (tid == 0) {
+      uint32_t spins = 0;
+      while (__hip_atomic_load(p.ready + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag &&
+             ++spins < kReadySpinLimit)
+        __builtin_amdgcn_s_sleep(8);
+    }
+    __syncthreads();
+  }
   for (int i = tid; i < kTokHistBins; i += kScoreThreads) {
     const int c = h[i];
     if (c) atomicAdd(&gh[i], c);
@@ -212,6 +265,8 @@ __global__ __launch_bounds__(kFinalThreads) void token_final_kernel(TokenSelectP
   __shared__ int misc[2];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int nf = p.nfchunk;
+  // the last kernel of the call to use the histogram advances the epoch
+  if (b == 0 && tid == 0) *p.epoch = *p.epoch + 1;
   // the first chunk counts are requested before the histogram is scanned, so
   // the two round trips overlap
   const int cnt0 = tid < nf ? p.cand_cnt[static_cast<long long>(b) * nf + tid] : 0;
@@ -342,8 +397,7 @@ __global__ __launch_bounds__(kFinalThreads) void token_final_kernel(TokenSelectP
 
 template <typename T>
 static hipError_t token_select_typed(const TokenSelectParams& p, hipStream_t s) {
-  hipError_t e = launch_fill_i32(p.hist, static_cast<long long>(p.B) * kTokHistBins, 0, s);
-  if (e != hipSuccess) return e;
+  hipError_t e;
   // shares per request: kScoreWorkgroups in all (every CU the same number of
   // workgroups), at least kScoreMinShare tokens each, at least one
   const long long want = (kScoreWorkgroups + p.B - 1) / p.B;
