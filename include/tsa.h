@@ -445,10 +445,11 @@ tsa_status tsa_sparse_decode_ex(const tsa_ivf_desc* desc, const tsa_decode_opts*
  *   sel_out (device, out, nullable) int32 [B][k], ascending token ids
  *   Workspace: tsa_workspace_bytes(TSA_OP_TOKEN_DECODE, desc, k, ...). It
  *   may hold anything before a call: the scan launch clears the score
- *   histogram itself and marks it cleared with a tag drawn from an epoch the
- *   workspace keeps and a per-call nonce (so no earlier contents or earlier
- *   call pass for this call's mark, save by a 2^-64 coincidence). Calls that
- *   share a workspace must not overlap.
+ *   histogram and its per-request chunk counters itself and marks them
+ *   cleared with a tag drawn from an epoch the workspace keeps and a
+ *   per-call nonce (so no earlier contents or earlier call pass for this
+ *   call's mark, save by a 2^-64 coincidence). Calls that share a workspace
+ *   must not overlap.
  * ---------------------------------------------------------------------- */
 tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const void* k_idx,
                             const void* q, const void* k_cache, const void* v_cache, int32_t k,

@@ -101,6 +101,20 @@ def test_token_topk_integer_ties():
     _run_exact(cfg, q_idx, k_idx)
 
 
+# The scan's workgroups cover the first N - N // 10 tokens in fixed shares and
+# take the rest in 512-token chunks: no shared tail (N < 10), one short
+# chunk, several chunks with a ragged last one, and one request alone (every
+# workgroup on its chunks, 64 of them sharing the tail).
+@pytest.mark.parametrize("batch,n,k", [(3, 7, 3), (3, 3000, 200), (2, 15_377, 700), (1, 120_001, 900)])
+def test_token_topk_shared_tail(batch, n, k):
+    cfg = W.config(3, batch=batch, n_tokens=n, top_k=k, n_planted=min(8, k), steps=1)
+    announce(f"token shared scan tail B={batch} N={n} k={k}")
+    g = torch.Generator().manual_seed(n)
+    q_idx = torch.randint(-2, 3, (batch, 64), generator=g).to(torch.bfloat16).to(DEV)
+    k_idx = torch.randint(-1, 2, (batch, n, 64), generator=g).to(torch.bfloat16).to(DEV)
+    _run_exact(cfg, q_idx, k_idx, attn=n <= 3000)
+
+
 def test_token_topk_all_scores_equal():
     # q_idx = 0: every score is 0, so the selection is the k lowest token ids
     cfg = W.config(3, batch=2, n_tokens=10_000, top_k=777, n_planted=8, steps=1)

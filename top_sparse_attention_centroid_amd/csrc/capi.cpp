@@ -185,7 +185,7 @@ IvfLayout ivf_layout(const tsa_ivf_desc& d, int k, bool with_fixed = false, int 
 struct TokLayout {
   int G = 0, smax = 0, seg_rows = 0, nfchunk = 0;
   size_t keys = 0, hist = 0, cand_key = 0, cand_id = 0, cand_cnt = 0, sel = 0, partial = 0, epoch = 0,
-         ready = 0, total = 0;
+         ready = 0, grab = 0, total = 0;
 };
 
 TokLayout tok_layout(const tsa_token_desc& d, int k) {
@@ -205,9 +205,10 @@ TokLayout tok_layout(const tsa_token_desc& d, int k) {
   L.partial = off;
   off += align_up(static_cast<size_t>(d.batch) * d.n_kv_heads * L.smax * L.G * kPartStride * sizeof(float));
   // the scan's histogram-clear handshake: the workspace's epoch and one
-  // ready tag per request
+  // ready tag per request; the scan's per-request chunk counters
   L.epoch = off;    off += align_up(sizeof(uint64_t));
   L.ready = off;    off += align_up(static_cast<size_t>(d.batch) * sizeof(uint64_t));
+  L.grab = off;     off += align_up(static_cast<size_t>(d.batch) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -792,6 +793,7 @@ tsa_status tsa_token_decode(const tsa_token_desc* desc, const void* q_idx, const
   tp.score_ev1 = g_scan_ev1;
   tp.epoch = reinterpret_cast<uint64_t*>(w + L.epoch);
   tp.ready = reinterpret_cast<uint64_t*>(w + L.ready);
+  tp.grab = reinterpret_cast<int32_t*>(w + L.grab);
   tp.nonce = next_token_nonce();
   g_scan_ev0 = g_scan_ev1 = nullptr;
   hipError_t e = launch_token_select(tp, d.dtype, s);

@@ -225,13 +225,15 @@ struct TokenSelectParams {
   int B, N, k, nfchunk;
   hipEvent_t score_ev0 = nullptr, score_ev1 = nullptr;  // recorded around the scan launch when set
   // The scan clears the histogram itself: workgroup 0 of request b zeroes
-  // hist[b], then publishes tag = mix(*epoch ^ nonce) in ready[b]; the
+  // hist[b] and grab[b], then publishes tag = mix(*epoch ^ nonce) in ready[b]; the
   // other workgroups add their counts once ready[b] holds that tag. The final
   // select advances *epoch, so every call (and every replay of a captured
   // call) has a tag of its own.
   uint64_t* epoch = nullptr;  // [1]
   uint64_t* ready = nullptr;  // [B]
   uint64_t nonce = 0;         // per call, from the host
+  // per-request counter of the scan's shared chunks, zeroed with hist[b]
+  int32_t* grab = nullptr;    // [B]
 };
 hipError_t launch_token_select(const TokenSelectParams& p, int dtype, hipStream_t s);
 

@@ -6,7 +6,8 @@
 // The selection is the k largest scores under the total order (score desc,
 // token id asc), emitted in ascending id order. Three kernels:
 //   score  -- streams the indexer keys (d_idx = 64 bf16 = 128 B per token,
-//             8 lanes x 16 B), each workgroup an equal share of a request,
+//             8 lanes x 16 B), each workgroup an equal share of a request's
+//             first nine tenths, then chunks of the rest as it gets to them,
 //             writes one order-preserving 32-bit key per token and adds
 //             every key's top 12 bits to a per-request histogram (one LDS
 //             histogram per workgroup, flushed once with global atomics
@@ -35,6 +36,9 @@ constexpr int kIdxDim = 64;
 constexpr int kScoreThreads = 256;
 constexpr int kScoreUnroll = 8;  // 16-B loads in flight per lane
 constexpr int kTokScoreTile = 2048;  // tokens per LDS-staged sub-tile of a scan workgroup
+constexpr int kTokFirstTile = 256;   // the clearing workgroup's first sub-tile, after which it publishes
+constexpr int kTokDynDiv = 10;       // the last N / kTokDynDiv tokens of a request are shared out in chunks
+constexpr int kTokGrab = 512;        // tokens per shared chunk
 constexpr long long kScoreWorkgroups = 1024;  // scan workgroups per launch: 4 per CU
 constexpr long long kScoreMinShare = 1024;    // fewest tokens a scan workgroup takes
 constexpr int kFilterThreads = 256;
@@ -97,29 +101,71 @@ __device__ __forceinline__ uint64_t ready_tag(uint64_t epoch, uint64_t nonce) {
 }
 constexpr uint32_t kReadySpinLimit = 1u << 20;  // about 0.2 s of s_sleep; workgroup 0 runs first
 
-// Workgroup x of request b scans tokens [x * N / X, (x + 1) * N / X), X =
-// gridDim.x, in sub-tiles of kTokScoreTile staged through LDS, so that each
-// wave round's keys leave as whole lines; its LDS histogram covers its whole
-// share and is flushed once. X is chosen so that the B * X workgroups fill
-// every CU the same number of times (a grid of fixed tiles left a last
-// partial round of workgroups running alone). Scores: bf16 dot2 products,
-// 8 lanes a token. The request's global histogram is cleared here, not by a
-// launch of its own: workgroup 0 of the request, the first of the request's
-// workgroups to be dispatched, zeroes it with agent-scope (write-through)
-// stores as it starts, and after its first sub-tile, once those stores have
-// completed, publishes the call's tag; every other workgroup waits for the
-// tag before it adds its counts, at the end of its share (a bounded wait:
-// the workgroup it waits on is already running).
+// Scores tokens [start, start + n) of request b, n <= kTokScoreTile: the
+// keys go to LDS first, so that each wave round's keys leave as whole lines,
+// then out to keys[b], and their top bits into the workgroup's LDS histogram.
+// Ends with every thread past the LDS reads of sk except its own: the caller
+// puts a barrier between two calls.
 template <typename T>
-__global__ __launch_bounds__(kScoreThreads) void token_score_kernel(TokenSelectParams p) {
+__device__ __forceinline__ void score_tile(const TokenSelectParams& p, const QFrag<T>& qv, int b, int start, int n,
+                                           uint32_t* sk, int* h) {
   constexpr int NW = kScoreThreads / kWave;
-  __shared__ uint32_t sk[kTokScoreTile];
-  __shared__ int h[kTokHistBins];
-  const int b = blockIdx.y;
-  const int share_lo = static_cast<int>(static_cast<long long>(p.N) * blockIdx.x / gridDim.x);
-  const int share_hi = static_cast<int>(static_cast<long long>(p.N) * (blockIdx.x + 1) / gridDim.x);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int e = lane & 7, tq = lane >> 3;
+  const T* kb = static_cast<const T*>(p.k_idx) + (static_cast<long long>(b) * p.N + start) * kIdxDim + e * 8;
+  for (int iw = wave * 8; iw < n; iw += NW * 8 * kScoreUnroll) {
+    Raw8<T> raw[kScoreUnroll];
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int i = min(iw + u * NW * 8 + tq, n - 1);  // clamped: straight-line loads
+      raw[u].load_stream(kb + static_cast<long long>(i) * kIdxDim);
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int i = iw + u * NW * 8 + tq;
+      const float sc = group8_sum(qv.dot(raw[u]));
+      if (e == 0 && i < n) sk[i] = order_key(sc);
+    }
+  }
+  __syncthreads();
+  uint32_t* kout = p.keys + static_cast<long long>(b) * p.N + start;
+  for (int i = tid; i < n; i += kScoreThreads) {
+    const uint32_t kv = sk[i];
+    kout[i] = kv;
+    atomicAdd(&h[kv >> kHistShift], 1);
+  }
+}
+
+// Workgroup x of request b first scans its fixed share of the request's
+// leading tokens, [x * S / X, (x + 1) * S / X) with S = N - N / kTokDynDiv and
+// X = gridDim.x, in sub-tiles of kTokScoreTile. The rest, [S, N), is taken in
+// kTokGrab-token chunks from a per-request counter by whichever workgroups of
+// the request get there first: CUs do not stream at the same rate (they
+// differ by about a sixth at 16 x 200K tokens, whole XCDs included), and the
+// launch ends with its slowest CU. Shorter chunks and larger shared parts
+// were slower: each chunk costs a barrier round and a drained load pipeline. X is chosen so that the B * X workgroups
+// fill every CU the same number of times. Scores: bf16 dot2 products, 8 lanes
+// a token. The workgroup's LDS histogram covers all the tokens it scanned and
+// is flushed once, at its end.
+//
+// The request's global histogram and chunk counter are cleared here, not by a
+// launch of their own: workgroup 0 of the request, the first of the request's
+// workgroups to be dispatched, zeroes them with agent-scope (write-through)
+// stores as it starts, scans a short first sub-tile and then, once those
+// stores have completed, publishes the call's tag. Every other workgroup
+// waits for the tag after its fixed share (a bounded wait: the workgroup it
+// waits on is already running) before it takes chunks or adds its counts.
+template <typename T>
+__global__ __launch_bounds__(kScoreThreads) void token_score_kernel(TokenSelectParams p) {
+  __shared__ uint32_t sk[kTokScoreTile];
+  __shared__ int h[kTokHistBins];
+  __shared__ int next_chunk;
+  const int b = blockIdx.y;
+  const int S = p.N - p.N / kTokDynDiv;
+  const int share_lo = static_cast<int>(static_cast<long long>(S) * blockIdx.x / gridDim.x);
+  const int share_hi = static_cast<int>(static_cast<long long>(S) * (blockIdx.x + 1) / gridDim.x);
+  const int tid = threadIdx.x, lane = lane_id();
+  const int e = lane & 7;
   for (int i = tid; i < kTokHistBins; i += kScoreThreads) h[i] = 0;
   int32_t* gh = p.hist + static_cast<long long>(b) * kTokHistBins;
   const uint64_t tag = ready_tag(*p.epoch, p.nonce);
@@ -128,35 +174,16 @@ __global__ __launch_bounds__(kScoreThreads) void token_score_kernel(TokenSelectP
     uint64_t* gh64 = reinterpret_cast<uint64_t*>(gh);
     for (int i = tid; i < kTokHistBins / 2; i += kScoreThreads)
       __hip_atomic_store(gh64 + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(p.grab + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   bool published = !clears;
 
   QFrag<T> qv;
   qv.load(static_cast<const T*>(p.q_idx) + static_cast<long long>(b) * kIdxDim + e * 8);
-  for (int start = share_lo; start < share_hi; start += kTokScoreTile) {
-    const int n = min(kTokScoreTile, share_hi - start);
-    const T* kb = static_cast<const T*>(p.k_idx) + (static_cast<long long>(b) * p.N + start) * kIdxDim + e * 8;
-    for (int iw = wave * 8; iw < n; iw += NW * 8 * kScoreUnroll) {
-      Raw8<T> raw[kScoreUnroll];
-#pragma unroll
-      for (int u = 0; u < kScoreUnroll; ++u) {
-        const int i = min(iw + u * NW * 8 + tq, n - 1);  // clamped: straight-line loads
-        raw[u].load_stream(kb + static_cast<long long>(i) * kIdxDim);
-      }
-#pragma unroll
-      for (int u = 0; u < kScoreUnroll; ++u) {
-        const int i = iw + u * NW * 8 + tq;
-        const float sc = group8_sum(qv.dot(raw[u]));
-        if (e == 0 && i < n) sk[i] = order_key(sc);
-      }
-    }
-    __syncthreads();
-    uint32_t* kout = p.keys + static_cast<long long>(b) * p.N + start;
-    for (int i = tid; i < n; i += kScoreThreads) {
-      const uint32_t kv = sk[i];
-      kout[i] = kv;
-      atomicAdd(&h[kv >> kHistShift], 1);
-    }
+  for (int start = share_lo; start < share_hi;) {
+    const int n = min(published ? kTokScoreTile : kTokFirstTile, share_hi - start);
+    score_tile<T>(p, qv, b, start, n, sk, h);
+    start += n;
     if (!published) {  // the clearing stores of every wave have completed
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
@@ -175,13 +202,23 @@ __global__ __launch_bounds__(kScoreThreads) void token_score_kernel(TokenSelectP
     __syncthreads();
     if (tid == 0) __hip_atomic_store(p.ready + b, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (!clears) {
-    if (tid == 0) {
-      uint32_t spins = 0;
-      while (__hip_atomic_load(p.ready + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag &&
-             ++spins < kReadySpinLimit)
-        __builtin_amdgcn_s_sleep(8);
-    }
+  if (!clears && tid == 0) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(p.ready + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag &&
+           ++spins < kReadySpinLimit)
+      __builtin_amdgcn_s_sleep(8);
+  }
+  // the shared tail, a chunk at a time; the next chunk is asked for before
+  // the current one is scanned
+  const int nchunks = (p.N - S + kTokGrab - 1) / kTokGrab;
+  if (tid == 0) next_chunk = atomicAdd(p.grab + b, 1);
+  __syncthreads();
+  for (int c = next_chunk; c < nchunks; c = next_chunk) {
+    int ahead = 0;
+    if (tid == 0) ahead = atomicAdd(p.grab + b, 1);
+    const int start = S + c * kTokGrab;
+    score_tile<T>(p, qv, b, start, min(kTokGrab, p.N - start), sk, h);
+    if (tid == 0) next_chunk = ahead;  // every thread read next_chunk before score_tile's barrier
     __syncthreads();
   }
   for (int i = tid; i < kTokHistBins; i += kScoreThreads) {
