@@ -33,15 +33,15 @@
 namespace tsa {
 
 constexpr int kIdxDim = 64;
-constexpr int kScoreThreads = 256;
-constexpr int kScoreUnroll = 8;  // 16-B loads in flight per lane
+constexpr int kScoreThreads = 512;
+constexpr int kScoreUnroll = 4;  // 16-B loads in flight per lane (8 waves x 4 beat 4 waves x 8)
 constexpr int kTokScoreTile = 2048;  // tokens per LDS-staged sub-tile of a scan workgroup
 constexpr int kTokFirstTile = 256;   // the clearing workgroup's first sub-tile, after which it publishes
 constexpr int kTokDynDiv = 10;       // the last N / kTokDynDiv tokens of a request are shared out in chunks
 constexpr int kTokGrab = 512;        // tokens per shared chunk
 constexpr long long kScoreWorkgroups = 1024;  // scan workgroups per launch: 4 per CU
 constexpr long long kScoreMinShare = 1024;    // fewest tokens a scan workgroup takes
-constexpr int kFilterThreads = 256;
+constexpr int kFilterThreads = 512;
 constexpr int kFinalThreads = 1024;
 constexpr int kHistShift = 32 - kTokHistBits;
 constexpr int kFinalLdsCands = 8192;  // candidates the final kernel stages in LDS
