@@ -395,10 +395,13 @@ int resolve_schedule(const tsa_ivf_desc& d, int k, const tsa_decode_opts* opts) 
 }
 
 // Split decode: shares per query head so that each of a share's kSplitWaves
-// waves attends about one batch (32 rows) of an average head (k * N / C rows),
-// at most kSplitMaxWorkgroups workgroups in all, and G * S partial records
-// within the plan's smax per group.
-constexpr long long kSplitRowsPerShare = kSplitWaves * 32;
+// waves attends about half a batch (16 rows) of an average head (k * N / C
+// rows), at most kSplitMaxWorkgroups workgroups in all, and G * S partial
+// records within the plan's smax per group. At one 100K-token request
+// (1,000 rows a head, 8 shares) 8 waves of 16 rows beat 4 waves of 32
+// (16.0 against 17.0 us for the kernel); 4 or 16 shares, and 4 or 16 waves,
+// were slower.
+constexpr long long kSplitRowsPerShare = kSplitWaves * 16;
 constexpr long long kSplitMaxWorkgroups = 2048;
 int split_shares(const tsa_ivf_desc& d, int k, const IvfLayout& L) {
   const long long rows = static_cast<long long>(k) * d.n_tokens / d.n_centroids;

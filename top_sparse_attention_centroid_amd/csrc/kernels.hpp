@@ -119,8 +119,8 @@ struct HeadDecodeParams {
   const void* kl = nullptr;  // list-major copies [B][Hkv][n_entries][d], read by entry instead of
   const void* vl = nullptr;  // k / v by row id; null: k / v
 };
-constexpr int kFusedWaves = 16;
-constexpr int kSplitWaves = 4;
+constexpr int kFusedWaves = 8;    // beat 16, 4 and 2 waves at one 4K-token fp32 head
+constexpr int kSplitWaves = 8;    // with 16 rows a wave per share; see split_shares
 constexpr int kHeadMaxC = 1024;   // lists of a group held in one workgroup's LDS
 constexpr int kHeadMaxK = 64;     // chosen lists of a head, one per lane
 hipError_t launch_fused_decode(const HeadDecodeParams& p, int dtype, int G, hipStream_t s);
