@@ -225,7 +225,7 @@ struct TokenSelectParams {
   int B, N, k, nfchunk;
   hipEvent_t score_ev0 = nullptr, score_ev1 = nullptr;  // recorded around the scan launch when set
   // The scan clears the histogram itself: workgroup 0 of request b zeroes
-  // hist[b] and grab[b], then publishes tag = mix(*epoch ^ nonce) in ready[b]; the
+  // hist[b] and grab[b], then publishes tag = mix(*epoch * phi + nonce) in ready[b]; the
   // other workgroups add their counts once ready[b] holds that tag. The final
   // select advances *epoch, so every call (and every replay of a captured
   // call) has a tag of its own.

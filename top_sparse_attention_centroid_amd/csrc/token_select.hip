@@ -90,11 +90,17 @@ __device__ __forceinline__ void threshold_bin(const int32_t* hist, int k, int* s
 }
 
 // The tag a call publishes once its histogram is clear: the SplitMix64
-// output function (Steele, Lea and Flood, OOPSLA 2014) of the workspace's
-// epoch and the call's nonce, so that neither a workspace of zeros nor one of
-// ones, nor a tag left by an earlier call, matches it.
+// output function (Steele, Lea and Flood, OOPSLA 2014), a bijection on 64-bit
+// words, of epoch * phi + nonce (phi = 0x9E3779B97F4A7C15, odd). Between a
+// call and the one before it on the same workspace the epoch has advanced by
+// one and the nonce has changed, so that input differs (by phi plus the nonce
+// step), and so does the tag: the tag left by the previous call never passes
+// for this call's. (Mixing epoch ^ nonce instead is not enough: when both go
+// up by one and end in the same run of one bits, the XOR does not change.)
+// Graph replays keep the nonce and advance the epoch, and a workspace of any
+// other contents matches only by a 2^-64 coincidence.
 __device__ __forceinline__ uint64_t ready_tag(uint64_t epoch, uint64_t nonce) {
-  uint64_t z = (epoch ^ nonce) + 0x9E3779B97F4A7C15ull;
+  uint64_t z = epoch * 0x9E3779B97F4A7C15ull + nonce;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   return z ^ (z >> 31);
