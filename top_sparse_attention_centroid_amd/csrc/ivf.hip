@@ -521,16 +521,17 @@ __global__ __launch_bounds__(256) void csr_kernel(CsrParams p) {
 // each list cut into segments of at most seg_rows rows, ascending list order.
 // ============================================================================
 // Scoring as its own launch, for batches too small to fill the chip with one
-// workgroup per (request, KV head): grid (ceil(C / 64), B * Hkv), each wave
-// one 16-centroid tile, keys to p.keys; with p.arrive_heads it also clears
+// workgroup per (request, KV head): grid (ceil(C / (16 * kScoreTileWaves)),
+// B * Hkv), each wave one 16-centroid tile, keys to p.keys; with p.arrive_heads it also clears
 // the group's arrival counters of the split decode.
+constexpr int kScoreTileWaves = 2;  // 16-centroid tiles (one a wave) per scoring workgroup; 2 beat 4 and 8
 template <int G>
-__global__ __launch_bounds__(256) void centroid_score_kernel(SelectParams p) {
+__global__ __launch_bounds__(kScoreTileWaves * kWave) void centroid_score_kernel(SelectParams p) {
   const int bg = blockIdx.y;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   // the split decode's arrival counters of the group, for the launch after
   if (p.arrive_heads && blockIdx.x == 0 && threadIdx.x < G) p.arrive_heads[bg * G + threadIdx.x] = 0u;
-  const int t = blockIdx.x * 4 + static_cast<int>(threadIdx.x) / kWave;
+  const int t = blockIdx.x * kScoreTileWaves + static_cast<int>(threadIdx.x) / kWave;
   const int ntile = (p.C + 15) / 16;
   if (t >= ntile) return;  // uniform over the wave
   score_tiles_mfma<G>(p, b, g, t, t + 1, p.keys + static_cast<long long>(bg) * G * p.C);
@@ -1139,8 +1140,8 @@ hipError_t launch_kv_list_major(const KvListsParams& p, int dtype, hipStream_t s
 
 template <int G>
 static void score_dispatch_g(const SelectParams& p, hipStream_t s) {
-  const dim3 grid((p.C + 63) / 64, p.B * p.Hkv);
-  hipLaunchKernelGGL(centroid_score_kernel<G>, grid, dim3(256), 0, s, p);
+  const dim3 grid((p.C + 16 * kScoreTileWaves - 1) / (16 * kScoreTileWaves), p.B * p.Hkv);
+  hipLaunchKernelGGL(centroid_score_kernel<G>, grid, dim3(kScoreTileWaves * kWave), 0, s, p);
 }
 
 hipError_t launch_centroid_score(const SelectParams& p, int G, hipStream_t s) {
