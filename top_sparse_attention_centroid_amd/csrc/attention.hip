@@ -566,7 +566,7 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 // trips, run one head per workgroup with kCombineWavesSmall waves: the
 // descriptors and (m, l) are requested together, and the NS partial states
 // of the head are merged through LDS in a fixed order.
-constexpr int kCombineWavesSmall = 16;  // waves per head when the batch is small
+constexpr int kCombineWavesSmall = 8;  // waves per head when the batch is small (8 beat 16 at 16 x 8 token selections)
 
 // The calling wave's share of query head h's partial states in group bg:
 // records part, part + NS, ... merged into (M, L, O0, O1), lane l holding
