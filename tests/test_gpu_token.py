@@ -162,3 +162,34 @@ def test_token_workspace_contents_never_reach_the_output(batch):
     torch.cuda.synchronize()
     assert all(bool(torch.isfinite(o).all()) for o in outs)
     assert torch.equal(outs[0], outs[1]) and torch.equal(sels[0], sels[1])
+
+
+def test_token_consecutive_calls_on_one_workspace():
+    """Twelve decodes in a row on one workspace, each selection against the
+    oracle. Every call clears the histogram and the chunk counters that the
+    previous call left and marks them cleared with a tag of its own; the
+    scan's other workgroups wait for that tag. A tag equal to the previous
+    call's would let them add their counts before the clear (a tag built from
+    epoch ^ nonce did so for about a third of consecutive calls, since both
+    advance by one a call)."""
+    cfg = W.config(3, batch=4, n_tokens=30_011, top_k=700, n_planted=16, steps=12)
+    announce("token: 12 consecutive calls on one workspace")
+    prob = W.token_problem(cfg, device=DEV)
+    q_idx, q = W.token_queries(cfg, prob, steps=12)
+    k_idx = condition_token_keys(q_idx, prob["k_idx"], cfg.top_k, 12, requests=range(cfg.batch))
+    B, k = cfg.batch, cfg.top_k
+    desc = tsa.binding.token_desc(k_idx, prob["keys"], cfg.n_q_heads)
+    ws = torch.empty(tsa.workspace_bytes(tsa.binding.OP_TOKEN_DECODE, desc, k), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device=DEV)
+    sels = torch.empty((12, B, k), dtype=torch.int32, device=DEV)
+    for t in range(12):  # back to back on one stream, no host sync between calls
+        tsa.token_decode(q_idx[t], k_idx, q[t], prob["keys"], prob["values"], k, out=out, sel_out=sels[t], ws=ws)
+    torch.cuda.synchronize()
+    got = sels.cpu().numpy()
+    qi64 = f64(q_idx)
+    for b in range(B):
+        kidx64 = f64(k_idx[b])
+        for t in range(12):
+            ref_sel, gap = token.token_topk(qi64[t, b], kidx64, k)
+            assert gap >= GAP_MIN
+            assert np.array_equal(got[t][b], ref_sel), f"selection differs (call {t}, request {b})"
